@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""FP32 SGEMM throughput on one MI355X.
+
+One step is one C = alpha*A*B + beta*C call through the C ABI (the whole hot
+path: tile loads, LDS staging, inner product, epilogue) on the square 8192^3
+problem (A, B ~ N(0,1) float32, seed 3, alpha = 1, beta = 0, C zeroed), with
+every operand already resident in HBM.  W untimed warm-up steps, then K timed
+steps bracketed by device synchronisation; one JSON line on stdout.
+
+  value      = 2*M*N*K*K_steps / (timed seconds) / 1e12      [TFLOP/s]
+  roofline   = the kernel's average duration from HIP events recorded on the
+               launch stream around every timed launch; achieved = 2MNK / that
+               duration; peak = 157.3 TFLOP/s (FP32 matrix, 256 CU x 256 FLOP/clk
+               x 2.4 GHz); traffic = HBM bytes per launch from rocprofv3
+               FETCH_SIZE + WRITE_SIZE (scaled by a copy-kernel calibration), read
+               from profiles/ when it was taken on the current kernel source,
+               else null.
+  cpu_baseline = the float64 CPU oracle on a bounded band of rows of the same
+               problem, on every host core (rank 0, N = 1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP32_TFLOPS = 157.3  # 256 CU x 256 FLOP/clk x 2.4 GHz (FP32 MFMA; packed VALU alike)
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = "square8192_normal"
+SECONDARY = "square4096_upm1"
+
+
+def kernel_source_hash() -> str:
+    from fp32_gemm_03_amd import build as b
+    h = hashlib.sha256()
+    for p in sorted(b.DEPENDS):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(variant_name: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when there is none for this kernel or it predates the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(WORKLOAD, {}).get(variant_name)
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def time_gpu(p, steps, warmup, path):
+    import torch
+    import fp32_gemm_03_amd as g
+
+    a = p.A.cuda()
+    b = p.B.cuda()
+    c = p.C.cuda()
+    stream = torch.cuda.Stream()
+    args = (p.M, p.N, p.K, p.alpha, a, p.lda, b, p.ldb, p.beta, c, p.ldc)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.sgemm_path(path, *args, stream=stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(steps):
+        g.sgemm_path(path, *args, stream=stream)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    total_ms = ev[0].elapsed_time(ev[steps])
+    del a, b, c
+    return total_ms, per_launch_ms, wall
+
+
+def cpu_baseline(p, target_s=10.0):
+    import numpy as np
+    import oracle
+
+    A, B = p.np("A"), p.np("B")
+    cores = oracle.nthreads()
+    rows = max(8, min(cores, p.M))
+    t0 = time.perf_counter()
+    oracle.sgemm_rows(p.M, p.N, p.K, p.alpha, A, p.lda, B, p.ldb, p.beta, None, p.ldc, 0, rows)
+    t_probe = time.perf_counter() - t0
+    rows2 = int(max(rows, min(p.M, rows * target_s / max(t_probe, 1e-3))))
+    rows2 = max(rows, (rows2 // cores) * cores)
+    t0 = time.perf_counter()
+    oracle.sgemm_rows(p.M, p.N, p.K, p.alpha, A, p.lda, B, p.ldb, p.beta, None, p.ldc, 0, rows2)
+    t = time.perf_counter() - t0
+    flops = 2.0 * rows2 * p.N * p.K
+    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"rows 0..{rows2 - 1} of the {p.M}x{p.N}x{p.K} problem "
+                      f"({rows2 * p.N} elements, float64 i-k-j loop), {t:.1f} s",
+            "seconds": round(t, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this SGEMM runs on one GPU; multi-GPU runs are not part of it "
+              "(a row-block split of C would need no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp32_gemm_03_amd as g
+    from fp32_gemm_03_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    g.load_library()
+    path = {"auto": g.SGEMM_PATH_AUTO, "valu": g.SGEMM_PATH_VALU, "mfma": g.SGEMM_PATH_MFMA}[args.path]
+
+    w = inputs.WORKLOADS[args.workload]
+    p = inputs.workload_problem(args.workload)
+    variant = g.sgemm_select_variant(path, p.M, p.N, p.K)
+    vname = g.sgemm_variant_name(variant)
+    print(f"bench: {args.workload} variant {vname}, {args.warmup} warm-up + {args.steps} timed",
+          file=sys.stderr, flush=True)
+    total_ms, per_launch, wall = time_gpu(p, args.steps, args.warmup, path)
+    ms_per_step = total_ms / args.steps
+    value = w.flops / (ms_per_step / 1e3) / 1e12
+    avg_kernel_ms = sum(per_launch) / len(per_launch)
+    achieved = w.flops / (avg_kernel_ms / 1e3) / 1e12
+
+    traffic = read_traffic(vname)
+    out = {
+        "metric": "FP32 SGEMM TFLOP/s (2MNK/t)",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": p.M, "N": p.N, "K": p.K,
+                   "alpha": p.alpha, "beta": p.beta, "dist": w.dist, "seed": w.seed,
+                   "variant": vname, "path": args.path},
+        "pct_of_fp32_peak": round(100.0 * value / PEAK_FP32_TFLOPS, 2),
+        "roofline": {"bound": "mfma" if g.sgemm_variant_path(variant) == g.SGEMM_PATH_MFMA else "alu",
+                     "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel_avg_ms": round(avg_kernel_ms, 4),
+                     "kernel_min_ms": round(min(per_launch), 4),
+                     "algorithmic_flops_per_launch": w.flops,
+                     "algorithmic_bytes_per_launch": w.algorithmic_bytes},
+    }
+    if not args.no_secondary and args.workload == WORKLOAD:
+        p2 = inputs.workload_problem(SECONDARY)
+        w2 = inputs.WORKLOADS[SECONDARY]
+        steps2 = max(args.steps, 20)
+        t2, per2, _ = time_gpu(p2, steps2, args.warmup, path)
+        v2 = g.sgemm_select_variant(path, p2.M, p2.N, p2.K)
+        out["secondary"] = {"workload": SECONDARY, "variant": g.sgemm_variant_name(v2),
+                            "value": round(w2.flops / (t2 / steps2 / 1e3) / 1e12, 3),
+                            "unit": "TFLOP/s", "ms_per_step": round(t2 / steps2, 4)}
+        del p2
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(p)
+    out["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+"""MI355X (gfx950) FP32 SGEMM: C = alpha*A*B + beta*C on row-major matrices.
+
+A thin Python binding of the C ABI in ``include/sgemm.h``: every function has
+the name and argument order of its C counterpart and only marshals arguments.
+All arithmetic runs in the HIP kernels of ``libsgemm_mi355x.so``; there is no
+CPU fallback, and a missing library raises :class:`LibraryNotBuilt`.
+
+Pointer arguments accept a torch tensor on the GPU (its ``data_ptr()`` is
+passed) or a raw device address as an ``int``.  ``stream`` accepts a
+``torch.cuda.Stream``, a raw ``hipStream_t`` as an ``int``, or ``None`` for
+torch's current stream on the current device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from . import inputs  # noqa: F401  (seeded synthetic inputs; no GPU needed)
+
+__all__ = [
+    "SGEMM_PATH_AUTO", "SGEMM_PATH_VALU", "SGEMM_PATH_MFMA",
+    "SgemmError", "LibraryNotBuilt", "library_path", "load_library",
+    "sgemm", "sgemm_path", "sgemm_variant", "sgemm_variant_count",
+    "sgemm_variant_name", "sgemm_variant_path", "sgemm_variant_tile",
+    "sgemm_select_variant", "sgemm_status_string", "variants",
+]
+
+SGEMM_PATH_AUTO = 0
+SGEMM_PATH_VALU = 1
+SGEMM_PATH_MFMA = 2
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIBNAME = "libsgemm_mi355x.so"
+_lock = threading.Lock()
+_lib = None
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int, where: str = "sgemm"):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {sgemm_status_string(status)}")
+
+
+def library_path() -> str:
+    return os.path.join(_PKG, _LIBNAME)
+
+
+def load_library():
+    """Load the in-tree HIP library (``python -m fp32_gemm_03_amd.build`` makes it)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise LibraryNotBuilt(
+                f"{path} is missing: build it with `python -m fp32_gemm_03_amd.build` "
+                "(hipcc, gfx950); there is no CPU fallback")
+        lib = ctypes.CDLL(path)
+        i, f, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+        gemm_args = [i, i, i, f, vp, i, vp, i, f, vp, i, vp]
+        lib.sgemm.argtypes = gemm_args
+        lib.sgemm.restype = i
+        lib.sgemm_path.argtypes = [i] + gemm_args
+        lib.sgemm_path.restype = i
+        lib.sgemm_variant.argtypes = [i] + gemm_args
+        lib.sgemm_variant.restype = i
+        lib.sgemm_variant_count.argtypes = []
+        lib.sgemm_variant_count.restype = i
+        lib.sgemm_variant_name.argtypes = [i]
+        lib.sgemm_variant_name.restype = ctypes.c_char_p
+        lib.sgemm_variant_path.argtypes = [i]
+        lib.sgemm_variant_path.restype = i
+        lib.sgemm_variant_tile.argtypes = [i, ctypes.POINTER(i), ctypes.POINTER(i)]
+        lib.sgemm_variant_tile.restype = i
+        lib.sgemm_select_variant.argtypes = [i, i, i, i]
+        lib.sgemm_select_variant.restype = i
+        lib.sgemm_status_string.argtypes = [i]
+        lib.sgemm_status_string.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    dp = getattr(x, "data_ptr", None)
+    if dp is None:
+        raise TypeError(f"expected a tensor or an int device address, got {type(x)!r}")
+    if getattr(x, "is_cuda", True) is False:
+        raise TypeError("SGEMM operands must live in GPU memory")
+    return dp()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _gemm_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream):
+    return (int(M), int(N), int(K), float(alpha), _ptr(A), int(lda), _ptr(B), int(ldb),
+            float(beta), _ptr(C), int(ldc), _stream(stream))
+
+
+def _ret(status, where, check):
+    if check and status != 0:
+        raise SgemmError(status, where)
+    return status
+
+
+def sgemm(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None, check=True):
+    """C = alpha*A*B + beta*C; returns the status (raises on nonzero when ``check``)."""
+    lib = load_library()
+    return _ret(lib.sgemm(*_gemm_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)),
+                "sgemm", check)
+
+
+def sgemm_path(path, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None, check=True):
+    lib = load_library()
+    return _ret(lib.sgemm_path(int(path), *_gemm_args(M, N, K, alpha, A, lda, B, ldb, beta,
+                                                      C, ldc, stream)), "sgemm_path", check)
+
+
+def sgemm_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None,
+                  check=True):
+    lib = load_library()
+    return _ret(lib.sgemm_variant(int(variant), *_gemm_args(M, N, K, alpha, A, lda, B, ldb,
+                                                            beta, C, ldc, stream)),
+                "sgemm_variant", check)
+
+
+def sgemm_variant_count() -> int:
+    return int(load_library().sgemm_variant_count())
+
+
+def sgemm_variant_name(variant):
+    r = load_library().sgemm_variant_name(int(variant))
+    return None if r is None else r.decode()
+
+
+def sgemm_variant_path(variant) -> int:
+    return int(load_library().sgemm_variant_path(int(variant)))
+
+
+def sgemm_variant_tile(variant):
+    """``(status, bm, bn)``."""
+    bm, bn = ctypes.c_int(0), ctypes.c_int(0)
+    rc = load_library().sgemm_variant_tile(int(variant), ctypes.byref(bm), ctypes.byref(bn))
+    return int(rc), bm.value, bn.value
+
+
+def sgemm_select_variant(path, M, N, K) -> int:
+    return int(load_library().sgemm_select_variant(int(path), int(M), int(N), int(K)))
+
+
+def sgemm_status_string(status) -> str:
+    return load_library().sgemm_status_string(int(status)).decode()
+
+
+def variants():
+    """``[(index, name, path, bm, bn), ...]`` for every compiled variant."""
+    out = []
+    for v in range(sgemm_variant_count()):
+        _, bm, bn = sgemm_variant_tile(v)
+        out.append((v, sgemm_variant_name(v), sgemm_variant_path(v), bm, bn))
+    return out

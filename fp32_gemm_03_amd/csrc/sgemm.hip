@@ -1,0 +1,202 @@
+// sgemm.hip -- C ABI of the gfx950 FP32 SGEMM library (see include/sgemm.h):
+// argument checks, the table of compiled kernel variants, the shape-based
+// choice of variant, and the launch on the caller's stream.
+//
+// The library holds no state: every call validates, picks a variant and
+// enqueues one kernel.  Nothing here allocates device memory.
+#include "sgemm.h"
+
+#include <limits.h>
+#include <stdint.h>
+
+#include "sgemm_kernels.hpp"
+
+namespace {
+
+using sgk::Args;
+
+typedef void (*KernelFn)(Args);
+
+struct Variant {
+    const char *name;
+    int path;           // SGEMM_PATH_VALU or SGEMM_PATH_MFMA
+    int bm, bn;         // block tile
+    int threads;        // workgroup size
+    KernelFn vec4;      // B, C and their leading dimensions 16-byte friendly
+    KernelFn vec1;      // anything else
+};
+
+// VALU: 128 x 128 x 16 block, 4 waves of 64 x 64, 8 x 8 per lane.
+#define VALU_CFG(BM, BN, BK, TM, TN, PA, PB)                                            \
+    {"valu_" #BM "x" #BN "x" #BK "_t" #TM "x" #TN, SGEMM_PATH_VALU, BM, BN,               \
+     (BM / (8 * TM)) * (BN / (8 * TN)) * 64,                                             \
+     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 4>,                                  \
+     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1>}
+
+#define MFMA_CFG(BM, BN, BK, WM, WN, PA, PB)                                            \
+    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN, SGEMM_PATH_MFMA, BM, BN,               \
+     (BM / WM) * (BN / WN) * 64,                                                         \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4>,                                  \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1>}
+
+const Variant kVariants[] = {
+    VALU_CFG(128, 128, 16, 8, 8, 4, 0),    // 0
+    MFMA_CFG(256, 256, 32, 128, 128, 4, 0), // 1
+    MFMA_CFG(128, 128, 32, 64, 64, 4, 0),   // 2
+    MFMA_CFG(64, 64, 32, 32, 32, 4, 0),     // 3
+};
+constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+constexpr int kValuDefault = 0;
+constexpr int kMfmaLarge = 1;
+constexpr int kMfmaMedium = 2;
+constexpr int kMfmaSmall = 3;
+
+// Compute units of an MI355X; the choice of tile is a pure function of the
+// sizes so that it is the same on every call and testable without a GPU.
+constexpr long long kComputeUnits = 256;
+
+long long tiles(int M, int N, int bm, int bn) {
+    return (long long)((M + bm - 1) / bm) * (long long)((N + bn - 1) / bn);
+}
+
+int select_variant(int path, int M, int N, int K) {
+    if (M < 0) return -1;
+    if (N < 0) return -2;
+    if (K < 0) return -3;
+    if (path == SGEMM_PATH_VALU) return kValuDefault;
+    if (path != SGEMM_PATH_AUTO && path != SGEMM_PATH_MFMA) return SGEMM_ERR_PATH;
+    // The largest tile that still gives every compute unit a workgroup.
+    if (tiles(M, N, 256, 256) >= kComputeUnits) return kMfmaLarge;
+    if (tiles(M, N, 128, 128) >= kComputeUnits) return kMfmaMedium;
+    return kMfmaSmall;
+}
+
+int check_args(int M, int N, int K, float alpha, const float *A, int lda,
+               const float *B, int ldb, const float *C, int ldc) {
+    if (M < 0) return -1;
+    if (N < 0) return -2;
+    if (K < 0) return -3;
+    const bool reads_ab = alpha != 0.0f && K > 0 && M > 0 && N > 0;
+    if (reads_ab && A == nullptr) return -5;
+    if (lda < (K > 1 ? K : 1)) return -6;
+    if (reads_ab && B == nullptr) return -7;
+    if (ldb < (N > 1 ? N : 1)) return -8;
+    if (M > 0 && N > 0 && C == nullptr) return -10;
+    if (ldc < (N > 1 ? N : 1)) return -11;
+    return SGEMM_OK;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int launch(int variant, int M, int N, int K, float alpha, const float *A,
+           int lda, const float *B, int ldb, float beta, float *C, int ldc,
+           hipStream_t stream) {
+    const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (rc != SGEMM_OK) return rc;
+    if (variant < 0 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
+    if (M == 0 || N == 0) return SGEMM_OK;
+    const bool no_product = alpha == 0.0f || K == 0;
+    if (no_product && beta == 1.0f) return SGEMM_OK;
+
+    const Variant &v = kVariants[variant];
+    const long long grid = tiles(M, N, v.bm, v.bn);
+    if (grid > INT_MAX) return SGEMM_ERR_TOO_LARGE;
+
+    Args a;
+    a.M = M;
+    a.N = N;
+    a.K = no_product ? 0 : K;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+
+    // 128-bit accesses to B and C need 16-byte aligned bases and every row
+    // start a multiple of 4 floats; N % 4 == 0 keeps each 4-wide piece wholly
+    // inside or wholly outside the matrix.  A is read 32 bits at a time.
+    const bool vec4 = (N % 4 == 0) && (ldb % 4 == 0) && (ldc % 4 == 0) &&
+                      aligned16(B) && aligned16(C);
+    KernelFn fn = vec4 ? v.vec4 : v.vec1;
+
+    (void)hipGetLastError();  // drop any stale error so the code below is this launch's
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(v.threads), 0, stream, a);
+    const hipError_t err = hipGetLastError();
+    return err == hipSuccess ? SGEMM_OK : (int)err;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
+          const float *B, int ldb, float beta, float *C, int ldc,
+          hipStream_t stream) {
+    return sgemm_path(SGEMM_PATH_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int sgemm_path(int path, int M, int N, int K, float alpha, const float *A,
+               int lda, const float *B, int ldb, float beta, float *C, int ldc,
+               hipStream_t stream) {
+    const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (rc != SGEMM_OK) return rc;
+    const int v = select_variant(path, M, N, K);
+    if (v < 0) return v;
+    return launch(v, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int sgemm_variant(int variant, int M, int N, int K, float alpha,
+                  const float *A, int lda, const float *B, int ldb, float beta,
+                  float *C, int ldc, hipStream_t stream) {
+    return launch(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int sgemm_variant_count(void) { return kNumVariants; }
+
+const char *sgemm_variant_name(int variant) {
+    if (variant < 0 || variant >= kNumVariants) return nullptr;
+    return kVariants[variant].name;
+}
+
+int sgemm_variant_path(int variant) {
+    if (variant < 0 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
+    return kVariants[variant].path;
+}
+
+int sgemm_variant_tile(int variant, int *bm, int *bn) {
+    if (variant < 0 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
+    if (bm) *bm = kVariants[variant].bm;
+    if (bn) *bn = kVariants[variant].bn;
+    return SGEMM_OK;
+}
+
+int sgemm_select_variant(int path, int M, int N, int K) {
+    return select_variant(path, M, N, K);
+}
+
+const char *sgemm_status_string(int status) {
+    switch (status) {
+        case SGEMM_OK: return "success";
+        case -1: return "invalid argument: M < 0";
+        case -2: return "invalid argument: N < 0";
+        case -3: return "invalid argument: K < 0";
+        case -5: return "invalid argument: A is NULL";
+        case -6: return "invalid argument: lda < max(1, K)";
+        case -7: return "invalid argument: B is NULL";
+        case -8: return "invalid argument: ldb < max(1, N)";
+        case -10: return "invalid argument: C is NULL";
+        case -11: return "invalid argument: ldc < max(1, N)";
+        case SGEMM_ERR_PATH: return "invalid argument: unknown path";
+        case SGEMM_ERR_VARIANT: return "invalid argument: unknown variant";
+        case SGEMM_ERR_TOO_LARGE: return "problem too large: tile grid exceeds one launch";
+        default: break;
+    }
+    if (status > 0) return hipGetErrorString((hipError_t)status);
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+/*
+ * sgemm.h -- C ABI of the MI355X (gfx950) FP32 SGEMM library.
+ *
+ * The operation.  C = alpha * A * B + beta * C on row-major matrices: A is
+ * M x K, B is K x N, C is M x N, alpha and beta are scalars, and alpha scales
+ * the finished dot product once ("如何高效实现矩阵乘？CUDA初学者的角度入门",
+ * section "樸素 GEMM 與前置知識", the naive GEMM with alpha and beta).
+ * Element (r, c) of a matrix with leading dimension ld sits at r*ld + c
+ * ("SGEMM CUDA kernel (Second Half)", Part 8, where the OFFSET(row, col, ld)
+ * macro is used for every global access).  Partial tiles at the right and
+ * bottom edges are handled by zero-filling out-of-range operand elements and
+ * masking out-of-range stores ("3.3 Shared memory ו tiling תרגול", exercise 1,
+ * zero padding of partial tiles).
+ *
+ * Precision.  Every product and every sum is an IEEE float32 operation (FMA
+ * on the VALU path, v_mfma_f32_*_f32 on the matrix path); there is no
+ * reduced-precision input rounding and no multi-pass emulation.  The
+ * summation order differs from a sequential loop, so results match a float64
+ * reference within |C - ref| <= 1e-5 * (|alpha| sum_k |A_ik||B_kj| +
+ * |beta||C_ij|), not bit for bit.  A given variant on given inputs is
+ * deterministic run to run (no atomics, no split-K).
+ *
+ * Pointers.  A, B and C are DEVICE pointers owned by the caller.  The library
+ * allocates no memory, copies nothing and keeps no handles; it holds no state
+ * between calls.  No alignment is required: 16-byte aligned bases with leading
+ * dimensions and N that are multiples of 4 take 128-bit global accesses,
+ * anything else takes 32-bit ones.  C must not overlap A or B (undefined
+ * behaviour).  Dimensions and leading dimensions are int; address arithmetic
+ * is 64-bit.
+ *
+ * Asynchrony.  The kernel is enqueued on `stream` (0 = the null stream) and
+ * the call returns without synchronising.  Faults inside the kernel (for
+ * example a device pointer that does not cover the stated extent) surface at
+ * the next synchronisation, not here.
+ *
+ * Special cases.  M == 0 or N == 0: nothing is launched, returns 0.
+ * (alpha == 0 or K == 0) and beta == 1: nothing is launched, returns 0.
+ * alpha == 0 or K == 0 otherwise: C = beta * C, with A and B not read.
+ * beta == 0: C is not read (NaN or Inf already in C does not propagate).
+ *
+ * Return value.  0 on success.  Negative: an invalid argument, numbered by its
+ * position in sgemm() (-1 M < 0, -2 N < 0, -3 K < 0, -5 A == NULL while
+ * M*K > 0 and alpha != 0, -6 lda < max(1, K), -7 B == NULL while K*N > 0 and
+ * alpha != 0, -8 ldb < max(1, N), -10 C == NULL while M*N > 0, -11
+ * ldc < max(1, N)); -20 unknown path; -21 unknown variant; -22 the tile grid
+ * does not fit one launch.  Argument checks run before any HIP call, so they
+ * need no GPU.  Positive: the hipError_t reported for the launch.  The library
+ * never exits or aborts the process.
+ */
+#ifndef SGEMM_MI355X_H
+#define SGEMM_MI355X_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGEMM_PATH_AUTO 0 /* the library picks the inner product and tile */
+#define SGEMM_PATH_VALU 1 /* FP32 FMA on the vector ALU, register outer product */
+#define SGEMM_PATH_MFMA 2 /* v_mfma_f32_32x32x2_f32 matrix-core inner product */
+
+#define SGEMM_OK 0
+#define SGEMM_ERR_PATH (-20)
+#define SGEMM_ERR_VARIANT (-21)
+#define SGEMM_ERR_TOO_LARGE (-22)
+
+/* C = alpha*A*B + beta*C, automatic choice of inner product and tile. */
+int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
+          const float *B, int ldb, float beta, float *C, int ldc,
+          hipStream_t stream);
+
+/* As sgemm(), restricted to one inner product: SGEMM_PATH_AUTO, _VALU or _MFMA.
+ * The tile is still chosen by shape.  Argument codes are sgemm()'s. */
+int sgemm_path(int path, int M, int N, int K, float alpha, const float *A,
+               int lda, const float *B, int ldb, float beta, float *C, int ldc,
+               hipStream_t stream);
+
+/* As sgemm(), with one compiled kernel variant (inner product + tile shape)
+ * forced by index, 0 <= variant < sgemm_variant_count().  For tests and
+ * benchmarks that must cover or time every variant. */
+int sgemm_variant(int variant, int M, int N, int K, float alpha,
+                  const float *A, int lda, const float *B, int ldb, float beta,
+                  float *C, int ldc, hipStream_t stream);
+
+/* Number of compiled kernel variants. */
+int sgemm_variant_count(void);
+
+/* Static, NUL-terminated name of a variant ("mfma_256x256x32_w128x128" ...),
+ * or NULL for an index out of range. */
+const char *sgemm_variant_name(int variant);
+
+/* SGEMM_PATH_VALU or SGEMM_PATH_MFMA for a variant, SGEMM_ERR_VARIANT if out of range. */
+int sgemm_variant_path(int variant);
+
+/* Block tile (rows, columns of C) of a variant through *bm and *bn; returns 0
+ * or SGEMM_ERR_VARIANT.  Either pointer may be NULL. */
+int sgemm_variant_tile(int variant, int *bm, int *bn);
+
+/* The variant sgemm_path(path, M, N, K, ...) launches for these sizes, or a
+ * negative code (-1..-3, SGEMM_ERR_PATH).  Host logic only, no HIP call. */
+int sgemm_select_variant(int path, int M, int N, int K);
+
+/* Static text for a status code returned by any entry point above. */
+const char *sgemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_MI355X_H */

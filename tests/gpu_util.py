@@ -1,0 +1,85 @@
+"""Helpers for the GPU parity tests: run the HIP library through its C ABI on
+seeded inputs and compare with the float64 oracle under the pass rule
+max |C_gpu - ref| / (|alpha| sum_k |A_ik||B_kj| + |beta||C_ij| + 1e-30) <= 1e-5."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import fp32_gemm_03_amd as g
+import oracle
+
+TOL = 1e-5
+
+
+def say(*args):
+    """Name the case before a GPU step, flushed, so a hard failure still leaves it."""
+    print("[gpu-case]", *args, flush=True)
+    sys.stdout.flush()
+
+
+GUARD = 256  # floats of NaN on each side of every operand buffer
+
+
+def to_gpu(t: torch.Tensor, offset_floats: int = 0) -> tuple:
+    """Copy a CPU tensor to the GPU inside a NaN-filled guard band; with
+    ``offset_floats`` the data starts that many floats later (a deliberately
+    misaligned base).  Returns ``(owner, first_index, base_address)``."""
+    flat = t.contiguous().reshape(-1)
+    first = GUARD + offset_floats
+    owner = torch.full((first + flat.numel() + GUARD,), float("nan"), dtype=torch.float32,
+                       device="cuda")
+    owner[first:first + flat.numel()].copy_(flat)
+    return owner, first, owner.data_ptr() + 4 * first
+
+
+def run(p, variant=None, path=None, offsets=(0, 0, 0), stream=None):
+    """Launch one SGEMM on ``p`` (an ``inputs.Problem``); returns the whole C buffer
+    (M x ldc, float32, numpy) after the call, and checks that nothing outside the
+    operands' extents was written."""
+    oa, _, a = to_gpu(p.A, offsets[0])
+    ob, _, b = to_gpu(p.B, offsets[1])
+    oc, first, c = to_gpu(p.C, offsets[2])
+    args = (p.M, p.N, p.K, p.alpha, a, p.lda, b, p.ldb, p.beta, c, p.ldc)
+    if variant is not None:
+        g.sgemm_variant(variant, *args, stream=stream)
+    elif path is not None:
+        g.sgemm_path(path, *args, stream=stream)
+    else:
+        g.sgemm(*args, stream=stream)
+    torch.cuda.synchronize()
+    n = p.C.numel()
+    host = oc.cpu().numpy()
+    guard = np.concatenate([host[:first], host[first + n:]])
+    assert np.all(np.isnan(guard)), "write outside C's extent"
+    for o in (oa, ob):
+        h = o.cpu().numpy()
+        assert np.isnan(h[:GUARD]).all() and np.isnan(h[-GUARD:]).all(), "write into A or B"
+    return host[first:first + n].reshape(p.C.shape)
+
+
+def oracle_full(p):
+    return oracle.sgemm(p.M, p.N, p.K, p.alpha, p.np("A"), p.lda, p.np("B"), p.ldb,
+                        p.beta, p.np("C"), p.ldc)
+
+
+def ratio_full(p, out, ref_den=None):
+    ref, den = oracle_full(p) if ref_den is None else ref_den
+    return oracle.max_error_ratio(out[:, :p.N], ref, den)
+
+
+def ratio_points(p, out, rows, cols):
+    ref, den = oracle.sgemm_points(p.M, p.N, p.K, p.alpha, p.np("A"), p.lda, p.np("B"),
+                                   p.ldb, p.beta, p.np("C"), p.ldc, rows, cols)
+    return oracle.max_error_ratio(out[rows, cols], ref, den)
+
+
+def pad_untouched(p, out):
+    """Columns N..ldc-1 of C are outside the matrix and must keep their sentinel bits."""
+    if p.ldc == p.N:
+        return True
+    before = p.C.numpy()[:, p.N:]
+    after = out[:, p.N:]
+    return np.array_equal(before.view(np.uint32), after.view(np.uint32))

@@ -1,0 +1,206 @@
+"""GPU parity: the HIP library, called through its C ABI, against the float64
+oracle on seeded inputs.  Pass rule: max |C_gpu - ref| / den <= 1e-5 with
+den = |alpha| sum_k |A_ik||B_kj| + |beta||C_ij| + 1e-30, at every element for
+sizes the oracle finishes in seconds, and at seeded samples (first and last
+rows and columns, seeded rows and columns, random points) for the full sizes.
+Exact cases (closed form, alpha = 0, K = 0) must match bit for bit."""
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import fp32_gemm_03_amd as g
+from fp32_gemm_03_amd import inputs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+TOL = gu.TOL
+
+
+def all_variants():
+    return list(range(g.sgemm_variant_count()))
+
+
+@functools.lru_cache(maxsize=None)
+def cached_problem(name):
+    return inputs.workload_problem(name)
+
+
+@functools.lru_cache(maxsize=None)
+def cached_oracle(name):
+    return gu.oracle_full(cached_problem(name))
+
+
+@pytest.fixture(autouse=True)
+def _gpu_available():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+# ------------------------------------------------------------------ exact cases
+@pytest.mark.parametrize("variant", all_variants())
+def test_closed_form_every_variant(variant):
+    p = cached_problem("square256_closed_form")
+    gu.say("closed form 256^3", g.sgemm_variant_name(variant))
+    out = gu.run(p, variant=variant)
+    assert np.all(out == 512.0), np.unique(out)[:8]
+
+
+@pytest.mark.parametrize("variant", all_variants())
+def test_closed_form_nonsquare_ragged(variant):
+    # every element is exactly 2K for any shape, including partial tiles
+    p = inputs.make_problem(131, 77, 203, dist="ones_twos")
+    gu.say("closed form 131x77x203", g.sgemm_variant_name(variant))
+    out = gu.run(p, variant=variant)
+    assert np.all(out == 2.0 * 203)
+
+
+@pytest.mark.parametrize("variant", all_variants())
+def test_alpha_zero_and_k_zero_give_beta_c(variant):
+    p = inputs.make_problem(70, 45, 33, dist="upm1", seed=5, alpha=0.0, beta=-0.5, c_fill="upm1")
+    gu.say("alpha=0", g.sgemm_variant_name(variant))
+    out = gu.run(p, variant=variant)
+    assert np.array_equal(out, (np.float32(-0.5) * p.C.numpy()))
+    p0 = inputs.make_problem(70, 45, 0, dist="upm1", seed=5, alpha=1.0, beta=2.0, c_fill="upm1")
+    gu.say("K=0", g.sgemm_variant_name(variant))
+    out = gu.run(p0, variant=variant)
+    assert np.array_equal(out, (np.float32(2.0) * p0.C.numpy()))
+    pz = inputs.make_problem(70, 45, 0, dist="upm1", seed=5, beta=0.0, c_fill="nan")
+    gu.say("K=0 beta=0", g.sgemm_variant_name(variant))
+    out = gu.run(pz, variant=variant)
+    assert np.all(out == 0.0)
+
+
+# ------------------------------------------------------------------ workloads, every element
+@pytest.mark.parametrize("name", ["square256_u01", "ragged_1000x1023x999", "square1024_normal"])
+@pytest.mark.parametrize("variant", all_variants())
+def test_workloads_every_variant(name, variant):
+    p = cached_problem(name)
+    gu.say(name, g.sgemm_variant_name(variant))
+    out = gu.run(p, variant=variant)
+    r = gu.ratio_full(p, out, cached_oracle(name))
+    assert r <= TOL, (name, g.sgemm_variant_name(variant), r)
+
+
+@pytest.mark.parametrize("name", ["square256_u01", "ragged_1000x1023x999", "square1024_normal"])
+@pytest.mark.parametrize("path", [g.SGEMM_PATH_AUTO, g.SGEMM_PATH_VALU, g.SGEMM_PATH_MFMA])
+def test_workloads_every_path(name, path):
+    p = cached_problem(name)
+    gu.say(name, "path", path)
+    out = gu.run(p, path=path)
+    assert gu.ratio_full(p, out, cached_oracle(name)) <= TOL
+
+
+# ------------------------------------------------------------------ edges
+EDGE = [1, 2, 3, 4, 5, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257]
+
+
+def edge_shapes():
+    rng = np.random.default_rng(2024)
+    shapes = [(e, e, e) for e in EDGE]
+    for _ in range(40):
+        shapes.append(tuple(int(x) for x in rng.choice(EDGE, 3)))
+    shapes += [(1, 300, 7), (300, 1, 7), (5, 5, 513), (257, 129, 1), (96, 260, 35)]
+    return shapes
+
+
+SCALARS = [(1.0, 0.0), (1.5, -0.5), (-1.0, 1.0), (2.0, 1.5), (0.5, 2.0)]
+
+
+@pytest.mark.parametrize("variant", all_variants())
+def test_edge_sweep(variant):
+    for idx, (M, N, K) in enumerate(edge_shapes()):
+        alpha, beta = SCALARS[idx % len(SCALARS)]
+        p = inputs.make_problem(M, N, K, dist="upm1", seed=idx, alpha=alpha, beta=beta,
+                                c_fill="upm1" if beta != 0 else None)
+        gu.say("edge", M, N, K, alpha, beta, g.sgemm_variant_name(variant))
+        out = gu.run(p, variant=variant)
+        r = gu.ratio_full(p, out)
+        assert r <= TOL, (M, N, K, alpha, beta, g.sgemm_variant_name(variant), r)
+
+
+@pytest.mark.parametrize("variant", all_variants())
+@pytest.mark.parametrize("offsets", [(0, 0, 0), (1, 0, 0), (0, 1, 0), (0, 0, 1), (3, 1, 2)])
+def test_wide_leading_dims_and_misaligned_bases(variant, offsets):
+    # pad columns of A, B, C hold NaN; they must never be read or written
+    for (M, N, K, lda, ldb, ldc) in [(130, 196, 72, 75, 200, 204), (97, 64, 40, 41, 67, 66),
+                                     (64, 128, 64, 68, 132, 128)]:
+        p = inputs.make_problem(M, N, K, dist="upm1", seed=M + N, alpha=1.25, beta=-0.75,
+                                c_fill="upm1", lda=lda, ldb=ldb, ldc=ldc)
+        gu.say("wide-ld", M, N, K, lda, ldb, ldc, offsets, g.sgemm_variant_name(variant))
+        out = gu.run(p, variant=variant, offsets=offsets)
+        assert gu.pad_untouched(p, out)
+        assert gu.ratio_full(p, out) <= TOL
+
+
+@pytest.mark.parametrize("variant", all_variants())
+def test_beta_zero_does_not_read_c(variant):
+    p = inputs.make_problem(150, 260, 70, dist="normal", seed=11, beta=0.0, c_fill="nan")
+    gu.say("beta=0 NaN C", g.sgemm_variant_name(variant))
+    out = gu.run(p, variant=variant)
+    assert np.all(np.isfinite(out))
+    assert gu.ratio_full(p, out) <= TOL
+
+
+# ------------------------------------------------------------------ properties
+@pytest.mark.parametrize("variant", all_variants())
+def test_deterministic(variant):
+    p = cached_problem("ragged_1000x1023x999")
+    gu.say("determinism", g.sgemm_variant_name(variant))
+    a = gu.run(p, variant=variant)
+    b = gu.run(p, variant=variant)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("variant", all_variants())
+def test_zero_padding_invariance(variant):
+    # the ragged problem inside a zero-padded larger one (same K, so the same
+    # K tiles): C[:M, :N] is bit for bit the same
+    p = inputs.make_problem(200, 301, 77, dist="upm1", seed=3, alpha=1.5, beta=-0.5, c_fill="upm1")
+    Mb, Nb = 256, 384
+    big = inputs.make_problem(Mb, Nb, 77, dist="upm1", seed=3)
+    big.A.zero_(); big.B.zero_(); big.C.zero_()
+    big.A[:200] = p.A
+    big.B[:, :301] = p.B
+    big.C[:200, :301] = p.C
+    big.alpha, big.beta = p.alpha, p.beta
+    gu.say("zero-padding invariance", g.sgemm_variant_name(variant))
+    small = gu.run(p, variant=variant)   # N = 301: 32-bit accesses
+    large = gu.run(big, variant=variant)  # N = 384: 128-bit accesses, same arithmetic
+    assert np.array_equal(small.view(np.uint32), large[:200, :301].copy().view(np.uint32))
+
+
+def test_runs_on_a_side_stream():
+    p = cached_problem("square256_u01")
+    s = torch.cuda.Stream()
+    gu.say("side stream")
+    with torch.cuda.stream(s):
+        out = gu.run(p, stream=s)
+    assert gu.ratio_full(p, out, cached_oracle("square256_u01")) <= TOL
+
+
+# ------------------------------------------------------------------ full sizes, sampled
+FULL = ["square2048_normal", "square4096_upm1", "square8192_normal", "lowk_16384x16384x128",
+        "square16384_normal"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_auto_path(name):
+    p = inputs.workload_problem(name)
+    gu.say("full size", name, "auto variant",
+           g.sgemm_variant_name(g.sgemm_select_variant(0, p.M, p.N, p.K)))
+    out = gu.run(p)
+    rows, cols = inputs.sample_points(p.M, p.N, n_random=4096, seed=17)
+    r = gu.ratio_points(p, out, rows, cols)
+    assert r <= TOL, (name, r)
+
+
+@pytest.mark.parametrize("name", ["square4096_upm1", "square8192_normal"])
+def test_full_size_sampled_valu_path(name):
+    p = inputs.workload_problem(name)
+    gu.say("full size", name, "VALU")
+    out = gu.run(p, path=g.SGEMM_PATH_VALU)
+    rows, cols = inputs.sample_points(p.M, p.N, n_random=2048, seed=19)
+    assert gu.ratio_points(p, out, rows, cols) <= TOL
