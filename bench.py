@@ -31,7 +31,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_FP32_TFLOPS = 157.3  # 256 CU x 256 FLOP/clk x 2.4 GHz (FP32 MFMA; packed VALU alike)
+PEAK_FP32_TFLOPS = 157.3  # 256 CU x 256 FLOP/clk x 2.4 GHz (FP32 MFMA)
+# The VALU path is built without packed FP32 instructions; gfx950 still issues a
+# wave-wide non-packed v_fma_f32 at the full FP32 vector rate (a probe loop of
+# independent v_fma_f32 sustains ~124 TFLOP/s, above half of 157.3), so the VALU
+# path is held to the same 157.3 TFLOP/s vector peak.
+PEAK_VALU_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "square8192_normal"
 SECONDARY = "square4096_upm1"
@@ -46,7 +51,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(variant_name: str):
+def read_traffic(workload: str, variant_name: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, or None
     when there is none for this kernel or it predates the current source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -57,13 +62,14 @@ def read_traffic(variant_name: str):
             data = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = data.get(WORKLOAD, {}).get(variant_name)
+    entry = data.get(workload, {}).get(variant_name)
     if not entry or entry.get("source_hash") != kernel_source_hash():
         return None
     return entry.get("hbm_bytes_per_launch")
 
 
-def time_gpu(p, steps, warmup, path):
+def time_gpu(p, steps, warmup, path, variant=None):
+    """Launch on a dedicated stream; HIP events on that stream around every launch."""
     import torch
     import fp32_gemm_03_amd as g
 
@@ -72,15 +78,22 @@ def time_gpu(p, steps, warmup, path):
     c = p.C.cuda()
     stream = torch.cuda.Stream()
     args = (p.M, p.N, p.K, p.alpha, a, p.lda, b, p.ldb, p.beta, c, p.ldc)
+
+    def step():
+        if variant is None:
+            g.sgemm_path(path, *args, stream=stream)
+        else:
+            g.sgemm_variant(variant, *args, stream=stream)
+
     torch.cuda.synchronize()
     for _ in range(warmup):
-        g.sgemm_path(path, *args, stream=stream)
+        step()
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(steps):
-        g.sgemm_path(path, *args, stream=stream)
+        step()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -119,9 +132,17 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--path", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--variant", type=int, default=None,
+                    help="force one compiled kernel variant by index instead of the path's choice")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--shape", metavar="MxNxK",
+                    help="time this square-workload recipe (N(0,1), seed 3) at another shape "
+                         "instead of --workload (used for counter differencing)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, metavar="BYTES", default=0,
+                    help="only run 5 plain device-to-device copies of BYTES bytes (the "
+                         "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -137,22 +158,43 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 4 * n, "copies": 5}), flush=True)
+        return
     g.load_library()
     path = {"auto": g.SGEMM_PATH_AUTO, "valu": g.SGEMM_PATH_VALU, "mfma": g.SGEMM_PATH_MFMA}[args.path]
 
-    w = inputs.WORKLOADS[args.workload]
-    p = inputs.workload_problem(args.workload)
-    variant = g.sgemm_select_variant(path, p.M, p.N, p.K)
+    if args.shape:
+        M, N, K = (int(x) for x in args.shape.lower().split("x"))
+        args.workload = f"square_recipe_{M}x{N}x{K}"
+        w = inputs.Workload(args.workload, M, N, K, "normal", 3)
+        p = inputs.make_problem(M, N, K, dist="normal", seed=3, name=args.workload)
+    else:
+        w = inputs.WORKLOADS[args.workload]
+        p = inputs.workload_problem(args.workload)
+    variant = g.sgemm_select_variant(path, p.M, p.N, p.K) if args.variant is None else args.variant
     vname = g.sgemm_variant_name(variant)
+    if vname is None:
+        print(f"bench.py: no variant {variant}", file=sys.stderr)
+        sys.exit(2)
     print(f"bench: {args.workload} variant {vname}, {args.warmup} warm-up + {args.steps} timed",
           file=sys.stderr, flush=True)
-    total_ms, per_launch, wall = time_gpu(p, args.steps, args.warmup, path)
+    total_ms, per_launch, wall = time_gpu(p, args.steps, args.warmup, path, args.variant)
     ms_per_step = total_ms / args.steps
     value = w.flops / (ms_per_step / 1e3) / 1e12
     avg_kernel_ms = sum(per_launch) / len(per_launch)
     achieved = w.flops / (avg_kernel_ms / 1e3) / 1e12
 
-    traffic = read_traffic(vname)
+    traffic = read_traffic(args.workload, vname)
+    is_mfma = g.sgemm_variant_path(variant) == g.SGEMM_PATH_MFMA
+    peak = PEAK_FP32_TFLOPS if is_mfma else PEAK_VALU_FP32_TFLOPS
     out = {
         "metric": "FP32 SGEMM TFLOP/s (2MNK/t)",
         "value": round(value, 3),
@@ -170,9 +212,9 @@ def main():
                    "alpha": p.alpha, "beta": p.beta, "dist": w.dist, "seed": w.seed,
                    "variant": vname, "path": args.path},
         "pct_of_fp32_peak": round(100.0 * value / PEAK_FP32_TFLOPS, 2),
-        "roofline": {"bound": "mfma" if g.sgemm_variant_path(variant) == g.SGEMM_PATH_MFMA else "alu",
-                     "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4),
+        "roofline": {"bound": "mfma" if is_mfma else "alu",
+                     "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,
                      "kernel_avg_ms": round(avg_kernel_ms, 4),
                      "kernel_min_ms": round(min(per_launch), 4),
@@ -183,8 +225,8 @@ def main():
         p2 = inputs.workload_problem(SECONDARY)
         w2 = inputs.WORKLOADS[SECONDARY]
         steps2 = max(args.steps, 20)
-        t2, per2, _ = time_gpu(p2, steps2, args.warmup, path)
-        v2 = g.sgemm_select_variant(path, p2.M, p2.N, p2.K)
+        t2, per2, _ = time_gpu(p2, steps2, args.warmup, path, args.variant)
+        v2 = g.sgemm_select_variant(path, p2.M, p2.N, p2.K) if args.variant is None else args.variant
         out["secondary"] = {"workload": SECONDARY, "variant": g.sgemm_variant_name(v2),
                             "value": round(w2.flops / (t2 / steps2 / 1e3) / 1e12, 3),
                             "unit": "TFLOP/s", "ms_per_step": round(t2 / steps2, 4)}
