@@ -20,7 +20,7 @@ typedef void (*KernelFn)(Args);
 struct Variant {
     const char *name;
     int path;           // SGEMM_PATH_VALU or SGEMM_PATH_MFMA
-    int bm, bn;         // block tile
+    int bm, bn, bk;     // block tile
     int threads;        // workgroup size
     KernelFn vec4;      // B, C and their leading dimensions 16-byte friendly
     KernelFn vec1;      // anything else
@@ -28,22 +28,26 @@ struct Variant {
 
 // VALU: 128 x 128 x 16 block, 4 waves of 64 x 64, 8 x 8 per lane.
 #define VALU_CFG(BM, BN, BK, TM, TN, PA, PB)                                            \
-    {"valu_" #BM "x" #BN "x" #BK "_t" #TM "x" #TN, SGEMM_PATH_VALU, BM, BN,               \
+    {"valu_" #BM "x" #BN "x" #BK "_t" #TM "x" #TN, SGEMM_PATH_VALU, BM, BN, BK,           \
      (BM / (8 * TM)) * (BN / (8 * TN)) * 64,                                             \
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 4>,                                  \
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1>}
 
-#define MFMA_CFG(BM, BN, BK, WM, WN, PA, PB)                                            \
-    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN, SGEMM_PATH_MFMA, BM, BN,               \
+#define MFMA_CFG(BM, BN, BK, WM, WN, PA, PB, WPE)                                       \
+    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN, SGEMM_PATH_MFMA, BM, BN, BK,           \
      (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4>,                                  \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1>}
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4, WPE>,                             \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE>}
 
 const Variant kVariants[] = {
-    VALU_CFG(128, 128, 16, 8, 8, 4, 0),    // 0
-    MFMA_CFG(256, 256, 32, 128, 128, 4, 0), // 1
-    MFMA_CFG(128, 128, 32, 64, 64, 4, 0),   // 2
-    MFMA_CFG(64, 64, 32, 32, 32, 4, 0),     // 3
+    VALU_CFG(128, 128, 16, 8, 8, 4, 0),        // 0
+    MFMA_CFG(256, 256, 32, 128, 128, 4, 0, 1), // 1: 4 waves, 1 per SIMD, 512 registers
+    MFMA_CFG(128, 128, 32, 64, 64, 4, 0, 2),   // 2
+    MFMA_CFG(64, 64, 32, 32, 32, 4, 0, 2),     // 3
+    MFMA_CFG(256, 256, 32, 128, 64, 4, 0, 2),  // 4: 8 waves, 2 per SIMD
+    MFMA_CFG(256, 128, 16, 128, 64, 4, 0, 2),  // 5: 4 waves, 2 workgroups per CU
+    MFMA_CFG(256, 256, 16, 128, 128, 4, 0, 1), // 6
+    MFMA_CFG(128, 256, 16, 64, 128, 4, 0, 2),  // 7: 4 waves, 2 workgroups per CU
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -115,6 +119,9 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A,
     a.lda = lda;
     a.ldb = ldb;
     a.ldc = ldc;
+    // The fast path forms byte offsets inside one block tile in 32 bits.
+    const long long lim = 1LL << 31;
+    a.fast = (long long)(v.bm + 4) * lda * 4 < lim && (long long)(v.bk + 4) * ldb * 4 < lim;
 
     // 128-bit accesses to B and C need 16-byte aligned bases and every row
     // start a multiple of 4 floats; N % 4 == 0 keeps each 4-wide piece wholly

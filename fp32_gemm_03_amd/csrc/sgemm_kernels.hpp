@@ -53,6 +53,9 @@ struct Args {
     const float *B;
     float *C;
     int64_t lda, ldb, ldc;
+    // Nonzero when every byte offset the fast path forms inside one block
+    // tile fits in 31 bits (set by the host per variant).
+    int fast;
 };
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -68,11 +71,21 @@ __device__ __forceinline__ float vget(const float4 &v, int i) {
     return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
+template <class T>
+__device__ __forceinline__ T load_at(const char *base, uint32_t byte_off) {
+    return *reinterpret_cast<const T *>(base + byte_off);
+}
+
 // ---------------------------------------------------------------------------
 // A tile: BM x BK block of A -> As[BK][BM + PADA] (transposed).
 // Thread tid covers column tid % BK of rows r0 + {0..3} + p * ROWS_PER_PASS,
 // r0 = 4 * (tid / BK): a load instruction reads NT/BK row segments of BK
-// consecutive floats.
+// consecutive floats, and each thread writes one 128-bit vector per 4 rows.
+//
+// load_fast: the block lies inside M and the K tile is full, so nothing is
+// checked; the address is a uniform (scalar) tile base plus a 32-bit
+// per-thread offset.  load_checked: every element is checked against M and K
+// and loads 0.0 outside.
 // ---------------------------------------------------------------------------
 template <int BM, int BK, int NT, int PADA>
 struct ATile {
@@ -84,25 +97,36 @@ struct ATile {
     static constexpr int SA = BM + PADA;
 
     float4 reg[PER];
-    const float *base;  // A + r0*lda + c
-    int64_t pass_step;  // ROWS_PER_PASS * lda
-    int rows_left;      // M - r0
-    int col;            // c
+    int col;           // column inside the tile
+    int r0;            // first row inside the block
+    uint32_t off[4];   // fast path: ((r0 + c) * lda + col) * 4
 
-    __device__ __forceinline__ void init(const Args &a, int bm, int tid) {
+    __device__ __forceinline__ void init(const Args &a, int tid) {
         col = tid % BK;
-        const int r0 = bm + 4 * (tid / BK);
-        rows_left = a.M - r0;
-        base = a.A + (int64_t)r0 * a.lda + col;
-        pass_step = (int64_t)ROWS_PER_PASS * a.lda;
+        r0 = 4 * (tid / BK);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) off[c] = (uint32_t)(((int64_t)(r0 + c) * a.lda + col) * 4);
     }
 
-    __device__ __forceinline__ void load(const Args &a, int k0) {
+    // tile: byte address of A[bm][k0]; pass: ROWS_PER_PASS * lda * 4
+    __device__ __forceinline__ void load_fast(const char *tile, int64_t pass) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const char *sb = tile + p * pass;
+            reg[p].x = load_at<float>(sb, off[0]);
+            reg[p].y = load_at<float>(sb, off[1]);
+            reg[p].z = load_at<float>(sb, off[2]);
+            reg[p].w = load_at<float>(sb, off[3]);
+        }
+    }
+
+    __device__ __forceinline__ void load_checked(const Args &a, int bm, int k0) {
         const bool kin = (k0 + col) < a.K;
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const float *q = base + p * pass_step + k0;
-            const int rl = rows_left - p * ROWS_PER_PASS;
+            const int row = bm + r0 + p * ROWS_PER_PASS;
+            const float *q = a.A + (int64_t)row * a.lda + k0 + col;
+            const int rl = a.M - row;
             reg[p].x = (kin && rl > 0) ? q[0] : 0.0f;
             reg[p].y = (kin && rl > 1) ? q[a.lda] : 0.0f;
             reg[p].z = (kin && rl > 2) ? q[2 * a.lda] : 0.0f;
@@ -134,11 +158,11 @@ struct BTile {
     typedef typename vec_t<VEC>::type V;
 
     V reg[PER];
-    const float *base;  // B + k_first*ldb + n_first
-    int k_first;        // tile row of piece 0
-    int n_first;        // absolute column of piece 0
+    int k_first;   // tile row of piece 0
+    int n_first;   // column of piece 0 inside the tile
+    uint32_t off;  // fast path: (k_first * ldb + n_first) * 4
 
-    // piece p of thread tid: tile row k_first + dk(p), column n_first + dn(p)
+    // piece p of a thread: tile row k_first + dk(p), tile column n_first + dn(p)
     static __device__ __forceinline__ constexpr int dk(int p) {
         return NT % PER_ROW == 0 ? p * (NT / PER_ROW) : (p * NT) / PER_ROW;
     }
@@ -146,19 +170,27 @@ struct BTile {
         return NT % PER_ROW == 0 ? 0 : ((p * NT) % PER_ROW) * VEC;
     }
 
-    __device__ __forceinline__ void init(const Args &a, int bn, int tid) {
+    __device__ __forceinline__ void init(const Args &a, int tid) {
         k_first = tid / PER_ROW;
-        n_first = bn + (tid % PER_ROW) * VEC;
-        base = a.B + (int64_t)k_first * a.ldb + n_first;
+        n_first = (tid % PER_ROW) * VEC;
+        off = (uint32_t)(((int64_t)k_first * a.ldb + n_first) * 4);
     }
 
-    __device__ __forceinline__ void load(const Args &a, int k0) {
+    // tile: byte address of B[k0][bn]; ldb_bytes: ldb * 4
+    __device__ __forceinline__ void load_fast(const char *tile, int64_t ldb_bytes) {
+#pragma unroll
+        for (int p = 0; p < PER; ++p)
+            reg[p] = load_at<V>(tile + dk(p) * ldb_bytes + dn(p) * 4, off);
+    }
+
+    __device__ __forceinline__ void load_checked(const Args &a, int bn, int k0) {
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
+            const int n = bn + n_first + dn(p);
+            const int k = k0 + k_first + dk(p);
             // VEC == 4 only when N % 4 == 0: a piece is all in or all out
-            const bool in = (n_first + dn(p)) < a.N && (k0 + k_first + dk(p)) < a.K;
-            if (in)
-                reg[p] = *reinterpret_cast<const V *>(base + (int64_t)(k0 + dk(p)) * a.ldb + dn(p));
+            if (n < a.N && k < a.K)
+                reg[p] = *reinterpret_cast<const V *>(a.B + (int64_t)k * a.ldb + n);
             else
                 reg[p] = V{};
         }
@@ -172,15 +204,33 @@ struct BTile {
     }
 };
 
+// Loads of K tile t into the staging registers: the fast path for a block
+// inside M and N with a full K tile, the checked path otherwise.
+template <class TA, class TB, int BK>
+__device__ __forceinline__ void load_tile(const Args &a, TA &ta, TB &tb, bool interior, int bm,
+                                          int bn, int t) {
+    const int k0 = t * BK;
+    if (interior && k0 + BK <= a.K) {
+        const char *at = reinterpret_cast<const char *>(a.A + (int64_t)bm * a.lda + k0);
+        const char *bt = reinterpret_cast<const char *>(a.B + (int64_t)k0 * a.ldb + bn);
+        ta.load_fast(at, (int64_t)TA::ROWS_PER_PASS * a.lda * 4);
+        tb.load_fast(bt, a.ldb * 4);
+    } else {
+        ta.load_checked(a, bm, k0);
+        tb.load_checked(a, bn, k0);
+    }
+}
+
 // Epilogue store of W consecutive columns: C = alpha*acc + beta*C (C read only
-// when beta != 0), masked to the matrix.  VEC == 4 means N, ldc and C are
-// 16-byte friendly, so a W-wide group at a multiple of W is all in or all out.
-template <int W, int VEC>
+// when beta != 0).  CHECK masks rows and columns to the matrix.  VEC == 4
+// means N, ldc and C are 16-byte friendly, so a W-wide group at a multiple of
+// W is all in or all out and goes out as one vector store.
+template <int W, int VEC, bool CHECK>
 __device__ __forceinline__ void store_c(const Args &a, int row, int col, const float (&v)[W]) {
-    if (row >= a.M) return;
+    if (CHECK && row >= a.M) return;
     float *c = a.C + (int64_t)row * a.ldc + col;
     if (VEC == 4 && W > 1) {
-        if (col >= a.N) return;
+        if (CHECK && col >= a.N) return;
         typedef typename vec_t<W>::type V;
         V out;
         float *o = reinterpret_cast<float *>(&out);
@@ -196,7 +246,7 @@ __device__ __forceinline__ void store_c(const Args &a, int row, int col, const f
     } else {
 #pragma unroll
         for (int i = 0; i < W; ++i) {
-            if (col + i < a.N) {
+            if (!CHECK || col + i < a.N) {
                 const float r = a.beta != 0.0f ? fmaf(a.alpha, v[i], a.beta * c[i]) : a.alpha * v[i];
                 c[i] = r;
             }
@@ -211,6 +261,22 @@ __device__ __forceinline__ void store_c(const Args &a, int row, int col, const f
 //      cols  wn + 4*lx + {0..3} + 32*s  (s < TN/4),
 // so every LDS read is one 128-bit load that 8 lanes share (broadcast).
 // ---------------------------------------------------------------------------
+template <int BM, int BN, int BK, int TM, int TN, int PADA, int PADB, int VEC, bool CHECK>
+__device__ __forceinline__ void valu_epilogue(const Args &a, int bm, int bn, int wm, int wn,
+                                              int ly, int lx, const float (&acc)[TM][TN]) {
+    // 8 lanes with the same ly cover 32 consecutive columns (128 bytes) of a row
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int row = bm + wm + 4 * ly + (i & 3) + 32 * (i >> 2);
+#pragma unroll
+        for (int s = 0; s < TN / 4; ++s) {
+            const int col = bn + wn + 4 * lx + 32 * s;
+            float v[4] = {acc[i][4 * s], acc[i][4 * s + 1], acc[i][4 * s + 2], acc[i][4 * s + 3]};
+            store_c<4, VEC, CHECK>(a, row, col, v);
+        }
+    }
+}
+
 template <int BM, int BN, int BK, int TM, int TN, int PADA, int PADB, int VEC>
 __global__ void __launch_bounds__((BM / (8 * TM)) * (BN / (8 * TN)) * 64)
 __attribute__((amdgpu_waves_per_eu(2))) sgemm_valu(Args a) {
@@ -219,7 +285,8 @@ __attribute__((amdgpu_waves_per_eu(2))) sgemm_valu(Args a) {
     constexpr int NT = (BM / WM) * WAVES_N * 64;
     static_assert(TM % 4 == 0 && TN % 4 == 0, "micro-tile sides must be multiples of 4");
     constexpr int SA = BM + PADA, SB = BN + PADB;
-    __shared__ __attribute__((aligned(16))) float smem[2 * BK * (SA + SB)];
+    constexpr int STAGE = BK * (SA + SB);
+    __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -228,11 +295,12 @@ __attribute__((amdgpu_waves_per_eu(2))) sgemm_valu(Args a) {
     const int bn = (int)(blockIdx.x % nbn) * BN;
     const int wm = (wave / WAVES_N) * WM, wn = (wave % WAVES_N) * WN;
     const int ly = lane >> 3, lx = lane & 7;
+    const bool interior = a.fast && bm + BM <= a.M && bn + BN <= a.N;
 
     ATile<BM, BK, NT, PADA> ta;
     BTile<BN, BK, NT, PADB, VEC> tb;
-    ta.init(a, bm, tid);
-    tb.init(a, bn, tid);
+    ta.init(a, tid);
+    tb.init(a, tid);
 
     float acc[TM][TN];
 #pragma unroll
@@ -242,20 +310,16 @@ __attribute__((amdgpu_waves_per_eu(2))) sgemm_valu(Args a) {
 
     const int KT = (a.K + BK - 1) / BK;
     if (KT > 0) {
-        ta.load(a, 0);
-        tb.load(a, 0);
+        load_tile<decltype(ta), decltype(tb), BK>(a, ta, tb, interior, bm, bn, 0);
         ta.store(smem, tid);
         tb.store(smem + BK * SA, tid);
     }
     __syncthreads();
 
     for (int t = 0; t < KT; ++t) {
-        float *As = smem + (t & 1) * BK * (SA + SB);
-        float *Bs = As + BK * SA;
-        if (t + 1 < KT) {
-            ta.load(a, (t + 1) * BK);
-            tb.load(a, (t + 1) * BK);
-        }
+        const float *As = smem + (t & 1) * STAGE;
+        const float *Bs = As + BK * SA;
+        if (t + 1 < KT) load_tile<decltype(ta), decltype(tb), BK>(a, ta, tb, interior, bm, bn, t + 1);
         const float *ap = As + wm + 4 * ly;
         const float *bp = Bs + wn + 4 * lx;
         // Partial unrolling bounds how many k-steps of fragments the compiler
@@ -277,29 +341,22 @@ __attribute__((amdgpu_waves_per_eu(2))) sgemm_valu(Args a) {
                 for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(ra[i], rb[j], acc[i][j]);
         }
         if (t + 1 < KT) {
-            float *An = smem + ((t + 1) & 1) * BK * (SA + SB);
+            float *An = smem + ((t + 1) & 1) * STAGE;
             ta.store(An, tid);
             tb.store(An + BK * SA, tid);
         }
         __syncthreads();
     }
 
-    // Epilogue: each lane writes rows of 4 consecutive columns; 8 lanes with the
-    // same ly cover 32 consecutive columns (128 bytes) of one row.
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int row = bm + wm + 4 * ly + (i & 3) + 32 * (i >> 2);
-#pragma unroll
-        for (int s = 0; s < TN / 4; ++s) {
-            const int col = bn + wn + 4 * lx + 32 * s;
-            float v[4] = {acc[i][4 * s], acc[i][4 * s + 1], acc[i][4 * s + 2], acc[i][4 * s + 3]};
-            store_c<4, VEC>(a, row, col, v);
-        }
-    }
+    if (bm + BM <= a.M && bn + BN <= a.N)
+        valu_epilogue<BM, BN, BK, TM, TN, PADA, PADB, VEC, false>(a, bm, bn, wm, wn, ly, lx, acc);
+    else
+        valu_epilogue<BM, BN, BK, TM, TN, PADA, PADB, VEC, true>(a, bm, bn, wm, wn, ly, lx, acc);
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel.  Block tile BM x BN, waves of WM x WN, NT = (BM/WM)*(BN/WN)*64.
+// MFMA kernel.  Block tile BM x BN, waves of WM x WN, NT = (BM/WM)*(BN/WN)*64,
+// at least WPE waves per SIMD (1 lets a wave use all 512 registers).
 // v_mfma_f32_32x32x2_f32 takes from lane l the A element (row l%32, k l/32)
 // and the B element (k l/32, col l%32), and leaves the 32 x 32 result with
 // lane l holding column l%32, rows 8*(r/4) + 4*(l/32) + r%4 in accumulator
@@ -312,20 +369,44 @@ __attribute__((amdgpu_waves_per_eu(2))) sgemm_valu(Args a) {
 // epilogue the NI accumulators of one register index are NI consecutive
 // columns, so each lane stores NI-wide vectors and 32 lanes cover 32*NI
 // consecutive columns of a row.
+//
+// The fragments of k-step j+1 are read from LDS while the MFMAs of step j
+// issue, so the LDS latency hides behind matrix work.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC>
+template <int BM, int BN, int WM, int WN, int VEC, bool CHECK>
+__device__ __forceinline__ void mfma_epilogue(const Args &a, int bm, int bn, int wm, int wn,
+                                              int li, int lh,
+                                              const floatx16 (&acc)[WM / 32][WN / 32]) {
+    constexpr int MI = WM / 32, NI = WN / 32;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int ib = 8 * (r >> 2) + 4 * lh + (r & 3);
+            const int row = bm + wm + MI * ib + i;
+            const int col = bn + wn + NI * li;
+            float v[NI];
+#pragma unroll
+            for (int j = 0; j < NI; ++j) v[j] = acc[i][j][r];
+            store_c<NI, VEC, CHECK>(a, row, col, v);
+        }
+    }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC, int WPE>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-sgemm_mfma(Args a) {
+__attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
     constexpr int WAVES_N = BN / WN;
     constexpr int NT = (BM / WM) * WAVES_N * 64;
     constexpr int SA = BM + PADA, SB = BN + PADB;
+    constexpr int STAGE = BK * (SA + SB);
     static_assert(BK % 2 == 0, "BK must be even (K = 2 per instruction)");
     static_assert(MI == 1 || MI == 2 || MI == 4, "MI in {1, 2, 4}");
     static_assert(NI == 1 || NI == 2 || NI == 4, "NI in {1, 2, 4}");
     typedef typename vec_t<MI>::type VA;
     typedef typename vec_t<NI>::type VB;
-    __shared__ __attribute__((aligned(16))) float smem[2 * BK * (SA + SB)];
+    __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -334,11 +415,12 @@ sgemm_mfma(Args a) {
     const int bn = (int)(blockIdx.x % nbn) * BN;
     const int wm = (wave / WAVES_N) * WM, wn = (wave % WAVES_N) * WN;
     const int li = lane & 31, lh = lane >> 5;
+    const bool interior = a.fast && bm + BM <= a.M && bn + BN <= a.N;
 
     ATile<BM, BK, NT, PADA> ta;
     BTile<BN, BK, NT, PADB, VEC> tb;
-    ta.init(a, bm, tid);
-    tb.init(a, bn, tid);
+    ta.init(a, tid);
+    tb.init(a, tid);
 
     floatx16 acc[MI][NI];
 #pragma unroll
@@ -350,54 +432,48 @@ sgemm_mfma(Args a) {
 
     const int KT = (a.K + BK - 1) / BK;
     if (KT > 0) {
-        ta.load(a, 0);
-        tb.load(a, 0);
+        load_tile<decltype(ta), decltype(tb), BK>(a, ta, tb, interior, bm, bn, 0);
         ta.store(smem, tid);
         tb.store(smem + BK * SA, tid);
     }
     __syncthreads();
 
     for (int t = 0; t < KT; ++t) {
-        float *As = smem + (t & 1) * BK * (SA + SB);
-        float *Bs = As + BK * SA;
-        if (t + 1 < KT) {
-            ta.load(a, (t + 1) * BK);
-            tb.load(a, (t + 1) * BK);
-        }
+        const float *As = smem + (t & 1) * STAGE;
+        const float *Bs = As + BK * SA;
+        if (t + 1 < KT) load_tile<decltype(ta), decltype(tb), BK>(a, ta, tb, interior, bm, bn, t + 1);
         const float *ap = As + lh * SA + wm + MI * li;
         const float *bp = Bs + lh * SB + wn + NI * li;
+        VA av[2];
+        VB bv[2];
+        av[0] = *reinterpret_cast<const VA *>(ap);
+        bv[0] = *reinterpret_cast<const VB *>(bp);
 #pragma unroll
         for (int k = 0; k < BK; k += 2) {
-            const VA av = *reinterpret_cast<const VA *>(ap + k * SA);
-            const VB bv = *reinterpret_cast<const VB *>(bp + k * SB);
+            const int cur = (k >> 1) & 1;
+            if (k + 2 < BK) {
+                av[cur ^ 1] = *reinterpret_cast<const VA *>(ap + (k + 2) * SA);
+                bv[cur ^ 1] = *reinterpret_cast<const VB *>(bp + (k + 2) * SB);
+            }
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(vget(av, i), vget(bv, j),
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(vget(av[cur], i), vget(bv[cur], j),
                                                                      acc[i][j], 0, 0, 0);
         }
         if (t + 1 < KT) {
-            float *An = smem + ((t + 1) & 1) * BK * (SA + SB);
+            float *An = smem + ((t + 1) & 1) * STAGE;
             ta.store(An, tid);
             tb.store(An + BK * SA, tid);
         }
         __syncthreads();
     }
 
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int ib = 8 * (r >> 2) + 4 * lh + (r & 3);
-            const int row = bm + wm + MI * ib + i;
-            const int col = bn + wn + NI * li;
-            float v[NI];
-#pragma unroll
-            for (int j = 0; j < NI; ++j) v[j] = acc[i][j][r];
-            store_c<NI, VEC>(a, row, col, v);
-        }
-    }
+    if (bm + BM <= a.M && bn + BN <= a.N)
+        mfma_epilogue<BM, BN, WM, WN, VEC, false>(a, bm, bn, wm, wn, li, lh, acc);
+    else
+        mfma_epilogue<BM, BN, WM, WN, VEC, true>(a, bm, bn, wm, wn, li, lh, acc);
 }
 
 }  // namespace sgk
