@@ -27,11 +27,11 @@ struct Variant {
 };
 
 // VALU: 128 x 128 x 16 block, 4 waves of 64 x 64, 8 x 8 per lane.
-#define VALU_CFG(BM, BN, BK, TM, TN, PA, PB)                                            \
+#define VALU_CFG(BM, BN, BK, TM, TN, PA, PB, WPE)                                       \
     {"valu_" #BM "x" #BN "x" #BK "_t" #TM "x" #TN, SGEMM_PATH_VALU, BM, BN, BK,           \
      (BM / (8 * TM)) * (BN / (8 * TN)) * 64,                                             \
-     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 4>,                                  \
-     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1>}
+     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 4, WPE>,                             \
+     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE>}
 
 #define MFMA_CFG(BM, BN, BK, WM, WN, PA, PB, WPE)                                       \
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN, SGEMM_PATH_MFMA, BM, BN, BK,           \
@@ -40,7 +40,7 @@ struct Variant {
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE>}
 
 const Variant kVariants[] = {
-    VALU_CFG(128, 128, 16, 8, 8, 4, 0),        // 0
+    VALU_CFG(128, 128, 16, 8, 8, 4, 0, 4),     // 0
     MFMA_CFG(256, 256, 32, 128, 128, 4, 0, 1), // 1: 4 waves, 1 per SIMD, 512 registers
     MFMA_CFG(128, 128, 32, 64, 64, 4, 0, 2),   // 2
     MFMA_CFG(64, 64, 32, 32, 32, 4, 0, 2),     // 3
@@ -48,11 +48,14 @@ const Variant kVariants[] = {
     MFMA_CFG(256, 128, 16, 128, 64, 4, 0, 2),  // 5: 4 waves, 2 workgroups per CU
     MFMA_CFG(256, 256, 16, 128, 128, 4, 0, 1), // 6
     MFMA_CFG(128, 256, 16, 64, 128, 4, 0, 2),  // 7: 4 waves, 2 workgroups per CU
+    VALU_CFG(128, 256, 16, 8, 16, 4, 0, 2),    // 8: 8 x 16 per lane
+    VALU_CFG(256, 128, 16, 16, 8, 4, 0, 2),    // 9: 16 x 8 per lane
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 constexpr int kValuDefault = 0;
-constexpr int kMfmaLarge = 1;
+constexpr int kMfma256x128 = 5;
+constexpr int kMfma128x256 = 7;
 constexpr int kMfmaMedium = 2;
 constexpr int kMfmaSmall = 3;
 
@@ -64,14 +67,19 @@ long long tiles(int M, int N, int bm, int bn) {
     return (long long)((M + bm - 1) / bm) * (long long)((N + bn - 1) / bn);
 }
 
+// Measured on MI355X (8192^3, 4096^3, 16384^3, 2048^3, 1024^3, 16384^2 x 128,
+// 1000 x 1023 x 999, 256^3): the 256 x 128 and 128 x 256 blocks with two
+// workgroups per CU are fastest once there are at least two blocks per CU;
+// with small K the epilogue (C read and write) dominates and the 128 x 256
+// block, whose lanes store 4 consecutive columns, is the faster of the two.
+// Below that, the largest block that still gives every CU a workgroup wins.
 int select_variant(int path, int M, int N, int K) {
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
     if (path == SGEMM_PATH_VALU) return kValuDefault;
     if (path != SGEMM_PATH_AUTO && path != SGEMM_PATH_MFMA) return SGEMM_ERR_PATH;
-    // The largest tile that still gives every compute unit a workgroup.
-    if (tiles(M, N, 256, 256) >= kComputeUnits) return kMfmaLarge;
+    if (tiles(M, N, 256, 128) >= 2 * kComputeUnits) return K < 2048 ? kMfma128x256 : kMfma256x128;
     if (tiles(M, N, 128, 128) >= kComputeUnits) return kMfmaMedium;
     return kMfmaSmall;
 }

@@ -277,9 +277,9 @@ __device__ __forceinline__ void valu_epilogue(const Args &a, int bm, int bn, int
     }
 }
 
-template <int BM, int BN, int BK, int TM, int TN, int PADA, int PADB, int VEC>
+template <int BM, int BN, int BK, int TM, int TN, int PADA, int PADB, int VEC, int WPE>
 __global__ void __launch_bounds__((BM / (8 * TM)) * (BN / (8 * TN)) * 64)
-__attribute__((amdgpu_waves_per_eu(2))) sgemm_valu(Args a) {
+__attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
     constexpr int WM = 8 * TM, WN = 8 * TN;
     constexpr int WAVES_N = BN / WN;
     constexpr int NT = (BM / WM) * WAVES_N * 64;
