@@ -20,6 +20,8 @@ from . import inputs  # noqa: F401  (seeded synthetic inputs; no GPU needed)
 
 __all__ = [
     "SGEMM_PATH_AUTO", "SGEMM_PATH_VALU", "SGEMM_PATH_MFMA",
+    "SGEMM_ACCESS_AUTO", "SGEMM_ACCESS_BUFFER_128", "SGEMM_ACCESS_BUFFER_32",
+    "SGEMM_ACCESS_CHECKED", "sgemm_variant_access",
     "SgemmError", "LibraryNotBuilt", "library_path", "load_library",
     "sgemm", "sgemm_path", "sgemm_variant", "sgemm_variant_count",
     "sgemm_variant_name", "sgemm_variant_path", "sgemm_variant_tile",
@@ -29,6 +31,11 @@ __all__ = [
 SGEMM_PATH_AUTO = 0
 SGEMM_PATH_VALU = 1
 SGEMM_PATH_MFMA = 2
+
+SGEMM_ACCESS_AUTO = 0
+SGEMM_ACCESS_BUFFER_128 = 1
+SGEMM_ACCESS_BUFFER_32 = 2
+SGEMM_ACCESS_CHECKED = 3
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIBNAME = "libsgemm_mi355x.so"
@@ -70,6 +77,8 @@ def load_library():
         lib.sgemm_path.restype = i
         lib.sgemm_variant.argtypes = [i] + gemm_args
         lib.sgemm_variant.restype = i
+        lib.sgemm_variant_access.argtypes = [i, i] + gemm_args
+        lib.sgemm_variant_access.restype = i
         lib.sgemm_variant_count.argtypes = []
         lib.sgemm_variant_count.restype = i
         lib.sgemm_variant_name.argtypes = [i]
@@ -138,6 +147,15 @@ def sgemm_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=
     return _ret(lib.sgemm_variant(int(variant), *_gemm_args(M, N, K, alpha, A, lda, B, ldb,
                                                             beta, C, ldc, stream)),
                 "sgemm_variant", check)
+
+
+def sgemm_variant_access(variant, access, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         stream=None, check=True):
+    lib = load_library()
+    return _ret(lib.sgemm_variant_access(int(variant), int(access),
+                                         *_gemm_args(M, N, K, alpha, A, lda, B, ldb, beta, C,
+                                                     ldc, stream)),
+                "sgemm_variant_access", check)
 
 
 def sgemm_variant_count() -> int:

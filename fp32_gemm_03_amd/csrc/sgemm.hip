@@ -22,22 +22,25 @@ struct Variant {
     int path;           // SGEMM_PATH_VALU or SGEMM_PATH_MFMA
     int bm, bn, bk;     // block tile
     int threads;        // workgroup size
-    KernelFn vec4;      // B, C and their leading dimensions 16-byte friendly
-    KernelFn vec1;      // anything else
+    KernelFn vec4;      // buffer accesses; B, C and their leading dimensions 16-byte friendly
+    KernelFn vec1;      // buffer accesses, 32-bit
+    KernelFn generic;   // per-element checked pointer accesses (any leading dimension)
 };
 
 // VALU: 128 x 128 x 16 block, 4 waves of 64 x 64, 8 x 8 per lane.
 #define VALU_CFG(BM, BN, BK, TM, TN, PA, PB, WPE)                                       \
     {"valu_" #BM "x" #BN "x" #BK "_t" #TM "x" #TN, SGEMM_PATH_VALU, BM, BN, BK,           \
      (BM / (8 * TM)) * (BN / (8 * TN)) * 64,                                             \
-     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 4, WPE>,                             \
-     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE>}
+     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 4, WPE, true>,                       \
+     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, true>,                       \
+     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, false>}
 
 #define MFMA_CFG(BM, BN, BK, WM, WN, PA, PB, WPE)                                       \
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN, SGEMM_PATH_MFMA, BM, BN, BK,           \
      (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4, WPE>,                             \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE>}
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4, WPE, true>,                       \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, true>,                       \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, false>}
 
 const Variant kVariants[] = {
     VALU_CFG(128, 128, 16, 8, 8, 4, 0, 4),     // 0
@@ -54,7 +57,6 @@ const Variant kVariants[] = {
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 constexpr int kValuDefault = 0;
-constexpr int kMfma256x128 = 5;
 constexpr int kMfma128x256 = 7;
 constexpr int kMfmaMedium = 2;
 constexpr int kMfmaSmall = 3;
@@ -67,19 +69,19 @@ long long tiles(int M, int N, int bm, int bn) {
     return (long long)((M + bm - 1) / bm) * (long long)((N + bn - 1) / bn);
 }
 
-// Measured on MI355X (8192^3, 4096^3, 16384^3, 2048^3, 1024^3, 16384^2 x 128,
-// 1000 x 1023 x 999, 256^3): the 256 x 128 and 128 x 256 blocks with two
-// workgroups per CU are fastest once there are at least two blocks per CU;
-// with small K the epilogue (C read and write) dominates and the 128 x 256
-// block, whose lanes store 4 consecutive columns, is the faster of the two.
-// Below that, the largest block that still gives every CU a workgroup wins.
+// Measured on MI355X (8192^3, 4096^3, 2048^3, 1024^3, 16384^2 x 128,
+// 1000 x 1023 x 999, 256^3): the 128 x 256 block with two workgroups per CU
+// is fastest once there are at least two blocks per CU (its lanes also store
+// 4 consecutive columns, which matters when the epilogue dominates at small
+// K).  Below that, the largest block that still gives every CU a workgroup
+// wins.
 int select_variant(int path, int M, int N, int K) {
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
     if (path == SGEMM_PATH_VALU) return kValuDefault;
     if (path != SGEMM_PATH_AUTO && path != SGEMM_PATH_MFMA) return SGEMM_ERR_PATH;
-    if (tiles(M, N, 256, 128) >= 2 * kComputeUnits) return K < 2048 ? kMfma128x256 : kMfma256x128;
+    if (tiles(M, N, 128, 256) >= 2 * kComputeUnits) return kMfma128x256;
     if (tiles(M, N, 128, 128) >= kComputeUnits) return kMfmaMedium;
     return kMfmaSmall;
 }
@@ -101,12 +103,13 @@ int check_args(int M, int N, int K, float alpha, const float *A, int lda,
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-int launch(int variant, int M, int N, int K, float alpha, const float *A,
+int launch(int variant, int access, int M, int N, int K, float alpha, const float *A,
            int lda, const float *B, int ldb, float beta, float *C, int ldc,
            hipStream_t stream) {
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     if (variant < 0 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
+    if (access < SGEMM_ACCESS_AUTO || access > SGEMM_ACCESS_CHECKED) return SGEMM_ERR_ACCESS;
     if (M == 0 || N == 0) return SGEMM_OK;
     const bool no_product = alpha == 0.0f || K == 0;
     if (no_product && beta == 1.0f) return SGEMM_OK;
@@ -127,16 +130,33 @@ int launch(int variant, int M, int N, int K, float alpha, const float *A,
     a.lda = lda;
     a.ldb = ldb;
     a.ldc = ldc;
-    // The fast path forms byte offsets inside one block tile in 32 bits.
+    // Buffer accesses form byte offsets inside one block tile in 31 bits.
     const long long lim = 1LL << 31;
-    a.fast = (long long)(v.bm + 4) * lda * 4 < lim && (long long)(v.bk + 4) * ldb * 4 < lim;
-
+    const bool buf_ok = (long long)(v.bm + 1) * lda * 4 < lim &&
+                        (long long)(v.bk + 1) * ldb * 4 + (long long)v.bn * 4 < lim &&
+                        (long long)(v.bm + 1) * ldc * 4 < lim;
     // 128-bit accesses to B and C need 16-byte aligned bases and every row
     // start a multiple of 4 floats; N % 4 == 0 keeps each 4-wide piece wholly
     // inside or wholly outside the matrix.  A is read 32 bits at a time.
     const bool vec4 = (N % 4 == 0) && (ldb % 4 == 0) && (ldc % 4 == 0) &&
                       aligned16(B) && aligned16(C);
-    KernelFn fn = vec4 ? v.vec4 : v.vec1;
+    KernelFn fn;
+    switch (access) {
+        case SGEMM_ACCESS_BUFFER_128:
+            if (!buf_ok || !vec4) return SGEMM_ERR_ACCESS;
+            fn = v.vec4;
+            break;
+        case SGEMM_ACCESS_BUFFER_32:
+            if (!buf_ok) return SGEMM_ERR_ACCESS;
+            fn = v.vec1;
+            break;
+        case SGEMM_ACCESS_CHECKED:
+            fn = v.generic;
+            break;
+        default:
+            fn = !buf_ok ? v.generic : (vec4 ? v.vec4 : v.vec1);
+            break;
+    }
 
     (void)hipGetLastError();  // drop any stale error so the code below is this launch's
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(v.threads), 0, stream, a);
@@ -161,13 +181,19 @@ int sgemm_path(int path, int M, int N, int K, float alpha, const float *A,
     if (rc != SGEMM_OK) return rc;
     const int v = select_variant(path, M, N, K);
     if (v < 0) return v;
-    return launch(v, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return launch(v, SGEMM_ACCESS_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int sgemm_variant(int variant, int M, int N, int K, float alpha,
                   const float *A, int lda, const float *B, int ldb, float beta,
                   float *C, int ldc, hipStream_t stream) {
-    return launch(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return launch(variant, SGEMM_ACCESS_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int sgemm_variant_access(int variant, int access, int M, int N, int K, float alpha,
+                         const float *A, int lda, const float *B, int ldb, float beta,
+                         float *C, int ldc, hipStream_t stream) {
+    return launch(variant, access, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int sgemm_variant_count(void) { return kNumVariants; }
@@ -208,6 +234,7 @@ const char *sgemm_status_string(int status) {
         case SGEMM_ERR_PATH: return "invalid argument: unknown path";
         case SGEMM_ERR_VARIANT: return "invalid argument: unknown variant";
         case SGEMM_ERR_TOO_LARGE: return "problem too large: tile grid exceeds one launch";
+        case SGEMM_ERR_ACCESS: return "invalid argument: access mode unknown or not possible for these arguments";
         default: break;
     }
     if (status > 0) return hipGetErrorString((hipError_t)status);

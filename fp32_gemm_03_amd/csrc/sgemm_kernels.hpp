@@ -13,12 +13,10 @@
 //     wave tile in 32 x 32 blocks (16 accumulators per lane per block).
 //
 // Staging (both kernels).  The block tile walks K in steps of BK.  Per step:
-//   1. global -> VGPR: A's BM x BK block and B's BK x BN block.  Elements
-//      outside M, N or K load as 0.0 (zero padding of partial tiles, "3.3
-//      Shared memory ו tiling תרגול", exercise 1).  B is read with 128-bit
-//      loads along N when VEC == 4, else with 32-bit loads.  A is read as
-//      4 rows x 1 column per thread group: consecutive lanes walk K, so every
-//      load instruction covers whole row segments of A.
+//   1. global -> VGPR: A's BM x BK block and B's BK x BN block.  B is read
+//      with 128-bit loads along N when VEC == 4, else with 32-bit loads.  A is
+//      read as 4 rows x 1 column per thread: consecutive lanes walk K, so
+//      every load instruction covers whole row segments of A.
 //   2. VGPR -> LDS: A is stored TRANSPOSED (k-major, As[k][m]) with its rows
 //      padded by PADA floats, one 128-bit store per 4 rows; B is stored as it
 //      is (Bs[k][n], padded by PADB).  This is the layout of "SGEMM CUDA kernel
@@ -30,6 +28,20 @@
 //      afterwards; one workgroup barrier per step ("如何高效实现矩阵乘", section
 //      "Double Buffer").
 //
+// Partial tiles ("3.3 Shared memory ו tiling תרגול", exercise 1: pad partial
+// tiles with zeros).  With BUF (the normal case) every global access is a raw
+// buffer access whose descriptor ends at the matrix's last element: reads
+// past it return 0.0 and writes past it are dropped by the hardware, with no
+// branch in the kernel.  What the descriptor cannot cut off is handled so:
+//   * A columns k >= K inside the matrix get an out-of-range offset in the
+//     last K tile, so they read 0.0 (they meet B rows k >= K, which also read
+//     0.0, and 0 * 0 keeps NaN and Inf out);
+//   * B columns n >= N inside the matrix are read as they are: they only feed
+//     C columns >= N, which are never stored;
+//   * C columns n >= N inside the matrix get an out-of-range offset.
+// Without BUF (leading dimensions too large for 31-bit offsets inside one
+// tile) every element is checked explicitly and loads 0.0 outside.
+//
 // Workgroup -> tile order: consecutive workgroup ids walk one row of C tiles
 // (the M tile index is the slow one), "如何高效实现矩阵乘", section "Wave & L2
 // cache Hit Rate".
@@ -39,6 +51,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace sgk {
 
@@ -53,12 +67,7 @@ struct Args {
     const float *B;
     float *C;
     int64_t lda, ldb, ldc;
-    // Nonzero when every byte offset the fast path forms inside one block
-    // tile fits in 31 bits (set by the host per variant).
-    int fast;
 };
-
-typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 template <int W> struct vec_t;
 template <> struct vec_t<1> { typedef float type; };
@@ -71,24 +80,72 @@ __device__ __forceinline__ float vget(const float4 &v, int i) {
     return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-template <class T>
-__device__ __forceinline__ T load_at(const char *base, uint32_t byte_off) {
-    return *reinterpret_cast<const T *>(base + byte_off);
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// ---------------------------------------------------------------------------
+// Raw buffer accesses.  A descriptor covers [base, base + bytes); an access at
+// a byte offset >= bytes reads 0 / writes nothing.  kOutOfRange is above every
+// extent used here (extents are clamped below 2^31).
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes) {
+    const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, kRsrcWord3);
 }
+
+// The LLVM raw buffer intrinsics, bound by name with explicit vector types
+// (the clang b64/b128 builtins of this toolchain lower to 32-bit loads).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ float raw_load_f32(rsrc_t, uint32_t, uint32_t, int) __asm("llvm.amdgcn.raw.ptr.buffer.load.f32");
+__device__ f32x2 raw_load_v2f32(rsrc_t, uint32_t, uint32_t, int) __asm("llvm.amdgcn.raw.ptr.buffer.load.v2f32");
+__device__ f32x4 raw_load_v4f32(rsrc_t, uint32_t, uint32_t, int) __asm("llvm.amdgcn.raw.ptr.buffer.load.v4f32");
+__device__ void raw_store_f32(float, rsrc_t, uint32_t, uint32_t, int) __asm("llvm.amdgcn.raw.ptr.buffer.store.f32");
+__device__ void raw_store_v2f32(f32x2, rsrc_t, uint32_t, uint32_t, int) __asm("llvm.amdgcn.raw.ptr.buffer.store.v2f32");
+__device__ void raw_store_v4f32(f32x4, rsrc_t, uint32_t, uint32_t, int) __asm("llvm.amdgcn.raw.ptr.buffer.store.v4f32");
+
+template <int W> struct buf;
+template <> struct buf<1> {
+    static __device__ __forceinline__ float load(rsrc_t r, uint32_t off) { return raw_load_f32(r, off, 0, 0); }
+    static __device__ __forceinline__ void store(float v, rsrc_t r, uint32_t off) { raw_store_f32(v, r, off, 0, 0); }
+};
+template <> struct buf<2> {
+    static __device__ __forceinline__ float2 load(rsrc_t r, uint32_t off) {
+        const f32x2 v = raw_load_v2f32(r, off, 0, 0);
+        return make_float2(v.x, v.y);
+    }
+    static __device__ __forceinline__ void store(float2 v, rsrc_t r, uint32_t off) {
+        f32x2 u;
+        u.x = v.x;
+        u.y = v.y;
+        raw_store_v2f32(u, r, off, 0, 0);
+    }
+};
+template <> struct buf<4> {
+    static __device__ __forceinline__ float4 load(rsrc_t r, uint32_t off) {
+        const f32x4 v = raw_load_v4f32(r, off, 0, 0);
+        return make_float4(v.x, v.y, v.z, v.w);
+    }
+    static __device__ __forceinline__ void store(float4 v, rsrc_t r, uint32_t off) {
+        f32x4 u;
+        u.x = v.x;
+        u.y = v.y;
+        u.z = v.z;
+        u.w = v.w;
+        raw_store_v4f32(u, r, off, 0, 0);
+    }
+};
 
 // ---------------------------------------------------------------------------
 // A tile: BM x BK block of A -> As[BK][BM + PADA] (transposed).
 // Thread tid covers column tid % BK of rows r0 + {0..3} + p * ROWS_PER_PASS,
-// r0 = 4 * (tid / BK): a load instruction reads NT/BK row segments of BK
-// consecutive floats, and each thread writes one 128-bit vector per 4 rows.
-//
-// load_fast: the block lies inside M and the K tile is full, so nothing is
-// checked; the address is a uniform (scalar) tile base plus a 32-bit
-// per-thread offset.  load_checked: every element is checked against M and K
-// and loads 0.0 outside.
+// r0 = 4 * (tid / BK), and writes one 128-bit LDS vector per 4 rows.
 // ---------------------------------------------------------------------------
 template <int BM, int BK, int NT, int PADA>
-struct ATile {
+struct ATileGeom {
     static_assert(BM % 4 == 0, "BM must be a multiple of 4");
     static_assert(NT % BK == 0, "BK must divide the thread count");
     static constexpr int ROWS_PER_PASS = 4 * (NT / BK);
@@ -97,42 +154,6 @@ struct ATile {
     static constexpr int SA = BM + PADA;
 
     float4 reg[PER];
-    int col;           // column inside the tile
-    int r0;            // first row inside the block
-    uint32_t off[4];   // fast path: ((r0 + c) * lda + col) * 4
-
-    __device__ __forceinline__ void init(const Args &a, int tid) {
-        col = tid % BK;
-        r0 = 4 * (tid / BK);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) off[c] = (uint32_t)(((int64_t)(r0 + c) * a.lda + col) * 4);
-    }
-
-    // tile: byte address of A[bm][k0]; pass: ROWS_PER_PASS * lda * 4
-    __device__ __forceinline__ void load_fast(const char *tile, int64_t pass) {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const char *sb = tile + p * pass;
-            reg[p].x = load_at<float>(sb, off[0]);
-            reg[p].y = load_at<float>(sb, off[1]);
-            reg[p].z = load_at<float>(sb, off[2]);
-            reg[p].w = load_at<float>(sb, off[3]);
-        }
-    }
-
-    __device__ __forceinline__ void load_checked(const Args &a, int bm, int k0) {
-        const bool kin = (k0 + col) < a.K;
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int row = bm + r0 + p * ROWS_PER_PASS;
-            const float *q = a.A + (int64_t)row * a.lda + k0 + col;
-            const int rl = a.M - row;
-            reg[p].x = (kin && rl > 0) ? q[0] : 0.0f;
-            reg[p].y = (kin && rl > 1) ? q[a.lda] : 0.0f;
-            reg[p].z = (kin && rl > 2) ? q[2 * a.lda] : 0.0f;
-            reg[p].w = (kin && rl > 3) ? q[3 * a.lda] : 0.0f;
-        }
-    }
 
     __device__ __forceinline__ void store(float *As, int tid) const {
         float *dst = As + (tid % BK) * SA + 4 * (tid / BK);
@@ -142,13 +163,71 @@ struct ATile {
     }
 };
 
+template <int BM, int BK, int NT, int PADA>
+struct ATileBuf : ATileGeom<BM, BK, NT, PADA> {
+    typedef ATileGeom<BM, BK, NT, PADA> G;
+    rsrc_t rsrc;       // rows bm.. of A, up to A's last element
+    uint32_t off[4];   // ((r0 + c) * lda + col) * 4
+    uint32_t pass;     // ROWS_PER_PASS * lda * 4
+    int col;
+
+    __device__ __forceinline__ void init(const Args &a, int bm, int tid) {
+        col = tid % BK;
+        const int r0 = 4 * (tid / BK);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) off[c] = (uint32_t)(((int64_t)(r0 + c) * a.lda + col) * 4);
+        pass = (uint32_t)(G::ROWS_PER_PASS * a.lda * 4);
+        rsrc = make_rsrc(a.A + (int64_t)bm * a.lda, ((int64_t)(a.M - bm - 1) * a.lda + a.K) * 4);
+    }
+
+    __device__ __forceinline__ void load(const Args &a, int, int k0) {
+        const bool kin = (k0 + col) < a.K;
+        uint32_t o[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) o[c] = kin ? off[c] + 4u * (uint32_t)k0 : kOutOfRange;
+#pragma unroll
+        for (int p = 0; p < G::PER; ++p) {
+            G::reg[p].x = buf<1>::load(rsrc, o[0] + p * pass);
+            G::reg[p].y = buf<1>::load(rsrc, o[1] + p * pass);
+            G::reg[p].z = buf<1>::load(rsrc, o[2] + p * pass);
+            G::reg[p].w = buf<1>::load(rsrc, o[3] + p * pass);
+        }
+    }
+};
+
+template <int BM, int BK, int NT, int PADA>
+struct ATilePtr : ATileGeom<BM, BK, NT, PADA> {
+    typedef ATileGeom<BM, BK, NT, PADA> G;
+    int col, r0;
+
+    __device__ __forceinline__ void init(const Args &, int, int tid) {
+        col = tid % BK;
+        r0 = 4 * (tid / BK);
+    }
+
+    __device__ __forceinline__ void load(const Args &a, int bm, int k0) {
+        const bool kin = (k0 + col) < a.K;
+#pragma unroll
+        for (int p = 0; p < G::PER; ++p) {
+            const int row = bm + r0 + p * G::ROWS_PER_PASS;
+            const float *q = a.A + (int64_t)row * a.lda + k0 + col;
+            const int rl = a.M - row;
+            G::reg[p].x = (kin && rl > 0) ? q[0] : 0.0f;
+            G::reg[p].y = (kin && rl > 1) ? q[a.lda] : 0.0f;
+            G::reg[p].z = (kin && rl > 2) ? q[2 * a.lda] : 0.0f;
+            G::reg[p].w = (kin && rl > 3) ? q[3 * a.lda] : 0.0f;
+        }
+    }
+};
+
 // ---------------------------------------------------------------------------
 // B tile: BK x BN block of B -> Bs[BK][BN + PADB] (as is), VEC floats per
-// load.  Consecutive threads take consecutive VEC-wide pieces of a row.
+// load.  Consecutive threads take consecutive VEC-wide pieces of a row; piece
+// p of a thread sits at tile row k_first + dk(p), tile column n_first + dn(p).
 // ---------------------------------------------------------------------------
 template <int BN, int BK, int NT, int PADB, int VEC>
-struct BTile {
-    static constexpr int PER_ROW = BN / VEC;  // pieces per tile row
+struct BTileGeom {
+    static constexpr int PER_ROW = BN / VEC;
     static_assert(BN % VEC == 0, "BN must be a multiple of VEC");
     static_assert(NT % PER_ROW == 0 || PER_ROW % NT == 0, "B tile rows and threads must nest");
     static constexpr int ITEMS = BK * PER_ROW;
@@ -158,42 +237,12 @@ struct BTile {
     typedef typename vec_t<VEC>::type V;
 
     V reg[PER];
-    int k_first;   // tile row of piece 0
-    int n_first;   // column of piece 0 inside the tile
-    uint32_t off;  // fast path: (k_first * ldb + n_first) * 4
 
-    // piece p of a thread: tile row k_first + dk(p), tile column n_first + dn(p)
     static __device__ __forceinline__ constexpr int dk(int p) {
         return NT % PER_ROW == 0 ? p * (NT / PER_ROW) : (p * NT) / PER_ROW;
     }
     static __device__ __forceinline__ constexpr int dn(int p) {
         return NT % PER_ROW == 0 ? 0 : ((p * NT) % PER_ROW) * VEC;
-    }
-
-    __device__ __forceinline__ void init(const Args &a, int tid) {
-        k_first = tid / PER_ROW;
-        n_first = (tid % PER_ROW) * VEC;
-        off = (uint32_t)(((int64_t)k_first * a.ldb + n_first) * 4);
-    }
-
-    // tile: byte address of B[k0][bn]; ldb_bytes: ldb * 4
-    __device__ __forceinline__ void load_fast(const char *tile, int64_t ldb_bytes) {
-#pragma unroll
-        for (int p = 0; p < PER; ++p)
-            reg[p] = load_at<V>(tile + dk(p) * ldb_bytes + dn(p) * 4, off);
-    }
-
-    __device__ __forceinline__ void load_checked(const Args &a, int bn, int k0) {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int n = bn + n_first + dn(p);
-            const int k = k0 + k_first + dk(p);
-            // VEC == 4 only when N % 4 == 0: a piece is all in or all out
-            if (n < a.N && k < a.K)
-                reg[p] = *reinterpret_cast<const V *>(a.B + (int64_t)k * a.ldb + n);
-            else
-                reg[p] = V{};
-        }
     }
 
     __device__ __forceinline__ void store(float *Bs, int tid) const {
@@ -204,55 +253,144 @@ struct BTile {
     }
 };
 
-// Loads of K tile t into the staging registers: the fast path for a block
-// inside M and N with a full K tile, the checked path otherwise.
-template <class TA, class TB, int BK>
-__device__ __forceinline__ void load_tile(const Args &a, TA &ta, TB &tb, bool interior, int bm,
-                                          int bn, int t) {
-    const int k0 = t * BK;
-    if (interior && k0 + BK <= a.K) {
-        const char *at = reinterpret_cast<const char *>(a.A + (int64_t)bm * a.lda + k0);
-        const char *bt = reinterpret_cast<const char *>(a.B + (int64_t)k0 * a.ldb + bn);
-        ta.load_fast(at, (int64_t)TA::ROWS_PER_PASS * a.lda * 4);
-        tb.load_fast(bt, a.ldb * 4);
-    } else {
-        ta.load_checked(a, bm, k0);
-        tb.load_checked(a, bn, k0);
+template <int BN, int BK, int NT, int PADB, int VEC>
+struct BTileBuf : BTileGeom<BN, BK, NT, PADB, VEC> {
+    typedef BTileGeom<BN, BK, NT, PADB, VEC> G;
+    uint32_t off;  // (k_first * ldb + n_first) * 4
+    uint32_t ldb4;
+
+    __device__ __forceinline__ void init(const Args &a, int, int tid) {
+        const int k_first = tid / G::PER_ROW;
+        const int n_first = (tid % G::PER_ROW) * VEC;
+        off = (uint32_t)(((int64_t)k_first * a.ldb + n_first) * 4);
+        ldb4 = (uint32_t)(a.ldb * 4);
     }
+
+    __device__ __forceinline__ void load(const Args &a, int bn, int k0) {
+        // Rows k0.. of B from column bn, up to B's last element: rows >= K
+        // read 0.0.  With VEC == 4, N and ldb are multiples of 4, so no
+        // 128-bit piece straddles the end.
+        const rsrc_t r = make_rsrc(a.B + (int64_t)k0 * a.ldb + bn,
+                                   ((int64_t)(a.K - k0 - 1) * a.ldb + (a.N - bn)) * 4);
+#pragma unroll
+        for (int p = 0; p < G::PER; ++p)
+            G::reg[p] = buf<VEC>::load(r, off + G::dk(p) * ldb4 + G::dn(p) * 4);
+    }
+};
+
+template <int BN, int BK, int NT, int PADB, int VEC>
+struct BTilePtr : BTileGeom<BN, BK, NT, PADB, VEC> {
+    typedef BTileGeom<BN, BK, NT, PADB, VEC> G;
+    int k_first, n_first;
+
+    __device__ __forceinline__ void init(const Args &, int, int tid) {
+        k_first = tid / G::PER_ROW;
+        n_first = (tid % G::PER_ROW) * VEC;
+    }
+
+    __device__ __forceinline__ void load(const Args &a, int bn, int k0) {
+#pragma unroll
+        for (int p = 0; p < G::PER; ++p) {
+            const int n = bn + n_first + G::dn(p);
+            const int k = k0 + k_first + G::dk(p);
+            // VEC == 4 only when N % 4 == 0: a piece is all in or all out
+            if (n < a.N && k < a.K)
+                G::reg[p] = *reinterpret_cast<const typename G::V *>(a.B + (int64_t)k * a.ldb + n);
+            else
+                G::reg[p] = typename G::V{};
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Epilogue: C = alpha*acc + beta*C (C read only when beta != 0) for W
+// consecutive columns of one row.  VEC == 4 means N, ldc and C are 16-byte
+// friendly, so a W-wide group at a multiple of W is wholly inside or wholly
+// outside the matrix and moves as one vector.
+// ---------------------------------------------------------------------------
+template <int W>
+__device__ __forceinline__ typename vec_t<W>::type axpby(const Args &a, const float (&v)[W],
+                                                         const typename vec_t<W>::type &old) {
+    typename vec_t<W>::type out;
+    float *o = reinterpret_cast<float *>(&out);
+#pragma unroll
+    for (int i = 0; i < W; ++i) o[i] = fmaf(a.alpha, v[i], a.beta * vget(old, i));
+    return out;
 }
 
-// Epilogue store of W consecutive columns: C = alpha*acc + beta*C (C read only
-// when beta != 0).  CHECK masks rows and columns to the matrix.  VEC == 4
-// means N, ldc and C are 16-byte friendly, so a W-wide group at a multiple of
-// W is all in or all out and goes out as one vector store.
-template <int W, int VEC, bool CHECK>
-__device__ __forceinline__ void store_c(const Args &a, int row, int col, const float (&v)[W]) {
-    if (CHECK && row >= a.M) return;
-    float *c = a.C + (int64_t)row * a.ldc + col;
-    if (VEC == 4 && W > 1) {
-        if (CHECK && col >= a.N) return;
-        typedef typename vec_t<W>::type V;
-        V out;
-        float *o = reinterpret_cast<float *>(&out);
-        if (a.beta != 0.0f) {
-            const V old = *reinterpret_cast<const V *>(c);
+template <int W>
+__device__ __forceinline__ typename vec_t<W>::type ax(const Args &a, const float (&v)[W]) {
+    typename vec_t<W>::type out;
+    float *o = reinterpret_cast<float *>(&out);
 #pragma unroll
-            for (int i = 0; i < W; ++i) o[i] = fmaf(a.alpha, v[i], a.beta * vget(old, i));
+    for (int i = 0; i < W; ++i) o[i] = a.alpha * v[i];
+    return out;
+}
+
+// Buffered: rc covers rows bm.. of C from column bn up to C's last element;
+// (r, c) are tile coordinates.
+template <int W, int VEC>
+struct CStoreBuf {
+    rsrc_t rc;
+    int ncols;  // N - bn
+
+    __device__ __forceinline__ void init(const Args &a, int bm, int bn) {
+        rc = make_rsrc(a.C + (int64_t)bm * a.ldc + bn, ((int64_t)(a.M - bm - 1) * a.ldc + (a.N - bn)) * 4);
+        ncols = a.N - bn;
+    }
+
+    __device__ __forceinline__ void operator()(const Args &a, int r, int c, const float (&v)[W]) const {
+        const uint32_t off = (uint32_t)(((int64_t)r * a.ldc + c) * 4);
+        if (VEC == 4 || W == 1) {
+            const uint32_t o = c < ncols ? off : kOutOfRange;
+            typedef typename vec_t<W>::type V;
+            const V out = a.beta != 0.0f ? axpby<W>(a, v, buf<W>::load(rc, o)) : ax<W>(a, v);
+            buf<W>::store(out, rc, o);
         } else {
 #pragma unroll
-            for (int i = 0; i < W; ++i) o[i] = a.alpha * v[i];
-        }
-        *reinterpret_cast<V *>(c) = out;
-    } else {
-#pragma unroll
-        for (int i = 0; i < W; ++i) {
-            if (!CHECK || col + i < a.N) {
-                const float r = a.beta != 0.0f ? fmaf(a.alpha, v[i], a.beta * c[i]) : a.alpha * v[i];
-                c[i] = r;
+            for (int i = 0; i < W; ++i) {
+                const uint32_t o = c + i < ncols ? off + 4u * i : kOutOfRange;
+                const float vi[1] = {v[i]};
+                const float out = a.beta != 0.0f ? axpby<1>(a, vi, buf<1>::load(rc, o)) : ax<1>(a, vi);
+                buf<1>::store(out, rc, o);
             }
         }
     }
-}
+};
+
+template <int W, int VEC>
+struct CStorePtr {
+    int bm, bn;
+
+    __device__ __forceinline__ void init(const Args &, int bm_, int bn_) {
+        bm = bm_;
+        bn = bn_;
+    }
+
+    __device__ __forceinline__ void operator()(const Args &a, int r, int c, const float (&v)[W]) const {
+        const int row = bm + r, col = bn + c;
+        if (row >= a.M) return;
+        float *p = a.C + (int64_t)row * a.ldc + col;
+        if (VEC == 4 && W > 1) {
+            if (col >= a.N) return;
+            typedef typename vec_t<W>::type V;
+            *reinterpret_cast<V *>(p) = a.beta != 0.0f ? axpby<W>(a, v, *reinterpret_cast<const V *>(p))
+                                                       : ax<W>(a, v);
+        } else {
+#pragma unroll
+            for (int i = 0; i < W; ++i)
+                if (col + i < a.N) p[i] = a.beta != 0.0f ? fmaf(a.alpha, v[i], a.beta * p[i]) : a.alpha * v[i];
+        }
+    }
+};
+
+template <bool BUF, int BM, int BN, int BK, int NT, int PADA, int PADB, int VEC, int W>
+struct Staging {
+    typedef typename std::conditional<BUF, ATileBuf<BM, BK, NT, PADA>, ATilePtr<BM, BK, NT, PADA>>::type TA;
+    typedef typename std::conditional<BUF, BTileBuf<BN, BK, NT, PADB, VEC>,
+                                      BTilePtr<BN, BK, NT, PADB, VEC>>::type TB;
+    typedef typename std::conditional<BUF, CStoreBuf<W, VEC>, CStorePtr<W, VEC>>::type TC;
+};
 
 // ---------------------------------------------------------------------------
 // VALU kernel.  Block tile BM x BN, NT = (BM / (8*TM)) * (BN / (8*TN)) * 64.
@@ -261,23 +399,7 @@ __device__ __forceinline__ void store_c(const Args &a, int row, int col, const f
 //      cols  wn + 4*lx + {0..3} + 32*s  (s < TN/4),
 // so every LDS read is one 128-bit load that 8 lanes share (broadcast).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int TM, int TN, int PADA, int PADB, int VEC, bool CHECK>
-__device__ __forceinline__ void valu_epilogue(const Args &a, int bm, int bn, int wm, int wn,
-                                              int ly, int lx, const float (&acc)[TM][TN]) {
-    // 8 lanes with the same ly cover 32 consecutive columns (128 bytes) of a row
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int row = bm + wm + 4 * ly + (i & 3) + 32 * (i >> 2);
-#pragma unroll
-        for (int s = 0; s < TN / 4; ++s) {
-            const int col = bn + wn + 4 * lx + 32 * s;
-            float v[4] = {acc[i][4 * s], acc[i][4 * s + 1], acc[i][4 * s + 2], acc[i][4 * s + 3]};
-            store_c<4, VEC, CHECK>(a, row, col, v);
-        }
-    }
-}
-
-template <int BM, int BN, int BK, int TM, int TN, int PADA, int PADB, int VEC, int WPE>
+template <int BM, int BN, int BK, int TM, int TN, int PADA, int PADB, int VEC, int WPE, bool BUF>
 __global__ void __launch_bounds__((BM / (8 * TM)) * (BN / (8 * TN)) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
     constexpr int WM = 8 * TM, WN = 8 * TN;
@@ -286,6 +408,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
     static_assert(TM % 4 == 0 && TN % 4 == 0, "micro-tile sides must be multiples of 4");
     constexpr int SA = BM + PADA, SB = BN + PADB;
     constexpr int STAGE = BK * (SA + SB);
+    typedef Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, 4> S;
     __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
     const int tid = threadIdx.x;
@@ -295,12 +418,11 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
     const int bn = (int)(blockIdx.x % nbn) * BN;
     const int wm = (wave / WAVES_N) * WM, wn = (wave % WAVES_N) * WN;
     const int ly = lane >> 3, lx = lane & 7;
-    const bool interior = a.fast && bm + BM <= a.M && bn + BN <= a.N;
 
-    ATile<BM, BK, NT, PADA> ta;
-    BTile<BN, BK, NT, PADB, VEC> tb;
-    ta.init(a, tid);
-    tb.init(a, tid);
+    typename S::TA ta;
+    typename S::TB tb;
+    ta.init(a, bm, tid);
+    tb.init(a, bn, tid);
 
     float acc[TM][TN];
 #pragma unroll
@@ -310,7 +432,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
 
     const int KT = (a.K + BK - 1) / BK;
     if (KT > 0) {
-        load_tile<decltype(ta), decltype(tb), BK>(a, ta, tb, interior, bm, bn, 0);
+        ta.load(a, bm, 0);
+        tb.load(a, bn, 0);
         ta.store(smem, tid);
         tb.store(smem + BK * SA, tid);
     }
@@ -319,7 +442,10 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
     for (int t = 0; t < KT; ++t) {
         const float *As = smem + (t & 1) * STAGE;
         const float *Bs = As + BK * SA;
-        if (t + 1 < KT) load_tile<decltype(ta), decltype(tb), BK>(a, ta, tb, interior, bm, bn, t + 1);
+        if (t + 1 < KT) {
+            ta.load(a, bm, (t + 1) * BK);
+            tb.load(a, bn, (t + 1) * BK);
+        }
         const float *ap = As + wm + 4 * ly;
         const float *bp = Bs + wn + 4 * lx;
         // Partial unrolling bounds how many k-steps of fragments the compiler
@@ -348,10 +474,18 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
         __syncthreads();
     }
 
-    if (bm + BM <= a.M && bn + BN <= a.N)
-        valu_epilogue<BM, BN, BK, TM, TN, PADA, PADB, VEC, false>(a, bm, bn, wm, wn, ly, lx, acc);
-    else
-        valu_epilogue<BM, BN, BK, TM, TN, PADA, PADB, VEC, true>(a, bm, bn, wm, wn, ly, lx, acc);
+    // 8 lanes with the same ly cover 32 consecutive columns (128 bytes) of a row
+    typename S::TC st;
+    st.init(a, bm, bn);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = wm + 4 * ly + (i & 3) + 32 * (i >> 2);
+#pragma unroll
+        for (int s = 0; s < TN / 4; ++s) {
+            const float v[4] = {acc[i][4 * s], acc[i][4 * s + 1], acc[i][4 * s + 2], acc[i][4 * s + 3]};
+            st(a, r, wn + 4 * lx + 32 * s, v);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -373,27 +507,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
 // The fragments of k-step j+1 are read from LDS while the MFMAs of step j
 // issue, so the LDS latency hides behind matrix work.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int VEC, bool CHECK>
-__device__ __forceinline__ void mfma_epilogue(const Args &a, int bm, int bn, int wm, int wn,
-                                              int li, int lh,
-                                              const floatx16 (&acc)[WM / 32][WN / 32]) {
-    constexpr int MI = WM / 32, NI = WN / 32;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int ib = 8 * (r >> 2) + 4 * lh + (r & 3);
-            const int row = bm + wm + MI * ib + i;
-            const int col = bn + wn + NI * li;
-            float v[NI];
-#pragma unroll
-            for (int j = 0; j < NI; ++j) v[j] = acc[i][j][r];
-            store_c<NI, VEC, CHECK>(a, row, col, v);
-        }
-    }
-}
-
-template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC, int WPE>
+template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC, int WPE, bool BUF>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -406,6 +520,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     static_assert(NI == 1 || NI == 2 || NI == 4, "NI in {1, 2, 4}");
     typedef typename vec_t<MI>::type VA;
     typedef typename vec_t<NI>::type VB;
+    typedef Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, NI> S;
     __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
     const int tid = threadIdx.x;
@@ -415,12 +530,11 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     const int bn = (int)(blockIdx.x % nbn) * BN;
     const int wm = (wave / WAVES_N) * WM, wn = (wave % WAVES_N) * WN;
     const int li = lane & 31, lh = lane >> 5;
-    const bool interior = a.fast && bm + BM <= a.M && bn + BN <= a.N;
 
-    ATile<BM, BK, NT, PADA> ta;
-    BTile<BN, BK, NT, PADB, VEC> tb;
-    ta.init(a, tid);
-    tb.init(a, tid);
+    typename S::TA ta;
+    typename S::TB tb;
+    ta.init(a, bm, tid);
+    tb.init(a, bn, tid);
 
     floatx16 acc[MI][NI];
 #pragma unroll
@@ -432,7 +546,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
 
     const int KT = (a.K + BK - 1) / BK;
     if (KT > 0) {
-        load_tile<decltype(ta), decltype(tb), BK>(a, ta, tb, interior, bm, bn, 0);
+        ta.load(a, bm, 0);
+        tb.load(a, bn, 0);
         ta.store(smem, tid);
         tb.store(smem + BK * SA, tid);
     }
@@ -441,7 +556,10 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     for (int t = 0; t < KT; ++t) {
         const float *As = smem + (t & 1) * STAGE;
         const float *Bs = As + BK * SA;
-        if (t + 1 < KT) load_tile<decltype(ta), decltype(tb), BK>(a, ta, tb, interior, bm, bn, t + 1);
+        if (t + 1 < KT) {
+            ta.load(a, bm, (t + 1) * BK);
+            tb.load(a, bn, (t + 1) * BK);
+        }
         const float *ap = As + lh * SA + wm + MI * li;
         const float *bp = Bs + lh * SB + wn + NI * li;
         VA av[2];
@@ -470,10 +588,19 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         __syncthreads();
     }
 
-    if (bm + BM <= a.M && bn + BN <= a.N)
-        mfma_epilogue<BM, BN, WM, WN, VEC, false>(a, bm, bn, wm, wn, li, lh, acc);
-    else
-        mfma_epilogue<BM, BN, WM, WN, VEC, true>(a, bm, bn, wm, wn, li, lh, acc);
+    typename S::TC st;
+    st.init(a, bm, bn);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int ib = 8 * (r >> 2) + 4 * lh + (r & 3);
+            float v[NI];
+#pragma unroll
+            for (int j = 0; j < NI; ++j) v[j] = acc[i][j][r];
+            st(a, wm + MI * ib + i, wn + NI * li, v);
+        }
+    }
 }
 
 }  // namespace sgk

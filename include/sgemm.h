@@ -24,7 +24,8 @@
  * allocates no memory, copies nothing and keeps no handles; it holds no state
  * between calls.  No alignment is required: 16-byte aligned bases with leading
  * dimensions and N that are multiples of 4 take 128-bit global accesses,
- * anything else takes 32-bit ones.  C must not overlap A or B (undefined
+ * anything else takes 32-bit ones (see sgemm_variant_access for the three
+ * access modes).  C must not overlap A or B (undefined
  * behaviour).  Dimensions and leading dimensions are int; address arithmetic
  * is 64-bit.
  *
@@ -43,7 +44,8 @@
  * M*K > 0 and alpha != 0, -6 lda < max(1, K), -7 B == NULL while K*N > 0 and
  * alpha != 0, -8 ldb < max(1, N), -10 C == NULL while M*N > 0, -11
  * ldc < max(1, N)); -20 unknown path; -21 unknown variant; -22 the tile grid
- * does not fit one launch.  Argument checks run before any HIP call, so they
+ * does not fit one launch; -23 an unknown access mode, or one these arguments
+ * do not allow.  Argument checks run before any HIP call, so they
  * need no GPU.  Positive: the hipError_t reported for the launch.  The library
  * never exits or aborts the process.
  */
@@ -60,10 +62,17 @@ extern "C" {
 #define SGEMM_PATH_VALU 1 /* FP32 FMA on the vector ALU, register outer product */
 #define SGEMM_PATH_MFMA 2 /* v_mfma_f32_32x32x2_f32 matrix-core inner product */
 
+/* How a kernel reaches global memory (sgemm_variant_access). */
+#define SGEMM_ACCESS_AUTO 0       /* the library's choice, as sgemm_variant() */
+#define SGEMM_ACCESS_BUFFER_128 1 /* range-checked buffer accesses, 128-bit on B and C */
+#define SGEMM_ACCESS_BUFFER_32 2  /* range-checked buffer accesses, 32-bit */
+#define SGEMM_ACCESS_CHECKED 3    /* per-element checked pointer accesses */
+
 #define SGEMM_OK 0
 #define SGEMM_ERR_PATH (-20)
 #define SGEMM_ERR_VARIANT (-21)
 #define SGEMM_ERR_TOO_LARGE (-22)
+#define SGEMM_ERR_ACCESS (-23)
 
 /* C = alpha*A*B + beta*C, automatic choice of inner product and tile. */
 int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
@@ -82,6 +91,23 @@ int sgemm_path(int path, int M, int N, int K, float alpha, const float *A,
 int sgemm_variant(int variant, int M, int N, int K, float alpha,
                   const float *A, int lda, const float *B, int ldb, float beta,
                   float *C, int ldc, hipStream_t stream);
+
+/* As sgemm_variant(), with the global-memory access mode forced as well
+ * (SGEMM_ACCESS_*).  Each variant is compiled three ways:
+ *   BUFFER_128  raw buffer accesses whose descriptors end at each matrix's
+ *               last element, so partial tiles need no branch; 128-bit on B
+ *               and C.  Needs 16-byte aligned B and C, N, ldb and ldc
+ *               multiples of 4, and byte offsets inside one block tile below
+ *               2^31 (about (BM+1)*lda*4, (BK+1)*ldb*4 and (BM+1)*ldc*4).
+ *   BUFFER_32   the same with 32-bit accesses: any alignment.
+ *   CHECKED     plain pointers with every element checked: any arguments.
+ * SGEMM_ACCESS_AUTO takes the first of these the arguments allow.  A forced
+ * mode the arguments do not allow returns SGEMM_ERR_ACCESS.  For tests and
+ * benchmarks that must cover every compiled kernel. */
+int sgemm_variant_access(int variant, int access, int M, int N, int K,
+                         float alpha, const float *A, int lda, const float *B,
+                         int ldb, float beta, float *C, int ldc,
+                         hipStream_t stream);
 
 /* Number of compiled kernel variants. */
 int sgemm_variant_count(void);

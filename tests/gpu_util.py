@@ -35,7 +35,7 @@ def to_gpu(t: torch.Tensor, offset_floats: int = 0) -> tuple:
     return owner, first, owner.data_ptr() + 4 * first
 
 
-def run(p, variant=None, path=None, offsets=(0, 0, 0), stream=None):
+def run(p, variant=None, path=None, offsets=(0, 0, 0), stream=None, access=None):
     """Launch one SGEMM on ``p`` (an ``inputs.Problem``); returns the whole C buffer
     (M x ldc, float32, numpy) after the call, and checks that nothing outside the
     operands' extents was written."""
@@ -43,7 +43,9 @@ def run(p, variant=None, path=None, offsets=(0, 0, 0), stream=None):
     ob, _, b = to_gpu(p.B, offsets[1])
     oc, first, c = to_gpu(p.C, offsets[2])
     args = (p.M, p.N, p.K, p.alpha, a, p.lda, b, p.ldb, p.beta, c, p.ldc)
-    if variant is not None:
+    if access is not None:
+        g.sgemm_variant_access(variant, access, *args, stream=stream)
+    elif variant is not None:
         g.sgemm_variant(variant, *args, stream=stream)
     elif path is not None:
         g.sgemm_path(path, *args, stream=stream)
@@ -83,3 +85,16 @@ def pad_untouched(p, out):
     before = p.C.numpy()[:, p.N:]
     after = out[:, p.N:]
     return np.array_equal(before.view(np.uint32), after.view(np.uint32))
+
+
+ACCESS_NAMES = {0: "auto", 1: "buf128", 2: "buf32", 3: "checked"}
+
+
+def allowed_accesses(p, offsets=(0, 0, 0)):
+    """The access modes whose preconditions these arguments meet (the test
+    operands are small, so the 31-bit offset bound always holds)."""
+    modes = [g.SGEMM_ACCESS_BUFFER_32, g.SGEMM_ACCESS_CHECKED]
+    aligned = offsets[1] % 4 == 0 and offsets[2] % 4 == 0
+    if p.N % 4 == 0 and p.ldb % 4 == 0 and p.ldc % 4 == 0 and aligned:
+        modes.insert(0, g.SGEMM_ACCESS_BUFFER_128)
+    return modes

@@ -93,6 +93,21 @@ def test_unknown_path_and_variant():
     assert "unknown variant" in g.sgemm_status_string(-21)
 
 
+def test_access_mode_codes():
+    def acc(mode, **kw):
+        base = dict(M=4, N=4, K=4, alpha=1.0, A=0x1000, lda=4, B=0x2000, ldb=4, beta=0.0,
+                    C=0x3000, ldc=4)
+        base.update(kw)
+        return g.sgemm_variant_access(0, mode, *base.values(), stream=0, check=False)
+    assert acc(4) == -23
+    assert acc(-1) == -23
+    assert acc(g.SGEMM_ACCESS_BUFFER_128, B=0x2004) == -23     # misaligned B
+    assert acc(g.SGEMM_ACCESS_BUFFER_128, N=3, ldb=4, ldc=4) == -23
+    assert acc(g.SGEMM_ACCESS_BUFFER_32, lda=1 << 30) == -23    # offsets beyond 31 bits
+    assert acc(4, M=-1) == -1                                   # argument checks come first
+    assert "access mode" in g.sgemm_status_string(-23)
+
+
 def test_variant_table():
     vs = g.variants()
     assert len(vs) == g.sgemm_variant_count() >= 2

@@ -23,6 +23,25 @@ def all_variants():
     return list(range(g.sgemm_variant_count()))
 
 
+ACCESSES = [g.SGEMM_ACCESS_BUFFER_128, g.SGEMM_ACCESS_BUFFER_32, g.SGEMM_ACCESS_CHECKED]
+
+
+def combos():
+    """Every compiled kernel: (variant, access mode)."""
+    return [(v, acc) for v in all_variants() for acc in ACCESSES]
+
+
+def combo_id(c):
+    return f"{g.sgemm_variant_name(c[0])}-{gu.ACCESS_NAMES[c[1]]}"
+
+
+def run_all_modes(p, variant, offsets=(0, 0, 0)):
+    """Run every access mode the arguments allow; yields (mode, output)."""
+    for acc in gu.allowed_accesses(p, offsets):
+        gu.say("  access", gu.ACCESS_NAMES[acc])
+        yield acc, gu.run(p, variant=variant, access=acc, offsets=offsets)
+
+
 @functools.lru_cache(maxsize=None)
 def cached_problem(name):
     return inputs.workload_problem(name)
@@ -44,33 +63,34 @@ def _gpu_available():
 def test_closed_form_every_variant(variant):
     p = cached_problem("square256_closed_form")
     gu.say("closed form 256^3", g.sgemm_variant_name(variant))
-    out = gu.run(p, variant=variant)
-    assert np.all(out == 512.0), np.unique(out)[:8]
+    for acc, out in run_all_modes(p, variant):
+        assert np.all(out == 512.0), (acc, np.unique(out)[:8])
 
 
 @pytest.mark.parametrize("variant", all_variants())
 def test_closed_form_nonsquare_ragged(variant):
     # every element is exactly 2K for any shape, including partial tiles
-    p = inputs.make_problem(131, 77, 203, dist="ones_twos")
-    gu.say("closed form 131x77x203", g.sgemm_variant_name(variant))
-    out = gu.run(p, variant=variant)
-    assert np.all(out == 2.0 * 203)
+    for M, N, K in [(131, 77, 203), (131, 80, 203)]:
+        p = inputs.make_problem(M, N, K, dist="ones_twos")
+        gu.say("closed form", M, N, K, g.sgemm_variant_name(variant))
+        for acc, out in run_all_modes(p, variant):
+            assert np.all(out == 2.0 * K), (M, N, K, acc)
 
 
 @pytest.mark.parametrize("variant", all_variants())
 def test_alpha_zero_and_k_zero_give_beta_c(variant):
     p = inputs.make_problem(70, 45, 33, dist="upm1", seed=5, alpha=0.0, beta=-0.5, c_fill="upm1")
     gu.say("alpha=0", g.sgemm_variant_name(variant))
-    out = gu.run(p, variant=variant)
-    assert np.array_equal(out, (np.float32(-0.5) * p.C.numpy()))
+    for acc, out in run_all_modes(p, variant):
+        assert np.array_equal(out, (np.float32(-0.5) * p.C.numpy())), acc
     p0 = inputs.make_problem(70, 45, 0, dist="upm1", seed=5, alpha=1.0, beta=2.0, c_fill="upm1")
     gu.say("K=0", g.sgemm_variant_name(variant))
-    out = gu.run(p0, variant=variant)
-    assert np.array_equal(out, (np.float32(2.0) * p0.C.numpy()))
-    pz = inputs.make_problem(70, 45, 0, dist="upm1", seed=5, beta=0.0, c_fill="nan")
+    for acc, out in run_all_modes(p0, variant):
+        assert np.array_equal(out, (np.float32(2.0) * p0.C.numpy())), acc
+    pz = inputs.make_problem(70, 48, 0, dist="upm1", seed=5, beta=0.0, c_fill="nan")
     gu.say("K=0 beta=0", g.sgemm_variant_name(variant))
-    out = gu.run(pz, variant=variant)
-    assert np.all(out == 0.0)
+    for acc, out in run_all_modes(pz, variant):
+        assert np.all(out == 0.0), acc
 
 
 # ------------------------------------------------------------------ workloads, every element
@@ -79,9 +99,25 @@ def test_alpha_zero_and_k_zero_give_beta_c(variant):
 def test_workloads_every_variant(name, variant):
     p = cached_problem(name)
     gu.say(name, g.sgemm_variant_name(variant))
-    out = gu.run(p, variant=variant)
-    r = gu.ratio_full(p, out, cached_oracle(name))
-    assert r <= TOL, (name, g.sgemm_variant_name(variant), r)
+    for acc, out in run_all_modes(p, variant):
+        r = gu.ratio_full(p, out, cached_oracle(name))
+        assert r <= TOL, (name, g.sgemm_variant_name(variant), acc, r)
+
+
+def test_forced_access_mode_preconditions():
+    # 128-bit accesses are refused when B or C cannot take them
+    p = inputs.make_problem(64, 63, 32, dist="upm1", seed=1)
+    _, _, a = gu.to_gpu(p.A)
+    _, _, b = gu.to_gpu(p.B)
+    oc, _, c = gu.to_gpu(p.C)
+    rc = g.sgemm_variant_access(1, g.SGEMM_ACCESS_BUFFER_128, p.M, p.N, p.K, 1.0, a, p.lda, b,
+                                p.ldb, 0.0, c, p.ldc, check=False)
+    assert rc == -23
+    rc = g.sgemm_variant_access(1, 7, p.M, p.N, p.K, 1.0, a, p.lda, b, p.ldb, 0.0, c, p.ldc,
+                                check=False)
+    assert rc == -23
+    torch.cuda.synchronize()
+    del oc
 
 
 @pytest.mark.parametrize("name", ["square256_u01", "ragged_1000x1023x999", "square1024_normal"])
@@ -116,9 +152,10 @@ def test_edge_sweep(variant):
         p = inputs.make_problem(M, N, K, dist="upm1", seed=idx, alpha=alpha, beta=beta,
                                 c_fill="upm1" if beta != 0 else None)
         gu.say("edge", M, N, K, alpha, beta, g.sgemm_variant_name(variant))
-        out = gu.run(p, variant=variant)
-        r = gu.ratio_full(p, out)
-        assert r <= TOL, (M, N, K, alpha, beta, g.sgemm_variant_name(variant), r)
+        ref = gu.oracle_full(p)
+        for acc, out in run_all_modes(p, variant):
+            r = gu.ratio_full(p, out, ref)
+            assert r <= TOL, (M, N, K, alpha, beta, g.sgemm_variant_name(variant), acc, r)
 
 
 @pytest.mark.parametrize("variant", all_variants())
@@ -130,18 +167,19 @@ def test_wide_leading_dims_and_misaligned_bases(variant, offsets):
         p = inputs.make_problem(M, N, K, dist="upm1", seed=M + N, alpha=1.25, beta=-0.75,
                                 c_fill="upm1", lda=lda, ldb=ldb, ldc=ldc)
         gu.say("wide-ld", M, N, K, lda, ldb, ldc, offsets, g.sgemm_variant_name(variant))
-        out = gu.run(p, variant=variant, offsets=offsets)
-        assert gu.pad_untouched(p, out)
-        assert gu.ratio_full(p, out) <= TOL
+        ref = gu.oracle_full(p)
+        for acc, out in run_all_modes(p, variant, offsets):
+            assert gu.pad_untouched(p, out), acc
+            assert gu.ratio_full(p, out, ref) <= TOL, acc
 
 
 @pytest.mark.parametrize("variant", all_variants())
 def test_beta_zero_does_not_read_c(variant):
     p = inputs.make_problem(150, 260, 70, dist="normal", seed=11, beta=0.0, c_fill="nan")
     gu.say("beta=0 NaN C", g.sgemm_variant_name(variant))
-    out = gu.run(p, variant=variant)
-    assert np.all(np.isfinite(out))
-    assert gu.ratio_full(p, out) <= TOL
+    for acc, out in run_all_modes(p, variant):
+        assert np.all(np.isfinite(out)), acc
+        assert gu.ratio_full(p, out) <= TOL, acc
 
 
 # ------------------------------------------------------------------ properties
@@ -149,9 +187,10 @@ def test_beta_zero_does_not_read_c(variant):
 def test_deterministic(variant):
     p = cached_problem("ragged_1000x1023x999")
     gu.say("determinism", g.sgemm_variant_name(variant))
-    a = gu.run(p, variant=variant)
-    b = gu.run(p, variant=variant)
-    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    for acc in gu.allowed_accesses(p):
+        a = gu.run(p, variant=variant, access=acc)
+        b = gu.run(p, variant=variant, access=acc)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), acc
 
 
 @pytest.mark.parametrize("variant", all_variants())
@@ -170,6 +209,10 @@ def test_zero_padding_invariance(variant):
     small = gu.run(p, variant=variant)   # N = 301: 32-bit accesses
     large = gu.run(big, variant=variant)  # N = 384: 128-bit accesses, same arithmetic
     assert np.array_equal(small.view(np.uint32), large[:200, :301].copy().view(np.uint32))
+    # every access mode computes the same sums in the same order
+    for acc in gu.allowed_accesses(big):
+        other = gu.run(big, variant=variant, access=acc)
+        assert np.array_equal(other.view(np.uint32), large.view(np.uint32)), acc
 
 
 def test_runs_on_a_side_stream():
@@ -204,3 +247,25 @@ def test_full_size_sampled_valu_path(name):
     out = gu.run(p, path=g.SGEMM_PATH_VALU)
     rows, cols = inputs.sample_points(p.M, p.N, n_random=2048, seed=19)
     assert gu.ratio_points(p, out, rows, cols) <= TOL
+
+
+def test_huge_leading_dimension_takes_checked_accesses():
+    # lda = 2.2M floats: (256 + 1) * lda * 4 bytes is past 2^31, so the
+    # 256-row variant cannot use 31-bit buffer offsets and falls back to the
+    # per-element checked kernel; the forced buffer modes are refused.
+    M, N, K, lda = 8, 64, 64, 2_200_000
+    p = inputs.make_problem(M, N, K, dist="upm1", seed=23, alpha=0.75, beta=0.5, c_fill="upm1",
+                            lda=lda)
+    v = 1
+    assert g.sgemm_variant_tile(v)[1] == 256
+    gu.say("huge lda", lda, g.sgemm_variant_name(v))
+    out = gu.run(p, variant=v)
+    assert gu.ratio_full(p, out) <= TOL
+    oa, _, a = gu.to_gpu(p.A)
+    ob, _, b = gu.to_gpu(p.B)
+    oc, _, c = gu.to_gpu(p.C)
+    for acc in (g.SGEMM_ACCESS_BUFFER_128, g.SGEMM_ACCESS_BUFFER_32):
+        assert g.sgemm_variant_access(v, acc, M, N, K, 0.75, a, lda, b, N, 0.5, c, N,
+                                      check=False) == -23
+    torch.cuda.synchronize()
+    del oa, ob, oc
