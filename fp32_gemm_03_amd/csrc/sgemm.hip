@@ -35,31 +35,33 @@ struct Variant {
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, true>,                       \
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, false>}
 
-#define MFMA_CFG(BM, BN, BK, WM, WN, PA, PB, WPE)                                       \
-    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN, SGEMM_PATH_MFMA, BM, BN, BK,           \
+#define MFMA_CFG(BM, BN, BK, WM, WN, PA, PB, WPE, PD, FD, SUFFIX)                        \
+    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
      (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4, WPE, true>,                       \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, true>,                       \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, false>}
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD>,               \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD>,               \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, false, PD, FD>}
 
 const Variant kVariants[] = {
-    VALU_CFG(128, 128, 16, 8, 8, 4, 0, 4),     // 0
-    MFMA_CFG(256, 256, 32, 128, 128, 4, 0, 1), // 1: 4 waves, 1 per SIMD, 512 registers
-    MFMA_CFG(128, 128, 32, 64, 64, 4, 0, 2),   // 2
-    MFMA_CFG(64, 64, 32, 32, 32, 4, 0, 2),     // 3
-    MFMA_CFG(256, 256, 32, 128, 64, 4, 0, 2),  // 4: 8 waves, 2 per SIMD
-    MFMA_CFG(256, 128, 16, 128, 64, 4, 0, 2),  // 5: 4 waves, 2 workgroups per CU
-    MFMA_CFG(256, 256, 16, 128, 128, 4, 0, 1), // 6
-    MFMA_CFG(128, 256, 16, 64, 128, 4, 0, 2),  // 7: 4 waves, 2 workgroups per CU
-    VALU_CFG(128, 256, 16, 8, 16, 4, 0, 2),    // 8: 8 x 16 per lane
-    VALU_CFG(256, 128, 16, 16, 8, 4, 0, 2),    // 9: 16 x 8 per lane
+    VALU_CFG(128, 128, 16, 8, 8, 4, 0, 4),                     // 0
+    MFMA_CFG(256, 256, 32, 128, 128, 4, 0, 1, 1, 1, ""),       // 1: 4 waves, 1 per SIMD, 512 registers
+    MFMA_CFG(128, 128, 32, 64, 64, 4, 0, 2, 1, 1, ""),         // 2
+    MFMA_CFG(64, 64, 32, 32, 32, 4, 0, 2, 1, 1, ""),           // 3
+    MFMA_CFG(256, 256, 32, 128, 64, 4, 0, 2, 1, 1, ""),        // 4: 8 waves, 2 per SIMD
+    MFMA_CFG(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, ""),        // 5: 4 waves, 2 workgroups per CU
+    MFMA_CFG(128, 256, 16, 64, 128, 4, 0, 2, 1, 1, ""),        // 6: 4 waves, 2 workgroups per CU
+    VALU_CFG(128, 256, 16, 8, 16, 4, 0, 2),                    // 7: 8 x 16 per lane
+    VALU_CFG(256, 128, 16, 16, 8, 4, 0, 2),                    // 8: 16 x 8 per lane
+    MFMA_CFG(64, 64, 32, 32, 32, 4, 0, 2, 2, 3, "_pf2_fd3"),   // 9: 2 K tiles in flight, fragments 3 steps ahead
+    MFMA_CFG(64, 64, 64, 32, 32, 4, 0, 2, 1, 3, "_fd3"),       // 10: fragments 3 steps ahead
+    MFMA_CFG(128, 128, 32, 64, 64, 4, 0, 2, 2, 2, "_pf2_fd2"), // 11
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 constexpr int kValuDefault = 0;
-constexpr int kMfma128x256 = 7;
-constexpr int kMfmaMedium = 2;
-constexpr int kMfmaSmall = 3;
+constexpr int kMfmaLarge = 6;   // 128 x 256 x 16, two workgroups per CU
+constexpr int kMfmaMedium = 9;  // 64 x 64 x 32, two K tiles in flight
+constexpr int kMfmaSmall = 10;  // 64 x 64 x 64, fragments three k-steps ahead
 
 // Compute units of an MI355X; the choice of tile is a pure function of the
 // sizes so that it is the same on every call and testable without a GPU.
@@ -69,19 +71,23 @@ long long tiles(int M, int N, int bm, int bn) {
     return (long long)((M + bm - 1) / bm) * (long long)((N + bn - 1) / bn);
 }
 
-// Measured on MI355X (8192^3, 4096^3, 2048^3, 1024^3, 16384^2 x 128,
-// 1000 x 1023 x 999, 256^3): the 128 x 256 block with two workgroups per CU
-// is fastest once there are at least two blocks per CU (its lanes also store
-// 4 consecutive columns, which matters when the epilogue dominates at small
-// K).  Below that, the largest block that still gives every CU a workgroup
-// wins.
+// Measured on MI355X over every variant (8192^3, 4096^3, 2048^3, 1024^3,
+// 16384^2 x 128, 1000 x 1023 x 999, 256^3):
+//   * at least two 128 x 256 blocks per CU: the 128 x 256 block with two
+//     workgroups per CU is fastest (its lanes also store 4 consecutive
+//     columns, which matters when the epilogue dominates at small K);
+//   * at least one 128 x 128 block per CU: 64 x 64 blocks with two K tiles
+//     in flight (4 workgroups per CU hide each other's latency);
+//   * below that the problem cannot fill the chip and each workgroup's
+//     latency decides: 64 x 64 blocks over BK = 64 with LDS fragments read
+//     three k-steps ahead.
 int select_variant(int path, int M, int N, int K) {
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
     if (path == SGEMM_PATH_VALU) return kValuDefault;
     if (path != SGEMM_PATH_AUTO && path != SGEMM_PATH_MFMA) return SGEMM_ERR_PATH;
-    if (tiles(M, N, 128, 256) >= 2 * kComputeUnits) return kMfma128x256;
+    if (tiles(M, N, 128, 256) >= 2 * kComputeUnits) return kMfmaLarge;
     if (tiles(M, N, 128, 128) >= kComputeUnits) return kMfmaMedium;
     return kMfmaSmall;
 }

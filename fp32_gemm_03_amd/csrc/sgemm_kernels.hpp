@@ -144,7 +144,7 @@ template <> struct buf<4> {
 // Thread tid covers column tid % BK of rows r0 + {0..3} + p * ROWS_PER_PASS,
 // r0 = 4 * (tid / BK), and writes one 128-bit LDS vector per 4 rows.
 // ---------------------------------------------------------------------------
-template <int BM, int BK, int NT, int PADA>
+template <int BM, int BK, int NT, int PADA, int STAGES>
 struct ATileGeom {
     static_assert(BM % 4 == 0, "BM must be a multiple of 4");
     static_assert(NT % BK == 0, "BK must divide the thread count");
@@ -153,19 +153,20 @@ struct ATileGeom {
     static constexpr int PER = BM / ROWS_PER_PASS;
     static constexpr int SA = BM + PADA;
 
-    float4 reg[PER];
+    float4 reg[STAGES][PER];  // register stages: K tiles in flight
 
+    template <int S>
     __device__ __forceinline__ void store(float *As, int tid) const {
         float *dst = As + (tid % BK) * SA + 4 * (tid / BK);
 #pragma unroll
         for (int p = 0; p < PER; ++p)
-            *reinterpret_cast<float4 *>(dst + p * ROWS_PER_PASS) = reg[p];
+            *reinterpret_cast<float4 *>(dst + p * ROWS_PER_PASS) = reg[S][p];
     }
 };
 
-template <int BM, int BK, int NT, int PADA>
-struct ATileBuf : ATileGeom<BM, BK, NT, PADA> {
-    typedef ATileGeom<BM, BK, NT, PADA> G;
+template <int BM, int BK, int NT, int PADA, int STAGES>
+struct ATileBuf : ATileGeom<BM, BK, NT, PADA, STAGES> {
+    typedef ATileGeom<BM, BK, NT, PADA, STAGES> G;
     rsrc_t rsrc;       // rows bm.. of A, up to A's last element
     uint32_t off[4];   // ((r0 + c) * lda + col) * 4
     uint32_t pass;     // ROWS_PER_PASS * lda * 4
@@ -180,6 +181,7 @@ struct ATileBuf : ATileGeom<BM, BK, NT, PADA> {
         rsrc = make_rsrc(a.A + (int64_t)bm * a.lda, ((int64_t)(a.M - bm - 1) * a.lda + a.K) * 4);
     }
 
+    template <int S>
     __device__ __forceinline__ void load(const Args &a, int, int k0) {
         const bool kin = (k0 + col) < a.K;
         uint32_t o[4];
@@ -187,17 +189,17 @@ struct ATileBuf : ATileGeom<BM, BK, NT, PADA> {
         for (int c = 0; c < 4; ++c) o[c] = kin ? off[c] + 4u * (uint32_t)k0 : kOutOfRange;
 #pragma unroll
         for (int p = 0; p < G::PER; ++p) {
-            G::reg[p].x = buf<1>::load(rsrc, o[0] + p * pass);
-            G::reg[p].y = buf<1>::load(rsrc, o[1] + p * pass);
-            G::reg[p].z = buf<1>::load(rsrc, o[2] + p * pass);
-            G::reg[p].w = buf<1>::load(rsrc, o[3] + p * pass);
+            G::reg[S][p].x = buf<1>::load(rsrc, o[0] + p * pass);
+            G::reg[S][p].y = buf<1>::load(rsrc, o[1] + p * pass);
+            G::reg[S][p].z = buf<1>::load(rsrc, o[2] + p * pass);
+            G::reg[S][p].w = buf<1>::load(rsrc, o[3] + p * pass);
         }
     }
 };
 
-template <int BM, int BK, int NT, int PADA>
-struct ATilePtr : ATileGeom<BM, BK, NT, PADA> {
-    typedef ATileGeom<BM, BK, NT, PADA> G;
+template <int BM, int BK, int NT, int PADA, int STAGES>
+struct ATilePtr : ATileGeom<BM, BK, NT, PADA, STAGES> {
+    typedef ATileGeom<BM, BK, NT, PADA, STAGES> G;
     int col, r0;
 
     __device__ __forceinline__ void init(const Args &, int, int tid) {
@@ -205,6 +207,7 @@ struct ATilePtr : ATileGeom<BM, BK, NT, PADA> {
         r0 = 4 * (tid / BK);
     }
 
+    template <int S>
     __device__ __forceinline__ void load(const Args &a, int bm, int k0) {
         const bool kin = (k0 + col) < a.K;
 #pragma unroll
@@ -212,10 +215,10 @@ struct ATilePtr : ATileGeom<BM, BK, NT, PADA> {
             const int row = bm + r0 + p * G::ROWS_PER_PASS;
             const float *q = a.A + (int64_t)row * a.lda + k0 + col;
             const int rl = a.M - row;
-            G::reg[p].x = (kin && rl > 0) ? q[0] : 0.0f;
-            G::reg[p].y = (kin && rl > 1) ? q[a.lda] : 0.0f;
-            G::reg[p].z = (kin && rl > 2) ? q[2 * a.lda] : 0.0f;
-            G::reg[p].w = (kin && rl > 3) ? q[3 * a.lda] : 0.0f;
+            G::reg[S][p].x = (kin && rl > 0) ? q[0] : 0.0f;
+            G::reg[S][p].y = (kin && rl > 1) ? q[a.lda] : 0.0f;
+            G::reg[S][p].z = (kin && rl > 2) ? q[2 * a.lda] : 0.0f;
+            G::reg[S][p].w = (kin && rl > 3) ? q[3 * a.lda] : 0.0f;
         }
     }
 };
@@ -225,7 +228,7 @@ struct ATilePtr : ATileGeom<BM, BK, NT, PADA> {
 // load.  Consecutive threads take consecutive VEC-wide pieces of a row; piece
 // p of a thread sits at tile row k_first + dk(p), tile column n_first + dn(p).
 // ---------------------------------------------------------------------------
-template <int BN, int BK, int NT, int PADB, int VEC>
+template <int BN, int BK, int NT, int PADB, int VEC, int STAGES>
 struct BTileGeom {
     static constexpr int PER_ROW = BN / VEC;
     static_assert(BN % VEC == 0, "BN must be a multiple of VEC");
@@ -236,7 +239,7 @@ struct BTileGeom {
     static constexpr int SB = BN + PADB;
     typedef typename vec_t<VEC>::type V;
 
-    V reg[PER];
+    V reg[STAGES][PER];  // register stages: K tiles in flight
 
     static __device__ __forceinline__ constexpr int dk(int p) {
         return NT % PER_ROW == 0 ? p * (NT / PER_ROW) : (p * NT) / PER_ROW;
@@ -245,17 +248,18 @@ struct BTileGeom {
         return NT % PER_ROW == 0 ? 0 : ((p * NT) % PER_ROW) * VEC;
     }
 
+    template <int S>
     __device__ __forceinline__ void store(float *Bs, int tid) const {
         float *dst = Bs + (tid / PER_ROW) * SB + (tid % PER_ROW) * VEC;
 #pragma unroll
         for (int p = 0; p < PER; ++p)
-            *reinterpret_cast<V *>(dst + dk(p) * SB + dn(p)) = reg[p];
+            *reinterpret_cast<V *>(dst + dk(p) * SB + dn(p)) = reg[S][p];
     }
 };
 
-template <int BN, int BK, int NT, int PADB, int VEC>
-struct BTileBuf : BTileGeom<BN, BK, NT, PADB, VEC> {
-    typedef BTileGeom<BN, BK, NT, PADB, VEC> G;
+template <int BN, int BK, int NT, int PADB, int VEC, int STAGES>
+struct BTileBuf : BTileGeom<BN, BK, NT, PADB, VEC, STAGES> {
+    typedef BTileGeom<BN, BK, NT, PADB, VEC, STAGES> G;
     uint32_t off;  // (k_first * ldb + n_first) * 4
     uint32_t ldb4;
 
@@ -266,6 +270,7 @@ struct BTileBuf : BTileGeom<BN, BK, NT, PADB, VEC> {
         ldb4 = (uint32_t)(a.ldb * 4);
     }
 
+    template <int S>
     __device__ __forceinline__ void load(const Args &a, int bn, int k0) {
         // Rows k0.. of B from column bn, up to B's last element: rows >= K
         // read 0.0.  With VEC == 4, N and ldb are multiples of 4, so no
@@ -274,13 +279,13 @@ struct BTileBuf : BTileGeom<BN, BK, NT, PADB, VEC> {
                                    ((int64_t)(a.K - k0 - 1) * a.ldb + (a.N - bn)) * 4);
 #pragma unroll
         for (int p = 0; p < G::PER; ++p)
-            G::reg[p] = buf<VEC>::load(r, off + G::dk(p) * ldb4 + G::dn(p) * 4);
+            G::reg[S][p] = buf<VEC>::load(r, off + G::dk(p) * ldb4 + G::dn(p) * 4);
     }
 };
 
-template <int BN, int BK, int NT, int PADB, int VEC>
-struct BTilePtr : BTileGeom<BN, BK, NT, PADB, VEC> {
-    typedef BTileGeom<BN, BK, NT, PADB, VEC> G;
+template <int BN, int BK, int NT, int PADB, int VEC, int STAGES>
+struct BTilePtr : BTileGeom<BN, BK, NT, PADB, VEC, STAGES> {
+    typedef BTileGeom<BN, BK, NT, PADB, VEC, STAGES> G;
     int k_first, n_first;
 
     __device__ __forceinline__ void init(const Args &, int, int tid) {
@@ -288,6 +293,7 @@ struct BTilePtr : BTileGeom<BN, BK, NT, PADB, VEC> {
         n_first = (tid % G::PER_ROW) * VEC;
     }
 
+    template <int S>
     __device__ __forceinline__ void load(const Args &a, int bn, int k0) {
 #pragma unroll
         for (int p = 0; p < G::PER; ++p) {
@@ -295,9 +301,9 @@ struct BTilePtr : BTileGeom<BN, BK, NT, PADB, VEC> {
             const int k = k0 + k_first + G::dk(p);
             // VEC == 4 only when N % 4 == 0: a piece is all in or all out
             if (n < a.N && k < a.K)
-                G::reg[p] = *reinterpret_cast<const typename G::V *>(a.B + (int64_t)k * a.ldb + n);
+                G::reg[S][p] = *reinterpret_cast<const typename G::V *>(a.B + (int64_t)k * a.ldb + n);
             else
-                G::reg[p] = typename G::V{};
+                G::reg[S][p] = typename G::V{};
         }
     }
 };
@@ -384,11 +390,12 @@ struct CStorePtr {
     }
 };
 
-template <bool BUF, int BM, int BN, int BK, int NT, int PADA, int PADB, int VEC, int W>
+template <bool BUF, int BM, int BN, int BK, int NT, int PADA, int PADB, int VEC, int W, int STAGES>
 struct Staging {
-    typedef typename std::conditional<BUF, ATileBuf<BM, BK, NT, PADA>, ATilePtr<BM, BK, NT, PADA>>::type TA;
-    typedef typename std::conditional<BUF, BTileBuf<BN, BK, NT, PADB, VEC>,
-                                      BTilePtr<BN, BK, NT, PADB, VEC>>::type TB;
+    typedef typename std::conditional<BUF, ATileBuf<BM, BK, NT, PADA, STAGES>,
+                                      ATilePtr<BM, BK, NT, PADA, STAGES>>::type TA;
+    typedef typename std::conditional<BUF, BTileBuf<BN, BK, NT, PADB, VEC, STAGES>,
+                                      BTilePtr<BN, BK, NT, PADB, VEC, STAGES>>::type TB;
     typedef typename std::conditional<BUF, CStoreBuf<W, VEC>, CStorePtr<W, VEC>>::type TC;
 };
 
@@ -408,7 +415,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
     static_assert(TM % 4 == 0 && TN % 4 == 0, "micro-tile sides must be multiples of 4");
     constexpr int SA = BM + PADA, SB = BN + PADB;
     constexpr int STAGE = BK * (SA + SB);
-    typedef Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, 4> S;
+    typedef Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, 4, 1> S;
     __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
     const int tid = threadIdx.x;
@@ -432,10 +439,10 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
 
     const int KT = (a.K + BK - 1) / BK;
     if (KT > 0) {
-        ta.load(a, bm, 0);
-        tb.load(a, bn, 0);
-        ta.store(smem, tid);
-        tb.store(smem + BK * SA, tid);
+        ta.template load<0>(a, bm, 0);
+        tb.template load<0>(a, bn, 0);
+        ta.template store<0>(smem, tid);
+        tb.template store<0>(smem + BK * SA, tid);
     }
     __syncthreads();
 
@@ -443,8 +450,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
         const float *As = smem + (t & 1) * STAGE;
         const float *Bs = As + BK * SA;
         if (t + 1 < KT) {
-            ta.load(a, bm, (t + 1) * BK);
-            tb.load(a, bn, (t + 1) * BK);
+            ta.template load<0>(a, bm, (t + 1) * BK);
+            tb.template load<0>(a, bn, (t + 1) * BK);
         }
         const float *ap = As + wm + 4 * ly;
         const float *bp = Bs + wn + 4 * lx;
@@ -468,8 +475,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
         }
         if (t + 1 < KT) {
             float *An = smem + ((t + 1) & 1) * STAGE;
-            ta.store(An, tid);
-            tb.store(An + BK * SA, tid);
+            ta.template store<0>(An, tid);
+            tb.template store<0>(An + BK * SA, tid);
         }
         __syncthreads();
     }
@@ -507,7 +514,48 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
 // The fragments of k-step j+1 are read from LDS while the MFMAs of step j
 // issue, so the LDS latency hides behind matrix work.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC, int WPE, bool BUF>
+// One K tile of MFMAs from one LDS stage.  The fragments of k-step j + FD
+// are read while the MFMAs of step j issue, so the LDS latency hides behind
+// FD steps of matrix work (FD > 1 for wave tiles with few MFMAs per step).
+template <int BK, int MI, int NI, int SA, int SB, int FD>
+__device__ __forceinline__ void mfma_tile(const float *ap, const float *bp,
+                                          floatx16 (&acc)[MI][NI]) {
+    typedef typename vec_t<MI>::type VA;
+    typedef typename vec_t<NI>::type VB;
+    constexpr int STEPS = BK / 2;
+    constexpr int RING = FD + 1;
+    VA av[RING];
+    VB bv[RING];
+#pragma unroll
+    for (int f = 0; f < FD && f < STEPS; ++f) {
+        av[f] = *reinterpret_cast<const VA *>(ap + 2 * f * SA);
+        bv[f] = *reinterpret_cast<const VB *>(bp + 2 * f * SB);
+    }
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j) {
+        if (j + FD < STEPS) {
+            av[(j + FD) % RING] = *reinterpret_cast<const VA *>(ap + 2 * (j + FD) * SA);
+            bv[(j + FD) % RING] = *reinterpret_cast<const VB *>(bp + 2 * (j + FD) * SB);
+        }
+        // Keep the early reads above this step's MFMAs: without the fence the
+        // scheduler sinks each read next to its first use and waits on it.
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int jj = 0; jj < NI; ++jj)
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(vget(av[j % RING], i),
+                                                                  vget(bv[j % RING], jj),
+                                                                  acc[i][jj], 0, 0, 0);
+    }
+}
+
+// PD is the prefetch depth: how many K tiles are in flight in registers while
+// one is multiplied from LDS (1, or 2 for shapes whose per-tile arithmetic is
+// too short to cover one global-load latency).  FD is the LDS fragment
+// prefetch distance in k-steps.
+template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC, int WPE, bool BUF,
+          int PD, int FD>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -518,9 +566,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     static_assert(BK % 2 == 0, "BK must be even (K = 2 per instruction)");
     static_assert(MI == 1 || MI == 2 || MI == 4, "MI in {1, 2, 4}");
     static_assert(NI == 1 || NI == 2 || NI == 4, "NI in {1, 2, 4}");
-    typedef typename vec_t<MI>::type VA;
-    typedef typename vec_t<NI>::type VB;
-    typedef Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, NI> S;
+    static_assert(PD == 1 || PD == 2, "prefetch depth 1 or 2");
+    typedef Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, NI, PD> S;
     __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
     const int tid = threadIdx.x;
@@ -544,48 +591,80 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // per-lane fragment bases inside one LDS stage
+    const int a_off = lh * SA + wm + MI * li;
+    const int b_off = BK * SA + lh * SB + wn + NI * li;
     const int KT = (a.K + BK - 1) / BK;
-    if (KT > 0) {
-        ta.load(a, bm, 0);
-        tb.load(a, bn, 0);
-        ta.store(smem, tid);
-        tb.store(smem + BK * SA, tid);
-    }
-    __syncthreads();
 
-    for (int t = 0; t < KT; ++t) {
-        const float *As = smem + (t & 1) * STAGE;
-        const float *Bs = As + BK * SA;
-        if (t + 1 < KT) {
-            ta.load(a, bm, (t + 1) * BK);
-            tb.load(a, bn, (t + 1) * BK);
-        }
-        const float *ap = As + lh * SA + wm + MI * li;
-        const float *bp = Bs + lh * SB + wn + NI * li;
-        VA av[2];
-        VB bv[2];
-        av[0] = *reinterpret_cast<const VA *>(ap);
-        bv[0] = *reinterpret_cast<const VB *>(bp);
-#pragma unroll
-        for (int k = 0; k < BK; k += 2) {
-            const int cur = (k >> 1) & 1;
-            if (k + 2 < BK) {
-                av[cur ^ 1] = *reinterpret_cast<const VA *>(ap + (k + 2) * SA);
-                bv[cur ^ 1] = *reinterpret_cast<const VB *>(bp + (k + 2) * SB);
-            }
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(vget(av[cur], i), vget(bv[cur], j),
-                                                                     acc[i][j], 0, 0, 0);
-        }
-        if (t + 1 < KT) {
-            float *An = smem + ((t + 1) & 1) * STAGE;
-            ta.store(An, tid);
-            tb.store(An + BK * SA, tid);
+    if (PD == 1) {
+        if (KT > 0) {
+            ta.template load<0>(a, bm, 0);
+            tb.template load<0>(a, bn, 0);
+            ta.template store<0>(smem, tid);
+            tb.template store<0>(smem + BK * SA, tid);
         }
         __syncthreads();
+        for (int t = 0; t < KT; ++t) {
+            const float *st = smem + (t & 1) * STAGE;
+            if (t + 1 < KT) {
+                ta.template load<0>(a, bm, (t + 1) * BK);
+                tb.template load<0>(a, bn, (t + 1) * BK);
+            }
+            mfma_tile<BK, MI, NI, SA, SB, FD>(st + a_off, st + b_off, acc);
+            if (t + 1 < KT) {
+                float *nx = smem + ((t + 1) & 1) * STAGE;
+                ta.template store<0>(nx, tid);
+                tb.template store<0>(nx + BK * SA, tid);
+            }
+            __syncthreads();
+        }
+    } else {
+        // Register stage s holds K tile t with t % 2 == s once issued; tile t
+        // is issued two tiles ahead of its LDS store.  The loop runs two tiles
+        // per trip so that every register index is a constant.
+        constexpr int R = PD - 1;  // the second register stage (1)
+        if (KT > 0) {
+            ta.template load<0>(a, bm, 0);
+            tb.template load<0>(a, bn, 0);
+        }
+        if (KT > 1) {
+            ta.template load<R>(a, bm, BK);
+            tb.template load<R>(a, bn, BK);
+        }
+        if (KT > 0) {
+            ta.template store<0>(smem, tid);
+            tb.template store<0>(smem + BK * SA, tid);
+        }
+        __syncthreads();
+        if (KT > 2) {
+            ta.template load<0>(a, bm, 2 * BK);
+            tb.template load<0>(a, bn, 2 * BK);
+        }
+        for (int t = 0; t < KT; t += 2) {
+            // tile t from LDS stage 0; tile t+1 (register stage 1) -> LDS stage 1
+            mfma_tile<BK, MI, NI, SA, SB, FD>(smem + a_off, smem + b_off, acc);
+            if (t + 1 < KT) {
+                ta.template store<R>(smem + STAGE, tid);
+                tb.template store<R>(smem + STAGE + BK * SA, tid);
+            }
+            __syncthreads();
+            if (t + 1 >= KT) break;
+            if (t + 3 < KT) {
+                ta.template load<R>(a, bm, (t + 3) * BK);
+                tb.template load<R>(a, bn, (t + 3) * BK);
+            }
+            // tile t+1 from LDS stage 1; tile t+2 (register stage 0) -> LDS stage 0
+            mfma_tile<BK, MI, NI, SA, SB, FD>(smem + STAGE + a_off, smem + STAGE + b_off, acc);
+            if (t + 2 < KT) {
+                ta.template store<0>(smem, tid);
+                tb.template store<0>(smem + BK * SA, tid);
+            }
+            __syncthreads();
+            if (t + 4 < KT) {
+                ta.template load<0>(a, bm, (t + 4) * BK);
+                tb.template load<0>(a, bn, (t + 4) * BK);
+            }
+        }
     }
 
     typename S::TC st;
