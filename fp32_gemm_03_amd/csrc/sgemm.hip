@@ -35,26 +35,28 @@ struct Variant {
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, true>,                       \
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, false>}
 
-#define MFMA_CFG(BM, BN, BK, WM, WN, PA, PB, WPE, PD, FD, SUFFIX)                        \
+#define MFMA_CFG(BM, BN, BK, WM, WN, PA, PB, WPE, PD, FD, ORD, SUFFIX)                   \
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
      (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD>,               \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD>,               \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, false, PD, FD>}
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD, ORD>,          \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD, ORD>,          \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, false, PD, FD, ORD>}
 
 const Variant kVariants[] = {
     VALU_CFG(128, 128, 16, 8, 8, 4, 0, 4),                     // 0
-    MFMA_CFG(256, 256, 32, 128, 128, 4, 0, 1, 1, 1, ""),       // 1: 4 waves, 1 per SIMD, 512 registers
-    MFMA_CFG(128, 128, 32, 64, 64, 4, 0, 2, 1, 1, ""),         // 2
-    MFMA_CFG(64, 64, 32, 32, 32, 4, 0, 2, 1, 1, ""),           // 3
-    MFMA_CFG(256, 256, 32, 128, 64, 4, 0, 2, 1, 1, ""),        // 4: 8 waves, 2 per SIMD
-    MFMA_CFG(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, ""),        // 5: 4 waves, 2 workgroups per CU
-    MFMA_CFG(128, 256, 16, 64, 128, 4, 0, 2, 1, 1, ""),        // 6: 4 waves, 2 workgroups per CU
+    MFMA_CFG(256, 256, 32, 128, 128, 4, 0, 1, 1, 1, 0, ""),       // 1: 4 waves, 1 per SIMD, 512 registers
+    MFMA_CFG(128, 128, 32, 64, 64, 4, 0, 2, 1, 1, 0, ""),         // 2
+    MFMA_CFG(64, 64, 32, 32, 32, 4, 0, 2, 1, 1, 0, ""),           // 3
+    MFMA_CFG(256, 256, 32, 128, 64, 4, 0, 2, 1, 1, 0, ""),        // 4: 8 waves, 2 per SIMD
+    MFMA_CFG(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, 0, ""),        // 5: 4 waves, 2 workgroups per CU
+    MFMA_CFG(128, 256, 16, 64, 128, 4, 0, 2, 1, 1, 0, ""),        // 6: 4 waves, 2 workgroups per CU
     VALU_CFG(128, 256, 16, 8, 16, 4, 0, 2),                    // 7: 8 x 16 per lane
     VALU_CFG(256, 128, 16, 16, 8, 4, 0, 2),                    // 8: 16 x 8 per lane
-    MFMA_CFG(64, 64, 32, 32, 32, 4, 0, 2, 2, 3, "_pf2_fd3"),   // 9: 2 K tiles in flight, fragments 3 steps ahead
-    MFMA_CFG(64, 64, 64, 32, 32, 4, 0, 2, 1, 3, "_fd3"),       // 10: fragments 3 steps ahead
-    MFMA_CFG(128, 128, 32, 64, 64, 4, 0, 2, 2, 2, "_pf2_fd2"), // 11
+    MFMA_CFG(64, 64, 32, 32, 32, 4, 0, 2, 2, 3, 0, "_pf2_fd3"),   // 9: 2 K tiles in flight, fragments 3 steps ahead
+    MFMA_CFG(64, 64, 64, 32, 32, 4, 0, 2, 1, 3, 0, "_fd3"),       // 10: fragments 3 steps ahead
+    MFMA_CFG(128, 128, 32, 64, 64, 4, 0, 2, 2, 2, 0, "_pf2_fd2"), // 11
+    MFMA_CFG(128, 256, 16, 64, 128, 4, 0, 2, 1, 1, 1, "_xcd"),    // 12: 6 in XCD-grouped tile order
+    MFMA_CFG(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, 1, "_xcd"),    // 13: 5 in XCD-grouped tile order
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 

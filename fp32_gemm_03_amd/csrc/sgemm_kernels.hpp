@@ -514,6 +514,35 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
 // The fragments of k-step j+1 are read from LDS while the MFMAs of step j
 // issue, so the LDS latency hides behind matrix work.
 // ---------------------------------------------------------------------------
+// Workgroup -> C tile.  ORDER 0: row-major over tiles, the M index slow
+// ("如何高效实现矩阵乘", section "Wave & L2 cache Hit Rate").  ORDER 1: the
+// same tiles, assigned so that each XCD works on a compact patch.  MI355X
+// hands consecutive workgroup ids to its 8 XCDs in turn (id % 8), and each
+// XCD has its own L2; the id is first renumbered so that every XCD receives
+// a contiguous run of the tile sequence, and the sequence then walks groups
+// of GROUP_M tile rows column by column, so the workgroups an XCD runs at
+// once share GROUP_M row blocks of A and a few column blocks of B.
+template <int ORDER, int GROUP_M>
+__device__ __forceinline__ void tile_of(int pid, int nbm, int nbn, int &tm, int &tn) {
+    if (ORDER == 0) {
+        tm = pid / nbn;
+        tn = pid % nbn;
+        return;
+    }
+    const int total = nbm * nbn;
+    const int q = total / 8, r = total % 8;
+    const int xcd = pid % 8, idx = pid / 8;
+    // XCD x received ids x, x + 8, ...: q + (x < r) of them
+    const int seq = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
+    const int per_group = GROUP_M * nbn;
+    const int group = seq / per_group;
+    const int first_m = group * GROUP_M;
+    const int rows = min(nbm - first_m, GROUP_M);
+    const int in_group = seq - group * per_group;
+    tm = first_m + in_group % rows;
+    tn = in_group / rows;
+}
+
 // One K tile of MFMAs from one LDS stage.  The fragments of k-step j + FD
 // are read while the MFMAs of step j issue, so the LDS latency hides behind
 // FD steps of matrix work (FD > 1 for wave tiles with few MFMAs per step).
@@ -555,7 +584,7 @@ __device__ __forceinline__ void mfma_tile(const float *ap, const float *bp,
 // too short to cover one global-load latency).  FD is the LDS fragment
 // prefetch distance in k-steps.
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC, int WPE, bool BUF,
-          int PD, int FD>
+          int PD, int FD, int ORDER>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -572,9 +601,10 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int nbn = (a.N + BN - 1) / BN;
-    const int bm = (int)(blockIdx.x / nbn) * BM;
-    const int bn = (int)(blockIdx.x % nbn) * BN;
+    const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
+    int tm, tn;
+    tile_of<ORDER, 8>((int)blockIdx.x, nbm, nbn, tm, tn);
+    const int bm = tm * BM, bn = tn * BN;
     const int wm = (wave / WAVES_N) * WM, wn = (wave % WAVES_N) * WN;
     const int li = lane & 31, lh = lane >> 5;
 
