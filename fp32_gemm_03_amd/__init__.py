@@ -22,6 +22,8 @@ __all__ = [
     "SGEMM_PATH_AUTO", "SGEMM_PATH_VALU", "SGEMM_PATH_MFMA",
     "SGEMM_ACCESS_AUTO", "SGEMM_ACCESS_BUFFER_128", "SGEMM_ACCESS_BUFFER_32",
     "SGEMM_ACCESS_CHECKED", "sgemm_variant_access",
+    "sgemm_ws", "sgemm_workspace_size", "sgemm_select_splits", "sgemm_splitk",
+    "sgemm_splitk_workspace_size",
     "SgemmError", "LibraryNotBuilt", "library_path", "load_library",
     "sgemm", "sgemm_path", "sgemm_variant", "sgemm_variant_count",
     "sgemm_variant_name", "sgemm_variant_path", "sgemm_variant_tile",
@@ -79,6 +81,17 @@ def load_library():
         lib.sgemm_variant.restype = i
         lib.sgemm_variant_access.argtypes = [i, i] + gemm_args
         lib.sgemm_variant_access.restype = i
+        ws_args = [i, i, i, f, vp, i, vp, i, f, vp, i, vp, ctypes.c_size_t, vp]
+        lib.sgemm_ws.argtypes = ws_args
+        lib.sgemm_ws.restype = i
+        lib.sgemm_splitk.argtypes = [i, i] + ws_args
+        lib.sgemm_splitk.restype = i
+        lib.sgemm_workspace_size.argtypes = [i, i, i]
+        lib.sgemm_workspace_size.restype = ctypes.c_size_t
+        lib.sgemm_select_splits.argtypes = [i, i, i]
+        lib.sgemm_select_splits.restype = i
+        lib.sgemm_splitk_workspace_size.argtypes = [i, i, i, i]
+        lib.sgemm_splitk_workspace_size.restype = ctypes.c_size_t
         lib.sgemm_variant_count.argtypes = []
         lib.sgemm_variant_count.restype = i
         lib.sgemm_variant_name.argtypes = [i]
@@ -156,6 +169,47 @@ def sgemm_variant_access(variant, access, M, N, K, alpha, A, lda, B, ldb, beta, 
                                          *_gemm_args(M, N, K, alpha, A, lda, B, ldb, beta, C,
                                                      ldc, stream)),
                 "sgemm_variant_access", check)
+
+
+def _ws_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_bytes, stream):
+    ws = _ptr(workspace)
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (int(M), int(N), int(K), float(alpha), _ptr(A), int(lda), _ptr(B), int(ldb),
+            float(beta), _ptr(C), int(ldc), ws, int(workspace_bytes), _stream(stream))
+
+
+def sgemm_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace=None, workspace_bytes=None,
+             stream=None, check=True):
+    """sgemm() that may split K over ``workspace`` (a GPU tensor, zeroed before first use)."""
+    lib = load_library()
+    return _ret(lib.sgemm_ws(*_ws_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                                       workspace_bytes, stream)), "sgemm_ws", check)
+
+
+def sgemm_splitk(variant, splits, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace=None,
+                 workspace_bytes=None, stream=None, check=True):
+    lib = load_library()
+    return _ret(lib.sgemm_splitk(int(variant), int(splits),
+                                 *_ws_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                                           workspace_bytes, stream)), "sgemm_splitk", check)
+
+
+def sgemm_workspace_size(M, N, K) -> int:
+    return int(load_library().sgemm_workspace_size(int(M), int(N), int(K)))
+
+
+def sgemm_select_splits(M, N, K) -> int:
+    return int(load_library().sgemm_select_splits(int(M), int(N), int(K)))
+
+
+def sgemm_splitk_workspace_size(variant, splits, M, N) -> int:
+    return int(load_library().sgemm_splitk_workspace_size(int(variant), int(splits), int(M), int(N)))
+
+
+def variant_has_splitk(variant) -> bool:
+    """True when the variant has a split-K build (workspace size > 0 for 2 splits)."""
+    return sgemm_splitk_workspace_size(variant, 2, 64, 64) > 0
 
 
 def sgemm_variant_count() -> int:

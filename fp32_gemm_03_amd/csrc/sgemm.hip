@@ -25,6 +25,8 @@ struct Variant {
     KernelFn vec4;      // buffer accesses; B, C and their leading dimensions 16-byte friendly
     KernelFn vec1;      // buffer accesses, 32-bit
     KernelFn generic;   // per-element checked pointer accesses (any leading dimension)
+    KernelFn split4;    // split-K, as vec4 (nullptr: no split-K build of this variant)
+    KernelFn split1;    // split-K, as vec1
 };
 
 // VALU: 128 x 128 x 16 block, 4 waves of 64 x 64, 8 x 8 per lane.
@@ -33,27 +35,41 @@ struct Variant {
      (BM / (8 * TM)) * (BN / (8 * TN)) * 64,                                             \
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 4, WPE, true>,                       \
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, true>,                       \
-     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, false>}
+     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, false>, nullptr, nullptr}
+
+#define MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, VEC, WPE, BUF, PD, FD, ORD, SPLIT)          \
+    sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, VEC, WPE, BUF, PD, FD, ORD, SPLIT>
 
 #define MFMA_CFG(BM, BN, BK, WM, WN, PA, PB, WPE, PD, FD, ORD, SUFFIX)                   \
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
      (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD, ORD>,          \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD, ORD>,          \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, false, PD, FD, ORD>}
+     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD, ORD, false),          \
+     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD, ORD, false),          \
+     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 1, WPE, false, PD, FD, ORD, false),         \
+     nullptr, nullptr}
+
+// The same, also compiled with split-K.
+#define MFMA_CFG_SPLIT(BM, BN, BK, WM, WN, PA, PB, WPE, PD, FD, ORD, SUFFIX)             \
+    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
+     (BM / WM) * (BN / WN) * 64,                                                         \
+     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD, ORD, false),          \
+     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD, ORD, false),          \
+     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 1, WPE, false, PD, FD, ORD, false),         \
+     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD, ORD, true),           \
+     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD, ORD, true)}
 
 const Variant kVariants[] = {
     VALU_CFG(128, 128, 16, 8, 8, 4, 0, 4),                     // 0
     MFMA_CFG(256, 256, 32, 128, 128, 4, 0, 1, 1, 1, 0, ""),       // 1: 4 waves, 1 per SIMD, 512 registers
-    MFMA_CFG(128, 128, 32, 64, 64, 4, 0, 2, 1, 1, 0, ""),         // 2
-    MFMA_CFG(64, 64, 32, 32, 32, 4, 0, 2, 1, 1, 0, ""),           // 3
+    MFMA_CFG_SPLIT(128, 128, 32, 64, 64, 4, 0, 2, 1, 1, 0, ""),   // 2
+    MFMA_CFG_SPLIT(64, 64, 32, 32, 32, 4, 0, 2, 1, 1, 0, ""),     // 3
     MFMA_CFG(256, 256, 32, 128, 64, 4, 0, 2, 1, 1, 0, ""),        // 4: 8 waves, 2 per SIMD
     MFMA_CFG(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, 0, ""),        // 5: 4 waves, 2 workgroups per CU
     MFMA_CFG(128, 256, 16, 64, 128, 4, 0, 2, 1, 1, 0, ""),        // 6: 4 waves, 2 workgroups per CU
     VALU_CFG(128, 256, 16, 8, 16, 4, 0, 2),                    // 7: 8 x 16 per lane
     VALU_CFG(256, 128, 16, 16, 8, 4, 0, 2),                    // 8: 16 x 8 per lane
-    MFMA_CFG(64, 64, 32, 32, 32, 4, 0, 2, 2, 3, 0, "_pf2_fd3"),   // 9: 2 K tiles in flight, fragments 3 steps ahead
-    MFMA_CFG(64, 64, 64, 32, 32, 4, 0, 2, 1, 3, 0, "_fd3"),       // 10: fragments 3 steps ahead
+    MFMA_CFG_SPLIT(64, 64, 32, 32, 32, 4, 0, 2, 2, 3, 0, "_pf2_fd3"), // 9: 2 K tiles in flight, fragments 3 steps ahead
+    MFMA_CFG_SPLIT(64, 64, 64, 32, 32, 4, 0, 2, 1, 3, 0, "_fd3"),     // 10: fragments 3 steps ahead
     MFMA_CFG(128, 128, 32, 64, 64, 4, 0, 2, 2, 2, 0, "_pf2_fd2"), // 11
     MFMA_CFG(128, 256, 16, 64, 128, 4, 0, 2, 1, 1, 1, "_xcd"),    // 12: 6 in XCD-grouped tile order
     MFMA_CFG(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, 1, "_xcd"),    // 13: 5 in XCD-grouped tile order
@@ -68,6 +84,7 @@ constexpr int kMfmaSmall = 10;  // 64 x 64 x 64, fragments three k-steps ahead
 // Compute units of an MI355X; the choice of tile is a pure function of the
 // sizes so that it is the same on every call and testable without a GPU.
 constexpr long long kComputeUnits = 256;
+constexpr int kMaxSplits = 64;
 
 long long tiles(int M, int N, int bm, int bn) {
     return (long long)((M + bm - 1) / bm) * (long long)((N + bn - 1) / bn);
@@ -94,6 +111,25 @@ int select_variant(int path, int M, int N, int K) {
     return kMfmaSmall;
 }
 
+// Split count for a variant when a workspace is available (measured on
+// MI355X with the 64 x 64 x 64 block: 512 x 512 x 8192 runs 3.7x faster in 8
+// parts, 1024 x 1024 x 4096 10% faster in 2, while 1024^3 and smaller lose):
+// split only when the tiles alone leave CUs idle, into enough parts for
+// about two workgroups per CU, keeping at least 16 K tiles per part so the
+// per-workgroup prologue and the extra pass over the partials stay small.
+int select_splits(int variant, int M, int N, int K) {
+    if (M <= 0 || N <= 0 || K <= 0) return 1;
+    const Variant &v = kVariants[variant];
+    if (v.split4 == nullptr) return 1;
+    const long long t = tiles(M, N, v.bm, v.bn);
+    if (t > kComputeUnits) return 1;
+    const long long kt = (K + v.bk - 1) / v.bk;
+    long long s = 2 * kComputeUnits / t;
+    if (s > kt / 16) s = kt / 16;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 2 ? 1 : (int)s;
+}
+
 int check_args(int M, int N, int K, float alpha, const float *A, int lda,
                const float *B, int ldb, const float *C, int ldc) {
     if (M < 0) return -1;
@@ -111,19 +147,30 @@ int check_args(int M, int N, int K, float alpha, const float *A, int lda,
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-int launch(int variant, int access, int M, int N, int K, float alpha, const float *A,
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace of a split-K launch: the partial tiles, float [tile][split][bm*bn].
+size_t splitk_bytes(const Variant &v, int splits, int M, int N) {
+    return round_up((size_t)splits * (size_t)tiles(M, N, v.bm, v.bn) * v.bm * v.bn * 4, 256);
+}
+
+int launch(int variant, int access, int splits, void *workspace, size_t workspace_bytes,
+           int M, int N, int K, float alpha, const float *A,
            int lda, const float *B, int ldb, float beta, float *C, int ldc,
            hipStream_t stream) {
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     if (variant < 0 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
     if (access < SGEMM_ACCESS_AUTO || access > SGEMM_ACCESS_CHECKED) return SGEMM_ERR_ACCESS;
+    if (splits < 1 || splits > kMaxSplits) return SGEMM_ERR_SPLITS;
+    if (splits > 1 && kVariants[variant].split4 == nullptr) return SGEMM_ERR_SPLITS;
     if (M == 0 || N == 0) return SGEMM_OK;
     const bool no_product = alpha == 0.0f || K == 0;
     if (no_product && beta == 1.0f) return SGEMM_OK;
 
     const Variant &v = kVariants[variant];
-    const long long grid = tiles(M, N, v.bm, v.bn);
+    if (no_product) splits = 1;  // C = beta * C needs no K split
+    const long long grid = tiles(M, N, v.bm, v.bn) * splits;
     if (grid > INT_MAX) return SGEMM_ERR_TOO_LARGE;
 
     Args a;
@@ -138,6 +185,9 @@ int launch(int variant, int access, int M, int N, int K, float alpha, const floa
     a.lda = lda;
     a.ldb = ldb;
     a.ldc = ldc;
+    a.splits = 1;
+    a.partial = nullptr;
+    a.phase = 0;
     // Buffer accesses form byte offsets inside one block tile in 31 bits.
     const long long lim = 1LL << 31;
     const bool buf_ok = (long long)(v.bm + 1) * lda * 4 < lim &&
@@ -165,10 +215,26 @@ int launch(int variant, int access, int M, int N, int K, float alpha, const floa
             fn = !buf_ok ? v.generic : (vec4 ? v.vec4 : v.vec1);
             break;
     }
+    if (splits > 1) {
+        // split-K kernels exist for buffer accesses only
+        if (fn == v.generic) return SGEMM_ERR_ACCESS;
+        const size_t need = splitk_bytes(v, splits, M, N);
+        if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+            return SGEMM_ERR_WORKSPACE;
+        fn = fn == v.vec4 ? v.split4 : v.split1;
+        a.splits = splits;
+        a.partial = static_cast<float *>(workspace);
+    }
 
     (void)hipGetLastError();  // drop any stale error so the code below is this launch's
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(v.threads), 0, stream, a);
-    const hipError_t err = hipGetLastError();
+    hipError_t err = hipGetLastError();
+    if (err == hipSuccess && splits > 1) {
+        // phase 1 on the same stream: it starts after every partial is written
+        a.phase = 1;
+        hipLaunchKernelGGL(fn, dim3((unsigned)(grid / splits)), dim3(v.threads), 0, stream, a);
+        err = hipGetLastError();
+    }
     return err == hipSuccess ? SGEMM_OK : (int)err;
 }
 
@@ -189,19 +255,61 @@ int sgemm_path(int path, int M, int N, int K, float alpha, const float *A,
     if (rc != SGEMM_OK) return rc;
     const int v = select_variant(path, M, N, K);
     if (v < 0) return v;
-    return launch(v, SGEMM_ACCESS_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return launch(v, SGEMM_ACCESS_AUTO, 1, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int sgemm_variant(int variant, int M, int N, int K, float alpha,
                   const float *A, int lda, const float *B, int ldb, float beta,
                   float *C, int ldc, hipStream_t stream) {
-    return launch(variant, SGEMM_ACCESS_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return launch(variant, SGEMM_ACCESS_AUTO, 1, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int sgemm_variant_access(int variant, int access, int M, int N, int K, float alpha,
                          const float *A, int lda, const float *B, int ldb, float beta,
                          float *C, int ldc, hipStream_t stream) {
-    return launch(variant, access, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return launch(variant, access, 1, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+int sgemm_splitk(int variant, int splits, int M, int N, int K, float alpha,
+                 const float *A, int lda, const float *B, int ldb, float beta,
+                 float *C, int ldc, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+    return launch(variant, SGEMM_ACCESS_AUTO, splits, workspace, workspace_bytes, M, N, K, alpha,
+                  A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+size_t sgemm_splitk_workspace_size(int variant, int splits, int M, int N) {
+    if (variant < 0 || variant >= kNumVariants || splits < 1 || splits > kMaxSplits || M < 0 ||
+        N < 0)
+        return 0;
+    if (splits == 1 || M == 0 || N == 0 || kVariants[variant].split4 == nullptr) return 0;
+    return splitk_bytes(kVariants[variant], splits, M, N);
+}
+
+int sgemm_select_splits(int M, int N, int K) {
+    const int v = select_variant(SGEMM_PATH_AUTO, M, N, K);
+    return v < 0 ? v : select_splits(v, M, N, K);
+}
+
+size_t sgemm_workspace_size(int M, int N, int K) {
+    const int v = select_variant(SGEMM_PATH_AUTO, M, N, K);
+    if (v < 0) return 0;
+    const int sp = select_splits(v, M, N, K);
+    return sp > 1 ? splitk_bytes(kVariants[v], sp, M, N) : 0;
+}
+
+int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+             int ldb, float beta, float *C, int ldc, void *workspace, size_t workspace_bytes,
+             hipStream_t stream) {
+    const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (rc != SGEMM_OK) return rc;
+    const int v = select_variant(SGEMM_PATH_AUTO, M, N, K);
+    if (v < 0) return v;
+    int sp = select_splits(v, M, N, K);
+    if (sp > 1 && (workspace == nullptr || workspace_bytes < splitk_bytes(kVariants[v], sp, M, N)))
+        sp = 1;  // not enough workspace: the unsplit kernel
+    return launch(v, SGEMM_ACCESS_AUTO, sp, workspace, workspace_bytes, M, N, K, alpha, A, lda, B,
+                  ldb, beta, C, ldc, stream);
 }
 
 int sgemm_variant_count(void) { return kNumVariants; }
@@ -243,6 +351,8 @@ const char *sgemm_status_string(int status) {
         case SGEMM_ERR_VARIANT: return "invalid argument: unknown variant";
         case SGEMM_ERR_TOO_LARGE: return "problem too large: tile grid exceeds one launch";
         case SGEMM_ERR_ACCESS: return "invalid argument: access mode unknown or not possible for these arguments";
+        case SGEMM_ERR_WORKSPACE: return "invalid argument: workspace missing, too small or not 256-byte aligned";
+        case SGEMM_ERR_SPLITS: return "invalid argument: split count out of range or variant without split-K";
         default: break;
     }
     if (status > 0) return hipGetErrorString((hipError_t)status);

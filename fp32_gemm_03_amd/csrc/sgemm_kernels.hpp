@@ -67,6 +67,11 @@ struct Args {
     const float *B;
     float *C;
     int64_t lda, ldb, ldc;
+    // split-K only: number of K ranges, partial tiles [tile][split][BM*BN],
+    // and the launch's phase (0: write partials, 1: sum them and store C)
+    int splits;
+    float *partial;
+    int phase;
 };
 
 template <int W> struct vec_t;
@@ -579,12 +584,33 @@ __device__ __forceinline__ void mfma_tile(const float *ap, const float *bp,
     }
 }
 
+// Epilogue of a wave's MI x NI accumulator blocks: register r of block
+// (mi, ni) on lane (li, lh) is tile row wm + MI*(8*(r/4) + 4*lh + r%4) + mi,
+// tile column wn + NI*li + ni.
+template <class S, int MI, int NI>
+__device__ __forceinline__ void epilogue_mfma(const Args &a, int bm, int bn, int wm, int wn, int li,
+                                              int lh, const floatx16 (&acc)[MI][NI]) {
+    typename S::TC st;
+    st.init(a, bm, bn);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int ib = 8 * (r >> 2) + 4 * lh + (r & 3);
+            float v[NI];
+#pragma unroll
+            for (int j = 0; j < NI; ++j) v[j] = acc[i][j][r];
+            st(a, wm + MI * ib + i, wn + NI * li, v);
+        }
+    }
+}
+
 // PD is the prefetch depth: how many K tiles are in flight in registers while
 // one is multiplied from LDS (1, or 2 for shapes whose per-tile arithmetic is
 // too short to cover one global-load latency).  FD is the LDS fragment
 // prefetch distance in k-steps.
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC, int WPE, bool BUF,
-          int PD, int FD, int ORDER>
+          int PD, int FD, int ORDER, bool SPLIT>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -602,8 +628,12 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
+    // split-K: workgroup id = split * tiles + tile
+    const int ntiles = nbm * nbn;
+    const int split = SPLIT && a.phase == 0 ? (int)blockIdx.x / ntiles : 0;
+    const int tile = SPLIT ? (int)blockIdx.x - split * ntiles : (int)blockIdx.x;
     int tm, tn;
-    tile_of<ORDER, 8>((int)blockIdx.x, nbm, nbn, tm, tn);
+    tile_of<ORDER, 8>(tile, nbm, nbn, tm, tn);
     const int bm = tm * BM, bn = tn * BN;
     const int wm = (wave / WAVES_N) * WM, wn = (wave % WAVES_N) * WN;
     const int li = lane & 31, lh = lane >> 5;
@@ -621,15 +651,43 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    if (SPLIT && a.phase == 1) {
+        // Split-K, phase 1 (one workgroup per tile, after every phase-0
+        // workgroup has finished): sum the partials in split order 0, 1, ...
+        // so the result does not depend on timing, then the usual epilogue.
+        for (int sp = 0; sp < a.splits; ++sp) {
+            const float4 *src = reinterpret_cast<const float4 *>(
+                a.partial + ((int64_t)tile * a.splits + sp) * (BM * BN));
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 v = src[((i * NI + j) * 4 + q) * NT + tid];
+                        acc[i][j][4 * q] += v.x;
+                        acc[i][j][4 * q + 1] += v.y;
+                        acc[i][j][4 * q + 2] += v.z;
+                        acc[i][j][4 * q + 3] += v.w;
+                    }
+        }
+        epilogue_mfma<S, MI, NI>(a, bm, bn, wm, wn, li, lh, acc);
+        return;
+    }
+
     // per-lane fragment bases inside one LDS stage
     const int a_off = lh * SA + wm + MI * li;
     const int b_off = BK * SA + lh * SB + wn + NI * li;
-    const int KT = (a.K + BK - 1) / BK;
+    // K tiles [kt0, kt0 + KT): all of K, or this split's share of it
+    const int KT_ALL = (a.K + BK - 1) / BK;
+    const int kt0 = SPLIT ? (int)((int64_t)KT_ALL * split / a.splits) : 0;
+    const int KT = SPLIT ? (int)((int64_t)KT_ALL * (split + 1) / a.splits) - kt0 : KT_ALL;
+    const int kb = kt0 * BK;
 
     if (PD == 1) {
         if (KT > 0) {
-            ta.template load<0>(a, bm, 0);
-            tb.template load<0>(a, bn, 0);
+            ta.template load<0>(a, bm, kb);
+            tb.template load<0>(a, bn, kb);
             ta.template store<0>(smem, tid);
             tb.template store<0>(smem + BK * SA, tid);
         }
@@ -637,8 +695,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         for (int t = 0; t < KT; ++t) {
             const float *st = smem + (t & 1) * STAGE;
             if (t + 1 < KT) {
-                ta.template load<0>(a, bm, (t + 1) * BK);
-                tb.template load<0>(a, bn, (t + 1) * BK);
+                ta.template load<0>(a, bm, kb + (t + 1) * BK);
+                tb.template load<0>(a, bn, kb + (t + 1) * BK);
             }
             mfma_tile<BK, MI, NI, SA, SB, FD>(st + a_off, st + b_off, acc);
             if (t + 1 < KT) {
@@ -654,12 +712,12 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         // per trip so that every register index is a constant.
         constexpr int R = PD - 1;  // the second register stage (1)
         if (KT > 0) {
-            ta.template load<0>(a, bm, 0);
-            tb.template load<0>(a, bn, 0);
+            ta.template load<0>(a, bm, kb);
+            tb.template load<0>(a, bn, kb);
         }
         if (KT > 1) {
-            ta.template load<R>(a, bm, BK);
-            tb.template load<R>(a, bn, BK);
+            ta.template load<R>(a, bm, kb + BK);
+            tb.template load<R>(a, bn, kb + BK);
         }
         if (KT > 0) {
             ta.template store<0>(smem, tid);
@@ -667,8 +725,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         }
         __syncthreads();
         if (KT > 2) {
-            ta.template load<0>(a, bm, 2 * BK);
-            tb.template load<0>(a, bn, 2 * BK);
+            ta.template load<0>(a, bm, kb + 2 * BK);
+            tb.template load<0>(a, bn, kb + 2 * BK);
         }
         for (int t = 0; t < KT; t += 2) {
             // tile t from LDS stage 0; tile t+1 (register stage 1) -> LDS stage 1
@@ -680,8 +738,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
             __syncthreads();
             if (t + 1 >= KT) break;
             if (t + 3 < KT) {
-                ta.template load<R>(a, bm, (t + 3) * BK);
-                tb.template load<R>(a, bn, (t + 3) * BK);
+                ta.template load<R>(a, bm, kb + (t + 3) * BK);
+                tb.template load<R>(a, bn, kb + (t + 3) * BK);
             }
             // tile t+1 from LDS stage 1; tile t+2 (register stage 0) -> LDS stage 0
             mfma_tile<BK, MI, NI, SA, SB, FD>(smem + STAGE + a_off, smem + STAGE + b_off, acc);
@@ -691,25 +749,29 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
             }
             __syncthreads();
             if (t + 4 < KT) {
-                ta.template load<0>(a, bm, (t + 4) * BK);
-                tb.template load<0>(a, bn, (t + 4) * BK);
+                ta.template load<0>(a, bm, kb + (t + 4) * BK);
+                tb.template load<0>(a, bn, kb + (t + 4) * BK);
             }
         }
     }
 
-    typename S::TC st;
-    st.init(a, bm, bn);
+    if (SPLIT) {
+        // Split-K, phase 0: store this split's partial tile in the lanes'
+        // own order (4-float chunks, consecutive threads adjacent).
+        float4 *mine = reinterpret_cast<float4 *>(a.partial + ((int64_t)tile * a.splits + split) * (BM * BN));
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int ib = 8 * (r >> 2) + 4 * lh + (r & 3);
-            float v[NI];
+            for (int j = 0; j < NI; ++j)
 #pragma unroll
-            for (int j = 0; j < NI; ++j) v[j] = acc[i][j][r];
-            st(a, wm + MI * ib + i, wn + NI * li, v);
-        }
+                for (int q = 0; q < 4; ++q)
+                    mine[((i * NI + j) * 4 + q) * NT + tid] =
+                        make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                    acc[i][j][4 * q + 3]);
+        return;
     }
+
+    epilogue_mfma<S, MI, NI>(a, bm, bn, wm, wn, li, lh, acc);
 }
 
 }  // namespace sgk

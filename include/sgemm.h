@@ -17,12 +17,12 @@
  * reduced-precision input rounding and no multi-pass emulation.  The
  * summation order differs from a sequential loop, so results match a float64
  * reference within |C - ref| <= 1e-5 * (|alpha| sum_k |A_ik||B_kj| +
- * |beta||C_ij|), not bit for bit.  A given variant on given inputs is
- * deterministic run to run (no atomics, no split-K).
+ * |beta||C_ij|), not bit for bit.  A given variant (and split count) on
+ * given inputs is deterministic run to run.
  *
  * Pointers.  A, B and C are DEVICE pointers owned by the caller.  The library
  * allocates no memory, copies nothing and keeps no handles; it holds no state
- * between calls.  No alignment is required: 16-byte aligned bases with leading
+ * between calls (split-K takes a caller-owned workspace, below).  No alignment is required: 16-byte aligned bases with leading
  * dimensions and N that are multiples of 4 take 128-bit global accesses,
  * anything else takes 32-bit ones (see sgemm_variant_access for the three
  * access modes).  C must not overlap A or B (undefined
@@ -45,7 +45,9 @@
  * alpha != 0, -8 ldb < max(1, N), -10 C == NULL while M*N > 0, -11
  * ldc < max(1, N)); -20 unknown path; -21 unknown variant; -22 the tile grid
  * does not fit one launch; -23 an unknown access mode, or one these arguments
- * do not allow.  Argument checks run before any HIP call, so they
+ * do not allow; -24 a split-K workspace that is missing, too small or not
+ * 256-byte aligned; -25 a split count outside 1..64 or a variant without a
+ * split-K build.  Argument checks run before any HIP call, so they
  * need no GPU.  Positive: the hipError_t reported for the launch.  The library
  * never exits or aborts the process.
  */
@@ -73,6 +75,8 @@ extern "C" {
 #define SGEMM_ERR_VARIANT (-21)
 #define SGEMM_ERR_TOO_LARGE (-22)
 #define SGEMM_ERR_ACCESS (-23)
+#define SGEMM_ERR_WORKSPACE (-24)
+#define SGEMM_ERR_SPLITS (-25)
 
 /* C = alpha*A*B + beta*C, automatic choice of inner product and tile. */
 int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
@@ -108,6 +112,45 @@ int sgemm_variant_access(int variant, int access, int M, int N, int K,
                          float alpha, const float *A, int lda, const float *B,
                          int ldb, float beta, float *C, int ldc,
                          hipStream_t stream);
+
+/* ---- split-K (for shapes too small to fill the chip with tiles) ----------
+ * The K range is cut into `splits` parts.  A first launch has every (tile,
+ * part) workgroup write its partial tile to the workspace; a second launch
+ * on the same stream has one workgroup per tile sum the partials in part
+ * order 0, 1, ..., splits-1 and apply alpha and beta ("如何高效实现矩阵乘？CUDA
+ * 初学者的角度入门", section "Epilogue", names split-K for the long tail of
+ * small shapes).  The order of the sum is fixed, so results are
+ * deterministic run to run.
+ *
+ * Workspace: caller-owned device memory, 256-byte aligned, at least
+ * sgemm_splitk_workspace_size() bytes, any contents.  Calls that share a
+ * workspace must not overlap in time (same stream, or synchronised).  The
+ * library allocates nothing. */
+
+/* C = alpha*A*B + beta*C like sgemm(), using split-K when the auto choice
+ * calls for it and `workspace_bytes` holds sgemm_workspace_size(M, N, K);
+ * otherwise exactly sgemm(). */
+int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda,
+             const float *B, int ldb, float beta, float *C, int ldc,
+             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes sgemm_ws() can use for these sizes (0: it never splits). */
+size_t sgemm_workspace_size(int M, int N, int K);
+
+/* The split count sgemm_ws() uses with enough workspace (1: no split), or a
+ * negative argument code.  Host logic only. */
+int sgemm_select_splits(int M, int N, int K);
+
+/* One variant with a forced split count (1 = no split, same as
+ * sgemm_variant()).  SGEMM_ERR_SPLITS for a variant without a split-K build. */
+int sgemm_splitk(int variant, int splits, int M, int N, int K, float alpha,
+                 const float *A, int lda, const float *B, int ldb, float beta,
+                 float *C, int ldc, void *workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/* Workspace bytes sgemm_splitk(variant, splits, M, N, ...) needs (0 for
+ * splits == 1, an empty C, or invalid arguments). */
+size_t sgemm_splitk_workspace_size(int variant, int splits, int M, int N);
 
 /* Number of compiled kernel variants. */
 int sgemm_variant_count(void);

@@ -155,3 +155,48 @@ def test_python_binding_rejects_cpu_tensors():
     a = torch.zeros(4, 4)
     with pytest.raises(TypeError):
         g.sgemm(4, 4, 4, 1.0, a, 4, a, 4, 0.0, a, 4, stream=0)
+
+
+def test_splitk_host_logic():
+    split_variants = [v for v in range(g.sgemm_variant_count()) if g.variant_has_splitk(v)]
+    assert split_variants, "no variant has a split-K build"
+    v = split_variants[0]
+    _, bm, bn = g.sgemm_variant_tile(v)
+    M, N = 3 * bm + 1, 2 * bn
+    tiles = 4 * 2
+    ws = g.sgemm_splitk_workspace_size(v, 4, M, N)
+    assert ws >= 4 * tiles * bm * bn * 4 and ws % 256 == 0
+    assert g.sgemm_splitk_workspace_size(v, 1, M, N) == 0
+    assert g.sgemm_splitk_workspace_size(v, 0, M, N) == 0
+    assert g.sgemm_splitk_workspace_size(v, 65, M, N) == 0
+    for nv in range(g.sgemm_variant_count()):
+        if nv not in split_variants:
+            assert g.sgemm_splitk_workspace_size(nv, 2, M, N) == 0
+    # large shapes fill the chip with tiles: no split, no workspace
+    assert g.sgemm_select_splits(8192, 8192, 8192) == 1
+    assert g.sgemm_workspace_size(8192, 8192, 8192) == 0
+    # few tiles and a deep K split; shallow K does not
+    assert g.sgemm_select_splits(512, 512, 8192) == 8
+    assert g.sgemm_workspace_size(512, 512, 8192) > 0
+    assert g.sgemm_select_splits(1024, 1024, 4096) == 2
+    assert g.sgemm_select_splits(1024, 1024, 1024) == 1
+    assert g.sgemm_select_splits(256, 256, 256) == 1
+    assert g.sgemm_select_splits(-1, 4, 4) == -1
+
+
+def test_splitk_argument_codes():
+    split_v = [v for v in range(g.sgemm_variant_count()) if g.variant_has_splitk(v)][0]
+    plain_v = [v for v in range(g.sgemm_variant_count()) if not g.variant_has_splitk(v)][0]
+    base = (64, 64, 64, 1.0, 0x1000, 64, 0x2000, 64, 0.0, 0x3000, 64)
+
+    def call(variant, splits, ws=0x10000, nbytes=1 << 30):
+        return g.sgemm_splitk(variant, splits, *base, workspace=ws, workspace_bytes=nbytes,
+                              stream=0, check=False)
+    assert call(split_v, 0) == -25
+    assert call(split_v, 65) == -25
+    assert call(plain_v, 2) == -25
+    assert call(split_v, 2, ws=0) == -24               # missing workspace
+    assert call(split_v, 2, nbytes=16) == -24          # too small
+    assert call(split_v, 2, ws=0x10010) == -24         # not 256-byte aligned
+    assert "workspace" in g.sgemm_status_string(-24)
+    assert "split" in g.sgemm_status_string(-25)

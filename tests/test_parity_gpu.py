@@ -269,3 +269,87 @@ def test_huge_leading_dimension_takes_checked_accesses():
                                       check=False) == -23
     torch.cuda.synchronize()
     del oa, ob, oc
+
+
+# ------------------------------------------------------------------ split-K
+def split_variants():
+    return [v for v in all_variants() if g.variant_has_splitk(v)]
+
+
+def run_split(p, variant, splits, ws=None):
+    """One split-K launch; returns (C, workspace tensor)."""
+    need = g.sgemm_splitk_workspace_size(variant, splits, p.M, p.N)
+    if ws is None:  # any contents: fill with NaN to show none of it leaks through
+        ws = torch.full((max(need, 256) // 4 + 64,), float("nan"), dtype=torch.float32,
+                        device="cuda")
+    oa, _, a = gu.to_gpu(p.A)
+    ob, _, b = gu.to_gpu(p.B)
+    oc, first, c = gu.to_gpu(p.C)
+    g.sgemm_splitk(variant, splits, p.M, p.N, p.K, p.alpha, a, p.lda, b, p.ldb, p.beta, c, p.ldc,
+                   workspace=ws)
+    torch.cuda.synchronize()
+    host = oc.cpu().numpy()
+    n = p.C.numel()
+    guard = np.concatenate([host[:first], host[first + n:]])
+    assert np.all(np.isnan(guard)), "write outside C's extent"
+    return host[first:first + n].reshape(p.C.shape), ws
+
+
+@pytest.mark.parametrize("variant", split_variants())
+@pytest.mark.parametrize("splits", [2, 3, 4, 7])
+def test_splitk_matches_oracle(variant, splits):
+    for (M, N, K, alpha, beta) in [(200, 301, 777, 1.5, -0.5), (256, 256, 256, 1.0, 0.0),
+                                   (65, 130, 1030, -1.0, 1.0), (64, 64, 40, 2.0, 0.5)]:
+        p = inputs.make_problem(M, N, K, dist="upm1", seed=M + K, alpha=alpha, beta=beta,
+                                c_fill="upm1" if beta != 0 else None)
+        gu.say("split-K", M, N, K, splits, g.sgemm_variant_name(variant))
+        out, ws = run_split(p, variant, splits)
+        assert gu.ratio_full(p, out) <= TOL, (M, N, K, splits)
+
+
+@pytest.mark.parametrize("variant", split_variants())
+def test_splitk_deterministic_and_reusable(variant):
+    p = cached_problem("ragged_1000x1023x999")
+    gu.say("split-K determinism", g.sgemm_variant_name(variant))
+    out1, ws = run_split(p, variant, 4)
+    out2, ws = run_split(p, variant, 4, ws)   # same workspace again
+    assert np.array_equal(out1.view(np.uint32), out2.view(np.uint32))
+    assert gu.ratio_full(p, out1, cached_oracle("ragged_1000x1023x999")) <= TOL
+
+
+@pytest.mark.parametrize("variant", split_variants())
+def test_splitk_closed_form_exact(variant):
+    p = inputs.make_problem(192, 128, 1000, dist="ones_twos")
+    gu.say("split-K closed form", g.sgemm_variant_name(variant))
+    for splits in (2, 5):
+        out, _ = run_split(p, variant, splits)
+        assert np.all(out == 2000.0), splits
+
+
+@pytest.mark.parametrize("name", ["square256_u01", "ragged_1000x1023x999", "512x512x8192",
+                                  "1024x1024x4096"])
+def test_sgemm_ws_auto(name):
+    if name[0].isdigit():
+        M, N, K = (int(x) for x in name.split("x"))
+        p = inputs.make_problem(M, N, K, dist="normal", seed=31, alpha=0.5, beta=-1.0, c_fill="u01")
+        ref_den = gu.oracle_full(p)
+    else:
+        p = cached_problem(name)
+        ref_den = cached_oracle(name)
+    need = g.sgemm_workspace_size(p.M, p.N, p.K)
+    ws = torch.zeros(max(need, 256) // 4 + 64, dtype=torch.float32, device="cuda")
+    oa, _, a = gu.to_gpu(p.A)
+    ob, _, b = gu.to_gpu(p.B)
+    oc, first, c = gu.to_gpu(p.C)
+    gu.say("sgemm_ws", name, "splits", g.sgemm_select_splits(p.M, p.N, p.K), "bytes", need)
+    g.sgemm_ws(p.M, p.N, p.K, p.alpha, a, p.lda, b, p.ldb, p.beta, c, p.ldc, workspace=ws)
+    torch.cuda.synchronize()
+    out = oc.cpu().numpy()[first:first + p.C.numel()].reshape(p.C.shape)
+    assert gu.ratio_full(p, out, ref_den) <= TOL
+    # too small a workspace falls back to the unsplit kernel
+    oc2, first2, c2 = gu.to_gpu(p.C)
+    g.sgemm_ws(p.M, p.N, p.K, p.alpha, a, p.lda, b, p.ldb, p.beta, c2, p.ldc, workspace=ws,
+               workspace_bytes=64)
+    torch.cuda.synchronize()
+    out2 = oc2.cpu().numpy()[first2:first2 + p.C.numel()].reshape(p.C.shape)
+    assert gu.ratio_full(p, out2, ref_den) <= TOL
