@@ -314,32 +314,15 @@ struct BTilePtr : BTileGeom<BN, BK, NT, PADB, VEC, STAGES> {
 };
 
 // ---------------------------------------------------------------------------
-// Epilogue: C = alpha*acc + beta*C (C read only when beta != 0) for W
-// consecutive columns of one row.  VEC == 4 means N, ldc and C are 16-byte
-// friendly, so a W-wide group at a multiple of W is wholly inside or wholly
-// outside the matrix and moves as one vector.
+// Epilogue: C = alpha*acc + beta*C (C read only when beta != 0).  VEC == 4
+// means N, ldc and C are 16-byte friendly, so a W-wide group at a multiple of
+// W is wholly inside or wholly outside the matrix and moves as one vector.
 // ---------------------------------------------------------------------------
-template <int W>
-__device__ __forceinline__ typename vec_t<W>::type axpby(const Args &a, const float (&v)[W],
-                                                         const typename vec_t<W>::type &old) {
-    typename vec_t<W>::type out;
-    float *o = reinterpret_cast<float *>(&out);
-#pragma unroll
-    for (int i = 0; i < W; ++i) o[i] = fmaf(a.alpha, v[i], a.beta * vget(old, i));
-    return out;
-}
-
-template <int W>
-__device__ __forceinline__ typename vec_t<W>::type ax(const Args &a, const float (&v)[W]) {
-    typename vec_t<W>::type out;
-    float *o = reinterpret_cast<float *>(&out);
-#pragma unroll
-    for (int i = 0; i < W; ++i) o[i] = a.alpha * v[i];
-    return out;
-}
-
-// Buffered: rc covers rows bm.. of C from column bn up to C's last element;
-// (r, c) are tile coordinates.
+// C accesses of the epilogue, W consecutive columns of one row at tile
+// coordinates (r, c).  load() reads the old values (only called when
+// beta != 0); store() writes the new ones; both skip what lies outside C.
+//
+// Buffered: rc covers rows bm.. of C from column bn up to C's last element.
 template <int W, int VEC>
 struct CStoreBuf {
     rsrc_t rc;
@@ -350,21 +333,33 @@ struct CStoreBuf {
         ncols = a.N - bn;
     }
 
-    __device__ __forceinline__ void operator()(const Args &a, int r, int c, const float (&v)[W]) const {
-        const uint32_t off = (uint32_t)(((int64_t)r * a.ldc + c) * 4);
+    __device__ __forceinline__ uint32_t offset(const Args &a, int r, int c) const {
+        return (uint32_t)(((int64_t)r * a.ldc + c) * 4);
+    }
+
+    __device__ __forceinline__ void load(const Args &a, int r, int c, float (&old)[W]) const {
+        const uint32_t off = offset(a, r, c);
         if (VEC == 4 || W == 1) {
-            const uint32_t o = c < ncols ? off : kOutOfRange;
-            typedef typename vec_t<W>::type V;
-            const V out = a.beta != 0.0f ? axpby<W>(a, v, buf<W>::load(rc, o)) : ax<W>(a, v);
-            buf<W>::store(out, rc, o);
+            const typename vec_t<W>::type v = buf<W>::load(rc, c < ncols ? off : kOutOfRange);
+#pragma unroll
+            for (int i = 0; i < W; ++i) old[i] = vget(v, i);
         } else {
 #pragma unroll
-            for (int i = 0; i < W; ++i) {
-                const uint32_t o = c + i < ncols ? off + 4u * i : kOutOfRange;
-                const float vi[1] = {v[i]};
-                const float out = a.beta != 0.0f ? axpby<1>(a, vi, buf<1>::load(rc, o)) : ax<1>(a, vi);
-                buf<1>::store(out, rc, o);
-            }
+            for (int i = 0; i < W; ++i) old[i] = buf<1>::load(rc, c + i < ncols ? off + 4u * i : kOutOfRange);
+        }
+    }
+
+    __device__ __forceinline__ void store(const Args &a, int r, int c, const float (&out)[W]) const {
+        const uint32_t off = offset(a, r, c);
+        if (VEC == 4 || W == 1) {
+            typename vec_t<W>::type v;
+            float *o = reinterpret_cast<float *>(&v);
+#pragma unroll
+            for (int i = 0; i < W; ++i) o[i] = out[i];
+            buf<W>::store(v, rc, c < ncols ? off : kOutOfRange);
+        } else {
+#pragma unroll
+            for (int i = 0; i < W; ++i) buf<1>::store(out[i], rc, c + i < ncols ? off + 4u * i : kOutOfRange);
         }
     }
 };
@@ -378,22 +373,76 @@ struct CStorePtr {
         bn = bn_;
     }
 
-    __device__ __forceinline__ void operator()(const Args &a, int r, int c, const float (&v)[W]) const {
+    __device__ __forceinline__ void load(const Args &a, int r, int c, float (&old)[W]) const {
+        const int row = bm + r, col = bn + c;
+        const float *p = a.C + (int64_t)row * a.ldc + col;
+#pragma unroll
+        for (int i = 0; i < W; ++i) old[i] = (row < a.M && col + i < a.N) ? p[i] : 0.0f;
+    }
+
+    __device__ __forceinline__ void store(const Args &a, int r, int c, const float (&out)[W]) const {
         const int row = bm + r, col = bn + c;
         if (row >= a.M) return;
         float *p = a.C + (int64_t)row * a.ldc + col;
         if (VEC == 4 && W > 1) {
             if (col >= a.N) return;
-            typedef typename vec_t<W>::type V;
-            *reinterpret_cast<V *>(p) = a.beta != 0.0f ? axpby<W>(a, v, *reinterpret_cast<const V *>(p))
-                                                       : ax<W>(a, v);
+            typename vec_t<W>::type v;
+            float *o = reinterpret_cast<float *>(&v);
+#pragma unroll
+            for (int i = 0; i < W; ++i) o[i] = out[i];
+            *reinterpret_cast<typename vec_t<W>::type *>(p) = v;
         } else {
 #pragma unroll
             for (int i = 0; i < W; ++i)
-                if (col + i < a.N) p[i] = a.beta != 0.0f ? fmaf(a.alpha, v[i], a.beta * p[i]) : a.alpha * v[i];
+                if (col + i < a.N) p[i] = out[i];
         }
     }
 };
+
+// The epilogue proper: NV vectors of W columns per lane, vector v at tile
+// coordinates pos(v) with values val(v).  beta is uniform, so the test is
+// taken once; with beta != 0 the old values of G vectors are requested
+// together before any of them is combined and stored, so the loads' latency
+// is paid once per group instead of once per vector (a group holds 32 old
+// values: 32 extra VGPRs at most).
+template <int NV, int W, class TC, class Pos, class Val>
+__device__ __forceinline__ void epilogue(const Args &a, const TC &st, Pos pos, Val val) {
+    if (a.beta != 0.0f) {
+        constexpr int G = NV < 32 / W ? NV : 32 / W;
+        static_assert(NV % G == 0, "epilogue groups");
+#pragma unroll
+        for (int b = 0; b < NV; b += G) {
+            float old[G][W];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                int r, c;
+                pos(b + g, r, c);
+                st.load(a, r, c, old[g]);
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                int r, c;
+                pos(b + g, r, c);
+                float v[W], out[W];
+                val(b + g, v);
+#pragma unroll
+                for (int i = 0; i < W; ++i) out[i] = fmaf(a.alpha, v[i], a.beta * old[g][i]);
+                st.store(a, r, c, out);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < NV; ++b) {
+            int r, c;
+            pos(b, r, c);
+            float v[W], out[W];
+            val(b, v);
+#pragma unroll
+            for (int i = 0; i < W; ++i) out[i] = a.alpha * v[i];
+            st.store(a, r, c, out);
+        }
+    }
+}
 
 template <bool BUF, int BM, int BN, int BK, int NT, int PADA, int PADB, int VEC, int W, int STAGES>
 struct Staging {
@@ -486,18 +535,23 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
         __syncthreads();
     }
 
-    // 8 lanes with the same ly cover 32 consecutive columns (128 bytes) of a row
+    // 8 lanes with the same ly cover 32 consecutive columns (128 bytes) of a row;
+    // vector v is micro-tile row v / (TN/4), column group v % (TN/4)
     typename S::TC st;
     st.init(a, bm, bn);
+    constexpr int CG = TN / 4;
+    epilogue<TM * CG, 4>(
+        a, st,
+        [&](int v, int &r, int &c) {
+            const int i = v / CG, g = v % CG;
+            r = wm + 4 * ly + (i & 3) + 32 * (i >> 2);
+            c = wn + 4 * lx + 32 * g;
+        },
+        [&](int v, float (&x)[4]) {
+            const int i = v / CG, g = v % CG;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int r = wm + 4 * ly + (i & 3) + 32 * (i >> 2);
-#pragma unroll
-        for (int s = 0; s < TN / 4; ++s) {
-            const float v[4] = {acc[i][4 * s], acc[i][4 * s + 1], acc[i][4 * s + 2], acc[i][4 * s + 3]};
-            st(a, r, wn + 4 * lx + 32 * s, v);
-        }
-    }
+            for (int e = 0; e < 4; ++e) x[e] = acc[i][4 * g + e];
+        });
 }
 
 // ---------------------------------------------------------------------------
@@ -592,17 +646,18 @@ __device__ __forceinline__ void epilogue_mfma(const Args &a, int bm, int bn, int
                                               int lh, const floatx16 (&acc)[MI][NI]) {
     typename S::TC st;
     st.init(a, bm, bn);
+    // vector v is accumulator register v % 16 of block row v / 16
+    epilogue<MI * 16, NI>(
+        a, st,
+        [&](int v, int &r, int &c) {
+            const int i = v / 16, reg = v % 16;
+            r = wm + MI * (8 * (reg >> 2) + 4 * lh + (reg & 3)) + i;
+            c = wn + NI * li;
+        },
+        [&](int v, float (&x)[NI]) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int ib = 8 * (r >> 2) + 4 * lh + (r & 3);
-            float v[NI];
-#pragma unroll
-            for (int j = 0; j < NI; ++j) v[j] = acc[i][j][r];
-            st(a, wm + MI * ib + i, wn + NI * li, v);
-        }
-    }
+            for (int j = 0; j < NI; ++j) x[j] = acc[v / 16][j][v % 16];
+        });
 }
 
 // PD is the prefetch depth: how many K tiles are in flight in registers while
