@@ -38,7 +38,16 @@ struct Variant {
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, false>, nullptr, nullptr}
 
 #define MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, VEC, WPE, BUF, PD, FD, ORD, SPLIT)          \
-    sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, VEC, WPE, BUF, PD, FD, ORD, SPLIT>
+    sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, VEC, WPE, BUF, PD, FD, ORD, SPLIT, 0>
+
+// A variant with the LDS-staged epilogue (no split-K build).
+#define MFMA_CFG_STAGED_EPI(BM, BN, BK, WM, WN, PA, PB, WPE, PD, FD, SUFFIX)             \
+    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
+     (BM / WM) * (BN / WN) * 64,                                                         \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD, 0, false, 1>,    \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD, 0, false, 1>,    \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, false, PD, FD, 0, false, 1>,   \
+     nullptr, nullptr}
 
 #define MFMA_CFG(BM, BN, BK, WM, WN, PA, PB, WPE, PD, FD, ORD, SUFFIX)                   \
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
@@ -73,6 +82,8 @@ const Variant kVariants[] = {
     MFMA_CFG(128, 128, 32, 64, 64, 4, 0, 2, 2, 2, 0, "_pf2_fd2"), // 11
     MFMA_CFG(128, 256, 16, 64, 128, 4, 0, 2, 1, 1, 1, "_xcd"),    // 12: 6 in XCD-grouped tile order
     MFMA_CFG(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, 1, "_xcd"),    // 13: 5 in XCD-grouped tile order
+    MFMA_CFG_STAGED_EPI(128, 256, 16, 64, 128, 4, 0, 2, 1, 1, "_ldsepi"), // 14: 6 with the LDS-staged epilogue
+    MFMA_CFG_STAGED_EPI(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, "_ldsepi"), // 15: 5 with the LDS-staged epilogue
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 

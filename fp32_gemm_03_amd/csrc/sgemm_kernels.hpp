@@ -660,12 +660,68 @@ __device__ __forceinline__ void epilogue_mfma(const Args &a, int bm, int bn, int
         });
 }
 
+// Epilogue through LDS ("SGEMM CUDA kernel (Second Half)", Part 9: each warp
+// stages its results in a shared buffer and flushes whole rows with
+// coalesced stores).  Each wave stages 16 of its tile rows at a time in its
+// own LDS area (16 x (WN + 4) floats), then its 64 lanes read them back as
+// 4-float vectors in row order and store them, so one store instruction
+// covers 64 x 16 contiguous-in-row bytes (whole rows of the wave tile).  The
+// direct epilogue already stores 32 x 4 x NI contiguous bytes per row; this
+// variant exists to measure the difference on MI355X.
+template <class TC4, int MI, int NI, int WN>
+__device__ __forceinline__ void epilogue_mfma_staged(const Args &a, const TC4 &st4, float *lds_wave,
+                                                     int wm, int wn, int li, int lh, int lane,
+                                                     const floatx16 (&acc)[MI][NI]) {
+    typedef typename vec_t<NI>::type VB;
+    constexpr int SW = WN + 4;
+    constexpr int ROW4 = WN / 4;             // 4-float vectors per staged row
+    constexpr int F4 = 16 * ROW4 / 64;       // vectors per lane per 16-row chunk
+    static_assert((16 * ROW4) % 64 == 0, "staged chunk must split over 64 lanes");
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int reg = 8 * h + q;
+                const int lr = 8 * (reg >> 2) + 4 * lh + (reg & 3) - 16 * h;  // 0..15
+                VB v;
+                float *pv = reinterpret_cast<float *>(&v);
+#pragma unroll
+                for (int j = 0; j < NI; ++j) pv[j] = acc[mi][j][reg];
+                *reinterpret_cast<VB *>(lds_wave + lr * SW + NI * li) = v;
+            }
+            __syncthreads();
+            float4 vals[F4];
+#pragma unroll
+            for (int k = 0; k < F4; ++k) {
+                const int f = lane + 64 * k;
+                vals[k] = *reinterpret_cast<const float4 *>(lds_wave + (f / ROW4) * SW + 4 * (f % ROW4));
+            }
+            epilogue<F4, 4>(
+                a, st4,
+                [&](int k, int &r, int &c) {
+                    const int f = lane + 64 * k;
+                    r = wm + MI * (16 * h + f / ROW4) + mi;
+                    c = wn + 4 * (f % ROW4);
+                },
+                [&](int k, float (&x)[4]) {
+                    x[0] = vals[k].x;
+                    x[1] = vals[k].y;
+                    x[2] = vals[k].z;
+                    x[3] = vals[k].w;
+                });
+        }
+    }
+}
+
 // PD is the prefetch depth: how many K tiles are in flight in registers while
 // one is multiplied from LDS (1, or 2 for shapes whose per-tile arithmetic is
 // too short to cover one global-load latency).  FD is the LDS fragment
 // prefetch distance in k-steps.
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC, int WPE, bool BUF,
-          int PD, int FD, int ORDER, bool SPLIT>
+          int PD, int FD, int ORDER, bool SPLIT, int EPI>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -826,7 +882,16 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         return;
     }
 
-    epilogue_mfma<S, MI, NI>(a, bm, bn, wm, wn, li, lh, acc);
+    if (EPI == 0) {
+        epilogue_mfma<S, MI, NI>(a, bm, bn, wm, wn, li, lh, acc);
+    } else {
+        static_assert(EPI == 0 || (BM / WM) * (BN / WN) * 16 * (WN + 4) <= 2 * STAGE,
+                      "staged epilogue needs 16 x (WN + 4) floats of LDS per wave");
+        typename Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, 4, PD>::TC st4;
+        st4.init(a, bm, bn);
+        epilogue_mfma_staged<decltype(st4), MI, NI, WN>(a, st4, smem + wave * 16 * (WN + 4), wm, wn,
+                                                         li, lh, lane, acc);
+    }
 }
 
 }  // namespace sgk
