@@ -38,15 +38,24 @@ struct Variant {
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, false>, nullptr, nullptr}
 
 #define MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, VEC, WPE, BUF, PD, FD, ORD, SPLIT)          \
-    sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, VEC, WPE, BUF, PD, FD, ORD, SPLIT, 0>
+    sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, VEC, WPE, BUF, PD, FD, ORD, SPLIT, 0, false>
 
 // A variant with the LDS-staged epilogue (no split-K build).
 #define MFMA_CFG_STAGED_EPI(BM, BN, BK, WM, WN, PA, PB, WPE, PD, FD, SUFFIX)             \
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
      (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD, 0, false, 1>,    \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD, 0, false, 1>,    \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, false, PD, FD, 0, false, 1>,   \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD, 0, false, 1, false>, \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD, 0, false, 1, false>, \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, false, PD, FD, 0, false, 1, false>, \
+     nullptr, nullptr}
+
+// A variant with A unpadded in LDS and its columns XOR-swizzled per row.
+#define MFMA_CFG_SWIZZLED_A(BM, BN, BK, WM, WN, WPE, PD, FD, SUFFIX)                     \
+    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
+     (BM / WM) * (BN / WN) * 64,                                                         \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, 0, 0, 4, WPE, true, PD, FD, 0, false, 0, true>,  \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, 0, 0, 1, WPE, true, PD, FD, 0, false, 0, true>,  \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, 0, 0, 1, WPE, false, PD, FD, 0, false, 0, true>, \
      nullptr, nullptr}
 
 #define MFMA_CFG(BM, BN, BK, WM, WN, PA, PB, WPE, PD, FD, ORD, SUFFIX)                   \
@@ -84,11 +93,13 @@ const Variant kVariants[] = {
     MFMA_CFG(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, 1, "_xcd"),    // 13: 5 in XCD-grouped tile order
     MFMA_CFG_STAGED_EPI(128, 256, 16, 64, 128, 4, 0, 2, 1, 1, "_ldsepi"), // 14: 6 with the LDS-staged epilogue
     MFMA_CFG_STAGED_EPI(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, "_ldsepi"), // 15: 5 with the LDS-staged epilogue
+    MFMA_CFG_SWIZZLED_A(128, 256, 16, 64, 128, 2, 1, 1, "_xorA"),         // 16: 6, A unpadded and XOR-swizzled
+    MFMA_CFG_SWIZZLED_A(64, 64, 64, 32, 32, 2, 1, 3, "_fd3_xorA"),        // 17: 10, A unpadded and XOR-swizzled
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 constexpr int kValuDefault = 0;
-constexpr int kMfmaLarge = 6;   // 128 x 256 x 16, two workgroups per CU
+constexpr int kMfmaLarge = 16;  // 128 x 256 x 16, A XOR-swizzled, two workgroups per CU
 constexpr int kMfmaMedium = 9;  // 64 x 64 x 32, two K tiles in flight
 constexpr int kMfmaSmall = 10;  // 64 x 64 x 64, fragments three k-steps ahead
 
@@ -105,7 +116,10 @@ long long tiles(int M, int N, int bm, int bn) {
 // 16384^2 x 128, 1000 x 1023 x 999, 256^3):
 //   * at least two 128 x 256 blocks per CU: the 128 x 256 block with two
 //     workgroups per CU is fastest (its lanes also store 4 consecutive
-//     columns, which matters when the epilogue dominates at small K);
+//     columns, which matters when the epilogue dominates at small K), with
+//     A XOR-swizzled in LDS rather than padded: 1-2% faster at 4096^3 to
+//     16384^3 and 15% at 6144^3 (on the 64 x 64 blocks the per-k-step
+//     address XOR costs 10-15% instead, so those stay padded);
 //   * at least one 128 x 128 block per CU: 64 x 64 blocks with two K tiles
 //     in flight (4 workgroups per CU hide each other's latency);
 //   * below that the problem cannot fill the chip and each workgroup's

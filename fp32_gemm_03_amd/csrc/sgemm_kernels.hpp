@@ -22,7 +22,9 @@
 //      is (Bs[k][n], padded by PADB).  This is the layout of "SGEMM CUDA kernel
 //      (Second Half)", Part 8 "Transposed As": A read as 4 x 1, written as a
 //      1 x 4 vector into a transposed tile whose rows are shifted by 4 extra
-//      columns so that the vector stores do not collide in LDS banks.
+//      columns so that the vector stores do not collide in LDS banks.  With
+//      SWZ the rows are not padded and the columns are XOR-permuted instead
+//      (see swz_col below); the large-shape tile uses that form.
 //   3. Two LDS stages: the global loads of step t+1 are issued before the
 //      LDS reads and arithmetic of step t, and written to the other stage
 //      afterwards; one workgroup barrier per step ("如何高效实现矩阵乘", section
@@ -149,9 +151,25 @@ template <> struct buf<4> {
 // Thread tid covers column tid % BK of rows r0 + {0..3} + p * ROWS_PER_PASS,
 // r0 = 4 * (tid / BK), and writes one 128-bit LDS vector per 4 rows.
 // ---------------------------------------------------------------------------
-template <int BM, int BK, int NT, int PADA, int STAGES>
+// The transposed store collides in LDS banks unless something breaks the
+// power-of-two row stride.  "如何高效实现矩阵乘？CUDA初学者的角度入门", section
+// "Shared Memory" / "128-bit conflict-free store", names two cures: pad the
+// leading dimension by 4 (PADA above), or leave the tile unpadded and move
+// the colliding data elsewhere by an index transform.  SWZ is a transform of
+// the second kind, fitted to this store: the lanes that collide are the BK
+// lanes writing the same 4-row chunk m of different rows k, so the 16-byte
+// chunk index of row k is XORed with (k mod 16).  Sixteen consecutive k then
+// hit sixteen different chunks (all 64 banks), no LDS is spent on padding,
+// and each row stays a permutation of its own aligned 64-float groups, so an
+// MFMA fragment read (one k, MI <= 4 consecutive m) stays one vector read.
+__device__ __forceinline__ int swz_col(int k, int col) {
+    return ((((col >> 2) ^ (k & 15))) << 2) | (col & 3);
+}
+
+template <int BM, int BK, int NT, int PADA, int STAGES, bool SWZ = false>
 struct ATileGeom {
     static_assert(BM % 4 == 0, "BM must be a multiple of 4");
+    static_assert(!SWZ || (BM % 64 == 0 && PADA == 0), "the swizzle permutes 64-float row blocks");
     static_assert(NT % BK == 0, "BK must divide the thread count");
     static constexpr int ROWS_PER_PASS = 4 * (NT / BK);
     static_assert(BM % ROWS_PER_PASS == 0, "A tile must divide evenly over the threads");
@@ -162,16 +180,19 @@ struct ATileGeom {
 
     template <int S>
     __device__ __forceinline__ void store(float *As, int tid) const {
-        float *dst = As + (tid % BK) * SA + 4 * (tid / BK);
+        const int k = tid % BK;
+        float *row = As + k * SA;
 #pragma unroll
-        for (int p = 0; p < PER; ++p)
-            *reinterpret_cast<float4 *>(dst + p * ROWS_PER_PASS) = reg[S][p];
+        for (int p = 0; p < PER; ++p) {
+            const int m = 4 * (tid / BK) + p * ROWS_PER_PASS;
+            *reinterpret_cast<float4 *>(row + (SWZ ? swz_col(k, m) : m)) = reg[S][p];
+        }
     }
 };
 
-template <int BM, int BK, int NT, int PADA, int STAGES>
-struct ATileBuf : ATileGeom<BM, BK, NT, PADA, STAGES> {
-    typedef ATileGeom<BM, BK, NT, PADA, STAGES> G;
+template <int BM, int BK, int NT, int PADA, int STAGES, bool SWZ>
+struct ATileBuf : ATileGeom<BM, BK, NT, PADA, STAGES, SWZ> {
+    typedef ATileGeom<BM, BK, NT, PADA, STAGES, SWZ> G;
     rsrc_t rsrc;       // rows bm.. of A, up to A's last element
     uint32_t off[4];   // ((r0 + c) * lda + col) * 4
     uint32_t pass;     // ROWS_PER_PASS * lda * 4
@@ -202,9 +223,9 @@ struct ATileBuf : ATileGeom<BM, BK, NT, PADA, STAGES> {
     }
 };
 
-template <int BM, int BK, int NT, int PADA, int STAGES>
-struct ATilePtr : ATileGeom<BM, BK, NT, PADA, STAGES> {
-    typedef ATileGeom<BM, BK, NT, PADA, STAGES> G;
+template <int BM, int BK, int NT, int PADA, int STAGES, bool SWZ>
+struct ATilePtr : ATileGeom<BM, BK, NT, PADA, STAGES, SWZ> {
+    typedef ATileGeom<BM, BK, NT, PADA, STAGES, SWZ> G;
     int col, r0;
 
     __device__ __forceinline__ void init(const Args &, int, int tid) {
@@ -444,10 +465,11 @@ __device__ __forceinline__ void epilogue(const Args &a, const TC &st, Pos pos, V
     }
 }
 
-template <bool BUF, int BM, int BN, int BK, int NT, int PADA, int PADB, int VEC, int W, int STAGES>
+template <bool BUF, int BM, int BN, int BK, int NT, int PADA, int PADB, int VEC, int W, int STAGES,
+          bool SWZ = false>
 struct Staging {
-    typedef typename std::conditional<BUF, ATileBuf<BM, BK, NT, PADA, STAGES>,
-                                      ATilePtr<BM, BK, NT, PADA, STAGES>>::type TA;
+    typedef typename std::conditional<BUF, ATileBuf<BM, BK, NT, PADA, STAGES, SWZ>,
+                                      ATilePtr<BM, BK, NT, PADA, STAGES, SWZ>>::type TA;
     typedef typename std::conditional<BUF, BTileBuf<BN, BK, NT, PADB, VEC, STAGES>,
                                       BTilePtr<BN, BK, NT, PADB, VEC, STAGES>>::type TB;
     typedef typename std::conditional<BUF, CStoreBuf<W, VEC>, CStorePtr<W, VEC>>::type TC;
@@ -605,24 +627,29 @@ __device__ __forceinline__ void tile_of(int pid, int nbm, int nbn, int &tm, int 
 // One K tile of MFMAs from one LDS stage.  The fragments of k-step j + FD
 // are read while the MFMAs of step j issue, so the LDS latency hides behind
 // FD steps of matrix work (FD > 1 for wave tiles with few MFMAs per step).
-template <int BK, int MI, int NI, int SA, int SB, int FD>
-__device__ __forceinline__ void mfma_tile(const float *ap, const float *bp,
+template <int BK, int MI, int NI, int SA, int SB, int FD, bool SWZ>
+__device__ __forceinline__ void mfma_tile(const float *as, int a_col, int lh, const float *bp,
                                           floatx16 (&acc)[MI][NI]) {
     typedef typename vec_t<MI>::type VA;
     typedef typename vec_t<NI>::type VB;
     constexpr int STEPS = BK / 2;
     constexpr int RING = FD + 1;
+    // A fragment of k-step j: LDS row 2j + lh, column a_col (swizzled or not)
+    auto a_at = [&](int j) -> const VA * {
+        const int row = 2 * j + lh;
+        return reinterpret_cast<const VA *>(as + row * SA + (SWZ ? swz_col(row, a_col) : a_col));
+    };
     VA av[RING];
     VB bv[RING];
 #pragma unroll
     for (int f = 0; f < FD && f < STEPS; ++f) {
-        av[f] = *reinterpret_cast<const VA *>(ap + 2 * f * SA);
+        av[f] = *a_at(f);
         bv[f] = *reinterpret_cast<const VB *>(bp + 2 * f * SB);
     }
 #pragma unroll
     for (int j = 0; j < STEPS; ++j) {
         if (j + FD < STEPS) {
-            av[(j + FD) % RING] = *reinterpret_cast<const VA *>(ap + 2 * (j + FD) * SA);
+            av[(j + FD) % RING] = *a_at(j + FD);
             bv[(j + FD) % RING] = *reinterpret_cast<const VB *>(bp + 2 * (j + FD) * SB);
         }
         // Keep the early reads above this step's MFMAs: without the fence the
@@ -721,7 +748,7 @@ __device__ __forceinline__ void epilogue_mfma_staged(const Args &a, const TC4 &s
 // too short to cover one global-load latency).  FD is the LDS fragment
 // prefetch distance in k-steps.
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC, int WPE, bool BUF,
-          int PD, int FD, int ORDER, bool SPLIT, int EPI>
+          int PD, int FD, int ORDER, bool SPLIT, int EPI, bool SWZ>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -733,7 +760,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     static_assert(MI == 1 || MI == 2 || MI == 4, "MI in {1, 2, 4}");
     static_assert(NI == 1 || NI == 2 || NI == 4, "NI in {1, 2, 4}");
     static_assert(PD == 1 || PD == 2, "prefetch depth 1 or 2");
-    typedef Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, NI, PD> S;
+    typedef Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, NI, PD, SWZ> S;
     __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
     const int tid = threadIdx.x;
@@ -787,7 +814,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     }
 
     // per-lane fragment bases inside one LDS stage
-    const int a_off = lh * SA + wm + MI * li;
+    const int a_col = wm + MI * li;
     const int b_off = BK * SA + lh * SB + wn + NI * li;
     // K tiles [kt0, kt0 + KT): all of K, or this split's share of it
     const int KT_ALL = (a.K + BK - 1) / BK;
@@ -809,7 +836,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
                 ta.template load<0>(a, bm, kb + (t + 1) * BK);
                 tb.template load<0>(a, bn, kb + (t + 1) * BK);
             }
-            mfma_tile<BK, MI, NI, SA, SB, FD>(st + a_off, st + b_off, acc);
+            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ>(st, a_col, lh, st + b_off, acc);
             if (t + 1 < KT) {
                 float *nx = smem + ((t + 1) & 1) * STAGE;
                 ta.template store<0>(nx, tid);
@@ -841,7 +868,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         }
         for (int t = 0; t < KT; t += 2) {
             // tile t from LDS stage 0; tile t+1 (register stage 1) -> LDS stage 1
-            mfma_tile<BK, MI, NI, SA, SB, FD>(smem + a_off, smem + b_off, acc);
+            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ>(smem, a_col, lh, smem + b_off, acc);
             if (t + 1 < KT) {
                 ta.template store<R>(smem + STAGE, tid);
                 tb.template store<R>(smem + STAGE + BK * SA, tid);
@@ -853,7 +880,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
                 tb.template load<R>(a, bn, kb + (t + 3) * BK);
             }
             // tile t+1 from LDS stage 1; tile t+2 (register stage 0) -> LDS stage 0
-            mfma_tile<BK, MI, NI, SA, SB, FD>(smem + STAGE + a_off, smem + STAGE + b_off, acc);
+            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ>(smem + STAGE, a_col, lh, smem + STAGE + b_off, acc);
             if (t + 2 < KT) {
                 ta.template store<0>(smem, tid);
                 tb.template store<0>(smem + BK * SA, tid);
@@ -887,7 +914,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     } else {
         static_assert(EPI == 0 || (BM / WM) * (BN / WN) * 16 * (WN + 4) <= 2 * STAGE,
                       "staged epilogue needs 16 x (WN + 4) floats of LDS per wave");
-        typename Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, 4, PD>::TC st4;
+        typename Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, 4, PD, SWZ>::TC st4;
         st4.init(a, bm, bn);
         epilogue_mfma_staged<decltype(st4), MI, NI, WN>(a, st4, smem + wave * 16 * (WN + 4), wm, wn,
                                                          li, lh, lane, acc);
