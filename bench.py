@@ -15,6 +15,10 @@ steps bracketed by device synchronisation; one JSON line on stdout.
                FETCH_SIZE + WRITE_SIZE (scaled by a copy-kernel calibration), read
                from profiles/ when it was taken on the current kernel source,
                else null.
+  secondary  = the same timing for 4096^3 and for the low-K 16384^2 x 128
+               problem (beta = 1), each with its fraction of the FP32 peak, of
+               the HBM peak (algorithmic bytes: A, B, C read, C written) and of
+               the larger of the two bounds.
   cpu_baseline = the float64 CPU oracle on a bounded band of rows of the same
                problem, on every host core (rank 0, N = 1 only).
 """
@@ -39,7 +43,10 @@ PEAK_FP32_TFLOPS = 157.3  # 256 CU x 256 FLOP/clk x 2.4 GHz (FP32 MFMA)
 PEAK_VALU_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "square8192_normal"
-SECONDARY = "square4096_upm1"
+# Reported beside the main line: the other square size the metric names, and
+# the low-K shape, whose bound is taken as the larger of its FLOP time at the
+# FP32 peak and its algorithmic bytes at the HBM peak.
+SECONDARY = ("square4096_upm1", "lowk_16384x16384x128")
 
 
 def kernel_source_hash() -> str:
@@ -222,15 +229,26 @@ def main():
                      "algorithmic_bytes_per_launch": w.algorithmic_bytes},
     }
     if not args.no_secondary and args.workload == WORKLOAD:
-        p2 = inputs.workload_problem(SECONDARY)
-        w2 = inputs.WORKLOADS[SECONDARY]
-        steps2 = max(args.steps, 20)
-        t2, per2, _ = time_gpu(p2, steps2, args.warmup, path, args.variant)
-        v2 = g.sgemm_select_variant(path, p2.M, p2.N, p2.K) if args.variant is None else args.variant
-        out["secondary"] = {"workload": SECONDARY, "variant": g.sgemm_variant_name(v2),
-                            "value": round(w2.flops / (t2 / steps2 / 1e3) / 1e12, 3),
-                            "unit": "TFLOP/s", "ms_per_step": round(t2 / steps2, 4)}
-        del p2
+        out["secondary"] = []
+        for name in SECONDARY:
+            p2 = inputs.workload_problem(name)
+            w2 = inputs.WORKLOADS[name]
+            steps2 = max(args.steps, 100)
+            t2, per2, _ = time_gpu(p2, steps2, args.warmup, path, args.variant)
+            v2 = g.sgemm_select_variant(path, p2.M, p2.N, p2.K) if args.variant is None else args.variant
+            sec_s = t2 / steps2 / 1e3
+            t_fp32 = w2.flops / (PEAK_FP32_TFLOPS * 1e12)
+            t_hbm = w2.algorithmic_bytes / (PEAK_HBM_GBS * 1e9)
+            out["secondary"].append({
+                "workload": name, "variant": g.sgemm_variant_name(v2),
+                "value": round(w2.flops / sec_s / 1e12, 3), "unit": "TFLOP/s",
+                "ms_per_step": round(sec_s * 1e3, 4), "steps": steps2,
+                "pct_of_fp32_peak": round(100.0 * t_fp32 / sec_s, 2),
+                "hbm_gbs": round(w2.algorithmic_bytes / sec_s / 1e9, 1),
+                "pct_of_hbm_peak": round(100.0 * t_hbm / sec_s, 2),
+                "roofline_bound": "mfma" if t_fp32 >= t_hbm else "hbm",
+                "frac_of_roofline": round(max(t_fp32, t_hbm) / sec_s, 4)})
+            del p2
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p)
     out["device"] = torch.cuda.get_device_name(0)

@@ -181,7 +181,7 @@ def _ws_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_
 
 def sgemm_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace=None, workspace_bytes=None,
              stream=None, check=True):
-    """sgemm() that may split K over ``workspace`` (a GPU tensor, zeroed before first use)."""
+    """sgemm() that may split K over ``workspace`` (a GPU tensor, 256-byte aligned, any contents)."""
     lib = load_library()
     return _ret(lib.sgemm_ws(*_ws_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
                                        workspace_bytes, stream)), "sgemm_ws", check)

@@ -95,13 +95,16 @@ const Variant kVariants[] = {
     MFMA_CFG_STAGED_EPI(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, "_ldsepi"), // 15: 5 with the LDS-staged epilogue
     MFMA_CFG_SWIZZLED_A(128, 256, 16, 64, 128, 2, 1, 1, "_xorA"),         // 16: 6, A unpadded and XOR-swizzled
     MFMA_CFG_SWIZZLED_A(64, 64, 64, 32, 32, 2, 1, 3, "_fd3_xorA"),        // 17: 10, A unpadded and XOR-swizzled
+    MFMA_CFG_SWIZZLED_A(128, 128, 32, 64, 64, 2, 1, 1, "_xorA"),          // 18: 2, A unpadded and XOR-swizzled
+    MFMA_CFG_SWIZZLED_A(128, 128, 16, 64, 64, 4, 1, 1, "_wpe4_xorA"),     // 19: 4 workgroups per CU
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 constexpr int kValuDefault = 0;
-constexpr int kMfmaLarge = 16;  // 128 x 256 x 16, A XOR-swizzled, two workgroups per CU
-constexpr int kMfmaMedium = 9;  // 64 x 64 x 32, two K tiles in flight
-constexpr int kMfmaSmall = 10;  // 64 x 64 x 64, fragments three k-steps ahead
+constexpr int kMfmaLarge = 16;   // 128 x 256 x 16, A XOR-swizzled, two workgroups per CU
+constexpr int kMfmaLarge4 = 19;  // 128 x 128 x 16, A XOR-swizzled, four workgroups per CU
+constexpr int kMfmaMedium = 9;   // 64 x 64 x 32, two K tiles in flight
+constexpr int kMfmaSmall = 10;   // 64 x 64 x 64, fragments three k-steps ahead
 
 // Compute units of an MI355X; the choice of tile is a pure function of the
 // sizes so that it is the same on every call and testable without a GPU.
@@ -112,14 +115,25 @@ long long tiles(int M, int N, int bm, int bn) {
     return (long long)((M + bm - 1) / bm) * (long long)((N + bn - 1) / bn);
 }
 
-// Measured on MI355X over every variant (8192^3, 4096^3, 2048^3, 1024^3,
-// 16384^2 x 128, 1000 x 1023 x 999, 256^3):
-//   * at least two 128 x 256 blocks per CU: the 128 x 256 block with two
-//     workgroups per CU is fastest (its lanes also store 4 consecutive
-//     columns, which matters when the epilogue dominates at small K), with
-//     A XOR-swizzled in LDS rather than padded: 1-2% faster at 4096^3 to
-//     16384^3 and 15% at 6144^3 (on the 64 x 64 blocks the per-k-step
-//     address XOR costs 10-15% instead, so those stay padded);
+// Fraction of the last round of tiles that keeps the compute units busy:
+// t tiles over 256 CUs take ceil(t / 256) rounds of per-CU work.
+double quantization(long long t) {
+    const long long rounds = (t + kComputeUnits - 1) / kComputeUnits;
+    return rounds == 0 ? 0.0 : (double)t / (double)(rounds * kComputeUnits);
+}
+
+// Measured on MI355X over every variant (cubes 1024..10240, 16384^2 x 128,
+// 16384 x 1024 x 1024 both ways, 1000 x 1023 x 999, 256^3):
+//   * once there are at least two 128 x 256 blocks per CU the problem is
+//     throughput-bound, and what decides is each block shape's full-chip rate
+//     times the share of CUs its last round of tiles keeps busy.  Full-chip
+//     rates: 128 x 256 x 16 (two workgroups per CU) 140 TFLOP/s, 128 x 128 x
+//     16 (four per CU) 137, 64 x 64 x 32 122.  So 8192^3 (exactly 8 blocks of
+//     128 x 256 per CU) keeps 128 x 256, 6144^3 and 10240^3 (4.5 and 12.5 per
+//     CU) take 128 x 128, 3072^3 (1.1 per CU) 64 x 64.  Both large blocks
+//     keep A XOR-swizzled in LDS rather than padded: 1-2% faster at 4096^3 to
+//     16384^3 (on 64 x 64 blocks the per-k-step address XOR costs 10-15%
+//     instead, so those stay padded);
 //   * at least one 128 x 128 block per CU: 64 x 64 blocks with two K tiles
 //     in flight (4 workgroups per CU hide each other's latency);
 //   * below that the problem cannot fill the chip and each workgroup's
@@ -131,7 +145,21 @@ int select_variant(int path, int M, int N, int K) {
     if (K < 0) return -3;
     if (path == SGEMM_PATH_VALU) return kValuDefault;
     if (path != SGEMM_PATH_AUTO && path != SGEMM_PATH_MFMA) return SGEMM_ERR_PATH;
-    if (tiles(M, N, 128, 256) >= 2 * kComputeUnits) return kMfmaLarge;
+    if (tiles(M, N, 128, 256) >= 2 * kComputeUnits) {
+        struct { int variant; double rate; } cand[] = {
+            {kMfmaLarge, 140.0}, {kMfmaLarge4, 137.0}, {kMfmaMedium, 122.0}};
+        int best = kMfmaLarge;
+        double best_score = -1.0;
+        for (const auto &c : cand) {
+            const Variant &v = kVariants[c.variant];
+            const double score = c.rate * quantization(tiles(M, N, v.bm, v.bn));
+            if (score > best_score) {
+                best_score = score;
+                best = c.variant;
+            }
+        }
+        return best;
+    }
     if (tiles(M, N, 128, 128) >= kComputeUnits) return kMfmaMedium;
     return kMfmaSmall;
 }

@@ -1,7 +1,9 @@
 """Summaries of rocprofv3 CSV output for the SGEMM kernels.
 
-    python -m fp32_gemm_03_amd.rocprof_summary stats DIR
-        per-kernel call count and durations from DIR/*_kernel_stats.csv
+    python -m fp32_gemm_03_amd.rocprof_summary stats DIR [--last N]
+        per-kernel call count and durations from DIR/*_kernel_stats.csv; with
+        --last, also each kernel's mean over its last N dispatches in
+        DIR/*_kernel_trace.csv (the timed launches after a benchmark's warm-up)
     python -m fp32_gemm_03_amd.rocprof_summary counters DIR [DIR ...]
         per-kernel mean of every counter over its dispatches (*_counter_collection.csv)
     python -m fp32_gemm_03_amd.rocprof_summary traffic --fetch D --write D \\
@@ -39,6 +41,17 @@ def kernel_stats(dirpath):
     return [{"name": r["Name"], "calls": int(r["Calls"]), "total_ns": float(r["TotalDurationNs"]),
              "avg_ns": float(r["AverageNs"]), "min_ns": float(r["MinNs"]),
              "max_ns": float(r["MaxNs"]), "pct": float(r["Percentage"])} for r in rows]
+
+
+def trace_durations(dirpath):
+    """``{kernel_name: [duration_ns per dispatch, in dispatch order]}`` from the kernel trace."""
+    with open(_one(dirpath, "_kernel_trace.csv")) as f:
+        rows = list(csv.DictReader(f))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    out = collections.defaultdict(list)
+    for r in rows:
+        out[r["Kernel_Name"]].append(float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return out
 
 
 def counters(dirpath):
@@ -83,11 +96,15 @@ def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, ke
             "dispatches": len(f[fk]["FETCH_SIZE"])}
 
 
-def _print_stats(dirpath):
+def _print_stats(dirpath, last=0):
+    tr = trace_durations(dirpath) if last else {}
     for r in kernel_stats(dirpath):
         print(f"{r['name']}\n    calls {r['calls']}  avg {r['avg_ns'] / 1e6:.4f} ms  "
               f"min {r['min_ns'] / 1e6:.4f} ms  max {r['max_ns'] / 1e6:.4f} ms  "
               f"total {r['total_ns'] / 1e6:.3f} ms  ({r['pct']:.2f}%)")
+        d = tr.get(r["name"], [])[-last:] if last else []
+        if d:
+            print(f"    last {len(d)} dispatches: avg {statistics.mean(d) / 1e6:.4f} ms")
 
 
 def _print_counters(dirpath):
@@ -102,6 +119,7 @@ def main():
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dir")
+    s.add_argument("--last", type=int, default=0)
     c = sub.add_parser("counters")
     c.add_argument("dirs", nargs="+")
     t = sub.add_parser("traffic")
@@ -111,7 +129,7 @@ def main():
     t.add_argument("--kernel", required=True)
     args = ap.parse_args()
     if args.cmd == "stats":
-        _print_stats(args.dir)
+        _print_stats(args.dir, args.last)
     elif args.cmd == "counters":
         for d in args.dirs:
             print(f"== {d}")

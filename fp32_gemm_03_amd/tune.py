@@ -1,0 +1,115 @@
+"""Time every compiled kernel variant on a set of shapes and compare each
+shape's fastest variant with the one the library's selection picks.
+
+    python -m fp32_gemm_03_amd.tune [--shapes S1,S2,...] [--variants V1,V2,...]
+
+A shape is a named synthetic workload (``square8192_normal`` ...) or MxNxK
+(A, B ~ N(0,1), seed 3, alpha 1, beta 0).  Every launch goes through the C
+ABI on one stream; the time per launch is HIP events around a run of
+launches.  Besides the forced variants, two rows time the library's own
+choice: ``auto`` (``sgemm``) and ``auto+ws`` (``sgemm_ws`` with the workspace
+it asks for, which may split K).  The last block is a table of the selection
+against the best variant per shape: the measurement the selection table in
+``sgemm.hip`` was fitted to, repeatable on any MI355X.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+
+DEFAULT_SHAPES = [
+    "square256_u01", "ragged_1000x1023x999", "square1024_normal", "square2048_normal",
+    "square4096_upm1", "6144x6144x6144", "square8192_normal", "lowk_16384x16384x128",
+    "512x512x8192", "1024x1024x4096", "16384x1024x1024", "1024x16384x1024",
+]
+
+
+def _problem(shape):
+    from . import inputs
+    if shape in inputs.WORKLOADS:
+        return inputs.workload_problem(shape)
+    M, N, K = (int(x) for x in shape.lower().split("x"))
+    return inputs.make_problem(M, N, K, dist="normal", seed=3, name=shape)
+
+
+def _time(launch, flops, stream, target_s=0.1, warmup=3):
+    import torch
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    est_ms = max(e0.elapsed_time(e1), 1e-3)
+    steps = int(min(500, max(5, target_s * 1e3 / est_ms)))
+    e0.record(stream)
+    for _ in range(steps):
+        launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return ms, flops / (ms * 1e-3) / 1e12
+
+
+def tune(shapes, variants=None, out=sys.stdout):
+    import torch
+    import fp32_gemm_03_amd as g
+
+    g.load_library()
+    if variants is None:
+        variants = list(range(g.sgemm_variant_count()))
+    stream = torch.cuda.Stream()
+    table = []
+    for shape in shapes:
+        p = _problem(shape)
+        a, b, c = p.A.cuda(), p.B.cuda(), p.C.cuda()
+        args = (p.M, p.N, p.K, p.alpha, a, p.lda, b, p.ldb, p.beta, c, p.ldc)
+        flops = 2.0 * p.M * p.N * p.K
+        auto = g.sgemm_select_variant(g.SGEMM_PATH_AUTO, p.M, p.N, p.K)
+        rows = {}
+        for v in variants:
+            ms, tf = _time(lambda: g.sgemm_variant(v, *args, stream=stream), flops, stream)
+            rows[g.sgemm_variant_name(v)] = (ms, tf)
+        ms, tf = _time(lambda: g.sgemm(*args, stream=stream), flops, stream)
+        rows["auto"] = (ms, tf)
+        ws_bytes = g.sgemm_workspace_size(p.M, p.N, p.K)
+        ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device="cuda")
+        ms, tf = _time(lambda: g.sgemm_ws(*args, workspace=ws, workspace_bytes=ws_bytes,
+                                          stream=stream), flops, stream)
+        rows["auto+ws"] = (ms, tf)
+        splits = g.sgemm_select_splits(p.M, p.N, p.K)
+        for name, (ms, tf) in rows.items():
+            print(f"{shape:24s} {name:34s} {tf:8.2f} TFLOP/s {ms:10.4f} ms", file=out, flush=True)
+        forced = {k: v for k, v in rows.items() if k not in ("auto", "auto+ws")}
+        best = min(forced, key=lambda k: forced[k][0])
+        table.append({"shape": shape, "M": p.M, "N": p.N, "K": p.K,
+                      "selected": g.sgemm_variant_name(auto), "splits": splits,
+                      "auto_ms": rows["auto"][0], "auto_ws_ms": rows["auto+ws"][0],
+                      "best": best, "best_ms": forced[best][0],
+                      "auto_ws_tflops": rows["auto+ws"][1]})
+        del a, b, c, ws, p
+        torch.cuda.empty_cache()
+    print("\n| shape | selected (splits) | auto+ws TFLOP/s | best forced variant | best / auto+ws time |",
+          file=out)
+    print("|---|---|---|---|---|", file=out)
+    for r in table:
+        print(f"| {r['shape']} | {r['selected']} ({r['splits']}) | {r['auto_ws_tflops']:.2f} | "
+              f"{r['best']} | {r['best_ms'] / r['auto_ws_ms']:.3f} |", file=out)
+    print(json.dumps(table), file=out, flush=True)
+    return table
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--shapes", default=",".join(DEFAULT_SHAPES))
+    ap.add_argument("--variants", default=None, help="comma-separated variant indices (default: all)")
+    args = ap.parse_args()
+    variants = None if args.variants is None else [int(x) for x in args.variants.split(",")]
+    tune(args.shapes.split(","), variants)
+
+
+if __name__ == "__main__":
+    main()

@@ -138,6 +138,21 @@ def test_select_variant_is_a_function_of_the_sizes():
     assert g.sgemm_select_variant(9, 4, 4, 4) == -20
 
 
+def test_large_shapes_pick_the_block_whose_last_round_is_fullest():
+    """Above two 128 x 256 blocks per CU the choice weighs each block's
+    full-chip rate by how full its last round over 256 CUs is."""
+    def block(M, N, K):
+        _, bm, bn = g.sgemm_variant_tile(g.sgemm_select_variant(g.SGEMM_PATH_AUTO, M, N, K))
+        return bm, bn
+    assert block(8192, 8192, 8192) == (128, 256)    # 2048 blocks: 8 per CU
+    assert block(4096, 4096, 4096) == (128, 256)    # 512: 2 per CU
+    assert block(16384, 1024, 1024) == (128, 256)   # 512
+    assert block(6144, 6144, 6144) == (128, 128)    # 1152 would leave half a round
+    assert block(10240, 10240, 10240) == (128, 128)
+    assert block(3072, 3072, 3072) == (64, 64)      # below two 128 x 256 blocks per CU
+    assert block(1024, 1024, 1024) == (64, 64)
+
+
 def test_status_strings():
     assert g.sgemm_status_string(0) == "success"
     assert "too large" in g.sgemm_status_string(-22)
