@@ -28,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -224,6 +225,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": traffic,
                      "kernel_avg_ms": round(avg_kernel_ms, 4),
+                     "kernel_median_ms": round(statistics.median(per_launch), 4),
                      "kernel_min_ms": round(min(per_launch), 4),
                      "algorithmic_flops_per_launch": w.flops,
                      "algorithmic_bytes_per_launch": w.algorithmic_bytes},
@@ -251,7 +253,11 @@ def main():
             del p2
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p)
-    out["device"] = torch.cuda.get_device_name(0)
+    cus, clk, peak_props = g.sgemm_device_fp32_peak(0)
+    out["device"] = {"name": torch.cuda.get_device_name(0),
+                     "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
+                     "compute_units": cus, "peak_clock_mhz": clk / 1e3,
+                     "fp32_peak_tflops_from_props": round(peak_props, 1)}
     print(json.dumps(out), flush=True)
 
 

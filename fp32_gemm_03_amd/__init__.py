@@ -27,7 +27,7 @@ __all__ = [
     "SgemmError", "LibraryNotBuilt", "library_path", "load_library",
     "sgemm", "sgemm_path", "sgemm_variant", "sgemm_variant_count",
     "sgemm_variant_name", "sgemm_variant_path", "sgemm_variant_tile",
-    "sgemm_select_variant", "sgemm_status_string", "variants",
+    "sgemm_select_variant", "sgemm_status_string", "variants", "sgemm_device_fp32_peak",
 ]
 
 SGEMM_PATH_AUTO = 0
@@ -104,6 +104,8 @@ def load_library():
         lib.sgemm_select_variant.restype = i
         lib.sgemm_status_string.argtypes = [i]
         lib.sgemm_status_string.restype = ctypes.c_char_p
+        lib.sgemm_device_fp32_peak.argtypes = [i, vp, vp, vp]
+        lib.sgemm_device_fp32_peak.restype = i
         _lib = lib
         return lib
 
@@ -238,6 +240,16 @@ def sgemm_select_variant(path, M, N, K) -> int:
 
 def sgemm_status_string(status) -> str:
     return load_library().sgemm_status_string(int(status)).decode()
+
+
+def sgemm_device_fp32_peak(device=0):
+    """``(compute_units, clock_khz, tflops)`` of a device from its properties."""
+    lib = load_library()
+    cu, clk, tf = ctypes.c_int(), ctypes.c_int(), ctypes.c_double()
+    st = lib.sgemm_device_fp32_peak(int(device), ctypes.byref(cu), ctypes.byref(clk), ctypes.byref(tf))
+    if st != 0:
+        raise SgemmError(st, "sgemm_device_fp32_peak")
+    return cu.value, clk.value, tf.value
 
 
 def variants():

@@ -103,7 +103,8 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 constexpr int kValuDefault = 0;
 constexpr int kMfmaLarge = 16;   // 128 x 256 x 16, A XOR-swizzled, two workgroups per CU
 constexpr int kMfmaLarge4 = 19;  // 128 x 128 x 16, A XOR-swizzled, four workgroups per CU
-constexpr int kMfmaMedium = 9;   // 64 x 64 x 32, two K tiles in flight
+constexpr int kMfmaMid = 2;      // 128 x 128 x 32, two workgroups per CU
+constexpr int kMfmaMedium = 9;   // 64 x 64 x 32, two K tiles in flight, four workgroups per CU
 constexpr int kMfmaSmall = 10;   // 64 x 64 x 64, fragments three k-steps ahead
 
 // Compute units of an MI355X; the choice of tile is a pure function of the
@@ -122,20 +123,25 @@ double quantization(long long t) {
     return rounds == 0 ? 0.0 : (double)t / (double)(rounds * kComputeUnits);
 }
 
-// Measured on MI355X over every variant (cubes 1024..10240, 16384^2 x 128,
-// 16384 x 1024 x 1024 both ways, 1000 x 1023 x 999, 256^3):
-//   * once there are at least two 128 x 256 blocks per CU the problem is
-//     throughput-bound, and what decides is each block shape's full-chip rate
-//     times the share of CUs its last round of tiles keeps busy.  Full-chip
-//     rates: 128 x 256 x 16 (two workgroups per CU) 140 TFLOP/s, 128 x 128 x
-//     16 (four per CU) 137, 64 x 64 x 32 122.  So 8192^3 (exactly 8 blocks of
-//     128 x 256 per CU) keeps 128 x 256, 6144^3 and 10240^3 (4.5 and 12.5 per
-//     CU) take 128 x 128, 3072^3 (1.1 per CU) 64 x 64.  Both large blocks
-//     keep A XOR-swizzled in LDS rather than padded: 1-2% faster at 4096^3 to
+// Measured on MI355X over every variant with `python -m fp32_gemm_03_amd.tune`
+// (cubes 256..10240, 16384^2 x 128, 1024 x 8192 x 8192, 16384 x 1024 x 1024
+// both ways, 1000 x 1023 x 999, and split-K shapes):
+//   * a block shape reaches its full-chip rate only once there is a tile for
+//     every workgroup slot on the chip (slots = workgroups per CU x 256);
+//     below that its workgroups run alone on their CUs and latency shows.
+//     Among the shapes that qualify, what decides is the full-chip rate times
+//     the share of CUs the last round of tiles keeps busy.  Rates, TFLOP/s:
+//     128 x 256 x 16 (2 per CU) 140, 128 x 128 x 16 (4 per CU) 137,
+//     128 x 128 x 32 (2 per CU) 135, 64 x 64 x 32 (4 per CU) 123.  So 8192^3
+//     (exactly 8 blocks of 128 x 256 per CU) keeps 128 x 256; 6144^3 and
+//     10240^3 (4.5 and 12.5 per CU) take 128 x 128 x 16; 1024 x 8192 x 8192
+//     (one 128 x 256 block per CU) takes 128 x 128 x 32; 3072^3 and 2048^3
+//     take 64 x 64 x 32.  Both 128-row blocks of the large shapes keep A
+//     XOR-swizzled in LDS rather than padded: 1-2% faster at 4096^3 to
 //     16384^3 (on 64 x 64 blocks the per-k-step address XOR costs 10-15%
 //     instead, so those stay padded);
-//   * at least one 128 x 128 block per CU: 64 x 64 blocks with two K tiles
-//     in flight (4 workgroups per CU hide each other's latency);
+//   * no block qualifies but there is a 128 x 128 block per CU: 64 x 64
+//     blocks with two K tiles in flight;
 //   * below that the problem cannot fill the chip and each workgroup's
 //     latency decides: 64 x 64 blocks over BK = 64 with LDS fragments read
 //     three k-steps ahead.
@@ -145,21 +151,26 @@ int select_variant(int path, int M, int N, int K) {
     if (K < 0) return -3;
     if (path == SGEMM_PATH_VALU) return kValuDefault;
     if (path != SGEMM_PATH_AUTO && path != SGEMM_PATH_MFMA) return SGEMM_ERR_PATH;
-    if (tiles(M, N, 128, 256) >= 2 * kComputeUnits) {
-        struct { int variant; double rate; } cand[] = {
-            {kMfmaLarge, 140.0}, {kMfmaLarge4, 137.0}, {kMfmaMedium, 122.0}};
-        int best = kMfmaLarge;
-        double best_score = -1.0;
-        for (const auto &c : cand) {
-            const Variant &v = kVariants[c.variant];
-            const double score = c.rate * quantization(tiles(M, N, v.bm, v.bn));
-            if (score > best_score) {
-                best_score = score;
-                best = c.variant;
-            }
+    struct Candidate {
+        int variant;
+        double rate;         // full-chip TFLOP/s, measured
+        int per_cu;          // workgroups resident per CU
+    };
+    static const Candidate cand[] = {
+        {kMfmaLarge, 140.0, 2}, {kMfmaLarge4, 137.0, 4}, {kMfmaMid, 135.0, 2}, {kMfmaMedium, 123.0, 4}};
+    int best = -1;
+    double best_score = -1.0;
+    for (const Candidate &c : cand) {
+        const Variant &v = kVariants[c.variant];
+        const long long t = tiles(M, N, v.bm, v.bn);
+        if (t < c.per_cu * kComputeUnits) continue;
+        const double score = c.rate * quantization(t);
+        if (score > best_score) {
+            best_score = score;
+            best = c.variant;
         }
-        return best;
     }
+    if (best >= 0) return best;
     if (tiles(M, N, 128, 128) >= kComputeUnits) return kMfmaMedium;
     return kMfmaSmall;
 }
@@ -410,6 +421,18 @@ const char *sgemm_status_string(int status) {
     }
     if (status > 0) return hipGetErrorString((hipError_t)status);
     return "unknown status";
+}
+
+int sgemm_device_fp32_peak(int device, int *compute_units, int *clock_khz, double *tflops) {
+    hipDeviceProp_t prop;
+    const hipError_t e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess) return (int)e;
+    // v_mfma_f32_32x32x2_f32: 32*32*2*2 FLOP per 64 cycles on each of 4 SIMDs
+    // = 256 FLOP per clock per CU, the same rate as the FP32 vector FMA.
+    if (compute_units) *compute_units = prop.multiProcessorCount;
+    if (clock_khz) *clock_khz = prop.clockRate;
+    if (tflops) *tflops = (double)prop.multiProcessorCount * 256.0 * (double)prop.clockRate * 1e3 / 1e12;
+    return SGEMM_OK;
 }
 
 }  // extern "C"

@@ -173,6 +173,13 @@ int sgemm_select_variant(int path, int M, int N, int K);
 /* Static text for a status code returned by any entry point above. */
 const char *sgemm_status_string(int status);
 
+/* The FP32 peak of a device from its properties: compute units x 256 FLOP per
+ * clock (4 SIMDs, each one v_mfma_f32_32x32x2_f32 = 4096 FLOP per 64 cycles,
+ * which is also the FP32 vector FMA rate) x the peak engine clock.  Any output
+ * pointer may be NULL.  Returns 0 or the hipError_t of the property query.
+ * For reports that state the peak they divide by. */
+int sgemm_device_fp32_peak(int device, int *compute_units, int *clock_khz, double *tflops);
+
 #ifdef __cplusplus
 }
 #endif

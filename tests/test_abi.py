@@ -149,7 +149,8 @@ def test_large_shapes_pick_the_block_whose_last_round_is_fullest():
     assert block(16384, 1024, 1024) == (128, 256)   # 512
     assert block(6144, 6144, 6144) == (128, 128)    # 1152 would leave half a round
     assert block(10240, 10240, 10240) == (128, 128)
-    assert block(3072, 3072, 3072) == (64, 64)      # below two 128 x 256 blocks per CU
+    assert block(3072, 3072, 3072) == (64, 64)      # 128 x 128 would leave 3/4 of a round
+    assert block(1024, 8192, 8192) == (128, 128)    # one 128 x 256 block per CU is too few
     assert block(1024, 1024, 1024) == (64, 64)
 
 

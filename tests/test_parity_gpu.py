@@ -224,6 +224,13 @@ def test_runs_on_a_side_stream():
     assert gu.ratio_full(p, out, cached_oracle("square256_u01")) <= TOL
 
 
+def test_device_fp32_peak_from_properties():
+    cu, clk, tf = g.sgemm_device_fp32_peak(0)
+    gu.say("device", cu, "CUs", clk, "kHz", tf, "TFLOP/s")
+    assert cu > 0 and clk > 0
+    assert tf == pytest.approx(cu * 256 * clk * 1e3 / 1e12, rel=1e-12)
+
+
 # ------------------------------------------------------------------ full sizes, sampled
 FULL = ["square2048_normal", "square4096_upm1", "square8192_normal", "lowk_16384x16384x128",
         "square16384_normal"]
