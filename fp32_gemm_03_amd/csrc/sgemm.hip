@@ -100,7 +100,8 @@ const Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-constexpr int kValuDefault = 0;
+constexpr int kValuDefault = 0;  // 128 x 128 x 16, 8 x 8 per lane, four workgroups per CU
+constexpr int kValuWide = 7;     // 128 x 256 x 16, 8 x 16 per lane, two workgroups per CU
 constexpr int kMfmaLarge = 16;   // 128 x 256 x 16, A XOR-swizzled, two workgroups per CU
 constexpr int kMfmaLarge4 = 19;  // 128 x 128 x 16, A XOR-swizzled, four workgroups per CU
 constexpr int kMfmaMid = 2;      // 128 x 128 x 32, two workgroups per CU
@@ -149,7 +150,16 @@ int select_variant(int path, int M, int N, int K) {
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
-    if (path == SGEMM_PATH_VALU) return kValuDefault;
+    if (path == SGEMM_PATH_VALU) {
+        // The 8 x 16 micro-tile reads 25% less LDS per FMA and is 11-19%
+        // faster at 4096^3 and 8192^3, but only where its 128 x 256 blocks
+        // fill whole rounds of the CUs and K is long: at 5120^3 to 10240^3,
+        // at 16384^2 x 128 and with fewer blocks than slots the 8 x 8 tile
+        // is as fast or faster (measured over the same shapes as below).
+        const long long t = tiles(M, N, 128, 256);
+        if (t >= 2 * kComputeUnits && t % kComputeUnits == 0 && K >= 1024) return kValuWide;
+        return kValuDefault;
+    }
     if (path != SGEMM_PATH_AUTO && path != SGEMM_PATH_MFMA) return SGEMM_ERR_PATH;
     struct Candidate {
         int variant;
