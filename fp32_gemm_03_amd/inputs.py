@@ -112,8 +112,10 @@ class Problem:
 
 def make_problem(M, N, K, dist="u01", seed=0, alpha=1.0, beta=0.0, c_fill=None,
                  lda=None, ldb=None, ldc=None, sentinel=float("nan"),
-                 name="") -> Problem:
-    """Draw one problem; see the module docstring for the recipe."""
+                 name="", with_c=True) -> Problem:
+    """Draw one problem; see the module docstring for the recipe.  With
+    ``with_c=False`` no host C is made (``C`` is an empty tensor): for problems
+    whose C is built on the device by the caller."""
     lda = K if lda is None else lda
     ldb = N if ldb is None else ldb
     ldc = N if ldc is None else ldc
@@ -125,7 +127,9 @@ def make_problem(M, N, K, dist="u01", seed=0, alpha=1.0, beta=0.0, c_fill=None,
     else:
         a = _draw(gen, dist, (M, K))
         b = _draw(gen, dist, (K, N))
-    if c_fill is None:
+    if not with_c:
+        c = None
+    elif c_fill is None:
         c = torch.zeros((M, N), dtype=torch.float32)
     elif c_fill == "nan":
         c = torch.full((M, N), float("nan"), dtype=torch.float32)
@@ -134,7 +138,8 @@ def make_problem(M, N, K, dist="u01", seed=0, alpha=1.0, beta=0.0, c_fill=None,
     lda, ldb, ldc = max(lda, 1), max(ldb, 1), max(ldc, 1)
     return Problem(M, N, K, float(alpha), float(beta),
                    _embed(a, lda, sentinel), _embed(b, ldb, sentinel),
-                   _embed(c, ldc, sentinel), lda, ldb, ldc, name=name)
+                   torch.empty((0,), dtype=torch.float32) if c is None else _embed(c, ldc, sentinel),
+                   lda, ldb, ldc, name=name)
 
 
 def workload_problem(name: str, **overrides) -> Problem:

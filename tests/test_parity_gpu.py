@@ -13,6 +13,7 @@ import torch
 import fp32_gemm_03_amd as g
 from fp32_gemm_03_amd import inputs
 from tests import gpu_util as gu
+import oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -276,6 +277,37 @@ def test_huge_leading_dimension_takes_checked_accesses():
                                       check=False) == -23
     torch.cuda.synchronize()
     del oa, ob, oc
+
+
+@pytest.mark.parametrize("path", [g.SGEMM_PATH_AUTO, g.SGEMM_PATH_VALU])
+def test_c_beyond_4_gib(path):
+    """C of 40000 x 32768 floats (5.2 GB): byte offsets into C pass 2^32 and
+    element counts pass 2^30, so any 32-bit address arithmetic would land in
+    the wrong place.  Sub-blocks at the first, middle and last tile rows and
+    columns are checked against the oracle on the same sub-problem."""
+    M, N, K, alpha, beta, c0 = 40000, 32768, 5, 1.5, -0.5, 0.25
+    p = inputs.make_problem(M, N, K, dist="upm1", seed=29, alpha=alpha, beta=beta, with_c=False)
+    a, b = p.A.cuda(), p.B.cuda()
+    c = torch.full((M, N), c0, dtype=torch.float32, device="cuda")
+    gu.say("C beyond 4 GiB", M, N, K, "path", path)
+    g.sgemm_path(path, M, N, K, alpha, a, K, b, N, beta, c, N)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(31)
+    rows = sorted(set([0, 1, 127, 128, 255, 256, M // 2, M - 257, M - 256, M - 129, M - 128, M - 2,
+                       M - 1] + list(rng.integers(0, M, 24))))
+    cols = sorted(set([0, 3, 4, 255, 256, N // 2, N - 257, N - 256, N - 5, N - 4, N - 1]
+                      + list(rng.integers(0, N, 24))))
+    ri = torch.tensor(rows, dtype=torch.long, device="cuda")
+    ci = torch.tensor(cols, dtype=torch.long, device="cuda")
+    got = c.index_select(0, ri).index_select(1, ci).cpu().numpy()
+    del c
+    torch.cuda.empty_cache()
+    As = p.A[rows].contiguous().numpy().reshape(-1)
+    Bs = p.B[:, cols].contiguous().numpy().reshape(-1)
+    Cs = np.full(len(rows) * len(cols), c0, dtype=np.float32)
+    ref, den = oracle.sgemm(len(rows), len(cols), K, alpha, As, K, Bs, len(cols), beta, Cs,
+                            len(cols))
+    assert oracle.max_error_ratio(got, ref, den) <= TOL
 
 
 # ------------------------------------------------------------------ split-K
