@@ -55,6 +55,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace sgk {
 
@@ -359,14 +360,20 @@ struct CStoreBuf {
     }
 
     __device__ __forceinline__ void load(const Args &a, int r, int c, float (&old)[W]) const {
+        load_if(true, a, r, c, old);
+    }
+
+    // With en == false every access is out of range: it reads 0.0 and touches no memory.
+    __device__ __forceinline__ void load_if(bool en, const Args &a, int r, int c, float (&old)[W]) const {
         const uint32_t off = offset(a, r, c);
         if (VEC == 4 || W == 1) {
-            const typename vec_t<W>::type v = buf<W>::load(rc, c < ncols ? off : kOutOfRange);
+            const typename vec_t<W>::type v = buf<W>::load(rc, en && c < ncols ? off : kOutOfRange);
 #pragma unroll
             for (int i = 0; i < W; ++i) old[i] = vget(v, i);
         } else {
 #pragma unroll
-            for (int i = 0; i < W; ++i) old[i] = buf<1>::load(rc, c + i < ncols ? off + 4u * i : kOutOfRange);
+            for (int i = 0; i < W; ++i)
+                old[i] = buf<1>::load(rc, en && c + i < ncols ? off + 4u * i : kOutOfRange);
         }
     }
 
@@ -395,10 +402,14 @@ struct CStorePtr {
     }
 
     __device__ __forceinline__ void load(const Args &a, int r, int c, float (&old)[W]) const {
+        load_if(true, a, r, c, old);
+    }
+
+    __device__ __forceinline__ void load_if(bool en, const Args &a, int r, int c, float (&old)[W]) const {
         const int row = bm + r, col = bn + c;
         const float *p = a.C + (int64_t)row * a.ldc + col;
 #pragma unroll
-        for (int i = 0; i < W; ++i) old[i] = (row < a.M && col + i < a.N) ? p[i] : 0.0f;
+        for (int i = 0; i < W; ++i) old[i] = (en && row < a.M && col + i < a.N) ? p[i] : 0.0f;
     }
 
     __device__ __forceinline__ void store(const Args &a, int r, int c, const float (&out)[W]) const {
@@ -918,6 +929,197 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         st4.init(a, bm, bn);
         epilogue_mfma_staged<decltype(st4), MI, NI, WN>(a, st4, smem + wave * 16 * (WN + 4), wm, wn,
                                                          li, lh, lane, acc);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent MFMA kernel with a deferred epilogue.  One workgroup per slot
+// (the grid is at most the resident workgroups of the chip) walks the tiles
+// blockIdx.x, blockIdx.x + gridDim.x, ... in row-major order and keeps two
+// accumulator sets.  While it runs the K loop of tile i+1 it retires tile i
+// in SL slices: at K step s it requests the old C values of slice s before
+// that step's MFMAs and combines and stores them after, so the epilogue's
+// memory traffic is spread over the next tile's matrix work instead of
+// stalling it.  When K is short and the epilogue's bytes rival
+// the product's FLOPs (16384^2 x 128: 2.2 GB of C traffic against 69 GFLOP)
+// that overlap is the whole game.  The last tile of each workgroup gets the
+// ordinary epilogue.
+// ---------------------------------------------------------------------------
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N-1>{}):
+// a loop whose index is a constant expression in the body.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <class TC, int MI, int NI, int SL>
+struct DeferredSlice {
+    static constexpr int NV = MI * 16;  // vectors of NI columns per lane
+    static constexpr int VS = NV / SL;  // vectors per slice
+    static_assert(NV % SL == 0, "slices");
+
+    __device__ __forceinline__ static void pos(int v, int wm, int wn, int li, int lh, int &r, int &c) {
+        const int i = v / 16, reg = v % 16;
+        r = wm + MI * (8 * (reg >> 2) + 4 * lh + (reg & 3)) + i;
+        c = wn + NI * li;
+    }
+
+    // request the old values of slice S (beta != 0)
+    // The empty asm makes the lane's coordinates opaque at each call, so the
+    // compiler recomputes a slice's C offsets where they are used instead of
+    // hoisting all NV of them out of the K loop into live registers.
+    // With en == false (beta == 0) the requests are out of range: C is not
+    // read and the old values are 0, so the combine below stores alpha * acc.
+    template <int S_>
+    __device__ __forceinline__ static void request(bool en, const Args &a, const TC &st, int wm, int wn,
+                                                   int li, int lh, float (&buf)[VS][NI]) {
+        asm volatile("" : "+v"(li), "+v"(lh));
+#pragma unroll
+        for (int u = 0; u < VS; ++u) {
+            int r, c;
+            pos(S_ * VS + u, wm, wn, li, lh, r, c);
+            st.load_if(en, a, r, c, buf[u]);
+        }
+    }
+
+    // combine slice S with the old values in buf, and store
+    template <int S_>
+    __device__ __forceinline__ static void retire(const Args &a, const TC &st, int wm, int wn, int li,
+                                                  int lh, const floatx16 (&acc)[MI][NI],
+                                                  const float (&buf)[VS][NI]) {
+        asm volatile("" : "+v"(li), "+v"(lh));
+#pragma unroll
+        for (int u = 0; u < VS; ++u) {
+            const int v = S_ * VS + u;
+            int r, c;
+            pos(v, wm, wn, li, lh, r, c);
+            float out[NI];
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                out[j] = fmaf(a.alpha, acc[v / 16][j][v % 16], a.beta * buf[u][j]);
+            st.store(a, r, c, out);
+        }
+    }
+};
+
+template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC, int WPE, bool BUF,
+          int FD, bool SWZ, int SL>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_persistent(Args a) {
+    constexpr int MI = WM / 32, NI = WN / 32;
+    constexpr int WAVES_N = BN / WN;
+    constexpr int NT = (BM / WM) * WAVES_N * 64;
+    constexpr int SA = BM + PADA, SB = BN + PADB;
+    constexpr int STAGE = BK * (SA + SB);
+    typedef Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, NI, 1, SWZ> S;
+    typedef typename S::TC TC;
+    typedef DeferredSlice<TC, MI, NI, SL> D;
+    __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
+    const int ntiles = nbm * nbn;
+    const int wm = (wave / WAVES_N) * WM, wn = (wave % WAVES_N) * WN;
+    const int li = lane & 31, lh = lane >> 5;
+    const int a_col = wm + MI * li;
+    const int b_off = BK * SA + lh * SB + wn + NI * li;
+    const int KT = (a.K + BK - 1) / BK;
+    const bool old = a.beta != 0.0f;
+
+    floatx16 acc0[MI][NI], acc1[MI][NI];
+    typename S::TA ta;
+    typename S::TB tb;
+    TC st_prev;
+    float cbuf[D::VS][NI];
+
+    // One tile into `acc`; with `pending`, retire `prev` (stored through
+    // st_prev) slice by slice along the way.  Leaves st_prev aimed at this tile.
+    auto pass = [&](floatx16(&acc)[MI][NI], const floatx16(&prev)[MI][NI], auto pending_c, int tile) {
+        constexpr bool pending = decltype(pending_c)::value;
+        const int bm = (tile / nbn) * BM, bn = (tile % nbn) * BN;
+        ta.init(a, bm, tid);
+        tb.init(a, bn, tid);
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        if (KT > 0) {
+            ta.template load<0>(a, bm, 0);
+            tb.template load<0>(a, bn, 0);
+            ta.template store<0>(smem, tid);
+            tb.template store<0>(smem + BK * SA, tid);
+        }
+        __syncthreads();
+        for (int t = 0; t < KT; ++t) {
+            const float *st = smem + (t & 1) * STAGE;
+            if (t + 1 < KT) {
+                ta.template load<0>(a, bm, (t + 1) * BK);
+                tb.template load<0>(a, bn, (t + 1) * BK);
+            }
+            // slice t of the previous tile: old values requested before this
+            // step's MFMAs, combined and stored after them
+            if (pending && t < SL) {
+                static_for<SL>([&](auto sc) {
+                    constexpr int s = decltype(sc)::value;
+                    if (s == t) D::template request<s>(old, a, st_prev, wm, wn, li, lh, cbuf);
+                });
+            }
+            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ>(st, a_col, lh, st + b_off, acc);
+            // keep the slice's arithmetic and stores out of the MFMA sequence,
+            // where their values would sit in registers across it
+            if (pending) __builtin_amdgcn_sched_barrier(0);
+            if (pending && t < SL) {
+                static_for<SL>([&](auto sc) {
+                    constexpr int s = decltype(sc)::value;
+                    if (s == t) D::template retire<s>(a, st_prev, wm, wn, li, lh, prev, cbuf);
+                });
+            }
+            if (t + 1 < KT) {
+                float *nx = smem + ((t + 1) & 1) * STAGE;
+                ta.template store<0>(nx, tid);
+                tb.template store<0>(nx + BK * SA, tid);
+            }
+            __syncthreads();
+        }
+        if (pending) {
+            // the slices the K loop did not reach (K < SL * BK)
+            static_for<SL>([&](auto sc) {
+                constexpr int s = decltype(sc)::value;
+                if (s >= KT) {
+                    D::template request<s>(old, a, st_prev, wm, wn, li, lh, cbuf);
+                    D::template retire<s>(a, st_prev, wm, wn, li, lh, prev, cbuf);
+                }
+            });
+        }
+        st_prev.init(a, bm, bn);
+    };
+
+    int tile = blockIdx.x;
+    if (tile >= ntiles) return;
+    pass(acc0, acc1, std::false_type{}, tile);
+    int last = tile;
+    for (;;) {
+        tile += gridDim.x;
+        if (tile >= ntiles) {
+            epilogue_mfma<S, MI, NI>(a, (last / nbn) * BM, (last % nbn) * BN, wm, wn, li, lh, acc0);
+            return;
+        }
+        pass(acc1, acc0, std::true_type{}, tile);
+        last = tile;
+        tile += gridDim.x;
+        if (tile >= ntiles) {
+            epilogue_mfma<S, MI, NI>(a, (last / nbn) * BM, (last % nbn) * BN, wm, wn, li, lh, acc1);
+            return;
+        }
+        pass(acc0, acc1, std::true_type{}, tile);
+        last = tile;
     }
 }
 

@@ -310,6 +310,27 @@ def test_c_beyond_4_gib(path):
     assert oracle.max_error_ratio(got, ref, den) <= TOL
 
 
+def persistent_variants():
+    return [v for v in all_variants() if "_persist" in g.sgemm_variant_name(v)]
+
+
+@pytest.mark.parametrize("variant", persistent_variants())
+@pytest.mark.parametrize("shape", [(2900, 3000, 37), (4000, 4500, 300)])
+@pytest.mark.parametrize("beta", [0.0, -0.75])
+def test_persistent_deferred_epilogue(variant, shape, beta):
+    """More tiles than resident workgroups, so each workgroup retires one
+    tile's epilogue during the next tile's K loop: 552 tiles of 128 x 128
+    (some workgroups take 2) with K shorter than the slices, and 1152 (up to 3
+    per workgroup) with K longer; ragged edges; beta zero and not."""
+    M, N, K = shape
+    p = inputs.make_problem(M, N, K, dist="upm1", seed=37, alpha=1.25, beta=beta, c_fill="upm1")
+    gu.say("persistent", g.sgemm_variant_name(variant), shape, "beta", beta)
+    out = gu.run(p, variant=variant)
+    assert gu.ratio_full(p, out) <= TOL
+    again = gu.run(p, variant=variant)
+    assert np.array_equal(out.view(np.uint32), again.view(np.uint32))
+
+
 # ------------------------------------------------------------------ split-K
 def split_variants():
     return [v for v in all_variants() if g.variant_has_splitk(v)]
