@@ -638,9 +638,13 @@ __device__ __forceinline__ void tile_of(int pid, int nbm, int nbn, int &tm, int 
 // One K tile of MFMAs from one LDS stage.  The fragments of k-step j + FD
 // are read while the MFMAs of step j issue, so the LDS latency hides behind
 // FD steps of matrix work (FD > 1 for wave tiles with few MFMAs per step).
-template <int BK, int MI, int NI, int SA, int SB, int FD, bool SWZ>
+// With CH == 2 the odd k-steps accumulate into acc_odd: a wave with a single
+// 32 x 32 block (MI = NI = 1) otherwise issues a chain of MFMAs that each wait
+// for the previous one's result.  The caller adds acc_odd into acc once, after
+// the K loop.
+template <int BK, int MI, int NI, int SA, int SB, int FD, bool SWZ, int CH = 1>
 __device__ __forceinline__ void mfma_tile(const float *as, int a_col, int lh, const float *bp,
-                                          floatx16 (&acc)[MI][NI]) {
+                                          floatx16 (&acc)[MI][NI], floatx16 (&acc_odd)[MI][NI]) {
     typedef typename vec_t<MI>::type VA;
     typedef typename vec_t<NI>::type VB;
     constexpr int STEPS = BK / 2;
@@ -669,11 +673,21 @@ __device__ __forceinline__ void mfma_tile(const float *as, int a_col, int lh, co
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int jj = 0; jj < NI; ++jj)
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(vget(av[j % RING], i),
-                                                                  vget(bv[j % RING], jj),
-                                                                  acc[i][jj], 0, 0, 0);
+            for (int jj = 0; jj < NI; ++jj) {
+                if (CH == 2 && (j & 1))
+                    acc_odd[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        vget(av[j % RING], i), vget(bv[j % RING], jj), acc_odd[i][jj], 0, 0, 0);
+                else
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        vget(av[j % RING], i), vget(bv[j % RING], jj), acc[i][jj], 0, 0, 0);
+            }
     }
+}
+
+template <int BK, int MI, int NI, int SA, int SB, int FD, bool SWZ>
+__device__ __forceinline__ void mfma_tile(const float *as, int a_col, int lh, const float *bp,
+                                          floatx16 (&acc)[MI][NI]) {
+    mfma_tile<BK, MI, NI, SA, SB, FD, SWZ, 1>(as, a_col, lh, bp, acc, acc);
 }
 
 // Epilogue of a wave's MI x NI accumulator blocks: register r of block
@@ -792,13 +806,16 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     ta.init(a, bm, tid);
     tb.init(a, bn, tid);
 
-    floatx16 acc[MI][NI];
+    // a lone 32 x 32 block per wave gets two accumulation chains (even and
+    // odd k-steps), added together once after the K loop
+    constexpr int CH = MI * NI == 1 ? 2 : 1;
+    floatx16 acc[MI][NI], acc_odd[MI][NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NI; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = acc_odd[i][j][r] = 0.0f;
 
     if (SPLIT && a.phase == 1) {
         // Split-K, phase 1 (one workgroup per tile, after every phase-0
@@ -847,7 +864,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
                 ta.template load<0>(a, bm, kb + (t + 1) * BK);
                 tb.template load<0>(a, bn, kb + (t + 1) * BK);
             }
-            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ>(st, a_col, lh, st + b_off, acc);
+            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ, CH>(st, a_col, lh, st + b_off, acc, acc_odd);
             if (t + 1 < KT) {
                 float *nx = smem + ((t + 1) & 1) * STAGE;
                 ta.template store<0>(nx, tid);
@@ -879,7 +896,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         }
         for (int t = 0; t < KT; t += 2) {
             // tile t from LDS stage 0; tile t+1 (register stage 1) -> LDS stage 1
-            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ>(smem, a_col, lh, smem + b_off, acc);
+            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ, CH>(smem, a_col, lh, smem + b_off, acc, acc_odd);
             if (t + 1 < KT) {
                 ta.template store<R>(smem + STAGE, tid);
                 tb.template store<R>(smem + STAGE + BK * SA, tid);
@@ -891,7 +908,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
                 tb.template load<R>(a, bn, kb + (t + 3) * BK);
             }
             // tile t+1 from LDS stage 1; tile t+2 (register stage 0) -> LDS stage 0
-            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ>(smem + STAGE, a_col, lh, smem + STAGE + b_off, acc);
+            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ, CH>(smem + STAGE, a_col, lh, smem + STAGE + b_off, acc,
+                                                         acc_odd);
             if (t + 2 < KT) {
                 ta.template store<0>(smem, tid);
                 tb.template store<0>(smem + BK * SA, tid);
@@ -902,6 +920,13 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
                 tb.template load<0>(a, bn, kb + (t + 4) * BK);
             }
         }
+    }
+
+    if (CH == 2) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) acc[i][j] += acc_odd[i][j];
     }
 
     if (SPLIT) {
