@@ -216,3 +216,16 @@ def test_splitk_argument_codes():
     assert call(split_v, 2, ws=0x10010) == -24         # not 256-byte aligned
     assert "workspace" in g.sgemm_status_string(-24)
     assert "split" in g.sgemm_status_string(-25)
+
+
+def test_grid_too_large_is_refused_before_any_hip_call():
+    # 2^31 - 1 square: tiles of every variant number far more than INT_MAX, so
+    # the launch is refused with SGEMM_ERR_TOO_LARGE before anything touches
+    # the (never dereferenced) pointers or a GPU
+    big = 2 ** 31 - 1
+    args = (big, big, 1, 1.0, 256, 1, 256, big, 0.0, 256, big)
+    assert g.sgemm(*args, stream=0, check=False) == -22
+    assert g.sgemm_path(g.SGEMM_PATH_VALU, *args, stream=0, check=False) == -22
+    for v in range(g.sgemm_variant_count()):
+        assert g.sgemm_variant(v, *args, stream=0, check=False) == -22, v
+

@@ -225,6 +225,24 @@ def test_runs_on_a_side_stream():
     assert gu.ratio_full(p, out, cached_oracle("square256_u01")) <= TOL
 
 
+@pytest.mark.parametrize("mn", [(0, 37), (29, 0), (0, 0)])
+def test_empty_c_launches_nothing_and_touches_nothing(mn):
+    M, N = mn
+    K = 19
+    p = inputs.make_problem(max(M, 1), max(N, 1), K, dist="upm1", seed=41, beta=0.5, c_fill="upm1")
+    oa, _, a = gu.to_gpu(p.A)
+    ob, _, b = gu.to_gpu(p.B)
+    oc, _, c = gu.to_gpu(p.C)
+    before = [o.cpu().numpy().copy() for o in (oa, ob, oc)]
+    gu.say("empty", M, N, K)
+    for v in all_variants():
+        assert g.sgemm_variant(v, M, N, K, 1.0, a, K, b, max(N, 1), 0.5, c, max(N, 1)) == 0
+    assert g.sgemm(M, N, K, 1.0, a, K, b, max(N, 1), 0.5, c, max(N, 1)) == 0
+    torch.cuda.synchronize()
+    for o, h in zip((oa, ob, oc), before):
+        assert np.array_equal(o.cpu().numpy().view(np.uint32), h.view(np.uint32))
+
+
 def test_device_fp32_peak_from_properties():
     cu, clk, tf = g.sgemm_device_fp32_peak(0)
     gu.say("device", cu, "CUs", clk, "kHz", tf, "TFLOP/s")
