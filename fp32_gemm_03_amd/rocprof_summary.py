@@ -1,9 +1,11 @@
 """Summaries of rocprofv3 CSV output for the SGEMM kernels.
 
-    python -m fp32_gemm_03_amd.rocprof_summary stats DIR [--last N]
+    python -m fp32_gemm_03_amd.rocprof_summary stats DIR [--last N] [--by-grid]
         per-kernel call count and durations from DIR/*_kernel_stats.csv; with
         --last, also each kernel's mean over its last N dispatches in
-        DIR/*_kernel_trace.csv (the timed launches after a benchmark's warm-up)
+        DIR/*_kernel_trace.csv (the timed launches after a benchmark's warm-up);
+        with --by-grid, each kernel's dispatches split by grid size (one
+        kernel launched on several problem shapes)
     python -m fp32_gemm_03_amd.rocprof_summary counters DIR [DIR ...]
         per-kernel mean of every counter over its dispatches (*_counter_collection.csv)
     python -m fp32_gemm_03_amd.rocprof_summary traffic --fetch D --write D \\
@@ -54,6 +56,18 @@ def trace_durations(dirpath):
     return out
 
 
+def trace_by_grid(dirpath):
+    """``{(kernel_name, grid_x): [duration_ns per dispatch, in dispatch order]}``."""
+    with open(_one(dirpath, "_kernel_trace.csv")) as f:
+        rows = list(csv.DictReader(f))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    out = collections.defaultdict(list)
+    for r in rows:
+        out[(r["Kernel_Name"], int(r["Grid_Size_X"]))].append(
+            float(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return out
+
+
 def counters(dirpath):
     """``{kernel_name: {counter: [value per dispatch]}}`` plus durations under '_duration_ns'."""
     with open(_one(dirpath, "_counter_collection.csv")) as f:
@@ -96,8 +110,9 @@ def traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, ke
             "dispatches": len(f[fk]["FETCH_SIZE"])}
 
 
-def _print_stats(dirpath, last=0):
+def _print_stats(dirpath, last=0, by_grid=False):
     tr = trace_durations(dirpath) if last else {}
+    grids = trace_by_grid(dirpath) if by_grid else {}
     for r in kernel_stats(dirpath):
         print(f"{r['name']}\n    calls {r['calls']}  avg {r['avg_ns'] / 1e6:.4f} ms  "
               f"min {r['min_ns'] / 1e6:.4f} ms  max {r['max_ns'] / 1e6:.4f} ms  "
@@ -105,6 +120,12 @@ def _print_stats(dirpath, last=0):
         d = tr.get(r["name"], [])[-last:] if last else []
         if d:
             print(f"    last {len(d)} dispatches: avg {statistics.mean(d) / 1e6:.4f} ms")
+        for (name, gx), ds in sorted(grids.items(), key=lambda kv: kv[0][1]):
+            if name != r["name"]:
+                continue
+            tail = ds[-last:] if last else ds
+            print(f"    grid {gx} threads: {len(ds)} dispatches, avg {statistics.mean(ds) / 1e6:.4f} ms"
+                  + (f", last {len(tail)} avg {statistics.mean(tail) / 1e6:.4f} ms" if last else ""))
 
 
 def _print_counters(dirpath):
@@ -120,6 +141,7 @@ def main():
     s = sub.add_parser("stats")
     s.add_argument("dir")
     s.add_argument("--last", type=int, default=0)
+    s.add_argument("--by-grid", action="store_true")
     c = sub.add_parser("counters")
     c.add_argument("dirs", nargs="+")
     t = sub.add_parser("traffic")
@@ -129,7 +151,7 @@ def main():
     t.add_argument("--kernel", required=True)
     args = ap.parse_args()
     if args.cmd == "stats":
-        _print_stats(args.dir, args.last)
+        _print_stats(args.dir, args.last, args.by_grid)
     elif args.cmd == "counters":
         for d in args.dirs:
             print(f"== {d}")
