@@ -3,7 +3,9 @@
 // choice of variant, and the launch on the caller's stream.
 //
 // The library holds no state: every call validates, picks a variant and
-// enqueues one kernel.  Nothing here allocates device memory.
+// enqueues one kernel (two for split-K: the partial tiles, then their sum in
+// a fixed order).  Nothing here allocates device memory; split-K writes its
+// partial tiles to a workspace the caller owns.
 #include "sgemm.h"
 
 #include <limits.h>
