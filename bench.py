@@ -28,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -50,12 +51,22 @@ WORKLOAD = "square8192_normal"
 SECONDARY = ("square4096_upm1", "lowk_16384x16384x128")
 
 
+def _code_tokens(text: str) -> str:
+    """C/C++ source with comments removed and whitespace collapsed, so that a
+    comment edit does not count as a kernel change (string literals in these
+    sources hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the code (not the comments) the library is built from."""
     from fp32_gemm_03_amd import build as b
     h = hashlib.sha256()
     for p in sorted(b.DEPENDS):
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(_code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 
