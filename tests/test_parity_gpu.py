@@ -349,6 +349,47 @@ def test_persistent_deferred_epilogue(variant, shape, beta):
     assert np.array_equal(out.view(np.uint32), again.view(np.uint32))
 
 
+def random_configs(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M, N, K = (int(x) for x in rng.integers(1, 700, 3))
+        if i % 4 == 3:  # few tiles, long K: sgemm_ws splits K
+            M, N = (int(x) for x in rng.integers(1, 300, 2))
+            K = int(rng.integers(2048, 6000))
+        alpha = float(rng.choice([1.0, -0.5, 2.0, 0.0, 1.25]))
+        beta = float(rng.choice([0.0, 1.0, -0.75, 0.5]))
+        pads = [int(x) for x in rng.integers(0, 6, 3)]
+        offs = tuple(int(x) for x in rng.integers(0, 4, 3))
+        out.append((i, M, N, K, alpha, beta, pads, offs))
+    return out
+
+
+@pytest.mark.parametrize("cfg", random_configs(60, 2024), ids=lambda c: f"r{c[0]}")
+def test_random_configs_every_entry_point(cfg):
+    """Seeded random sizes, leading-dimension padding, base misalignment and
+    alpha/beta, through sgemm, sgemm_ws (which may split K) and the VALU path."""
+    i, M, N, K, alpha, beta, pads, offs = cfg
+    p = inputs.make_problem(M, N, K, dist="upm1", seed=100 + i, alpha=alpha, beta=beta,
+                            c_fill="upm1", lda=K + pads[0], ldb=N + pads[1], ldc=N + pads[2])
+    ref_den = gu.oracle_full(p)
+    gu.say("random", cfg)
+    out = gu.run(p, offsets=offs)
+    assert gu.ratio_full(p, out, ref_den) <= TOL
+    out = gu.run(p, path=g.SGEMM_PATH_VALU, offsets=offs)
+    assert gu.ratio_full(p, out, ref_den) <= TOL
+    # sgemm_ws with the workspace it asks for (NaN-filled: any contents)
+    need = g.sgemm_workspace_size(M, N, K)
+    ws = torch.full((max(need, 256) // 4 + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    oa, _, a = gu.to_gpu(p.A, offs[0])
+    ob, _, b = gu.to_gpu(p.B, offs[1])
+    oc, first, c = gu.to_gpu(p.C, offs[2])
+    g.sgemm_ws(M, N, K, alpha, a, p.lda, b, p.ldb, beta, c, p.ldc, workspace=ws)
+    torch.cuda.synchronize()
+    got = oc.cpu().numpy()[first:first + p.C.numel()].reshape(p.C.shape)
+    assert oracle.max_error_ratio(got[:, :N], *ref_den) <= TOL
+
+
 # ------------------------------------------------------------------ split-K
 def split_variants():
     return [v for v in all_variants() if g.variant_has_splitk(v)]
