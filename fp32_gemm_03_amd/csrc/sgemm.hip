@@ -114,11 +114,18 @@ const Variant kVariants[] = {
     // 0.71 ms against 0.67 for 16, and 10% below 19 where the epilogue does
     // not matter, so it is not chosen by shape.
     MFMA_CFG_PERSISTENT(128, 128, 16, 64, 64, 2, 1, 8, 2, "_persist"),
+    // 21: variant 1 with the next K tile's loads and LDS stores interleaved
+    // into the MFMA sequence (one workgroup per CU, so nothing else hides them)
+    {"mfma_256x256x32_w128x128_il", SGEMM_PATH_MFMA, 256, 256, 32, 256,
+     sgk::sgemm_mfma<256, 256, 32, 128, 128, 4, 0, 4, 1, true, 1, 1, 0, false, 0, false, true>,
+     sgk::sgemm_mfma<256, 256, 32, 128, 128, 4, 0, 1, 1, true, 1, 1, 0, false, 0, false, true>,
+     sgk::sgemm_mfma<256, 256, 32, 128, 128, 4, 0, 1, 1, false, 1, 1, 0, false, 0, false, true>, nullptr, nullptr},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 constexpr int kValuDefault = 0;  // 128 x 128 x 16, 8 x 8 per lane, four workgroups per CU
 constexpr int kValuWide = 7;     // 128 x 256 x 16, 8 x 16 per lane, two workgroups per CU
+constexpr int kMfmaHuge = 21;    // 256 x 256 x 32, interleaved schedule, one workgroup per CU
 constexpr int kMfmaLarge = 16;   // 128 x 256 x 16, A XOR-swizzled, two workgroups per CU
 constexpr int kMfmaLarge4 = 19;  // 128 x 128 x 16, A XOR-swizzled, four workgroups per CU
 constexpr int kMfmaMid = 2;      // 128 x 128 x 32, two workgroups per CU
@@ -149,15 +156,18 @@ double quantization(long long t) {
 //     below that its workgroups run alone on their CUs and latency shows.
 //     Among the shapes that qualify, what decides is the full-chip rate times
 //     the share of CUs the last round of tiles keeps busy.  Rates, TFLOP/s:
-//     128 x 256 x 16 (2 per CU) 140, 128 x 128 x 16 (4 per CU) 137,
-//     128 x 128 x 32 (2 per CU) 135, 64 x 64 x 32 (4 per CU) 123.  So 8192^3
-//     (exactly 8 blocks of 128 x 256 per CU) keeps 128 x 256; 6144^3 and
-//     10240^3 (4.5 and 12.5 per CU) take 128 x 128 x 16; 1024 x 8192 x 8192
-//     (one 128 x 256 block per CU) takes 128 x 128 x 32; 3072^3 and 2048^3
-//     take 64 x 64 x 32.  Both 128-row blocks of the large shapes keep A
-//     XOR-swizzled in LDS rather than padded: 1-2% faster at 4096^3 to
-//     16384^3 (on 64 x 64 blocks the per-k-step address XOR costs 10-15%
-//     instead, so those stay padded);
+//     256 x 256 x 32 interleaved (1 per CU) 143.5, 128 x 256 x 16 (2 per CU)
+//     140, 128 x 128 x 16 (4 per CU) 137, 128 x 128 x 32 (2 per CU) 135,
+//     64 x 64 x 32 (4 per CU) 123.  The 256 x 256 block has no second
+//     workgroup to hide its epilogue, so it needs K >= 512 (at 16384^2 x 128
+//     it runs 86 TFLOP/s against 99).  So 8192^3, 4096^3 and 16384 x 1024 x
+//     1024 (whole rounds of 256 x 256 blocks) take 256 x 256; 6144^3 and
+//     10240^3 (0.75 and 0.89 of a last round) take 128 x 128 x 16;
+//     1024 x 8192 x 8192 (one 128 x 256 block per CU) takes 128 x 128 x 32;
+//     3072^3 and 2048^3 take 64 x 64 x 32; the low-K square takes 128 x 256.
+//     The 128-row blocks keep A XOR-swizzled in LDS rather than padded: 1-2%
+//     faster at 4096^3 to 16384^3 (on 64 x 64 and 256-row blocks the address
+//     XOR costs more than it saves, so those stay padded);
 //   * no block qualifies but there is a 128 x 128 block per CU: 64 x 64
 //     blocks with two K tiles in flight;
 //   * below that the problem cannot fill the chip and each workgroup's
@@ -182,15 +192,19 @@ int select_variant(int path, int M, int N, int K) {
         int variant;
         double rate;         // full-chip TFLOP/s, measured
         int per_cu;          // workgroups resident per CU
+        int min_k;           // shortest K at which that rate holds
     };
-    static const Candidate cand[] = {
-        {kMfmaLarge, 140.0, 2}, {kMfmaLarge4, 137.0, 4}, {kMfmaMid, 135.0, 2}, {kMfmaMedium, 123.0, 4}};
+    static const Candidate cand[] = {{kMfmaHuge, 143.5, 1, 512},
+                                     {kMfmaLarge, 140.0, 2, 0},
+                                     {kMfmaLarge4, 137.0, 4, 0},
+                                     {kMfmaMid, 135.0, 2, 0},
+                                     {kMfmaMedium, 123.0, 4, 0}};
     int best = -1;
     double best_score = -1.0;
     for (const Candidate &c : cand) {
         const Variant &v = kVariants[c.variant];
         const long long t = tiles(M, N, v.bm, v.bn);
-        if (t < c.per_cu * kComputeUnits) continue;
+        if (t < c.per_cu * kComputeUnits || K < c.min_k) continue;
         const double score = c.rate * quantization(t);
         if (score > best_score) {
             best_score = score;

@@ -181,13 +181,16 @@ struct ATileGeom {
 
     template <int S>
     __device__ __forceinline__ void store(float *As, int tid) const {
-        const int k = tid % BK;
-        float *row = As + k * SA;
 #pragma unroll
-        for (int p = 0; p < PER; ++p) {
-            const int m = 4 * (tid / BK) + p * ROWS_PER_PASS;
-            *reinterpret_cast<float4 *>(row + (SWZ ? swz_col(k, m) : m)) = reg[S][p];
-        }
+        for (int p = 0; p < PER; ++p) store_piece<S>(As, tid, p);
+    }
+
+    // one 128-bit LDS store: rows 4 (tid / BK) + p ROWS_PER_PASS + {0..3}
+    template <int S>
+    __device__ __forceinline__ void store_piece(float *As, int tid, int p) const {
+        const int k = tid % BK;
+        const int m = 4 * (tid / BK) + p * ROWS_PER_PASS;
+        *reinterpret_cast<float4 *>(As + k * SA + (SWZ ? swz_col(k, m) : m)) = reg[S][p];
     }
 };
 
@@ -209,18 +212,22 @@ struct ATileBuf : ATileGeom<BM, BK, NT, PADA, STAGES, SWZ> {
     }
 
     template <int S>
-    __device__ __forceinline__ void load(const Args &a, int, int k0) {
+    __device__ __forceinline__ void load(const Args &a, int bm, int k0) {
+#pragma unroll
+        for (int p = 0; p < G::PER; ++p) load_piece<S>(a, bm, k0, p);
+    }
+
+    // the 4 rows of one 128-bit LDS store (rows >= M and columns >= K read 0.0)
+    template <int S>
+    __device__ __forceinline__ void load_piece(const Args &a, int, int k0, int p) {
         const bool kin = (k0 + col) < a.K;
         uint32_t o[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) o[c] = kin ? off[c] + 4u * (uint32_t)k0 : kOutOfRange;
-#pragma unroll
-        for (int p = 0; p < G::PER; ++p) {
-            G::reg[S][p].x = buf<1>::load(rsrc, o[0] + p * pass);
-            G::reg[S][p].y = buf<1>::load(rsrc, o[1] + p * pass);
-            G::reg[S][p].z = buf<1>::load(rsrc, o[2] + p * pass);
-            G::reg[S][p].w = buf<1>::load(rsrc, o[3] + p * pass);
-        }
+        for (int c = 0; c < 4; ++c) o[c] = kin ? off[c] + 4u * (uint32_t)k0 + p * pass : kOutOfRange;
+        G::reg[S][p].x = buf<1>::load(rsrc, o[0]);
+        G::reg[S][p].y = buf<1>::load(rsrc, o[1]);
+        G::reg[S][p].z = buf<1>::load(rsrc, o[2]);
+        G::reg[S][p].w = buf<1>::load(rsrc, o[3]);
     }
 };
 
@@ -236,17 +243,20 @@ struct ATilePtr : ATileGeom<BM, BK, NT, PADA, STAGES, SWZ> {
 
     template <int S>
     __device__ __forceinline__ void load(const Args &a, int bm, int k0) {
-        const bool kin = (k0 + col) < a.K;
 #pragma unroll
-        for (int p = 0; p < G::PER; ++p) {
-            const int row = bm + r0 + p * G::ROWS_PER_PASS;
-            const float *q = a.A + (int64_t)row * a.lda + k0 + col;
-            const int rl = a.M - row;
-            G::reg[S][p].x = (kin && rl > 0) ? q[0] : 0.0f;
-            G::reg[S][p].y = (kin && rl > 1) ? q[a.lda] : 0.0f;
-            G::reg[S][p].z = (kin && rl > 2) ? q[2 * a.lda] : 0.0f;
-            G::reg[S][p].w = (kin && rl > 3) ? q[3 * a.lda] : 0.0f;
-        }
+        for (int p = 0; p < G::PER; ++p) load_piece<S>(a, bm, k0, p);
+    }
+
+    template <int S>
+    __device__ __forceinline__ void load_piece(const Args &a, int bm, int k0, int p) {
+        const bool kin = (k0 + col) < a.K;
+        const int row = bm + r0 + p * G::ROWS_PER_PASS;
+        const float *q = a.A + (int64_t)row * a.lda + k0 + col;
+        const int rl = a.M - row;
+        G::reg[S][p].x = (kin && rl > 0) ? q[0] : 0.0f;
+        G::reg[S][p].y = (kin && rl > 1) ? q[a.lda] : 0.0f;
+        G::reg[S][p].z = (kin && rl > 2) ? q[2 * a.lda] : 0.0f;
+        G::reg[S][p].w = (kin && rl > 3) ? q[3 * a.lda] : 0.0f;
     }
 };
 
@@ -277,10 +287,14 @@ struct BTileGeom {
 
     template <int S>
     __device__ __forceinline__ void store(float *Bs, int tid) const {
-        float *dst = Bs + (tid / PER_ROW) * SB + (tid % PER_ROW) * VEC;
 #pragma unroll
-        for (int p = 0; p < PER; ++p)
-            *reinterpret_cast<V *>(dst + dk(p) * SB + dn(p)) = reg[S][p];
+        for (int p = 0; p < PER; ++p) store_piece<S>(Bs, tid, p);
+    }
+
+    template <int S>
+    __device__ __forceinline__ void store_piece(float *Bs, int tid, int p) const {
+        float *dst = Bs + (tid / PER_ROW) * SB + (tid % PER_ROW) * VEC;
+        *reinterpret_cast<V *>(dst + dk(p) * SB + dn(p)) = reg[S][p];
     }
 };
 
@@ -302,11 +316,19 @@ struct BTileBuf : BTileGeom<BN, BK, NT, PADB, VEC, STAGES> {
         // Rows k0.. of B from column bn, up to B's last element: rows >= K
         // read 0.0.  With VEC == 4, N and ldb are multiples of 4, so no
         // 128-bit piece straddles the end.
-        const rsrc_t r = make_rsrc(a.B + (int64_t)k0 * a.ldb + bn,
-                                   ((int64_t)(a.K - k0 - 1) * a.ldb + (a.N - bn)) * 4);
+        const rsrc_t r = rows(a, bn, k0);
 #pragma unroll
         for (int p = 0; p < G::PER; ++p)
             G::reg[S][p] = buf<VEC>::load(r, off + G::dk(p) * ldb4 + G::dn(p) * 4);
+    }
+
+    __device__ __forceinline__ rsrc_t rows(const Args &a, int bn, int k0) const {
+        return make_rsrc(a.B + (int64_t)k0 * a.ldb + bn, ((int64_t)(a.K - k0 - 1) * a.ldb + (a.N - bn)) * 4);
+    }
+
+    template <int S>
+    __device__ __forceinline__ void load_piece(const Args &a, int bn, int k0, int p) {
+        G::reg[S][p] = buf<VEC>::load(rows(a, bn, k0), off + G::dk(p) * ldb4 + G::dn(p) * 4);
     }
 };
 
@@ -323,15 +345,18 @@ struct BTilePtr : BTileGeom<BN, BK, NT, PADB, VEC, STAGES> {
     template <int S>
     __device__ __forceinline__ void load(const Args &a, int bn, int k0) {
 #pragma unroll
-        for (int p = 0; p < G::PER; ++p) {
-            const int n = bn + n_first + G::dn(p);
-            const int k = k0 + k_first + G::dk(p);
-            // VEC == 4 only when N % 4 == 0: a piece is all in or all out
-            if (n < a.N && k < a.K)
-                G::reg[S][p] = *reinterpret_cast<const typename G::V *>(a.B + (int64_t)k * a.ldb + n);
-            else
-                G::reg[S][p] = typename G::V{};
-        }
+        for (int p = 0; p < G::PER; ++p) load_piece<S>(a, bn, k0, p);
+    }
+
+    template <int S>
+    __device__ __forceinline__ void load_piece(const Args &a, int bn, int k0, int p) {
+        const int n = bn + n_first + G::dn(p);
+        const int k = k0 + k_first + G::dk(p);
+        // VEC == 4 only when N % 4 == 0: a piece is all in or all out
+        if (n < a.N && k < a.K)
+            G::reg[S][p] = *reinterpret_cast<const typename G::V *>(a.B + (int64_t)k * a.ldb + n);
+        else
+            G::reg[S][p] = typename G::V{};
     }
 };
 
@@ -642,9 +667,18 @@ __device__ __forceinline__ void tile_of(int pid, int nbm, int nbn, int &tm, int 
 // 32 x 32 block (MI = NI = 1) otherwise issues a chain of MFMAs that each wait
 // for the previous one's result.  The caller adds acc_odd into acc once, after
 // the K loop.
-template <int BK, int MI, int NI, int SA, int SB, int FD, bool SWZ, int CH = 1>
+struct NoHook {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+
+// hook(j) runs after the first MFMA of k-step j, fenced so that it stays
+// there: other work (the next K tile's global loads and LDS stores) issued
+// while the matrix pipe is busy instead of before or after the MFMAs.
+template <int BK, int MI, int NI, int SA, int SB, int FD, bool SWZ, int CH = 1, class Hook = NoHook>
 __device__ __forceinline__ void mfma_tile(const float *as, int a_col, int lh, const float *bp,
-                                          floatx16 (&acc)[MI][NI], floatx16 (&acc_odd)[MI][NI]) {
+                                          floatx16 (&acc)[MI][NI], floatx16 (&acc_odd)[MI][NI],
+                                          Hook hook = Hook()) {
+    constexpr bool HOOKED = !std::is_same<Hook, NoHook>::value;
     typedef typename vec_t<MI>::type VA;
     typedef typename vec_t<NI>::type VB;
     constexpr int STEPS = BK / 2;
@@ -680,6 +714,11 @@ __device__ __forceinline__ void mfma_tile(const float *as, int a_col, int lh, co
                 else
                     acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                         vget(av[j % RING], i), vget(bv[j % RING], jj), acc[i][jj], 0, 0, 0);
+                if (HOOKED && i == 0 && jj == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    hook(j);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
     }
 }
@@ -773,7 +812,7 @@ __device__ __forceinline__ void epilogue_mfma_staged(const Args &a, const TC4 &s
 // too short to cover one global-load latency).  FD is the LDS fragment
 // prefetch distance in k-steps.
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC, int WPE, bool BUF,
-          int PD, int FD, int ORDER, bool SPLIT, int EPI, bool SWZ>
+          int PD, int FD, int ORDER, bool SPLIT, int EPI, bool SWZ, bool IL = false>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -850,7 +889,53 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     const int KT = SPLIT ? (int)((int64_t)KT_ALL * (split + 1) / a.splits) - kt0 : KT_ALL;
     const int kb = kt0 * BK;
 
-    if (PD == 1) {
+    if constexpr (IL) {
+        // Interleaved schedule (PD == 1, no split): the loads of K tile t+1
+        // are issued in pieces after the first MFMA of the first k-steps of
+        // tile t, and stored to the other LDS stage in pieces over the last
+        // k-steps, so the matrix pipe is fed throughout.  The loads are not
+        // conditional: past K they read 0.0 into a stage nobody reads.
+        static_assert(PD == 1 && !SPLIT, "interleaved schedule: one register stage, no split");
+        constexpr int STEPS = BK / 2;
+        constexpr int PA = S::TA::PER, PB = S::TB::PER, NP = PA + PB;
+        // the first quarter of the k-steps carries the loads, the second half
+        // the stores (measured best of quarter/half/eighth splits)
+        constexpr int LSTEPS = STEPS / 4 > 0 ? STEPS / 4 : 1;
+        constexpr int SSTEPS = STEPS / 2 > 0 ? STEPS / 2 : 1;
+        constexpr int LPER = (NP + LSTEPS - 1) / LSTEPS, SPER = (NP + SSTEPS - 1) / SSTEPS;
+        if (KT > 0) {
+            ta.template load<0>(a, bm, 0);
+            tb.template load<0>(a, bn, 0);
+            ta.template store<0>(smem, tid);
+            tb.template store<0>(smem + BK * SA, tid);
+        }
+        __syncthreads();
+        for (int t = 0; t < KT; ++t) {
+            const float *st = smem + (t & 1) * STAGE;
+            float *nx = smem + ((t + 1) & 1) * STAGE;
+            const int kn = (t + 1) * BK;
+            auto hook = [&](int j) {
+                if (j < LSTEPS) {
+#pragma unroll
+                    for (int q = 0; q < LPER; ++q) {
+                        const int piece = j * LPER + q;
+                        if (piece < PA) ta.template load_piece<0>(a, bm, kn, piece);
+                        else if (piece < NP) tb.template load_piece<0>(a, bn, kn, piece - PA);
+                    }
+                }
+                if (j >= STEPS - SSTEPS) {
+#pragma unroll
+                    for (int q = 0; q < SPER; ++q) {
+                        const int piece = (j - (STEPS - SSTEPS)) * SPER + q;
+                        if (piece < PA) ta.template store_piece<0>(nx, tid, piece);
+                        else if (piece < NP) tb.template store_piece<0>(nx + BK * SA, tid, piece - PA);
+                    }
+                }
+            };
+            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ, CH>(st, a_col, lh, st + b_off, acc, acc_odd, hook);
+            __syncthreads();
+        }
+    } else if (PD == 1) {
         if (KT > 0) {
             ta.template load<0>(a, bm, kb);
             tb.template load<0>(a, bn, kb);

@@ -144,9 +144,10 @@ def test_large_shapes_pick_the_block_whose_last_round_is_fullest():
     def block(M, N, K):
         _, bm, bn = g.sgemm_variant_tile(g.sgemm_select_variant(g.SGEMM_PATH_AUTO, M, N, K))
         return bm, bn
-    assert block(8192, 8192, 8192) == (128, 256)    # 2048 blocks: 8 per CU
-    assert block(4096, 4096, 4096) == (128, 256)    # 512: 2 per CU
-    assert block(16384, 1024, 1024) == (128, 256)   # 512
+    assert block(8192, 8192, 8192) == (256, 256)    # 1024 blocks of 256 x 256: 4 per CU
+    assert block(4096, 4096, 4096) == (256, 256)    # 256: 1 per CU
+    assert block(16384, 1024, 1024) == (256, 256)   # 256
+    assert block(16384, 16384, 128) == (128, 256)   # short K: the 256 x 256 block is left out
     assert block(6144, 6144, 6144) == (128, 128)    # 1152 would leave half a round
     assert block(10240, 10240, 10240) == (128, 128)
     assert block(3072, 3072, 3072) == (64, 64)      # 128 x 128 would leave 3/4 of a round
