@@ -156,7 +156,7 @@ double quantization(long long t) {
 //     below that its workgroups run alone on their CUs and latency shows.
 //     Among the shapes that qualify, what decides is the full-chip rate times
 //     the share of CUs the last round of tiles keeps busy.  Rates, TFLOP/s:
-//     256 x 256 x 32 interleaved (1 per CU) 143.5, 128 x 256 x 16 (2 per CU)
+//     256 x 256 x 32 interleaved (1 per CU) 145.5, 128 x 256 x 16 (2 per CU)
 //     140, 128 x 128 x 16 (4 per CU) 137, 128 x 128 x 32 (2 per CU) 135,
 //     64 x 64 x 32 (4 per CU) 123.  The 256 x 256 block has no second
 //     workgroup to hide its epilogue, so it needs K >= 512 (at 16384^2 x 128
@@ -194,7 +194,7 @@ int select_variant(int path, int M, int N, int K) {
         int per_cu;          // workgroups resident per CU
         int min_k;           // shortest K at which that rate holds
     };
-    static const Candidate cand[] = {{kMfmaHuge, 143.5, 1, 512},
+    static const Candidate cand[] = {{kMfmaHuge, 145.5, 1, 512},
                                      {kMfmaLarge, 140.0, 2, 0},
                                      {kMfmaLarge4, 137.0, 4, 0},
                                      {kMfmaMid, 135.0, 2, 0},

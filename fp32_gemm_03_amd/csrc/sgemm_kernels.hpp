@@ -668,12 +668,12 @@ __device__ __forceinline__ void tile_of(int pid, int nbm, int nbn, int &tm, int 
 // for the previous one's result.  The caller adds acc_odd into acc once, after
 // the K loop.
 struct NoHook {
-    __device__ __forceinline__ void operator()(int) const {}
+    __device__ __forceinline__ void operator()(int, int) const {}
 };
 
-// hook(j) runs after the first MFMA of k-step j, fenced so that it stays
-// there: other work (the next K tile's global loads and LDS stores) issued
-// while the matrix pipe is busy instead of before or after the MFMAs.
+// hook(j, u) runs after MFMA u of k-step j (u = i * NI + jj), fenced so that
+// it stays there: other work (the next K tile's global loads and LDS stores)
+// issued while the matrix pipe is busy instead of before or after the MFMAs.
 template <int BK, int MI, int NI, int SA, int SB, int FD, bool SWZ, int CH = 1, class Hook = NoHook>
 __device__ __forceinline__ void mfma_tile(const float *as, int a_col, int lh, const float *bp,
                                           floatx16 (&acc)[MI][NI], floatx16 (&acc_odd)[MI][NI],
@@ -714,9 +714,9 @@ __device__ __forceinline__ void mfma_tile(const float *as, int a_col, int lh, co
                 else
                     acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                         vget(av[j % RING], i), vget(bv[j % RING], jj), acc[i][jj], 0, 0, 0);
-                if (HOOKED && i == 0 && jj == 0) {
+                if (HOOKED) {
                     __builtin_amdgcn_sched_barrier(0);
-                    hook(j);
+                    hook(j, i * NI + jj);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -899,7 +899,9 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         constexpr int STEPS = BK / 2;
         constexpr int PA = S::TA::PER, PB = S::TB::PER, NP = PA + PB;
         // the first quarter of the k-steps carries the loads, the second half
-        // the stores (measured best of quarter/half/eighth splits)
+        // the stores, one piece after every few MFMAs (spreading the pieces
+        // over a step's MFMAs, rather than issuing them in one burst, was
+        // worth 1.6%; with them spread, other splits measure the same)
         constexpr int LSTEPS = STEPS / 4 > 0 ? STEPS / 4 : 1;
         constexpr int SSTEPS = STEPS / 2 > 0 ? STEPS / 2 : 1;
         constexpr int LPER = (NP + LSTEPS - 1) / LSTEPS, SPER = (NP + SSTEPS - 1) / SSTEPS;
@@ -914,22 +916,19 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
             const float *st = smem + (t & 1) * STAGE;
             float *nx = smem + ((t + 1) & 1) * STAGE;
             const int kn = (t + 1) * BK;
-            auto hook = [&](int j) {
-                if (j < LSTEPS) {
-#pragma unroll
-                    for (int q = 0; q < LPER; ++q) {
-                        const int piece = j * LPER + q;
-                        if (piece < PA) ta.template load_piece<0>(a, bm, kn, piece);
-                        else if (piece < NP) tb.template load_piece<0>(a, bn, kn, piece - PA);
-                    }
+            // piece q of a step goes after MFMA q * (MI * NI / pieces per step)
+            constexpr int NU = MI * NI;
+            constexpr int LGAP = NU / LPER > 0 ? NU / LPER : 1, SGAP = NU / SPER > 0 ? NU / SPER : 1;
+            auto hook = [&](int j, int u) {
+                if (j < LSTEPS && u % LGAP == 0 && u / LGAP < LPER) {
+                    const int piece = j * LPER + u / LGAP;
+                    if (piece < PA) ta.template load_piece<0>(a, bm, kn, piece);
+                    else if (piece < NP) tb.template load_piece<0>(a, bn, kn, piece - PA);
                 }
-                if (j >= STEPS - SSTEPS) {
-#pragma unroll
-                    for (int q = 0; q < SPER; ++q) {
-                        const int piece = (j - (STEPS - SSTEPS)) * SPER + q;
-                        if (piece < PA) ta.template store_piece<0>(nx, tid, piece);
-                        else if (piece < NP) tb.template store_piece<0>(nx + BK * SA, tid, piece - PA);
-                    }
+                if (j >= STEPS - SSTEPS && u % SGAP == 0 && u / SGAP < SPER) {
+                    const int piece = (j - (STEPS - SSTEPS)) * SPER + u / SGAP;
+                    if (piece < PA) ta.template store_piece<0>(nx, tid, piece);
+                    else if (piece < NP) tb.template store_piece<0>(nx + BK * SA, tid, piece - PA);
                 }
             };
             mfma_tile<BK, MI, NI, SA, SB, FD, SWZ, CH>(st, a_col, lh, st + b_off, acc, acc_odd, hook);
