@@ -89,6 +89,17 @@ struct Variant {
      MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD, ORD, true),           \
      MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD, ORD, true)}
 
+// A variant on the interleaved schedule (A padded by 4 or XOR-swizzled),
+// also compiled with split-K.
+#define MFMA_CFG_IL(BM, BN, BK, WM, WN, PA, WPE, SWZ, SUFFIX)                           \
+    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
+     (BM / WM) * (BN / WN) * 64,                                                         \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 4, WPE, true, 1, 1, 0, false, 0, SWZ, true>,  \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 1, 0, false, 0, SWZ, true>,  \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, 1, 0, false, 0, SWZ, true>, \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 4, WPE, true, 1, 1, 0, true, 0, SWZ, true>,   \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 1, 0, true, 0, SWZ, true>}
+
 const Variant kVariants[] = {
     VALU_CFG(128, 128, 16, 8, 8, 4, 0, 4),                     // 0
     MFMA_CFG(256, 256, 32, 128, 128, 4, 0, 1, 1, 1, 0, ""),       // 1: 4 waves, 1 per SIMD, 512 registers
@@ -120,17 +131,27 @@ const Variant kVariants[] = {
      sgk::sgemm_mfma<256, 256, 32, 128, 128, 4, 0, 4, 1, true, 1, 1, 0, false, 0, false, true>,
      sgk::sgemm_mfma<256, 256, 32, 128, 128, 4, 0, 1, 1, true, 1, 1, 0, false, 0, false, true>,
      sgk::sgemm_mfma<256, 256, 32, 128, 128, 4, 0, 1, 1, false, 1, 1, 0, false, 0, false, true>, nullptr, nullptr},
+    MFMA_CFG_IL(256, 256, 32, 128, 64, 4, 2, false, "_il"),      // 22: 8 waves, 2 per SIMD
+    MFMA_CFG_IL(128, 128, 16, 64, 64, 4, 4, false, "_wpe4_il"),  // 23: 4 workgroups per CU
+    MFMA_CFG_IL(128, 128, 32, 64, 64, 4, 2, false, "_il"),       // 24: 2 workgroups per CU
+    MFMA_CFG_IL(128, 256, 16, 64, 128, 0, 2, true, "_il_xorA"),  // 25: 2 workgroups per CU
+    MFMA_CFG_IL(128, 256, 32, 64, 128, 4, 1, false, "_il"),      // 26: 1 workgroup per CU
+    MFMA_CFG_IL(64, 64, 32, 32, 32, 4, 4, false, "_il"),         // 27: 4 workgroups per CU
+    MFMA_CFG_IL(128, 128, 64, 64, 64, 4, 1, false, "_il"),       // 28: 1 workgroup per CU
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 constexpr int kValuDefault = 0;  // 128 x 128 x 16, 8 x 8 per lane, four workgroups per CU
 constexpr int kValuWide = 7;     // 128 x 256 x 16, 8 x 16 per lane, two workgroups per CU
-constexpr int kMfmaHuge = 21;    // 256 x 256 x 32, interleaved schedule, one workgroup per CU
-constexpr int kMfmaLarge = 16;   // 128 x 256 x 16, A XOR-swizzled, two workgroups per CU
-constexpr int kMfmaLarge4 = 19;  // 128 x 128 x 16, A XOR-swizzled, four workgroups per CU
-constexpr int kMfmaMid = 2;      // 128 x 128 x 32, two workgroups per CU
-constexpr int kMfmaMedium = 9;   // 64 x 64 x 32, two K tiles in flight, four workgroups per CU
 constexpr int kMfmaSmall = 10;   // 64 x 64 x 64, fragments three k-steps ahead
+// the interleaved-schedule blocks
+constexpr int kIlHuge = 22;      // 256 x 256 x 32, 8 waves, one workgroup per CU
+constexpr int kIlLarge4 = 23;    // 128 x 128 x 16, four workgroups per CU
+constexpr int kIlMid = 24;       // 128 x 128 x 32, two workgroups per CU
+constexpr int kIlShortK = 25;    // 128 x 256 x 16, A XOR-swizzled, two workgroups per CU
+constexpr int kIlWide = 26;      // 128 x 256 x 32, one workgroup per CU
+constexpr int kIlSmall = 27;     // 64 x 64 x 32, four workgroups per CU
+constexpr int kIlDeep = 28;      // 128 x 128 x 64, one workgroup per CU
 
 // Compute units of an MI355X; the choice of tile is a pure function of the
 // sizes so that it is the same on every call and testable without a GPU.
@@ -149,27 +170,30 @@ double quantization(long long t) {
 }
 
 // Measured on MI355X over every variant with `python -m fp32_gemm_03_amd.tune`
-// (cubes 256..10240, 16384^2 x 128, 1024 x 8192 x 8192, 16384 x 1024 x 1024
-// both ways, 1000 x 1023 x 999, and split-K shapes):
+// (cubes 256..10240, 16384^2 x K for K = 128..1024, 1024 x 8192 x 8192,
+// 16384 x 1024 x 1024 both ways, 1000 x 1023 x 999, and split-K shapes):
+//   * the blocks on the interleaved schedule beat the same blocks on the
+//     plain two-stage loop by 3-8%, so every block chosen for a shape that
+//     fills the chip is one of them;
 //   * a block shape reaches its full-chip rate only once there is a tile for
 //     every workgroup slot on the chip (slots = workgroups per CU x 256);
 //     below that its workgroups run alone on their CUs and latency shows.
 //     Among the shapes that qualify, what decides is the full-chip rate times
 //     the share of CUs the last round of tiles keeps busy.  Rates, TFLOP/s:
-//     256 x 256 x 32 interleaved (1 per CU) 145.5, 128 x 256 x 16 (2 per CU)
-//     140, 128 x 128 x 16 (4 per CU) 137, 128 x 128 x 32 (2 per CU) 135,
-//     64 x 64 x 32 (4 per CU) 123.  The 256 x 256 block has no second
-//     workgroup to hide its epilogue, so it needs K >= 512 (at 16384^2 x 128
-//     it runs 86 TFLOP/s against 99).  So 8192^3, 4096^3 and 16384 x 1024 x
-//     1024 (whole rounds of 256 x 256 blocks) take 256 x 256; 6144^3 and
-//     10240^3 (0.75 and 0.89 of a last round) take 128 x 128 x 16;
-//     1024 x 8192 x 8192 (one 128 x 256 block per CU) takes 128 x 128 x 32;
-//     3072^3 and 2048^3 take 64 x 64 x 32; the low-K square takes 128 x 256.
-//     The 128-row blocks keep A XOR-swizzled in LDS rather than padded: 1-2%
-//     faster at 4096^3 to 16384^3 (on 64 x 64 and 256-row blocks the address
-//     XOR costs more than it saves, so those stay padded);
-//   * no block qualifies but there is a 128 x 128 block per CU: 64 x 64
-//     blocks with two K tiles in flight;
+//     256 x 256 x 32 (1 per CU) 145.5, 128 x 256 x 32 (1 per CU) 141.5,
+//     128 x 128 x 16 (4 per CU) 141, 128 x 128 x 32 (2 per CU) 140.5,
+//     128 x 256 x 16 (2 per CU) 138, 128 x 128 x 64 (1 per CU) 137,
+//     64 x 64 x 32 (4 per CU) 124.  With K short the epilogue is a larger
+//     share of a tile's time and blocks with more workgroups per CU, which
+//     hide one workgroup's epilogue under another's K loop, win: the
+//     one-per-CU blocks need K >= 512 and the 128 x 128 ones K >= 256 (at
+//     16384^2 x 128 the 128 x 256 x 16 block runs 108 TFLOP/s against 104
+//     and 89).  So 8192^3, 4096^3 and 16384 x 1024 x 1024 (whole rounds of
+//     256 x 256 blocks) take 256 x 256; 6144^3, 7168^3 and 10240^3 take
+//     128 x 128 x 16; 1024 x 8192 x 8192 (one 128 x 256 block per CU) takes
+//     128 x 256 x 32; 2048^3 (one 128 x 128 block per CU) 128 x 128 x 64;
+//     3072^3 and 5120^3 take 64 x 64 x 32 or 128 x 128 x 16; the low-K
+//     square takes 128 x 256 x 16;
 //   * below that the problem cannot fill the chip and each workgroup's
 //     latency decides: 64 x 64 blocks over BK = 64 with LDS fragments read
 //     three k-steps ahead.
@@ -194,11 +218,10 @@ int select_variant(int path, int M, int N, int K) {
         int per_cu;          // workgroups resident per CU
         int min_k;           // shortest K at which that rate holds
     };
-    static const Candidate cand[] = {{kMfmaHuge, 145.5, 1, 512},
-                                     {kMfmaLarge, 140.0, 2, 0},
-                                     {kMfmaLarge4, 137.0, 4, 0},
-                                     {kMfmaMid, 135.0, 2, 0},
-                                     {kMfmaMedium, 123.0, 4, 0}};
+    static const Candidate cand[] = {{kIlHuge, 145.5, 1, 512},  {kIlWide, 141.5, 1, 512},
+                                     {kIlLarge4, 141.0, 4, 256}, {kIlMid, 140.5, 2, 256},
+                                     {kIlShortK, 138.0, 2, 0},   {kIlDeep, 137.0, 1, 512},
+                                     {kIlSmall, 124.0, 4, 0}};
     int best = -1;
     double best_score = -1.0;
     for (const Candidate &c : cand) {
@@ -211,9 +234,7 @@ int select_variant(int path, int M, int N, int K) {
             best = c.variant;
         }
     }
-    if (best >= 0) return best;
-    if (tiles(M, N, 128, 128) >= kComputeUnits) return kMfmaMedium;
-    return kMfmaSmall;
+    return best >= 0 ? best : kMfmaSmall;
 }
 
 // Split count for a variant when a workspace is available (measured on
@@ -222,8 +243,10 @@ int select_variant(int path, int M, int N, int K) {
 // split only when the tiles alone leave CUs idle, into enough parts for
 // about two workgroups per CU, keeping at least 16 K tiles per part so the
 // per-workgroup prologue and the extra pass over the partials stay small.
+// Only the latency block splits: the blocks chosen by rate have a tile for
+// every one of their workgroup slots on the chip already.
 int select_splits(int variant, int M, int N, int K) {
-    if (M <= 0 || N <= 0 || K <= 0) return 1;
+    if (M <= 0 || N <= 0 || K <= 0 || variant != kMfmaSmall) return 1;
     const Variant &v = kVariants[variant];
     if (v.split4 == nullptr) return 1;
     const long long t = tiles(M, N, v.bm, v.bn);

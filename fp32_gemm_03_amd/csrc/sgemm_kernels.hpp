@@ -890,12 +890,13 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     const int kb = kt0 * BK;
 
     if constexpr (IL) {
-        // Interleaved schedule (PD == 1, no split): the loads of K tile t+1
-        // are issued in pieces after the first MFMA of the first k-steps of
-        // tile t, and stored to the other LDS stage in pieces over the last
-        // k-steps, so the matrix pipe is fed throughout.  The loads are not
-        // conditional: past K they read 0.0 into a stage nobody reads.
-        static_assert(PD == 1 && !SPLIT, "interleaved schedule: one register stage, no split");
+        // Interleaved schedule (PD == 1): the loads of K tile t+1 are issued
+        // in pieces after the MFMAs of the first k-steps of tile t, and
+        // stored to the other LDS stage in pieces over the last k-steps, so
+        // the matrix pipe is fed throughout.  The loads are not conditional:
+        // after a split's last tile they read the next split's first tile,
+        // or past K 0.0, into a stage nobody reads.
+        static_assert(PD == 1, "interleaved schedule: one register stage");
         constexpr int STEPS = BK / 2;
         constexpr int PA = S::TA::PER, PB = S::TB::PER, NP = PA + PB;
         // the first quarter of the k-steps carries the loads, the second half
@@ -906,8 +907,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         constexpr int SSTEPS = STEPS / 2 > 0 ? STEPS / 2 : 1;
         constexpr int LPER = (NP + LSTEPS - 1) / LSTEPS, SPER = (NP + SSTEPS - 1) / SSTEPS;
         if (KT > 0) {
-            ta.template load<0>(a, bm, 0);
-            tb.template load<0>(a, bn, 0);
+            ta.template load<0>(a, bm, kb);
+            tb.template load<0>(a, bn, kb);
             ta.template store<0>(smem, tid);
             tb.template store<0>(smem + BK * SA, tid);
         }
@@ -915,20 +916,29 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         for (int t = 0; t < KT; ++t) {
             const float *st = smem + (t & 1) * STAGE;
             float *nx = smem + ((t + 1) & 1) * STAGE;
-            const int kn = (t + 1) * BK;
-            // piece q of a step goes after MFMA q * (MI * NI / pieces per step)
+            const int kn = kb + (t + 1) * BK;
+            // piece q of a step goes after MFMA (q * MI * NI) / pieces per step:
+            // spread evenly, several after one MFMA when there are more
+            // pieces than MFMAs
             constexpr int NU = MI * NI;
-            constexpr int LGAP = NU / LPER > 0 ? NU / LPER : 1, SGAP = NU / SPER > 0 ? NU / SPER : 1;
             auto hook = [&](int j, int u) {
-                if (j < LSTEPS && u % LGAP == 0 && u / LGAP < LPER) {
-                    const int piece = j * LPER + u / LGAP;
-                    if (piece < PA) ta.template load_piece<0>(a, bm, kn, piece);
-                    else if (piece < NP) tb.template load_piece<0>(a, bn, kn, piece - PA);
+                if (j < LSTEPS) {
+#pragma unroll
+                    for (int q = 0; q < LPER; ++q) {
+                        const int piece = j * LPER + q;
+                        if ((q * NU) / LPER != u || piece >= NP) continue;
+                        if (piece < PA) ta.template load_piece<0>(a, bm, kn, piece);
+                        else tb.template load_piece<0>(a, bn, kn, piece - PA);
+                    }
                 }
-                if (j >= STEPS - SSTEPS && u % SGAP == 0 && u / SGAP < SPER) {
-                    const int piece = (j - (STEPS - SSTEPS)) * SPER + u / SGAP;
-                    if (piece < PA) ta.template store_piece<0>(nx, tid, piece);
-                    else if (piece < NP) tb.template store_piece<0>(nx + BK * SA, tid, piece - PA);
+                if (j >= STEPS - SSTEPS) {
+#pragma unroll
+                    for (int q = 0; q < SPER; ++q) {
+                        const int piece = (j - (STEPS - SSTEPS)) * SPER + q;
+                        if ((q * NU) / SPER != u || piece >= NP) continue;
+                        if (piece < PA) ta.template store_piece<0>(nx, tid, piece);
+                        else tb.template store_piece<0>(nx + BK * SA, tid, piece - PA);
+                    }
                 }
             };
             mfma_tile<BK, MI, NI, SA, SB, FD, SWZ, CH>(st, a_col, lh, st + b_off, acc, acc_odd, hook);

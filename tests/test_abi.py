@@ -139,20 +139,35 @@ def test_select_variant_is_a_function_of_the_sizes():
 
 
 def test_large_shapes_pick_the_block_whose_last_round_is_fullest():
-    """Above two 128 x 256 blocks per CU the choice weighs each block's
-    full-chip rate by how full its last round over 256 CUs is."""
+    """Once a block shape has a tile for every workgroup slot on the chip, the
+    choice weighs each block's full-chip rate by how full its last round over
+    256 CUs is; short K leaves out the blocks that run one workgroup per CU."""
     def block(M, N, K):
-        _, bm, bn = g.sgemm_variant_tile(g.sgemm_select_variant(g.SGEMM_PATH_AUTO, M, N, K))
-        return bm, bn
-    assert block(8192, 8192, 8192) == (256, 256)    # 1024 blocks of 256 x 256: 4 per CU
-    assert block(4096, 4096, 4096) == (256, 256)    # 256: 1 per CU
-    assert block(16384, 1024, 1024) == (256, 256)   # 256
-    assert block(16384, 16384, 128) == (128, 256)   # short K: the 256 x 256 block is left out
-    assert block(6144, 6144, 6144) == (128, 128)    # 1152 would leave half a round
-    assert block(10240, 10240, 10240) == (128, 128)
-    assert block(3072, 3072, 3072) == (64, 64)      # 128 x 128 would leave 3/4 of a round
-    assert block(1024, 8192, 8192) == (128, 128)    # one 128 x 256 block per CU is too few
-    assert block(1024, 1024, 1024) == (64, 64)
+        v = g.sgemm_select_variant(g.SGEMM_PATH_AUTO, M, N, K)
+        _, bm, bn = g.sgemm_variant_tile(v)
+        bk = int(g.sgemm_variant_name(v).split("_")[1].split("x")[2])
+        return bm, bn, bk
+    assert block(8192, 8192, 8192) == (256, 256, 32)    # 1024 blocks of 256 x 256: 4 per CU
+    assert block(4096, 4096, 4096) == (256, 256, 32)    # 256: 1 per CU
+    assert block(16384, 1024, 1024) == (256, 256, 32)   # 256
+    assert block(16384, 16384, 128) == (128, 256, 16)   # short K: one-per-CU blocks left out
+    assert block(6144, 6144, 6144) == (128, 128, 16)    # 576 of 256 x 256 would leave 1/4 idle
+    assert block(7168, 7168, 7168) == (128, 128, 16)
+    assert block(10240, 10240, 10240) == (128, 128, 16)
+    assert block(1024, 8192, 8192) == (128, 256, 32)    # 256 blocks: one per CU
+    assert block(2048, 2048, 2048) == (128, 128, 64)    # 256 blocks: one per CU
+    assert block(3072, 3072, 3072) == (64, 64, 32)      # 128 x 128 would leave 1/4 of a round
+    assert block(1024, 1024, 1024) == (64, 64, 64)      # too few tiles: latency decides
+    assert block(1000, 1023, 999) == (64, 64, 64)
+
+
+def test_only_the_latency_block_splits_k():
+    """A block chosen by rate already has a tile per workgroup slot on the
+    chip; only the 64 x 64 x 64 fallback splits K when a workspace is given."""
+    assert g.sgemm_select_splits(1024, 8192, 8192) == 1
+    assert g.sgemm_select_splits(2048, 2048, 2048) == 1
+    assert g.sgemm_select_splits(16384, 1024, 1024) == 1
+    assert g.sgemm_workspace_size(1024, 8192, 8192) == 0
 
 
 def test_status_strings():

@@ -72,20 +72,25 @@ def geometry(variant):
     return name, bm, bn, bk
 
 
-def mfma_lds_per_wave_tile(name, bm, bn, bk, threads):
-    # reads: one A and one B fragment vector per k-step (BK / 2 steps);
-    # writes: A as float4 per 4 rows, B as float4 along N
+def mfma_lds_per_wave(name, bm, bn, bk, threads, kt):
+    """LDS instructions of one wave over a tile's K loop of kt K tiles.
+    Reads: one A and one B fragment vector per k-step (BK / 2 steps per K
+    tile); writes: A as float4 per 4 rows, B as float4 along N, once per K
+    tile, plus, on the interleaved schedule, the tile past the end that the
+    last iteration stores unconditionally."""
     reads = 2 * (bk // 2)
     writes = bm * bk // (4 * threads) + bk * bn // (4 * threads)
-    return reads + writes
+    stored = kt + 1 if "_il" in name else kt
+    return kt * reads + stored * writes, kt * (bk // 2)
 
 
-MFMA_CASES = [16, 19, 2, 9, 10]
-# Kernels whose every LDS access is its own instruction.  In the others the
-# compiler fuses some pairs of fragment reads into one ds_read2 / ds_read2st64
-# instruction, so the counter lies between the fully fused and the unfused
-# design count.
-EXACT_LDS = {16, 0, 7}
+# the blocks the selection picks
+MFMA_CASES = [22, 23, 24, 25, 26, 27, 28, 10]
+# MFMA kernels whose every LDS access is its own instruction (none of the
+# chosen ones).  In the others the compiler fuses some pairs of fragment reads
+# into one ds_read2 / ds_read2st64 instruction, so the counter lies between
+# the fully fused and the unfused design count.
+EXACT_LDS = set()
 
 
 @pytest.mark.parametrize("variant", MFMA_CASES)
@@ -103,18 +108,18 @@ def test_mfma_counters_equal_design(variant):
     assert c["SQ_INSTS_MFMA"] == S * S * S // (32 * 32 * 2)
     assert c["SQ_INSTS_VALU_MFMA_MOPS_F32"] * 512 == 2 * S ** 3
     assert c["SQ_LDS_BANK_CONFLICT"] == 0
-    per = mfma_lds_per_wave_tile(name, bm, bn, bk, threads)
-    design = tiles * waves_per_wg * kt * per
+    per, pairs = mfma_lds_per_wave(name, bm, bn, bk, threads, kt)
+    design = tiles * waves_per_wg * per
     if variant in EXACT_LDS:
         assert c["SQ_INSTS_LDS"] == design, (kernel, per)
     else:
-        fused = tiles * waves_per_wg * kt * (per - bk // 2)  # every read pair fused
+        fused = tiles * waves_per_wg * (per - pairs)  # every read pair fused
         assert fused <= c["SQ_INSTS_LDS"] <= design, (kernel, c["SQ_INSTS_LDS"], fused, design)
 
 
 def test_mfma_runs_no_reduced_precision_matrix_ops():
     c, kernel = run_pmc(["SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
-                         "SQ_INSTS_VALU_MFMA_MOPS_F16"], 16)
+                         "SQ_INSTS_VALU_MFMA_MOPS_F16"], 22)
     if c is None:
         pytest.skip("bf16/f16 MFMA op counters not offered by this rocprofv3")
     assert c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] == 0
