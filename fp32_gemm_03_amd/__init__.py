@@ -26,7 +26,7 @@ __all__ = [
     "sgemm_splitk_workspace_size",
     "SgemmError", "LibraryNotBuilt", "library_path", "load_library",
     "sgemm", "sgemm_path", "sgemm_variant", "sgemm_variant_count",
-    "sgemm_variant_name", "sgemm_variant_path", "sgemm_variant_tile",
+    "sgemm_variant_name", "sgemm_variant_path", "sgemm_variant_tile", "sgemm_variant_reads_a128",
     "sgemm_select_variant", "sgemm_status_string", "variants", "sgemm_device_fp32_peak",
 ]
 
@@ -100,6 +100,8 @@ def load_library():
         lib.sgemm_variant_path.restype = i
         lib.sgemm_variant_tile.argtypes = [i, ctypes.POINTER(i), ctypes.POINTER(i)]
         lib.sgemm_variant_tile.restype = i
+        lib.sgemm_variant_reads_a128.argtypes = [i]
+        lib.sgemm_variant_reads_a128.restype = i
         lib.sgemm_select_variant.argtypes = [i, i, i, i]
         lib.sgemm_select_variant.restype = i
         lib.sgemm_status_string.argtypes = [i]
@@ -232,6 +234,11 @@ def sgemm_variant_tile(variant):
     bm, bn = ctypes.c_int(0), ctypes.c_int(0)
     rc = load_library().sgemm_variant_tile(int(variant), ctypes.byref(bm), ctypes.byref(bn))
     return int(rc), bm.value, bn.value
+
+
+def sgemm_variant_reads_a128(variant) -> int:
+    """1 if the variant's 128-bit build also reads A 128 bits at a time along K, else 0."""
+    return int(load_library().sgemm_variant_reads_a128(int(variant)))
 
 
 def sgemm_select_variant(path, M, N, K) -> int:

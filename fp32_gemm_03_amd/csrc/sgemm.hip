@@ -30,6 +30,7 @@ struct Variant {
     KernelFn split4;    // split-K, as vec4 (nullptr: no split-K build of this variant)
     KernelFn split1;    // split-K, as vec1
     int persistent;     // 0: one workgroup per tile; n: a persistent grid of n workgroups per CU
+    int a128;           // 1: the vec4 build also reads A 128 bits at a time along K
 };
 
 // VALU: 128 x 128 x 16 block, 4 waves of 64 x 64, 8 x 8 per lane.
@@ -100,6 +101,18 @@ struct Variant {
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 4, WPE, true, 1, 1, 0, true, 0, SWZ, true>,   \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 1, 0, true, 0, SWZ, true>}
 
+// A variant with A kept in K order (sgemm_mfma_kc): its buffer builds load
+// straight into LDS, its checked build stages through registers; also
+// compiled with split-K.
+#define MFMA_CFG_KCD(BM, BN, BK, WM, WN, WPE, SUFFIX)                                   \
+    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
+     (BM / WM) * (BN / WN) * 64,                                                         \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 0, 4, WPE, true, false, true>,               \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 0, 1, WPE, true, false, true>,               \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 0, 1, WPE, false, false, false>,             \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 0, 4, WPE, true, true, true>,                \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 0, 1, WPE, true, true, true>, 0, 1}
+
 const Variant kVariants[] = {
     VALU_CFG(128, 128, 16, 8, 8, 4, 0, 4),                     // 0
     MFMA_CFG(256, 256, 32, 128, 128, 4, 0, 1, 1, 1, 0, ""),       // 1: 4 waves, 1 per SIMD, 512 registers
@@ -138,20 +151,25 @@ const Variant kVariants[] = {
     MFMA_CFG_IL(128, 256, 32, 64, 128, 4, 1, false, "_il"),      // 26: 1 workgroup per CU
     MFMA_CFG_IL(64, 64, 32, 32, 32, 4, 4, false, "_il"),         // 27: 4 workgroups per CU
     MFMA_CFG_IL(128, 128, 64, 64, 64, 4, 1, false, "_il"),       // 28: 1 workgroup per CU
+    MFMA_CFG_KCD(256, 256, 32, 128, 64, 2, "_kcd"),              // 29: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(128, 128, 16, 64, 64, 4, "_wpe4_kcd"),          // 30: 4 workgroups per CU
+    MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, "_kcd"),              // 31: 2 workgroups per CU
+    MFMA_CFG_KCD(128, 256, 32, 64, 128, 1, "_kcd"),              // 32: 1 workgroup per CU
+    MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, "_kcd"),                 // 33: 4 workgroups per CU
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 constexpr int kValuDefault = 0;  // 128 x 128 x 16, 8 x 8 per lane, four workgroups per CU
 constexpr int kValuWide = 7;     // 128 x 256 x 16, 8 x 16 per lane, two workgroups per CU
-constexpr int kMfmaSmall = 10;   // 64 x 64 x 64, fragments three k-steps ahead
-// the interleaved-schedule blocks
-constexpr int kIlHuge = 22;      // 256 x 256 x 32, 8 waves, one workgroup per CU
-constexpr int kIlLarge4 = 23;    // 128 x 128 x 16, four workgroups per CU
+// the blocks on the interleaved schedule, A as is ...
 constexpr int kIlMid = 24;       // 128 x 128 x 32, two workgroups per CU
-constexpr int kIlShortK = 25;    // 128 x 256 x 16, A XOR-swizzled, two workgroups per CU
-constexpr int kIlWide = 26;      // 128 x 256 x 32, one workgroup per CU
-constexpr int kIlSmall = 27;     // 64 x 64 x 32, four workgroups per CU
 constexpr int kIlDeep = 28;      // 128 x 128 x 64, one workgroup per CU
+// ... and with A in K order, loaded straight into LDS
+constexpr int kKcHuge = 29;      // 256 x 256 x 32, 8 waves, one workgroup per CU
+constexpr int kKcLarge4 = 30;    // 128 x 128 x 16, four workgroups per CU
+constexpr int kKcShortK = 31;    // 128 x 256 x 16, two workgroups per CU
+constexpr int kKcWide = 32;      // 128 x 256 x 32, one workgroup per CU
+constexpr int kKcSmall4 = 33;    // 64 x 64 x 32, four workgroups per CU
 
 // Compute units of an MI355X; the choice of tile is a pure function of the
 // sizes so that it is the same on every call and testable without a GPU.
@@ -172,31 +190,31 @@ double quantization(long long t) {
 // Measured on MI355X over every variant with `python -m fp32_gemm_03_amd.tune`
 // (cubes 256..10240, 16384^2 x K for K = 128..1024, 1024 x 8192 x 8192,
 // 16384 x 1024 x 1024 both ways, 1000 x 1023 x 999, and split-K shapes):
-//   * the blocks on the interleaved schedule beat the same blocks on the
-//     plain two-stage loop by 3-8%, so every block chosen for a shape that
-//     fills the chip is one of them;
+//   * blocks with A in K order, loaded straight into LDS, match or beat the
+//     same blocks on the interleaved schedule with A transposed (by 2-3% at
+//     128 x 128 x 16, up to 10% on 64 x 64 blocks), except 128 x 128 x 32
+//     and 128 x 128 x 64, which keep the interleaved schedule;
 //   * a block shape reaches its full-chip rate only once there is a tile for
 //     every workgroup slot on the chip (slots = workgroups per CU x 256);
 //     below that its workgroups run alone on their CUs and latency shows.
 //     Among the shapes that qualify, what decides is the full-chip rate times
 //     the share of CUs the last round of tiles keeps busy.  Rates, TFLOP/s:
-//     256 x 256 x 32 (1 per CU) 145.5, 128 x 256 x 32 (1 per CU) 141.5,
-//     128 x 128 x 16 (4 per CU) 141, 128 x 128 x 32 (2 per CU) 140.5,
-//     128 x 256 x 16 (2 per CU) 138, 128 x 128 x 64 (1 per CU) 137,
-//     64 x 64 x 32 (4 per CU) 124.  With K short the epilogue is a larger
+//     256 x 256 x 32 (1 per CU) 146.5, 128 x 128 x 16 (4 per CU) 146,
+//     128 x 256 x 16 (2 per CU) 144, 128 x 256 x 32 (1 per CU) 142,
+//     128 x 128 x 32 (2 per CU) 140.5, 128 x 128 x 64 (1 per CU) 137,
+//     64 x 64 x 32 (4 per CU) 130.  With K short the epilogue is a larger
 //     share of a tile's time and blocks with more workgroups per CU, which
 //     hide one workgroup's epilogue under another's K loop, win: the
 //     one-per-CU blocks need K >= 512 and the 128 x 128 ones K >= 256 (at
-//     16384^2 x 128 the 128 x 256 x 16 block runs 108 TFLOP/s against 104
-//     and 89).  So 8192^3, 4096^3 and 16384 x 1024 x 1024 (whole rounds of
-//     256 x 256 blocks) take 256 x 256; 6144^3, 7168^3 and 10240^3 take
+//     16384^2 x 128 the 128 x 256 x 16 block runs 112 TFLOP/s against 105
+//     and 90).  So 8192^3, 4096^3 and 16384 x 1024 x 1024 (whole rounds of
+//     256 x 256 blocks) take 256 x 256; 5120^3 to 10240^3 take
 //     128 x 128 x 16; 1024 x 8192 x 8192 (one 128 x 256 block per CU) takes
 //     128 x 256 x 32; 2048^3 (one 128 x 128 block per CU) 128 x 128 x 64;
-//     3072^3 and 5120^3 take 64 x 64 x 32 or 128 x 128 x 16; the low-K
-//     square takes 128 x 256 x 16;
-//   * below that the problem cannot fill the chip and each workgroup's
-//     latency decides: 64 x 64 blocks over BK = 64 with LDS fragments read
-//     three k-steps ahead.
+//     3072^3 takes 64 x 64 x 32; the low-K square takes 128 x 256 x 16;
+//   * below that the problem cannot fill the chip: 64 x 64 x 32 blocks
+//     (10-15% faster there than 64 x 64 x 64 blocks with fragments three
+//     k-steps ahead), split along K when K is long (select_splits).
 int select_variant(int path, int M, int N, int K) {
     if (M < 0) return -1;
     if (N < 0) return -2;
@@ -218,10 +236,10 @@ int select_variant(int path, int M, int N, int K) {
         int per_cu;          // workgroups resident per CU
         int min_k;           // shortest K at which that rate holds
     };
-    static const Candidate cand[] = {{kIlHuge, 145.5, 1, 512},  {kIlWide, 141.5, 1, 512},
-                                     {kIlLarge4, 141.0, 4, 256}, {kIlMid, 140.5, 2, 256},
-                                     {kIlShortK, 138.0, 2, 0},   {kIlDeep, 137.0, 1, 512},
-                                     {kIlSmall, 124.0, 4, 0}};
+    static const Candidate cand[] = {{kKcHuge, 146.5, 1, 512},  {kKcLarge4, 146.0, 4, 256},
+                                     {kKcShortK, 144.0, 2, 0},  {kKcWide, 142.0, 1, 512},
+                                     {kIlMid, 140.5, 2, 256},   {kIlDeep, 137.0, 1, 512},
+                                     {kKcSmall4, 130.0, 4, 0}};
     int best = -1;
     double best_score = -1.0;
     for (const Candidate &c : cand) {
@@ -234,26 +252,25 @@ int select_variant(int path, int M, int N, int K) {
             best = c.variant;
         }
     }
-    return best >= 0 ? best : kMfmaSmall;
+    return best >= 0 ? best : kKcSmall4;
 }
 
 // Split count for a variant when a workspace is available (measured on
-// MI355X with the 64 x 64 x 64 block: 512 x 512 x 8192 runs 3.7x faster in 8
-// parts, 1024 x 1024 x 4096 10% faster in 2, while 1024^3 and smaller lose):
-// split only when the tiles alone leave CUs idle, into enough parts for
-// about two workgroups per CU, keeping at least 16 K tiles per part so the
-// per-workgroup prologue and the extra pass over the partials stay small.
-// Only the latency block splits: the blocks chosen by rate have a tile for
-// every one of their workgroup slots on the chip already.
+// MI355X: 512 x 512 x 8192 runs 3.5x faster in 8 parts, 1024 x 1024 x 4096
+// about 10% faster in 2, while 1024^3 and smaller lose): split only when the
+// tiles alone leave CUs idle, into enough parts for about two workgroups per
+// CU, keeping at least 1024 of K per part so the per-workgroup prologue and
+// the extra pass over the partials stay small.  Only the latency block
+// splits: the blocks chosen by rate have a tile for every one of their
+// workgroup slots on the chip already.
 int select_splits(int variant, int M, int N, int K) {
-    if (M <= 0 || N <= 0 || K <= 0 || variant != kMfmaSmall) return 1;
+    if (M <= 0 || N <= 0 || K <= 0 || variant != kKcSmall4) return 1;
     const Variant &v = kVariants[variant];
     if (v.split4 == nullptr) return 1;
     const long long t = tiles(M, N, v.bm, v.bn);
     if (t > kComputeUnits) return 1;
-    const long long kt = (K + v.bk - 1) / v.bk;
     long long s = 2 * kComputeUnits / t;
-    if (s > kt / 16) s = kt / 16;
+    if (s > K / 1024) s = K / 1024;
     if (s > kMaxSplits) s = kMaxSplits;
     return s < 2 ? 1 : (int)s;
 }
@@ -323,9 +340,12 @@ int launch(int variant, int access, int splits, void *workspace, size_t workspac
                         (long long)(v.bm + 1) * ldc * 4 < lim;
     // 128-bit accesses to B and C need 16-byte aligned bases and every row
     // start a multiple of 4 floats; N % 4 == 0 keeps each 4-wide piece wholly
-    // inside or wholly outside the matrix.  A is read 32 bits at a time.
+    // inside or wholly outside the matrix.  A is read 32 bits at a time, or,
+    // by the variants that read it along K, 128 bits at a time under the
+    // same rules with K and lda in place of N and ldb.
     const bool vec4 = (N % 4 == 0) && (ldb % 4 == 0) && (ldc % 4 == 0) &&
-                      aligned16(B) && aligned16(C);
+                      aligned16(B) && aligned16(C) &&
+                      (!v.a128 || ((K % 4 == 0) && (lda % 4 == 0) && aligned16(A)));
     KernelFn fn;
     switch (access) {
         case SGEMM_ACCESS_BUFFER_128:
@@ -460,6 +480,11 @@ int sgemm_variant_tile(int variant, int *bm, int *bn) {
     if (bm) *bm = kVariants[variant].bm;
     if (bn) *bn = kVariants[variant].bn;
     return SGEMM_OK;
+}
+
+int sgemm_variant_reads_a128(int variant) {
+    if (variant < 0 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
+    return kVariants[variant].a128;
 }
 
 int sgemm_select_variant(int path, int M, int N, int K) {

@@ -1052,6 +1052,452 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// A tile kept in K order: As[BM][BK], each row one row of A.  Its BK / 4
+// 16-byte chunks are permuted per row: chunk c of row m sits at chunk
+// c ^ g(m), g(m) = (m / RP) % CPR, where CPR = BK / 4 chunks fill a row and
+// RP = 16 / CPR rows fill the 256 bytes that span the 64 banks.  A store
+// instruction writes CPR chunks of each of 16 / CPR consecutive rows (one
+// 16-lane phase), and a fragment read takes one chunk of each of 16
+// consecutive rows; both then touch 16 different 16-byte bank groups.
+// ---------------------------------------------------------------------------
+template <int BM, int BK, int NT, int STAGES>
+struct AKGeom {
+    static_assert(BK == 16 || BK == 32 || BK == 64, "K-ordered A tile: BK in {16, 32, 64}");
+    static constexpr int CPR = BK / 4;
+    static constexpr int RP = 16 / CPR;
+    static_assert(NT % CPR == 0, "threads must cover whole rows");
+    static constexpr int ROWS_PER_PASS = NT / CPR;
+    static_assert(BM % ROWS_PER_PASS == 0, "A tile must divide evenly over the threads");
+    static_assert((ROWS_PER_PASS / RP) % CPR == 0, "a thread's chunk position must not change between passes");
+    static constexpr int PER = BM / ROWS_PER_PASS;
+
+    float4 reg[STAGES][PER];  // register stages: K tiles in flight
+
+    static __device__ __forceinline__ int chunk_pos(int m, int c) { return c ^ ((m / RP) % CPR); }
+
+    template <int S>
+    __device__ __forceinline__ void store(float *As, int tid) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) store_piece<S>(As, tid, p);
+    }
+
+    // one 128-bit LDS store: chunk tid % CPR of row tid / CPR + p ROWS_PER_PASS
+    template <int S>
+    __device__ __forceinline__ void store_piece(float *As, int tid, int p) const {
+        const int m = tid / CPR + p * ROWS_PER_PASS;
+        *reinterpret_cast<float4 *>(As + m * BK + 4 * chunk_pos(m, tid % CPR)) = reg[S][p];
+    }
+};
+
+// Buffer loads of the K-ordered A tile: one 128-bit load per chunk (VEC 4:
+// K, lda multiples of 4 and A 16-byte aligned, so a chunk is wholly inside or
+// wholly past K), else four 32-bit loads.  Columns >= K and rows >= M read 0.0.
+template <int BM, int BK, int NT, int STAGES, int VEC>
+struct AKBuf : AKGeom<BM, BK, NT, STAGES> {
+    typedef AKGeom<BM, BK, NT, STAGES> G;
+    rsrc_t rsrc;
+    uint32_t off, pass;
+    int c4;
+
+    __device__ __forceinline__ void init(const Args &a, int bm, int tid) {
+        c4 = 4 * (tid % G::CPR);
+        off = (uint32_t)(((int64_t)(tid / G::CPR) * a.lda + c4) * 4);
+        pass = (uint32_t)(G::ROWS_PER_PASS * a.lda * 4);
+        rsrc = make_rsrc(a.A + (int64_t)bm * a.lda, ((int64_t)(a.M - bm - 1) * a.lda + a.K) * 4);
+    }
+
+    template <int S>
+    __device__ __forceinline__ void load(const Args &a, int bm, int k0) {
+#pragma unroll
+        for (int p = 0; p < G::PER; ++p) load_piece<S>(a, bm, k0, p);
+    }
+
+    template <int S>
+    __device__ __forceinline__ void load_piece(const Args &a, int, int k0, int p) {
+        const uint32_t o = off + 4u * (uint32_t)k0 + p * pass;
+        if (VEC == 4) {
+            G::reg[S][p] = buf<4>::load(rsrc, k0 + c4 < a.K ? o : kOutOfRange);
+        } else {
+            G::reg[S][p].x = buf<1>::load(rsrc, k0 + c4 < a.K ? o : kOutOfRange);
+            G::reg[S][p].y = buf<1>::load(rsrc, k0 + c4 + 1 < a.K ? o + 4 : kOutOfRange);
+            G::reg[S][p].z = buf<1>::load(rsrc, k0 + c4 + 2 < a.K ? o + 8 : kOutOfRange);
+            G::reg[S][p].w = buf<1>::load(rsrc, k0 + c4 + 3 < a.K ? o + 12 : kOutOfRange);
+        }
+    }
+};
+
+template <int BM, int BK, int NT, int STAGES>
+struct AKPtr : AKGeom<BM, BK, NT, STAGES> {
+    typedef AKGeom<BM, BK, NT, STAGES> G;
+    int c4, r0;
+
+    __device__ __forceinline__ void init(const Args &, int, int tid) {
+        c4 = 4 * (tid % G::CPR);
+        r0 = tid / G::CPR;
+    }
+
+    template <int S>
+    __device__ __forceinline__ void load(const Args &a, int bm, int k0) {
+#pragma unroll
+        for (int p = 0; p < G::PER; ++p) load_piece<S>(a, bm, k0, p);
+    }
+
+    template <int S>
+    __device__ __forceinline__ void load_piece(const Args &a, int bm, int k0, int p) {
+        const int row = bm + r0 + p * G::ROWS_PER_PASS, k = k0 + c4;
+        const float *q = a.A + (int64_t)row * a.lda + k;
+        const bool rin = row < a.M;
+        G::reg[S][p].x = (rin && k < a.K) ? q[0] : 0.0f;
+        G::reg[S][p].y = (rin && k + 1 < a.K) ? q[1] : 0.0f;
+        G::reg[S][p].z = (rin && k + 2 < a.K) ? q[2] : 0.0f;
+        G::reg[S][p].w = (rin && k + 3 < a.K) ? q[3] : 0.0f;
+    }
+};
+
+// Buffer loads that write LDS directly: lane l's W floats land at
+// lds + W * l, so one instruction fills 64 W consecutive floats of LDS, and
+// a lane out of range writes zeros.  lds must be wave-uniform.
+template <int W>
+__device__ __forceinline__ void load_to_lds(rsrc_t r, float *lds, uint32_t voff) {
+    static_assert(W == 1 || W == 4, "4 or 16 bytes per lane");
+    typedef __attribute__((address_space(3))) void lds_t;
+    if constexpr (W == 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t *)lds, 16, voff, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_t *)lds, 4, voff, 0, 0, 0);
+}
+
+// The K-ordered A tile and the B tile ([BK][BN], unpadded) of one stage
+// filled by loads that write LDS directly.  Instruction p of wave w fills
+// floats (p * WAVES + w) * 64 W .. + 64 W of each tile, so each lane's
+// global address is the one whose data belongs at its LDS position (for A
+// through the chunk permutation of AKGeom).  Columns of A >= K and rows of
+// B >= K read 0.0 (so do rows of A >= M); columns of B >= N read whatever
+// lies there, which only reaches columns of C that are never stored.
+template <int BM, int BN, int BK, int NT, int W>
+struct DirectStage {
+    static constexpr int WAVES = NT / 64;
+    static constexpr int CPR = BK / 4, RP = 16 / CPR;
+    static constexpr int PER_INST = 64 * W;
+    static_assert((BM * BK) % (NT * W) == 0 && (BK * BN) % (NT * W) == 0, "tiles must split into whole instructions");
+    static constexpr int PA = BM * BK / (NT * W), PB = BK * BN / (NT * W);
+    rsrc_t ra;
+    uint32_t aoff[PA], boff[PB];
+    int acol[PA];
+    int wave;
+
+    __device__ __forceinline__ void init(const Args &a, int bm, int tid) {
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int lane = tid & 63;
+        ra = make_rsrc(a.A + (int64_t)bm * a.lda, ((int64_t)(a.M - bm - 1) * a.lda + a.K) * 4);
+#pragma unroll
+        for (int p = 0; p < PA; ++p) {
+            const int f = (p * WAVES + wave) * PER_INST + lane * W;
+            const int row = f / BK, pos = f % BK;
+            const int col = 4 * ((pos / 4) ^ ((row / RP) % CPR)) + pos % 4;
+            aoff[p] = (uint32_t)(((int64_t)row * a.lda + col) * 4);
+            acol[p] = col;
+        }
+#pragma unroll
+        for (int p = 0; p < PB; ++p) {
+            const int f = (p * WAVES + wave) * PER_INST + lane * W;
+            boff[p] = (uint32_t)(((int64_t)(f / BN) * a.ldb + f % BN) * 4);
+        }
+    }
+
+    // B rows k0.. from column bn, up to B's last element
+    __device__ __forceinline__ rsrc_t b_rows(const Args &a, int bn, int k0) const {
+        return make_rsrc(a.B + (int64_t)k0 * a.ldb + bn, ((int64_t)(a.K - k0 - 1) * a.ldb + (a.N - bn)) * 4);
+    }
+
+    __device__ __forceinline__ void load_a(const Args &a, float *As, int k0, int p) const {
+        load_to_lds<W>(ra, As + (p * WAVES + wave) * PER_INST,
+                       k0 + acol[p] < a.K ? aoff[p] + 4u * (uint32_t)k0 : kOutOfRange);
+    }
+
+    __device__ __forceinline__ void load_b(rsrc_t rb, float *Bs, int p) const {
+        load_to_lds<W>(rb, Bs + (p * WAVES + wave) * PER_INST, boff[p]);
+    }
+};
+
+// One K tile of MFMAs over a K-ordered A tile.  Inside the tile the k index
+// is permuted (the sum is the same in any order): k-step j of lane half lh
+// takes k = lh * BK / 2 + j, so lane (li, lh) reads A row (wm + 32 i + li)
+// as BK / 8 chunks of 4 consecutive k, one 128-bit read per chunk and block
+// row i, and B row lh * BK / 2 + j.  a_row points at the lane's row of
+// block row 0 in this stage, a_off[q] is 4 * (position of chunk q of its
+// half); bp at B row lh * BK / 2, column wn + NI * li.  hook(j, u) as in
+// mfma_tile.
+template <int BK, int MI, int NI, int SB, int FD, int CH, class Hook>
+__device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_off)[BK / 8], const float *bp,
+                                             floatx16 (&acc)[MI][NI], floatx16 (&acc_odd)[MI][NI], Hook hook) {
+    typedef typename vec_t<NI>::type VB;
+    constexpr int STEPS = BK / 2, QN = BK / 8;
+    constexpr int RING = FD + 1;
+    float4 av[2][MI];
+    VB bv[RING];
+#pragma unroll
+    for (int i = 0; i < MI; ++i) av[0][i] = *reinterpret_cast<const float4 *>(a_row + i * 32 * BK + a_off[0]);
+#pragma unroll
+    for (int f = 0; f < FD && f < STEPS; ++f) bv[f] = *reinterpret_cast<const VB *>(bp + f * SB);
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = 4 * q + e;
+            if (e == 0 && q + 1 < QN) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+                    av[(q + 1) & 1][i] = *reinterpret_cast<const float4 *>(a_row + i * 32 * BK + a_off[q + 1]);
+            }
+            if (j + FD < STEPS) bv[(j + FD) % RING] = *reinterpret_cast<const VB *>(bp + (j + FD) * SB);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const float4 &ac = av[q & 1][i];
+                const float x = e == 0 ? ac.x : e == 1 ? ac.y : e == 2 ? ac.z : ac.w;
+#pragma unroll
+                for (int jj = 0; jj < NI; ++jj) {
+                    if (CH == 2 && (j & 1))
+                        acc_odd[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(x, vget(bv[j % RING], jj),
+                                                                              acc_odd[i][jj], 0, 0, 0);
+                    else
+                        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(x, vget(bv[j % RING], jj),
+                                                                          acc[i][jj], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    hook(j, i * NI + jj);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+    }
+}
+
+// Epilogue of the K-ordered kernel: register r of block (mi, ni) on lane
+// (li, lh) is tile row wm + 32 mi + 8 (r / 4) + 4 lh + r % 4, tile column
+// wn + NI li + ni.
+template <class TC, int MI, int NI>
+__device__ __forceinline__ void epilogue_mfma_kc(const Args &a, int bm, int bn, int wm, int wn, int li, int lh,
+                                                 const floatx16 (&acc)[MI][NI]) {
+    TC st;
+    st.init(a, bm, bn);
+    epilogue<MI * 16, NI>(
+        a, st,
+        [&](int v, int &r, int &c) {
+            const int i = v / 16, reg = v % 16;
+            r = wm + 32 * i + 8 * (reg >> 2) + 4 * lh + (reg & 3);
+            c = wn + NI * li;
+        },
+        [&](int v, float (&x)[NI]) {
+#pragma unroll
+            for (int j = 0; j < NI; ++j) x[j] = acc[v / 16][j][v % 16];
+        });
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel with A kept in K order in LDS and read from global memory along
+// K (128-bit loads when VEC == 4).  The next K tile's loads are issued in
+// pieces after the MFMAs of the first quarter of the k-steps: with DL they
+// write the other LDS stage directly, else they land in registers and are
+// stored to it in pieces over the second half.  Same tiles, split-K and
+// epilogue contract as sgemm_mfma.
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int BK, int WM, int WN, int PADB, int VEC, int WPE, bool BUF, bool SPLIT,
+          bool DL = false>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+__attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
+    constexpr int MI = WM / 32, NI = WN / 32;
+    constexpr int WAVES_N = BN / WN;
+    constexpr int NT = (BM / WM) * WAVES_N * 64;
+    constexpr int SB = BN + PADB;
+    constexpr int ASZ = BM * BK;
+    constexpr int STAGE = ASZ + BK * SB;
+    static_assert(MI == 1 || MI == 2 || MI == 4, "MI in {1, 2, 4}");
+    static_assert(NI == 1 || NI == 2 || NI == 4, "NI in {1, 2, 4}");
+    typedef typename std::conditional<BUF, AKBuf<BM, BK, NT, 1, VEC>, AKPtr<BM, BK, NT, 1>>::type TA;
+    typedef typename std::conditional<BUF, BTileBuf<BN, BK, NT, PADB, VEC, 1>,
+                                      BTilePtr<BN, BK, NT, PADB, VEC, 1>>::type TB;
+    typedef typename std::conditional<BUF, CStoreBuf<NI, VEC>, CStorePtr<NI, VEC>>::type TC;
+    __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
+    const int ntiles = nbm * nbn;
+    const int split = SPLIT && a.phase == 0 ? (int)blockIdx.x / ntiles : 0;
+    const int tile = SPLIT ? (int)blockIdx.x - split * ntiles : (int)blockIdx.x;
+    int tm, tn;
+    tile_of<0, 8>(tile, nbm, nbn, tm, tn);
+    const int bm = tm * BM, bn = tn * BN;
+    const int wm = (wave / WAVES_N) * WM, wn = (wave % WAVES_N) * WN;
+    const int li = lane & 31, lh = lane >> 5;
+
+    TA ta;
+    TB tb;
+    ta.init(a, bm, tid);
+    tb.init(a, bn, tid);
+
+    constexpr int CH = MI * NI == 1 ? 2 : 1;
+    floatx16 acc[MI][NI], acc_odd[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = acc_odd[i][j][r] = 0.0f;
+
+    if (SPLIT && a.phase == 1) {
+        // split-K, phase 1: the partials summed in split order (see sgemm_mfma)
+        for (int sp = 0; sp < a.splits; ++sp) {
+            const float4 *src = reinterpret_cast<const float4 *>(
+                a.partial + ((int64_t)tile * a.splits + sp) * (BM * BN));
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 v = src[((i * NI + j) * 4 + q) * NT + tid];
+                        acc[i][j][4 * q] += v.x;
+                        acc[i][j][4 * q + 1] += v.y;
+                        acc[i][j][4 * q + 2] += v.z;
+                        acc[i][j][4 * q + 3] += v.w;
+                    }
+        }
+        epilogue_mfma_kc<TC, MI, NI>(a, bm, bn, wm, wn, li, lh, acc);
+        return;
+    }
+
+    // the lane's A row in a stage, its chunk positions, its B row and column
+    constexpr int QN = BK / 8;
+    const int a_row = (wm + li) * BK;
+    int a_off[QN];
+#pragma unroll
+    for (int q = 0; q < QN; ++q) a_off[q] = 4 * TA::chunk_pos(wm + li, lh * QN + q);
+    const int b_off = ASZ + lh * (BK / 2) * SB + wn + NI * li;
+
+    const int KT_ALL = (a.K + BK - 1) / BK;
+    const int kt0 = SPLIT ? (int)((int64_t)KT_ALL * split / a.splits) : 0;
+    const int KT = SPLIT ? (int)((int64_t)KT_ALL * (split + 1) / a.splits) - kt0 : KT_ALL;
+    const int kb = kt0 * BK;
+
+    constexpr int STEPS = BK / 2;
+    constexpr int PA = TA::PER, PB = TB::PER, NP = PA + PB;
+    constexpr int LSTEPS = STEPS / 4 > 0 ? STEPS / 4 : 1;
+    constexpr int SSTEPS = STEPS / 2 > 0 ? STEPS / 2 : 1;
+    constexpr int LPER = (NP + LSTEPS - 1) / LSTEPS, SPER = (NP + SSTEPS - 1) / SSTEPS;
+    constexpr int NU = MI * NI;
+    if constexpr (DL) {
+        // Loads that write LDS directly: the next K tile goes straight into
+        // the other stage (last read before the previous barrier) in pieces
+        // after the MFMAs of the first k-steps; a wave waits for its own
+        // loads before the barrier that hands the stage to every wave.
+        static_assert(BUF && PADB == 0, "direct LDS loads: buffer accesses, unpadded B");
+        typedef DirectStage<BM, BN, BK, NT, VEC> D;
+        constexpr int DP = D::PA + D::PB;
+        // the loads go after the MFMAs of the first quarter of the k-steps
+        // (spreading them over a half or three quarters measured the same)
+        constexpr int DLPER = (DP + LSTEPS - 1) / LSTEPS;
+        D d;
+        d.init(a, bm, tid);
+        if (KT > 0) {
+            const rsrc_t rb = d.b_rows(a, bn, kb);
+#pragma unroll
+            for (int p = 0; p < D::PA; ++p) d.load_a(a, smem, kb, p);
+#pragma unroll
+            for (int p = 0; p < D::PB; ++p) d.load_b(rb, smem + ASZ, p);
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have written LDS
+        __syncthreads();
+        // The two stages as restrict pointers: the scoped no-alias
+        // information lets the compiler see that the reads of the current
+        // stage need not wait for the loads into the other one.
+        auto tile_body = [&](const float *__restrict__ st, float *__restrict__ nx, int kn) {
+            const rsrc_t rb = d.b_rows(a, bn, kn);
+            auto hook = [&](int j, int u) {
+                if (j < LSTEPS) {
+#pragma unroll
+                    for (int q = 0; q < DLPER; ++q) {
+                        const int piece = j * DLPER + q;
+                        if ((q * NU) / DLPER != u || piece >= DP) continue;
+                        if (piece < D::PA) d.load_a(a, nx, kn, piece);
+                        else d.load_b(rb, nx + ASZ, piece - D::PA);
+                    }
+                }
+            };
+            mfma_tile_kc<BK, MI, NI, SB, 1, CH>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
+        };
+        for (int t = 0; t < KT; ++t) {
+            tile_body(smem + (t & 1) * STAGE, smem + ((t + 1) & 1) * STAGE, kb + (t + 1) * BK);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+    } else {
+        // through registers (the checked build): loads in pieces over the
+        // first quarter of the k-steps, LDS stores over the second half
+        if (KT > 0) {
+            ta.template load<0>(a, bm, kb);
+            tb.template load<0>(a, bn, kb);
+            ta.template store<0>(smem, tid);
+            tb.template store<0>(smem + ASZ, tid);
+        }
+        __syncthreads();
+        for (int t = 0; t < KT; ++t) {
+            const float *st = smem + (t & 1) * STAGE;
+            float *nx = smem + ((t + 1) & 1) * STAGE;
+            const int kn = kb + (t + 1) * BK;
+            // piece q of a step goes after MFMA (q * MI * NI) / pieces per step;
+            // the loads after a split's last tile (the next split's first tile,
+            // or 0.0 past K) land in a stage nobody reads
+            auto hook = [&](int j, int u) {
+                if (j < LSTEPS) {
+#pragma unroll
+                    for (int q = 0; q < LPER; ++q) {
+                        const int piece = j * LPER + q;
+                        if ((q * NU) / LPER != u || piece >= NP) continue;
+                        if (piece < PA) ta.template load_piece<0>(a, bm, kn, piece);
+                        else tb.template load_piece<0>(a, bn, kn, piece - PA);
+                    }
+                }
+                if (j >= STEPS - SSTEPS) {
+#pragma unroll
+                    for (int q = 0; q < SPER; ++q) {
+                        const int piece = (j - (STEPS - SSTEPS)) * SPER + q;
+                        if ((q * NU) / SPER != u || piece >= NP) continue;
+                        if (piece < PA) ta.template store_piece<0>(nx, tid, piece);
+                        else tb.template store_piece<0>(nx + ASZ, tid, piece - PA);
+                    }
+                }
+            };
+            mfma_tile_kc<BK, MI, NI, SB, 1, CH>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
+            __syncthreads();
+        }
+    }
+
+    if (CH == 2) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) acc[i][j] += acc_odd[i][j];
+    }
+
+    if (SPLIT) {
+        float4 *mine = reinterpret_cast<float4 *>(a.partial + ((int64_t)tile * a.splits + split) * (BM * BN));
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    mine[((i * NI + j) * 4 + q) * NT + tid] =
+                        make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                    acc[i][j][4 * q + 3]);
+        return;
+    }
+    epilogue_mfma_kc<TC, MI, NI>(a, bm, bn, wm, wn, li, lh, acc);
+}
+
+// ---------------------------------------------------------------------------
 // Persistent MFMA kernel with a deferred epilogue.  One workgroup per slot
 // (the grid is at most the resident workgroups of the chip) walks the tiles
 // blockIdx.x, blockIdx.x + gridDim.x, ... in row-major order and keeps two

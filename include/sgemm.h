@@ -23,7 +23,8 @@
  * Pointers.  A, B and C are DEVICE pointers owned by the caller.  The library
  * allocates no memory, copies nothing and keeps no handles; it holds no state
  * between calls (split-K takes a caller-owned workspace, below).  No alignment is required: 16-byte aligned bases with leading
- * dimensions and N that are multiples of 4 take 128-bit global accesses,
+ * dimensions and N that are multiples of 4 take 128-bit global accesses
+ * (and K a multiple of 4 for the variants that read A 128 bits at a time),
  * anything else takes 32-bit ones (see sgemm_variant_access for the three
  * access modes).  C must not overlap A or B (undefined
  * behaviour).  Dimensions and leading dimensions are int; address arithmetic
@@ -66,7 +67,7 @@ extern "C" {
 
 /* How a kernel reaches global memory (sgemm_variant_access). */
 #define SGEMM_ACCESS_AUTO 0       /* the library's choice, as sgemm_variant() */
-#define SGEMM_ACCESS_BUFFER_128 1 /* range-checked buffer accesses, 128-bit on B and C */
+#define SGEMM_ACCESS_BUFFER_128 1 /* range-checked buffer accesses, 128-bit on B and C (and A) */
 #define SGEMM_ACCESS_BUFFER_32 2  /* range-checked buffer accesses, 32-bit */
 #define SGEMM_ACCESS_CHECKED 3    /* per-element checked pointer accesses */
 
@@ -103,6 +104,9 @@ int sgemm_variant(int variant, int M, int N, int K, float alpha,
  *               and C.  Needs 16-byte aligned B and C, N, ldb and ldc
  *               multiples of 4, and byte offsets inside one block tile below
  *               2^31 (about (BM+1)*lda*4, (BK+1)*ldb*4 and (BM+1)*ldc*4).
+ *               A variant for which sgemm_variant_reads_a128() is 1 also
+ *               reads A 128 bits at a time along K in this mode, and needs a
+ *               16-byte aligned A and K and lda multiples of 4 as well.
  *   BUFFER_32   the same with 32-bit accesses: any alignment.
  *   CHECKED     plain pointers with every element checked: any arguments.
  * SGEMM_ACCESS_AUTO takes the first of these the arguments allow.  A forced
@@ -165,6 +169,12 @@ int sgemm_variant_path(int variant);
 /* Block tile (rows, columns of C) of a variant through *bm and *bn; returns 0
  * or SGEMM_ERR_VARIANT.  Either pointer may be NULL. */
 int sgemm_variant_tile(int variant, int *bm, int *bn);
+
+/* 1 if the variant's SGEMM_ACCESS_BUFFER_128 build reads A 128 bits at a time
+ * along K (so that mode also needs K, lda multiples of 4 and A 16-byte
+ * aligned), 0 if it reads A 32 bits at a time, SGEMM_ERR_VARIANT if out of
+ * range.  Host logic only. */
+int sgemm_variant_reads_a128(int variant);
 
 /* The variant sgemm_path(path, M, N, K, ...) launches for these sizes, or a
  * negative code (-1..-3, SGEMM_ERR_PATH).  Host logic only, no HIP call. */

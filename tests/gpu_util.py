@@ -90,11 +90,15 @@ def pad_untouched(p, out):
 ACCESS_NAMES = {0: "auto", 1: "buf128", 2: "buf32", 3: "checked"}
 
 
-def allowed_accesses(p, offsets=(0, 0, 0)):
-    """The access modes whose preconditions these arguments meet (the test
-    operands are small, so the 31-bit offset bound always holds)."""
+def allowed_accesses(p, offsets=(0, 0, 0), variant=None):
+    """The access modes whose preconditions these arguments meet for a
+    variant (the test operands are small, so the 31-bit offset bound always
+    holds)."""
     modes = [g.SGEMM_ACCESS_BUFFER_32, g.SGEMM_ACCESS_CHECKED]
     aligned = offsets[1] % 4 == 0 and offsets[2] % 4 == 0
-    if p.N % 4 == 0 and p.ldb % 4 == 0 and p.ldc % 4 == 0 and aligned:
+    ok128 = p.N % 4 == 0 and p.ldb % 4 == 0 and p.ldc % 4 == 0 and aligned
+    if variant is not None and g.sgemm_variant_reads_a128(variant) == 1:
+        ok128 = ok128 and p.K % 4 == 0 and p.lda % 4 == 0 and offsets[0] % 4 == 0
+    if ok128:
         modes.insert(0, g.SGEMM_ACCESS_BUFFER_128)
     return modes

@@ -108,6 +108,32 @@ def test_access_mode_codes():
     assert "access mode" in g.sgemm_status_string(-23)
 
 
+def test_variants_reading_a_128_bits_need_k_and_a_aligned():
+    """The K-ordered blocks' 128-bit build also reads A 128 bits at a time
+    along K, so forcing it needs K, lda multiples of 4 and A 16-byte aligned
+    (the refusal comes before any HIP call)."""
+    a128 = [v for v in range(g.sgemm_variant_count()) if g.sgemm_variant_reads_a128(v) == 1]
+    assert a128 and all(g.sgemm_variant_reads_a128(v) == 0
+                        for v in range(g.sgemm_variant_count()) if v not in a128)
+    assert all("_kcd" in g.sgemm_variant_name(v) for v in a128)
+    assert g.sgemm_variant_reads_a128(g.sgemm_variant_count()) == -21
+    assert g.sgemm_variant_reads_a128(-1) == -21
+    # the automatic choice for large shapes is one of them
+    assert g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 8192, 8192, 8192) in a128
+    v = a128[0]
+
+    def acc(**kw):
+        base = dict(M=4, N=4, K=4, alpha=1.0, A=0x1000, lda=4, B=0x2000, ldb=4, beta=0.0,
+                    C=0x3000, ldc=4)
+        base.update(kw)
+        return g.sgemm_variant_access(v, g.SGEMM_ACCESS_BUFFER_128, *base.values(), stream=0,
+                                      check=False)
+    assert acc(K=3, lda=4) == -23        # K not a multiple of 4
+    assert acc(K=4, lda=5) == -23        # lda not a multiple of 4
+    assert acc(A=0x1004) == -23          # A not 16-byte aligned
+    assert acc(K=0, lda=4, beta=1.0) == 0  # no product: quick return before any launch
+
+
 def test_variant_table():
     vs = g.variants()
     assert len(vs) == g.sgemm_variant_count() >= 2
@@ -157,13 +183,13 @@ def test_large_shapes_pick_the_block_whose_last_round_is_fullest():
     assert block(1024, 8192, 8192) == (128, 256, 32)    # 256 blocks: one per CU
     assert block(2048, 2048, 2048) == (128, 128, 64)    # 256 blocks: one per CU
     assert block(3072, 3072, 3072) == (64, 64, 32)      # 128 x 128 would leave 1/4 of a round
-    assert block(1024, 1024, 1024) == (64, 64, 64)      # too few tiles: latency decides
-    assert block(1000, 1023, 999) == (64, 64, 64)
+    assert block(1024, 1024, 1024) == (64, 64, 32)      # too few tiles for any slot count
+    assert block(1000, 1023, 999) == (64, 64, 32)
 
 
 def test_only_the_latency_block_splits_k():
     """A block chosen by rate already has a tile per workgroup slot on the
-    chip; only the 64 x 64 x 64 fallback splits K when a workspace is given."""
+    chip; only the 64 x 64 fallback splits K when a workspace is given."""
     assert g.sgemm_select_splits(1024, 8192, 8192) == 1
     assert g.sgemm_select_splits(2048, 2048, 2048) == 1
     assert g.sgemm_select_splits(16384, 1024, 1024) == 1

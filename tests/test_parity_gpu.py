@@ -38,7 +38,7 @@ def combo_id(c):
 
 def run_all_modes(p, variant, offsets=(0, 0, 0)):
     """Run every access mode the arguments allow; yields (mode, output)."""
-    for acc in gu.allowed_accesses(p, offsets):
+    for acc in gu.allowed_accesses(p, offsets, variant):
         gu.say("  access", gu.ACCESS_NAMES[acc])
         yield acc, gu.run(p, variant=variant, access=acc, offsets=offsets)
 
@@ -188,7 +188,7 @@ def test_beta_zero_does_not_read_c(variant):
 def test_deterministic(variant):
     p = cached_problem("ragged_1000x1023x999")
     gu.say("determinism", g.sgemm_variant_name(variant))
-    for acc in gu.allowed_accesses(p):
+    for acc in gu.allowed_accesses(p, variant=variant):
         a = gu.run(p, variant=variant, access=acc)
         b = gu.run(p, variant=variant, access=acc)
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), acc
@@ -211,7 +211,7 @@ def test_zero_padding_invariance(variant):
     large = gu.run(big, variant=variant)  # N = 384: 128-bit accesses, same arithmetic
     assert np.array_equal(small.view(np.uint32), large[:200, :301].copy().view(np.uint32))
     # every access mode computes the same sums in the same order
-    for acc in gu.allowed_accesses(big):
+    for acc in gu.allowed_accesses(big, variant=variant):
         other = gu.run(big, variant=variant, access=acc)
         assert np.array_equal(other.view(np.uint32), large.view(np.uint32)), acc
 

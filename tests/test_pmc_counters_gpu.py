@@ -72,12 +72,22 @@ def geometry(variant):
     return name, bm, bn, bk
 
 
-def mfma_lds_per_wave(name, bm, bn, bk, threads, kt):
-    """LDS instructions of one wave over a tile's K loop of kt K tiles.
-    Reads: one A and one B fragment vector per k-step (BK / 2 steps per K
-    tile); writes: A as float4 per 4 rows, B as float4 along N, once per K
-    tile, plus, on the interleaved schedule, the tile past the end that the
-    last iteration stores unconditionally."""
+def mfma_lds_per_wave(name, bm, bn, bk, threads, kt, mi):
+    """LDS instructions of one wave over a tile's K loop of kt K tiles, and
+    how many of them the compiler may fuse in pairs (ds_read2).
+
+    A transposed (``_il`` and the plain loop): one A and one B fragment
+    vector per k-step (BK / 2 steps per K tile), any two of which may fuse;
+    writes: A as float4 per 4 rows, B as float4 along N, once per K tile,
+    plus, on the interleaved schedule, the tile past the end that the last
+    iteration stores unconditionally.
+    A in K order, loaded straight into LDS (``_kcd``): per K tile one
+    128-bit A read per block row and 4 k-steps (MI BK / 8) and one B read per
+    k-step (BK / 2, which may fuse in pairs); no LDS store instruction (the
+    buffer loads write LDS themselves)."""
+    if "_kcd" in name:
+        reads = mi * bk // 8 + bk // 2
+        return kt * reads, kt * (bk // 4)
     reads = 2 * (bk // 2)
     writes = bm * bk // (4 * threads) + bk * bn // (4 * threads)
     stored = kt + 1 if "_il" in name else kt
@@ -85,7 +95,7 @@ def mfma_lds_per_wave(name, bm, bn, bk, threads, kt):
 
 
 # the blocks the selection picks
-MFMA_CASES = [22, 23, 24, 25, 26, 27, 28, 10]
+MFMA_CASES = [29, 30, 31, 32, 33, 24, 28]
 # MFMA kernels whose every LDS access is its own instruction (none of the
 # chosen ones).  In the others the compiler fuses some pairs of fragment reads
 # into one ds_read2 / ds_read2st64 instruction, so the counter lies between
@@ -108,7 +118,7 @@ def test_mfma_counters_equal_design(variant):
     assert c["SQ_INSTS_MFMA"] == S * S * S // (32 * 32 * 2)
     assert c["SQ_INSTS_VALU_MFMA_MOPS_F32"] * 512 == 2 * S ** 3
     assert c["SQ_LDS_BANK_CONFLICT"] == 0
-    per, pairs = mfma_lds_per_wave(name, bm, bn, bk, threads, kt)
+    per, pairs = mfma_lds_per_wave(name, bm, bn, bk, threads, kt, wm // 32)
     design = tiles * waves_per_wg * per
     if variant in EXACT_LDS:
         assert c["SQ_INSTS_LDS"] == design, (kernel, per)
@@ -119,7 +129,7 @@ def test_mfma_counters_equal_design(variant):
 
 def test_mfma_runs_no_reduced_precision_matrix_ops():
     c, kernel = run_pmc(["SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
-                         "SQ_INSTS_VALU_MFMA_MOPS_F16"], 22)
+                         "SQ_INSTS_VALU_MFMA_MOPS_F16"], 29)
     if c is None:
         pytest.skip("bf16/f16 MFMA op counters not offered by this rocprofv3")
     assert c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] == 0
