@@ -23,7 +23,8 @@ __all__ = [
     "SGEMM_ACCESS_AUTO", "SGEMM_ACCESS_BUFFER_128", "SGEMM_ACCESS_BUFFER_32",
     "SGEMM_ACCESS_CHECKED", "sgemm_variant_access",
     "sgemm_ws", "sgemm_workspace_size", "sgemm_select_splits", "sgemm_splitk",
-    "sgemm_splitk_workspace_size",
+    "sgemm_splitk_workspace_size", "sgemm_streamk", "sgemm_streamk_workspace_size",
+    "sgemm_select_streamk", "sgemm_ws_plan",
     "SgemmError", "LibraryNotBuilt", "library_path", "load_library",
     "sgemm", "sgemm_path", "sgemm_variant", "sgemm_variant_count",
     "sgemm_variant_name", "sgemm_variant_path", "sgemm_variant_tile", "sgemm_variant_reads_a128",
@@ -92,6 +93,14 @@ def load_library():
         lib.sgemm_select_splits.restype = i
         lib.sgemm_splitk_workspace_size.argtypes = [i, i, i, i]
         lib.sgemm_splitk_workspace_size.restype = ctypes.c_size_t
+        lib.sgemm_streamk.argtypes = [i, i] + ws_args
+        lib.sgemm_streamk.restype = i
+        lib.sgemm_streamk_workspace_size.argtypes = [i, i]
+        lib.sgemm_streamk_workspace_size.restype = ctypes.c_size_t
+        lib.sgemm_select_streamk.argtypes = [i, i, i]
+        lib.sgemm_select_streamk.restype = i
+        lib.sgemm_ws_plan.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
+        lib.sgemm_ws_plan.restype = i
         lib.sgemm_variant_count.argtypes = []
         lib.sgemm_variant_count.restype = i
         lib.sgemm_variant_name.argtypes = [i]
@@ -185,7 +194,8 @@ def _ws_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace, workspace_
 
 def sgemm_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace=None, workspace_bytes=None,
              stream=None, check=True):
-    """sgemm() that may split K over ``workspace`` (a GPU tensor, 256-byte aligned, any contents)."""
+    """sgemm() that may split K, or share K tiles stream-K, over ``workspace`` (a GPU tensor,
+    256-byte aligned, any contents)."""
     lib = load_library()
     return _ret(lib.sgemm_ws(*_ws_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
                                        workspace_bytes, stream)), "sgemm_ws", check)
@@ -197,6 +207,35 @@ def sgemm_splitk(variant, splits, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, 
     return _ret(lib.sgemm_splitk(int(variant), int(splits),
                                  *_ws_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
                                            workspace_bytes, stream)), "sgemm_splitk", check)
+
+
+def sgemm_streamk(variant, workers, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace=None,
+                  workspace_bytes=None, stream=None, check=True):
+    lib = load_library()
+    return _ret(lib.sgemm_streamk(int(variant), int(workers),
+                                  *_ws_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
+                                            workspace_bytes, stream)), "sgemm_streamk", check)
+
+
+def sgemm_streamk_workspace_size(variant, workers) -> int:
+    return int(load_library().sgemm_streamk_workspace_size(int(variant), int(workers)))
+
+
+def sgemm_select_streamk(M, N, K) -> int:
+    return int(load_library().sgemm_select_streamk(int(M), int(N), int(K)))
+
+
+def sgemm_ws_plan(M, N, K):
+    """``(status, variant, splits, workers)``: what sgemm_ws() runs with enough workspace."""
+    v, sp, w = ctypes.c_int(-1), ctypes.c_int(0), ctypes.c_int(0)
+    rc = load_library().sgemm_ws_plan(int(M), int(N), int(K), ctypes.byref(v), ctypes.byref(sp),
+                                      ctypes.byref(w))
+    return int(rc), v.value, sp.value, w.value
+
+
+def variant_has_streamk(variant) -> bool:
+    """True when the variant's split builds also run stream-K."""
+    return sgemm_streamk_workspace_size(variant, 256) > 0
 
 
 def sgemm_workspace_size(M, N, K) -> int:

@@ -31,6 +31,7 @@ struct Variant {
     KernelFn split1;    // split-K, as vec1
     int persistent;     // 0: one workgroup per tile; n: a persistent grid of n workgroups per CU
     int a128;           // 1: the vec4 build also reads A 128 bits at a time along K
+    int streamk;        // 1: the split builds also run stream-K (phases 2 and 3)
 };
 
 // VALU: 128 x 128 x 16 block, 4 waves of 64 x 64, 8 x 8 per lane.
@@ -111,7 +112,7 @@ struct Variant {
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 0, 1, WPE, true, false, true>,               \
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 0, 1, WPE, false, false, false>,             \
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 0, 4, WPE, true, true, true>,                \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 0, 1, WPE, true, true, true>, 0, 1}
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 0, 1, WPE, true, true, true>, 0, 1, 1}
 
 const Variant kVariants[] = {
     VALU_CFG(128, 128, 16, 8, 8, 4, 0, 4),                     // 0
@@ -175,6 +176,7 @@ constexpr int kKcSmall4 = 33;    // 64 x 64 x 32, four workgroups per CU
 // sizes so that it is the same on every call and testable without a GPU.
 constexpr long long kComputeUnits = 256;
 constexpr int kMaxSplits = 64;
+constexpr int kMaxWorkers = 4096;
 
 long long tiles(int M, int N, int bm, int bn) {
     return (long long)((M + bm - 1) / bm) * (long long)((N + bn - 1) / bn);
@@ -215,7 +217,17 @@ double quantization(long long t) {
 //   * below that the problem cannot fill the chip: 64 x 64 x 32 blocks
 //     (10-15% faster there than 64 x 64 x 64 blocks with fragments three
 //     k-steps ahead), split along K when K is long (select_splits).
-int select_variant(int path, int M, int N, int K) {
+// Stream-K (with a workspace): a block whose last round of tiles leaves
+// workgroup slots idle runs its whole rounds as usual and spreads the K tiles
+// of the rest over one workgroup per slot, so every slot ends at about the
+// same time.  Scored as the block's full-chip rate times kStreamKShare, the
+// measured cost of the partial tiles and their summing pass, when each
+// worker gets at least kStreamKMinK K tiles.
+constexpr double kStreamKShare = 0.985;
+constexpr int kStreamKMinK = 8;
+
+int choose(int path, int M, int N, int K, bool streamk, int *workers) {
+    if (workers) *workers = 0;
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
@@ -240,20 +252,33 @@ int select_variant(int path, int M, int N, int K) {
                                      {kKcShortK, 144.0, 2, 0},  {kKcWide, 142.0, 1, 512},
                                      {kIlMid, 140.5, 2, 256},   {kIlDeep, 137.0, 1, 512},
                                      {kKcSmall4, 130.0, 4, 0}};
-    int best = -1;
+    int best = -1, best_workers = 0;
     double best_score = -1.0;
     for (const Candidate &c : cand) {
         const Variant &v = kVariants[c.variant];
         const long long t = tiles(M, N, v.bm, v.bn);
-        if (t < c.per_cu * kComputeUnits || K < c.min_k) continue;
-        const double score = c.rate * quantization(t);
+        const long long slots = c.per_cu * kComputeUnits;
+        if (t < slots || K < c.min_k) continue;
+        double score = c.rate * quantization(t);
+        int w = 0;
+        const long long rest = t % slots, kt = (K + v.bk - 1) / v.bk;
+        if (streamk && v.streamk && rest > 0 && rest * kt >= kStreamKMinK * slots &&
+            c.rate * kStreamKShare > score) {
+            score = c.rate * kStreamKShare;
+            w = (int)slots;
+        }
         if (score > best_score) {
             best_score = score;
             best = c.variant;
+            best_workers = w;
         }
     }
-    return best >= 0 ? best : kKcSmall4;
+    if (best < 0) return kKcSmall4;
+    if (workers) *workers = best_workers;
+    return best;
 }
+
+int select_variant(int path, int M, int N, int K) { return choose(path, M, N, K, false, nullptr); }
 
 // Split count for a variant when a workspace is available (measured on
 // MI355X: 512 x 512 x 8192 runs 3.5x faster in 8 parts, 1024 x 1024 x 4096
@@ -299,7 +324,13 @@ size_t splitk_bytes(const Variant &v, int splits, int M, int N) {
     return round_up((size_t)splits * (size_t)tiles(M, N, v.bm, v.bn) * v.bm * v.bn * 4, 256);
 }
 
-int launch(int variant, int access, int splits, void *workspace, size_t workspace_bytes,
+// Workspace of a stream-K launch: two partial tiles per worker,
+// float [worker][2][bm*bn].
+size_t streamk_bytes(const Variant &v, int workers) {
+    return round_up((size_t)workers * 2 * v.bm * v.bn * 4, 256);
+}
+
+int launch(int variant, int access, int splits, int workers, void *workspace, size_t workspace_bytes,
            int M, int N, int K, float alpha, const float *A,
            int lda, const float *B, int ldb, float beta, float *C, int ldc,
            hipStream_t stream) {
@@ -309,14 +340,23 @@ int launch(int variant, int access, int splits, void *workspace, size_t workspac
     if (access < SGEMM_ACCESS_AUTO || access > SGEMM_ACCESS_CHECKED) return SGEMM_ERR_ACCESS;
     if (splits < 1 || splits > kMaxSplits) return SGEMM_ERR_SPLITS;
     if (splits > 1 && kVariants[variant].split4 == nullptr) return SGEMM_ERR_SPLITS;
+    if (workers < 0 || workers > kMaxWorkers || (workers > 0 && splits > 1)) return SGEMM_ERR_SPLITS;
+    if (workers > 0 && !kVariants[variant].streamk) return SGEMM_ERR_SPLITS;
     if (M == 0 || N == 0) return SGEMM_OK;
     const bool no_product = alpha == 0.0f || K == 0;
     if (no_product && beta == 1.0f) return SGEMM_OK;
 
     const Variant &v = kVariants[variant];
-    if (no_product) splits = 1;  // C = beta * C needs no K split
-    const long long grid = tiles(M, N, v.bm, v.bn) * splits;
-    if (grid > INT_MAX) return SGEMM_ERR_TOO_LARGE;
+    if (no_product) {  // C = beta * C needs no K split
+        splits = 1;
+        workers = 0;
+    }
+    const long long ntiles = tiles(M, N, v.bm, v.bn);
+    // stream-K: the last ntiles % workers tiles are shared by the workers
+    const long long shared = workers > 0 ? ntiles % workers : 0;
+    if (shared == 0) workers = 0;  // whole rounds: every tile whole
+    const long long grid = workers > 0 ? ntiles - shared + workers : ntiles * splits;
+    if (ntiles * splits > INT_MAX || grid > INT_MAX) return SGEMM_ERR_TOO_LARGE;
 
     Args a;
     a.M = M;
@@ -333,6 +373,8 @@ int launch(int variant, int access, int splits, void *workspace, size_t workspac
     a.splits = 1;
     a.partial = nullptr;
     a.phase = 0;
+    a.sk_whole = 0;
+    a.sk_workers = 0;
     // Buffer accesses form byte offsets inside one block tile in 31 bits.
     const long long lim = 1LL << 31;
     const bool buf_ok = (long long)(v.bm + 1) * lda * 4 < lim &&
@@ -363,15 +405,20 @@ int launch(int variant, int access, int splits, void *workspace, size_t workspac
             fn = !buf_ok ? v.generic : (vec4 ? v.vec4 : v.vec1);
             break;
     }
-    if (splits > 1) {
-        // split-K kernels exist for buffer accesses only
+    if (splits > 1 || workers > 0) {
+        // split-K and stream-K kernels exist for buffer accesses only
         if (fn == v.generic) return SGEMM_ERR_ACCESS;
-        const size_t need = splitk_bytes(v, splits, M, N);
+        const size_t need = workers > 0 ? streamk_bytes(v, workers) : splitk_bytes(v, splits, M, N);
         if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
             return SGEMM_ERR_WORKSPACE;
         fn = fn == v.vec4 ? v.split4 : v.split1;
         a.splits = splits;
         a.partial = static_cast<float *>(workspace);
+        if (workers > 0) {
+            a.phase = 2;
+            a.sk_whole = (int)(ntiles - shared);
+            a.sk_workers = workers;
+        }
     }
 
     // a persistent variant launches one workgroup per resident slot and loops over the tiles
@@ -380,10 +427,13 @@ int launch(int variant, int access, int splits, void *workspace, size_t workspac
     (void)hipGetLastError();  // drop any stale error so the code below is this launch's
     hipLaunchKernelGGL(fn, dim3((unsigned)launch_grid), dim3(v.threads), 0, stream, a);
     hipError_t err = hipGetLastError();
-    if (err == hipSuccess && splits > 1) {
-        // phase 1 on the same stream: it starts after every partial is written
-        a.phase = 1;
-        hipLaunchKernelGGL(fn, dim3((unsigned)(grid / splits)), dim3(v.threads), 0, stream, a);
+    if (err == hipSuccess && (splits > 1 || workers > 0)) {
+        // the summing phase on the same stream: it starts after every
+        // partial is written (split-K: one workgroup per tile; stream-K: one
+        // per shared tile)
+        a.phase = workers > 0 ? 3 : 1;
+        const long long grid2 = workers > 0 ? shared : ntiles;
+        hipLaunchKernelGGL(fn, dim3((unsigned)grid2), dim3(v.threads), 0, stream, a);
         err = hipGetLastError();
     }
     return err == hipSuccess ? SGEMM_OK : (int)err;
@@ -406,26 +456,28 @@ int sgemm_path(int path, int M, int N, int K, float alpha, const float *A,
     if (rc != SGEMM_OK) return rc;
     const int v = select_variant(path, M, N, K);
     if (v < 0) return v;
-    return launch(v, SGEMM_ACCESS_AUTO, 1, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return launch(v, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                  stream);
 }
 
 int sgemm_variant(int variant, int M, int N, int K, float alpha,
                   const float *A, int lda, const float *B, int ldb, float beta,
                   float *C, int ldc, hipStream_t stream) {
-    return launch(variant, SGEMM_ACCESS_AUTO, 1, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return launch(variant, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                  ldc, stream);
 }
 
 int sgemm_variant_access(int variant, int access, int M, int N, int K, float alpha,
                          const float *A, int lda, const float *B, int ldb, float beta,
                          float *C, int ldc, hipStream_t stream) {
-    return launch(variant, access, 1, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return launch(variant, access, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 int sgemm_splitk(int variant, int splits, int M, int N, int K, float alpha,
                  const float *A, int lda, const float *B, int ldb, float beta,
                  float *C, int ldc, void *workspace, size_t workspace_bytes,
                  hipStream_t stream) {
-    return launch(variant, SGEMM_ACCESS_AUTO, splits, workspace, workspace_bytes, M, N, K, alpha,
+    return launch(variant, SGEMM_ACCESS_AUTO, splits, 0, workspace, workspace_bytes, M, N, K, alpha,
                   A, lda, B, ldb, beta, C, ldc, stream);
 }
 
@@ -437,14 +489,50 @@ size_t sgemm_splitk_workspace_size(int variant, int splits, int M, int N) {
     return splitk_bytes(kVariants[variant], splits, M, N);
 }
 
+int sgemm_streamk(int variant, int workers, int M, int N, int K, float alpha,
+                  const float *A, int lda, const float *B, int ldb, float beta,
+                  float *C, int ldc, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+    if (workers < 1) return SGEMM_ERR_SPLITS;
+    return launch(variant, SGEMM_ACCESS_AUTO, 1, workers, workspace, workspace_bytes, M, N, K, alpha,
+                  A, lda, B, ldb, beta, C, ldc, stream);
+}
+
+size_t sgemm_streamk_workspace_size(int variant, int workers) {
+    if (variant < 0 || variant >= kNumVariants || workers < 1 || workers > kMaxWorkers) return 0;
+    if (!kVariants[variant].streamk) return 0;
+    return streamk_bytes(kVariants[variant], workers);
+}
+
 int sgemm_select_splits(int M, int N, int K) {
-    const int v = select_variant(SGEMM_PATH_AUTO, M, N, K);
-    return v < 0 ? v : select_splits(v, M, N, K);
+    int workers = 0;
+    const int v = choose(SGEMM_PATH_AUTO, M, N, K, true, &workers);
+    if (v < 0) return v;
+    return workers > 0 ? 1 : select_splits(v, M, N, K);
+}
+
+int sgemm_ws_plan(int M, int N, int K, int *variant, int *splits, int *workers) {
+    int w = 0;
+    int v = choose(SGEMM_PATH_AUTO, M, N, K, true, &w);
+    if (v < 0) return v;
+    const int sp = w > 0 ? 1 : select_splits(v, M, N, K);
+    if (variant) *variant = v;
+    if (splits) *splits = sp;
+    if (workers) *workers = w;
+    return SGEMM_OK;
+}
+
+int sgemm_select_streamk(int M, int N, int K) {
+    int workers = 0;
+    const int v = choose(SGEMM_PATH_AUTO, M, N, K, true, &workers);
+    return v < 0 ? v : workers;
 }
 
 size_t sgemm_workspace_size(int M, int N, int K) {
-    const int v = select_variant(SGEMM_PATH_AUTO, M, N, K);
+    int workers = 0;
+    const int v = choose(SGEMM_PATH_AUTO, M, N, K, true, &workers);
     if (v < 0) return 0;
+    if (workers > 0) return streamk_bytes(kVariants[v], workers);
     const int sp = select_splits(v, M, N, K);
     return sp > 1 ? splitk_bytes(kVariants[v], sp, M, N) : 0;
 }
@@ -454,12 +542,20 @@ int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const fl
              hipStream_t stream) {
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
-    const int v = select_variant(SGEMM_PATH_AUTO, M, N, K);
+    int workers = 0;
+    int v = choose(SGEMM_PATH_AUTO, M, N, K, true, &workers);
     if (v < 0) return v;
+    const bool room = workspace != nullptr && ((uintptr_t)workspace & 255u) == 0;
+    if (workers > 0) {
+        if (room && workspace_bytes >= streamk_bytes(kVariants[v], workers))
+            return launch(v, SGEMM_ACCESS_AUTO, 1, workers, workspace, workspace_bytes, M, N, K, alpha,
+                          A, lda, B, ldb, beta, C, ldc, stream);
+        v = select_variant(SGEMM_PATH_AUTO, M, N, K);  // not enough workspace: whole tiles only
+    }
     int sp = select_splits(v, M, N, K);
-    if (sp > 1 && (workspace == nullptr || workspace_bytes < splitk_bytes(kVariants[v], sp, M, N)))
+    if (sp > 1 && (!room || workspace_bytes < splitk_bytes(kVariants[v], sp, M, N)))
         sp = 1;  // not enough workspace: the unsplit kernel
-    return launch(v, SGEMM_ACCESS_AUTO, sp, workspace, workspace_bytes, M, N, K, alpha, A, lda, B,
+    return launch(v, SGEMM_ACCESS_AUTO, sp, 0, workspace, workspace_bytes, M, N, K, alpha, A, lda, B,
                   ldb, beta, C, ldc, stream);
 }
 
@@ -508,7 +604,8 @@ const char *sgemm_status_string(int status) {
         case SGEMM_ERR_TOO_LARGE: return "problem too large: tile grid exceeds one launch";
         case SGEMM_ERR_ACCESS: return "invalid argument: access mode unknown or not possible for these arguments";
         case SGEMM_ERR_WORKSPACE: return "invalid argument: workspace missing, too small or not 256-byte aligned";
-        case SGEMM_ERR_SPLITS: return "invalid argument: split count out of range or variant without split-K";
+        case SGEMM_ERR_SPLITS:
+            return "invalid argument: split or worker count out of range, or variant without split-K or stream-K";
         default: break;
     }
     if (status > 0) return hipGetErrorString((hipError_t)status);

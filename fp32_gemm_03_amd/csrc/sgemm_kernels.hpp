@@ -71,10 +71,14 @@ struct Args {
     float *C;
     int64_t lda, ldb, ldc;
     // split-K only: number of K ranges, partial tiles [tile][split][BM*BN],
-    // and the launch's phase (0: write partials, 1: sum them and store C)
+    // and the launch's phase (0: write partials, 1: sum them and store C;
+    // stream-K: 2: whole tiles and workers' partial tiles, 3: sum them)
     int splits;
     float *partial;
     int phase;
+    // stream-K only: tiles done whole (the first sk_whole in tile order) and
+    // the workers that share the K tiles of the rest
+    int sk_whole, sk_workers;
 };
 
 template <int W> struct vec_t;
@@ -1324,33 +1328,167 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     const int lane = tid & 63, wave = tid >> 6;
     const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
     const int ntiles = nbm * nbn;
-    const int split = SPLIT && a.phase == 0 ? (int)blockIdx.x / ntiles : 0;
-    const int tile = SPLIT ? (int)blockIdx.x - split * ntiles : (int)blockIdx.x;
-    int tm, tn;
-    tile_of<0, 8>(tile, nbm, nbn, tm, tn);
-    const int bm = tm * BM, bn = tn * BN;
     const int wm = (wave / WAVES_N) * WM, wn = (wave % WAVES_N) * WN;
     const int li = lane & 31, lh = lane >> 5;
-
-    TA ta;
-    TB tb;
-    ta.init(a, bm, tid);
-    tb.init(a, bn, tid);
+    const int KT_ALL = (a.K + BK - 1) / BK;
 
     constexpr int CH = MI * NI == 1 ? 2 : 1;
     floatx16 acc[MI][NI], acc_odd[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = acc_odd[i][j][r] = 0.0f;
 
-    if (SPLIT && a.phase == 1) {
-        // split-K, phase 1: the partials summed in split order (see sgemm_mfma)
-        for (int sp = 0; sp < a.splits; ++sp) {
-            const float4 *src = reinterpret_cast<const float4 *>(
-                a.partial + ((int64_t)tile * a.splits + sp) * (BM * BN));
+    // the lane's A row in a stage, its chunk positions, its B row and column
+    constexpr int QN = BK / 8;
+    const int a_row = (wm + li) * BK;
+    int a_off[QN];
+#pragma unroll
+    for (int q = 0; q < QN; ++q) a_off[q] = 4 * TA::chunk_pos(wm + li, lh * QN + q);
+    const int b_off = ASZ + lh * (BK / 2) * SB + wn + NI * li;
+
+    constexpr int STEPS = BK / 2;
+    constexpr int LSTEPS = STEPS / 4 > 0 ? STEPS / 4 : 1;
+    constexpr int SSTEPS = STEPS / 2 > 0 ? STEPS / 2 : 1;
+    constexpr int NU = MI * NI;
+
+    // acc = the product of the tile at (bm, bn) over K tiles [k_lo, k_hi).
+    // Starts and ends with every wave past a barrier, so it may run again
+    // on the same LDS.
+    auto k_range = [&](int bm, int bn, int k_lo, int k_hi) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = acc_odd[i][j][r] = 0.0f;
+        const int KT = k_hi - k_lo, kb = k_lo * BK;
+        if constexpr (DL) {
+            // Loads that write LDS directly: the next K tile goes straight
+            // into the other stage (last read before the previous barrier)
+            // in pieces after the MFMAs of the first k-steps; a wave waits
+            // for its own loads before the barrier that hands the stage to
+            // every wave.
+            static_assert(BUF && PADB == 0, "direct LDS loads: buffer accesses, unpadded B");
+            typedef DirectStage<BM, BN, BK, NT, VEC> D;
+            constexpr int DP = D::PA + D::PB;
+            // the loads go after the MFMAs of the first quarter of the
+            // k-steps (spreading them over a half or three quarters measured
+            // the same)
+            constexpr int DLPER = (DP + LSTEPS - 1) / LSTEPS;
+            D d;
+            d.init(a, bm, tid);
+            if (KT > 0) {
+                const rsrc_t rb = d.b_rows(a, bn, kb);
+#pragma unroll
+                for (int p = 0; p < D::PA; ++p) d.load_a(a, smem, kb, p);
+#pragma unroll
+                for (int p = 0; p < D::PB; ++p) d.load_b(rb, smem + ASZ, p);
+            }
+            __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have written LDS
+            __syncthreads();
+            // The two stages as restrict pointers: the scoped no-alias
+            // information lets the compiler see that the reads of the current
+            // stage need not wait for the loads into the other one.
+            auto tile_body = [&](const float *__restrict__ st, float *__restrict__ nx, int kn) {
+                const rsrc_t rb = d.b_rows(a, bn, kn);
+                auto hook = [&](int j, int u) {
+                    if (j < LSTEPS) {
+#pragma unroll
+                        for (int q = 0; q < DLPER; ++q) {
+                            const int piece = j * DLPER + q;
+                            if ((q * NU) / DLPER != u || piece >= DP) continue;
+                            if (piece < D::PA) d.load_a(a, nx, kn, piece);
+                            else d.load_b(rb, nx + ASZ, piece - D::PA);
+                        }
+                    }
+                };
+                mfma_tile_kc<BK, MI, NI, SB, 1, CH>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
+            };
+            for (int t = 0; t < KT; ++t) {
+                tile_body(smem + (t & 1) * STAGE, smem + ((t + 1) & 1) * STAGE, kb + (t + 1) * BK);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            }
+        } else {
+            // through registers (the checked build): loads in pieces over
+            // the first quarter of the k-steps, LDS stores over the second half
+            constexpr int PA = TA::PER, PB = TB::PER, NP = PA + PB;
+            constexpr int LPER = (NP + LSTEPS - 1) / LSTEPS, SPER = (NP + SSTEPS - 1) / SSTEPS;
+            TA ta;
+            TB tb;
+            ta.init(a, bm, tid);
+            tb.init(a, bn, tid);
+            if (KT > 0) {
+                ta.template load<0>(a, bm, kb);
+                tb.template load<0>(a, bn, kb);
+                ta.template store<0>(smem, tid);
+                tb.template store<0>(smem + ASZ, tid);
+            }
+            __syncthreads();
+            for (int t = 0; t < KT; ++t) {
+                const float *st = smem + (t & 1) * STAGE;
+                float *nx = smem + ((t + 1) & 1) * STAGE;
+                const int kn = kb + (t + 1) * BK;
+                // piece q of a step goes after MFMA (q * MI * NI) / pieces per
+                // step; the loads after a range's last tile (the next tile,
+                // or 0.0 past K) land in a stage nobody reads
+                auto hook = [&](int j, int u) {
+                    if (j < LSTEPS) {
+#pragma unroll
+                        for (int q = 0; q < LPER; ++q) {
+                            const int piece = j * LPER + q;
+                            if ((q * NU) / LPER != u || piece >= NP) continue;
+                            if (piece < PA) ta.template load_piece<0>(a, bm, kn, piece);
+                            else tb.template load_piece<0>(a, bn, kn, piece - PA);
+                        }
+                    }
+                    if (j >= STEPS - SSTEPS) {
+#pragma unroll
+                        for (int q = 0; q < SPER; ++q) {
+                            const int piece = (j - (STEPS - SSTEPS)) * SPER + q;
+                            if ((q * NU) / SPER != u || piece >= NP) continue;
+                            if (piece < PA) ta.template store_piece<0>(nx, tid, piece);
+                            else tb.template store_piece<0>(nx + ASZ, tid, piece - PA);
+                        }
+                    }
+                };
+                mfma_tile_kc<BK, MI, NI, SB, 1, CH>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
+                __syncthreads();
+            }
+        }
+        if (CH == 2) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j) acc[i][j] += acc_odd[i][j];
+        }
+    };
+    auto origin = [&](int tile, int &bm, int &bn) {
+        int tm, tn;
+        tile_of<0, 8>(tile, nbm, nbn, tm, tn);
+        bm = tm * BM;
+        bn = tn * BN;
+    };
+    auto finish = [&](int bm, int bn) { epilogue_mfma_kc<TC, MI, NI>(a, bm, bn, wm, wn, li, lh, acc); };
+
+    if constexpr (!SPLIT) {
+        int bm, bn;
+        origin((int)blockIdx.x, bm, bn);
+        k_range(bm, bn, 0, KT_ALL);
+        finish(bm, bn);
+    } else {
+        // A partial tile in the lanes' own order (4-float chunks,
+        // consecutive threads adjacent), written and added back.
+        auto store_partial = [&](float *dst) {
+            float4 *mine = reinterpret_cast<float4 *>(dst);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        mine[((i * NI + j) * 4 + q) * NT + tid] = make_float4(
+                            acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        };
+        auto add_partial = [&](const float *src_) {
+            const float4 *src = reinterpret_cast<const float4 *>(src_);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -1363,138 +1501,88 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
                         acc[i][j][4 * q + 2] += v.z;
                         acc[i][j][4 * q + 3] += v.w;
                     }
-        }
-        epilogue_mfma_kc<TC, MI, NI>(a, bm, bn, wm, wn, li, lh, acc);
-        return;
-    }
-
-    // the lane's A row in a stage, its chunk positions, its B row and column
-    constexpr int QN = BK / 8;
-    const int a_row = (wm + li) * BK;
-    int a_off[QN];
-#pragma unroll
-    for (int q = 0; q < QN; ++q) a_off[q] = 4 * TA::chunk_pos(wm + li, lh * QN + q);
-    const int b_off = ASZ + lh * (BK / 2) * SB + wn + NI * li;
-
-    const int KT_ALL = (a.K + BK - 1) / BK;
-    const int kt0 = SPLIT ? (int)((int64_t)KT_ALL * split / a.splits) : 0;
-    const int KT = SPLIT ? (int)((int64_t)KT_ALL * (split + 1) / a.splits) - kt0 : KT_ALL;
-    const int kb = kt0 * BK;
-
-    constexpr int STEPS = BK / 2;
-    constexpr int PA = TA::PER, PB = TB::PER, NP = PA + PB;
-    constexpr int LSTEPS = STEPS / 4 > 0 ? STEPS / 4 : 1;
-    constexpr int SSTEPS = STEPS / 2 > 0 ? STEPS / 2 : 1;
-    constexpr int LPER = (NP + LSTEPS - 1) / LSTEPS, SPER = (NP + SSTEPS - 1) / SSTEPS;
-    constexpr int NU = MI * NI;
-    if constexpr (DL) {
-        // Loads that write LDS directly: the next K tile goes straight into
-        // the other stage (last read before the previous barrier) in pieces
-        // after the MFMAs of the first k-steps; a wave waits for its own
-        // loads before the barrier that hands the stage to every wave.
-        static_assert(BUF && PADB == 0, "direct LDS loads: buffer accesses, unpadded B");
-        typedef DirectStage<BM, BN, BK, NT, VEC> D;
-        constexpr int DP = D::PA + D::PB;
-        // the loads go after the MFMAs of the first quarter of the k-steps
-        // (spreading them over a half or three quarters measured the same)
-        constexpr int DLPER = (DP + LSTEPS - 1) / LSTEPS;
-        D d;
-        d.init(a, bm, tid);
-        if (KT > 0) {
-            const rsrc_t rb = d.b_rows(a, bn, kb);
-#pragma unroll
-            for (int p = 0; p < D::PA; ++p) d.load_a(a, smem, kb, p);
-#pragma unroll
-            for (int p = 0; p < D::PB; ++p) d.load_b(rb, smem + ASZ, p);
-        }
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have written LDS
-        __syncthreads();
-        // The two stages as restrict pointers: the scoped no-alias
-        // information lets the compiler see that the reads of the current
-        // stage need not wait for the loads into the other one.
-        auto tile_body = [&](const float *__restrict__ st, float *__restrict__ nx, int kn) {
-            const rsrc_t rb = d.b_rows(a, bn, kn);
-            auto hook = [&](int j, int u) {
-                if (j < LSTEPS) {
-#pragma unroll
-                    for (int q = 0; q < DLPER; ++q) {
-                        const int piece = j * DLPER + q;
-                        if ((q * NU) / DLPER != u || piece >= DP) continue;
-                        if (piece < D::PA) d.load_a(a, nx, kn, piece);
-                        else d.load_b(rb, nx + ASZ, piece - D::PA);
-                    }
-                }
-            };
-            mfma_tile_kc<BK, MI, NI, SB, 1, CH>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
         };
-        for (int t = 0; t < KT; ++t) {
-            tile_body(smem + (t & 1) * STAGE, smem + ((t + 1) & 1) * STAGE, kb + (t + 1) * BK);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-        }
-    } else {
-        // through registers (the checked build): loads in pieces over the
-        // first quarter of the k-steps, LDS stores over the second half
-        if (KT > 0) {
-            ta.template load<0>(a, bm, kb);
-            tb.template load<0>(a, bn, kb);
-            ta.template store<0>(smem, tid);
-            tb.template store<0>(smem + ASZ, tid);
-        }
-        __syncthreads();
-        for (int t = 0; t < KT; ++t) {
-            const float *st = smem + (t & 1) * STAGE;
-            float *nx = smem + ((t + 1) & 1) * STAGE;
-            const int kn = kb + (t + 1) * BK;
-            // piece q of a step goes after MFMA (q * MI * NI) / pieces per step;
-            // the loads after a split's last tile (the next split's first tile,
-            // or 0.0 past K) land in a stage nobody reads
-            auto hook = [&](int j, int u) {
-                if (j < LSTEPS) {
+        auto zero = [&]() {
 #pragma unroll
-                    for (int q = 0; q < LPER; ++q) {
-                        const int piece = j * LPER + q;
-                        if ((q * NU) / LPER != u || piece >= NP) continue;
-                        if (piece < PA) ta.template load_piece<0>(a, bm, kn, piece);
-                        else tb.template load_piece<0>(a, bn, kn, piece - PA);
-                    }
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+        };
+        // Stream-K: the K tiles of the last R tiles, R * KT_ALL in all, are
+        // shared by S workers; worker w takes [w I / S, (w + 1) I / S), and
+        // the worker holding K tile x of that sequence is owner(x).
+        const int R = ntiles - a.sk_whole, S = a.sk_workers;
+        const int64_t I = (int64_t)R * KT_ALL;
+        auto first = [&](int64_t w) { return w * I / S; };
+        auto owner = [&](int64_t x) { return (int)(((x + 1) * S - 1) / I); };
+        int bm, bn;
+        if (a.phase == 1 || a.phase == 3) {
+            // The partials of one tile summed in a fixed order, then C:
+            // split-K in split order, stream-K in worker order.
+            zero();
+            if (a.phase == 1) {
+                const int tile = (int)blockIdx.x;
+                origin(tile, bm, bn);
+                for (int sp = 0; sp < a.splits; ++sp)
+                    add_partial(a.partial + ((int64_t)tile * a.splits + sp) * (BM * BN));
+            } else {
+                const int r = (int)blockIdx.x;
+                const int w0 = owner((int64_t)r * KT_ALL), w1 = owner((int64_t)(r + 1) * KT_ALL - 1);
+                if (w0 == w1) return;  // one worker held the tile whole: already in C
+                origin(a.sk_whole + r, bm, bn);
+                for (int w = w0; w <= w1; ++w) {
+                    if (first(w) == first(w + 1)) continue;  // a worker with no K tiles
+                    add_partial(a.partial + ((int64_t)w * 2 + (first(w) / KT_ALL == r ? 0 : 1)) * (BM * BN));
                 }
-                if (j >= STEPS - SSTEPS) {
-#pragma unroll
-                    for (int q = 0; q < SPER; ++q) {
-                        const int piece = (j - (STEPS - SSTEPS)) * SPER + q;
-                        if ((q * NU) / SPER != u || piece >= NP) continue;
-                        if (piece < PA) ta.template store_piece<0>(nx, tid, piece);
-                        else tb.template store_piece<0>(nx + ASZ, tid, piece - PA);
-                    }
-                }
-            };
-            mfma_tile_kc<BK, MI, NI, SB, 1, CH>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
-            __syncthreads();
+            }
+            finish(bm, bn);
+            return;
+        }
+        // Phases 0 and 2: one or two K ranges, each stored as a partial tile
+        // or, when it is a whole tile, finished into C.
+        //   split-K: this split's K range of its tile;
+        //   stream-K: a whole tile (the first sk_whole workgroups), or a
+        //   worker's K tiles, fewer than KT_ALL (R < S), so at most the end
+        //   of one tile (slot 0) and the start of the next (slot 1).
+        const bool worker = a.phase == 2 && (int)blockIdx.x >= a.sk_whole;
+        const int w = (int)blockIdx.x - a.sk_whole;
+        int64_t x = worker ? first(w) : 0;
+        const int64_t end = worker ? first(w + 1) : 0;
+#pragma unroll 1
+        for (int slot = 0; slot < 2; ++slot) {
+            int tile, k_lo, k_hi;
+            float *dst = nullptr;
+            if (a.phase == 0) {
+                if (slot > 0) break;
+                const int split = (int)blockIdx.x / ntiles;
+                tile = (int)blockIdx.x - split * ntiles;
+                k_lo = (int)((int64_t)KT_ALL * split / a.splits);
+                k_hi = (int)((int64_t)KT_ALL * (split + 1) / a.splits);
+                dst = a.partial + ((int64_t)tile * a.splits + split) * (BM * BN);
+            } else if (!worker) {
+                if (slot > 0) break;
+                tile = (int)blockIdx.x;
+                k_lo = 0;
+                k_hi = KT_ALL;
+            } else {
+                if (x >= end) break;
+                const int r = (int)(x / KT_ALL);
+                tile = a.sk_whole + r;
+                k_lo = (int)(x - (int64_t)r * KT_ALL);
+                k_hi = end - x < KT_ALL - k_lo ? k_lo + (int)(end - x) : KT_ALL;
+                if (k_lo != 0 || k_hi != KT_ALL) dst = a.partial + ((int64_t)w * 2 + slot) * (BM * BN);
+                x += k_hi - k_lo;
+            }
+            origin(tile, bm, bn);
+            k_range(bm, bn, k_lo, k_hi);
+            if (dst)
+                store_partial(dst);
+            else
+                finish(bm, bn);
         }
     }
-
-    if (CH == 2) {
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NI; ++j) acc[i][j] += acc_odd[i][j];
-    }
-
-    if (SPLIT) {
-        float4 *mine = reinterpret_cast<float4 *>(a.partial + ((int64_t)tile * a.splits + split) * (BM * BN));
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    mine[((i * NI + j) * 4 + q) * NT + tid] =
-                        make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                    acc[i][j][4 * q + 3]);
-        return;
-    }
-    epilogue_mfma_kc<TC, MI, NI>(a, bm, bn, wm, wn, li, lh, acc);
 }
 
 // ---------------------------------------------------------------------------

@@ -8,7 +8,8 @@ A shape is a named synthetic workload (``square8192_normal`` ...) or MxNxK
 ABI on one stream; the time per launch is HIP events around a run of
 launches.  Besides the forced variants, two rows time the library's own
 choice: ``auto`` (``sgemm``) and ``auto+ws`` (``sgemm_ws`` with the workspace
-it asks for, which may split K).  The last block is a table of the selection
+it asks for, which may split K or share the K tiles of a last partial round
+of tiles over stream-K workers).  The last block is a table of the selection
 against the best variant per shape: the measurement the selection table in
 ``sgemm.hip`` was fitted to, repeatable on any MI355X.
 """
@@ -81,23 +82,25 @@ def tune(shapes, variants=None, out=sys.stdout):
         ms, tf = _time(lambda: g.sgemm_ws(*args, workspace=ws, workspace_bytes=ws_bytes,
                                           stream=stream), flops, stream)
         rows["auto+ws"] = (ms, tf)
-        splits = g.sgemm_select_splits(p.M, p.N, p.K)
+        _, ws_variant, splits, workers = g.sgemm_ws_plan(p.M, p.N, p.K)
         for name, (ms, tf) in rows.items():
             print(f"{shape:24s} {name:34s} {tf:8.2f} TFLOP/s {ms:10.4f} ms", file=out, flush=True)
         forced = {k: v for k, v in rows.items() if k not in ("auto", "auto+ws")}
         best = min(forced, key=lambda k: forced[k][0])
         table.append({"shape": shape, "M": p.M, "N": p.N, "K": p.K,
-                      "selected": g.sgemm_variant_name(auto), "splits": splits,
+                      "selected": g.sgemm_variant_name(auto), "selected_ws": g.sgemm_variant_name(ws_variant),
+                      "splits": splits, "workers": workers,
                       "auto_ms": rows["auto"][0], "auto_ws_ms": rows["auto+ws"][0],
                       "best": best, "best_ms": forced[best][0],
-                      "auto_ws_tflops": rows["auto+ws"][1]})
+                      "auto_ws_tflops": rows["auto+ws"][1], "auto_tflops": rows["auto"][1]})
         del a, b, c, ws, p
         torch.cuda.empty_cache()
-    print("\n| shape | selected (splits) | auto+ws TFLOP/s | best forced variant | best / auto+ws time |",
-          file=out)
-    print("|---|---|---|---|---|", file=out)
+    print("\n| shape | selected (`sgemm`) | with workspace (`sgemm_ws`: splits, stream-K workers) | "
+          "auto TFLOP/s | auto+ws TFLOP/s | best forced variant | best / auto+ws time |", file=out)
+    print("|---|---|---|---|---|---|---|", file=out)
     for r in table:
-        print(f"| {r['shape']} | {r['selected']} ({r['splits']}) | {r['auto_ws_tflops']:.2f} | "
+        print(f"| {r['shape']} | {r['selected']} | {r['selected_ws']} ({r['splits']}, {r['workers']}) | "
+              f"{r['auto_tflops']:.2f} | {r['auto_ws_tflops']:.2f} | "
               f"{r['best']} | {r['best_ms'] / r['auto_ws_ms']:.3f} |", file=out)
     print(json.dumps(table), file=out, flush=True)
     return table

@@ -46,9 +46,9 @@
  * alpha != 0, -8 ldb < max(1, N), -10 C == NULL while M*N > 0, -11
  * ldc < max(1, N)); -20 unknown path; -21 unknown variant; -22 the tile grid
  * does not fit one launch; -23 an unknown access mode, or one these arguments
- * do not allow; -24 a split-K workspace that is missing, too small or not
- * 256-byte aligned; -25 a split count outside 1..64 or a variant without a
- * split-K build.  Argument checks run before any HIP call, so they
+ * do not allow; -24 a split-K or stream-K workspace that is missing, too
+ * small or not 256-byte aligned; -25 a split count outside 1..64, a worker
+ * count outside 1..4096, or a variant without a split-K (stream-K) build.  Argument checks run before any HIP call, so they
  * need no GPU.  Positive: the hipError_t reported for the launch.  The library
  * never exits or aborts the process.
  */
@@ -131,9 +131,9 @@ int sgemm_variant_access(int variant, int access, int M, int N, int K,
  * workspace must not overlap in time (same stream, or synchronised).  The
  * library allocates nothing. */
 
-/* C = alpha*A*B + beta*C like sgemm(), using split-K when the auto choice
- * calls for it and `workspace_bytes` holds sgemm_workspace_size(M, N, K);
- * otherwise exactly sgemm(). */
+/* C = alpha*A*B + beta*C like sgemm(), using split-K or stream-K (below)
+ * when the auto choice calls for it and `workspace_bytes` holds
+ * sgemm_workspace_size(M, N, K); otherwise exactly sgemm(). */
 int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda,
              const float *B, int ldb, float beta, float *C, int ldc,
              void *workspace, size_t workspace_bytes, hipStream_t stream);
@@ -145,6 +145,16 @@ size_t sgemm_workspace_size(int M, int N, int K);
  * negative argument code.  Host logic only. */
 int sgemm_select_splits(int M, int N, int K);
 
+/* The stream-K worker count sgemm_ws() uses with enough workspace (0: no
+ * stream-K), or a negative argument code.  Host logic only. */
+int sgemm_select_streamk(int M, int N, int K);
+
+/* What sgemm_ws() runs with enough workspace: the variant, the split count
+ * (1: none) and the stream-K worker count (0: none), through the pointers
+ * (each may be NULL).  Returns 0 or a negative argument code (-1..-3).
+ * Host logic only. */
+int sgemm_ws_plan(int M, int N, int K, int *variant, int *splits, int *workers);
+
 /* One variant with a forced split count (1 = no split, same as
  * sgemm_variant()).  SGEMM_ERR_SPLITS for a variant without a split-K build. */
 int sgemm_splitk(int variant, int splits, int M, int N, int K, float alpha,
@@ -155,6 +165,36 @@ int sgemm_splitk(int variant, int splits, int M, int N, int K, float alpha,
 /* Workspace bytes sgemm_splitk(variant, splits, M, N, ...) needs (0 for
  * splits == 1, an empty C, or invalid arguments). */
 size_t sgemm_splitk_workspace_size(int variant, int splits, int M, int N);
+
+/* ---- stream-K (for shapes whose last round of tiles leaves slots idle) ---
+ * With T tiles and W workers, the first T - (T mod W) tiles (whole rounds)
+ * are computed whole, and the K tiles of the remaining R = T mod W tiles,
+ * R * ceil(K / BK) in all, are shared by the W workers in equal contiguous
+ * ranges: worker w takes [w I / W, (w + 1) I / W) with I = R ceil(K / BK),
+ * in tile order.  A range is shorter than one tile, so a worker holds at
+ * most the end of one tile and the start of the next; it writes each as a
+ * partial tile to the workspace, or, when it holds a whole tile, C itself.
+ * A second launch on the same stream sums each shared tile's partials in
+ * worker order and applies alpha and beta, so results are deterministic run
+ * to run.  No atomics, flags or waits between workgroups.  R = 0 (whole
+ * rounds) is an ordinary launch.
+ *
+ * Workspace: caller-owned device memory, 256-byte aligned, at least
+ * sgemm_streamk_workspace_size() bytes, any contents; the same sharing rule
+ * as split-K. */
+
+/* One variant with stream-K over `workers` workers (1 .. 4096; one per
+ * workgroup slot of the chip fills it evenly).  SGEMM_ERR_SPLITS for a
+ * worker count out of range or a variant without stream-K. */
+int sgemm_streamk(int variant, int workers, int M, int N, int K, float alpha,
+                  const float *A, int lda, const float *B, int ldb, float beta,
+                  float *C, int ldc, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/* Workspace bytes sgemm_streamk(variant, workers, ...) needs (0 for a
+ * variant without stream-K or a worker count out of range): two partial
+ * tiles per worker. */
+size_t sgemm_streamk_workspace_size(int variant, int workers);
 
 /* Number of compiled kernel variants. */
 int sgemm_variant_count(void);

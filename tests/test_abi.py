@@ -187,6 +187,51 @@ def test_large_shapes_pick_the_block_whose_last_round_is_fullest():
     assert block(1000, 1023, 999) == (64, 64, 32)
 
 
+def test_streamk_host_logic():
+    sk = [v for v in range(g.sgemm_variant_count()) if g.variant_has_streamk(v)]
+    assert sk and all(g.variant_has_splitk(v) for v in sk)
+    v = sk[0]
+    _, bm, bn = g.sgemm_variant_tile(v)
+    assert g.sgemm_streamk_workspace_size(v, 256) == 256 * 2 * bm * bn * 4
+    assert g.sgemm_streamk_workspace_size(v, 0) == 0
+    assert g.sgemm_streamk_workspace_size(v, 4097) == 0
+    assert all(g.sgemm_streamk_workspace_size(w, 256) == 0
+               for w in range(g.sgemm_variant_count()) if w not in sk)
+    # sgemm_ws shares K tiles where the last round of tiles leaves slots idle
+    for M, N, K in [(5120, 5120, 5120), (7168, 7168, 7168), (3072, 3072, 3072)]:
+        w = g.sgemm_select_streamk(M, N, K)
+        assert w > 0 and w % 256 == 0, (M, N, K, w)
+        assert g.sgemm_select_splits(M, N, K) == 1
+        assert g.sgemm_workspace_size(M, N, K) > 0
+    # whole rounds, short K and small shapes do not
+    for M, N, K in [(8192, 8192, 8192), (4096, 4096, 4096), (16384, 16384, 128), (1024, 1024, 1024),
+                    (512, 512, 8192)]:
+        assert g.sgemm_select_streamk(M, N, K) == 0, (M, N, K)
+    assert g.sgemm_select_streamk(-1, 4, 4) == -1
+    # the plan agrees with the single-number queries
+    for M, N, K in [(5120, 5120, 5120), (8192, 8192, 8192), (512, 512, 8192), (1000, 1023, 999)]:
+        rc, pv, psp, pw = g.sgemm_ws_plan(M, N, K)
+        assert rc == 0 and 0 <= pv < g.sgemm_variant_count()
+        assert psp == g.sgemm_select_splits(M, N, K) and pw == g.sgemm_select_streamk(M, N, K)
+        assert not (psp > 1 and pw > 0)
+        if pw == 0 and psp == 1:
+            assert pv == g.sgemm_select_variant(g.SGEMM_PATH_AUTO, M, N, K)
+    assert g.sgemm_ws_plan(4, -1, 4)[0] == -2
+
+    def call(variant, workers, ws=0x10000, nbytes=1 << 30):
+        # fake addresses: every call here must stop at a check before any launch
+        return g.sgemm_streamk(variant, workers, 300, 260, 1030, 1.0, 0x1000, 1032, 0x2000, 260,
+                               0.0, 0x3000, 260, workspace=ws, workspace_bytes=nbytes, stream=0,
+                               check=False)
+    assert call(v, 0) == -25
+    assert call(v, 4097) == -25
+    non_sk = [w for w in range(g.sgemm_variant_count()) if w not in sk][0]
+    assert call(non_sk, 3) == -25
+    assert call(v, 3, ws=0) == -24                      # missing workspace
+    assert call(v, 3, nbytes=16) == -24                 # too small
+    assert call(v, 3, ws=0x10010) == -24                # not 256-byte aligned
+
+
 def test_only_the_latency_block_splits_k():
     """A block chosen by rate already has a tile per workgroup slot on the
     chip; only the 64 x 64 fallback splits K when a workspace is given."""

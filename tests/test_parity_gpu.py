@@ -445,6 +445,88 @@ def test_splitk_closed_form_exact(variant):
         assert np.all(out == 2000.0), splits
 
 
+# ------------------------------------------------------------------ stream-K
+def streamk_variants():
+    return [v for v in all_variants() if g.variant_has_streamk(v)]
+
+
+def run_streamk(p, variant, workers, ws=None):
+    """One stream-K launch; returns (C, workspace tensor)."""
+    need = g.sgemm_streamk_workspace_size(variant, workers)
+    assert need > 0
+    if ws is None:  # any contents: fill with NaN to show none of it leaks through
+        ws = torch.full((need // 4 + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    oa, _, a = gu.to_gpu(p.A)
+    ob, _, b = gu.to_gpu(p.B)
+    oc, first, c = gu.to_gpu(p.C)
+    g.sgemm_streamk(variant, workers, p.M, p.N, p.K, p.alpha, a, p.lda, b, p.ldb, p.beta, c, p.ldc,
+                    workspace=ws)
+    torch.cuda.synchronize()
+    host = oc.cpu().numpy()
+    n = p.C.numel()
+    guard = np.concatenate([host[:first], host[first + n:]])
+    assert np.all(np.isnan(guard)), "write outside C's extent"
+    return host[first:first + n].reshape(p.C.shape), ws
+
+
+# Shapes whose tile counts leave a remainder for the worker counts below
+# (from 2 tiles of 256 x 256 to 20 of 64 x 64, so the shared tiles range from
+# all of them to a few), with K from 2 K tiles (most workers hold nothing) to
+# 65 (each shared tile spread over several workers).
+STREAMK_SHAPES = [(200, 301, 777, 1.5, -0.5), (300, 260, 1030, -1.0, 1.0), (520, 130, 96, 2.0, 0.5),
+                  (64, 64, 40, 1.0, 0.0)]
+
+
+@pytest.mark.parametrize("variant", streamk_variants())
+@pytest.mark.parametrize("workers", [3, 5, 16, 256])
+def test_streamk_matches_oracle(variant, workers):
+    for (M, N, K, alpha, beta) in STREAMK_SHAPES:
+        p = inputs.make_problem(M, N, K, dist="upm1", seed=M + K + 1, alpha=alpha, beta=beta,
+                                c_fill="upm1" if beta != 0 else None)
+        gu.say("stream-K", M, N, K, workers, g.sgemm_variant_name(variant))
+        out, _ = run_streamk(p, variant, workers)
+        assert gu.ratio_full(p, out) <= TOL, (M, N, K, workers)
+
+
+@pytest.mark.parametrize("variant", streamk_variants())
+def test_streamk_deterministic_reusable_and_exact(variant):
+    p = cached_problem("ragged_1000x1023x999")
+    gu.say("stream-K determinism", g.sgemm_variant_name(variant))
+    out1, ws = run_streamk(p, variant, 7)
+    out2, ws = run_streamk(p, variant, 7, ws)   # same workspace again
+    assert np.array_equal(out1.view(np.uint32), out2.view(np.uint32))
+    assert gu.ratio_full(p, out1, cached_oracle("ragged_1000x1023x999")) <= TOL
+    q = inputs.make_problem(192, 128, 1000, dist="ones_twos")
+    for workers in (3, 7):
+        out, _ = run_streamk(q, variant, workers)
+        assert np.all(out == 2000.0), workers
+
+
+@pytest.mark.parametrize("name", ["5120x5120x5120", "3072x3072x3072"])
+def test_sgemm_ws_streamk_full_size_sampled(name):
+    """Shapes whose last round of tiles leaves slots idle: sgemm_ws shares
+    the K tiles of the rest over one worker per slot (checked on sampled
+    points against the oracle), and with no workspace falls back to whole
+    tiles."""
+    M, N, K = (int(x) for x in name.split("x"))
+    p = inputs.make_problem(M, N, K, dist="normal", seed=37, alpha=0.75, beta=0.5, c_fill="upm1")
+    workers = g.sgemm_select_streamk(M, N, K)
+    assert workers > 0
+    need = g.sgemm_workspace_size(M, N, K)
+    ws = torch.full((need // 4 + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    rows, cols = inputs.sample_points(M, N, n_random=2048, seed=41)
+    for workspace in (ws, None):
+        oa, _, a = gu.to_gpu(p.A)
+        ob, _, b = gu.to_gpu(p.B)
+        oc, first, c = gu.to_gpu(p.C)
+        gu.say("sgemm_ws stream-K", name, "workers", workers, "workspace", workspace is not None)
+        g.sgemm_ws(M, N, K, p.alpha, a, p.lda, b, p.ldb, p.beta, c, p.ldc, workspace=workspace)
+        torch.cuda.synchronize()
+        out = oc.cpu().numpy()[first:first + p.C.numel()].reshape(p.C.shape)
+        assert gu.ratio_points(p, out, rows, cols) <= TOL, workspace is not None
+        del oa, ob, oc
+
+
 @pytest.mark.parametrize("name", ["square256_u01", "ragged_1000x1023x999", "512x512x8192",
                                   "1024x1024x4096"])
 def test_sgemm_ws_auto(name):
