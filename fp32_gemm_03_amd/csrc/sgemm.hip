@@ -250,7 +250,7 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
     };
     static const Candidate cand[] = {{kKcHuge, 146.5, 1, 512},  {kKcLarge4, 146.0, 4, 256},
                                      {kKcShortK, 144.0, 2, 0},  {kKcWide, 142.0, 1, 512},
-                                     {kIlMid, 140.5, 2, 256},   {kIlDeep, 137.0, 1, 512},
+                                     {kIlMid, 140.5, 2, 256},   {kIlDeep, 137.0, 1, 1024},
                                      {kKcSmall4, 130.0, 4, 0}};
     int best = -1, best_workers = 0;
     double best_score = -1.0;
@@ -273,7 +273,18 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
             best_workers = w;
         }
     }
-    if (best < 0) return kKcSmall4;
+    if (best < 0) {
+        // No block fills the chip: 64 x 64 blocks.  With more tiles than
+        // CUs but not a whole number per CU, stream-K over one worker per CU
+        // evens out the K tiles each CU runs (1536^3: 107.5 TFLOP/s against
+        // 95.4); with at most one tile per CU, select_splits may split K.
+        const Variant &v = kVariants[kKcSmall4];
+        const long long t = tiles(M, N, v.bm, v.bn), rest = t % kComputeUnits;
+        const long long kt = (K + v.bk - 1) / v.bk;
+        if (streamk && workers && t > kComputeUnits && rest > 0 && rest * kt >= kStreamKMinK * kComputeUnits)
+            *workers = (int)kComputeUnits;
+        return kKcSmall4;
+    }
     if (workers) *workers = best_workers;
     return best;
 }
@@ -281,13 +292,14 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
 int select_variant(int path, int M, int N, int K) { return choose(path, M, N, K, false, nullptr); }
 
 // Split count for a variant when a workspace is available (measured on
-// MI355X: 512 x 512 x 8192 runs 3.5x faster in 8 parts, 1024 x 1024 x 4096
-// about 10% faster in 2, while 1024^3 and smaller lose): split only when the
-// tiles alone leave CUs idle, into enough parts for about two workgroups per
-// CU, keeping at least 1024 of K per part so the per-workgroup prologue and
-// the extra pass over the partials stay small.  Only the latency block
-// splits: the blocks chosen by rate have a tile for every one of their
-// workgroup slots on the chip already.
+// MI355X: 512 x 512 x 8192 runs 3.5x faster in 8 parts, 768^3 13% faster in
+// 3, 1024 x 1024 x 4096 about 10% faster in 2, while 1024^3 loses): split
+// only when the tiles alone leave CUs idle, into enough parts for about two
+// workgroups per CU, keeping at least 256 of K per part (1024 when there is
+// already a tile for every CU) so the per-workgroup prologue and the extra
+// pass over the partials stay small.  Only the latency block splits: the
+// blocks chosen by rate have a tile for every one of their workgroup slots
+// on the chip already.
 int select_splits(int variant, int M, int N, int K) {
     if (M <= 0 || N <= 0 || K <= 0 || variant != kKcSmall4) return 1;
     const Variant &v = kVariants[variant];
@@ -295,7 +307,8 @@ int select_splits(int variant, int M, int N, int K) {
     const long long t = tiles(M, N, v.bm, v.bn);
     if (t > kComputeUnits) return 1;
     long long s = 2 * kComputeUnits / t;
-    if (s > K / 1024) s = K / 1024;
+    const long long k_min = t < kComputeUnits ? 256 : 1024;
+    if (s > K / k_min) s = K / k_min;
     if (s > kMaxSplits) s = kMaxSplits;
     return s < 2 ? 1 : (int)s;
 }

@@ -203,9 +203,12 @@ def test_streamk_host_logic():
         assert w > 0 and w % 256 == 0, (M, N, K, w)
         assert g.sgemm_select_splits(M, N, K) == 1
         assert g.sgemm_workspace_size(M, N, K) > 0
-    # whole rounds, short K and small shapes do not
+    # below the blocks that fill the chip: one worker per CU evens out the K
+    # tiles per CU when the 64 x 64 tiles do not divide evenly over the CUs
+    assert g.sgemm_select_streamk(1536, 1536, 1536) == 256
+    # whole rounds, short K, one tile per CU and small shapes do not
     for M, N, K in [(8192, 8192, 8192), (4096, 4096, 4096), (16384, 16384, 128), (1024, 1024, 1024),
-                    (512, 512, 8192)]:
+                    (512, 512, 8192), (768, 768, 768)]:
         assert g.sgemm_select_streamk(M, N, K) == 0, (M, N, K)
     assert g.sgemm_select_streamk(-1, 4, 4) == -1
     # the plan agrees with the single-number queries
@@ -284,6 +287,8 @@ def test_splitk_host_logic():
     assert g.sgemm_select_splits(1024, 1024, 4096) == 2
     assert g.sgemm_select_splits(1024, 1024, 1024) == 1
     assert g.sgemm_select_splits(256, 256, 256) == 1
+    # fewer tiles than CUs: parts may be as short as 256 of K
+    assert g.sgemm_select_splits(768, 768, 768) == 3
     assert g.sgemm_select_splits(-1, 4, 4) == -1
 
 
