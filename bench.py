@@ -61,12 +61,18 @@ def _code_tokens(text: str) -> str:
 
 
 def kernel_source_hash() -> str:
-    """Hash of the code (not the comments) the library is built from."""
+    """Hash of the code (not the comments) the kernels are built from: the
+    kernel templates and the variant table that instantiates them.  Host
+    logic (argument checks, the shape-to-variant choice, the launch) is left
+    out, so changing it does not void a stored kernel measurement."""
     from fp32_gemm_03_amd import build as b
     h = hashlib.sha256()
-    for p in sorted(b.DEPENDS):
-        with open(p, encoding="utf-8") as f:
-            h.update(_code_tokens(f.read()).encode())
+    with open(os.path.join(b.CSRC, "sgemm_kernels.hpp"), encoding="utf-8") as f:
+        h.update(_code_tokens(f.read()).encode())
+    with open(os.path.join(b.CSRC, "sgemm.hip"), encoding="utf-8") as f:
+        text = f.read()
+    i, j = text.find("#define VALU_CFG"), text.find("constexpr int kNumVariants")
+    h.update(_code_tokens(text[i:j] if 0 <= i < j else text).encode())
     return h.hexdigest()[:16]
 
 
