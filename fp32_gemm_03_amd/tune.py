@@ -6,10 +6,10 @@ shape's fastest variant with the one the library's selection picks.
 A shape is a named synthetic workload (``square8192_normal`` ...) or MxNxK
 (A, B ~ N(0,1), seed 3, alpha 1, beta 0).  Every launch goes through the C
 ABI on one stream; the time per launch is HIP events around a run of
-launches.  Besides the forced variants, two rows time the library's own
-choice: ``auto`` (``sgemm``) and ``auto+ws`` (``sgemm_ws`` with the workspace
-it asks for, which may split K or share the K tiles of a last partial round
-of tiles over stream-K workers).  The last block is a table of the selection
+launches after about 30 ms of untimed ones.  Besides the forced variants,
+two rows time the library's own choice: ``auto`` (``sgemm``) and ``auto+ws``
+(``sgemm_ws`` with the workspace it asks for, which may split K or share the
+K tiles of a last partial round of tiles over stream-K workers).  The last block is a table of the selection
 against the best variant per shape: the measurement the selection table in
 ``sgemm.hip`` was fitted to, repeatable on any MI355X.
 """
@@ -35,12 +35,20 @@ def _problem(shape):
     return inputs.make_problem(M, N, K, dist="normal", seed=3, name=shape)
 
 
-def _time(launch, flops, stream, target_s=0.1, warmup=3):
+def _time(launch, flops, stream, target_s=0.1, warmup_s=0.03):
+    """Mean ms per launch and TFLOP/s over about target_s of launches, after
+    about warmup_s of untimed ones (a fixed time rather than a count, so that
+    the clock has settled whatever the launch length)."""
     import torch
-    for _ in range(warmup):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    launch()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    est_ms = max(e0.elapsed_time(e1), 1e-3)
+    for _ in range(int(min(2000, max(3, warmup_s * 1e3 / est_ms)))):
         launch()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     launch()
     e1.record(stream)
