@@ -1059,103 +1059,17 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
 // A tile kept in K order: As[BM][BK], each row one row of A.  Its BK / 4
 // 16-byte chunks are permuted per row: chunk c of row m sits at chunk
 // c ^ g(m), g(m) = (m / RP) % CPR, where CPR = BK / 4 chunks fill a row and
-// RP = 16 / CPR rows fill the 256 bytes that span the 64 banks.  A store
-// instruction writes CPR chunks of each of 16 / CPR consecutive rows (one
-// 16-lane phase), and a fragment read takes one chunk of each of 16
-// consecutive rows; both then touch 16 different 16-byte bank groups.
+// RP = 16 / CPR rows fill the 256 bytes that span the 64 banks.  A load
+// instruction fills 64 consecutive chunks (16 / CPR whole rows per 16-lane
+// phase), and a fragment read takes one chunk of each of 16 consecutive
+// rows; both then touch 16 different 16-byte bank groups.
 // ---------------------------------------------------------------------------
-template <int BM, int BK, int NT, int STAGES>
-struct AKGeom {
+template <int BK>
+struct AKLayout {
     static_assert(BK == 16 || BK == 32 || BK == 64, "K-ordered A tile: BK in {16, 32, 64}");
     static constexpr int CPR = BK / 4;
     static constexpr int RP = 16 / CPR;
-    static_assert(NT % CPR == 0, "threads must cover whole rows");
-    static constexpr int ROWS_PER_PASS = NT / CPR;
-    static_assert(BM % ROWS_PER_PASS == 0, "A tile must divide evenly over the threads");
-    static_assert((ROWS_PER_PASS / RP) % CPR == 0, "a thread's chunk position must not change between passes");
-    static constexpr int PER = BM / ROWS_PER_PASS;
-
-    float4 reg[STAGES][PER];  // register stages: K tiles in flight
-
     static __device__ __forceinline__ int chunk_pos(int m, int c) { return c ^ ((m / RP) % CPR); }
-
-    template <int S>
-    __device__ __forceinline__ void store(float *As, int tid) const {
-#pragma unroll
-        for (int p = 0; p < PER; ++p) store_piece<S>(As, tid, p);
-    }
-
-    // one 128-bit LDS store: chunk tid % CPR of row tid / CPR + p ROWS_PER_PASS
-    template <int S>
-    __device__ __forceinline__ void store_piece(float *As, int tid, int p) const {
-        const int m = tid / CPR + p * ROWS_PER_PASS;
-        *reinterpret_cast<float4 *>(As + m * BK + 4 * chunk_pos(m, tid % CPR)) = reg[S][p];
-    }
-};
-
-// Buffer loads of the K-ordered A tile: one 128-bit load per chunk (VEC 4:
-// K, lda multiples of 4 and A 16-byte aligned, so a chunk is wholly inside or
-// wholly past K), else four 32-bit loads.  Columns >= K and rows >= M read 0.0.
-template <int BM, int BK, int NT, int STAGES, int VEC>
-struct AKBuf : AKGeom<BM, BK, NT, STAGES> {
-    typedef AKGeom<BM, BK, NT, STAGES> G;
-    rsrc_t rsrc;
-    uint32_t off, pass;
-    int c4;
-
-    __device__ __forceinline__ void init(const Args &a, int bm, int tid) {
-        c4 = 4 * (tid % G::CPR);
-        off = (uint32_t)(((int64_t)(tid / G::CPR) * a.lda + c4) * 4);
-        pass = (uint32_t)(G::ROWS_PER_PASS * a.lda * 4);
-        rsrc = make_rsrc(a.A + (int64_t)bm * a.lda, ((int64_t)(a.M - bm - 1) * a.lda + a.K) * 4);
-    }
-
-    template <int S>
-    __device__ __forceinline__ void load(const Args &a, int bm, int k0) {
-#pragma unroll
-        for (int p = 0; p < G::PER; ++p) load_piece<S>(a, bm, k0, p);
-    }
-
-    template <int S>
-    __device__ __forceinline__ void load_piece(const Args &a, int, int k0, int p) {
-        const uint32_t o = off + 4u * (uint32_t)k0 + p * pass;
-        if (VEC == 4) {
-            G::reg[S][p] = buf<4>::load(rsrc, k0 + c4 < a.K ? o : kOutOfRange);
-        } else {
-            G::reg[S][p].x = buf<1>::load(rsrc, k0 + c4 < a.K ? o : kOutOfRange);
-            G::reg[S][p].y = buf<1>::load(rsrc, k0 + c4 + 1 < a.K ? o + 4 : kOutOfRange);
-            G::reg[S][p].z = buf<1>::load(rsrc, k0 + c4 + 2 < a.K ? o + 8 : kOutOfRange);
-            G::reg[S][p].w = buf<1>::load(rsrc, k0 + c4 + 3 < a.K ? o + 12 : kOutOfRange);
-        }
-    }
-};
-
-template <int BM, int BK, int NT, int STAGES>
-struct AKPtr : AKGeom<BM, BK, NT, STAGES> {
-    typedef AKGeom<BM, BK, NT, STAGES> G;
-    int c4, r0;
-
-    __device__ __forceinline__ void init(const Args &, int, int tid) {
-        c4 = 4 * (tid % G::CPR);
-        r0 = tid / G::CPR;
-    }
-
-    template <int S>
-    __device__ __forceinline__ void load(const Args &a, int bm, int k0) {
-#pragma unroll
-        for (int p = 0; p < G::PER; ++p) load_piece<S>(a, bm, k0, p);
-    }
-
-    template <int S>
-    __device__ __forceinline__ void load_piece(const Args &a, int bm, int k0, int p) {
-        const int row = bm + r0 + p * G::ROWS_PER_PASS, k = k0 + c4;
-        const float *q = a.A + (int64_t)row * a.lda + k;
-        const bool rin = row < a.M;
-        G::reg[S][p].x = (rin && k < a.K) ? q[0] : 0.0f;
-        G::reg[S][p].y = (rin && k + 1 < a.K) ? q[1] : 0.0f;
-        G::reg[S][p].z = (rin && k + 2 < a.K) ? q[2] : 0.0f;
-        G::reg[S][p].w = (rin && k + 3 < a.K) ? q[3] : 0.0f;
-    }
 };
 
 // Buffer loads that write LDS directly: lane l's W floats land at
@@ -1175,13 +1089,12 @@ __device__ __forceinline__ void load_to_lds(rsrc_t r, float *lds, uint32_t voff)
 // filled by loads that write LDS directly.  Instruction p of wave w fills
 // floats (p * WAVES + w) * 64 W .. + 64 W of each tile, so each lane's
 // global address is the one whose data belongs at its LDS position (for A
-// through the chunk permutation of AKGeom).  Columns of A >= K and rows of
+// through the chunk permutation of AKLayout).  Columns of A >= K and rows of
 // B >= K read 0.0 (so do rows of A >= M); columns of B >= N read whatever
 // lies there, which only reaches columns of C that are never stored.
 template <int BM, int BN, int BK, int NT, int W>
 struct DirectStage {
     static constexpr int WAVES = NT / 64;
-    static constexpr int CPR = BK / 4, RP = 16 / CPR;
     static constexpr int PER_INST = 64 * W;
     static_assert((BM * BK) % (NT * W) == 0 && (BK * BN) % (NT * W) == 0, "tiles must split into whole instructions");
     static constexpr int PA = BM * BK / (NT * W), PB = BK * BN / (NT * W);
@@ -1198,7 +1111,7 @@ struct DirectStage {
         for (int p = 0; p < PA; ++p) {
             const int f = (p * WAVES + wave) * PER_INST + lane * W;
             const int row = f / BK, pos = f % BK;
-            const int col = 4 * ((pos / 4) ^ ((row / RP) % CPR)) + pos % 4;
+            const int col = 4 * AKLayout<BK>::chunk_pos(row, pos / 4) + pos % 4;
             aoff[p] = (uint32_t)(((int64_t)row * a.lda + col) * 4);
             acol[p] = col;
         }
@@ -1299,29 +1212,25 @@ __device__ __forceinline__ void epilogue_mfma_kc(const Args &a, int bm, int bn, 
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel with A kept in K order in LDS and read from global memory along
-// K (128-bit loads when VEC == 4).  The next K tile's loads are issued in
-// pieces after the MFMAs of the first quarter of the k-steps: with DL they
-// write the other LDS stage directly, else they land in registers and are
-// stored to it in pieces over the second half.  Same tiles, split-K and
-// epilogue contract as sgemm_mfma.
+// MFMA kernel with A kept in K order in LDS, both tiles loaded from global
+// memory straight into LDS (16 bytes per lane when VEC == 4, else 4): the
+// next K tile's loads go after the MFMAs of the first quarter of the k-steps,
+// into the other LDS stage.  Same tiles and epilogue contract as sgemm_mfma;
+// the SPLIT build also runs split-K and stream-K (phases 0-3 of Args).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, int PADB, int VEC, int WPE, bool BUF, bool SPLIT,
-          bool DL = false>
+template <int BM, int BN, int BK, int WM, int WN, int VEC, int WPE, bool SPLIT>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
     constexpr int WAVES_N = BN / WN;
     constexpr int NT = (BM / WM) * WAVES_N * 64;
-    constexpr int SB = BN + PADB;
+    constexpr int SB = BN;
     constexpr int ASZ = BM * BK;
     constexpr int STAGE = ASZ + BK * SB;
     static_assert(MI == 1 || MI == 2 || MI == 4, "MI in {1, 2, 4}");
     static_assert(NI == 1 || NI == 2 || NI == 4, "NI in {1, 2, 4}");
-    typedef typename std::conditional<BUF, AKBuf<BM, BK, NT, 1, VEC>, AKPtr<BM, BK, NT, 1>>::type TA;
-    typedef typename std::conditional<BUF, BTileBuf<BN, BK, NT, PADB, VEC, 1>,
-                                      BTilePtr<BN, BK, NT, PADB, VEC, 1>>::type TB;
-    typedef typename std::conditional<BUF, CStoreBuf<NI, VEC>, CStorePtr<NI, VEC>>::type TC;
+    typedef DirectStage<BM, BN, BK, NT, VEC> D;
+    typedef CStoreBuf<NI, VEC> TC;
     __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
     const int tid = threadIdx.x;
@@ -1340,12 +1249,11 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     const int a_row = (wm + li) * BK;
     int a_off[QN];
 #pragma unroll
-    for (int q = 0; q < QN; ++q) a_off[q] = 4 * TA::chunk_pos(wm + li, lh * QN + q);
+    for (int q = 0; q < QN; ++q) a_off[q] = 4 * AKLayout<BK>::chunk_pos(wm + li, lh * QN + q);
     const int b_off = ASZ + lh * (BK / 2) * SB + wn + NI * li;
 
     constexpr int STEPS = BK / 2;
     constexpr int LSTEPS = STEPS / 4 > 0 ? STEPS / 4 : 1;
-    constexpr int SSTEPS = STEPS / 2 > 0 ? STEPS / 2 : 1;
     constexpr int NU = MI * NI;
 
     // acc = the product of the tile at (bm, bn) over K tiles [k_lo, k_hi).
@@ -1359,99 +1267,46 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = acc_odd[i][j][r] = 0.0f;
         const int KT = k_hi - k_lo, kb = k_lo * BK;
-        if constexpr (DL) {
-            // Loads that write LDS directly: the next K tile goes straight
-            // into the other stage (last read before the previous barrier)
-            // in pieces after the MFMAs of the first k-steps; a wave waits
-            // for its own loads before the barrier that hands the stage to
-            // every wave.
-            static_assert(BUF && PADB == 0, "direct LDS loads: buffer accesses, unpadded B");
-            typedef DirectStage<BM, BN, BK, NT, VEC> D;
-            constexpr int DP = D::PA + D::PB;
-            // the loads go after the MFMAs of the first quarter of the
-            // k-steps (spreading them over a half or three quarters measured
-            // the same)
-            constexpr int DLPER = (DP + LSTEPS - 1) / LSTEPS;
-            D d;
-            d.init(a, bm, tid);
-            if (KT > 0) {
-                const rsrc_t rb = d.b_rows(a, bn, kb);
+        // The next K tile goes straight into the other stage (last read
+        // before the previous barrier) in pieces after the MFMAs of the first
+        // quarter of the k-steps (spreading them over a half or three
+        // quarters measured the same); a wave waits for its own loads before
+        // the barrier that hands the stage to every wave.
+        constexpr int DP = D::PA + D::PB;
+        constexpr int DLPER = (DP + LSTEPS - 1) / LSTEPS;
+        D d;
+        d.init(a, bm, tid);
+        if (KT > 0) {
+            const rsrc_t rb = d.b_rows(a, bn, kb);
 #pragma unroll
-                for (int p = 0; p < D::PA; ++p) d.load_a(a, smem, kb, p);
+            for (int p = 0; p < D::PA; ++p) d.load_a(a, smem, kb, p);
 #pragma unroll
-                for (int p = 0; p < D::PB; ++p) d.load_b(rb, smem + ASZ, p);
-            }
-            __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have written LDS
-            __syncthreads();
-            // The two stages as restrict pointers: the scoped no-alias
-            // information lets the compiler see that the reads of the current
-            // stage need not wait for the loads into the other one.
-            auto tile_body = [&](const float *__restrict__ st, float *__restrict__ nx, int kn) {
-                const rsrc_t rb = d.b_rows(a, bn, kn);
-                auto hook = [&](int j, int u) {
-                    if (j < LSTEPS) {
+            for (int p = 0; p < D::PB; ++p) d.load_b(rb, smem + ASZ, p);
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have written LDS
+        __syncthreads();
+        // The two stages as restrict pointers: the scoped no-alias
+        // information lets the compiler see that the reads of the current
+        // stage need not wait for the loads into the other one.
+        auto tile_body = [&](const float *__restrict__ st, float *__restrict__ nx, int kn) {
+            const rsrc_t rb = d.b_rows(a, bn, kn);
+            auto hook = [&](int j, int u) {
+                if (j < LSTEPS) {
 #pragma unroll
-                        for (int q = 0; q < DLPER; ++q) {
-                            const int piece = j * DLPER + q;
-                            if ((q * NU) / DLPER != u || piece >= DP) continue;
-                            if (piece < D::PA) d.load_a(a, nx, kn, piece);
-                            else d.load_b(rb, nx + ASZ, piece - D::PA);
-                        }
+                    for (int q = 0; q < DLPER; ++q) {
+                        const int piece = j * DLPER + q;
+                        if ((q * NU) / DLPER != u || piece >= DP) continue;
+                        if (piece < D::PA) d.load_a(a, nx, kn, piece);
+                        else d.load_b(rb, nx + ASZ, piece - D::PA);
                     }
-                };
-                mfma_tile_kc<BK, MI, NI, SB, 1, CH>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
+                }
             };
-            for (int t = 0; t < KT; ++t) {
-                tile_body(smem + (t & 1) * STAGE, smem + ((t + 1) & 1) * STAGE, kb + (t + 1) * BK);
-                __builtin_amdgcn_s_waitcnt(0);
-                __syncthreads();
-            }
-        } else {
-            // through registers (the checked build): loads in pieces over
-            // the first quarter of the k-steps, LDS stores over the second half
-            constexpr int PA = TA::PER, PB = TB::PER, NP = PA + PB;
-            constexpr int LPER = (NP + LSTEPS - 1) / LSTEPS, SPER = (NP + SSTEPS - 1) / SSTEPS;
-            TA ta;
-            TB tb;
-            ta.init(a, bm, tid);
-            tb.init(a, bn, tid);
-            if (KT > 0) {
-                ta.template load<0>(a, bm, kb);
-                tb.template load<0>(a, bn, kb);
-                ta.template store<0>(smem, tid);
-                tb.template store<0>(smem + ASZ, tid);
-            }
+            mfma_tile_kc<BK, MI, NI, SB, 1, CH>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
+        };
+        for (int t = 0; t < KT; ++t) {
+            tile_body(smem + (t & 1) * STAGE, smem + ((t + 1) & 1) * STAGE, kb + (t + 1) * BK);
+            __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
-            for (int t = 0; t < KT; ++t) {
-                const float *st = smem + (t & 1) * STAGE;
-                float *nx = smem + ((t + 1) & 1) * STAGE;
-                const int kn = kb + (t + 1) * BK;
-                // piece q of a step goes after MFMA (q * MI * NI) / pieces per
-                // step; the loads after a range's last tile (the next tile,
-                // or 0.0 past K) land in a stage nobody reads
-                auto hook = [&](int j, int u) {
-                    if (j < LSTEPS) {
-#pragma unroll
-                        for (int q = 0; q < LPER; ++q) {
-                            const int piece = j * LPER + q;
-                            if ((q * NU) / LPER != u || piece >= NP) continue;
-                            if (piece < PA) ta.template load_piece<0>(a, bm, kn, piece);
-                            else tb.template load_piece<0>(a, bn, kn, piece - PA);
-                        }
-                    }
-                    if (j >= STEPS - SSTEPS) {
-#pragma unroll
-                        for (int q = 0; q < SPER; ++q) {
-                            const int piece = (j - (STEPS - SSTEPS)) * SPER + q;
-                            if ((q * NU) / SPER != u || piece >= NP) continue;
-                            if (piece < PA) ta.template store_piece<0>(nx, tid, piece);
-                            else tb.template store_piece<0>(nx + ASZ, tid, piece - PA);
-                        }
-                    }
-                };
-                mfma_tile_kc<BK, MI, NI, SB, 1, CH>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
-                __syncthreads();
-            }
         }
         if (CH == 2) {
 #pragma unroll
