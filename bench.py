@@ -16,10 +16,12 @@ steps bracketed by device synchronisation; one JSON line on stdout.
                from profiles/ when it was taken on the current kernel source,
                else null.
   secondary  = the same timing (after at least 50 ms of untimed launches) for
-               4096^3 and for the low-K 16384^2 x 128
-               problem (beta = 1), each with its fraction of the FP32 peak, of
-               the HBM peak (algorithmic bytes: A, B, C read, C written) and of
-               the larger of the two bounds.
+               every other workload of the sweep: 4096^3, the low-K
+               16384^2 x 128 problem (beta = 1), 256^3, the ragged
+               1000 x 1023 x 999 problem (beta = -0.5), 1024^3, 2048^3 and
+               16384^3, each with its fraction of the FP32 peak, of the HBM
+               peak (algorithmic bytes: A, B, C read, C written) and of the
+               larger of the two bounds.
   cpu_baseline = the float64 CPU oracle on a bounded band of rows of the same
                problem, on every host core (rank 0, N = 1 only).
 """
@@ -46,10 +48,11 @@ PEAK_FP32_TFLOPS = 157.3  # 256 CU x 256 FLOP/clk x 2.4 GHz (FP32 MFMA)
 PEAK_VALU_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 WORKLOAD = "square8192_normal"
-# Reported beside the main line: the other square size the metric names, and
-# the low-K shape, whose bound is taken as the larger of its FLOP time at the
-# FP32 peak and its algorithmic bytes at the HBM peak.
-SECONDARY = ("square4096_upm1", "lowk_16384x16384x128")
+# Reported beside the main line: the other square size the metric names, the
+# low-K shape, whose bound is taken as the larger of its FLOP time at the FP32
+# peak and its algorithmic bytes at the HBM peak, and the rest of the sweep.
+SECONDARY = ("square4096_upm1", "lowk_16384x16384x128", "square256_u01", "ragged_1000x1023x999",
+             "square1024_normal", "square2048_normal", "square16384_normal")
 
 
 def _code_tokens(text: str) -> str:

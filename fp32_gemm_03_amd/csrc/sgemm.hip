@@ -161,20 +161,23 @@ const Variant kVariants[] = {
     MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, 0, true, "_kcd"),     // 31: 2 workgroups per CU
     MFMA_CFG_KCD(128, 256, 32, 64, 128, 1, 4, false, "_kcd"),    // 32: 1 workgroup per CU
     MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, "_kcd"),       // 33: 4 workgroups per CU
+    MFMA_CFG_KCD(128, 128, 64, 64, 32, 2, 4, false, "_w8_kcd"),  // 34: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(64, 64, 64, 32, 32, 2, 4, false, "_kcd"),       // 35: 2 workgroups per CU
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 constexpr int kValuDefault = 0;  // 128 x 128 x 16, 8 x 8 per lane, four workgroups per CU
 constexpr int kValuWide = 7;     // 128 x 256 x 16, 8 x 16 per lane, two workgroups per CU
-// the blocks on the interleaved schedule, A as is ...
+// the block on the interleaved schedule, A as is ...
 constexpr int kIlMid = 24;       // 128 x 128 x 32, two workgroups per CU
-constexpr int kIlDeep = 28;      // 128 x 128 x 64, one workgroup per CU
 // ... and with A in K order, loaded straight into LDS
 constexpr int kKcHuge = 29;      // 256 x 256 x 32, 8 waves, one workgroup per CU
 constexpr int kKcLarge4 = 30;    // 128 x 128 x 16, four workgroups per CU
 constexpr int kKcShortK = 31;    // 128 x 256 x 16, two workgroups per CU
 constexpr int kKcWide = 32;      // 128 x 256 x 32, one workgroup per CU
 constexpr int kKcSmall4 = 33;    // 64 x 64 x 32, four workgroups per CU
+constexpr int kKcDeep8 = 34;     // 128 x 128 x 64, 8 waves, one workgroup per CU
+constexpr int kKcSmall64 = 35;   // 64 x 64 x 64, two workgroups per CU
 
 // Compute units of an MI355X; the choice of tile is a pure function of the
 // sizes so that it is the same on every call and testable without a GPU.
@@ -198,8 +201,10 @@ double quantization(long long t) {
 // 16384 x 1024 x 1024 both ways, 1000 x 1023 x 999, and split-K shapes):
 //   * blocks with A in K order, loaded straight into LDS, match or beat the
 //     same blocks on the interleaved schedule with A transposed (by 2-3% at
-//     128 x 128 x 16, up to 10% on 64 x 64 blocks), except 128 x 128 x 32
-//     and 128 x 128 x 64, which keep the interleaved schedule;
+//     128 x 128 x 16, up to 10% on 64 x 64 blocks), except 128 x 128 x 32,
+//     which keeps the interleaved schedule; at 128 x 128 x 64 the K-ordered
+//     block with 4 waves of 64 x 64 was 0.5-1% slower than the interleaved
+//     one, with 8 waves of 64 x 32 (two per SIMD) 1.5-2% faster;
 //   * a block shape reaches its full-chip rate only once there is a tile for
 //     every workgroup slot on the chip (slots = workgroups per CU x 256);
 //     below that its workgroups run alone on their CUs and latency shows.
@@ -207,8 +212,8 @@ double quantization(long long t) {
 //     the share of CUs the last round of tiles keeps busy.  Rates, TFLOP/s:
 //     256 x 256 x 32 (1 per CU) 146.5, 128 x 128 x 16 (4 per CU) 146,
 //     128 x 256 x 16 (2 per CU) 144, 128 x 256 x 32 (1 per CU) 142,
-//     128 x 128 x 32 (2 per CU) 140.5, 128 x 128 x 64 (1 per CU) 137,
-//     64 x 64 x 32 (4 per CU) 130.  With K short the epilogue is a larger
+//     128 x 128 x 32 (2 per CU) 140.5, 128 x 128 x 64 with 8 waves (1 per
+//     CU) 139, 64 x 64 x 32 (4 per CU) 130.  With K short the epilogue is a larger
 //     share of a tile's time and blocks with more workgroups per CU, which
 //     hide one workgroup's epilogue under another's K loop, win: the
 //     one-per-CU blocks need K >= 512 and the 128 x 128 ones K >= 256 (at
@@ -218,9 +223,13 @@ double quantization(long long t) {
 //     128 x 128 x 16; 1024 x 8192 x 8192 (one 128 x 256 block per CU) takes
 //     128 x 256 x 32; 2048^3 (one 128 x 128 block per CU) 128 x 128 x 64;
 //     3072^3 takes 64 x 64 x 32; the low-K square takes 128 x 256 x 16;
-//   * below that the problem cannot fill the chip: 64 x 64 x 32 blocks
-//     (10-15% faster there than 64 x 64 x 64 blocks with fragments three
-//     k-steps ahead), split along K when K is long (select_splits).
+//   * below that the problem cannot fill the chip: 64 x 64 blocks, split
+//     along K when K is long (select_splits).  With at most one tile per CU
+//     the K-ordered 64 x 64 x 64 block, which halves the barriers per FLOP,
+//     is 5-8% faster than 64 x 64 x 32 (1024^3 96.5 against 91.4 TFLOP/s,
+//     1000 x 1023 x 999 77 against 71, 1024 x 1024 x 4096 109 against
+//     102); with more tiles, 64 x 64 x 32 at four workgroups per CU is
+//     (3072^3 121 against 116, 5120^3 131 against 125).
 // Stream-K (with a workspace): a block whose last round of tiles leaves
 // workgroup slots idle runs its whole rounds as usual and spreads the K tiles
 // of the rest over one workgroup per slot, so every slot ends at about the
@@ -254,7 +263,7 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
     };
     static const Candidate cand[] = {{kKcHuge, 146.5, 1, 512},  {kKcLarge4, 146.0, 4, 256},
                                      {kKcShortK, 144.0, 2, 0},  {kKcWide, 142.0, 1, 512},
-                                     {kIlMid, 140.5, 2, 256},   {kIlDeep, 137.0, 1, 1024},
+                                     {kIlMid, 140.5, 2, 256},   {kKcDeep8, 139.0, 1, 1024},
                                      {kKcSmall4, 130.0, 4, 0}};
     int best = -1, best_workers = 0;
     double best_score = -1.0;
@@ -281,11 +290,13 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
         // No block fills the chip: 64 x 64 blocks.  With more tiles than
         // CUs but not a whole number per CU, stream-K over one worker per CU
         // evens out the K tiles each CU runs (1536^3: 107.5 TFLOP/s against
-        // 95.4); with at most one tile per CU, select_splits may split K.
+        // 95.4); with at most one tile per CU, the deeper K tile, and
+        // select_splits may split K.
         const Variant &v = kVariants[kKcSmall4];
         const long long t = tiles(M, N, v.bm, v.bn), rest = t % kComputeUnits;
+        if (t <= kComputeUnits) return kKcSmall64;
         const long long kt = (K + v.bk - 1) / v.bk;
-        if (streamk && workers && t > kComputeUnits && rest > 0 && rest * kt >= kStreamKMinK * kComputeUnits)
+        if (streamk && workers && rest > 0 && rest * kt >= kStreamKMinK * kComputeUnits)
             *workers = (int)kComputeUnits;
         return kKcSmall4;
     }
@@ -305,7 +316,7 @@ int select_variant(int path, int M, int N, int K) { return choose(path, M, N, K,
 // blocks chosen by rate have a tile for every one of their workgroup slots
 // on the chip already.
 int select_splits(int variant, int M, int N, int K) {
-    if (M <= 0 || N <= 0 || K <= 0 || variant != kKcSmall4) return 1;
+    if (M <= 0 || N <= 0 || K <= 0 || (variant != kKcSmall4 && variant != kKcSmall64)) return 1;
     const Variant &v = kVariants[variant];
     if (v.split4 == nullptr) return 1;
     const long long t = tiles(M, N, v.bm, v.bn);

@@ -22,7 +22,7 @@ import sys
 DEFAULT_SHAPES = [
     "square256_u01", "ragged_1000x1023x999", "square1024_normal", "square2048_normal",
     "3072x3072x3072", "square4096_upm1", "5120x5120x5120", "6144x6144x6144", "7168x7168x7168",
-    "square8192_normal", "10240x10240x10240", "lowk_16384x16384x128", "512x512x8192",
+    "square8192_normal", "10240x10240x10240", "square16384_normal", "lowk_16384x16384x128", "512x512x8192",
     "1024x1024x4096", "1024x8192x8192", "16384x1024x1024", "1024x16384x1024",
 ]
 

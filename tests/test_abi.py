@@ -182,9 +182,13 @@ def test_large_shapes_pick_the_block_whose_last_round_is_fullest():
     assert block(10240, 10240, 10240) == (128, 128, 16)
     assert block(1024, 8192, 8192) == (128, 256, 32)    # 256 blocks: one per CU
     assert block(2048, 2048, 2048) == (128, 128, 64)    # 256 blocks: one per CU
+    assert "_w8_" in g.sgemm_variant_name(g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 2048, 2048, 2048))
     assert block(3072, 3072, 3072) == (64, 64, 32)      # 128 x 128 would leave 1/4 of a round
-    assert block(1024, 1024, 1024) == (64, 64, 32)      # too few tiles for any slot count
-    assert block(1000, 1023, 999) == (64, 64, 32)
+    # too few tiles for any slot count, at most one 64 x 64 tile per CU: the deeper K tile
+    assert block(1024, 1024, 1024) == (64, 64, 64)
+    assert block(1000, 1023, 999) == (64, 64, 64)
+    assert block(512, 512, 8192) == (64, 64, 64)
+    assert block(1088, 1024, 1024) == (64, 64, 32)      # 272 tiles: more than one per CU
 
 
 def test_streamk_host_logic():
@@ -237,7 +241,7 @@ def test_streamk_host_logic():
 
 def test_only_the_latency_block_splits_k():
     """A block chosen by rate already has a tile per workgroup slot on the
-    chip; only the 64 x 64 fallback splits K when a workspace is given."""
+    chip; only the 64 x 64 fallbacks split K when a workspace is given."""
     assert g.sgemm_select_splits(1024, 8192, 8192) == 1
     assert g.sgemm_select_splits(2048, 2048, 2048) == 1
     assert g.sgemm_select_splits(16384, 1024, 1024) == 1
