@@ -15,7 +15,8 @@ steps bracketed by device synchronisation; one JSON line on stdout.
                FETCH_SIZE + WRITE_SIZE (scaled by a copy-kernel calibration), read
                from profiles/ when it was taken on the current kernel source,
                else null.
-  secondary  = the same timing (after at least 50 ms of untimed launches) for
+  secondary  = the same timing (after at least 50 ms of untimed launches, and
+               with events only around the whole run of launches) for
                every other workload of the sweep: 4096^3, the low-K
                16384^2 x 128 problem (beta = 1), 256^3, the ragged
                1000 x 1023 x 999 problem (beta = -0.5), 1024^3, 2048^3 and
@@ -97,11 +98,12 @@ def read_traffic(workload: str, variant_name: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-def time_gpu(p, steps, warmup, path, variant=None, min_warmup_s=0.0):
-    """Launch on a dedicated stream; HIP events on that stream around every launch.
-    After the `warmup` untimed launches, further untimed ones until about
-    min_warmup_s has passed (so a short kernel after host work starts timing
-    at a settled clock)."""
+def time_gpu(p, steps, warmup, path, variant=None, min_warmup_s=0.0, per_launch=True):
+    """Launch on a dedicated stream; HIP events on that stream around every launch
+    (with per_launch False only around the whole run, so that the host's event
+    records do not leave a short kernel's queue empty).  After the `warmup`
+    untimed launches, further untimed ones until about min_warmup_s has passed
+    (so a short kernel after host work starts timing at a settled clock)."""
     import torch
     import fp32_gemm_03_amd as g
 
@@ -127,16 +129,19 @@ def time_gpu(p, steps, warmup, path, variant=None, min_warmup_s=0.0):
             for _ in range(8):
                 step()
             torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_launch else 2)]
     t0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(steps):
         step()
-        ev[i + 1].record(stream)
+        if per_launch:
+            ev[i + 1].record(stream)
+    if not per_launch:
+        ev[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    total_ms = ev[0].elapsed_time(ev[steps])
+    per_launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)] if per_launch else []
+    total_ms = ev[0].elapsed_time(ev[-1])
     del a, b, c
     return total_ms, per_launch_ms, wall
 
@@ -266,7 +271,8 @@ def main():
             p2 = inputs.workload_problem(name)
             w2 = inputs.WORKLOADS[name]
             steps2 = max(args.steps, 100)
-            t2, per2, _ = time_gpu(p2, steps2, args.warmup, path, args.variant, min_warmup_s=0.05)
+            t2, _, _ = time_gpu(p2, steps2, args.warmup, path, args.variant, min_warmup_s=0.05,
+                                per_launch=False)
             v2 = g.sgemm_select_variant(path, p2.M, p2.N, p2.K) if args.variant is None else args.variant
             sec_s = t2 / steps2 / 1e3
             t_fp32 = w2.flops / (PEAK_FP32_TFLOPS * 1e12)
