@@ -109,14 +109,16 @@ struct Variant {
 // or XOR-swizzled): loading straight into LDS 4 bytes per lane is 4% slower
 // than that at 8192^3 (140 against 146 TFLOP/s).  Those two sum the k of a
 // K tile in the same order as each other, the 128-bit builds in another.
-#define MFMA_CFG_KCD(BM, BN, BK, WM, WN, WPE, PA, SWZ, SUFFIX)                          \
+// RO is the order of the LDS fragment reads at a K tile's start
+// (mfma_tile_kc), chosen per block by measurement.
+#define MFMA_CFG_KCD(BM, BN, BK, WM, WN, WPE, PA, SWZ, RO, SUFFIX)                      \
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
      (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false>,                              \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO>,                          \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 1, 0, false, 0, SWZ, true>, \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, 1, 0, false, 0, SWZ, true>, \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true>,                               \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 1, WPE, true>, 0, 1, 1}
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO>,                           \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 1, WPE, true, RO>, 0, 1, 1}
 
 const Variant kVariants[] = {
     VALU_CFG(128, 128, 16, 8, 8, 4, 0, 4),                     // 0
@@ -156,13 +158,13 @@ const Variant kVariants[] = {
     MFMA_CFG_IL(128, 256, 32, 64, 128, 4, 1, false, "_il"),      // 26: 1 workgroup per CU
     MFMA_CFG_IL(64, 64, 32, 32, 32, 4, 4, false, "_il"),         // 27: 4 workgroups per CU
     MFMA_CFG_IL(128, 128, 64, 64, 64, 4, 1, false, "_il"),       // 28: 1 workgroup per CU
-    MFMA_CFG_KCD(256, 256, 32, 128, 64, 2, 4, false, "_kcd"),    // 29: 8 waves, 2 per SIMD
-    MFMA_CFG_KCD(128, 128, 16, 64, 64, 4, 4, false, "_wpe4_kcd"),  // 30: 4 workgroups per CU
-    MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, 0, true, "_kcd"),     // 31: 2 workgroups per CU
-    MFMA_CFG_KCD(128, 256, 32, 64, 128, 1, 4, false, "_kcd"),    // 32: 1 workgroup per CU
-    MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, "_kcd"),       // 33: 4 workgroups per CU
-    MFMA_CFG_KCD(128, 128, 64, 64, 32, 2, 4, false, "_w8_kcd"),  // 34: 8 waves, 2 per SIMD
-    MFMA_CFG_KCD(64, 64, 64, 32, 32, 2, 4, false, "_kcd"),       // 35: 2 workgroups per CU
+    MFMA_CFG_KCD(256, 256, 32, 128, 64, 2, 4, false, 1, "_kcd"),    // 29: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(128, 128, 16, 64, 64, 4, 4, false, 0, "_wpe4_kcd"),  // 30: 4 workgroups per CU
+    MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, 0, true, 0, "_kcd"),     // 31: 2 workgroups per CU
+    MFMA_CFG_KCD(128, 256, 32, 64, 128, 1, 4, false, 1, "_kcd"),    // 32: 1 workgroup per CU
+    MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, 1, "_kcd"),       // 33: 4 workgroups per CU
+    MFMA_CFG_KCD(128, 128, 64, 64, 32, 2, 4, false, 1, "_w8_kcd"),  // 34: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(64, 64, 64, 32, 32, 2, 4, false, 1, "_kcd"),       // 35: 2 workgroups per CU
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
