@@ -158,12 +158,12 @@ const Variant kVariants[] = {
     MFMA_CFG_IL(128, 256, 32, 64, 128, 4, 1, false, "_il"),      // 26: 1 workgroup per CU
     MFMA_CFG_IL(64, 64, 32, 32, 32, 4, 4, false, "_il"),         // 27: 4 workgroups per CU
     MFMA_CFG_IL(128, 128, 64, 64, 64, 4, 1, false, "_il"),       // 28: 1 workgroup per CU
-    MFMA_CFG_KCD(256, 256, 32, 128, 64, 2, 4, false, 1, "_kcd"),    // 29: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(256, 256, 32, 128, 64, 2, 4, false, 2, "_kcd"),    // 29: 8 waves, 2 per SIMD
     MFMA_CFG_KCD(128, 128, 16, 64, 64, 4, 4, false, 0, "_wpe4_kcd"),  // 30: 4 workgroups per CU
     MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, 0, true, 0, "_kcd"),     // 31: 2 workgroups per CU
     MFMA_CFG_KCD(128, 256, 32, 64, 128, 1, 4, false, 1, "_kcd"),    // 32: 1 workgroup per CU
     MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, 1, "_kcd"),       // 33: 4 workgroups per CU
-    MFMA_CFG_KCD(128, 128, 64, 64, 32, 2, 4, false, 1, "_w8_kcd"),  // 34: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(128, 128, 64, 64, 32, 2, 4, false, 2, "_w8_kcd"),  // 34: 8 waves, 2 per SIMD
     MFMA_CFG_KCD(64, 64, 64, 32, 32, 2, 4, false, 1, "_kcd"),       // 35: 2 workgroups per CU
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);

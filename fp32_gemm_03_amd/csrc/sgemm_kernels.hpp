@@ -1167,23 +1167,38 @@ __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_o
     // RO == 0: the first group of four k's of A, the B fragments and the
     // next group of A, all before the first MFMA.  RO == 1: the B fragment
     // first and the next group of A one k-step later, so the first MFMA
-    // waits for about half as many bytes.  Measured per block: RO == 1 is
-    // 0.5-0.7% faster on the 256 x 256 block and up to 4% on 64 x 64 x 32,
-    // but 11% slower on 128 x 128 x 16 at four workgroups per CU where the
-    // last round of tiles is partial (6144^3, 5120^3) and 0.4-0.7% slower on
-    // 128 x 256 x 16 at 16384^2 x 128; no cause was found for either.
+    // waits for about half as many bytes.  RO == 2: only the B fragment and
+    // A block row 0 before the first MFMA, the rest of the group and the
+    // next B fragment right after it.  Measured per block: RO == 1 is
+    // 0.5-0.7% faster than RO == 0 on the 256 x 256 block and up to 4% on
+    // 64 x 64 x 32, RO == 2 another 0.2-0.4% on 256 x 256 and 128 x 128 x 64;
+    // both are 11% slower on 128 x 128 x 16 at four workgroups per CU where
+    // the last round of tiles is partial (6144^3, 5120^3) and 0.4-1% slower
+    // on 128 x 256 x 16 at 16384^2 x 128; no cause was found for those two.
     if (RO == 0) {
 #pragma unroll
     for (int i = 0; i < MI; ++i) av[0][i] = *reinterpret_cast<const float4 *>(a_row + i * 32 * BK + a_off[0]);
 #pragma unroll
     for (int f = 0; f < FD && f < STEPS; ++f) bv[f] = *reinterpret_cast<const VB *>(bp + f * SB);
-    } else {
+    } else if (RO == 1) {
 #pragma unroll
     for (int f = 0; f < FD && f < STEPS; ++f) bv[f] = *reinterpret_cast<const VB *>(bp + f * SB);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < MI; ++i) av[0][i] = *reinterpret_cast<const float4 *>(a_row + i * 32 * BK + a_off[0]);
+    } else {
+    bv[0] = *reinterpret_cast<const VB *>(bp);
+    __builtin_amdgcn_sched_barrier(0);
+    av[0][0] = *reinterpret_cast<const float4 *>(a_row + a_off[0]);
     }
+    // RO == 2: the rest of the first group of A and the next B fragment
+    // right after the first MFMA
+    auto rest_of_first = [&]() {
+#pragma unroll
+        for (int i = 1; i < MI; ++i) av[0][i] = *reinterpret_cast<const float4 *>(a_row + i * 32 * BK + a_off[0]);
+#pragma unroll
+        for (int f = 1; f <= FD && f < STEPS; ++f) bv[f % RING] = *reinterpret_cast<const VB *>(bp + f * SB);
+    };
 #pragma unroll
     for (int q = 0; q < QN; ++q) {
 #pragma unroll
@@ -1194,8 +1209,9 @@ __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_o
                 for (int i = 0; i < MI; ++i)
                     av[(q + 1) & 1][i] = *reinterpret_cast<const float4 *>(a_row + i * 32 * BK + a_off[q + 1]);
             }
-            if (j + FD < STEPS) bv[(j + FD) % RING] = *reinterpret_cast<const VB *>(bp + (j + FD) * SB);
-            if (RO == 1 && e == 1 && q + 1 < QN) {
+            if (j + FD < STEPS && !(RO == 2 && j == 0))
+                bv[(j + FD) % RING] = *reinterpret_cast<const VB *>(bp + (j + FD) * SB);
+            if (RO >= 1 && e == 1 && q + 1 < QN) {
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
                     av[(q + 1) & 1][i] = *reinterpret_cast<const float4 *>(a_row + i * 32 * BK + a_off[q + 1]);
@@ -1214,6 +1230,10 @@ __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_o
                         acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(x, vget(bv[j % RING], jj),
                                                                           acc[i][jj], 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
+                    if (RO == 2 && j == 0 && i == 0 && jj == 0) {
+                        rest_of_first();
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                     hook(j, i * NI + jj);
                     __builtin_amdgcn_sched_barrier(0);
                 }
