@@ -25,6 +25,10 @@ steps bracketed by device synchronisation; one JSON line on stdout.
                larger of the two bounds.
   cpu_baseline = the float64 CPU oracle on a bounded band of rows of the same
                problem, on every host core (rank 0, N = 1 only).
+  parity     = those oracle rows against the same rows of C after the first
+               launch (from the workload's initial C), copied back before the
+               warm-up: max error ratio and the 1e-5 pass rule.
+  clocks     = rocm-smi's clock readings just before and after the timed run.
 """
 from __future__ import annotations
 
@@ -33,9 +37,13 @@ import hashlib
 import json
 import os
 import re
+import shutil
 import statistics
+import subprocess
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -48,6 +56,10 @@ PEAK_FP32_TFLOPS = 157.3  # 256 CU x 256 FLOP/clk x 2.4 GHz (FP32 MFMA)
 # path is held to the same 157.3 TFLOP/s vector peak.
 PEAK_VALU_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+# The pass rule against the oracle: max |C - ref| / (|alpha| sum_k |A_ik B_kj| + |beta C_ij| + 1e-30)
+TOLERANCE = 1e-5
+# Elements of C (rows x N) copied back after the first launch for the parity check.
+CAPTURE_ELEMENTS = 1 << 25
 WORKLOAD = "square8192_normal"
 # Reported beside the main line: the other square size the metric names, the
 # low-K shape, whose bound is taken as the larger of its FLOP time at the FP32
@@ -98,12 +110,15 @@ def read_traffic(workload: str, variant_name: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-def time_gpu(p, steps, warmup, path, variant=None, min_warmup_s=0.0, per_launch=True):
+def time_gpu(p, steps, warmup, path, variant=None, min_warmup_s=0.0, per_launch=True, capture_rows=0):
     """Launch on a dedicated stream; HIP events on that stream around every launch
     (with per_launch False only around the whole run, so that the host's event
     records do not leave a short kernel's queue empty).  After the `warmup`
     untimed launches, further untimed ones until about min_warmup_s has passed
-    (so a short kernel after host work starts timing at a settled clock)."""
+    (so a short kernel after host work starts timing at a settled clock).
+    With capture_rows > 0, the first `capture_rows` rows of C after the first
+    launch (from the problem's initial C) are copied to the host and returned
+    as a fourth value, for checking against the oracle."""
     import torch
     import fp32_gemm_03_amd as g
 
@@ -120,6 +135,11 @@ def time_gpu(p, steps, warmup, path, variant=None, min_warmup_s=0.0, per_launch=
             g.sgemm_variant(variant, *args, stream=stream)
 
     torch.cuda.synchronize()
+    first_rows = None
+    if capture_rows > 0:
+        step()
+        torch.cuda.synchronize()
+        first_rows = c[:capture_rows, :p.N].cpu().numpy().astype(np.float64)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -143,30 +163,58 @@ def time_gpu(p, steps, warmup, path, variant=None, min_warmup_s=0.0, per_launch=
     per_launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)] if per_launch else []
     total_ms = ev[0].elapsed_time(ev[-1])
     del a, b, c
+    if capture_rows > 0:
+        return total_ms, per_launch_ms, wall, first_rows
     return total_ms, per_launch_ms, wall
 
 
-def cpu_baseline(p, target_s=10.0):
-    import numpy as np
+def cpu_baseline(p, target_s=10.0, gpu_rows=None):
+    """The oracle timed on a band of rows 0..r-1; with gpu_rows (the GPU's first
+    rows of C), also the parity of those rows against the same oracle rows."""
     import oracle
 
     A, B = p.np("A"), p.np("B")
+    Cin = p.np("C") if p.beta != 0 else None
     cores = oracle.nthreads()
     rows = max(8, min(cores, p.M))
     t0 = time.perf_counter()
-    oracle.sgemm_rows(p.M, p.N, p.K, p.alpha, A, p.lda, B, p.ldb, p.beta, None, p.ldc, 0, rows)
+    oracle.sgemm_rows(p.M, p.N, p.K, p.alpha, A, p.lda, B, p.ldb, p.beta, Cin, p.ldc, 0, rows)
     t_probe = time.perf_counter() - t0
     rows2 = int(max(rows, min(p.M, rows * target_s / max(t_probe, 1e-3))))
     rows2 = max(rows, (rows2 // cores) * cores)
     t0 = time.perf_counter()
-    oracle.sgemm_rows(p.M, p.N, p.K, p.alpha, A, p.lda, B, p.ldb, p.beta, None, p.ldc, 0, rows2)
+    ref, den = oracle.sgemm_rows(p.M, p.N, p.K, p.alpha, A, p.lda, B, p.ldb, p.beta, Cin, p.ldc, 0, rows2)
     t = time.perf_counter() - t0
     flops = 2.0 * rows2 * p.N * p.K
-    return {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"rows 0..{rows2 - 1} of the {p.M}x{p.N}x{p.K} problem "
-                      f"({rows2 * p.N} elements, float64 i-k-j loop), {t:.1f} s",
-            "seconds": round(t, 3)}
+    out = {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"rows 0..{rows2 - 1} of the {p.M}x{p.N}x{p.K} problem "
+                     f"({rows2 * p.N} elements, float64 i-k-j loop), {t:.1f} s",
+           "seconds": round(t, 3)}
+    parity = None
+    if gpu_rows is not None:
+        r = min(rows2, gpu_rows.shape[0])
+        err = oracle.max_error_ratio(gpu_rows[:r], ref[:r], den[:r])
+        parity = {"rows": r, "elements": r * p.N, "max_err_ratio": err, "tolerance": TOLERANCE,
+                  "pass": bool(err <= TOLERANCE),
+                  "against": "the oracle's rows of the CPU baseline; C after the first launch "
+                             "from the workload's initial C"}
+    return out, parity
+
+
+def gpu_clocks():
+    """Current clocks from `rocm-smi --showgpuclocks --json` (a read-only query,
+    run as a child process), or None where it is not available."""
+    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
+    try:
+        r = subprocess.run([exe, "--showgpuclocks", "--json"], capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    if not isinstance(data, dict) or not data:
+        return None
+    card = data[sorted(data)[0]]
+    return {k: v for k, v in card.items() if "clk" in k.lower() or "clock" in k.lower()} if isinstance(card, dict) else None
 
 
 def main():
@@ -229,7 +277,12 @@ def main():
         sys.exit(2)
     print(f"bench: {args.workload} variant {vname}, {args.warmup} warm-up + {args.steps} timed",
           file=sys.stderr, flush=True)
-    total_ms, per_launch, wall = time_gpu(p, args.steps, args.warmup, path, args.variant)
+    capture = 0 if args.no_cpu_baseline else max(1, min(p.M, CAPTURE_ELEMENTS // max(p.N, 1)))
+    clocks_before = gpu_clocks()
+    timed = time_gpu(p, args.steps, args.warmup, path, args.variant, capture_rows=capture)
+    clocks_after = gpu_clocks()
+    total_ms, per_launch, wall = timed[:3]
+    first_rows = timed[3] if capture else None
     ms_per_step = total_ms / args.steps
     value = w.flops / (ms_per_step / 1e3) / 1e12
     avg_kernel_ms = sum(per_launch) / len(per_launch)
@@ -288,7 +341,10 @@ def main():
                 "frac_of_roofline": round(max(t_fp32, t_hbm) / sec_s, 4)})
             del p2
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(p)
+        out["cpu_baseline"], out["parity"] = cpu_baseline(p, gpu_rows=first_rows)
+    out["clocks"] = {"before": clocks_before, "after": clocks_after,
+                     "note": "idle snapshots around the timed run; the clock under load is "
+                             "GRBM_GUI_ACTIVE over the kernel's duration (profiles/)"}
     cus, clk, peak_props = g.sgemm_device_fp32_peak(0)
     out["device"] = {"name": torch.cuda.get_device_name(0),
                      "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
