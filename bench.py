@@ -238,7 +238,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this SGEMM runs on one GPU; multi-GPU runs are not part of it "
-              "(a row-block split of C would need no exchange, see the design notes)",
+              "(C would split by row blocks of A, with B replicated and no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 

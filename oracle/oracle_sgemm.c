@@ -1,7 +1,7 @@
 /*
  * oracle_sgemm.c -- plain, slow, obviously correct CPU SGEMM in float64.
  *
- * TEST INFRASTRUCTURE ONLY.  This file is the checker for the GPU library,
+ * TEST INFRASTRUCTURE ONLY.  This file is the reference the GPU library is tested against,
  * not part of it: only the test suite, the smoke check and the benchmark's
  * CPU-baseline leg may build, load or call it.  It shares no code, header or
  * table with the HIP library and includes nothing from it.
