@@ -215,16 +215,18 @@ double quantization(long long t) {
 //     256 x 256 x 32 (1 per CU) 146.5, 128 x 128 x 16 (4 per CU) 146,
 //     128 x 256 x 16 (2 per CU) 144, 128 x 256 x 32 (1 per CU) 142,
 //     128 x 128 x 32 (2 per CU) 140.5, 128 x 128 x 64 with 8 waves (1 per
-//     CU) 139, 64 x 64 x 32 (4 per CU) 130.  With K short the epilogue is a larger
+//     CU) 139, 64 x 64 x 32 (4 per CU) 134 (its rate at 2048^3-6144^3; it
+//     falls to 117-130 from 8192^3 up, where better-filled blocks win).  With K short the epilogue is a larger
 //     share of a tile's time and blocks with more workgroups per CU, which
 //     hide one workgroup's epilogue under another's K loop, win: the
 //     one-per-CU blocks need K >= 512 and the 128 x 128 ones K >= 256 (at
 //     16384^2 x 128 the 128 x 256 x 16 block runs 112 TFLOP/s against 105
 //     and 90).  So 8192^3, 4096^3 and 16384 x 1024 x 1024 (whole rounds of
-//     256 x 256 blocks) take 256 x 256; 5120^3 to 10240^3 take
+//     256 x 256 blocks) take 256 x 256; 6144^3 to 10240^3 take
 //     128 x 128 x 16; 1024 x 8192 x 8192 (one 128 x 256 block per CU) takes
 //     128 x 256 x 32; 2048^3 (one 128 x 128 block per CU) 128 x 128 x 64;
-//     3072^3 takes 64 x 64 x 32; the low-K square takes 128 x 256 x 16;
+//     3072^3, 3840^3 and 5120^3 take 64 x 64 x 32 (5120^3: 135 against 128.5
+//     for 128 x 128 x 16); the low-K square takes 128 x 256 x 16;
 //   * below that the problem cannot fill the chip: 64 x 64 blocks, split
 //     along K when K is long (select_splits).  With at most one tile per CU
 //     the K-ordered 64 x 64 x 64 block, which halves the barriers per FLOP,
@@ -266,7 +268,7 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
     static const Candidate cand[] = {{kKcHuge, 146.5, 1, 512},  {kKcLarge4, 146.0, 4, 256},
                                      {kKcShortK, 144.0, 2, 0},  {kKcWide, 142.0, 1, 512},
                                      {kIlMid, 140.5, 2, 256},   {kKcDeep8, 139.0, 1, 1024},
-                                     {kKcSmall4, 130.0, 4, 0}};
+                                     {kKcSmall4, 134.0, 4, 0}};
     int best = -1, best_workers = 0;
     double best_score = -1.0;
     for (const Candidate &c : cand) {

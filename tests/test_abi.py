@@ -184,6 +184,7 @@ def test_large_shapes_pick_the_block_whose_last_round_is_fullest():
     assert block(2048, 2048, 2048) == (128, 128, 64)    # 256 blocks: one per CU
     assert "_w8_" in g.sgemm_variant_name(g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 2048, 2048, 2048))
     assert block(3072, 3072, 3072) == (64, 64, 32)      # 128 x 128 would leave 1/4 of a round
+    assert block(5120, 5120, 5120) == (64, 64, 32)      # whole rounds of 64 x 64, 6.25 of 128 x 128
     # too few tiles for any slot count, at most one 64 x 64 tile per CU: the deeper K tile
     assert block(1024, 1024, 1024) == (64, 64, 64)
     assert block(1000, 1023, 999) == (64, 64, 64)
