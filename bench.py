@@ -28,18 +28,18 @@ steps bracketed by device synchronisation; one JSON line on stdout.
   parity     = those oracle rows against the same rows of C after the first
                launch (from the workload's initial C), copied back before the
                warm-up: max error ratio and the 1e-5 pass rule.
-  clocks     = rocm-smi's clock readings just before and after the timed run.
+  clocks     = the shader clock level sysfs reports for each GPU just before and
+               after the timed run.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
 import re
-import shutil
 import statistics
-import subprocess
 import sys
 import time
 
@@ -203,18 +203,19 @@ def cpu_baseline(p, target_s=10.0, gpu_rows=None):
 
 
 def gpu_clocks():
-    """Current clocks from `rocm-smi --showgpuclocks --json` (a read-only query,
-    run as a child process), or None where it is not available."""
-    exe = shutil.which("rocm-smi") or "/opt/rocm/bin/rocm-smi"
-    try:
-        r = subprocess.run([exe, "--showgpuclocks", "--json"], capture_output=True, text=True, timeout=30)
-        data = json.loads(r.stdout)
-    except (OSError, ValueError, subprocess.SubprocessError):
-        return None
-    if not isinstance(data, dict) or not data:
-        return None
-    card = data[sorted(data)[0]]
-    return {k: v for k, v in card.items() if "clk" in k.lower() or "clock" in k.lower()} if isinstance(card, dict) else None
+    """The current shader clock level of each GPU the driver lists, read from
+    sysfs (pp_dpm_sclk, the line marked '*'); plain file reads, no program is
+    started.  None where the files are not readable."""
+    out = {}
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                cur = [line.strip() for line in f if line.rstrip().endswith("*")]
+        except OSError:
+            continue
+        if cur:
+            out[path.split("/")[4]] = cur[0].rstrip("* ").strip()
+    return out or None
 
 
 def main():
@@ -246,6 +247,9 @@ def main():
     import fp32_gemm_03_amd as g
     from fp32_gemm_03_amd import inputs
 
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.default()  # loaded (or compiled) before the GPU is initialised
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)

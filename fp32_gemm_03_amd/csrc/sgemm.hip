@@ -161,7 +161,7 @@ const Variant kVariants[] = {
     MFMA_CFG_KCD(256, 256, 32, 128, 64, 2, 4, false, 2, "_kcd"),    // 29: 8 waves, 2 per SIMD
     MFMA_CFG_KCD(128, 128, 16, 64, 64, 4, 4, false, 0, "_wpe4_kcd"),  // 30: 4 workgroups per CU
     MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, 0, true, 0, "_kcd"),     // 31: 2 workgroups per CU
-    MFMA_CFG_KCD(128, 256, 32, 64, 128, 1, 4, false, 1, "_kcd"),    // 32: 1 workgroup per CU
+    MFMA_CFG_KCD(128, 256, 32, 64, 64, 2, 4, false, 2, "_w8_kcd"),  // 32: 8 waves, 2 per SIMD
     MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, 1, "_kcd"),       // 33: 4 workgroups per CU
     MFMA_CFG_KCD(128, 128, 64, 64, 32, 2, 4, false, 2, "_w8_kcd"),  // 34: 8 waves, 2 per SIMD
     MFMA_CFG_KCD(64, 64, 64, 32, 32, 2, 4, false, 1, "_kcd"),       // 35: 2 workgroups per CU
@@ -176,7 +176,7 @@ constexpr int kIlMid = 24;       // 128 x 128 x 32, two workgroups per CU
 constexpr int kKcHuge = 29;      // 256 x 256 x 32, 8 waves, one workgroup per CU
 constexpr int kKcLarge4 = 30;    // 128 x 128 x 16, four workgroups per CU
 constexpr int kKcShortK = 31;    // 128 x 256 x 16, two workgroups per CU
-constexpr int kKcWide = 32;      // 128 x 256 x 32, one workgroup per CU
+constexpr int kKcWide = 32;      // 128 x 256 x 32, 8 waves, one workgroup per CU
 constexpr int kKcSmall4 = 33;    // 64 x 64 x 32, four workgroups per CU
 constexpr int kKcDeep8 = 34;     // 128 x 128 x 64, 8 waves, one workgroup per CU
 constexpr int kKcSmall64 = 35;   // 64 x 64 x 64, two workgroups per CU
@@ -213,7 +213,8 @@ double quantization(long long t) {
 //     Among the shapes that qualify, what decides is the full-chip rate times
 //     the share of CUs the last round of tiles keeps busy.  Rates, TFLOP/s:
 //     256 x 256 x 32 (1 per CU) 146.5, 128 x 128 x 16 (4 per CU) 146,
-//     128 x 256 x 16 (2 per CU) 144, 128 x 256 x 32 (1 per CU) 142,
+//     128 x 256 x 16 (2 per CU) 144, 128 x 256 x 32 with 8 waves (1 per CU)
+//     143,
 //     128 x 128 x 32 (2 per CU) 140.5, 128 x 128 x 64 with 8 waves (1 per
 //     CU) 139, 64 x 64 x 32 (4 per CU) 134 (its rate at 2048^3-6144^3; it
 //     falls to 117-130 from 8192^3 up, where better-filled blocks win).  With K short the epilogue is a larger
@@ -225,8 +226,8 @@ double quantization(long long t) {
 //     256 x 256 blocks) take 256 x 256; 6144^3 to 10240^3 take
 //     128 x 128 x 16; 1024 x 8192 x 8192 (one 128 x 256 block per CU) takes
 //     128 x 256 x 32; 2048^3 (one 128 x 128 block per CU) 128 x 128 x 64;
-//     3072^3, 3840^3 and 5120^3 take 64 x 64 x 32 (5120^3: 135 against 128.5
-//     for 128 x 128 x 16); the low-K square takes 128 x 256 x 16;
+//     3072^3 and 5120^3 take 64 x 64 x 32 (5120^3: 135 against 128.5 for
+//     128 x 128 x 16); the low-K square takes 128 x 256 x 16;
 //   * below that the problem cannot fill the chip: 64 x 64 blocks, split
 //     along K when K is long (select_splits).  With at most one tile per CU
 //     the K-ordered 64 x 64 x 64 block, which halves the barriers per FLOP,
@@ -266,7 +267,7 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
         int min_k;           // shortest K at which that rate holds
     };
     static const Candidate cand[] = {{kKcHuge, 146.5, 1, 512},  {kKcLarge4, 146.0, 4, 256},
-                                     {kKcShortK, 144.0, 2, 0},  {kKcWide, 142.0, 1, 512},
+                                     {kKcShortK, 144.0, 2, 0},  {kKcWide, 143.0, 1, 512},
                                      {kIlMid, 140.5, 2, 256},   {kKcDeep8, 139.0, 1, 1024},
                                      {kKcSmall4, 134.0, 4, 0}};
     int best = -1, best_workers = 0;

@@ -9,6 +9,11 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
+    # Load (or compile) the oracle before any test touches the GPU: a compiler
+    # started from a process that has initialised the GPU would be a program
+    # started after GPU initialisation.
+    import oracle
+    oracle.default()
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line(
