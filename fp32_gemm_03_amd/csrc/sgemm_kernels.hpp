@@ -1268,7 +1268,8 @@ __device__ __forceinline__ void epilogue_mfma_kc(const Args &a, int bm, int bn, 
 // memory straight into LDS (16 bytes per lane when VEC == 4, else 4): the
 // next K tile's loads go after the MFMAs of the first quarter of the k-steps,
 // into the other LDS stage.  Same tiles and epilogue contract as sgemm_mfma;
-// the SPLIT build also runs split-K and stream-K (phases 0-3 of Args).
+// the SPLIT build also runs split-K and stream-K (phases 0-3 of Args).  RO
+// is the order of the fragment reads at a K tile's start (mfma_tile_kc).
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WM, int WN, int VEC, int WPE, bool SPLIT, int RO>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
