@@ -163,16 +163,15 @@ const Variant kVariants[] = {
     MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, 0, true, 0, "_kcd"),     // 31: 2 workgroups per CU
     MFMA_CFG_KCD(128, 256, 32, 64, 64, 2, 4, false, 2, "_w8_kcd"),  // 32: 8 waves, 2 per SIMD
     MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, 1, "_kcd"),       // 33: 4 workgroups per CU
-    MFMA_CFG_KCD(128, 128, 64, 64, 32, 2, 4, false, 2, "_w8_kcd"),  // 34: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(128, 128, 64, 32, 64, 2, 4, false, 2, "_w8_kcd"),  // 34: 8 waves, 2 per SIMD
     MFMA_CFG_KCD(64, 64, 64, 32, 32, 2, 4, false, 1, "_kcd"),       // 35: 2 workgroups per CU
+    MFMA_CFG_KCD(128, 128, 32, 64, 32, 4, 4, false, 2, "_w8_kcd"),  // 36: 8 waves, 2 workgroups per CU
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 constexpr int kValuDefault = 0;  // 128 x 128 x 16, 8 x 8 per lane, four workgroups per CU
 constexpr int kValuWide = 7;     // 128 x 256 x 16, 8 x 16 per lane, two workgroups per CU
-// the block on the interleaved schedule, A as is ...
-constexpr int kIlMid = 24;       // 128 x 128 x 32, two workgroups per CU
-// ... and with A in K order, loaded straight into LDS
+// the blocks with A in K order, loaded straight into LDS
 constexpr int kKcHuge = 29;      // 256 x 256 x 32, 8 waves, one workgroup per CU
 constexpr int kKcLarge4 = 30;    // 128 x 128 x 16, four workgroups per CU
 constexpr int kKcShortK = 31;    // 128 x 256 x 16, two workgroups per CU
@@ -180,6 +179,7 @@ constexpr int kKcWide = 32;      // 128 x 256 x 32, 8 waves, one workgroup per C
 constexpr int kKcSmall4 = 33;    // 64 x 64 x 32, four workgroups per CU
 constexpr int kKcDeep8 = 34;     // 128 x 128 x 64, 8 waves, one workgroup per CU
 constexpr int kKcSmall64 = 35;   // 64 x 64 x 64, two workgroups per CU
+constexpr int kKcMid8 = 36;      // 128 x 128 x 32, 8 waves, two workgroups per CU
 
 // Compute units of an MI355X; the choice of tile is a pure function of the
 // sizes so that it is the same on every call and testable without a GPU.
@@ -203,10 +203,11 @@ double quantization(long long t) {
 // 16384 x 1024 x 1024 both ways, 1000 x 1023 x 999, and split-K shapes):
 //   * blocks with A in K order, loaded straight into LDS, match or beat the
 //     same blocks on the interleaved schedule with A transposed (by 2-3% at
-//     128 x 128 x 16, up to 10% on 64 x 64 blocks), except 128 x 128 x 32,
-//     which keeps the interleaved schedule; at 128 x 128 x 64 the K-ordered
-//     block with 4 waves of 64 x 64 was 0.5-1% slower than the interleaved
-//     one, with 8 waves of 64 x 32 (two per SIMD) 1.5-2% faster;
+//     128 x 128 x 16, up to 10% on 64 x 64 blocks).  On the 128 x 128 x 32
+//     and 128 x 128 x 64 blocks that holds with 8 waves (two per SIMD):
+//     with 4 waves of 64 x 64 the K-ordered blocks were 0.5-1% slower than
+//     the interleaved ones, with 8 waves 1.5-3% faster (128 x 128 x 32:
+//     143.1 against 139.4 TFLOP/s at 4096^3, 143.9 against 140.2 at 6144^3);
 //   * a block shape reaches its full-chip rate only once there is a tile for
 //     every workgroup slot on the chip (slots = workgroups per CU x 256);
 //     below that its workgroups run alone on their CUs and latency shows.
@@ -214,10 +215,10 @@ double quantization(long long t) {
 //     the share of CUs the last round of tiles keeps busy.  Rates, TFLOP/s:
 //     256 x 256 x 32 (1 per CU) 146.5, 128 x 128 x 16 (4 per CU) 146,
 //     128 x 256 x 16 (2 per CU) 144, 128 x 256 x 32 with 8 waves (1 per CU)
-//     143,
-//     128 x 128 x 32 (2 per CU) 140.5, 128 x 128 x 64 with 8 waves (1 per
-//     CU) 139, 64 x 64 x 32 (4 per CU) 134 (its rate at 2048^3-6144^3; it
-//     falls to 117-130 from 8192^3 up, where better-filled blocks win).  With K short the epilogue is a larger
+//     143, 128 x 128 x 32 with 8 waves (2 per CU) 142.5, 128 x 128 x 64 with
+//     8 waves (1 per CU) 139.5, 64 x 64 x 32 (4 per CU) 134 (its rate at
+//     2048^3-6144^3; it falls to 117-130 from 8192^3 up, where better-filled
+//     blocks win).  With K short the epilogue is a larger
 //     share of a tile's time and blocks with more workgroups per CU, which
 //     hide one workgroup's epilogue under another's K loop, win: the
 //     one-per-CU blocks need K >= 512 and the 128 x 128 ones K >= 256 (at
@@ -235,12 +236,15 @@ double quantization(long long t) {
 //     1000 x 1023 x 999 77 against 71, 1024 x 1024 x 4096 109 against
 //     102); with more tiles, 64 x 64 x 32 at four workgroups per CU is
 //     (3072^3 121 against 116, 5120^3 131 against 125).
-// Stream-K (with a workspace): a block whose last round of tiles leaves
-// workgroup slots idle runs its whole rounds as usual and spreads the K tiles
-// of the rest over one workgroup per slot, so every slot ends at about the
-// same time.  Scored as the block's full-chip rate times kStreamKShare, the
-// measured cost of the partial tiles and their summing pass, when each
-// worker gets at least kStreamKMinK K tiles.
+// Stream-K (with a workspace): a block whose tiles do not divide evenly over
+// the CUs runs the whole rounds as usual and spreads the K tiles of the rest
+// over one worker per CU, so every CU ends at about the same time.  One per
+// CU also for the blocks that run two or four workgroups per CU: measured
+// 3-5% faster than one per workgroup slot at 3072^3 and 2560^2 x 4096 on
+// 128 x 128 x 32, and up to 1% at 5120^3-7168^3 on 128 x 128 x 16.  Scored
+// as the block's full-chip rate times kStreamKShare, the measured cost of the
+// partial tiles and their summing pass, when each worker gets at least
+// kStreamKMinK K tiles.
 constexpr double kStreamKShare = 0.985;
 constexpr int kStreamKMinK = 8;
 
@@ -268,7 +272,7 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
     };
     static const Candidate cand[] = {{kKcHuge, 146.5, 1, 512},  {kKcLarge4, 146.0, 4, 256},
                                      {kKcShortK, 144.0, 2, 0},  {kKcWide, 143.0, 1, 512},
-                                     {kIlMid, 140.5, 2, 256},   {kKcDeep8, 139.0, 1, 1024},
+                                     {kKcMid8, 142.5, 2, 256},  {kKcDeep8, 139.5, 1, 1024},
                                      {kKcSmall4, 134.0, 4, 0}};
     int best = -1, best_workers = 0;
     double best_score = -1.0;
@@ -279,11 +283,11 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
         if (t < slots || K < c.min_k) continue;
         double score = c.rate * quantization(t);
         int w = 0;
-        const long long rest = t % slots, kt = (K + v.bk - 1) / v.bk;
-        if (streamk && v.streamk && rest > 0 && rest * kt >= kStreamKMinK * slots &&
+        const long long rest = t % kComputeUnits, kt = (K + v.bk - 1) / v.bk;
+        if (streamk && v.streamk && rest > 0 && rest * kt >= kStreamKMinK * kComputeUnits &&
             c.rate * kStreamKShare > score) {
             score = c.rate * kStreamKShare;
-            w = (int)slots;
+            w = (int)kComputeUnits;
         }
         if (score > best_score) {
             best_score = score;
