@@ -166,6 +166,14 @@ const Variant kVariants[] = {
     MFMA_CFG_KCD(128, 128, 64, 32, 64, 2, 4, false, 2, "_w8_kcd"),  // 34: 8 waves, 2 per SIMD
     MFMA_CFG_KCD(64, 64, 64, 32, 32, 2, 4, false, 1, "_kcd"),       // 35: 2 workgroups per CU
     MFMA_CFG_KCD(128, 128, 32, 64, 32, 4, 4, false, 2, "_w8_kcd"),  // 36: 8 waves, 2 workgroups per CU
+    // 37: 29 with 16 waves of 64 x 64, four per SIMD, whole tiles only: its
+    // split builds would spill (55-96 registers at the 128-register cap), so
+    // split-K and stream-K stay with 29
+    {"mfma_256x256x32_w64x64_w16_kcd", SGEMM_PATH_MFMA, 256, 256, 32, 1024,
+     sgk::sgemm_mfma_kc<256, 256, 32, 64, 64, 4, 4, false, 2>,
+     sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, true, 1, 1, 0, false, 0, false, true>,
+     sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, false, 1, 1, 0, false, 0, false, true>,
+     nullptr, nullptr, 0, 1, 0},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -180,6 +188,7 @@ constexpr int kKcSmall4 = 33;    // 64 x 64 x 32, four workgroups per CU
 constexpr int kKcDeep8 = 34;     // 128 x 128 x 64, 8 waves, one workgroup per CU
 constexpr int kKcSmall64 = 35;   // 64 x 64 x 64, two workgroups per CU
 constexpr int kKcMid8 = 36;      // 128 x 128 x 32, 8 waves, two workgroups per CU
+constexpr int kKcHuge16 = 37;    // 256 x 256 x 32, 16 waves, one workgroup per CU, whole tiles only
 
 // Compute units of an MI355X; the choice of tile is a pure function of the
 // sizes so that it is the same on every call and testable without a GPU.
@@ -213,7 +222,9 @@ double quantization(long long t) {
 //     below that its workgroups run alone on their CUs and latency shows.
 //     Among the shapes that qualify, what decides is the full-chip rate times
 //     the share of CUs the last round of tiles keeps busy.  Rates, TFLOP/s:
-//     256 x 256 x 32 (1 per CU) 146.5, 128 x 128 x 16 (4 per CU) 146,
+//     256 x 256 x 32 with 16 waves (1 per CU) 147 (0.25-0.6% above 8 waves
+//     on whole rounds; no stream-K build), with 8 waves 146.5,
+//     128 x 128 x 16 (4 per CU) 146,
 //     128 x 256 x 16 (2 per CU) 144, 128 x 256 x 32 with 8 waves (1 per CU)
 //     143, 128 x 128 x 32 with 8 waves (2 per CU) 142.5, 128 x 128 x 64 with
 //     8 waves (1 per CU) 139.5, 64 x 64 x 32 (4 per CU) 134 (its rate at
@@ -270,7 +281,8 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
         int per_cu;          // workgroups resident per CU
         int min_k;           // shortest K at which that rate holds
     };
-    static const Candidate cand[] = {{kKcHuge, 146.5, 1, 512},  {kKcLarge4, 146.0, 4, 256},
+    static const Candidate cand[] = {{kKcHuge16, 147.0, 1, 512}, {kKcHuge, 146.5, 1, 512},
+                                     {kKcLarge4, 146.0, 4, 256},
                                      {kKcShortK, 144.0, 2, 0},  {kKcWide, 143.0, 1, 512},
                                      {kKcMid8, 142.5, 2, 256},  {kKcDeep8, 139.5, 1, 1024},
                                      {kKcSmall4, 134.0, 4, 0}};

@@ -95,7 +95,7 @@ def mfma_lds_per_wave(name, bm, bn, bk, threads, kt, mi):
 
 
 # the blocks the selection picks
-MFMA_CASES = [29, 30, 31, 32, 33, 34, 35, 36]
+MFMA_CASES = [29, 30, 31, 32, 33, 34, 35, 36, 37]
 # MFMA kernels whose every LDS access is its own instruction (none of the
 # chosen ones).  In the others the compiler fuses some pairs of fragment reads
 # into one ds_read2 / ds_read2st64 instruction, so the counter lies between
