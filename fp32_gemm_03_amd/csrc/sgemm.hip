@@ -224,7 +224,7 @@ double quantization(long long t) {
 //     the share of CUs the last round of tiles keeps busy.  Rates, TFLOP/s:
 //     256 x 256 x 32 with 16 waves (1 per CU) 147 (0.25-0.6% above 8 waves
 //     on whole rounds; no stream-K build), with 8 waves 146.5,
-//     128 x 128 x 16 (4 per CU) 146,
+//     128 x 128 x 16 (4 per CU) 144 (141-145.5 from 6144^3 to 14848^3),
 //     128 x 256 x 16 (2 per CU) 144, 128 x 256 x 32 with 8 waves (1 per CU)
 //     143, 128 x 128 x 32 with 8 waves (2 per CU) 142.5, 128 x 128 x 64 with
 //     8 waves (1 per CU) 139.5, 64 x 64 x 32 (4 per CU) 134 (its rate at
@@ -255,7 +255,11 @@ double quantization(long long t) {
 // 128 x 128 x 32, and up to 1% at 5120^3-7168^3 on 128 x 128 x 16.  Scored
 // as the block's full-chip rate times kStreamKShare, the measured cost of the
 // partial tiles and their summing pass, when each worker gets at least
-// kStreamKMinK K tiles.
+// kStreamKMinK K tiles.  So with a workspace the large squares whose
+// 256 x 256 tiles leave a partial round (of the cubes measured from 5120^3
+// to 14848^3, all but 8192^3 and 12288^3) run stream-K on 256 x 256 x 32 at
+// 141-146 TFLOP/s: 3-5% above the best whole-tile block, 1% at 12800^3,
+// level at 10240^3 and 0.4% below 128 x 128 x 16 at 6144^3.
 constexpr double kStreamKShare = 0.985;
 constexpr int kStreamKMinK = 8;
 
@@ -282,7 +286,7 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
         int min_k;           // shortest K at which that rate holds
     };
     static const Candidate cand[] = {{kKcHuge16, 147.0, 1, 512}, {kKcHuge, 146.5, 1, 512},
-                                     {kKcLarge4, 146.0, 4, 256},
+                                     {kKcLarge4, 144.0, 4, 256},
                                      {kKcShortK, 144.0, 2, 0},  {kKcWide, 143.0, 1, 512},
                                      {kKcMid8, 142.5, 2, 256},  {kKcDeep8, 139.5, 1, 1024},
                                      {kKcSmall4, 134.0, 4, 0}};

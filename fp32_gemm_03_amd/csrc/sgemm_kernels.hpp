@@ -653,11 +653,37 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
 // a contiguous run of the tile sequence, and the sequence then walks groups
 // of GROUP_M tile rows column by column, so the workgroups an XCD runs at
 // once share GROUP_M row blocks of A and a few column blocks of B.
+// ORDER 2: row-major as seen from each XCD.  With the tile columns a multiple
+// of 8, row-major dealing already gives XCD x the columns x, x + 8, ... in
+// every row, and this order is the same mapping.  Otherwise the column an
+// XCD receives shifts from row to row and the workgroups it runs at once
+// need up to 8 times as many B column blocks; here XCD x keeps the columns
+// x, x + 8, ... below 8 floor(nbn / 8) and walks them row by row, and the
+// remaining nbn mod 8 columns, row-major, are dealt out last in one
+// contiguous run per XCD.
 template <int ORDER, int GROUP_M>
 __device__ __forceinline__ void tile_of(int pid, int nbm, int nbn, int &tm, int &tn) {
-    if (ORDER == 0) {
+    const int c = nbn / 8, rem = nbn % 8;
+    if (ORDER == 0 || (ORDER == 2 && (rem == 0 || c == 0))) {
         tm = pid / nbn;
         tn = pid % nbn;
+        return;
+    }
+    if (ORDER == 2) {
+        const int total = nbm * nbn;
+        const int q = total / 8, r = total % 8;
+        const int x = pid % 8, idx = pid / 8;
+        const int common = nbm * c;  // tiles of XCD x in its own columns
+        if (idx < common) {
+            tm = idx / c;
+            tn = x + 8 * (idx - tm * c);
+            return;
+        }
+        // XCDs before x hold x q + min(x, r) ids, x * common of them in
+        // their own columns; the rest index the remaining columns' tiles
+        const int g = x * q + min(x, r) - x * common + (idx - common);
+        tm = g / rem;
+        tn = 8 * c + (g - tm * rem);
         return;
     }
     const int total = nbm * nbn;
@@ -1370,7 +1396,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     };
     auto origin = [&](int tile, int &bm, int &bn) {
         int tm, tn;
-        tile_of<0, 8>(tile, nbm, nbn, tm, tn);
+        tile_of<2, 8>(tile, nbm, nbn, tm, tn);
         bm = tm * BM;
         bn = tn * BN;
     };

@@ -505,6 +505,32 @@ def test_streamk_deterministic_reusable_and_exact(variant):
         assert np.all(out == 2000.0), workers
 
 
+def kcd_variants():
+    return [v for v in all_variants() if g.sgemm_variant_name(v).endswith("_kcd")]
+
+
+@pytest.mark.parametrize("variant", kcd_variants())
+def test_tile_order_with_ragged_tile_columns(variant):
+    """11 tile columns (8 + 3) and 3 tile rows, both ragged: the blocks with
+    A in K order keep each XCD on columns x, x + 8 and deal the last 3
+    columns out at the end, so every tile must still be computed exactly
+    once on whole tiles, split-K and stream-K (whole tiles first, then one
+    shared)."""
+    _, bm, bn = g.sgemm_variant_tile(variant)
+    M, N, K = 3 * bm - 5, 11 * bn - 7, 77
+    p = inputs.make_problem(M, N, K, dist="upm1", seed=M + N, alpha=1.25, beta=-0.5, c_fill="upm1")
+    ref_den = gu.oracle_full(p)
+    gu.say("ragged tile columns", M, N, K, g.sgemm_variant_name(variant))
+    out = gu.run(p, variant=variant)
+    assert gu.ratio_full(p, out, ref_den) <= TOL
+    if g.variant_has_splitk(variant):
+        out, _ = run_split(p, variant, 3)
+        assert gu.ratio_full(p, out, ref_den) <= TOL, "split-K"
+    if g.variant_has_streamk(variant):
+        out, _ = run_streamk(p, variant, 16)  # 33 tiles: 32 whole, 1 shared
+        assert gu.ratio_full(p, out, ref_den) <= TOL, "stream-K"
+
+
 @pytest.mark.parametrize("name", ["5120x5120x5120", "3072x3072x3072"])
 def test_sgemm_ws_streamk_full_size_sampled(name):
     """Shapes whose last round of tiles leaves slots idle: sgemm_ws shares
