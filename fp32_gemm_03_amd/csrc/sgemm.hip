@@ -168,9 +168,10 @@ const Variant kVariants[] = {
     MFMA_CFG_KCD(128, 128, 32, 64, 32, 4, 4, false, 2, "_w8_kcd"),  // 36: 8 waves, 2 workgroups per CU
     // 37: 29 with 16 waves of 64 x 64, four per SIMD, whole tiles only: its
     // split builds would spill (55-96 registers at the 128-register cap), so
-    // split-K and stream-K stay with 29
+    // split-K and stream-K stay with 29.  Wave priority falls over each K tile
+    // (PR 1).
     {"mfma_256x256x32_w64x64_w16_kcd", SGEMM_PATH_MFMA, 256, 256, 32, 1024,
-     sgk::sgemm_mfma_kc<256, 256, 32, 64, 64, 4, 4, false, 2>,
+     sgk::sgemm_mfma_kc<256, 256, 32, 64, 64, 4, 4, false, 2, 1>,
      sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, true, 1, 1, 0, false, 0, false, true>,
      sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, false, 1, 1, 0, false, 0, false, true>,
      nullptr, nullptr, 0, 1, 0},

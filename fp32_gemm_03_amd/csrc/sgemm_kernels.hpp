@@ -1181,7 +1181,7 @@ struct DirectStage {
 // block row 0 in this stage, a_off[q] is 4 * (position of chunk q of its
 // half); bp at B row lh * BK / 2, column wn + NI * li.  hook(j, u) as in
 // mfma_tile.
-template <int BK, int MI, int NI, int SB, int FD, int CH, int RO, class Hook>
+template <int BK, int MI, int NI, int SB, int FD, int CH, int RO, int PR, class Hook>
 __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_off)[BK / 8], const float *bp,
                                              floatx16 (&acc)[MI][NI], floatx16 (&acc_odd)[MI][NI], Hook hook) {
     typedef typename vec_t<NI>::type VB;
@@ -1189,6 +1189,10 @@ __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_o
     constexpr int RING = FD + 1;
     float4 av[2][MI];
     VB bv[RING];
+    if (PR == 1) {
+        __builtin_amdgcn_s_setprio(3);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     // At the tile's start every wave of the workgroup reads LDS at once.
     // RO == 0: the first group of four k's of A, the B fragments and the
     // next group of A, all before the first MFMA.  RO == 1: the B fragment
@@ -1201,6 +1205,15 @@ __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_o
     // both are 11% slower on 128 x 128 x 16 at four workgroups per CU where
     // the last round of tiles is partial (6144^3, 5120^3) and 0.4-1% slower
     // on 128 x 256 x 16 at 16384^2 x 128; no cause was found for those two.
+    // PR == 1: the wave's issue priority falls from 3 to 0 over the K tile
+    // (3 - 4q / QN at A group q), so of the waves on a SIMD the one furthest
+    // behind in the tile issues first and they reach the closing barrier
+    // closer together.  On the 256 x 256 x 32 block with 16 waves (four per
+    // SIMD, one workgroup per CU) that is 0.1-0.3% faster in every one of 16
+    // paired runs at 4096^3-16384^3.  It is level on the 8-wave blocks with
+    // one workgroup per CU and up to 23% slower on blocks with two or four
+    // per CU where the last round of tiles is partial, so only that block
+    // uses it.
     if (RO == 0) {
 #pragma unroll
     for (int i = 0; i < MI; ++i) av[0][i] = *reinterpret_cast<const float4 *>(a_row + i * 32 * BK + a_off[0]);
@@ -1230,6 +1243,13 @@ __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_o
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int j = 4 * q + e;
+            if (PR == 1 && e == 0 && q > 0 && (4 * q) / QN != (4 * (q - 1)) / QN) {
+                const int level = 3 - (4 * q) / QN;
+                if (level == 2) __builtin_amdgcn_s_setprio(2);
+                else if (level == 1) __builtin_amdgcn_s_setprio(1);
+                else __builtin_amdgcn_s_setprio(0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             if (RO == 0 && e == 0 && q + 1 < QN) {
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
@@ -1295,9 +1315,10 @@ __device__ __forceinline__ void epilogue_mfma_kc(const Args &a, int bm, int bn, 
 // next K tile's loads go after the MFMAs of the first quarter of the k-steps,
 // into the other LDS stage.  Same tiles and epilogue contract as sgemm_mfma;
 // the SPLIT build also runs split-K and stream-K (phases 0-3 of Args).  RO
-// is the order of the fragment reads at a K tile's start (mfma_tile_kc).
+// is the order of the fragment reads at a K tile's start and PR the wave
+// priority over a K tile (mfma_tile_kc).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, int VEC, int WPE, bool SPLIT, int RO>
+template <int BM, int BN, int BK, int WM, int WN, int VEC, int WPE, bool SPLIT, int RO, int PR = 0>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -1380,7 +1401,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
                     }
                 }
             };
-            mfma_tile_kc<BK, MI, NI, SB, 1, CH, RO>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
+            mfma_tile_kc<BK, MI, NI, SB, 1, CH, RO, PR>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
         };
         for (int t = 0; t < KT; ++t) {
             tile_body(smem + (t & 1) * STAGE, smem + ((t + 1) & 1) * STAGE, kb + (t + 1) * BK);
