@@ -1209,8 +1209,9 @@ __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_o
     // (3 - 4q / QN at A group q), so of the waves on a SIMD the one furthest
     // behind in the tile issues first and they reach the closing barrier
     // closer together.  On the 256 x 256 x 32 block with 16 waves (four per
-    // SIMD, one workgroup per CU) that is 0.1-0.3% faster in every one of 16
-    // paired runs at 4096^3-16384^3.  It is level on the 8-wave blocks with
+    // SIMD, one workgroup per CU) that is 0.1-0.6% faster in every one of 24
+    // paired runs at 4096^3-16384^3, and faster than priority 3 for the first
+    // quarter or half of the tile only.  It is level on the 8-wave blocks with
     // one workgroup per CU and up to 23% slower on blocks with two or four
     // per CU where the last round of tiles is partial, so only that block
     // uses it.
