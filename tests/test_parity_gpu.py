@@ -531,12 +531,14 @@ def test_tile_order_with_ragged_tile_columns(variant):
         assert gu.ratio_full(p, out, ref_den) <= TOL, "stream-K"
 
 
-@pytest.mark.parametrize("name", ["5120x5120x5120", "3072x3072x3072"])
+@pytest.mark.parametrize("name", ["5120x5120x5120", "3072x3072x3072", "13824x13824x13824"])
 def test_sgemm_ws_streamk_full_size_sampled(name):
     """Shapes whose last round of tiles leaves slots idle: sgemm_ws shares
     the K tiles of the rest over one worker per slot (checked on sampled
     points against the oracle), and with no workspace falls back to whole
-    tiles."""
+    tiles.  At 13824^3 neither tile grid has a multiple of 8 columns (54 of
+    256 x 256, 108 of 128 x 128), so both runs take the per-XCD column
+    order."""
     M, N, K = (int(x) for x in name.split("x"))
     p = inputs.make_problem(M, N, K, dist="normal", seed=37, alpha=0.75, beta=0.5, c_fill="upm1")
     workers = g.sgemm_select_streamk(M, N, K)
