@@ -110,13 +110,14 @@ struct Variant {
 // than that at 8192^3 (140 against 146 TFLOP/s).  Those two sum the k of a
 // K tile in the same order as each other, the 128-bit builds in another.
 // RO is the order of the LDS fragment reads at a K tile's start
-// (mfma_tile_kc), chosen per block by measurement.
+// (mfma_tile_kc), chosen per block by measurement.  All four builds map
+// workgroups to tiles with tile_of<2, 8> (each XCD on its own tile columns).
 #define MFMA_CFG_KCD(BM, BN, BK, WM, WN, WPE, PA, SWZ, RO, SUFFIX)                      \
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
      (BM / WM) * (BN / WN) * 64,                                                         \
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO>,                          \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 1, 0, false, 0, SWZ, true>, \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, 1, 0, false, 0, SWZ, true>, \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 1, 2, false, 0, SWZ, true>, \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, 1, 2, false, 0, SWZ, true>, \
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO>,                           \
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 1, WPE, true, RO>, 0, 1, 1}
 
@@ -172,8 +173,8 @@ const Variant kVariants[] = {
     // (PR 1).
     {"mfma_256x256x32_w64x64_w16_kcd", SGEMM_PATH_MFMA, 256, 256, 32, 1024,
      sgk::sgemm_mfma_kc<256, 256, 32, 64, 64, 4, 4, false, 2, 1>,
-     sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, true, 1, 1, 0, false, 0, false, true>,
-     sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, false, 1, 1, 0, false, 0, false, true>,
+     sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, true, 1, 1, 2, false, 0, false, true>,
+     sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, false, 1, 1, 2, false, 0, false, true>,
      nullptr, nullptr, 0, 1, 0},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);

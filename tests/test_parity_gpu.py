@@ -509,20 +509,24 @@ def kcd_variants():
     return [v for v in all_variants() if g.sgemm_variant_name(v).endswith("_kcd")]
 
 
+@pytest.mark.parametrize("aligned", [True, False])
 @pytest.mark.parametrize("variant", kcd_variants())
-def test_tile_order_with_ragged_tile_columns(variant):
+def test_tile_order_with_ragged_tile_columns(variant, aligned):
     """11 tile columns (8 + 3) and 3 tile rows, both ragged: the blocks with
     A in K order keep each XCD on columns x, x + 8 and deal the last 3
     columns out at the end, so every tile must still be computed exactly
-    once on whole tiles, split-K and stream-K (whole tiles first, then one
-    shared)."""
+    once, by every build: each access mode the operands allow (aligned:
+    the 128-bit build too), split-K and stream-K (whole tiles first, then
+    one shared)."""
     _, bm, bn = g.sgemm_variant_tile(variant)
-    M, N, K = 3 * bm - 5, 11 * bn - 7, 77
+    M, N, K = (3 * bm - 5, 11 * bn - 8, 76) if aligned else (3 * bm - 5, 11 * bn - 7, 77)
     p = inputs.make_problem(M, N, K, dist="upm1", seed=M + N, alpha=1.25, beta=-0.5, c_fill="upm1")
     ref_den = gu.oracle_full(p)
     gu.say("ragged tile columns", M, N, K, g.sgemm_variant_name(variant))
-    out = gu.run(p, variant=variant)
-    assert gu.ratio_full(p, out, ref_den) <= TOL
+    modes = gu.allowed_accesses(p, variant=variant)
+    assert (g.SGEMM_ACCESS_BUFFER_128 in modes) == aligned
+    for acc, out in run_all_modes(p, variant):
+        assert gu.ratio_full(p, out, ref_den) <= TOL, gu.ACCESS_NAMES[acc]
     if g.variant_has_splitk(variant):
         out, _ = run_split(p, variant, 3)
         assert gu.ratio_full(p, out, ref_den) <= TOL, "split-K"
