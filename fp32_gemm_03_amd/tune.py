@@ -6,7 +6,8 @@ shape's fastest variant with the one the library's selection picks.
 A shape is a named synthetic workload (``square8192_normal`` ...) or MxNxK
 (A, B ~ N(0,1), seed 3, alpha 1, beta 0).  Every launch goes through the C
 ABI on one stream; the time per launch is HIP events around a run of
-launches after about 30 ms of untimed ones.  Besides the forced variants,
+launches after about 30 ms of untimed ones (0.5 s after the GPU has idled,
+so that the clock has ramped up).  Besides the forced variants,
 two rows time the library's own choice: ``auto`` (``sgemm``) and ``auto+ws``
 (``sgemm_ws`` with the workspace it asks for, which may split K or share the
 K tiles of a last partial round of tiles over stream-K workers).  The last block is a table of the selection
@@ -21,6 +22,7 @@ from __future__ import annotations
 import argparse
 import json
 import sys
+import time
 
 DEFAULT_SHAPES = [
     "square256_u01", "ragged_1000x1023x999", "square1024_normal", "square2048_normal",
@@ -38,11 +40,21 @@ def _problem(shape):
     return inputs.make_problem(M, N, K, dist="normal", seed=3, name=shape)
 
 
+_last_timed = None  # time.monotonic() at the end of the previous _time
+
+
 def _time(launch, flops, stream, target_s=0.1, warmup_s=0.03):
     """Mean ms per launch and TFLOP/s over about target_s of launches, after
     about warmup_s of untimed ones (a fixed time rather than a count, so that
-    the clock has settled whatever the launch length)."""
+    the clock has settled whatever the launch length).  After the GPU has
+    idled (the first timing of a process, or a pause of over 0.5 s while the
+    next shape's inputs are made) the warm-up is at least 0.5 s: from idle the
+    clock takes longer than 30 ms to ramp up, and the first variant timed on
+    2048^3 ran 3-4% slow without it."""
     import torch
+    global _last_timed
+    if _last_timed is None or time.monotonic() - _last_timed > 0.5:
+        warmup_s = max(warmup_s, 0.5)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     launch()
@@ -64,6 +76,7 @@ def _time(launch, flops, stream, target_s=0.1, warmup_s=0.03):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    _last_timed = time.monotonic()
     return ms, flops / (ms * 1e-3) / 1e12
 
 
