@@ -24,7 +24,7 @@ __all__ = [
     "SGEMM_ACCESS_CHECKED", "sgemm_variant_access",
     "sgemm_ws", "sgemm_workspace_size", "sgemm_select_splits", "sgemm_splitk",
     "sgemm_splitk_workspace_size", "sgemm_streamk", "sgemm_streamk_workspace_size",
-    "sgemm_select_streamk", "sgemm_ws_plan",
+    "sgemm_select_streamk", "sgemm_ws_plan", "sgemm_select_rows",
     "SgemmError", "LibraryNotBuilt", "library_path", "load_library",
     "sgemm", "sgemm_path", "sgemm_variant", "sgemm_variant_count",
     "sgemm_variant_name", "sgemm_variant_path", "sgemm_variant_tile", "sgemm_variant_reads_a128",
@@ -99,6 +99,8 @@ def load_library():
         lib.sgemm_streamk_workspace_size.restype = ctypes.c_size_t
         lib.sgemm_select_streamk.argtypes = [i, i, i]
         lib.sgemm_select_streamk.restype = i
+        lib.sgemm_select_rows.argtypes = [i, i, i]
+        lib.sgemm_select_rows.restype = i
         lib.sgemm_ws_plan.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
         lib.sgemm_ws_plan.restype = i
         lib.sgemm_variant_count.argtypes = []
@@ -223,6 +225,11 @@ def sgemm_streamk_workspace_size(variant, workers) -> int:
 
 def sgemm_select_streamk(M, N, K) -> int:
     return int(load_library().sgemm_select_streamk(int(M), int(N), int(K)))
+
+
+def sgemm_select_rows(M, N, K) -> int:
+    """Rows of C that ``sgemm`` runs as a first launch of 256 x 256 tiles (0: one launch)."""
+    return int(load_library().sgemm_select_rows(int(M), int(N), int(K)))
 
 
 def sgemm_ws_plan(M, N, K):

@@ -265,8 +265,17 @@ double quantization(long long t) {
 constexpr double kStreamKShare = 0.985;
 constexpr int kStreamKMinK = 8;
 
-int choose(int path, int M, int N, int K, bool streamk, int *workers) {
+// Candidate rates, TFLOP/s, of the two 256 x 256 x 32 blocks and of 64 x 64
+// blocks that cannot fill the chip (256 rows of 7168^2 x 7168 ran 114 on
+// 64 x 64 x 32; 1024^3 runs 96 on 64 x 64 x 64).
+constexpr double kHuge16Rate = 147.0;
+constexpr double kSmallRate = 110.0;
+
+// The variant for a whole-tile (or, with streamk, stream-K) launch; *score
+// gets its predicted TFLOP/s (rate x the busy share of the last round).
+int choose(int path, int M, int N, int K, bool streamk, int *workers, double *score_out = nullptr) {
     if (workers) *workers = 0;
+    if (score_out) *score_out = 0.0;
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
@@ -287,7 +296,7 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
         int per_cu;          // workgroups resident per CU
         int min_k;           // shortest K at which that rate holds
     };
-    static const Candidate cand[] = {{kKcHuge16, 147.0, 1, 512}, {kKcHuge, 146.5, 1, 512},
+    static const Candidate cand[] = {{kKcHuge16, kHuge16Rate, 1, 512}, {kKcHuge, 146.5, 1, 512},
                                      {kKcLarge4, 144.0, 4, 256},
                                      {kKcShortK, 144.0, 2, 0},  {kKcWide, 143.0, 1, 512},
                                      {kKcMid8, 142.5, 2, 256},  {kKcDeep8, 139.5, 1, 1024},
@@ -321,6 +330,7 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
         // select_splits may split K.
         const Variant &v = kVariants[kKcSmall4];
         const long long t = tiles(M, N, v.bm, v.bn), rest = t % kComputeUnits;
+        if (score_out) *score_out = kSmallRate;
         if (t <= kComputeUnits) return kKcSmall64;
         const long long kt = (K + v.bk - 1) / v.bk;
         if (streamk && workers && rest > 0 && rest * kt >= kStreamKMinK * kComputeUnits)
@@ -328,10 +338,47 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers) {
         return kKcSmall4;
     }
     if (workers) *workers = best_workers;
+    if (score_out) *score_out = best_score;
     return best;
 }
 
 int select_variant(int path, int M, int N, int K) { return choose(path, M, N, K, false, nullptr); }
+
+// Without a workspace there is no stream-K, and a partial last round of
+// tiles leaves CUs idle.  C can instead be split by rows into two launches:
+// the first 256 r rows as 256 x 256 tiles that fill their rounds (at least
+// 96% of the last one busy), and the rest with the block chosen for it.
+// Returns those first rows, or 0 when one launch is predicted within 2% of
+// the best split.  Measured at 7168^3, 9216^3 and 11264^3: 143.4, 143.7 and
+// 144.5 TFLOP/s against 136.4, 139.1 and 140.2 for one launch (the split the
+// model picks there was within 1% of the best one tried).  Only bottom parts
+// of up to 64 block rows are tried.
+int split_rows(int M, int N, int K) {
+    if (K < 512 || M < 512) return 0;
+    double single = 0.0;
+    if (choose(SGEMM_PATH_AUTO, M, N, K, false, nullptr, &single) < 0 || single <= 0.0) return 0;
+    const long long nbn = (N + 255) / 256;
+    const double per_row = 2.0 * N * (double)K;
+    const double t_single = per_row * M / single;
+    double best_t = t_single;
+    int best_rows = 0;
+    const long long r_hi = (M - 1) / 256, r_lo = r_hi > 64 ? r_hi - 64 : 1;
+    for (long long r = r_hi; r >= r_lo; --r) {
+        const long long t = r * nbn;
+        if (t < kComputeUnits) break;
+        const double q = quantization(t);
+        if (q < 0.96) continue;
+        const int m1 = (int)(r * 256), m2 = M - m1;
+        double s2 = 0.0;
+        if (choose(SGEMM_PATH_AUTO, m2, N, K, false, nullptr, &s2) < 0 || s2 <= 0.0) continue;
+        const double t_split = per_row * m1 / (kHuge16Rate * q) + per_row * m2 / s2;
+        if (t_split < best_t) {
+            best_t = t_split;
+            best_rows = m1;
+        }
+    }
+    return best_t < 0.98 * t_single ? best_rows : 0;
+}
 
 // Split count for a variant when a workspace is available (measured on
 // MI355X: 512 x 512 x 8192 runs 3.5x faster in 8 parts, 768^3 13% faster in
@@ -494,6 +541,19 @@ int launch(int variant, int access, int splits, int workers, void *workspace, si
     return err == hipSuccess ? SGEMM_OK : (int)err;
 }
 
+// C split by rows: rows [0, rows) on the 16-wave 256 x 256 block, the rest
+// with the block chosen for it, one launch each on the same stream.
+int launch_rows(int rows, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+                int ldb, float beta, float *C, int ldc, hipStream_t stream) {
+    int rc = launch(kKcHuge16, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, rows, N, K, alpha, A, lda, B, ldb,
+                    beta, C, ldc, stream);
+    if (rc != SGEMM_OK) return rc;
+    const int v2 = select_variant(SGEMM_PATH_AUTO, M - rows, N, K);
+    if (v2 < 0) return v2;
+    return launch(v2, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M - rows, N, K, alpha,
+                  A + (size_t)rows * lda, lda, B, ldb, beta, C + (size_t)rows * ldc, ldc, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -511,6 +571,10 @@ int sgemm_path(int path, int M, int N, int K, float alpha, const float *A,
     if (rc != SGEMM_OK) return rc;
     const int v = select_variant(path, M, N, K);
     if (v < 0) return v;
+    if (path != SGEMM_PATH_VALU) {
+        const int rows = split_rows(M, N, K);
+        if (rows > 0) return launch_rows(rows, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    }
     return launch(v, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                   stream);
 }
@@ -577,6 +641,13 @@ int sgemm_ws_plan(int M, int N, int K, int *variant, int *splits, int *workers) 
     return SGEMM_OK;
 }
 
+int sgemm_select_rows(int M, int N, int K) {
+    if (M < 0) return -1;
+    if (N < 0) return -2;
+    if (K < 0) return -3;
+    return split_rows(M, N, K);
+}
+
 int sgemm_select_streamk(int M, int N, int K) {
     int workers = 0;
     const int v = choose(SGEMM_PATH_AUTO, M, N, K, true, &workers);
@@ -610,6 +681,10 @@ int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const fl
     int sp = select_splits(v, M, N, K);
     if (sp > 1 && (!room || workspace_bytes < splitk_bytes(kVariants[v], sp, M, N)))
         sp = 1;  // not enough workspace: the unsplit kernel
+    if (sp == 1) {
+        const int rows = split_rows(M, N, K);
+        if (rows > 0) return launch_rows(rows, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    }
     return launch(v, SGEMM_ACCESS_AUTO, sp, 0, workspace, workspace_bytes, M, N, K, alpha, A, lda, B,
                   ldb, beta, C, ldc, stream);
 }

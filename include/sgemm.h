@@ -79,7 +79,10 @@ extern "C" {
 #define SGEMM_ERR_WORKSPACE (-24)
 #define SGEMM_ERR_SPLITS (-25)
 
-/* C = alpha*A*B + beta*C, automatic choice of inner product and tile. */
+/* C = alpha*A*B + beta*C, automatic choice of inner product and tile.  One
+ * kernel launch, or two on the same stream when sgemm_select_rows() is
+ * positive (C split by rows, each part a whole product of its own; nothing
+ * allocated, no order between the parts' results). */
 int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
           const float *B, int ldb, float beta, float *C, int ldc,
           hipStream_t stream);
@@ -217,8 +220,20 @@ int sgemm_variant_tile(int variant, int *bm, int *bn);
 int sgemm_variant_reads_a128(int variant);
 
 /* The variant sgemm_path(path, M, N, K, ...) launches for these sizes, or a
- * negative code (-1..-3, SGEMM_ERR_PATH).  Host logic only, no HIP call. */
+ * negative code (-1..-3, SGEMM_ERR_PATH).  Host logic only, no HIP call.
+ * When sgemm_select_rows() is positive, an AUTO or MFMA call runs another
+ * plan (below). */
 int sgemm_select_variant(int path, int M, int N, int K);
+
+/* Rows of C that sgemm() (path AUTO or MFMA), and sgemm_ws() when it
+ * neither splits K nor runs stream-K, compute as a first launch of 256 x 256
+ * tiles that fill their rounds of the 256 compute units; the rows below
+ * follow in a second launch with the variant
+ * sgemm_select_variant(path, M - rows, N, K).  0: one launch.  A multiple
+ * of 256 below M, or a negative argument code (-1..-3).  Host logic only.
+ * (Quantisation of tiles over the compute units: "如何高效实现矩阵乘？CUDA
+ * 初学者的角度入门", section "Wave & L2 cache Hit Rate".) */
+int sgemm_select_rows(int M, int N, int K);
 
 /* Static text for a status code returned by any entry point above. */
 const char *sgemm_status_string(int status);

@@ -240,6 +240,31 @@ def test_streamk_host_logic():
     assert call(v, 3, ws=0x10010) == -24                # not 256-byte aligned
 
 
+def test_row_split_host_logic():
+    """Without a workspace, a partial last round of 256 x 256 tiles is
+    avoided by a first launch over the rows whose tiles fill their rounds
+    (7168^3: 27 block rows of 28 tiles, 756 = 2.95 rounds); the rows below
+    go to a second launch.  Whole rounds, short K and small shapes keep one
+    launch."""
+    for M, N, K, rows in [(7168, 7168, 7168, 6912), (9216, 9216, 9216, 8960),
+                          (13824, 13824, 13824, 13312)]:
+        got = g.sgemm_select_rows(M, N, K)
+        assert got == rows, (M, N, K, got)
+        t = (got // 256) * ((N + 255) // 256)
+        assert t / (-(-t // 256) * 256) >= 0.96  # busy share of the rounds
+    for M, N, K in [(8192, 8192, 8192), (4096, 4096, 4096), (16384, 16384, 16384), (6144, 6144, 6144),
+                    (5120, 5120, 5120), (16384, 16384, 128), (1024, 8192, 8192), (1000, 1023, 999),
+                    (256, 256, 256), (0, 8192, 8192), (8192, 0, 8192), (8192, 8192, 0)]:
+        assert g.sgemm_select_rows(M, N, K) == 0, (M, N, K)
+    for M in range(512, 20000, 509):
+        for N in (3000, 7168, 11000):
+            r = g.sgemm_select_rows(M, N, 4096)
+            assert r == 0 or (r % 256 == 0 and 0 < r < M), (M, N, r)
+    assert g.sgemm_select_rows(-1, 4, 4) == -1
+    assert g.sgemm_select_rows(4, -1, 4) == -2
+    assert g.sgemm_select_rows(4, 4, -1) == -3
+
+
 def test_only_the_latency_block_splits_k():
     """A block chosen by rate already has a tile per workgroup slot on the
     chip; only the 64 x 64 fallbacks split K when a workspace is given."""

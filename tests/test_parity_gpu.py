@@ -535,21 +535,29 @@ def test_tile_order_with_ragged_tile_columns(variant, aligned):
         assert gu.ratio_full(p, out, ref_den) <= TOL, "stream-K"
 
 
-@pytest.mark.parametrize("name", ["5120x5120x5120", "3072x3072x3072", "13824x13824x13824"])
+@pytest.mark.parametrize("name", ["5120x5120x5120", "3072x3072x3072", "13824x13824x13824",
+                                  "7168x7168x7168"])
 def test_sgemm_ws_streamk_full_size_sampled(name):
     """Shapes whose last round of tiles leaves slots idle: sgemm_ws shares
     the K tiles of the rest over one worker per slot (checked on sampled
-    points against the oracle), and with no workspace falls back to whole
-    tiles.  At 13824^3 neither tile grid has a multiple of 8 columns (54 of
-    256 x 256, 108 of 128 x 128), so both runs take the per-XCD column
-    order."""
+    points against the oracle).  With no workspace it runs whole tiles, at
+    13824^3 and 7168^3 split by rows into two launches (the two rows at the
+    split are checked in full).  At 13824^3 neither tile grid has a multiple
+    of 8 columns (54 of 256 x 256, 108 of 128 x 128), so both runs take the
+    per-XCD column order."""
     M, N, K = (int(x) for x in name.split("x"))
     p = inputs.make_problem(M, N, K, dist="normal", seed=37, alpha=0.75, beta=0.5, c_fill="upm1")
     workers = g.sgemm_select_streamk(M, N, K)
     assert workers > 0
+    split = g.sgemm_select_rows(M, N, K)
+    assert (split > 0) == (M in (13824, 7168)), split
     need = g.sgemm_workspace_size(M, N, K)
     ws = torch.full((need // 4 + 64,), float("nan"), dtype=torch.float32, device="cuda")
     rows, cols = inputs.sample_points(M, N, n_random=2048, seed=41)
+    if split > 0:
+        edge = np.repeat(np.array([split - 1, split]), N)
+        rows = np.concatenate([rows, edge])
+        cols = np.concatenate([cols, np.tile(np.arange(N), 2)])
     for workspace in (ws, None):
         oa, _, a = gu.to_gpu(p.A)
         ob, _, b = gu.to_gpu(p.B)
