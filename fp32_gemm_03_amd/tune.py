@@ -130,8 +130,14 @@ def tune(shapes, variants=None, out=sys.stdout, vendor=False):
             print(f"{shape:24s} {name:34s} {tf:8.2f} TFLOP/s {ms:10.4f} ms", file=out, flush=True)
         forced = {k: v for k, v in rows.items() if k not in ("auto", "auto+ws", "vendor_blas")}
         best = min(forced, key=lambda k: forced[k][0])
+        selected = g.sgemm_variant_name(auto)
+        rows_first = g.sgemm_select_rows(p.M, p.N, p.K)
+        if rows_first > 0:  # C split by rows: two launches
+            rest = g.sgemm_select_variant(g.SGEMM_PATH_AUTO, p.M - rows_first, p.N, p.K)
+            selected = (f"rows 0..{rows_first - 1} as 256 x 256 tiles, "
+                        f"rest: {g.sgemm_variant_name(rest)}")
         table.append({"shape": shape, "M": p.M, "N": p.N, "K": p.K,
-                      "selected": g.sgemm_variant_name(auto), "selected_ws": g.sgemm_variant_name(ws_variant),
+                      "selected": selected, "selected_ws": g.sgemm_variant_name(ws_variant),
                       "splits": splits, "workers": workers,
                       "auto_ms": rows["auto"][0], "auto_ws_ms": rows["auto+ws"][0],
                       "best": best, "best_ms": forced[best][0],
