@@ -8,7 +8,8 @@ It wraps ``oracle_sgemm.c`` (plain C, float64 sums, POSIX threads), which
 follows the plain definition of the naive GEMM in "如何高效实现矩阵乘？CUDA初学者的
 角度入门", section "樸素 GEMM 與前置知識": C = alpha * (A @ B) + beta * C on
 row-major matrices, alpha applied once to the finished dot product.  With
-beta == 0 the input C is not read.
+beta == 0 the input C is not read; with alpha == 0 neither A nor B is read
+(the product term is dropped, so the result is beta * C exactly).
 
 The pass rule used against it is ``max |C_gpu - ref| / den``, with
 ``den = |alpha| * sum_k |A_ik||B_kj| + |beta||C_ij| + 1e-30``; see

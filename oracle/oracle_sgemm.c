@@ -18,8 +18,10 @@
  *     S_ij      = sum_{k=0..K-1} (double)A[i][k] * (double)B[k][j]
  *   with the sum formed from 0.0 in ascending k.  The beta term is dropped
  *   when beta == 0 (BLAS convention: C is then not read, so NaN or Inf in C
- *   does not propagate).  Element (r, c) of a matrix with leading dimension
- *   ld sits at r*ld + c.
+ *   does not propagate), and the alpha term is dropped when alpha == 0 (the
+ *   same convention for A and B: they are not read, so NaN or Inf in them
+ *   does not propagate and ref = beta * C).  Element (r, c) of a matrix
+ *   with leading dimension ld sits at r*ld + c.
  *
  *   Every product of two floats is exact in double (24 + 24 < 53 significand
  *   bits); only the sums and the two scalings round.
@@ -58,7 +60,7 @@ int oracle_nthreads(void)
     return n > 0 ? (int)n : 1;
 }
 
-static int bad_args(int M, int N, int K, const float *A, int lda,
+static int bad_args(int M, int N, int K, float alpha, const float *A, int lda,
                     const float *B, int ldb, float beta, const float *C,
                     int ldc)
 {
@@ -66,7 +68,7 @@ static int bad_args(int M, int N, int K, const float *A, int lda,
         return 1;
     if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
         return 1;
-    if ((M > 0 && K > 0 && A == NULL) || (K > 0 && N > 0 && B == NULL))
+    if (alpha != 0.0f && ((M > 0 && K > 0 && A == NULL) || (K > 0 && N > 0 && B == NULL)))
         return 1;
     if (beta != 0.0f && M > 0 && N > 0 && C == NULL)
         return 1;
@@ -101,7 +103,9 @@ static void *run_band(void *arg)
             sum[j] = 0.0;
             abs_sum[j] = 0.0;
         }
-        for (int k = 0; k < b->K; ++k) {
+        /* alpha == 0: the product term is dropped and A, B are not read */
+        const int nk = b->alpha != 0.0 ? b->K : 0;
+        for (int k = 0; k < nk; ++k) {
             const double a = (double)b->A[(size_t)i * b->lda + k];
             const float *brow = b->B + (size_t)k * b->ldb;
             for (int j = 0; j < N; ++j) {
@@ -135,7 +139,7 @@ int oracle_sgemm_rows(int M, int N, int K, float alpha, const float *A, int lda,
                       int ldc, int row0, int nrows, double *ref, double *den,
                       int nthreads)
 {
-    if (bad_args(M, N, K, A, lda, B, ldb, beta, C, ldc))
+    if (bad_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc))
         return -1;
     if (row0 < 0 || nrows < 0 || row0 > M || nrows > M - row0)
         return -1;
@@ -200,7 +204,7 @@ int oracle_sgemm_points(int M, int N, int K, float alpha, const float *A,
                         const float *C, int ldc, int npts, const int *rows,
                         const int *cols, double *ref, double *den)
 {
-    if (bad_args(M, N, K, A, lda, B, ldb, beta, C, ldc) || npts < 0)
+    if (bad_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc) || npts < 0)
         return -1;
     if (npts == 0)
         return 0;
@@ -211,7 +215,9 @@ int oracle_sgemm_points(int M, int N, int K, float alpha, const float *A,
         if (i < 0 || i >= M || j < 0 || j >= N)
             return -1;
         double s = 0.0, s_abs = 0.0;
-        for (int k = 0; k < K; ++k) {
+        /* alpha == 0: the product term is dropped and A, B are not read */
+        const int kend = alpha != 0.0f ? K : 0;
+        for (int k = 0; k < kend; ++k) {
             const double prod = (double)A[(size_t)i * lda + k] * (double)B[(size_t)k * ldb + j];
             s += prod;
             s_abs += fabs(prod);

@@ -9,8 +9,9 @@ raises ``AssertionError`` when that oracle disagrees with:
 * exact rational arithmetic (``fractions.Fraction``) on tiny shapes, with wide
   leading dimensions whose pad columns hold NaN;
 * numpy's float64 ``matmul`` of the up-cast inputs (a library routine);
-* invariants of the definition: identity, K = 1, power-of-two alpha, alpha = 0,
-  beta = 0 with NaN in C (C not read), transposition, and that the two entry
+* invariants of the definition: identity, K = 1, power-of-two alpha, alpha = 0
+  with NaN and Inf in A and B (A and B not read), beta = 0 with NaN in C (C
+  not read), transposition, and that the two entry
   points, every thread count and every row band give the same sums bit for bit.
 
 They are run against the real oracle by ``test_oracle.py`` and against
@@ -171,6 +172,22 @@ def pin_invariants(api, seed=99):
     assert np.array_equal(d8 - 1e-30, 8.0 * (d1 - 1e-30)), "alpha = 8, den"
     r0, _ = api.sgemm(M, N, K, 0.0, A, K, B, N, -0.5, C, N)
     assert np.array_equal(r0, -0.5 * C.reshape(M, N).astype(np.float64)), "alpha = 0"
+
+    # alpha = 0: A and B are not read, so NaN and Inf in them do not reach the
+    # result, which is beta*C exactly (0 with beta = 0), in both entry points
+    Abad = np.where(np.arange(M * K) % 2 == 0, np.nan, np.inf).astype(np.float32)
+    Bbad = np.full(K * N, np.nan, dtype=np.float32)
+    want = -0.5 * C.reshape(M, N).astype(np.float64)
+    want_den = 0.5 * np.abs(C.reshape(M, N).astype(np.float64)) + 1e-30
+    rz, dz = api.sgemm(M, N, K, 0.0, Abad, K, Bbad, N, -0.5, C, N)
+    assert np.array_equal(rz, want) and np.array_equal(dz, want_den), "alpha = 0, NaN A and B"
+    rows, cols = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+    pz, pdz = api.sgemm_points(M, N, K, 0.0, Abad, K, Bbad, N, -0.5, C, N,
+                               rows.reshape(-1), cols.reshape(-1))
+    assert np.array_equal(pz.reshape(M, N), want) and np.array_equal(pdz.reshape(M, N), want_den), \
+        "alpha = 0, NaN A and B, points"
+    rzz, _ = api.sgemm(M, N, K, 0.0, Abad, K, Bbad, N, 0.0, _nan_c(M, N), N)
+    assert np.all(rzz == 0.0), "alpha = beta = 0 with NaN everywhere"
 
     # beta = 0: C is not read, so NaN in C does not reach the result
     Cnan = np.full(M * N, np.nan, dtype=np.float32)

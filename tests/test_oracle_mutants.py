@@ -20,7 +20,8 @@ from tests import oracle_pins as pins
 
 MUTANTS = {
     # row entry (i-k-j walk)
-    "rows_drop_last_k": ("for (int k = 0; k < b->K; ++k) {", "for (int k = 0; k + 1 < b->K; ++k) {"),
+    "rows_drop_last_k": ("for (int k = 0; k < nk; ++k) {", "for (int k = 0; k + 1 < nk; ++k) {"),
+    "rows_product_at_alpha_zero": ("const int nk = b->alpha != 0.0 ? b->K : 0;", "const int nk = b->K;"),
     "rows_beta_sign": ("r += b->beta * c;", "r -= b->beta * c;"),
     "rows_transposed_B": ("const double p = a * (double)brow[j];",
                           "const double p = a * (double)b->B[(size_t)j * b->ldb + k];"),
@@ -33,7 +34,8 @@ MUTANTS = {
     "rows_float_accumulator": ("sum[j] += p;", "sum[j] = (float)(sum[j] + p);"),
     # point entry (one dot product per element)
     "points_transposed_B": ("(double)B[(size_t)k * ldb + j]", "(double)B[(size_t)j * ldb + k]"),
-    "points_skip_first_k": ("for (int k = 0; k < K; ++k) {", "for (int k = 1; k < K; ++k) {"),
+    "points_skip_first_k": ("for (int k = 0; k < kend; ++k) {", "for (int k = 1; k < kend; ++k) {"),
+    "points_product_at_alpha_zero": ("const int kend = alpha != 0.0f ? K : 0;", "const int kend = K;"),
     "points_beta_uses_alpha": ("r += (double)beta * c;", "r += (double)alpha * c;"),
     "points_ldc_is_N": ("(double)C[(size_t)i * ldc + j]", "(double)C[(size_t)i * N + j]"),
 }
