@@ -28,6 +28,10 @@ steps bracketed by device synchronisation; one JSON line on stdout.
   parity     = those oracle rows against the same rows of C after the first
                launch (from the workload's initial C), copied back before the
                warm-up: max error ratio and the 1e-5 pass rule.
+               Every secondary entry carries its own cpu_baseline and parity:
+               the oracle on the whole problem (its time, and every element
+               of C after the first launch against it), or, at 16384^3, on a
+               band of the first rows, labelled in its "sample".
   clocks     = the shader clock level sysfs reports for each GPU just before and
                after the timed run.
 """
@@ -66,6 +70,12 @@ WORKLOAD = "square8192_normal"
 # peak and its algorithmic bytes at the HBM peak, and the rest of the sweep.
 SECONDARY = ("square4096_upm1", "lowk_16384x16384x128", "square256_u01", "ragged_1000x1023x999",
              "square1024_normal", "square2048_normal", "square16384_normal")
+# Each secondary workload is checked against the oracle too: the whole
+# problem, except where that takes minutes of host time (16384^3, about
+# 3 minutes on 16 cores), where a band of the first rows is used, labelled so.
+BAND_ONLY = ("square16384_normal",)
+BAND_SECONDS = 6.0
+BAND_CAPTURE_ROWS = 2048
 
 
 def _code_tokens(text: str) -> str:
@@ -168,37 +178,45 @@ def time_gpu(p, steps, warmup, path, variant=None, min_warmup_s=0.0, per_launch=
     return total_ms, per_launch_ms, wall
 
 
-def cpu_baseline(p, target_s=10.0, gpu_rows=None):
-    """The oracle timed on a band of rows 0..r-1; with gpu_rows (the GPU's first
-    rows of C), also the parity of those rows against the same oracle rows."""
+def cpu_baseline(p, target_s=10.0, gpu_rows=None, full=False):
+    """The oracle timed on the whole problem (full) or on a band of rows
+    0..r-1 sized to about target_s seconds; with gpu_rows (the GPU's first
+    rows of C after its first launch), also the parity of those rows against
+    the same oracle rows."""
     import oracle
 
     A, B = p.np("A"), p.np("B")
     Cin = p.np("C") if p.beta != 0 else None
     cores = oracle.nthreads()
-    rows = max(8, min(cores, p.M))
-    t0 = time.perf_counter()
-    oracle.sgemm_rows(p.M, p.N, p.K, p.alpha, A, p.lda, B, p.ldb, p.beta, Cin, p.ldc, 0, rows)
-    t_probe = time.perf_counter() - t0
-    rows2 = int(max(rows, min(p.M, rows * target_s / max(t_probe, 1e-3))))
-    rows2 = max(rows, (rows2 // cores) * cores)
+    if full:
+        rows2 = p.M
+    else:
+        rows = max(8, min(cores, p.M))
+        t0 = time.perf_counter()
+        oracle.sgemm_rows(p.M, p.N, p.K, p.alpha, A, p.lda, B, p.ldb, p.beta, Cin, p.ldc, 0, rows)
+        t_probe = time.perf_counter() - t0
+        rows2 = int(max(rows, min(p.M, rows * target_s / max(t_probe, 1e-3))))
+        rows2 = min(p.M, max(rows, (rows2 // cores) * cores))
     t0 = time.perf_counter()
     ref, den = oracle.sgemm_rows(p.M, p.N, p.K, p.alpha, A, p.lda, B, p.ldb, p.beta, Cin, p.ldc, 0, rows2)
     t = time.perf_counter() - t0
     flops = 2.0 * rows2 * p.N * p.K
+    sample = (f"the whole {p.M}x{p.N}x{p.K} problem ({rows2 * p.N} elements, float64 i-k-j loop), "
+              f"{t:.1f} s" if rows2 == p.M else
+              f"rows 0..{rows2 - 1} of the {p.M}x{p.N}x{p.K} problem "
+              f"({rows2 * p.N} elements, float64 i-k-j loop), {t:.1f} s")
     out = {"value": round(flops / t / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-           "kind": "oracle",
-           "sample": f"rows 0..{rows2 - 1} of the {p.M}x{p.N}x{p.K} problem "
-                     f"({rows2 * p.N} elements, float64 i-k-j loop), {t:.1f} s",
-           "seconds": round(t, 3)}
+           "kind": "oracle", "sample": sample, "seconds": round(t, 3)}
     parity = None
     if gpu_rows is not None:
         r = min(rows2, gpu_rows.shape[0])
         err = oracle.max_error_ratio(gpu_rows[:r], ref[:r], den[:r])
         parity = {"rows": r, "elements": r * p.N, "max_err_ratio": err, "tolerance": TOLERANCE,
                   "pass": bool(err <= TOLERANCE),
-                  "against": "the oracle's rows of the CPU baseline; C after the first launch "
-                             "from the workload's initial C"}
+                  "against": ("every element of the oracle's result" if r == p.M else
+                              "the oracle's rows of the CPU baseline") +
+                             "; C after the first launch from the workload's initial C"}
+    del ref, den
     return out, parity
 
 
@@ -328,13 +346,17 @@ def main():
             p2 = inputs.workload_problem(name)
             w2 = inputs.WORKLOADS[name]
             steps2 = max(args.steps, 100)
-            t2, _, _ = time_gpu(p2, steps2, args.warmup, path, args.variant, min_warmup_s=0.05,
-                                per_launch=False)
+            full = name not in BAND_ONLY
+            cap2 = 0 if args.no_cpu_baseline else (p2.M if full else BAND_CAPTURE_ROWS)
+            print(f"bench: secondary {name}, {steps2} timed", file=sys.stderr, flush=True)
+            timed2 = time_gpu(p2, steps2, args.warmup, path, args.variant, min_warmup_s=0.05,
+                              per_launch=False, capture_rows=cap2)
+            t2 = timed2[0]
             v2 = g.sgemm_select_variant(path, p2.M, p2.N, p2.K) if args.variant is None else args.variant
             sec_s = t2 / steps2 / 1e3
             t_fp32 = w2.flops / (PEAK_FP32_TFLOPS * 1e12)
             t_hbm = w2.algorithmic_bytes / (PEAK_HBM_GBS * 1e9)
-            out["secondary"].append({
+            entry = {
                 "workload": name, "variant": g.sgemm_variant_name(v2),
                 "value": round(w2.flops / sec_s / 1e12, 3), "unit": "TFLOP/s",
                 "ms_per_step": round(sec_s * 1e3, 4), "steps": steps2,
@@ -342,8 +364,14 @@ def main():
                 "hbm_gbs": round(w2.algorithmic_bytes / sec_s / 1e9, 1),
                 "pct_of_hbm_peak": round(100.0 * t_hbm / sec_s, 2),
                 "roofline_bound": "mfma" if t_fp32 >= t_hbm else "hbm",
-                "frac_of_roofline": round(max(t_fp32, t_hbm) / sec_s, 4)})
-            del p2
+                "frac_of_roofline": round(max(t_fp32, t_hbm) / sec_s, 4)}
+            if cap2:
+                print(f"bench: oracle on {name} ({'whole problem' if full else 'row band'})",
+                      file=sys.stderr, flush=True)
+                entry["cpu_baseline"], entry["parity"] = cpu_baseline(
+                    p2, target_s=BAND_SECONDS, gpu_rows=timed2[3], full=full)
+            out["secondary"].append(entry)
+            del p2, timed2
     if not args.no_cpu_baseline:
         out["cpu_baseline"], out["parity"] = cpu_baseline(p, gpu_rows=first_rows)
     out["clocks"] = {"before": clocks_before, "after": clocks_after,

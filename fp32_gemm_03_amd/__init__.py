@@ -24,7 +24,8 @@ __all__ = [
     "SGEMM_ACCESS_CHECKED", "sgemm_variant_access",
     "sgemm_ws", "sgemm_workspace_size", "sgemm_select_splits", "sgemm_splitk",
     "sgemm_splitk_workspace_size", "sgemm_streamk", "sgemm_streamk_workspace_size",
-    "sgemm_select_streamk", "sgemm_ws_plan", "sgemm_select_rows",
+    "sgemm_select_streamk", "sgemm_ws_plan", "sgemm_select_rows", "sgemm_plan_for",
+    "sgemm_device_shape", "sgemm_tile_order",
     "SgemmError", "LibraryNotBuilt", "library_path", "load_library",
     "sgemm", "sgemm_path", "sgemm_variant", "sgemm_variant_count",
     "sgemm_variant_name", "sgemm_variant_path", "sgemm_variant_tile", "sgemm_variant_reads_a128",
@@ -103,6 +104,12 @@ def load_library():
         lib.sgemm_select_rows.restype = i
         lib.sgemm_ws_plan.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i), ctypes.POINTER(i)]
         lib.sgemm_ws_plan.restype = i
+        lib.sgemm_plan_for.argtypes = [i, i, i, i, i] + [ctypes.POINTER(i)] * 4
+        lib.sgemm_plan_for.restype = i
+        lib.sgemm_device_shape.argtypes = [ctypes.POINTER(i), ctypes.POINTER(i)]
+        lib.sgemm_device_shape.restype = i
+        lib.sgemm_tile_order.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+        lib.sgemm_tile_order.restype = i
         lib.sgemm_variant_count.argtypes = []
         lib.sgemm_variant_count.restype = i
         lib.sgemm_variant_name.argtypes = [i]
@@ -238,6 +245,32 @@ def sgemm_ws_plan(M, N, K):
     rc = load_library().sgemm_ws_plan(int(M), int(N), int(K), ctypes.byref(v), ctypes.byref(sp),
                                       ctypes.byref(w))
     return int(rc), v.value, sp.value, w.value
+
+
+def sgemm_plan_for(compute_units, M, N, K, with_workspace=False):
+    """``(status, variant, splits, workers, rows)``: the plan for these sizes on a device of
+    ``compute_units`` CUs (``sgemm_ws`` with enough workspace, or ``sgemm`` without)."""
+    v, sp, w, r = ctypes.c_int(-1), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    rc = load_library().sgemm_plan_for(int(compute_units), int(M), int(N), int(K),
+                                       1 if with_workspace else 0, ctypes.byref(v),
+                                       ctypes.byref(sp), ctypes.byref(w), ctypes.byref(r))
+    return int(rc), v.value, sp.value, w.value, r.value
+
+
+def sgemm_device_shape():
+    """``(compute_units, xcds)`` the current device's choices use."""
+    cu, x = ctypes.c_int(0), ctypes.c_int(0)
+    load_library().sgemm_device_shape(ctypes.byref(cu), ctypes.byref(x))
+    return cu.value, x.value
+
+
+def sgemm_tile_order(xcds, nbm, nbn):
+    """``(status, tile_m, tile_n)``: the tile each workgroup of an nbm x nbn grid computes."""
+    n = max(int(nbm) * int(nbn), 0)
+    tm = (ctypes.c_int * max(n, 1))()
+    tn = (ctypes.c_int * max(n, 1))()
+    rc = load_library().sgemm_tile_order(int(xcds), int(nbm), int(nbn), tm, tn)
+    return int(rc), list(tm)[:n], list(tn)[:n]
 
 
 def variant_has_streamk(variant) -> bool:

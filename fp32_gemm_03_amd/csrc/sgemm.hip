@@ -2,14 +2,17 @@
 // argument checks, the table of compiled kernel variants, the shape-based
 // choice of variant, and the launch on the caller's stream.
 //
-// The library holds no state: every call validates, picks a variant and
-// enqueues one kernel (two for split-K: the partial tiles, then their sum in
-// a fixed order).  Nothing here allocates device memory; split-K writes its
-// partial tiles to a workspace the caller owns.
+// The only state is a per-device cache of the machine shape (compute units
+// and XCDs), read once.  Every call validates, picks a variant and enqueues
+// one kernel (two for split-K and stream-K: the partial tiles, then their sum
+// in a fixed order).  Nothing here allocates device memory; split-K writes
+// its partial tiles to a workspace the caller owns.
 #include "sgemm.h"
 
 #include <limits.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "sgemm_kernels.hpp"
 
@@ -29,78 +32,28 @@ struct Variant {
     KernelFn generic;   // per-element checked pointer accesses (any leading dimension)
     KernelFn split4;    // split-K, as vec4 (nullptr: no split-K build of this variant)
     KernelFn split1;    // split-K, as vec1
-    int persistent;     // 0: one workgroup per tile; n: a persistent grid of n workgroups per CU
     int a128;           // 1: the vec4 build also reads A 128 bits at a time along K
     int streamk;        // 1: the split builds also run stream-K (phases 2 and 3)
 };
 
-// VALU: 128 x 128 x 16 block, 4 waves of 64 x 64, 8 x 8 per lane.
+// VALU: BM x BN x BK block, waves of (8 TM) x (8 TN), TM x TN per lane.
 #define VALU_CFG(BM, BN, BK, TM, TN, PA, PB, WPE)                                       \
     {"valu_" #BM "x" #BN "x" #BK "_t" #TM "x" #TN, SGEMM_PATH_VALU, BM, BN, BK,           \
      (BM / (8 * TM)) * (BN / (8 * TN)) * 64,                                             \
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 4, WPE, true>,                       \
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, true>,                       \
-     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, false>, nullptr, nullptr}
+     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, false>, nullptr, nullptr, 0, 0}
 
-#define MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, VEC, WPE, BUF, PD, FD, ORD, SPLIT)          \
-    sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, VEC, WPE, BUF, PD, FD, ORD, SPLIT, 0, false>
-
-// A variant with the LDS-staged epilogue (no split-K build).
-#define MFMA_CFG_STAGED_EPI(BM, BN, BK, WM, WN, PA, PB, WPE, PD, FD, SUFFIX)             \
+// A register-staged MFMA block (sgemm_mfma), A transposed in LDS: padded by
+// PA, or unpadded and XOR-swizzled (SWZ); EPI 1 stages the epilogue through
+// LDS; ORD is the workgroup -> tile order.
+#define MFMA_CFG(BM, BN, BK, WM, WN, PA, WPE, ORD, EPI, SWZ, SUFFIX)                     \
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
      (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD, 0, false, 1, false>, \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD, 0, false, 1, false>, \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, PB, 1, WPE, false, PD, FD, 0, false, 1, false>, \
-     nullptr, nullptr}
-
-// A variant with A unpadded in LDS and its columns XOR-swizzled per row.
-#define MFMA_CFG_SWIZZLED_A(BM, BN, BK, WM, WN, WPE, PD, FD, SUFFIX)                     \
-    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
-     (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, 0, 0, 4, WPE, true, PD, FD, 0, false, 0, true>,  \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, 0, 0, 1, WPE, true, PD, FD, 0, false, 0, true>,  \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, 0, 0, 1, WPE, false, PD, FD, 0, false, 0, true>, \
-     nullptr, nullptr}
-
-// A persistent variant (A XOR-swizzled): WPC workgroups per CU walk the
-// tiles, each retiring one tile's epilogue during the next tile's K loop.
-#define MFMA_CFG_PERSISTENT(BM, BN, BK, WM, WN, WPE, FD, SL, WPC, SUFFIX)                 \
-    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
-     (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma_persistent<BM, BN, BK, WM, WN, 0, 0, 4, WPE, true, FD, true, SL>,   \
-     sgk::sgemm_mfma_persistent<BM, BN, BK, WM, WN, 0, 0, 1, WPE, true, FD, true, SL>,   \
-     sgk::sgemm_mfma_persistent<BM, BN, BK, WM, WN, 0, 0, 1, WPE, false, FD, true, SL>,  \
-     nullptr, nullptr, WPC}
-
-#define MFMA_CFG(BM, BN, BK, WM, WN, PA, PB, WPE, PD, FD, ORD, SUFFIX)                   \
-    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
-     (BM / WM) * (BN / WN) * 64,                                                         \
-     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD, ORD, false),          \
-     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD, ORD, false),          \
-     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 1, WPE, false, PD, FD, ORD, false),         \
-     nullptr, nullptr}
-
-// The same, also compiled with split-K.
-#define MFMA_CFG_SPLIT(BM, BN, BK, WM, WN, PA, PB, WPE, PD, FD, ORD, SUFFIX)             \
-    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
-     (BM / WM) * (BN / WN) * 64,                                                         \
-     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD, ORD, false),          \
-     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD, ORD, false),          \
-     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 1, WPE, false, PD, FD, ORD, false),         \
-     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 4, WPE, true, PD, FD, ORD, true),           \
-     MFMA_KERNEL(BM, BN, BK, WM, WN, PA, PB, 1, WPE, true, PD, FD, ORD, true)}
-
-// A variant on the interleaved schedule (A padded by 4 or XOR-swizzled),
-// also compiled with split-K.
-#define MFMA_CFG_IL(BM, BN, BK, WM, WN, PA, WPE, SWZ, SUFFIX)                           \
-    {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
-     (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 4, WPE, true, 1, 1, 0, false, 0, SWZ, true>,  \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 1, 0, false, 0, SWZ, true>,  \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, 1, 0, false, 0, SWZ, true>, \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 4, WPE, true, 1, 1, 0, true, 0, SWZ, true>,   \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 1, 0, true, 0, SWZ, true>}
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 4, WPE, true, 1, ORD, EPI, SWZ, false>,  \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, ORD, EPI, SWZ, false>,  \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, ORD, EPI, SWZ, false>, \
+     nullptr, nullptr, 0, 0}
 
 // A variant with A kept in K order (sgemm_mfma_kc): its 128-bit builds load
 // straight into LDS; also compiled with split-K and stream-K (32-bit split
@@ -116,97 +69,124 @@ struct Variant {
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
      (BM / WM) * (BN / WN) * 64,                                                         \
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO>,                          \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 1, 2, false, 0, SWZ, true>, \
-     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, 1, 2, false, 0, SWZ, true>, \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 2, 0, SWZ, true>,       \
+     sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, 2, 0, SWZ, true>,      \
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO>,                           \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 1, WPE, true, RO>, 0, 1, 1}
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 1, WPE, true, RO>, 1, 1}
 
+// The table holds the blocks the choice by shape can pick (the VALU pair and
+// the K-ordered blocks) and the alternatives kept for measurement: the
+// XCD-grouped tile order, the LDS-staged epilogue and A unpadded with an XOR
+// swizzle, each on the register-staged 128 x 256 / 256 x 128 x 16 blocks.
 const Variant kVariants[] = {
-    VALU_CFG(128, 128, 16, 8, 8, 4, 0, 4),                     // 0
-    MFMA_CFG(256, 256, 32, 128, 128, 4, 0, 1, 1, 1, 0, ""),       // 1: 4 waves, 1 per SIMD, 512 registers
-    MFMA_CFG_SPLIT(128, 128, 32, 64, 64, 4, 0, 2, 1, 1, 0, ""),   // 2
-    MFMA_CFG_SPLIT(64, 64, 32, 32, 32, 4, 0, 2, 1, 1, 0, ""),     // 3
-    MFMA_CFG(256, 256, 32, 128, 64, 4, 0, 2, 1, 1, 0, ""),        // 4: 8 waves, 2 per SIMD
-    MFMA_CFG(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, 0, ""),        // 5: 4 waves, 2 workgroups per CU
-    MFMA_CFG(128, 256, 16, 64, 128, 4, 0, 2, 1, 1, 0, ""),        // 6: 4 waves, 2 workgroups per CU
-    VALU_CFG(128, 256, 16, 8, 16, 4, 0, 2),                    // 7: 8 x 16 per lane
-    VALU_CFG(256, 128, 16, 16, 8, 4, 0, 2),                    // 8: 16 x 8 per lane
-    MFMA_CFG_SPLIT(64, 64, 32, 32, 32, 4, 0, 2, 2, 3, 0, "_pf2_fd3"), // 9: 2 K tiles in flight, fragments 3 steps ahead
-    MFMA_CFG_SPLIT(64, 64, 64, 32, 32, 4, 0, 2, 1, 3, 0, "_fd3"),     // 10: fragments 3 steps ahead
-    MFMA_CFG(128, 128, 32, 64, 64, 4, 0, 2, 2, 2, 0, "_pf2_fd2"), // 11
-    MFMA_CFG(128, 256, 16, 64, 128, 4, 0, 2, 1, 1, 1, "_xcd"),    // 12: 6 in XCD-grouped tile order
-    MFMA_CFG(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, 1, "_xcd"),    // 13: 5 in XCD-grouped tile order
-    MFMA_CFG_STAGED_EPI(128, 256, 16, 64, 128, 4, 0, 2, 1, 1, "_ldsepi"), // 14: 6 with the LDS-staged epilogue
-    MFMA_CFG_STAGED_EPI(256, 128, 16, 128, 64, 4, 0, 2, 1, 1, "_ldsepi"), // 15: 5 with the LDS-staged epilogue
-    MFMA_CFG_SWIZZLED_A(128, 256, 16, 64, 128, 2, 1, 1, "_xorA"),         // 16: 6, A unpadded and XOR-swizzled
-    MFMA_CFG_SWIZZLED_A(64, 64, 64, 32, 32, 2, 1, 3, "_fd3_xorA"),        // 17: 10, A unpadded and XOR-swizzled
-    MFMA_CFG_SWIZZLED_A(128, 128, 32, 64, 64, 2, 1, 1, "_xorA"),          // 18: 2, A unpadded and XOR-swizzled
-    MFMA_CFG_SWIZZLED_A(128, 128, 16, 64, 64, 4, 1, 1, "_wpe4_xorA"),     // 19: 4 workgroups per CU
-    // 20: persistent with the deferred epilogue.  Measured: low K 16384^2 x 128
-    // 0.71 ms against 0.67 for 16, and 10% below 19 where the epilogue does
-    // not matter, so it is not chosen by shape.
-    MFMA_CFG_PERSISTENT(128, 128, 16, 64, 64, 2, 1, 8, 2, "_persist"),
-    // 21: variant 1 with the next K tile's loads and LDS stores interleaved
-    // into the MFMA sequence (one workgroup per CU, so nothing else hides them)
-    {"mfma_256x256x32_w128x128_il", SGEMM_PATH_MFMA, 256, 256, 32, 256,
-     sgk::sgemm_mfma<256, 256, 32, 128, 128, 4, 0, 4, 1, true, 1, 1, 0, false, 0, false, true>,
-     sgk::sgemm_mfma<256, 256, 32, 128, 128, 4, 0, 1, 1, true, 1, 1, 0, false, 0, false, true>,
-     sgk::sgemm_mfma<256, 256, 32, 128, 128, 4, 0, 1, 1, false, 1, 1, 0, false, 0, false, true>, nullptr, nullptr},
-    MFMA_CFG_IL(256, 256, 32, 128, 64, 4, 2, false, "_il"),      // 22: 8 waves, 2 per SIMD
-    MFMA_CFG_IL(128, 128, 16, 64, 64, 4, 4, false, "_wpe4_il"),  // 23: 4 workgroups per CU
-    MFMA_CFG_IL(128, 128, 32, 64, 64, 4, 2, false, "_il"),       // 24: 2 workgroups per CU
-    MFMA_CFG_IL(128, 256, 16, 64, 128, 0, 2, true, "_il_xorA"),  // 25: 2 workgroups per CU
-    MFMA_CFG_IL(128, 256, 32, 64, 128, 4, 1, false, "_il"),      // 26: 1 workgroup per CU
-    MFMA_CFG_IL(64, 64, 32, 32, 32, 4, 4, false, "_il"),         // 27: 4 workgroups per CU
-    MFMA_CFG_IL(128, 128, 64, 64, 64, 4, 1, false, "_il"),       // 28: 1 workgroup per CU
-    MFMA_CFG_KCD(256, 256, 32, 128, 64, 2, 4, false, 2, "_kcd"),    // 29: 8 waves, 2 per SIMD
-    MFMA_CFG_KCD(128, 128, 16, 64, 64, 4, 4, false, 0, "_wpe4_kcd"),  // 30: 4 workgroups per CU
-    MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, 0, true, 0, "_kcd"),     // 31: 2 workgroups per CU
-    MFMA_CFG_KCD(128, 256, 32, 64, 64, 2, 4, false, 2, "_w8_kcd"),  // 32: 8 waves, 2 per SIMD
-    MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, 1, "_kcd"),       // 33: 4 workgroups per CU
-    MFMA_CFG_KCD(128, 128, 64, 32, 64, 2, 4, false, 2, "_w8_kcd"),  // 34: 8 waves, 2 per SIMD
-    MFMA_CFG_KCD(64, 64, 64, 32, 32, 2, 4, false, 1, "_kcd"),       // 35: 2 workgroups per CU
-    MFMA_CFG_KCD(128, 128, 32, 64, 32, 4, 4, false, 2, "_w8_kcd"),  // 36: 8 waves, 2 workgroups per CU
-    // 37: 29 with 16 waves of 64 x 64, four per SIMD, whole tiles only: its
+    VALU_CFG(128, 128, 16, 8, 8, 4, 0, 4),                         // 0: 8 x 8 per lane
+    VALU_CFG(128, 256, 16, 8, 16, 4, 0, 2),                        // 1: 8 x 16 per lane
+    MFMA_CFG(128, 256, 16, 64, 128, 4, 2, 1, 0, false, "_xcd"),    // 2: XCD-grouped tile order
+    MFMA_CFG(256, 128, 16, 128, 64, 4, 2, 1, 0, false, "_xcd"),    // 3: XCD-grouped tile order
+    MFMA_CFG(128, 256, 16, 64, 128, 4, 2, 0, 1, false, "_ldsepi"), // 4: LDS-staged epilogue
+    MFMA_CFG(256, 128, 16, 128, 64, 4, 2, 0, 1, false, "_ldsepi"), // 5: LDS-staged epilogue
+    MFMA_CFG(128, 256, 16, 64, 128, 0, 2, 0, 0, true, "_xorA"),    // 6: A unpadded, XOR-swizzled
+    MFMA_CFG_KCD(256, 256, 32, 128, 64, 2, 4, false, 2, "_kcd"),    // 7: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(128, 128, 16, 64, 64, 4, 4, false, 0, "_wpe4_kcd"),  // 8: 4 workgroups per CU
+    MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, 0, true, 0, "_kcd"),     // 9: 2 workgroups per CU
+    MFMA_CFG_KCD(128, 256, 32, 64, 64, 2, 4, false, 2, "_w8_kcd"),  // 10: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, 1, "_kcd"),       // 11: 4 workgroups per CU
+    MFMA_CFG_KCD(128, 128, 64, 32, 64, 2, 4, false, 2, "_w8_kcd"),  // 12: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(64, 64, 64, 32, 32, 2, 4, false, 1, "_kcd"),       // 13: 2 workgroups per CU
+    MFMA_CFG_KCD(128, 128, 32, 64, 32, 4, 4, false, 2, "_w8_kcd"),  // 14: 8 waves, 2 workgroups per CU
+    // 15: 7 with 16 waves of 64 x 64, four per SIMD, whole tiles only: its
     // split builds would spill (55-96 registers at the 128-register cap), so
-    // split-K and stream-K stay with 29.  Wave priority falls over each K tile
+    // split-K and stream-K stay with 7.  Wave priority falls over each K tile
     // (PR 1).
     {"mfma_256x256x32_w64x64_w16_kcd", SGEMM_PATH_MFMA, 256, 256, 32, 1024,
      sgk::sgemm_mfma_kc<256, 256, 32, 64, 64, 4, 4, false, 2, 1>,
-     sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, true, 1, 1, 2, false, 0, false, true>,
-     sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, false, 1, 1, 2, false, 0, false, true>,
-     nullptr, nullptr, 0, 1, 0},
+     sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, true, 1, 2, 0, false, true>,
+     sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, false, 1, 2, 0, false, true>,
+     nullptr, nullptr, 1, 0},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
 constexpr int kValuDefault = 0;  // 128 x 128 x 16, 8 x 8 per lane, four workgroups per CU
-constexpr int kValuWide = 7;     // 128 x 256 x 16, 8 x 16 per lane, two workgroups per CU
+constexpr int kValuWide = 1;     // 128 x 256 x 16, 8 x 16 per lane, two workgroups per CU
 // the blocks with A in K order, loaded straight into LDS
-constexpr int kKcHuge = 29;      // 256 x 256 x 32, 8 waves, one workgroup per CU
-constexpr int kKcLarge4 = 30;    // 128 x 128 x 16, four workgroups per CU
-constexpr int kKcShortK = 31;    // 128 x 256 x 16, two workgroups per CU
-constexpr int kKcWide = 32;      // 128 x 256 x 32, 8 waves, one workgroup per CU
-constexpr int kKcSmall4 = 33;    // 64 x 64 x 32, four workgroups per CU
-constexpr int kKcDeep8 = 34;     // 128 x 128 x 64, 8 waves, one workgroup per CU
-constexpr int kKcSmall64 = 35;   // 64 x 64 x 64, two workgroups per CU
-constexpr int kKcMid8 = 36;      // 128 x 128 x 32, 8 waves, two workgroups per CU
-constexpr int kKcHuge16 = 37;    // 256 x 256 x 32, 16 waves, one workgroup per CU, whole tiles only
+constexpr int kKcHuge = 7;       // 256 x 256 x 32, 8 waves, one workgroup per CU
+constexpr int kKcLarge4 = 8;     // 128 x 128 x 16, four workgroups per CU
+constexpr int kKcShortK = 9;     // 128 x 256 x 16, two workgroups per CU
+constexpr int kKcWide = 10;      // 128 x 256 x 32, 8 waves, one workgroup per CU
+constexpr int kKcSmall4 = 11;    // 64 x 64 x 32, four workgroups per CU
+constexpr int kKcDeep8 = 12;     // 128 x 128 x 64, 8 waves, one workgroup per CU
+constexpr int kKcSmall64 = 13;   // 64 x 64 x 64, two workgroups per CU
+constexpr int kKcMid8 = 14;      // 128 x 128 x 32, 8 waves, two workgroups per CU
+constexpr int kKcHuge16 = 15;    // 256 x 256 x 32, 16 waves, one workgroup per CU, whole tiles only
 
-// Compute units of an MI355X; the choice of tile is a pure function of the
-// sizes so that it is the same on every call and testable without a GPU.
-constexpr long long kComputeUnits = 256;
+// The machine shape the choices depend on: compute units (tile quantisation,
+// stream-K workers, the split-K and row-split thresholds) and XCDs (the
+// workgroup -> tile order).  The choice of tile is a pure function of the
+// sizes and this shape, so it is the same on every call and testable without
+// a GPU (sgemm_plan_for).
+struct Machine {
+    long long cus;
+    int xcds;
+};
+constexpr Machine kMI355X = {256, 8};
 constexpr int kMaxSplits = 64;
 constexpr int kMaxWorkers = 4096;
+constexpr int kMaxDevices = 64;
+
+// The current device's shape, read once per device from its attributes
+// (MI355X's 256 CUs in 8 XCDs when there is no device to ask, so that the
+// host-only queries still answer on a machine without a GPU).
+Machine device_machine() {
+    static std::once_flag once[kMaxDevices];
+    static Machine shape[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return kMI355X;
+    }
+    std::call_once(once[dev], [dev]() {
+        Machine m = kMI355X;
+        int cus = 0, xcds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            cus > 0)
+            m.cus = cus;
+        // the workgroup -> tile order takes a power of two (8 on an MI355X,
+        // 4, 2 or 1 on its partitions); any other count gets the row-major
+        // order of one XCD
+        if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess && xcds > 0 &&
+            (xcds & (xcds - 1)) == 0)
+            m.xcds = xcds;
+        else
+            m.xcds = 1;
+        (void)hipGetLastError();
+        shape[dev] = m;
+    });
+    return shape[dev];
+}
+
+// log2 of a power of two
+int log2_of(int x) {
+    int s = 0;
+    while ((1 << (s + 1)) <= x) ++s;
+    return s;
+}
 
 long long tiles(int M, int N, int bm, int bn) {
     return (long long)((M + bm - 1) / bm) * (long long)((N + bn - 1) / bn);
 }
 
 // Fraction of the last round of tiles that keeps the compute units busy:
-// t tiles over 256 CUs take ceil(t / 256) rounds of per-CU work.
-double quantization(long long t) {
-    const long long rounds = (t + kComputeUnits - 1) / kComputeUnits;
-    return rounds == 0 ? 0.0 : (double)t / (double)(rounds * kComputeUnits);
+// t tiles over c CUs take ceil(t / c) rounds of per-CU work.
+double quantization(long long t, long long c) {
+    const long long rounds = (t + c - 1) / c;
+    return rounds == 0 ? 0.0 : (double)t / (double)(rounds * c);
+}
+
+// Fraction of the tiles' area that lies inside C: padded rows and columns of
+// edge tiles still issue every MFMA.
+double fill(int M, int N, int bm, int bn) {
+    const long long t = tiles(M, N, bm, bn);
+    return t == 0 ? 0.0 : (double)M * (double)N / ((double)t * bm * bn);
 }
 
 // Measured on MI355X over every variant with `python -m fp32_gemm_03_amd.tune`
@@ -271,14 +251,17 @@ constexpr int kStreamKMinK = 8;
 constexpr double kHuge16Rate = 147.0;
 constexpr double kSmallRate = 110.0;
 
-// The variant for a whole-tile (or, with streamk, stream-K) launch; *score
-// gets its predicted TFLOP/s (rate x the busy share of the last round).
-int choose(int path, int M, int N, int K, bool streamk, int *workers, double *score_out = nullptr) {
+// The variant for a whole-tile (or, with streamk, stream-K) launch on a
+// machine of m.cus compute units; *score gets its predicted TFLOP/s (rate x
+// the busy share of the last round x the share of the tiles' area inside C).
+int choose(const Machine &m, int path, int M, int N, int K, bool streamk, int *workers,
+           double *score_out = nullptr) {
     if (workers) *workers = 0;
     if (score_out) *score_out = 0.0;
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
+    const long long cus = m.cus;
     if (path == SGEMM_PATH_VALU) {
         // The 8 x 16 micro-tile reads 25% less LDS per FMA and is 11-19%
         // faster at 4096^3 and 8192^3, but only where its 128 x 256 blocks
@@ -286,7 +269,7 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers, double *sc
         // at 16384^2 x 128 and with fewer blocks than slots the 8 x 8 tile
         // is as fast or faster (measured over the same shapes as below).
         const long long t = tiles(M, N, 128, 256);
-        if (t >= 2 * kComputeUnits && t % kComputeUnits == 0 && K >= 1024) return kValuWide;
+        if (t >= 2 * cus && t % cus == 0 && K >= 1024) return kValuWide;
         return kValuDefault;
     }
     if (path != SGEMM_PATH_AUTO && path != SGEMM_PATH_MFMA) return SGEMM_ERR_PATH;
@@ -306,15 +289,16 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers, double *sc
     for (const Candidate &c : cand) {
         const Variant &v = kVariants[c.variant];
         const long long t = tiles(M, N, v.bm, v.bn);
-        const long long slots = c.per_cu * kComputeUnits;
+        const long long slots = c.per_cu * cus;
         if (t < slots || K < c.min_k) continue;
-        double score = c.rate * quantization(t);
+        const double f = fill(M, N, v.bm, v.bn);
+        double score = c.rate * quantization(t, cus) * f;
         int w = 0;
-        const long long rest = t % kComputeUnits, kt = (K + v.bk - 1) / v.bk;
-        if (streamk && v.streamk && rest > 0 && rest * kt >= kStreamKMinK * kComputeUnits &&
-            c.rate * kStreamKShare > score) {
-            score = c.rate * kStreamKShare;
-            w = (int)kComputeUnits;
+        const long long rest = t % cus, kt = (K + v.bk - 1) / v.bk;
+        if (streamk && v.streamk && rest > 0 && rest * kt >= kStreamKMinK * cus &&
+            c.rate * kStreamKShare * f > score) {
+            score = c.rate * kStreamKShare * f;
+            w = (int)cus;
         }
         if (score > best_score) {
             best_score = score;
@@ -329,12 +313,11 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers, double *sc
         // 95.4); with at most one tile per CU, the deeper K tile, and
         // select_splits may split K.
         const Variant &v = kVariants[kKcSmall4];
-        const long long t = tiles(M, N, v.bm, v.bn), rest = t % kComputeUnits;
-        if (score_out) *score_out = kSmallRate;
-        if (t <= kComputeUnits) return kKcSmall64;
+        const long long t = tiles(M, N, v.bm, v.bn), rest = t % cus;
+        if (score_out) *score_out = kSmallRate * fill(M, N, v.bm, v.bn);
+        if (t <= cus) return kKcSmall64;
         const long long kt = (K + v.bk - 1) / v.bk;
-        if (streamk && workers && rest > 0 && rest * kt >= kStreamKMinK * kComputeUnits)
-            *workers = (int)kComputeUnits;
+        if (streamk && workers && rest > 0 && rest * kt >= kStreamKMinK * cus) *workers = (int)cus;
         return kKcSmall4;
     }
     if (workers) *workers = best_workers;
@@ -342,7 +325,9 @@ int choose(int path, int M, int N, int K, bool streamk, int *workers, double *sc
     return best;
 }
 
-int select_variant(int path, int M, int N, int K) { return choose(path, M, N, K, false, nullptr); }
+int select_variant(const Machine &m, int path, int M, int N, int K) {
+    return choose(m, path, M, N, K, false, nullptr);
+}
 
 // Without a workspace there is no stream-K, and a partial last round of
 // tiles leaves CUs idle.  C can instead be split by rows into two launches:
@@ -353,25 +338,27 @@ int select_variant(int path, int M, int N, int K) { return choose(path, M, N, K,
 // 144.5 TFLOP/s against 136.4, 139.1 and 140.2 for one launch (the split the
 // model picks there was within 1% of the best one tried).  Only bottom parts
 // of up to 64 block rows are tried.
-int split_rows(int M, int N, int K) {
+int split_rows(const Machine &m, int M, int N, int K) {
     if (K < 512 || M < 512) return 0;
     double single = 0.0;
-    if (choose(SGEMM_PATH_AUTO, M, N, K, false, nullptr, &single) < 0 || single <= 0.0) return 0;
+    if (choose(m, SGEMM_PATH_AUTO, M, N, K, false, nullptr, &single) < 0 || single <= 0.0) return 0;
     const long long nbn = (N + 255) / 256;
     const double per_row = 2.0 * N * (double)K;
     const double t_single = per_row * M / single;
+    // the first part's rows are whole 256-row blocks: only its columns pad
+    const double fill_n = (double)N / (double)(nbn * 256);
     double best_t = t_single;
     int best_rows = 0;
     const long long r_hi = (M - 1) / 256, r_lo = r_hi > 64 ? r_hi - 64 : 1;
     for (long long r = r_hi; r >= r_lo; --r) {
         const long long t = r * nbn;
-        if (t < kComputeUnits) break;
-        const double q = quantization(t);
+        if (t < m.cus) break;
+        const double q = quantization(t, m.cus);
         if (q < 0.96) continue;
         const int m1 = (int)(r * 256), m2 = M - m1;
         double s2 = 0.0;
-        if (choose(SGEMM_PATH_AUTO, m2, N, K, false, nullptr, &s2) < 0 || s2 <= 0.0) continue;
-        const double t_split = per_row * m1 / (kHuge16Rate * q) + per_row * m2 / s2;
+        if (choose(m, SGEMM_PATH_AUTO, m2, N, K, false, nullptr, &s2) < 0 || s2 <= 0.0) continue;
+        const double t_split = per_row * m1 / (kHuge16Rate * q * fill_n) + per_row * m2 / s2;
         if (t_split < best_t) {
             best_t = t_split;
             best_rows = m1;
@@ -389,17 +376,35 @@ int split_rows(int M, int N, int K) {
 // pass over the partials stay small.  Only the latency block splits: the
 // blocks chosen by rate have a tile for every one of their workgroup slots
 // on the chip already.
-int select_splits(int variant, int M, int N, int K) {
+int select_splits(const Machine &m, int variant, int M, int N, int K) {
     if (M <= 0 || N <= 0 || K <= 0 || (variant != kKcSmall4 && variant != kKcSmall64)) return 1;
     const Variant &v = kVariants[variant];
     if (v.split4 == nullptr) return 1;
     const long long t = tiles(M, N, v.bm, v.bn);
-    if (t > kComputeUnits) return 1;
-    long long s = 2 * kComputeUnits / t;
-    const long long k_min = t < kComputeUnits ? 256 : 1024;
+    if (t > m.cus) return 1;
+    long long s = 2 * m.cus / t;
+    const long long k_min = t < m.cus ? 256 : 1024;
     if (s > K / k_min) s = K / k_min;
     if (s > kMaxSplits) s = kMaxSplits;
     return s < 2 ? 1 : (int)s;
+}
+
+// What sgemm_ws (with_workspace) or sgemm (without) runs for these sizes:
+// the variant, split count, stream-K workers and the rows of a first
+// row-split launch (0: none).  Returns 0 or a negative argument code.
+int plan(const Machine &m, int M, int N, int K, bool with_workspace, int *variant, int *splits,
+         int *workers, int *rows) {
+    int w = 0;
+    const int v = choose(m, SGEMM_PATH_AUTO, M, N, K, with_workspace, &w);
+    if (v < 0) return v;
+    int sp = 1, r = 0;
+    if (with_workspace && w == 0) sp = select_splits(m, v, M, N, K);
+    if (w == 0 && sp == 1) r = split_rows(m, M, N, K);
+    if (variant) *variant = v;
+    if (splits) *splits = sp;
+    if (workers) *workers = w;
+    if (rows) *rows = r;
+    return SGEMM_OK;
 }
 
 int check_args(int M, int N, int K, float alpha, const float *A, int lda,
@@ -432,10 +437,9 @@ size_t streamk_bytes(const Variant &v, int workers) {
     return round_up((size_t)workers * 2 * v.bm * v.bn * 4, 256);
 }
 
-int launch(int variant, int access, int splits, int workers, void *workspace, size_t workspace_bytes,
-           int M, int N, int K, float alpha, const float *A,
-           int lda, const float *B, int ldb, float beta, float *C, int ldc,
-           hipStream_t stream) {
+int launch(const Machine &m, int variant, int access, int splits, int workers, void *workspace,
+           size_t workspace_bytes, int M, int N, int K, float alpha, const float *A, int lda,
+           const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     if (variant < 0 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
@@ -477,6 +481,7 @@ int launch(int variant, int access, int splits, int workers, void *workspace, si
     a.phase = 0;
     a.sk_whole = 0;
     a.sk_workers = 0;
+    a.xcd_shift = log2_of(m.xcds);
     // Buffer accesses form byte offsets inside one block tile in 31 bits.
     const long long lim = 1LL << 31;
     const bool buf_ok = (long long)(v.bm + 1) * lda * 4 < lim &&
@@ -523,11 +528,8 @@ int launch(int variant, int access, int splits, int workers, void *workspace, si
         }
     }
 
-    // a persistent variant launches one workgroup per resident slot and loops over the tiles
-    const long long launch_grid =
-        v.persistent > 0 && grid > v.persistent * kComputeUnits ? v.persistent * kComputeUnits : grid;
     (void)hipGetLastError();  // drop any stale error so the code below is this launch's
-    hipLaunchKernelGGL(fn, dim3((unsigned)launch_grid), dim3(v.threads), 0, stream, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(v.threads), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err == hipSuccess && (splits > 1 || workers > 0)) {
         // the summing phase on the same stream: it starts after every
@@ -543,14 +545,14 @@ int launch(int variant, int access, int splits, int workers, void *workspace, si
 
 // C split by rows: rows [0, rows) on the 16-wave 256 x 256 block, the rest
 // with the block chosen for it, one launch each on the same stream.
-int launch_rows(int rows, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
-                int ldb, float beta, float *C, int ldc, hipStream_t stream) {
-    int rc = launch(kKcHuge16, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, rows, N, K, alpha, A, lda, B, ldb,
-                    beta, C, ldc, stream);
+int launch_rows(const Machine &m, int rows, int M, int N, int K, float alpha, const float *A, int lda,
+                const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
+    int rc = launch(m, kKcHuge16, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, rows, N, K, alpha, A, lda, B,
+                    ldb, beta, C, ldc, stream);
     if (rc != SGEMM_OK) return rc;
-    const int v2 = select_variant(SGEMM_PATH_AUTO, M - rows, N, K);
+    const int v2 = select_variant(m, SGEMM_PATH_AUTO, M - rows, N, K);
     if (v2 < 0) return v2;
-    return launch(v2, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M - rows, N, K, alpha,
+    return launch(m, v2, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M - rows, N, K, alpha,
                   A + (size_t)rows * lda, lda, B, ldb, beta, C + (size_t)rows * ldc, ldc, stream);
 }
 
@@ -569,35 +571,37 @@ int sgemm_path(int path, int M, int N, int K, float alpha, const float *A,
                hipStream_t stream) {
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
-    const int v = select_variant(path, M, N, K);
+    const Machine m = device_machine();
+    const int v = select_variant(m, path, M, N, K);
     if (v < 0) return v;
     if (path != SGEMM_PATH_VALU) {
-        const int rows = split_rows(M, N, K);
-        if (rows > 0) return launch_rows(rows, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+        const int rows = split_rows(m, M, N, K);
+        if (rows > 0) return launch_rows(m, rows, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
     }
-    return launch(v, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
-                  stream);
+    return launch(m, v, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                  ldc, stream);
 }
 
 int sgemm_variant(int variant, int M, int N, int K, float alpha,
                   const float *A, int lda, const float *B, int ldb, float beta,
                   float *C, int ldc, hipStream_t stream) {
-    return launch(variant, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C,
-                  ldc, stream);
+    return launch(device_machine(), variant, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M, N, K, alpha, A,
+                  lda, B, ldb, beta, C, ldc, stream);
 }
 
 int sgemm_variant_access(int variant, int access, int M, int N, int K, float alpha,
                          const float *A, int lda, const float *B, int ldb, float beta,
                          float *C, int ldc, hipStream_t stream) {
-    return launch(variant, access, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return launch(device_machine(), variant, access, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb,
+                  beta, C, ldc, stream);
 }
 
 int sgemm_splitk(int variant, int splits, int M, int N, int K, float alpha,
                  const float *A, int lda, const float *B, int ldb, float beta,
                  float *C, int ldc, void *workspace, size_t workspace_bytes,
                  hipStream_t stream) {
-    return launch(variant, SGEMM_ACCESS_AUTO, splits, 0, workspace, workspace_bytes, M, N, K, alpha,
-                  A, lda, B, ldb, beta, C, ldc, stream);
+    return launch(device_machine(), variant, SGEMM_ACCESS_AUTO, splits, 0, workspace, workspace_bytes,
+                  M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 size_t sgemm_splitk_workspace_size(int variant, int splits, int M, int N) {
@@ -613,8 +617,8 @@ int sgemm_streamk(int variant, int workers, int M, int N, int K, float alpha,
                   float *C, int ldc, void *workspace, size_t workspace_bytes,
                   hipStream_t stream) {
     if (workers < 1) return SGEMM_ERR_SPLITS;
-    return launch(variant, SGEMM_ACCESS_AUTO, 1, workers, workspace, workspace_bytes, M, N, K, alpha,
-                  A, lda, B, ldb, beta, C, ldc, stream);
+    return launch(device_machine(), variant, SGEMM_ACCESS_AUTO, 1, workers, workspace, workspace_bytes,
+                  M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
 }
 
 size_t sgemm_streamk_workspace_size(int variant, int workers) {
@@ -624,20 +628,36 @@ size_t sgemm_streamk_workspace_size(int variant, int workers) {
 }
 
 int sgemm_select_splits(int M, int N, int K) {
-    int workers = 0;
-    const int v = choose(SGEMM_PATH_AUTO, M, N, K, true, &workers);
-    if (v < 0) return v;
-    return workers > 0 ? 1 : select_splits(v, M, N, K);
+    int sp = 1;
+    const int rc = plan(device_machine(), M, N, K, true, nullptr, &sp, nullptr, nullptr);
+    return rc < 0 ? rc : sp;
 }
 
 int sgemm_ws_plan(int M, int N, int K, int *variant, int *splits, int *workers) {
-    int w = 0;
-    int v = choose(SGEMM_PATH_AUTO, M, N, K, true, &w);
-    if (v < 0) return v;
-    const int sp = w > 0 ? 1 : select_splits(v, M, N, K);
-    if (variant) *variant = v;
-    if (splits) *splits = sp;
-    if (workers) *workers = w;
+    return plan(device_machine(), M, N, K, true, variant, splits, workers, nullptr);
+}
+
+int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int *variant,
+                   int *splits, int *workers, int *rows) {
+    if (compute_units < 1 || compute_units > (1 << 20)) return SGEMM_ERR_MACHINE;
+    const Machine m = {compute_units, kMI355X.xcds};
+    return plan(m, M, N, K, with_workspace != 0, variant, splits, workers, rows);
+}
+
+int sgemm_device_shape(int *compute_units, int *xcds) {
+    const Machine m = device_machine();
+    if (compute_units) *compute_units = (int)m.cus;
+    if (xcds) *xcds = m.xcds;
+    return SGEMM_OK;
+}
+
+int sgemm_tile_order(int xcds, int nbm, int nbn, int *tile_m, int *tile_n) {
+    if (xcds < 1 || xcds > 1024 || (xcds & (xcds - 1)) != 0 || nbm < 0 || nbn < 0 ||
+        (long long)nbm * nbn > INT_MAX)
+        return SGEMM_ERR_MACHINE;
+    if ((long long)nbm * nbn > 0 && (tile_m == nullptr || tile_n == nullptr)) return SGEMM_ERR_MACHINE;
+    const int total = nbm * nbn, xs = log2_of(xcds);
+    for (int pid = 0; pid < total; ++pid) sgk::tile_of<2, 8>(pid, nbm, nbn, xs, tile_m[pid], tile_n[pid]);
     return SGEMM_OK;
 }
 
@@ -645,21 +665,19 @@ int sgemm_select_rows(int M, int N, int K) {
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
-    return split_rows(M, N, K);
+    return split_rows(device_machine(), M, N, K);
 }
 
 int sgemm_select_streamk(int M, int N, int K) {
-    int workers = 0;
-    const int v = choose(SGEMM_PATH_AUTO, M, N, K, true, &workers);
-    return v < 0 ? v : workers;
+    int w = 0;
+    const int rc = plan(device_machine(), M, N, K, true, nullptr, nullptr, &w, nullptr);
+    return rc < 0 ? rc : w;
 }
 
 size_t sgemm_workspace_size(int M, int N, int K) {
-    int workers = 0;
-    const int v = choose(SGEMM_PATH_AUTO, M, N, K, true, &workers);
-    if (v < 0) return 0;
-    if (workers > 0) return streamk_bytes(kVariants[v], workers);
-    const int sp = select_splits(v, M, N, K);
+    int v = 0, sp = 1, w = 0;
+    if (plan(device_machine(), M, N, K, true, &v, &sp, &w, nullptr) < 0) return 0;
+    if (w > 0) return streamk_bytes(kVariants[v], w);
     return sp > 1 ? splitk_bytes(kVariants[v], sp, M, N) : 0;
 }
 
@@ -668,24 +686,25 @@ int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const fl
              hipStream_t stream) {
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
+    const Machine m = device_machine();
     int workers = 0;
-    int v = choose(SGEMM_PATH_AUTO, M, N, K, true, &workers);
+    int v = choose(m, SGEMM_PATH_AUTO, M, N, K, true, &workers);
     if (v < 0) return v;
     const bool room = workspace != nullptr && ((uintptr_t)workspace & 255u) == 0;
     if (workers > 0) {
         if (room && workspace_bytes >= streamk_bytes(kVariants[v], workers))
-            return launch(v, SGEMM_ACCESS_AUTO, 1, workers, workspace, workspace_bytes, M, N, K, alpha,
-                          A, lda, B, ldb, beta, C, ldc, stream);
-        v = select_variant(SGEMM_PATH_AUTO, M, N, K);  // not enough workspace: whole tiles only
+            return launch(m, v, SGEMM_ACCESS_AUTO, 1, workers, workspace, workspace_bytes, M, N, K,
+                          alpha, A, lda, B, ldb, beta, C, ldc, stream);
+        v = select_variant(m, SGEMM_PATH_AUTO, M, N, K);  // not enough workspace: whole tiles only
     }
-    int sp = select_splits(v, M, N, K);
+    int sp = select_splits(m, v, M, N, K);
     if (sp > 1 && (!room || workspace_bytes < splitk_bytes(kVariants[v], sp, M, N)))
         sp = 1;  // not enough workspace: the unsplit kernel
     if (sp == 1) {
-        const int rows = split_rows(M, N, K);
-        if (rows > 0) return launch_rows(rows, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+        const int rows = split_rows(m, M, N, K);
+        if (rows > 0) return launch_rows(m, rows, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
     }
-    return launch(v, SGEMM_ACCESS_AUTO, sp, 0, workspace, workspace_bytes, M, N, K, alpha, A, lda, B,
+    return launch(m, v, SGEMM_ACCESS_AUTO, sp, 0, workspace, workspace_bytes, M, N, K, alpha, A, lda, B,
                   ldb, beta, C, ldc, stream);
 }
 
@@ -714,7 +733,7 @@ int sgemm_variant_reads_a128(int variant) {
 }
 
 int sgemm_select_variant(int path, int M, int N, int K) {
-    return select_variant(path, M, N, K);
+    return select_variant(device_machine(), path, M, N, K);
 }
 
 const char *sgemm_status_string(int status) {
@@ -736,6 +755,7 @@ const char *sgemm_status_string(int status) {
         case SGEMM_ERR_WORKSPACE: return "invalid argument: workspace missing, too small or not 256-byte aligned";
         case SGEMM_ERR_SPLITS:
             return "invalid argument: split or worker count out of range, or variant without split-K or stream-K";
+        case SGEMM_ERR_MACHINE: return "invalid argument: machine shape or tile grid out of range";
         default: break;
     }
     if (status > 0) return hipGetErrorString((hipError_t)status);

@@ -55,7 +55,6 @@
 #include <stdint.h>
 
 #include <type_traits>
-#include <utility>
 
 namespace sgk {
 
@@ -79,6 +78,9 @@ struct Args {
     // stream-K only: tiles done whole (the first sk_whole in tile order) and
     // the workers that share the K tiles of the rest
     int sk_whole, sk_workers;
+    // log2 of the device's XCD count: consecutive workgroup ids go to the
+    // XCDs in turn
+    int xcd_shift;
 };
 
 template <int W> struct vec_t;
@@ -255,11 +257,16 @@ struct ATilePtr : ATileGeom<BM, BK, NT, PADA, STAGES, SWZ> {
         for (int p = 0; p < G::PER; ++p) load_piece<S>(a, bm, k0, p);
     }
 
+    // The lane's column and first row pass through an empty asm at each
+    // load, so the compiler recomputes the 64-bit row addresses here instead
+    // of hoisting one per row out of the K loop into registers.
     template <int S>
     __device__ __forceinline__ void load_piece(const Args &a, int bm, int k0, int p) {
-        const bool kin = (k0 + col) < a.K;
-        const int row = bm + r0 + p * G::ROWS_PER_PASS;
-        const float *q = a.A + (int64_t)row * a.lda + k0 + col;
+        int c_ = col, r_ = r0;
+        asm volatile("" : "+v"(c_), "+v"(r_));
+        const bool kin = (k0 + c_) < a.K;
+        const int row = bm + r_ + p * G::ROWS_PER_PASS;
+        const float *q = a.A + (int64_t)row * a.lda + k0 + c_;
         const int rl = a.M - row;
         G::reg[S][p].x = (kin && rl > 0) ? q[0] : 0.0f;
         G::reg[S][p].y = (kin && rl > 1) ? q[a.lda] : 0.0f;
@@ -356,10 +363,13 @@ struct BTilePtr : BTileGeom<BN, BK, NT, PADB, VEC, STAGES> {
         for (int p = 0; p < G::PER; ++p) load_piece<S>(a, bn, k0, p);
     }
 
+    // As in ATilePtr: the lane's coordinates are opaque at each load.
     template <int S>
     __device__ __forceinline__ void load_piece(const Args &a, int bn, int k0, int p) {
-        const int n = bn + n_first + G::dn(p);
-        const int k = k0 + k_first + G::dk(p);
+        int nf = n_first, kf = k_first;
+        asm volatile("" : "+v"(nf), "+v"(kf));
+        const int n = bn + nf + G::dn(p);
+        const int k = k0 + kf + G::dk(p);
         // VEC == 4 only when N % 4 == 0: a piece is all in or all out
         if (n < a.N && k < a.K)
             G::reg[S][p] = *reinterpret_cast<const typename G::V *>(a.B + (int64_t)k * a.ldb + n);
@@ -474,12 +484,12 @@ struct CStorePtr {
 // coordinates pos(v) with values val(v).  beta is uniform, so the test is
 // taken once; with beta != 0 the old values of G vectors are requested
 // together before any of them is combined and stored, so the loads' latency
-// is paid once per group instead of once per vector (a group holds 32 old
-// values: 32 extra VGPRs at most).
-template <int NV, int W, class TC, class Pos, class Val>
+// is paid once per group instead of once per vector (a group holds GV old
+// values: GV extra VGPRs at most).
+template <int NV, int W, class TC, class Pos, class Val, int GV = 32>
 __device__ __forceinline__ void epilogue(const Args &a, const TC &st, Pos pos, Val val) {
     if (a.beta != 0.0f) {
-        constexpr int G = NV < 32 / W ? NV : 32 / W;
+        constexpr int G = NV < GV / W ? NV : (GV / W > 0 ? GV / W : 1);
         static_assert(NV % G == 0, "epilogue groups");
 #pragma unroll
         for (int b = 0; b < NV; b += G) {
@@ -612,18 +622,19 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
     typename S::TC st;
     st.init(a, bm, bn);
     constexpr int CG = TN / 4;
-    epilogue<TM * CG, 4>(
-        a, st,
-        [&](int v, int &r, int &c) {
-            const int i = v / CG, g = v % CG;
-            r = wm + 4 * ly + (i & 3) + 32 * (i >> 2);
-            c = wn + 4 * lx + 32 * g;
-        },
-        [&](int v, float (&x)[4]) {
-            const int i = v / CG, g = v % CG;
+    auto pos = [&](int v, int &r, int &c) {
+        const int i = v / CG, g = v % CG;
+        r = wm + 4 * ly + (i & 3) + 32 * (i >> 2);
+        c = wn + 4 * lx + 32 * g;
+    };
+    auto val = [&](int v, float (&x)[4]) {
+        const int i = v / CG, g = v % CG;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = acc[i][4 * g + e];
-        });
+        for (int e = 0; e < 4; ++e) x[e] = acc[i][4 * g + e];
+    };
+    // 32-bit accesses take 4 loads per vector: fewer old values in flight
+    // (beta != 0) keep the 8 x 8 tile within its 128 registers
+    epilogue<TM * CG, 4, typename S::TC, decltype(pos), decltype(val), VEC == 4 ? 32 : 16>(a, st, pos, val);
 }
 
 // ---------------------------------------------------------------------------
@@ -648,53 +659,59 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_valu(Args a) {
 // Workgroup -> C tile.  ORDER 0: row-major over tiles, the M index slow
 // ("如何高效实现矩阵乘", section "Wave & L2 cache Hit Rate").  ORDER 1: the
 // same tiles, assigned so that each XCD works on a compact patch.  MI355X
-// hands consecutive workgroup ids to its 8 XCDs in turn (id % 8), and each
+// hands consecutive workgroup ids to its X XCDs in turn (id % X), and each
 // XCD has its own L2; the id is first renumbered so that every XCD receives
 // a contiguous run of the tile sequence, and the sequence then walks groups
 // of GROUP_M tile rows column by column, so the workgroups an XCD runs at
 // once share GROUP_M row blocks of A and a few column blocks of B.
 // ORDER 2: row-major as seen from each XCD.  With the tile columns a multiple
-// of 8, row-major dealing already gives XCD x the columns x, x + 8, ... in
+// of X, row-major dealing already gives XCD x the columns x, x + X, ... in
 // every row, and this order is the same mapping.  Otherwise the column an
 // XCD receives shifts from row to row and the workgroups it runs at once
-// need up to 8 times as many B column blocks; here XCD x keeps the columns
-// x, x + 8, ... below 8 floor(nbn / 8) and walks them row by row, and the
-// remaining nbn mod 8 columns, row-major, are dealt out last in one
-// contiguous run per XCD.
+// need up to X times as many B column blocks; here XCD x keeps the columns
+// x, x + X, ... below X floor(nbn / X) and walks them row by row, and the
+// remaining nbn mod X columns, row-major, are dealt out last in one
+// contiguous run per XCD.  X = 2^xs is the device's XCD count (8 on an
+// MI355X, 4, 2 or 1 on its partitions: a power of two, so no division by
+// it is needed; X = 1 makes every order row-major).  Every order is a
+// bijection of [0, nbm nbn) onto the tiles.
 template <int ORDER, int GROUP_M>
-__device__ __forceinline__ void tile_of(int pid, int nbm, int nbn, int &tm, int &tn) {
-    const int c = nbn / 8, rem = nbn % 8;
-    if (ORDER == 0 || (ORDER == 2 && (rem == 0 || c == 0))) {
+__host__ __device__ __forceinline__ void tile_of(int pid, int nbm, int nbn, int xs, int &tm, int &tn) {
+    const int X = 1 << xs;
+    if (ORDER == 0 || X == 1) {
         tm = pid / nbn;
         tn = pid % nbn;
         return;
     }
+    const int c = nbn >> xs, rem = nbn & (X - 1);
+    if (ORDER == 2 && (rem == 0 || c == 0)) {
+        tm = pid / nbn;
+        tn = pid % nbn;
+        return;
+    }
+    const int total = nbm * nbn;
+    const int q = total >> xs, r = total & (X - 1);
+    const int x = pid & (X - 1), idx = pid >> xs;
     if (ORDER == 2) {
-        const int total = nbm * nbn;
-        const int q = total / 8, r = total % 8;
-        const int x = pid % 8, idx = pid / 8;
         const int common = nbm * c;  // tiles of XCD x in its own columns
         if (idx < common) {
             tm = idx / c;
-            tn = x + 8 * (idx - tm * c);
+            tn = x + X * (idx - tm * c);
             return;
         }
         // XCDs before x hold x q + min(x, r) ids, x * common of them in
         // their own columns; the rest index the remaining columns' tiles
-        const int g = x * q + min(x, r) - x * common + (idx - common);
+        const int g = x * q + (x < r ? x : r) - x * common + (idx - common);
         tm = g / rem;
-        tn = 8 * c + (g - tm * rem);
+        tn = X * c + (g - tm * rem);
         return;
     }
-    const int total = nbm * nbn;
-    const int q = total / 8, r = total % 8;
-    const int xcd = pid % 8, idx = pid / 8;
-    // XCD x received ids x, x + 8, ...: q + (x < r) of them
-    const int seq = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + idx;
+    // XCD x received ids x, x + X, ...: q + (x < r) of them
+    const int seq = (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + idx;
     const int per_group = GROUP_M * nbn;
     const int group = seq / per_group;
     const int first_m = group * GROUP_M;
-    const int rows = min(nbm - first_m, GROUP_M);
+    const int rows = nbm - first_m < GROUP_M ? nbm - first_m : GROUP_M;
     const int in_group = seq - group * per_group;
     tm = first_m + in_group % rows;
     tn = in_group / rows;
@@ -772,23 +789,23 @@ __device__ __forceinline__ void mfma_tile(const float *as, int a_col, int lh, co
 // Epilogue of a wave's MI x NI accumulator blocks: register r of block
 // (mi, ni) on lane (li, lh) is tile row wm + MI*(8*(r/4) + 4*lh + r%4) + mi,
 // tile column wn + NI*li + ni.
-template <class S, int MI, int NI>
+// GV bounds the old C values requested at once when beta != 0.
+template <class S, int MI, int NI, int GV = 32>
 __device__ __forceinline__ void epilogue_mfma(const Args &a, int bm, int bn, int wm, int wn, int li,
                                               int lh, const floatx16 (&acc)[MI][NI]) {
     typename S::TC st;
     st.init(a, bm, bn);
     // vector v is accumulator register v % 16 of block row v / 16
-    epilogue<MI * 16, NI>(
-        a, st,
-        [&](int v, int &r, int &c) {
-            const int i = v / 16, reg = v % 16;
-            r = wm + MI * (8 * (reg >> 2) + 4 * lh + (reg & 3)) + i;
-            c = wn + NI * li;
-        },
-        [&](int v, float (&x)[NI]) {
+    auto pos = [&](int v, int &r, int &c) {
+        const int i = v / 16, reg = v % 16;
+        r = wm + MI * (8 * (reg >> 2) + 4 * lh + (reg & 3)) + i;
+        c = wn + NI * li;
+    };
+    auto val = [&](int v, float (&x)[NI]) {
 #pragma unroll
-            for (int j = 0; j < NI; ++j) x[j] = acc[v / 16][j][v % 16];
-        });
+        for (int j = 0; j < NI; ++j) x[j] = acc[v / 16][j][v % 16];
+    };
+    epilogue<MI * 16, NI, typename S::TC, decltype(pos), decltype(val), GV>(a, st, pos, val);
 }
 
 // Epilogue through LDS ("SGEMM CUDA kernel (Second Half)", Part 9: each warp
@@ -847,12 +864,15 @@ __device__ __forceinline__ void epilogue_mfma_staged(const Args &a, const TC4 &s
     }
 }
 
-// PD is the prefetch depth: how many K tiles are in flight in registers while
-// one is multiplied from LDS (1, or 2 for shapes whose per-tile arithmetic is
-// too short to cover one global-load latency).  FD is the LDS fragment
-// prefetch distance in k-steps.
+// Register-staged MFMA kernel: the global loads of K tile t+1 land in
+// registers and are stored to the other LDS stage (one register stage).  FD
+// is the LDS fragment prefetch distance in k-steps.  IL selects the
+// interleaved schedule (the loads and stores threaded between the MFMAs);
+// otherwise the loads are issued before a tile's MFMAs and stored after them.
+// EPI 1 takes the LDS-staged epilogue.  ORDER is the workgroup -> tile order
+// of tile_of.
 template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC, int WPE, bool BUF,
-          int PD, int FD, int ORDER, bool SPLIT, int EPI, bool SWZ, bool IL = false>
+          int FD, int ORDER, int EPI, bool SWZ, bool IL>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -863,19 +883,14 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     static_assert(BK % 2 == 0, "BK must be even (K = 2 per instruction)");
     static_assert(MI == 1 || MI == 2 || MI == 4, "MI in {1, 2, 4}");
     static_assert(NI == 1 || NI == 2 || NI == 4, "NI in {1, 2, 4}");
-    static_assert(PD == 1 || PD == 2, "prefetch depth 1 or 2");
-    typedef Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, NI, PD, SWZ> S;
+    typedef Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, NI, 1, SWZ> S;
     __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
-    // split-K: workgroup id = split * tiles + tile
-    const int ntiles = nbm * nbn;
-    const int split = SPLIT && a.phase == 0 ? (int)blockIdx.x / ntiles : 0;
-    const int tile = SPLIT ? (int)blockIdx.x - split * ntiles : (int)blockIdx.x;
     int tm, tn;
-    tile_of<ORDER, 8>(tile, nbm, nbn, tm, tn);
+    tile_of<ORDER, 8>((int)blockIdx.x, nbm, nbn, a.xcd_shift, tm, tn);
     const int bm = tm * BM, bn = tn * BN;
     const int wm = (wave / WAVES_N) * WM, wn = (wave % WAVES_N) * WN;
     const int li = lane & 31, lh = lane >> 5;
@@ -896,47 +911,17 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = acc_odd[i][j][r] = 0.0f;
 
-    if (SPLIT && a.phase == 1) {
-        // Split-K, phase 1 (one workgroup per tile, after every phase-0
-        // workgroup has finished): sum the partials in split order 0, 1, ...
-        // so the result does not depend on timing, then the usual epilogue.
-        for (int sp = 0; sp < a.splits; ++sp) {
-            const float4 *src = reinterpret_cast<const float4 *>(
-                a.partial + ((int64_t)tile * a.splits + sp) * (BM * BN));
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float4 v = src[((i * NI + j) * 4 + q) * NT + tid];
-                        acc[i][j][4 * q] += v.x;
-                        acc[i][j][4 * q + 1] += v.y;
-                        acc[i][j][4 * q + 2] += v.z;
-                        acc[i][j][4 * q + 3] += v.w;
-                    }
-        }
-        epilogue_mfma<S, MI, NI>(a, bm, bn, wm, wn, li, lh, acc);
-        return;
-    }
-
     // per-lane fragment bases inside one LDS stage
     const int a_col = wm + MI * li;
     const int b_off = BK * SA + lh * SB + wn + NI * li;
-    // K tiles [kt0, kt0 + KT): all of K, or this split's share of it
-    const int KT_ALL = (a.K + BK - 1) / BK;
-    const int kt0 = SPLIT ? (int)((int64_t)KT_ALL * split / a.splits) : 0;
-    const int KT = SPLIT ? (int)((int64_t)KT_ALL * (split + 1) / a.splits) - kt0 : KT_ALL;
-    const int kb = kt0 * BK;
+    const int KT = (a.K + BK - 1) / BK;
 
     if constexpr (IL) {
-        // Interleaved schedule (PD == 1): the loads of K tile t+1 are issued
-        // in pieces after the MFMAs of the first k-steps of tile t, and
-        // stored to the other LDS stage in pieces over the last k-steps, so
-        // the matrix pipe is fed throughout.  The loads are not conditional:
-        // after a split's last tile they read the next split's first tile,
-        // or past K 0.0, into a stage nobody reads.
-        static_assert(PD == 1, "interleaved schedule: one register stage");
+        // Interleaved schedule: the loads of K tile t+1 are issued in pieces
+        // after the MFMAs of the first k-steps of tile t, and stored to the
+        // other LDS stage in pieces over the last k-steps, so the matrix pipe
+        // is fed throughout.  The loads are not conditional: after the last
+        // tile they read past K, 0.0, into a stage nobody reads.
         constexpr int STEPS = BK / 2;
         constexpr int PA = S::TA::PER, PB = S::TB::PER, NP = PA + PB;
         // the first quarter of the k-steps carries the loads, the second half
@@ -947,8 +932,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         constexpr int SSTEPS = STEPS / 2 > 0 ? STEPS / 2 : 1;
         constexpr int LPER = (NP + LSTEPS - 1) / LSTEPS, SPER = (NP + SSTEPS - 1) / SSTEPS;
         if (KT > 0) {
-            ta.template load<0>(a, bm, kb);
-            tb.template load<0>(a, bn, kb);
+            ta.template load<0>(a, bm, 0);
+            tb.template load<0>(a, bn, 0);
             ta.template store<0>(smem, tid);
             tb.template store<0>(smem + BK * SA, tid);
         }
@@ -956,7 +941,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         for (int t = 0; t < KT; ++t) {
             const float *st = smem + (t & 1) * STAGE;
             float *nx = smem + ((t + 1) & 1) * STAGE;
-            const int kn = kb + (t + 1) * BK;
+            const int kn = (t + 1) * BK;
             // piece q of a step goes after MFMA (q * MI * NI) / pieces per step:
             // spread evenly, several after one MFMA when there are more
             // pieces than MFMAs
@@ -984,10 +969,10 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
             mfma_tile<BK, MI, NI, SA, SB, FD, SWZ, CH>(st, a_col, lh, st + b_off, acc, acc_odd, hook);
             __syncthreads();
         }
-    } else if (PD == 1) {
+    } else {
         if (KT > 0) {
-            ta.template load<0>(a, bm, kb);
-            tb.template load<0>(a, bn, kb);
+            ta.template load<0>(a, bm, 0);
+            tb.template load<0>(a, bn, 0);
             ta.template store<0>(smem, tid);
             tb.template store<0>(smem + BK * SA, tid);
         }
@@ -995,8 +980,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         for (int t = 0; t < KT; ++t) {
             const float *st = smem + (t & 1) * STAGE;
             if (t + 1 < KT) {
-                ta.template load<0>(a, bm, kb + (t + 1) * BK);
-                tb.template load<0>(a, bn, kb + (t + 1) * BK);
+                ta.template load<0>(a, bm, (t + 1) * BK);
+                tb.template load<0>(a, bn, (t + 1) * BK);
             }
             mfma_tile<BK, MI, NI, SA, SB, FD, SWZ, CH>(st, a_col, lh, st + b_off, acc, acc_odd);
             if (t + 1 < KT) {
@@ -1005,54 +990,6 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
                 tb.template store<0>(nx + BK * SA, tid);
             }
             __syncthreads();
-        }
-    } else {
-        // Register stage s holds K tile t with t % 2 == s once issued; tile t
-        // is issued two tiles ahead of its LDS store.  The loop runs two tiles
-        // per trip so that every register index is a constant.
-        constexpr int R = PD - 1;  // the second register stage (1)
-        if (KT > 0) {
-            ta.template load<0>(a, bm, kb);
-            tb.template load<0>(a, bn, kb);
-        }
-        if (KT > 1) {
-            ta.template load<R>(a, bm, kb + BK);
-            tb.template load<R>(a, bn, kb + BK);
-        }
-        if (KT > 0) {
-            ta.template store<0>(smem, tid);
-            tb.template store<0>(smem + BK * SA, tid);
-        }
-        __syncthreads();
-        if (KT > 2) {
-            ta.template load<0>(a, bm, kb + 2 * BK);
-            tb.template load<0>(a, bn, kb + 2 * BK);
-        }
-        for (int t = 0; t < KT; t += 2) {
-            // tile t from LDS stage 0; tile t+1 (register stage 1) -> LDS stage 1
-            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ, CH>(smem, a_col, lh, smem + b_off, acc, acc_odd);
-            if (t + 1 < KT) {
-                ta.template store<R>(smem + STAGE, tid);
-                tb.template store<R>(smem + STAGE + BK * SA, tid);
-            }
-            __syncthreads();
-            if (t + 1 >= KT) break;
-            if (t + 3 < KT) {
-                ta.template load<R>(a, bm, kb + (t + 3) * BK);
-                tb.template load<R>(a, bn, kb + (t + 3) * BK);
-            }
-            // tile t+1 from LDS stage 1; tile t+2 (register stage 0) -> LDS stage 0
-            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ, CH>(smem + STAGE, a_col, lh, smem + STAGE + b_off, acc,
-                                                         acc_odd);
-            if (t + 2 < KT) {
-                ta.template store<0>(smem, tid);
-                tb.template store<0>(smem + BK * SA, tid);
-            }
-            __syncthreads();
-            if (t + 4 < KT) {
-                ta.template load<0>(a, bm, kb + (t + 4) * BK);
-                tb.template load<0>(a, bn, kb + (t + 4) * BK);
-            }
         }
     }
 
@@ -1063,28 +1000,14 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
             for (int j = 0; j < NI; ++j) acc[i][j] += acc_odd[i][j];
     }
 
-    if (SPLIT) {
-        // Split-K, phase 0: store this split's partial tile in the lanes'
-        // own order (4-float chunks, consecutive threads adjacent).
-        float4 *mine = reinterpret_cast<float4 *>(a.partial + ((int64_t)tile * a.splits + split) * (BM * BN));
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    mine[((i * NI + j) * 4 + q) * NT + tid] =
-                        make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                    acc[i][j][4 * q + 3]);
-        return;
-    }
-
     if (EPI == 0) {
-        epilogue_mfma<S, MI, NI>(a, bm, bn, wm, wn, li, lh, acc);
+        // the checked C accesses are branches, each load waited for in its
+        // own branch: few old values in flight, or they spill
+        epilogue_mfma<S, MI, NI, BUF ? 32 : 8>(a, bm, bn, wm, wn, li, lh, acc);
     } else {
         static_assert(EPI == 0 || (BM / WM) * (BN / WN) * 16 * (WN + 4) <= 2 * STAGE,
                       "staged epilogue needs 16 x (WN + 4) floats of LDS per wave");
-        typename Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, 4, PD, SWZ>::TC st4;
+        typename Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, 4, 1, SWZ>::TC st4;
         st4.init(a, bm, bn);
         epilogue_mfma_staged<decltype(st4), MI, NI, WN>(a, st4, smem + wave * 16 * (WN + 4), wm, wn,
                                                          li, lh, lane, acc);
@@ -1134,27 +1057,46 @@ struct DirectStage {
     static constexpr int PER_INST = 64 * W;
     static_assert((BM * BK) % (NT * W) == 0 && (BK * BN) % (NT * W) == 0, "tiles must split into whole instructions");
     static constexpr int PA = BM * BK / (NT * W), PB = BK * BN / (NT * W);
+    // With up to 8 instructions per tile the lanes' offsets are kept in
+    // registers; with more (4-byte loads) they are recomputed at each load
+    // from the lane index, which an empty asm makes opaque so that the
+    // compiler cannot hoist PA + PB offsets into registers held across the
+    // K loop (they would spill).
+    static constexpr bool KEEP = PA + PB <= 8;
     rsrc_t ra;
-    uint32_t aoff[PA], boff[PB];
-    int acol[PA];
-    int wave;
+    uint32_t aoff[KEEP ? PA : 1], boff[KEEP ? PB : 1];
+    int acol[KEEP ? PA : 1];
+    int wave, lane;
+    int64_t lda, ldb;
+
+    // row and column of A's tile held by instruction p at this lane
+    __device__ __forceinline__ void a_pos(int p, int l, int &row, int &col) const {
+        const int f = (p * WAVES + wave) * PER_INST + l * W;
+        row = f / BK;
+        const int pos = f % BK;
+        col = 4 * AKLayout<BK>::chunk_pos(row, pos / 4) + pos % 4;
+    }
+    __device__ __forceinline__ uint32_t b_at(int p, int l) const {
+        const int f = (p * WAVES + wave) * PER_INST + l * W;
+        return (uint32_t)(((int64_t)(f / BN) * ldb + f % BN) * 4);
+    }
 
     __device__ __forceinline__ void init(const Args &a, int bm, int tid) {
         wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        const int lane = tid & 63;
+        lane = tid & 63;
+        lda = a.lda;
+        ldb = a.ldb;
         ra = make_rsrc(a.A + (int64_t)bm * a.lda, ((int64_t)(a.M - bm - 1) * a.lda + a.K) * 4);
+        if constexpr (KEEP) {
 #pragma unroll
-        for (int p = 0; p < PA; ++p) {
-            const int f = (p * WAVES + wave) * PER_INST + lane * W;
-            const int row = f / BK, pos = f % BK;
-            const int col = 4 * AKLayout<BK>::chunk_pos(row, pos / 4) + pos % 4;
-            aoff[p] = (uint32_t)(((int64_t)row * a.lda + col) * 4);
-            acol[p] = col;
-        }
+            for (int p = 0; p < PA; ++p) {
+                int row, col;
+                a_pos(p, lane, row, col);
+                aoff[p] = (uint32_t)(((int64_t)row * a.lda + col) * 4);
+                acol[p] = col;
+            }
 #pragma unroll
-        for (int p = 0; p < PB; ++p) {
-            const int f = (p * WAVES + wave) * PER_INST + lane * W;
-            boff[p] = (uint32_t)(((int64_t)(f / BN) * a.ldb + f % BN) * 4);
+            for (int p = 0; p < PB; ++p) boff[p] = b_at(p, lane);
         }
     }
 
@@ -1164,12 +1106,30 @@ struct DirectStage {
     }
 
     __device__ __forceinline__ void load_a(const Args &a, float *As, int k0, int p) const {
-        load_to_lds<W>(ra, As + (p * WAVES + wave) * PER_INST,
-                       k0 + acol[p] < a.K ? aoff[p] + 4u * (uint32_t)k0 : kOutOfRange);
+        uint32_t off;
+        int col;
+        if constexpr (KEEP) {
+            off = aoff[p];
+            col = acol[p];
+        } else {
+            int l = lane, row;
+            asm volatile("" : "+v"(l));
+            a_pos(p, l, row, col);
+            off = (uint32_t)(((int64_t)row * lda + col) * 4);
+        }
+        load_to_lds<W>(ra, As + (p * WAVES + wave) * PER_INST, k0 + col < a.K ? off + 4u * (uint32_t)k0 : kOutOfRange);
     }
 
     __device__ __forceinline__ void load_b(rsrc_t rb, float *Bs, int p) const {
-        load_to_lds<W>(rb, Bs + (p * WAVES + wave) * PER_INST, boff[p]);
+        uint32_t off;
+        if constexpr (KEEP) {
+            off = boff[p];
+        } else {
+            int l = lane;
+            asm volatile("" : "+v"(l));
+            off = b_at(p, l);
+        }
+        load_to_lds<W>(rb, Bs + (p * WAVES + wave) * PER_INST, off);
     }
 };
 
@@ -1292,22 +1252,21 @@ __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_o
 // Epilogue of the K-ordered kernel: register r of block (mi, ni) on lane
 // (li, lh) is tile row wm + 32 mi + 8 (r / 4) + 4 lh + r % 4, tile column
 // wn + NI li + ni.
-template <class TC, int MI, int NI>
+template <class TC, int MI, int NI, int GV = 32>
 __device__ __forceinline__ void epilogue_mfma_kc(const Args &a, int bm, int bn, int wm, int wn, int li, int lh,
                                                  const floatx16 (&acc)[MI][NI]) {
     TC st;
     st.init(a, bm, bn);
-    epilogue<MI * 16, NI>(
-        a, st,
-        [&](int v, int &r, int &c) {
-            const int i = v / 16, reg = v % 16;
-            r = wm + 32 * i + 8 * (reg >> 2) + 4 * lh + (reg & 3);
-            c = wn + NI * li;
-        },
-        [&](int v, float (&x)[NI]) {
+    auto pos = [&](int v, int &r, int &c) {
+        const int i = v / 16, reg = v % 16;
+        r = wm + 32 * i + 8 * (reg >> 2) + 4 * lh + (reg & 3);
+        c = wn + NI * li;
+    };
+    auto val = [&](int v, float (&x)[NI]) {
 #pragma unroll
-            for (int j = 0; j < NI; ++j) x[j] = acc[v / 16][j][v % 16];
-        });
+        for (int j = 0; j < NI; ++j) x[j] = acc[v / 16][j][v % 16];
+    };
+    epilogue<MI * 16, NI, TC, decltype(pos), decltype(val), GV>(a, st, pos, val);
 }
 
 // ---------------------------------------------------------------------------
@@ -1418,11 +1377,20 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     };
     auto origin = [&](int tile, int &bm, int &bn) {
         int tm, tn;
-        tile_of<2, 8>(tile, nbm, nbn, tm, tn);
+        tile_of<2, 8>(tile, nbm, nbn, a.xcd_shift, tm, tn);
         bm = tm * BM;
         bn = tn * BN;
     };
-    auto finish = [&](int bm, int bn) { epilogue_mfma_kc<TC, MI, NI>(a, bm, bn, wm, wn, li, lh, acc); };
+    // In the split builds the epilogue sits in a loop (a stream-K worker may
+    // finish a tile in either of its two K ranges), and its C offsets, which
+    // depend only on the lane, would be hoisted out of that loop and held in
+    // registers across the whole K loop.  The empty asm makes the lane's
+    // coordinates opaque at each epilogue, so they are recomputed there.
+    auto finish = [&](int bm, int bn) {
+        int li_ = li, lh_ = lh;
+        if constexpr (SPLIT) asm volatile("" : "+v"(li_), "+v"(lh_));
+        epilogue_mfma_kc<TC, MI, NI, SPLIT ? 8 : 32>(a, bm, bn, wm, wn, li_, lh_, acc);
+    };
 
     if constexpr (!SPLIT) {
         int bm, bn;
@@ -1432,31 +1400,48 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     } else {
         // A partial tile in the lanes' own order (4-float chunks,
         // consecutive threads adjacent), written and added back.
+        // Through a buffer descriptor over the one partial tile: the lane's
+        // 32-bit offset is tid * 16 and each vector's constant part goes in
+        // the scalar offset, so no 64-bit addresses are held.
+        const uint32_t lane_off = (uint32_t)tid * 16u;
         auto store_partial = [&](float *dst) {
-            float4 *mine = reinterpret_cast<float4 *>(dst);
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        mine[((i * NI + j) * 4 + q) * NT + tid] = make_float4(
-                            acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        };
-        auto add_partial = [&](const float *src_) {
-            const float4 *src = reinterpret_cast<const float4 *>(src_);
+            const rsrc_t r = make_rsrc(dst, (int64_t)BM * BN * 4);
 #pragma unroll
             for (int i = 0; i < MI; ++i)
 #pragma unroll
                 for (int j = 0; j < NI; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const float4 v = src[((i * NI + j) * 4 + q) * NT + tid];
-                        acc[i][j][4 * q] += v.x;
-                        acc[i][j][4 * q + 1] += v.y;
-                        acc[i][j][4 * q + 2] += v.z;
-                        acc[i][j][4 * q + 3] += v.w;
+                        f32x4 v;
+                        v.x = acc[i][j][4 * q];
+                        v.y = acc[i][j][4 * q + 1];
+                        v.z = acc[i][j][4 * q + 2];
+                        v.w = acc[i][j][4 * q + 3];
+                        raw_store_v4f32(v, r, lane_off, (uint32_t)(((i * NI + j) * 4 + q) * NT * 16), 0);
                     }
+        };
+        // One accumulator block (16 values) in flight at a time: issued all
+        // at once, the loads of a whole partial tile would hold as many
+        // registers again as the accumulators and spill.
+        auto add_partial = [&](const float *src) {
+            const rsrc_t r = make_rsrc(src, (int64_t)BM * BN * 4);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j) {
+                    f32x4 v[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        v[q] = raw_load_v4f32(r, lane_off, (uint32_t)(((i * NI + j) * 4 + q) * NT * 16), 0);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[i][j][4 * q] += v[q].x;
+                        acc[i][j][4 * q + 1] += v[q].y;
+                        acc[i][j][4 * q + 2] += v[q].z;
+                        acc[i][j][4 * q + 3] += v[q].w;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
         };
         auto zero = [&]() {
 #pragma unroll
@@ -1538,197 +1523,6 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
             else
                 finish(bm, bn);
         }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Persistent MFMA kernel with a deferred epilogue.  One workgroup per slot
-// (the grid is at most the resident workgroups of the chip) walks the tiles
-// blockIdx.x, blockIdx.x + gridDim.x, ... in row-major order and keeps two
-// accumulator sets.  While it runs the K loop of tile i+1 it retires tile i
-// in SL slices: at K step s it requests the old C values of slice s before
-// that step's MFMAs and combines and stores them after, so the epilogue's
-// memory traffic is spread over the next tile's matrix work instead of
-// stalling it.  When K is short and the epilogue's bytes rival
-// the product's FLOPs (16384^2 x 128: 2.2 GB of C traffic against 69 GFLOP)
-// that overlap is the whole game.  The last tile of each workgroup gets the
-// ordinary epilogue.
-// ---------------------------------------------------------------------------
-// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N-1>{}):
-// a loop whose index is a constant expression in the body.
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-template <class TC, int MI, int NI, int SL>
-struct DeferredSlice {
-    static constexpr int NV = MI * 16;  // vectors of NI columns per lane
-    static constexpr int VS = NV / SL;  // vectors per slice
-    static_assert(NV % SL == 0, "slices");
-
-    __device__ __forceinline__ static void pos(int v, int wm, int wn, int li, int lh, int &r, int &c) {
-        const int i = v / 16, reg = v % 16;
-        r = wm + MI * (8 * (reg >> 2) + 4 * lh + (reg & 3)) + i;
-        c = wn + NI * li;
-    }
-
-    // request the old values of slice S (beta != 0)
-    // The empty asm makes the lane's coordinates opaque at each call, so the
-    // compiler recomputes a slice's C offsets where they are used instead of
-    // hoisting all NV of them out of the K loop into live registers.
-    // With en == false (beta == 0) the requests are out of range: C is not
-    // read and the old values are 0, so the combine below stores alpha * acc.
-    template <int S_>
-    __device__ __forceinline__ static void request(bool en, const Args &a, const TC &st, int wm, int wn,
-                                                   int li, int lh, float (&buf)[VS][NI]) {
-        asm volatile("" : "+v"(li), "+v"(lh));
-#pragma unroll
-        for (int u = 0; u < VS; ++u) {
-            int r, c;
-            pos(S_ * VS + u, wm, wn, li, lh, r, c);
-            st.load_if(en, a, r, c, buf[u]);
-        }
-    }
-
-    // combine slice S with the old values in buf, and store
-    template <int S_>
-    __device__ __forceinline__ static void retire(const Args &a, const TC &st, int wm, int wn, int li,
-                                                  int lh, const floatx16 (&acc)[MI][NI],
-                                                  const float (&buf)[VS][NI]) {
-        asm volatile("" : "+v"(li), "+v"(lh));
-#pragma unroll
-        for (int u = 0; u < VS; ++u) {
-            const int v = S_ * VS + u;
-            int r, c;
-            pos(v, wm, wn, li, lh, r, c);
-            float out[NI];
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-                out[j] = fmaf(a.alpha, acc[v / 16][j][v % 16], a.beta * buf[u][j]);
-            st.store(a, r, c, out);
-        }
-    }
-};
-
-template <int BM, int BN, int BK, int WM, int WN, int PADA, int PADB, int VEC, int WPE, bool BUF,
-          int FD, bool SWZ, int SL>
-__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-__attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_persistent(Args a) {
-    constexpr int MI = WM / 32, NI = WN / 32;
-    constexpr int WAVES_N = BN / WN;
-    constexpr int NT = (BM / WM) * WAVES_N * 64;
-    constexpr int SA = BM + PADA, SB = BN + PADB;
-    constexpr int STAGE = BK * (SA + SB);
-    typedef Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, NI, 1, SWZ> S;
-    typedef typename S::TC TC;
-    typedef DeferredSlice<TC, MI, NI, SL> D;
-    __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
-    const int ntiles = nbm * nbn;
-    const int wm = (wave / WAVES_N) * WM, wn = (wave % WAVES_N) * WN;
-    const int li = lane & 31, lh = lane >> 5;
-    const int a_col = wm + MI * li;
-    const int b_off = BK * SA + lh * SB + wn + NI * li;
-    const int KT = (a.K + BK - 1) / BK;
-    const bool old = a.beta != 0.0f;
-
-    floatx16 acc0[MI][NI], acc1[MI][NI];
-    typename S::TA ta;
-    typename S::TB tb;
-    TC st_prev;
-    float cbuf[D::VS][NI];
-
-    // One tile into `acc`; with `pending`, retire `prev` (stored through
-    // st_prev) slice by slice along the way.  Leaves st_prev aimed at this tile.
-    auto pass = [&](floatx16(&acc)[MI][NI], const floatx16(&prev)[MI][NI], auto pending_c, int tile) {
-        constexpr bool pending = decltype(pending_c)::value;
-        const int bm = (tile / nbn) * BM, bn = (tile % nbn) * BN;
-        ta.init(a, bm, tid);
-        tb.init(a, bn, tid);
-#pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-        if (KT > 0) {
-            ta.template load<0>(a, bm, 0);
-            tb.template load<0>(a, bn, 0);
-            ta.template store<0>(smem, tid);
-            tb.template store<0>(smem + BK * SA, tid);
-        }
-        __syncthreads();
-        for (int t = 0; t < KT; ++t) {
-            const float *st = smem + (t & 1) * STAGE;
-            if (t + 1 < KT) {
-                ta.template load<0>(a, bm, (t + 1) * BK);
-                tb.template load<0>(a, bn, (t + 1) * BK);
-            }
-            // slice t of the previous tile: old values requested before this
-            // step's MFMAs, combined and stored after them
-            if (pending && t < SL) {
-                static_for<SL>([&](auto sc) {
-                    constexpr int s = decltype(sc)::value;
-                    if (s == t) D::template request<s>(old, a, st_prev, wm, wn, li, lh, cbuf);
-                });
-            }
-            mfma_tile<BK, MI, NI, SA, SB, FD, SWZ>(st, a_col, lh, st + b_off, acc);
-            // keep the slice's arithmetic and stores out of the MFMA sequence,
-            // where their values would sit in registers across it
-            if (pending) __builtin_amdgcn_sched_barrier(0);
-            if (pending && t < SL) {
-                static_for<SL>([&](auto sc) {
-                    constexpr int s = decltype(sc)::value;
-                    if (s == t) D::template retire<s>(a, st_prev, wm, wn, li, lh, prev, cbuf);
-                });
-            }
-            if (t + 1 < KT) {
-                float *nx = smem + ((t + 1) & 1) * STAGE;
-                ta.template store<0>(nx, tid);
-                tb.template store<0>(nx + BK * SA, tid);
-            }
-            __syncthreads();
-        }
-        if (pending) {
-            // the slices the K loop did not reach (K < SL * BK)
-            static_for<SL>([&](auto sc) {
-                constexpr int s = decltype(sc)::value;
-                if (s >= KT) {
-                    D::template request<s>(old, a, st_prev, wm, wn, li, lh, cbuf);
-                    D::template retire<s>(a, st_prev, wm, wn, li, lh, prev, cbuf);
-                }
-            });
-        }
-        st_prev.init(a, bm, bn);
-    };
-
-    int tile = blockIdx.x;
-    if (tile >= ntiles) return;
-    pass(acc0, acc1, std::false_type{}, tile);
-    int last = tile;
-    for (;;) {
-        tile += gridDim.x;
-        if (tile >= ntiles) {
-            epilogue_mfma<S, MI, NI>(a, (last / nbn) * BM, (last % nbn) * BN, wm, wn, li, lh, acc0);
-            return;
-        }
-        pass(acc1, acc0, std::true_type{}, tile);
-        last = tile;
-        tile += gridDim.x;
-        if (tile >= ntiles) {
-            epilogue_mfma<S, MI, NI>(a, (last / nbn) * BM, (last % nbn) * BN, wm, wn, li, lh, acc1);
-            return;
-        }
-        pass(acc0, acc1, std::true_type{}, tile);
-        last = tile;
     }
 }
 

@@ -21,8 +21,11 @@
  * given inputs is deterministic run to run.
  *
  * Pointers.  A, B and C are DEVICE pointers owned by the caller.  The library
- * allocates no memory, copies nothing and keeps no handles; it holds no state
- * between calls (split-K takes a caller-owned workspace, below).  No alignment is required: 16-byte aligned bases with leading
+ * allocates no memory, copies nothing and keeps no handles (split-K takes a
+ * caller-owned workspace, below).  Its only state is a per-device cache of
+ * the machine shape (compute units and XCDs, sgemm_device_shape), read from
+ * the device's attributes on first use; the choice of kernel depends on the
+ * sizes and that shape only.  No alignment is required: 16-byte aligned bases with leading
  * dimensions and N that are multiples of 4 take 128-bit global accesses
  * (and K a multiple of 4 for the variants that read A 128 bits at a time),
  * anything else takes 32-bit ones (see sgemm_variant_access for the three
@@ -48,7 +51,9 @@
  * does not fit one launch; -23 an unknown access mode, or one these arguments
  * do not allow; -24 a split-K or stream-K workspace that is missing, too
  * small or not 256-byte aligned; -25 a split count outside 1..64, a worker
- * count outside 1..4096, or a variant without a split-K (stream-K) build.  Argument checks run before any HIP call, so they
+ * count outside 1..4096, or a variant without a split-K (stream-K) build;
+ * -26 a machine shape or tile grid out of range (sgemm_plan_for,
+ * sgemm_tile_order).  Argument checks run before any HIP call, so they
  * need no GPU.  Positive: the hipError_t reported for the launch.  The library
  * never exits or aborts the process.
  */
@@ -78,6 +83,7 @@ extern "C" {
 #define SGEMM_ERR_ACCESS (-23)
 #define SGEMM_ERR_WORKSPACE (-24)
 #define SGEMM_ERR_SPLITS (-25)
+#define SGEMM_ERR_MACHINE (-26)
 
 /* C = alpha*A*B + beta*C, automatic choice of inner product and tile.  One
  * kernel launch, or two on the same stream when sgemm_select_rows() is
@@ -227,13 +233,43 @@ int sgemm_select_variant(int path, int M, int N, int K);
 
 /* Rows of C that sgemm() (path AUTO or MFMA), and sgemm_ws() when it
  * neither splits K nor runs stream-K, compute as a first launch of 256 x 256
- * tiles that fill their rounds of the 256 compute units; the rows below
+ * tiles that fill their rounds of the device's compute units; the rows below
  * follow in a second launch with the variant
  * sgemm_select_variant(path, M - rows, N, K).  0: one launch.  A multiple
  * of 256 below M, or a negative argument code (-1..-3).  Host logic only.
  * (Quantisation of tiles over the compute units: "如何高效实现矩阵乘？CUDA
  * 初学者的角度入门", section "Wave & L2 cache Hit Rate".) */
 int sgemm_select_rows(int M, int N, int K);
+
+/* The machine shape the current device's choices use: its compute units and
+ * XCDs, read once per device from hipDeviceAttributeMultiprocessorCount and
+ * hipDeviceAttributeNumberOfXccs (256 and 8, an MI355X, when no device can
+ * be queried, so the host-only queries above answer without a GPU; an XCD
+ * count that is not a power of two is taken as 1).  Either
+ * pointer may be NULL.  Returns 0.  (Tile quantisation over the compute
+ * units and the XCDs' separate L2 caches: "如何高效实现矩阵乘？CUDA初学者的角度
+ * 入门", section "Wave & L2 cache Hit Rate".) */
+int sgemm_device_shape(int *compute_units, int *xcds);
+
+/* The plan the library makes for these sizes on a device of
+ * `compute_units` compute units: with with_workspace != 0 what sgemm_ws()
+ * runs with enough workspace, else what sgemm() runs.  Through the pointers
+ * (each may be NULL): the variant, the split count (1: none), the stream-K
+ * worker count (0: none) and the rows of a first row-split launch (0: one
+ * launch).  Returns 0, a negative argument code (-1..-3 for M, N, K), or
+ * SGEMM_ERR_MACHINE for compute_units outside 1..2^20.  Host logic only. */
+int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int *variant,
+                   int *splits, int *workers, int *rows);
+
+/* The workgroup -> tile order of the K-ordered blocks on a device of `xcds`
+ * XCDs, for a grid of nbm x nbn tiles: workgroup p computes tile
+ * (tile_m[p], tile_n[p]).  The arrays hold nbm * nbn ints each (caller-owned
+ * host memory; may be NULL when the grid is empty).  Returns 0 or
+ * SGEMM_ERR_MACHINE (xcds not a power of two in 1..1024, a negative or too
+ * large grid, NULL arrays).
+ * Host logic only.  (Block order and L2 locality: "如何高效实现矩阵乘？CUDA
+ * 初学者的角度入门", section "Wave & L2 cache Hit Rate".) */
+int sgemm_tile_order(int xcds, int nbm, int nbn, int *tile_m, int *tile_n);
 
 /* Static text for a status code returned by any entry point above. */
 const char *sgemm_status_string(int status);

@@ -78,6 +78,42 @@ def ratio_points(p, out, rows, cols):
     return oracle.max_error_ratio(out[rows, cols], ref, den)
 
 
+def line_sample(M, N, n_lines=62, n_random=4096, seed=0):
+    """The full-size sample: whole rows {0, M-1, n_lines seeded}, whole
+    columns {0, N-1, n_lines seeded}, and n_random seeded points."""
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, n_lines)])).astype(np.int64)
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, n_lines)])).astype(np.int64)
+    pr = rng.integers(0, M, n_random).astype(np.int32)
+    pc = rng.integers(0, N, n_random).astype(np.int32)
+    return rows, cols, pr, pc
+
+
+def ratio_lines(p, out, n_lines=62, n_random=4096, seed=0):
+    """Max error ratio over whole sampled rows and columns of C plus random
+    points.  Row i of the sample is the oracle on A's row i alone (the rows
+    gathered into a small problem); column j likewise on B's column j: the
+    same products summed in the same order as over the full problem.
+    Returns (ratio, rows, cols)."""
+    M, N, K = p.M, p.N, p.K
+    rows, cols, pr, pc = line_sample(M, N, n_lines, n_random, seed)
+    A = p.A.numpy()[:, :K] if p.A.numel() else np.zeros((M, max(K, 1)), np.float32)
+    B = p.B.numpy()[:, :N] if p.B.numel() else np.zeros((max(K, 1), N), np.float32)
+    C = p.C.numpy()[:, :N] if p.beta != 0 else None
+    As = np.ascontiguousarray(A[rows]).reshape(-1)
+    Cr = np.ascontiguousarray(C[rows]).reshape(-1) if C is not None else None
+    ref, den = oracle.sgemm(len(rows), N, K, p.alpha, As, K, np.ascontiguousarray(B).reshape(-1) if
+                            p.ldb != N else p.np("B"), N, p.beta, Cr, N)
+    r_rows = oracle.max_error_ratio(out[rows, :N], ref, den)
+    Bs = np.ascontiguousarray(B[:, cols]).reshape(-1)
+    Cc = np.ascontiguousarray(C[:, cols]).reshape(-1) if C is not None else None
+    ref, den = oracle.sgemm(M, len(cols), K, p.alpha, p.np("A") if p.lda == K else
+                            np.ascontiguousarray(A).reshape(-1), K, Bs, len(cols), p.beta, Cc, len(cols))
+    r_cols = oracle.max_error_ratio(out[:, cols], ref, den)
+    r_pts = ratio_points(p, out, pr, pc)
+    return max(r_rows, r_cols, r_pts), rows, cols
+
+
 def pad_untouched(p, out):
     """Columns N..ldc-1 of C are outside the matrix and must keep their sentinel bits."""
     if p.ldc == p.N:

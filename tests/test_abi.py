@@ -351,3 +351,140 @@ def test_grid_too_large_is_refused_before_any_hip_call():
     for v in range(g.sgemm_variant_count()):
         assert g.sgemm_variant(v, *args, stream=0, check=False) == -22, v
 
+
+
+def test_device_shape_and_plan_for_256_cus():
+    """Without a GPU the library plans for an MI355X (256 CUs, 8 XCDs), and
+    the explicit-shape plan at 256 CUs is exactly what the device queries
+    return, with and without a workspace."""
+    cus, xcds = g.sgemm_device_shape()
+    assert cus > 0 and xcds >= 1 and xcds & (xcds - 1) == 0
+    import torch
+    if not torch.cuda.is_available():
+        assert (cus, xcds) == (256, 8)
+    shapes = [(256, 256, 256), (1000, 1023, 999), (1024, 1024, 1024), (2048, 2048, 2048),
+              (4096, 4096, 4096), (8192, 8192, 8192), (16384, 16384, 128), (5120, 5120, 5120),
+              (7168, 7168, 7168), (13824, 13824, 13824), (512, 512, 8192), (1536, 1536, 1536),
+              (40000, 300, 4096), (1, 1, 1), (0, 5, 5)]
+    for M, N, K in shapes:
+        rc, v, sp, w, rows = g.sgemm_plan_for(cus, M, N, K)
+        assert rc == 0 and sp == 1 and w == 0
+        assert v == g.sgemm_select_variant(g.SGEMM_PATH_AUTO, M, N, K), (M, N, K)
+        assert rows == g.sgemm_select_rows(M, N, K), (M, N, K)
+        rc, v2, sp2, w2, rows2 = g.sgemm_plan_for(cus, M, N, K, with_workspace=True)
+        assert (rc, v2, sp2, w2) == g.sgemm_ws_plan(M, N, K), (M, N, K)
+        assert sp2 == g.sgemm_select_splits(M, N, K) and w2 == g.sgemm_select_streamk(M, N, K)
+        assert rows2 == (g.sgemm_select_rows(M, N, K) if (sp2, w2) == (1, 0) else 0)
+    assert g.sgemm_plan_for(0, 4, 4, 4)[0] == -26
+    assert g.sgemm_plan_for(256, -1, 4, 4)[0] == -1
+    assert g.sgemm_plan_for(256, 4, 4, -1)[0] == -3
+    assert "machine shape" in g.sgemm_status_string(-26)
+
+
+def _block(v):
+    _, bm, bn = g.sgemm_variant_tile(v)
+    bk = int(g.sgemm_variant_name(v).split("_")[1].split("x")[2])
+    return bm, bn, bk
+
+
+def _last_round_busy(tiles, cus):
+    return tiles / (-(-tiles // cus) * cus)
+
+
+@pytest.mark.parametrize("cus", [32, 80])
+def test_plan_quantises_over_other_cu_counts(cus):
+    """On a device with another CU count (a one-XCD partition of 32 CUs, or
+    80) the same rates are weighed against that count: the chosen block has a
+    tile for every one of its workgroup slots or is the latency block, its
+    last round keeps most CUs busy, stream-K takes one worker per CU and
+    split-K aims at about two workgroups per CU."""
+    per_cu = {"_w16_kcd": 1, "x32_w128x64_kcd": 1, "_wpe4_kcd": 4, "x16_w64x128_kcd": 2,
+              "x32_w64x64_w8_kcd": 1, "64x64x32_w32x32_kcd": 4, "x64_w32x64_w8_kcd": 1,
+              "64x64x64_w32x32_kcd": 2, "x32_w64x32_w8_kcd": 2}
+    for M, N, K in [(8192, 8192, 8192), (4096, 4096, 4096), (2048, 2048, 2048), (1024, 1024, 1024),
+                    (6144, 6144, 6144), (16384, 16384, 128), (3000, 5000, 2000)]:
+        rc, v, sp, w, rows = g.sgemm_plan_for(cus, M, N, K)
+        assert rc == 0 and g.sgemm_variant_path(v) == g.SGEMM_PATH_MFMA
+        bm, bn, _ = _block(v)
+        name = g.sgemm_variant_name(v)
+        t = -(-M // bm) * -(-N // bn)
+        slots = [n for k, n in per_cu.items() if name.endswith(k)]
+        assert slots, name
+        if name != "mfma_64x64x64_w32x32_kcd":
+            assert t >= slots[0] * cus or name == "mfma_64x64x32_w32x32_kcd", (cus, M, N, K, name)
+        if t >= 4 * cus and rows == 0:
+            assert _last_round_busy(t, cus) >= 0.8, (cus, M, N, K, name, t)
+        rc, v2, sp2, w2, _ = g.sgemm_plan_for(cus, M, N, K, with_workspace=True)
+        assert w2 in (0, cus)
+        if sp2 > 1:
+            bm2, bn2, _ = _block(v2)
+            t2 = -(-M // bm2) * -(-N // bn2)
+            assert t2 <= cus and t2 * sp2 <= 2 * cus
+    # a 32-CU partition fills its CUs with 128 x 256 blocks at 1024^3, where
+    # 256 CUs need the 64 x 64 latency block
+    assert _block(g.sgemm_plan_for(32, 1024, 1024, 1024)[1])[:2] == (128, 256)
+    assert _block(g.sgemm_plan_for(256, 1024, 1024, 1024)[1])[:2] == (64, 64)
+    # split-K: 64 tiles of 64 x 64 at 512 x 512 x 8192 split in 8 on 256 CUs,
+    # in 2 on 80
+    assert g.sgemm_plan_for(256, 512, 512, 8192, True)[2] == 8
+    assert g.sgemm_plan_for(80, 512, 512, 8192, True)[2] == 2
+
+
+def test_tile_order_is_a_bijection_for_every_xcd_count():
+    """Workgroup -> tile order of the K-ordered blocks: every tile exactly
+    once for 1, 2, 4 and 8 XCDs on every grid up to 24 x 24 (and a few
+    larger); row-major when the tile columns divide evenly over the XCDs or
+    there is one XCD; otherwise XCD x (workgroups x, x + X, ...) keeps its own
+    columns x, x + X, ... until the remainder columns."""
+    grids = [(a, b) for a in range(1, 25) for b in range(1, 25)] + [(3, 11), (32, 54), (69, 69), (1, 200)]
+    for X in (1, 2, 4, 8):
+        for nbm, nbn in grids:
+            rc, tm, tn = g.sgemm_tile_order(X, nbm, nbn)
+            assert rc == 0
+            seen = set(zip(tm, tn))
+            assert len(seen) == nbm * nbn and seen == {(m, n) for m in range(nbm) for n in range(nbn)}, \
+                (X, nbm, nbn)
+            if X == 1 or nbn % X == 0 or nbn < X:
+                assert tm == [p // nbn for p in range(nbm * nbn)] and tn == [p % nbn for p in range(nbm * nbn)]
+            else:
+                own = nbm * (nbn // X)  # tiles each XCD takes in its own columns
+                for p in range(X * own):
+                    assert tn[p] % X == p % X and tn[p] < X * (nbn // X), (X, nbm, nbn, p)
+    assert g.sgemm_tile_order(3, 2, 2)[0] == -26   # not a power of two
+    assert g.sgemm_tile_order(0, 2, 2)[0] == -26
+    assert g.sgemm_tile_order(8, -1, 2)[0] == -26
+    assert g.sgemm_tile_order(8, 0, 5) == (0, [], [])
+
+
+def test_narrow_n_weighs_the_tiles_area_inside_c():
+    """Padded tile columns still issue every MFMA: with N = 260 or 300 a
+    256-wide block is 51-59% inside C, a 64 x 64 block 81-94%, and the
+    choice follows that share.  The row split's first part is 256 columns
+    wide too, so it is not taken either."""
+    for M, N, K in [(40000, 300, 4096), (65536, 260, 4096), (40000, 260, 4096), (16384, 300, 4096)]:
+        v = g.sgemm_select_variant(g.SGEMM_PATH_AUTO, M, N, K)
+        bm, bn, _ = _block(v)
+        fill = M * N / (-(-M // bm) * bm * -(-N // bn) * bn)
+        assert bn == 64 and fill >= 0.8, (M, N, K, g.sgemm_variant_name(v), fill)
+        assert g.sgemm_select_rows(M, N, K) == 0, (M, N, K)
+    # wide N keeps the 256 x 256 block and the row split where they fill C
+    assert _block(g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 8192, 8192, 8192))[:2] == (256, 256)
+    assert g.sgemm_select_rows(7168, 7168, 7168) == 6912
+
+
+def test_no_kernel_uses_scratch():
+    """Every kernel in the library keeps its state in registers and LDS: no
+    register spills to scratch memory (read from the AMDGPU metadata of the
+    built gfx950 code object)."""
+    from fp32_gemm_03_amd import build as b
+    try:
+        res = b.kernel_resources()
+    except (RuntimeError, OSError) as e:
+        pytest.skip(f"cannot read the code object: {e}")
+    assert len(res) >= 3 * g.sgemm_variant_count(), len(res)
+    names = dict(zip(res, b.demangle(res)))
+    bad = {names[k]: r for k, r in res.items()
+           if r.get("private_segment_fixed_size", -1) != 0 or r.get("vgpr_spill_count", -1) != 0}
+    assert not bad, bad
+    # the LDS each kernel declares fits a CU's 160 KiB
+    assert all(0 < r["group_segment_fixed_size"] <= 160 * 1024 for r in res.values())

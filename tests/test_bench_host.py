@@ -50,3 +50,20 @@ def test_no_parity_without_gpu_rows(bench):
     p = inputs.make_problem(64, 64, 64, dist="u01", seed=0)
     base, parity = bench.cpu_baseline(p, target_s=0.01)
     assert parity is None and base["unit"] == "TFLOP/s"
+
+
+def test_whole_problem_oracle_and_parity(bench):
+    """The secondary workloads' check: the oracle on the whole problem, every
+    element of C against it, the sample labelled as the whole problem."""
+    p = inputs.make_problem(120, 77, 45, dist="upm1", seed=5, alpha=-0.5, beta=1.5, c_fill="upm1")
+    exact = p.alpha * (p.A.double() @ p.B.double()) + p.beta * p.C.double()
+    c = exact.float().double().numpy()
+    base, parity = bench.cpu_baseline(p, gpu_rows=c, full=True)
+    assert base["sample"].startswith("the whole 120x77x45 problem")
+    assert parity["rows"] == 120 and parity["elements"] == 120 * 77 and parity["pass"]
+    assert parity["against"].startswith("every element")
+    bad = c.copy()
+    bad[119, 76] += 1e-2
+    assert not bench.cpu_baseline(p, gpu_rows=bad, full=True)[1]["pass"]
+    # every secondary workload but the band-only ones runs the whole oracle
+    assert set(bench.BAND_ONLY) <= set(bench.SECONDARY)

@@ -94,6 +94,28 @@ def test_alpha_zero_and_k_zero_give_beta_c(variant):
         assert np.all(out == 0.0), acc
 
 
+@pytest.mark.parametrize("variant", all_variants())
+def test_alpha_zero_reads_neither_a_nor_b(variant):
+    """alpha = 0: A and B are not read, so NaN and Inf in them do not reach C,
+    which is beta*C exactly (0 with beta = 0, even over NaN in C), as the
+    oracle reads it too."""
+    p = inputs.make_problem(70, 48, 33, dist="upm1", seed=6, alpha=0.0, beta=-0.5, c_fill="upm1")
+    p.A[:, ::2] = float("nan")
+    p.A[:, 1::2] = float("inf")
+    p.B[:] = float("nan")
+    ref, den = gu.oracle_full(p)
+    assert np.array_equal(ref, np.float64(-0.5) * p.C.numpy().astype(np.float64))
+    gu.say("alpha=0 NaN/Inf A, B", g.sgemm_variant_name(variant))
+    for acc, out in run_all_modes(p, variant):
+        assert np.array_equal(out, np.float32(-0.5) * p.C.numpy()), acc
+        assert gu.ratio_full(p, out, (ref, den)) == 0.0, acc
+    pz = inputs.make_problem(70, 48, 33, dist="upm1", seed=6, alpha=0.0, beta=0.0, c_fill="nan")
+    pz.A[:] = float("nan")
+    pz.B[:] = float("inf")
+    for acc, out in run_all_modes(pz, variant):
+        assert np.all(out == 0.0), acc
+
+
 # ------------------------------------------------------------------ workloads, every element
 @pytest.mark.parametrize("name", ["square256_u01", "ragged_1000x1023x999", "square1024_normal"])
 @pytest.mark.parametrize("variant", all_variants())
@@ -260,12 +282,15 @@ FULL = ["square2048_normal", "square4096_upm1", "square8192_normal", "lowk_16384
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled_auto_path(name):
+    """The full workloads through sgemm(): whole rows {0, M-1, 62 seeded},
+    whole columns {0, N-1, 62 seeded} and 4096 seeded random points against
+    the oracle."""
     p = inputs.workload_problem(name)
     gu.say("full size", name, "auto variant",
            g.sgemm_variant_name(g.sgemm_select_variant(0, p.M, p.N, p.K)))
     out = gu.run(p)
-    rows, cols = inputs.sample_points(p.M, p.N, n_random=4096, seed=17)
-    r = gu.ratio_points(p, out, rows, cols)
+    r, rows, cols = gu.ratio_lines(p, out, seed=17)
+    assert len(rows) >= 60 and len(cols) >= 60 and rows[0] == 0 and rows[-1] == p.M - 1
     assert r <= TOL, (name, r)
 
 
@@ -274,8 +299,8 @@ def test_full_size_sampled_valu_path(name):
     p = inputs.workload_problem(name)
     gu.say("full size", name, "VALU")
     out = gu.run(p, path=g.SGEMM_PATH_VALU)
-    rows, cols = inputs.sample_points(p.M, p.N, n_random=2048, seed=19)
-    assert gu.ratio_points(p, out, rows, cols) <= TOL
+    r, _, _ = gu.ratio_lines(p, out, n_lines=30, n_random=2048, seed=19)
+    assert r <= TOL
 
 
 def test_huge_leading_dimension_takes_checked_accesses():
@@ -285,8 +310,8 @@ def test_huge_leading_dimension_takes_checked_accesses():
     M, N, K, lda = 8, 64, 64, 2_200_000
     p = inputs.make_problem(M, N, K, dist="upm1", seed=23, alpha=0.75, beta=0.5, c_fill="upm1",
                             lda=lda)
-    v = 1
-    assert g.sgemm_variant_tile(v)[1] == 256
+    v = [i for i in all_variants() if g.sgemm_variant_name(i) == "mfma_256x256x32_w64x64_w16_kcd"][0]
+    assert g.sgemm_variant_tile(v)[1:] == (256, 256)
     gu.say("huge lda", lda, g.sgemm_variant_name(v))
     out = gu.run(p, variant=v)
     assert gu.ratio_full(p, out) <= TOL
@@ -329,27 +354,6 @@ def test_c_beyond_4_gib(path):
     ref, den = oracle.sgemm(len(rows), len(cols), K, alpha, As, K, Bs, len(cols), beta, Cs,
                             len(cols))
     assert oracle.max_error_ratio(got, ref, den) <= TOL
-
-
-def persistent_variants():
-    return [v for v in all_variants() if "_persist" in g.sgemm_variant_name(v)]
-
-
-@pytest.mark.parametrize("variant", persistent_variants())
-@pytest.mark.parametrize("shape", [(2900, 3000, 37), (4000, 4500, 300)])
-@pytest.mark.parametrize("beta", [0.0, -0.75])
-def test_persistent_deferred_epilogue(variant, shape, beta):
-    """More tiles than resident workgroups, so each workgroup retires one
-    tile's epilogue during the next tile's K loop: 552 tiles of 128 x 128
-    (some workgroups take 2) with K shorter than the slices, and 1152 (up to 3
-    per workgroup) with K longer; ragged edges; beta zero and not."""
-    M, N, K = shape
-    p = inputs.make_problem(M, N, K, dist="upm1", seed=37, alpha=1.25, beta=beta, c_fill="upm1")
-    gu.say("persistent", g.sgemm_variant_name(variant), shape, "beta", beta)
-    out = gu.run(p, variant=variant)
-    assert gu.ratio_full(p, out) <= TOL
-    again = gu.run(p, variant=variant)
-    assert np.array_equal(out.view(np.uint32), again.view(np.uint32))
 
 
 def random_configs(n, seed):
@@ -568,6 +572,26 @@ def test_sgemm_ws_streamk_full_size_sampled(name):
         out = oc.cpu().numpy()[first:first + p.C.numel()].reshape(p.C.shape)
         assert gu.ratio_points(p, out, rows, cols) <= TOL, workspace is not None
         del oa, ob, oc
+
+
+@pytest.mark.parametrize("offsets", [(0, 0, 0), (1, 2, 3)])
+@pytest.mark.parametrize("beta", [0.0, -0.75])
+def test_row_split_through_sgemm(offsets, beta):
+    """A shape that sgemm() splits by rows into two launches (8256 x 2047 x
+    512: the first 8192 rows on 256 x 256 tiles, the last 64 rows with their
+    own block): N % 4 != 0 and the misaligned bases take the 32-bit builds;
+    ldc is padded (its pad columns must keep their bits), nothing outside C
+    is written, beta = 0 runs over a NaN C; every element against the
+    oracle."""
+    M, N, K = 8256, 2047, 512
+    assert g.sgemm_select_rows(M, N, K) == 8192
+    p = inputs.make_problem(M, N, K, dist="upm1", seed=47, alpha=1.25, beta=beta,
+                            c_fill="upm1" if beta != 0 else "nan", lda=K + 3, ldb=N + 1, ldc=N + 5)
+    gu.say("row split via sgemm", M, N, K, "beta", beta, "offsets", offsets)
+    out = gu.run(p, offsets=offsets)
+    assert gu.pad_untouched(p, out)
+    assert np.all(np.isfinite(out[:, :N]))
+    assert gu.ratio_full(p, out) <= TOL
 
 
 @pytest.mark.parametrize("name", ["square256_u01", "ragged_1000x1023x999", "512x512x8192",

@@ -94,8 +94,9 @@ def mfma_lds_per_wave(name, bm, bn, bk, threads, kt, mi):
     return kt * reads + stored * writes, kt * (bk // 2)
 
 
-# the blocks the selection picks
-MFMA_CASES = [29, 30, 31, 32, 33, 34, 35, 36, 37]
+# the blocks the selection picks (every K-ordered block)
+MFMA_CASES = [v for v in range(g.sgemm_variant_count()) if "_kcd" in (g.sgemm_variant_name(v) or "")]
+VALU_CASES = [v for v in range(g.sgemm_variant_count()) if g.sgemm_variant_path(v) == g.SGEMM_PATH_VALU]
 # MFMA kernels whose every LDS access is its own instruction (none of the
 # chosen ones).  In the others the compiler fuses some pairs of fragment reads
 # into one ds_read2 / ds_read2st64 instruction, so the counter lies between
@@ -137,7 +138,7 @@ def test_mfma_runs_no_reduced_precision_matrix_ops():
     assert c["SQ_INSTS_VALU_MFMA_MOPS_F32"] * 512 == 2 * S ** 3
 
 
-@pytest.mark.parametrize("variant", [0, 7])
+@pytest.mark.parametrize("variant", VALU_CASES)
 def test_valu_counters_equal_design(variant):
     name, bm, bn, bk = geometry(variant)
     assert g.sgemm_variant_path(variant) == g.SGEMM_PATH_VALU
