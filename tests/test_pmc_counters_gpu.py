@@ -129,8 +129,9 @@ def test_mfma_counters_equal_design(variant):
 
 
 def test_mfma_runs_no_reduced_precision_matrix_ops():
+    v = [i for i in MFMA_CASES if g.sgemm_variant_name(i) == "mfma_256x256x32_w128x64_kcd"][0]
     c, kernel = run_pmc(["SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
-                         "SQ_INSTS_VALU_MFMA_MOPS_F16"], 29)
+                         "SQ_INSTS_VALU_MFMA_MOPS_F16"], v)
     if c is None:
         pytest.skip("bf16/f16 MFMA op counters not offered by this rocprofv3")
     assert c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] == 0
