@@ -77,7 +77,8 @@ struct Variant {
 // The table holds the blocks the choice by shape can pick (the VALU pair and
 // the K-ordered blocks) and the alternatives kept for measurement: the
 // XCD-grouped tile order, the LDS-staged epilogue and A unpadded with an XOR
-// swizzle, each on the register-staged 128 x 256 / 256 x 128 x 16 blocks.
+// swizzle, each on the register-staged 128 x 256 / 256 x 128 x 16 blocks,
+// and a four-stage LDS ring on the 256 x 256 block.
 const Variant kVariants[] = {
     VALU_CFG(128, 128, 16, 8, 8, 4, 0, 4),                         // 0: 8 x 8 per lane
     VALU_CFG(128, 256, 16, 8, 16, 4, 0, 2),                        // 1: 8 x 16 per lane
@@ -92,7 +93,18 @@ const Variant kVariants[] = {
     MFMA_CFG_KCD(128, 256, 32, 64, 64, 2, 4, false, 2, "_w8_kcd"),  // 10: 8 waves, 2 per SIMD
     MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, 1, "_kcd"),       // 11: 4 workgroups per CU
     MFMA_CFG_KCD(128, 128, 64, 32, 64, 2, 4, false, 2, "_w8_kcd"),  // 12: 8 waves, 2 per SIMD
-    MFMA_CFG_KCD(64, 64, 64, 32, 32, 2, 4, false, 1, "_kcd"),       // 13: 2 workgroups per CU
+    // 13: the block for at most one tile per CU.  Its 128-bit build is two
+    // wave groups (KG 2) of two 64 x 32 waves, each group half of every K
+    // tile: two MFMAs per k-step and wave instead of one, and per MFMA half
+    // the LDS fragment reads of four 32 x 32 waves.  Its 32-bit and checked
+    // builds are the register-staged 64 x 64 x 64 block, its split-K and
+    // stream-K builds the K-ordered one with four 32 x 32 waves.
+    {"mfma_64x64x64_w64x32_kg2_kcd", SGEMM_PATH_MFMA, 64, 64, 64, 256,
+     sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2>,
+     sgk::sgemm_mfma<64, 64, 64, 32, 32, 4, 0, 1, 2, true, 1, 2, 0, false, true>,
+     sgk::sgemm_mfma<64, 64, 64, 32, 32, 4, 0, 1, 2, false, 1, 2, 0, false, true>,
+     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1>,
+     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 1, 2, true, 1>, 1, 1},
     MFMA_CFG_KCD(128, 128, 32, 64, 32, 4, 4, false, 2, "_w8_kcd"),  // 14: 8 waves, 2 workgroups per CU
     // 15: 7 with 16 waves of 64 x 64, four per SIMD, whole tiles only: its
     // split builds would spill (55-96 registers at the 128-register cap), so
@@ -102,6 +114,16 @@ const Variant kVariants[] = {
      sgk::sgemm_mfma_kc<256, 256, 32, 64, 64, 4, 4, false, 2, 1>,
      sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, true, 1, 2, 0, false, true>,
      sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, false, 1, 2, 0, false, true>,
+     nullptr, nullptr, 1, 0},
+    // 16: 15 with K tiles of 16 in a ring of four LDS stages, each tile's
+    // loads issued three tiles ahead (sgemm_mfma_kc, STG): a measured
+    // alternative to the two-stage double buffer, 3% slower at 4096^3 and
+    // 8192^3 (twice the barriers per FLOP), so not chosen.  Its 32-bit and
+    // checked builds are the register-staged block of the same tile.
+    {"mfma_256x256x16_w64x64_w16_s4_kcd", SGEMM_PATH_MFMA, 256, 256, 16, 1024,
+     sgk::sgemm_mfma_kc<256, 256, 16, 64, 64, 4, 4, false, 2, 1, 1, 4>,
+     sgk::sgemm_mfma<256, 256, 16, 64, 64, 4, 0, 1, 4, true, 1, 2, 0, false, true>,
+     sgk::sgemm_mfma<256, 256, 16, 64, 64, 4, 0, 1, 4, false, 1, 2, 0, false, true>,
      nullptr, nullptr, 1, 0},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
@@ -115,7 +137,7 @@ constexpr int kKcShortK = 9;     // 128 x 256 x 16, two workgroups per CU
 constexpr int kKcWide = 10;      // 128 x 256 x 32, 8 waves, one workgroup per CU
 constexpr int kKcSmall4 = 11;    // 64 x 64 x 32, four workgroups per CU
 constexpr int kKcDeep8 = 12;     // 128 x 128 x 64, 8 waves, one workgroup per CU
-constexpr int kKcSmall64 = 13;   // 64 x 64 x 64, two workgroups per CU
+constexpr int kKcSmall64 = 13;   // 64 x 64 x 64, one tile per CU (two wave groups)
 constexpr int kKcMid8 = 14;      // 128 x 128 x 32, 8 waves, two workgroups per CU
 constexpr int kKcHuge16 = 15;    // 256 x 256 x 32, 16 waves, one workgroup per CU, whole tiles only
 
@@ -731,6 +753,7 @@ int sgemm_variant_reads_a128(int variant) {
     if (variant < 0 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
     return kVariants[variant].a128;
 }
+
 
 int sgemm_select_variant(int path, int M, int N, int K) {
     return select_variant(device_machine(), path, M, N, K);

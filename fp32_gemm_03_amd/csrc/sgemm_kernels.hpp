@@ -1134,18 +1134,21 @@ struct DirectStage {
 };
 
 // One K tile of MFMAs over a K-ordered A tile.  Inside the tile the k index
-// is permuted (the sum is the same in any order): k-step j of lane half lh
-// takes k = lh * BK / 2 + j, so lane (li, lh) reads A row (wm + 32 i + li)
-// as BK / 8 chunks of 4 consecutive k, one 128-bit read per chunk and block
-// row i, and B row lh * BK / 2 + j.  a_row points at the lane's row of
-// block row 0 in this stage, a_off[q] is 4 * (position of chunk q of its
-// half); bp at B row lh * BK / 2, column wn + NI * li.  hook(j, u) as in
-// mfma_tile.
-template <int BK, int MI, int NI, int SB, int FD, int CH, int RO, int PR, class Hook>
-__device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_off)[BK / 8], const float *bp,
+// is permuted (the sum is the same in any order): of the wave's KX k values
+// starting at k0, k-step j of lane half lh takes k = k0 + lh * KX / 2 + j, so
+// lane (li, lh) reads A row (wm + 32 i + li) as KX / 8 chunks of 4
+// consecutive k, one 128-bit read per chunk and block row i, and B row
+// k0 + lh * KX / 2 + j.  a_row points at the lane's row of block row 0 in
+// this stage, a_off[q] is 4 * (position of chunk q of its half); bp at B row
+// k0 + lh * KX / 2, column wn + NI * li.  hook(j, u) as in mfma_tile.
+// KX is the k extent the wave covers in this call (all of the tile, BK, or
+// its wave group's share of it); A rows stay BK floats long.
+template <int BK, int MI, int NI, int SB, int FD, int CH, int RO, int PR, int KX, class Hook>
+__device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_off)[KX / 8], const float *bp,
                                              floatx16 (&acc)[MI][NI], floatx16 (&acc_odd)[MI][NI], Hook hook) {
     typedef typename vec_t<NI>::type VB;
-    constexpr int STEPS = BK / 2, QN = BK / 8;
+    static_assert(KX % 8 == 0 && KX <= BK, "k extent: whole chunks of 4 per lane half");
+    constexpr int STEPS = KX / 2, QN = KX / 8;
     constexpr int RING = FD + 1;
     float4 av[2][MI];
     VB bv[RING];
@@ -1269,35 +1272,78 @@ __device__ __forceinline__ void epilogue_mfma_kc(const Args &a, int bm, int bn, 
     epilogue<MI * 16, NI, TC, decltype(pos), decltype(val), GV>(a, st, pos, val);
 }
 
+// The barrier that ends a K tile of the LDS ring: this wave's loads but the
+// newest N have landed (vmcnt; gfx9 encoding, vmcnt in bits 3:0 and 15:14,
+// expcnt left at its maximum), its LDS reads have returned (lgkmcnt 0:
+// nothing it read can be overwritten early), then every wave meets.
+// __syncthreads() would wrap the barrier in workgroup fences, and those wait
+// for every outstanding load that writes LDS, which would drain the ring; the
+// empty asm statements and the scheduling fences keep the compiler from
+// moving LDS accesses across the barrier instead.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+    static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---------------------------------------------------------------------------
 // MFMA kernel with A kept in K order in LDS, both tiles loaded from global
-// memory straight into LDS (16 bytes per lane when VEC == 4, else 4): the
-// next K tile's loads go after the MFMAs of the first quarter of the k-steps,
-// into the other LDS stage.  Same tiles and epilogue contract as sgemm_mfma;
-// the SPLIT build also runs split-K and stream-K (phases 0-3 of Args).  RO
-// is the order of the fragment reads at a K tile's start and PR the wave
-// priority over a K tile (mfma_tile_kc).
+// memory straight into LDS (16 bytes per lane when VEC == 4, else 4).  Same
+// tiles and epilogue contract as sgemm_mfma; the SPLIT build also runs
+// split-K and stream-K (phases 0-3 of Args).  RO is the order of the
+// fragment reads at a K tile's start and PR the wave priority over a K tile
+// (mfma_tile_kc).
+//
+// STG LDS stages form a ring ("如何高效实现矩阵乘", section "Double Buffer",
+// with two; deeper rings for tiles whose arithmetic is too short to cover
+// one load latency): the loads of K tile t + STG - 1 go, in pieces after the
+// MFMAs of the first quarter of tile t's k-steps, into the stage tile t - 1
+// was read from, and before the barrier that ends tile t each wave waits
+// only until its loads of tile t + 1 have landed, leaving the later ones in
+// flight.
+//
+// KG wave groups split every K tile: group g takes k in
+// [g BK / KG, (g + 1) BK / KG) of each tile for the whole block tile, so a
+// block tile that is the CU's only work still has KG waves per SIMD to
+// interleave (in-workgroup split-K).  The groups' partial tiles are summed
+// through LDS in group order (deterministic), and the epilogue is shared by
+// every wave of the workgroup.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, int VEC, int WPE, bool SPLIT, int RO, int PR = 0>
-__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+template <int BM, int BN, int BK, int WM, int WN, int VEC, int WPE, bool SPLIT, int RO, int PR = 0,
+          int KG = 1, int STG = 2>
+__global__ void __launch_bounds__(KG * (BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
     constexpr int WAVES_N = BN / WN;
-    constexpr int NT = (BM / WM) * WAVES_N * 64;
+    constexpr int WPG = (BM / WM) * WAVES_N;  // waves per group
+    constexpr int NT = KG * WPG * 64;
     constexpr int SB = BN;
     constexpr int ASZ = BM * BK;
     constexpr int STAGE = ASZ + BK * SB;
+    constexpr int KX = BK / KG;  // k per K tile of one group
     static_assert(MI == 1 || MI == 2 || MI == 4, "MI in {1, 2, 4}");
     static_assert(NI == 1 || NI == 2 || NI == 4, "NI in {1, 2, 4}");
+    static_assert(KG == 1 || KG == 2 || KG == 4, "KG in {1, 2, 4}");
+    static_assert(STG >= 2 && STG <= 4, "2 to 4 LDS stages");
+    static_assert(!SPLIT || KG == 1, "split-K and stream-K builds run one wave group");
+    // the groups' partial tiles, each in the lanes' own order
+    constexpr int RED = KG > 1 ? KG * BM * BN : 0;
+    constexpr int SMEM = STG * STAGE > RED ? STG * STAGE : RED;
     typedef DirectStage<BM, BN, BK, NT, VEC> D;
     typedef CStoreBuf<NI, VEC> TC;
-    __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) float smem[SMEM];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const int grp = wave / WPG, wg = wave % WPG;
     const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
     const int ntiles = nbm * nbn;
-    const int wm = (wave / WAVES_N) * WM, wn = (wave % WAVES_N) * WN;
+    const int wm = (wg / WAVES_N) * WM, wn = (wg % WAVES_N) * WN;
     const int li = lane & 31, lh = lane >> 5;
     const int KT_ALL = (a.K + BK - 1) / BK;
 
@@ -1305,20 +1351,21 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     floatx16 acc[MI][NI], acc_odd[MI][NI];
 
     // the lane's A row in a stage, its chunk positions, its B row and column
-    constexpr int QN = BK / 8;
+    constexpr int QN = KX / 8;
     const int a_row = (wm + li) * BK;
     int a_off[QN];
 #pragma unroll
-    for (int q = 0; q < QN; ++q) a_off[q] = 4 * AKLayout<BK>::chunk_pos(wm + li, lh * QN + q);
-    const int b_off = ASZ + lh * (BK / 2) * SB + wn + NI * li;
+    for (int q = 0; q < QN; ++q) a_off[q] = 4 * AKLayout<BK>::chunk_pos(wm + li, (grp * KX) / 4 + lh * QN + q);
+    const int b_off = ASZ + (grp * KX + lh * (KX / 2)) * SB + wn + NI * li;
 
-    constexpr int STEPS = BK / 2;
+    constexpr int STEPS = KX / 2;
     constexpr int LSTEPS = STEPS / 4 > 0 ? STEPS / 4 : 1;
     constexpr int NU = MI * NI;
 
-    // acc = the product of the tile at (bm, bn) over K tiles [k_lo, k_hi).
-    // Starts and ends with every wave past a barrier, so it may run again
-    // on the same LDS.
+    // acc = the product of the tile at (bm, bn) over K tiles [k_lo, k_hi)
+    // (this wave group's share of each).  Starts and ends with every wave
+    // past a barrier and every load landed, so it may run again on the same
+    // LDS.
     auto k_range = [&](int bm, int bn, int k_lo, int k_hi) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
@@ -1327,31 +1374,42 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = acc_odd[i][j][r] = 0.0f;
         const int KT = k_hi - k_lo, kb = k_lo * BK;
-        // The next K tile goes straight into the other stage (last read
-        // before the previous barrier) in pieces after the MFMAs of the first
+        // The loads of a K tile are spread over the MFMAs of the first
         // quarter of the k-steps (spreading them over a half or three
-        // quarters measured the same); a wave waits for its own loads before
-        // the barrier that hands the stage to every wave.
+        // quarters measured the same).
         constexpr int DP = D::PA + D::PB;
         constexpr int DLPER = (DP + LSTEPS - 1) / LSTEPS;
         D d;
         d.init(a, bm, tid);
-        if (KT > 0) {
-            const rsrc_t rb = d.b_rows(a, bn, kb);
+        // tiles 0 .. STG - 2 into stages 0 .. STG - 2
 #pragma unroll
-            for (int p = 0; p < D::PA; ++p) d.load_a(a, smem, kb, p);
+        for (int s = 0; s < STG - 1; ++s) {
+            if (s < KT) {
+                const rsrc_t rb = d.b_rows(a, bn, kb + s * BK);
 #pragma unroll
-            for (int p = 0; p < D::PB; ++p) d.load_b(rb, smem + ASZ, p);
+                for (int p = 0; p < D::PA; ++p) d.load_a(a, smem + s * STAGE, kb + s * BK, p);
+#pragma unroll
+                for (int p = 0; p < D::PB; ++p) d.load_b(rb, smem + s * STAGE + ASZ, p);
+            }
         }
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have written LDS
-        __syncthreads();
-        // The two stages as restrict pointers: the scoped no-alias
-        // information lets the compiler see that the reads of the current
-        // stage need not wait for the loads into the other one.
-        auto tile_body = [&](const float *__restrict__ st, float *__restrict__ nx, int kn) {
+        // this wave's loads of tile 0 have written LDS (a count beyond the
+        // counter's 63 waits for a few loads more than needed)
+        constexpr int AHEAD = (STG - 2) * DP < 63 ? (STG - 2) * DP : 63;
+        if constexpr (STG == 2) {
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        } else if (KT >= STG - 1) {
+            ring_barrier<AHEAD>();
+        } else {
+            ring_barrier<0>();
+        }
+        // The stages as restrict pointers: the scoped no-alias information
+        // lets the compiler see that the reads of the current stage need not
+        // wait for the loads into another one (the waits are explicit).
+        auto tile_body = [&](const float *__restrict__ st, float *__restrict__ nx, int kn, bool issue) {
             const rsrc_t rb = d.b_rows(a, bn, kn);
             auto hook = [&](int j, int u) {
-                if (j < LSTEPS) {
+                if (j < LSTEPS && issue) {
 #pragma unroll
                     for (int q = 0; q < DLPER; ++q) {
                         const int piece = j * DLPER + q;
@@ -1361,12 +1419,29 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
                     }
                 }
             };
-            mfma_tile_kc<BK, MI, NI, SB, 1, CH, RO, PR>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
+            mfma_tile_kc<BK, MI, NI, SB, 1, CH, RO, PR, KX>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
         };
-        for (int t = 0; t < KT; ++t) {
-            tile_body(smem + (t & 1) * STAGE, smem + ((t + 1) & 1) * STAGE, kb + (t + 1) * BK);
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
+        if constexpr (STG == 2) {
+            // the next tile is always loaded (past the last one it reads
+            // zeros or the next range's data into a stage nobody reads)
+            for (int t = 0; t < KT; ++t) {
+                tile_body(smem + (t & 1) * STAGE, smem + ((t + 1) & 1) * STAGE, kb + (t + 1) * BK, true);
+                __builtin_amdgcn_s_waitcnt(0);
+                __syncthreads();
+            }
+        } else {
+            int cur = 0, nxt = STG - 1;  // stage of tile t and of tile t + STG - 1
+            for (int t = 0; t < KT; ++t) {
+                const bool issue = t + STG - 1 < KT;
+                tile_body(smem + cur * STAGE, smem + nxt * STAGE, kb + (t + STG - 1) * BK, issue);
+                // tile t + 1 has landed; tiles t + 2 .. t + STG - 1 may still be in flight
+                if (issue)
+                    ring_barrier<AHEAD>();
+                else
+                    ring_barrier<0>();
+                cur = cur + 1 == STG ? 0 : cur + 1;
+                nxt = nxt + 1 == STG ? 0 : nxt + 1;
+            }
         }
         if (CH == 2) {
 #pragma unroll
@@ -1392,11 +1467,70 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
         epilogue_mfma_kc<TC, MI, NI, SPLIT ? 8 : 32>(a, bm, bn, wm, wn, li_, lh_, acc);
     };
 
-    if constexpr (!SPLIT) {
+    if constexpr (!SPLIT && KG == 1) {
         int bm, bn;
         origin((int)blockIdx.x, bm, bn);
         k_range(bm, bn, 0, KT_ALL);
         finish(bm, bn);
+    } else if constexpr (!SPLIT) {
+        int bm, bn;
+        origin((int)blockIdx.x, bm, bn);
+        k_range(bm, bn, 0, KT_ALL);
+        // Every wave is past the K loop's last barrier and every load has
+        // landed: the stages are free.  Group g writes its partial tile to
+        // region g in the lanes' own order: 4-float piece
+        // ((i NI + j) 4 + q) WPG 64 + 64 wg + lane holds registers 4q .. 4q + 3
+        // of block (i, j), so each write instruction of a wave fills 1 KiB of
+        // consecutive LDS.
+        constexpr int NTG = WPG * 64;  // threads per group
+        float4 *red = reinterpret_cast<float4 *>(smem) + grp * (BM * BN / 4);
+        const int tg = tid - grp * NTG;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int jj = 0; jj < NI; ++jj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    red[((i * NI + jj) * 4 + q) * NTG + tg] =
+                        make_float4(acc[i][jj][4 * q], acc[i][jj][4 * q + 1], acc[i][jj][4 * q + 2],
+                                    acc[i][jj][4 * q + 3]);
+        __syncthreads();
+        // Thread t takes pieces f = t, t + NT, ...: the sum of the groups'
+        // piece f, in group order.  Piece f holds 4 consecutive rows of one
+        // column of C (registers 4q .. 4q + 3 of a block are rows
+        // 8 q + 4 lh + 0 .. 3), stored one float at a time, 32 lanes to a
+        // 128-byte row segment as in the one-group epilogue.
+        constexpr int F4 = BM * BN / 4, PER = F4 / NT;
+        static_assert(F4 % NT == 0, "the tile splits into whole 4-float pieces per thread");
+        CStoreBuf<1, VEC> st;
+        st.init(a, bm, bn);
+        auto pos = [&](int v, int &r, int &c) {
+            const int f = tid + NT * (v / 4), e = v % 4;
+            const int blk = f / (4 * NTG), q = (f / NTG) % 4, t = f % NTG;
+            const int i = blk / NI, jj = blk % NI, w = t / 64, l = t % 64;
+            r = (w / WAVES_N) * WM + 32 * i + 8 * q + 4 * (l >> 5) + e;
+            c = (w % WAVES_N) * WN + NI * (l & 31) + jj;
+        };
+        float4 sum[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const float4 *src = reinterpret_cast<const float4 *>(smem) + tid + NT * u;
+            sum[u] = src[0];
+#pragma unroll
+            for (int g = 1; g < KG; ++g) {
+                const float4 w = src[g * (BM * BN / 4)];
+                sum[u].x += w.x;
+                sum[u].y += w.y;
+                sum[u].z += w.z;
+                sum[u].w += w.w;
+            }
+        }
+        auto val = [&](int v, float (&x)[1]) {
+            const float4 &p4 = sum[v / 4];
+            const int e = v % 4;
+            x[0] = e == 0 ? p4.x : e == 1 ? p4.y : e == 2 ? p4.z : p4.w;
+        };
+        epilogue<4 * PER, 1, decltype(st), decltype(pos), decltype(val)>(a, st, pos, val);
     } else {
         // A partial tile in the lanes' own order (4-float chunks,
         // consecutive threads adjacent), written and added back.

@@ -126,6 +126,19 @@ def pad_untouched(p, out):
 ACCESS_NAMES = {0: "auto", 1: "buf128", 2: "buf32", 3: "checked"}
 
 
+def sum_family(variant, access):
+    """Which kernel a build of a variant runs, as far as the order of its sums
+    goes: the K-ordered direct-load kernel ("kc", the 128-bit builds of the
+    ``_kcd`` variants) or the register-staged one ("rs", every other build:
+    their 32-bit and checked builds, and every build of the others)."""
+    name = g.sgemm_variant_name(variant)
+    return "kc" if name.endswith("_kcd") and access == g.SGEMM_ACCESS_BUFFER_128 else "rs"
+
+
+def same_sum_order(variant, a1, a2):
+    return sum_family(variant, a1) == sum_family(variant, a2)
+
+
 def allowed_accesses(p, offsets=(0, 0, 0), variant=None):
     """The access modes whose preconditions these arguments meet for a
     variant (the test operands are small, so the 31-bit offset bound always

@@ -488,3 +488,4 @@ def test_no_kernel_uses_scratch():
     assert not bad, bad
     # the LDS each kernel declares fits a CU's 160 KiB
     assert all(0 < r["group_segment_fixed_size"] <= 160 * 1024 for r in res.values())
+

@@ -235,10 +235,14 @@ def test_zero_padding_invariance(variant):
     # the 32-bit build here): the same arithmetic
     large = gu.run(big, variant=variant)
     assert np.array_equal(small.view(np.uint32), large[:200, :301].copy().view(np.uint32))
-    # every access mode computes the same sums in the same order
+    # the access modes of one kernel family compute the same sums in the same
+    # order (bit for bit); a build of the other family is held to the pass rule
     for acc in gu.allowed_accesses(big, variant=variant):
         other = gu.run(big, variant=variant, access=acc)
-        assert np.array_equal(other.view(np.uint32), large.view(np.uint32)), acc
+        if gu.same_sum_order(variant, acc, g.SGEMM_ACCESS_BUFFER_32):
+            assert np.array_equal(other.view(np.uint32), large.view(np.uint32)), acc
+        else:
+            assert gu.ratio_full(big, other) <= TOL, acc
 
 
 def test_runs_on_a_side_stream():

@@ -86,8 +86,18 @@ def mfma_lds_per_wave(name, bm, bn, bk, threads, kt, mi):
     k-step (BK / 2, which may fuse in pairs); no LDS store instruction (the
     buffer loads write LDS themselves)."""
     if "_kcd" in name:
-        reads = mi * bk // 8 + bk // 2
-        return kt * reads, kt * (bk // 4)
+        # with KG wave groups (``_kgN``) each wave covers bk / KG of every K
+        # tile, then writes its 32 x 32 blocks to LDS once (four 128-bit
+        # writes per block) and reads, per 4-float piece of the tile it
+        # stores, that piece of every group (one 128-bit read each)
+        kg = int(name.split("_kg")[1].split("_")[0]) if "_kg" in name else 1
+        kx = bk // kg
+        reads = mi * kx // 8 + kx // 2
+        per, pairs = kt * reads, kt * (kx // 4)
+        if kg > 1:
+            blocks = (bm * bn // (32 * 32)) // (threads // 64 // kg)  # 32 x 32 blocks per wave
+            per += 4 * blocks + kg * (bm * bn // 4) // threads
+        return per, pairs
     reads = 2 * (bk // 2)
     writes = bm * bk // (4 * threads) + bk * bn // (4 * threads)
     stored = kt + 1 if "_il" in name else kt
@@ -111,7 +121,8 @@ def test_mfma_counters_equal_design(variant):
     c, kernel = run_pmc(["SQ_LDS_BANK_CONFLICT", "SQ_INSTS_LDS", "SQ_INSTS_MFMA",
                          "SQ_INSTS_VALU_MFMA_MOPS_F32"], variant)
     wm, wn = (int(x) for x in name.split("_w")[1].split("_")[0].split("x"))
-    waves_per_wg = (bm // wm) * (bn // wn)
+    kg = int(name.split("_kg")[1].split("_")[0]) if "_kg" in name else 1
+    waves_per_wg = kg * (bm // wm) * (bn // wn)
     threads = 64 * waves_per_wg
     tiles = (S // bm) * (S // bn)
     kt = S // bk
