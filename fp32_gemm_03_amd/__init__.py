@@ -22,7 +22,7 @@ __all__ = [
     "SGEMM_PATH_AUTO", "SGEMM_PATH_VALU", "SGEMM_PATH_MFMA",
     "SGEMM_ACCESS_AUTO", "SGEMM_ACCESS_BUFFER_128", "SGEMM_ACCESS_BUFFER_32",
     "SGEMM_ACCESS_CHECKED", "sgemm_variant_access",
-    "sgemm_ws", "sgemm_workspace_size", "sgemm_select_splits", "sgemm_splitk",
+    "sgemm_ws", "sgemm_ws_noalloc", "SGEMM_NOALLOC_SCRATCH_BYTES", "sgemm_workspace_size", "sgemm_select_splits", "sgemm_splitk",
     "sgemm_splitk_workspace_size", "sgemm_streamk", "sgemm_streamk_workspace_size",
     "sgemm_select_streamk", "sgemm_ws_plan", "sgemm_select_rows", "sgemm_plan_for",
     "sgemm_device_shape", "sgemm_tile_order",
@@ -86,6 +86,8 @@ def load_library():
         ws_args = [i, i, i, f, vp, i, vp, i, f, vp, i, vp, ctypes.c_size_t, vp]
         lib.sgemm_ws.argtypes = ws_args
         lib.sgemm_ws.restype = i
+        lib.sgemm_ws_noalloc.argtypes = gemm_args
+        lib.sgemm_ws_noalloc.restype = i
         lib.sgemm_splitk.argtypes = [i, i] + ws_args
         lib.sgemm_splitk.restype = i
         lib.sgemm_workspace_size.argtypes = [i, i, i]
@@ -208,6 +210,17 @@ def sgemm_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace=None, works
     lib = load_library()
     return _ret(lib.sgemm_ws(*_ws_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace,
                                        workspace_bytes, stream)), "sgemm_ws", check)
+
+
+SGEMM_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def sgemm_ws_noalloc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=None, check=True):
+    """sgemm_ws() with its partial tiles in the library's static device scratch (no
+    workspace, no allocation); SGEMM_ERR_SCRATCH (-27) when the plan needs more."""
+    lib = load_library()
+    return _ret(lib.sgemm_ws_noalloc(*_gemm_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)),
+                "sgemm_ws_noalloc", check)
 
 
 def sgemm_splitk(variant, splits, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, workspace=None,

@@ -186,6 +186,37 @@ Machine device_machine() {
     return shape[dev];
 }
 
+// The scratch of sgemm_ws_noalloc: the split-K / stream-K partial tiles of
+// one call, in a file-scope device array (one per GPU, held until the
+// process ends) instead of a caller's workspace.  Its address comes from
+// hipGetSymbolAddress, once per device with that device current: in host
+// code the array's name is only a host-side stand-in.
+constexpr size_t kScratchBytes = SGEMM_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) float scratch[kScratchBytes / sizeof(float)];
+
+struct ScratchPtr {
+    void *ptr;
+    int err;  // hipError_t of the lookup
+};
+
+ScratchPtr scratch_for_device() {
+    static std::once_flag once[kMaxDevices];
+    static ScratchPtr cache[kMaxDevices];
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return {nullptr, e != hipSuccess ? (int)e : (int)hipErrorInvalidDevice};
+    }
+    std::call_once(once[dev], [dev]() {
+        void *p = nullptr;
+        const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) (void)hipGetLastError();
+        cache[dev] = {err == hipSuccess ? p : nullptr, (int)err};
+    });
+    return cache[dev];
+}
+
 // log2 of a power of two
 int log2_of(int x) {
     int s = 0;
@@ -730,6 +761,27 @@ int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const fl
                   ldb, beta, C, ldc, stream);
 }
 
+int sgemm_ws_noalloc(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+                     float beta, float *C, int ldc, hipStream_t stream) {
+    const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (rc != SGEMM_OK) return rc;
+    const Machine m = device_machine();
+    int v = 0, sp = 1, w = 0;
+    const int prc = plan(m, M, N, K, true, &v, &sp, &w, nullptr);
+    if (prc != SGEMM_OK) return prc;
+    // the bytes sgemm_ws would use with enough workspace (none when there is
+    // no product to split)
+    size_t need = 0;
+    if (M > 0 && N > 0 && K > 0 && alpha != 0.0f)
+        need = w > 0 ? streamk_bytes(kVariants[v], w) : (sp > 1 ? splitk_bytes(kVariants[v], sp, M, N) : 0);
+    if (need > kScratchBytes) return SGEMM_ERR_SCRATCH;
+    if (need == 0) return sgemm_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, nullptr, 0, stream);
+    const ScratchPtr s = scratch_for_device();
+    if (s.ptr == nullptr) return s.err != 0 ? s.err : (int)hipErrorInvalidSymbol;
+    // the same plan as sgemm_ws with a workspace of `need` bytes or more
+    return sgemm_ws(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s.ptr, kScratchBytes, stream);
+}
+
 int sgemm_variant_count(void) { return kNumVariants; }
 
 const char *sgemm_variant_name(int variant) {
@@ -779,6 +831,9 @@ const char *sgemm_status_string(int status) {
         case SGEMM_ERR_SPLITS:
             return "invalid argument: split or worker count out of range, or variant without split-K or stream-K";
         case SGEMM_ERR_MACHINE: return "invalid argument: machine shape or tile grid out of range";
+        case SGEMM_ERR_SCRATCH:
+            return "problem too large for sgemm_ws_noalloc: its plan needs more scratch than the library's static "
+                   "buffer holds (use sgemm_ws with a workspace, or sgemm)";
         default: break;
     }
     if (status > 0) return hipGetErrorString((hipError_t)status);

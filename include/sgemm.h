@@ -53,7 +53,8 @@
  * small or not 256-byte aligned; -25 a split count outside 1..64, a worker
  * count outside 1..4096, or a variant without a split-K (stream-K) build;
  * -26 a machine shape or tile grid out of range (sgemm_plan_for,
- * sgemm_tile_order).  Argument checks run before any HIP call, so they
+ * sgemm_tile_order); -27 a plan that needs more scratch than
+ * sgemm_ws_noalloc's static buffer holds.  Argument checks run before any HIP call, so they
  * need no GPU.  Positive: the hipError_t reported for the launch.  The library
  * never exits or aborts the process.
  */
@@ -84,6 +85,7 @@ extern "C" {
 #define SGEMM_ERR_WORKSPACE (-24)
 #define SGEMM_ERR_SPLITS (-25)
 #define SGEMM_ERR_MACHINE (-26)
+#define SGEMM_ERR_SCRATCH (-27)
 
 /* C = alpha*A*B + beta*C, automatic choice of inner product and tile.  One
  * kernel launch, or two on the same stream when sgemm_select_rows() is
@@ -146,6 +148,28 @@ int sgemm_variant_access(int variant, int access, int M, int N, int K,
 int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda,
              const float *B, int ldb, float beta, float *C, int ldc,
              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---- no allocation at all --------------------------------------------------
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Exactly sgemm_ws() with enough workspace (the same plan and
+ * kernels, so the same results bit for bit), with the split-K / stream-K
+ * partial tiles kept in a static device array of the library,
+ * SGEMM_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held from the first call on
+ * that GPU until the process ends.  That covers every split-K plan and
+ * stream-K on the 64 x 64 and 128 x 128 blocks; a plan that needs more
+ * (stream-K on the 128 x 256 and 256 x 256 blocks of large squares, 64 and
+ * 128 MiB) returns SGEMM_ERR_SCRATCH before any HIP call: use sgemm_ws() with
+ * a workspace, or sgemm().  The call allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine); its first call on a GPU looks the array's
+ * address up once.  The array needs no clearing: a call writes every partial
+ * tile it reads.  Calls on one GPU share the array, so calls that overlap in
+ * time on one GPU (different streams, not ordered) race and give wrong
+ * results; calls on one stream are ordered and safe. */
+#define SGEMM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int sgemm_ws_noalloc(int M, int N, int K, float alpha, const float *A, int lda,
+                     const float *B, int ldb, float beta, float *C, int ldc,
+                     hipStream_t stream);
 
 /* Workspace bytes sgemm_ws() can use for these sizes (0: it never splits). */
 size_t sgemm_workspace_size(int M, int N, int K);

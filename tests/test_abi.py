@@ -489,3 +489,19 @@ def test_no_kernel_uses_scratch():
     # the LDS each kernel declares fits a CU's 160 KiB
     assert all(0 < r["group_segment_fixed_size"] <= 160 * 1024 for r in res.values())
 
+
+def test_noalloc_entry_point_checks_before_any_hip_call():
+    """sgemm_ws_noalloc validates like sgemm_ws, and refuses a plan whose
+    partial tiles exceed its static scratch (stream-K on 256 x 256 tiles of
+    7168^3 needs 128 MiB) before touching the (fake) pointers or a GPU."""
+    assert g.SGEMM_NOALLOC_SCRATCH_BYTES == 32 << 20
+    args = lambda M, N, K: (M, N, K, 1.0, 0x1000, K, 0x2000, N, 0.0, 0x3000, N)
+    assert g.sgemm_ws_noalloc(*args(-1, 4, 4), stream=0, check=False) == -1
+    assert g.sgemm_ws_noalloc(*args(7168, 7168, 7168), stream=0, check=False) == -27
+    assert g.sgemm_workspace_size(7168, 7168, 7168) > g.SGEMM_NOALLOC_SCRATCH_BYTES
+    assert "static buffer" in g.sgemm_status_string(-27)
+    # quick returns need no scratch and no launch
+    assert g.sgemm_ws_noalloc(0, 5, 5, 1.0, 0, 5, 0x2000, 5, 0.0, 0, 5, stream=0, check=False) == 0
+    # every split-K plan fits: at most two partial 64 x 64 tiles per CU
+    for M, N, K in [(512, 512, 8192), (256, 256, 4096), (1024, 1024, 4096), (64, 64, 16384), (1536, 1536, 1536)]:
+        assert 0 < g.sgemm_workspace_size(M, N, K) <= g.SGEMM_NOALLOC_SCRATCH_BYTES, (M, N, K)
