@@ -784,6 +784,16 @@ int sgemm_ws_noalloc(int M, int N, int K, float alpha, const float *A, int lda, 
 
 int sgemm_variant_count(void) { return kNumVariants; }
 
+#ifdef SGEMM_PHASES
+// The phase log of the measurement build (fp32_gemm_03_amd/phases.py): n
+// words, 8 per workgroup of the last launch, into host memory.
+int sgemm_phase_read(unsigned long long *host, int n) {
+    if (host == nullptr || n < 0 || n > sgk::kPhaseWorkgroups * sgk::kPhaseSlots) return SGEMM_ERR_MACHINE;
+    return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(sgk::sgemm_phase_log), (size_t)n * 8, 0,
+                                    hipMemcpyDeviceToHost);
+}
+#endif
+
 const char *sgemm_variant_name(int variant) {
     if (variant < 0 || variant >= kNumVariants) return nullptr;
     return kVariants[variant].name;

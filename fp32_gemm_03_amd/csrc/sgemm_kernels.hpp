@@ -97,6 +97,61 @@ __device__ __forceinline__ float vget(const float4 &v, int i) {
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
+// Phase stamps, for a measurement build only (compiled with SGEMM_PHASES; in
+// the library itself every method is empty and no code is generated).  Lane
+// 0 of each workgroup's first wave records, per workgroup: the shader clock
+// (s_memtime) at entry, after the first K tile has landed, after the K loop
+// and after the epilogue's stores have completed; the sums over the K tiles
+// of the tile body (MFMAs and the next tile's loads) and of the wait and
+// barrier that end it; and the 100 MHz real-time clock at entry and at the
+// end.  sgemm_phase_read copies the log out.
+// ---------------------------------------------------------------------------
+#ifdef SGEMM_PHASES
+constexpr int kPhaseSlots = 8;
+constexpr int kPhaseWorkgroups = 65536;
+__device__ unsigned long long sgemm_phase_log[kPhaseWorkgroups * kPhaseSlots];
+
+struct PhaseLog {
+    unsigned long long t0 = 0, t1 = 0, body = 0, wait = 0;
+    static __device__ __forceinline__ bool lead() { return threadIdx.x == 0 && blockIdx.x < kPhaseWorkgroups; }
+    static __device__ __forceinline__ void put(int slot, unsigned long long v) {
+        if (lead()) sgemm_phase_log[blockIdx.x * kPhaseSlots + slot] = v;
+    }
+    __device__ __forceinline__ void entry() {
+        put(0, __builtin_amdgcn_s_memtime());
+        put(6, __builtin_amdgcn_s_memrealtime());
+    }
+    __device__ __forceinline__ void landed() { put(1, __builtin_amdgcn_s_memtime()); }
+    __device__ __forceinline__ void tile_begin() { t0 = __builtin_amdgcn_s_memtime(); }
+    __device__ __forceinline__ void tile_mid() {
+        t1 = __builtin_amdgcn_s_memtime();
+        body += t1 - t0;
+    }
+    __device__ __forceinline__ void tile_end() { wait += __builtin_amdgcn_s_memtime() - t1; }
+    __device__ __forceinline__ void looped() {
+        put(2, __builtin_amdgcn_s_memtime());
+        put(4, body);
+        put(5, wait);
+    }
+    __device__ __forceinline__ void stored() {
+        __builtin_amdgcn_s_waitcnt(0);  // the epilogue's stores have completed
+        put(3, __builtin_amdgcn_s_memtime());
+        put(7, __builtin_amdgcn_s_memrealtime());
+    }
+};
+#else
+struct PhaseLog {
+    __device__ __forceinline__ void entry() {}
+    __device__ __forceinline__ void landed() {}
+    __device__ __forceinline__ void tile_begin() {}
+    __device__ __forceinline__ void tile_mid() {}
+    __device__ __forceinline__ void tile_end() {}
+    __device__ __forceinline__ void looped() {}
+    __device__ __forceinline__ void stored() {}
+};
+#endif
+
+// ---------------------------------------------------------------------------
 // Raw buffer accesses.  A descriptor covers [base, base + bytes); an access at
 // a byte offset >= bytes reads 0 / writes nothing.  kOutOfRange is above every
 // extent used here (extents are clamped below 2^31).
@@ -886,6 +941,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
     typedef Staging<BUF, BM, BN, BK, NT, PADA, PADB, VEC, NI, 1, SWZ> S;
     __shared__ __attribute__((aligned(16))) float smem[2 * STAGE];
 
+    PhaseLog ph;
+    ph.entry();
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int nbm = (a.M + BM - 1) / BM, nbn = (a.N + BN - 1) / BN;
@@ -938,7 +995,9 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
             tb.template store<0>(smem + BK * SA, tid);
         }
         __syncthreads();
+        ph.landed();
         for (int t = 0; t < KT; ++t) {
+            ph.tile_begin();
             const float *st = smem + (t & 1) * STAGE;
             float *nx = smem + ((t + 1) & 1) * STAGE;
             const int kn = (t + 1) * BK;
@@ -967,7 +1026,9 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
                 }
             };
             mfma_tile<BK, MI, NI, SA, SB, FD, SWZ, CH>(st, a_col, lh, st + b_off, acc, acc_odd, hook);
+            ph.tile_mid();
             __syncthreads();
+            ph.tile_end();
         }
     } else {
         if (KT > 0) {
@@ -977,7 +1038,9 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
             tb.template store<0>(smem + BK * SA, tid);
         }
         __syncthreads();
+        ph.landed();
         for (int t = 0; t < KT; ++t) {
+            ph.tile_begin();
             const float *st = smem + (t & 1) * STAGE;
             if (t + 1 < KT) {
                 ta.template load<0>(a, bm, (t + 1) * BK);
@@ -989,9 +1052,12 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
                 ta.template store<0>(nx, tid);
                 tb.template store<0>(nx + BK * SA, tid);
             }
+            ph.tile_mid();
             __syncthreads();
+            ph.tile_end();
         }
     }
+    ph.looped();
 
     if (CH == 2) {
 #pragma unroll
@@ -1004,6 +1070,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         // the checked C accesses are branches, each load waited for in its
         // own branch: few old values in flight, or they spill
         epilogue_mfma<S, MI, NI, BUF ? 32 : 8>(a, bm, bn, wm, wn, li, lh, acc);
+        ph.stored();
     } else {
         static_assert(EPI == 0 || (BM / WM) * (BN / WN) * 16 * (WN + 4) <= 2 * STAGE,
                       "staged epilogue needs 16 x (WN + 4) floats of LDS per wave");
@@ -1011,6 +1078,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma(Args a) {
         st4.init(a, bm, bn);
         epilogue_mfma_staged<decltype(st4), MI, NI, WN>(a, st4, smem + wave * 16 * (WN + 4), wm, wn,
                                                          li, lh, lane, acc);
+        ph.stored();
     }
 }
 
@@ -1338,6 +1406,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     typedef CStoreBuf<NI, VEC> TC;
     __shared__ __attribute__((aligned(16))) float smem[SMEM];
 
+    PhaseLog ph;  // whole-tile builds only
+    if (!SPLIT) ph.entry();
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int grp = wave / WPG, wg = wave % WPG;
@@ -1403,6 +1473,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
         } else {
             ring_barrier<0>();
         }
+        if (!SPLIT) ph.landed();
         // The stages as restrict pointers: the scoped no-alias information
         // lets the compiler see that the reads of the current stage need not
         // wait for the loads into another one (the waits are explicit).
@@ -1425,20 +1496,26 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
             // the next tile is always loaded (past the last one it reads
             // zeros or the next range's data into a stage nobody reads)
             for (int t = 0; t < KT; ++t) {
+                if (!SPLIT) ph.tile_begin();
                 tile_body(smem + (t & 1) * STAGE, smem + ((t + 1) & 1) * STAGE, kb + (t + 1) * BK, true);
+                if (!SPLIT) ph.tile_mid();
                 __builtin_amdgcn_s_waitcnt(0);
                 __syncthreads();
+                if (!SPLIT) ph.tile_end();
             }
         } else {
             int cur = 0, nxt = STG - 1;  // stage of tile t and of tile t + STG - 1
             for (int t = 0; t < KT; ++t) {
                 const bool issue = t + STG - 1 < KT;
+                if (!SPLIT) ph.tile_begin();
                 tile_body(smem + cur * STAGE, smem + nxt * STAGE, kb + (t + STG - 1) * BK, issue);
+                if (!SPLIT) ph.tile_mid();
                 // tile t + 1 has landed; tiles t + 2 .. t + STG - 1 may still be in flight
                 if (issue)
                     ring_barrier<AHEAD>();
                 else
                     ring_barrier<0>();
+                if (!SPLIT) ph.tile_end();
                 cur = cur + 1 == STG ? 0 : cur + 1;
                 nxt = nxt + 1 == STG ? 0 : nxt + 1;
             }
@@ -1471,11 +1548,14 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
         int bm, bn;
         origin((int)blockIdx.x, bm, bn);
         k_range(bm, bn, 0, KT_ALL);
+        ph.looped();
         finish(bm, bn);
+        ph.stored();
     } else if constexpr (!SPLIT) {
         int bm, bn;
         origin((int)blockIdx.x, bm, bn);
         k_range(bm, bn, 0, KT_ALL);
+        ph.looped();
         // Every wave is past the K loop's last barrier and every load has
         // landed: the stages are free.  Group g writes its partial tile to
         // region g in the lanes' own order: 4-float piece
@@ -1531,6 +1611,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
             x[0] = e == 0 ? p4.x : e == 1 ? p4.y : e == 2 ? p4.z : p4.w;
         };
         epilogue<4 * PER, 1, decltype(st), decltype(pos), decltype(val)>(a, st, pos, val);
+        ph.stored();
     } else {
         // A partial tile in the lanes' own order (4-float chunks,
         // consecutive threads adjacent), written and added back.
