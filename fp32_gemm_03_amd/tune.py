@@ -1,7 +1,7 @@
 """Time every compiled kernel variant on a set of shapes and compare each
 shape's fastest variant with the one the library's selection picks.
 
-    python -m fp32_gemm_03_amd.tune [--shapes S1,S2,...] [--variants V1,V2,...] [--vendor]
+    python -m fp32_gemm_03_amd.tune [--shapes S1,S2,...] [--variants V1,V2,...]
 
 A shape is a named synthetic workload (``square8192_normal`` ...) or MxNxK
 (A, B ~ N(0,1), seed 3, alpha 1, beta 0).  Every launch goes through the C
@@ -12,10 +12,7 @@ two rows time the library's own choice: ``auto`` (``sgemm``) and ``auto+ws``
 (``sgemm_ws`` with the workspace it asks for, which may split K or share the
 K tiles of a last partial round of tiles over stream-K workers).  The last block is a table of the selection
 against the best variant per shape: the measurement the selection table in
-``sgemm.hip`` was fitted to, repeatable on any MI355X.  With ``--vendor`` a
-further row times the platform BLAS (``torch.mm`` / ``torch.addmm`` with TF32
-off) on the same operands and stream, and a last table sets it beside
-``auto+ws``.
+``sgemm.hip`` was fitted to, repeatable on any MI355X.
 """
 from __future__ import annotations
 
@@ -80,14 +77,11 @@ def _time(launch, flops, stream, target_s=0.1, warmup_s=0.03):
     return ms, flops / (ms * 1e-3) / 1e12
 
 
-def tune(shapes, variants=None, out=sys.stdout, vendor=False):
+def tune(shapes, variants=None, out=sys.stdout):
     import torch
     import fp32_gemm_03_amd as g
 
     g.load_library()
-    if vendor:
-        # the platform BLAS in true FP32, for comparison only
-        torch.backends.cuda.matmul.allow_tf32 = False
     if variants is None:
         variants = list(range(g.sgemm_variant_count()))
     stream = torch.cuda.Stream()
@@ -109,26 +103,10 @@ def tune(shapes, variants=None, out=sys.stdout, vendor=False):
         ms, tf = _time(lambda: g.sgemm_ws(*args, workspace=ws, workspace_bytes=ws_bytes,
                                           stream=stream), flops, stream)
         rows["auto+ws"] = (ms, tf)
-        if vendor:
-            av, bv = a[:, :p.K], b[:, :p.N]
-            cv = c[:, :p.N].contiguous()
-            out_c = torch.empty_like(cv)
-
-            def blas():
-                with torch.cuda.stream(stream):
-                    if p.beta == 0:
-                        torch.mm(av, bv, out=out_c)
-                    else:
-                        torch.addmm(cv, av, bv, beta=p.beta, alpha=p.alpha, out=out_c)
-                    if p.beta == 0 and p.alpha != 1:
-                        out_c.mul_(p.alpha)
-            ms, tf = _time(blas, flops, stream)
-            rows["vendor_blas"] = (ms, tf)
-            del out_c, cv
         _, ws_variant, splits, workers = g.sgemm_ws_plan(p.M, p.N, p.K)
         for name, (ms, tf) in rows.items():
             print(f"{shape:24s} {name:34s} {tf:8.2f} TFLOP/s {ms:10.4f} ms", file=out, flush=True)
-        forced = {k: v for k, v in rows.items() if k not in ("auto", "auto+ws", "vendor_blas")}
+        forced = {k: v for k, v in rows.items() if k not in ("auto", "auto+ws")}
         best = min(forced, key=lambda k: forced[k][0])
         selected = g.sgemm_variant_name(auto)
         rows_first = g.sgemm_select_rows(p.M, p.N, p.K)
@@ -141,8 +119,7 @@ def tune(shapes, variants=None, out=sys.stdout, vendor=False):
                       "splits": splits, "workers": workers,
                       "auto_ms": rows["auto"][0], "auto_ws_ms": rows["auto+ws"][0],
                       "best": best, "best_ms": forced[best][0],
-                      "auto_ws_tflops": rows["auto+ws"][1], "auto_tflops": rows["auto"][1],
-                      "vendor_tflops": rows["vendor_blas"][1] if vendor else None})
+                      "auto_ws_tflops": rows["auto+ws"][1], "auto_tflops": rows["auto"][1]})
         del a, b, c, ws, p
         torch.cuda.empty_cache()
     print("\n| shape | selected (`sgemm`) | with workspace (`sgemm_ws`: splits, stream-K workers) | "
@@ -152,12 +129,6 @@ def tune(shapes, variants=None, out=sys.stdout, vendor=False):
         print(f"| {r['shape']} | {r['selected']} | {r['selected_ws']} ({r['splits']}, {r['workers']}) | "
               f"{r['auto_tflops']:.2f} | {r['auto_ws_tflops']:.2f} | "
               f"{r['best']} | {r['best_ms'] / r['auto_ws_ms']:.3f} |", file=out)
-    if vendor:
-        print("\n| shape | auto+ws TFLOP/s | vendor BLAS TFLOP/s (TF32 off) | ratio |", file=out)
-        print("|---|---|---|---|", file=out)
-        for r in table:
-            print(f"| {r['shape']} | {r['auto_ws_tflops']:.2f} | {r['vendor_tflops']:.2f} | "
-                  f"{r['auto_ws_tflops'] / r['vendor_tflops']:.3f} |", file=out)
     print(json.dumps(table), file=out, flush=True)
     return table
 
@@ -166,12 +137,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--shapes", default=",".join(DEFAULT_SHAPES))
     ap.add_argument("--variants", default=None, help="comma-separated variant indices (default: all)")
-    ap.add_argument("--vendor", action="store_true",
-                    help="also time the platform BLAS (torch.mm / torch.addmm, TF32 off) on the same "
-                         "operands and stream, for comparison")
     args = ap.parse_args()
     variants = None if args.variants is None else [int(x) for x in args.variants.split(",")]
-    tune(args.shapes.split(","), variants, vendor=args.vendor)
+    tune(args.shapes.split(","), variants)
 
 
 if __name__ == "__main__":
