@@ -120,7 +120,8 @@ def read_traffic(workload: str, variant_name: str):
     return entry.get("hbm_bytes_per_launch")
 
 
-def time_gpu(p, steps, warmup, path, variant=None, min_warmup_s=0.0, per_launch=True, capture_rows=0):
+def time_gpu(p, steps, warmup, path, variant=None, min_warmup_s=0.0, per_launch=True, capture_rows=0,
+             info=None):
     """Launch on a dedicated stream; HIP events on that stream around every launch
     (with per_launch False only around the whole run, so that the host's event
     records do not leave a short kernel's queue empty).  After the `warmup`
@@ -128,7 +129,9 @@ def time_gpu(p, steps, warmup, path, variant=None, min_warmup_s=0.0, per_launch=
     (so a short kernel after host work starts timing at a settled clock).
     With capture_rows > 0, the first `capture_rows` rows of C after the first
     launch (from the problem's initial C) are copied to the host and returned
-    as a fourth value, for checking against the oracle."""
+    as a fourth value, for checking against the oracle.  With an `info` dict,
+    info["variant"] is the variant the launches ran (the library's choice for
+    these very operands, whose alignment it depends on, or the forced one)."""
     import torch
     import fp32_gemm_03_amd as g
 
@@ -137,6 +140,9 @@ def time_gpu(p, steps, warmup, path, variant=None, min_warmup_s=0.0, per_launch=
     c = p.C.cuda()
     stream = torch.cuda.Stream()
     args = (p.M, p.N, p.K, p.alpha, a, p.lda, b, p.ldb, p.beta, c, p.ldc)
+    if info is not None:
+        info["variant"] = (g.sgemm_select_variant_for(path, p.M, p.N, p.K, a, p.lda, b, p.ldb, c, p.ldc)
+                           if variant is None else variant)
 
     def step():
         if variant is None:
@@ -292,17 +298,18 @@ def main():
     else:
         w = inputs.WORKLOADS[args.workload]
         p = inputs.workload_problem(args.workload)
-    variant = g.sgemm_select_variant(path, p.M, p.N, p.K) if args.variant is None else args.variant
-    vname = g.sgemm_variant_name(variant)
-    if vname is None:
-        print(f"bench.py: no variant {variant}", file=sys.stderr)
+    if args.variant is not None and g.sgemm_variant_name(args.variant) is None:
+        print(f"bench.py: no variant {args.variant}", file=sys.stderr)
         sys.exit(2)
-    print(f"bench: {args.workload} variant {vname}, {args.warmup} warm-up + {args.steps} timed",
-          file=sys.stderr, flush=True)
+    print(f"bench: {args.workload}, {args.warmup} warm-up + {args.steps} timed", file=sys.stderr, flush=True)
     capture = 0 if args.no_cpu_baseline else max(1, min(p.M, CAPTURE_ELEMENTS // max(p.N, 1)))
     clocks_before = gpu_clocks()
-    timed = time_gpu(p, args.steps, args.warmup, path, args.variant, capture_rows=capture)
+    info = {}
+    timed = time_gpu(p, args.steps, args.warmup, path, args.variant, capture_rows=capture, info=info)
     clocks_after = gpu_clocks()
+    variant = info["variant"]
+    vname = g.sgemm_variant_name(variant)
+    print(f"bench: {args.workload} ran variant {vname}", file=sys.stderr, flush=True)
     total_ms, per_launch, wall = timed[:3]
     first_rows = timed[3] if capture else None
     ms_per_step = total_ms / args.steps
@@ -349,10 +356,11 @@ def main():
             full = name not in BAND_ONLY
             cap2 = 0 if args.no_cpu_baseline else (p2.M if full else BAND_CAPTURE_ROWS)
             print(f"bench: secondary {name}, {steps2} timed", file=sys.stderr, flush=True)
-            timed2 = time_gpu(p2, steps2, args.warmup, path, args.variant, min_warmup_s=0.05,
+            info2 = {}
+            timed2 = time_gpu(p2, steps2, args.warmup, path, args.variant, min_warmup_s=0.05, info=info2,
                               per_launch=False, capture_rows=cap2)
             t2 = timed2[0]
-            v2 = g.sgemm_select_variant(path, p2.M, p2.N, p2.K) if args.variant is None else args.variant
+            v2 = info2["variant"]
             sec_s = t2 / steps2 / 1e3
             t_fp32 = w2.flops / (PEAK_FP32_TFLOPS * 1e12)
             t_hbm = w2.algorithmic_bytes / (PEAK_HBM_GBS * 1e9)

@@ -74,6 +74,15 @@ struct Variant {
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO>,                           \
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 1, WPE, true, RO>, 1, 1}
 
+// A small K-ordered block of 32 x 32 waves split over KG wave groups; all
+// three builds are sgemm_mfma_kc (128-bit, then 4-byte loads into LDS).
+#define MFMA_CFG_KG(BM, BN, BK, KG, SUFFIX)                                                   \
+    {"mfma_" #BM "x" #BN "x" #BK "_w32x32" SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,                 \
+     KG * (BM / 32) * (BN / 32) * 64,                                                         \
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2>,                        \
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2>,                        \
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2>, nullptr, nullptr, 1, 0}
+
 // The table holds the blocks the choice by shape can pick (the VALU pair and
 // the K-ordered blocks) and the alternatives kept for measurement: the
 // XCD-grouped tile order, the LDS-staged epilogue and A unpadded with an XOR
@@ -125,6 +134,17 @@ const Variant kVariants[] = {
      sgk::sgemm_mfma<256, 256, 16, 64, 64, 4, 0, 1, 4, true, 1, 2, 0, false, true>,
      sgk::sgemm_mfma<256, 256, 16, 64, 64, 4, 0, 1, 4, false, 1, 2, 0, false, true>,
      nullptr, nullptr, 1, 0},
+    // 17, 18: small tiles for shapes that cannot give every CU a 64 x 64
+    // tile, each tile split over wave groups (KG) so that a workgroup still
+    // has four waves: 32 x 32 in four groups of one wave, 32 x 64 in two
+    // groups of two.  More, smaller workgroups per CU hide each other's
+    // prologue and epilogue (512^3: 47 against 22 TFLOP/s on 64 x 64).
+    // Their 32-bit and checked builds are the same block loading 4 bytes
+    // per lane straight into LDS, which is slow (the choice takes these
+    // blocks only for operands that allow 128-bit accesses); no split
+    // builds.
+    MFMA_CFG_KG(32, 32, 64, 4, "_kg4_kcd"),
+    MFMA_CFG_KG(32, 64, 64, 2, "_kg2_kcd"),
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -140,6 +160,8 @@ constexpr int kKcDeep8 = 12;     // 128 x 128 x 64, 8 waves, one workgroup per C
 constexpr int kKcSmall64 = 13;   // 64 x 64 x 64, one tile per CU (two wave groups)
 constexpr int kKcMid8 = 14;      // 128 x 128 x 32, 8 waves, two workgroups per CU
 constexpr int kKcHuge16 = 15;    // 256 x 256 x 32, 16 waves, one workgroup per CU, whole tiles only
+constexpr int kKcTiny4 = 17;     // 32 x 32 x 64 in four wave groups
+constexpr int kKcTiny2 = 18;     // 32 x 64 x 64 in two wave groups
 
 // The machine shape the choices depend on: compute units (tile quantisation,
 // stream-K workers, the split-K and row-split thresholds) and XCDs (the
@@ -307,7 +329,9 @@ constexpr double kSmallRate = 110.0;
 // The variant for a whole-tile (or, with streamk, stream-K) launch on a
 // machine of m.cus compute units; *score gets its predicted TFLOP/s (rate x
 // the busy share of the last round x the share of the tiles' area inside C).
-int choose(const Machine &m, int path, int M, int N, int K, bool streamk, int *workers,
+// aligned: the operands allow 128-bit accesses (launch's BUFFER_128 mode for
+// a variant that reads A along K), which the small blocks need to be fast.
+int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool aligned, int *workers,
            double *score_out = nullptr) {
     if (workers) *workers = 0;
     if (score_out) *score_out = 0.0;
@@ -360,13 +384,27 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, int *w
         }
     }
     if (best < 0) {
-        // No block fills the chip: 64 x 64 blocks.  With more tiles than
-        // CUs but not a whole number per CU, stream-K over one worker per CU
-        // evens out the K tiles each CU runs (1536^3: 107.5 TFLOP/s against
-        // 95.4); with at most one tile per CU, the deeper K tile, and
-        // select_splits may split K.
+        // No block fills the chip.  With 128-bit operands and at most three
+        // 32 x 32 tiles per CU, the 32 x 32 block in four wave groups (256^3
+        // 6.2 TFLOP/s against 4.5 on 64 x 64, 512^3 47 against 22, 768^3 69
+        // against 54, 512 x 512 x 8192 62 against 29); else, with at most
+        // one 64 x 64 tile per CU, the 32 x 64 block in two wave groups
+        // (1024^3 104 against 99, 1024 x 1024 x 4096 120 against 113,
+        // 4096 x 256 x 1024 104 against 86).  Otherwise 64 x 64 blocks:
+        // with more tiles than CUs but not a whole number per CU, stream-K
+        // over one worker per CU evens out the K tiles each CU runs (1536^3:
+        // 107.5 TFLOP/s against 95.4); with at most one tile per CU, the
+        // deeper K tile, and select_splits may split K.
         const Variant &v = kVariants[kKcSmall4];
         const long long t = tiles(M, N, v.bm, v.bn), rest = t % cus;
+        if (aligned && tiles(M, N, 32, 32) <= 3 * cus) {
+            if (score_out) *score_out = kSmallRate * fill(M, N, 32, 32);
+            return kKcTiny4;
+        }
+        if (aligned && t <= cus) {
+            if (score_out) *score_out = kSmallRate * fill(M, N, 32, 64);
+            return kKcTiny2;
+        }
         if (score_out) *score_out = kSmallRate * fill(M, N, v.bm, v.bn);
         if (t <= cus) return kKcSmall64;
         const long long kt = (K + v.bk - 1) / v.bk;
@@ -378,8 +416,8 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, int *w
     return best;
 }
 
-int select_variant(const Machine &m, int path, int M, int N, int K) {
-    return choose(m, path, M, N, K, false, nullptr);
+int select_variant(const Machine &m, int path, int M, int N, int K, bool aligned) {
+    return choose(m, path, M, N, K, false, aligned, nullptr);
 }
 
 // Without a workspace there is no stream-K, and a partial last round of
@@ -391,10 +429,10 @@ int select_variant(const Machine &m, int path, int M, int N, int K) {
 // 144.5 TFLOP/s against 136.4, 139.1 and 140.2 for one launch (the split the
 // model picks there was within 1% of the best one tried).  Only bottom parts
 // of up to 64 block rows are tried.
-int split_rows(const Machine &m, int M, int N, int K) {
+int split_rows(const Machine &m, int M, int N, int K, bool aligned) {
     if (K < 512 || M < 512) return 0;
     double single = 0.0;
-    if (choose(m, SGEMM_PATH_AUTO, M, N, K, false, nullptr, &single) < 0 || single <= 0.0) return 0;
+    if (choose(m, SGEMM_PATH_AUTO, M, N, K, false, aligned, nullptr, &single) < 0 || single <= 0.0) return 0;
     const long long nbn = (N + 255) / 256;
     const double per_row = 2.0 * N * (double)K;
     const double t_single = per_row * M / single;
@@ -410,7 +448,7 @@ int split_rows(const Machine &m, int M, int N, int K) {
         if (q < 0.96) continue;
         const int m1 = (int)(r * 256), m2 = M - m1;
         double s2 = 0.0;
-        if (choose(m, SGEMM_PATH_AUTO, m2, N, K, false, nullptr, &s2) < 0 || s2 <= 0.0) continue;
+        if (choose(m, SGEMM_PATH_AUTO, m2, N, K, false, aligned, nullptr, &s2) < 0 || s2 <= 0.0) continue;
         const double t_split = per_row * m1 / (kHuge16Rate * q * fill_n) + per_row * m2 / s2;
         if (t_split < best_t) {
             best_t = t_split;
@@ -442,17 +480,34 @@ int select_splits(const Machine &m, int variant, int M, int N, int K) {
     return s < 2 ? 1 : (int)s;
 }
 
+// With a workspace, a shape the small blocks would take runs split-K on the
+// 64 x 64 x 64 block instead when K is long enough for 4 parts or more
+// (512 x 512 x 8192 in 8 parts: 99.6 TFLOP/s against 62 on 32 x 32; with 2
+// or 3 parts the small blocks win: 512^3 47 against 26, 768^3 69 against
+// 57, 1024 x 1024 x 4096 120 against 115).
+constexpr int kTinySplitMin = 4;
+
 // What sgemm_ws (with_workspace) or sgemm (without) runs for these sizes:
 // the variant, split count, stream-K workers and the rows of a first
 // row-split launch (0: none).  Returns 0 or a negative argument code.
-int plan(const Machine &m, int M, int N, int K, bool with_workspace, int *variant, int *splits,
-         int *workers, int *rows) {
+int plan(const Machine &m, int M, int N, int K, bool with_workspace, bool aligned, int *variant,
+         int *splits, int *workers, int *rows) {
     int w = 0;
-    const int v = choose(m, SGEMM_PATH_AUTO, M, N, K, with_workspace, &w);
+    int v = choose(m, SGEMM_PATH_AUTO, M, N, K, with_workspace, aligned, &w);
     if (v < 0) return v;
     int sp = 1, r = 0;
-    if (with_workspace && w == 0) sp = select_splits(m, v, M, N, K);
-    if (w == 0 && sp == 1) r = split_rows(m, M, N, K);
+    if (with_workspace && w == 0) {
+        if (v == kKcTiny4 || v == kKcTiny2) {
+            const int s = select_splits(m, kKcSmall64, M, N, K);
+            if (s >= kTinySplitMin) {
+                v = kKcSmall64;
+                sp = s;
+            }
+        } else {
+            sp = select_splits(m, v, M, N, K);
+        }
+    }
+    if (w == 0 && sp == 1) r = split_rows(m, M, N, K, aligned);
     if (variant) *variant = v;
     if (splits) *splits = sp;
     if (workers) *workers = w;
@@ -476,6 +531,14 @@ int check_args(int M, int N, int K, float alpha, const float *A, int lda,
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// The operands allow 128-bit accesses to A (along K), B and C: launch's
+// BUFFER_128 condition for a variant that reads A 128 bits at a time (the
+// 31-bit offset limit aside, which only large leading dimensions break).
+bool operands128(int N, int K, const float *A, int lda, const float *B, int ldb, const float *C, int ldc) {
+    return N % 4 == 0 && K % 4 == 0 && lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0 && aligned16(A) &&
+           aligned16(B) && aligned16(C);
+}
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -603,7 +666,8 @@ int launch_rows(const Machine &m, int rows, int M, int N, int K, float alpha, co
     int rc = launch(m, kKcHuge16, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, rows, N, K, alpha, A, lda, B,
                     ldb, beta, C, ldc, stream);
     if (rc != SGEMM_OK) return rc;
-    const int v2 = select_variant(m, SGEMM_PATH_AUTO, M - rows, N, K);
+    const bool aligned = operands128(N, K, A, lda, B, ldb, C, ldc);
+    const int v2 = select_variant(m, SGEMM_PATH_AUTO, M - rows, N, K, aligned);
     if (v2 < 0) return v2;
     return launch(m, v2, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M - rows, N, K, alpha,
                   A + (size_t)rows * lda, lda, B, ldb, beta, C + (size_t)rows * ldc, ldc, stream);
@@ -625,10 +689,11 @@ int sgemm_path(int path, int M, int N, int K, float alpha, const float *A,
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     const Machine m = device_machine();
-    const int v = select_variant(m, path, M, N, K);
+    const bool aligned = operands128(N, K, A, lda, B, ldb, C, ldc);
+    const int v = select_variant(m, path, M, N, K, aligned);
     if (v < 0) return v;
     if (path != SGEMM_PATH_VALU) {
-        const int rows = split_rows(m, M, N, K);
+        const int rows = split_rows(m, M, N, K, aligned);
         if (rows > 0) return launch_rows(m, rows, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
     }
     return launch(m, v, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C,
@@ -682,19 +747,19 @@ size_t sgemm_streamk_workspace_size(int variant, int workers) {
 
 int sgemm_select_splits(int M, int N, int K) {
     int sp = 1;
-    const int rc = plan(device_machine(), M, N, K, true, nullptr, &sp, nullptr, nullptr);
+    const int rc = plan(device_machine(), M, N, K, true, true, nullptr, &sp, nullptr, nullptr);
     return rc < 0 ? rc : sp;
 }
 
 int sgemm_ws_plan(int M, int N, int K, int *variant, int *splits, int *workers) {
-    return plan(device_machine(), M, N, K, true, variant, splits, workers, nullptr);
+    return plan(device_machine(), M, N, K, true, true, variant, splits, workers, nullptr);
 }
 
-int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int *variant,
-                   int *splits, int *workers, int *rows) {
+int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int operands_128,
+                   int *variant, int *splits, int *workers, int *rows) {
     if (compute_units < 1 || compute_units > (1 << 20)) return SGEMM_ERR_MACHINE;
     const Machine m = {compute_units, kMI355X.xcds};
-    return plan(m, M, N, K, with_workspace != 0, variant, splits, workers, rows);
+    return plan(m, M, N, K, with_workspace != 0, operands_128 != 0, variant, splits, workers, rows);
 }
 
 int sgemm_device_shape(int *compute_units, int *xcds) {
@@ -718,20 +783,29 @@ int sgemm_select_rows(int M, int N, int K) {
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
-    return split_rows(device_machine(), M, N, K);
+    return split_rows(device_machine(), M, N, K, true);
 }
 
 int sgemm_select_streamk(int M, int N, int K) {
     int w = 0;
-    const int rc = plan(device_machine(), M, N, K, true, nullptr, nullptr, &w, nullptr);
+    const int rc = plan(device_machine(), M, N, K, true, true, nullptr, nullptr, &w, nullptr);
     return rc < 0 ? rc : w;
 }
 
-size_t sgemm_workspace_size(int M, int N, int K) {
+// Workspace bytes of the plan sgemm_ws makes with enough of it.
+size_t plan_bytes(const Machine &m, int M, int N, int K, bool aligned) {
     int v = 0, sp = 1, w = 0;
-    if (plan(device_machine(), M, N, K, true, &v, &sp, &w, nullptr) < 0) return 0;
+    if (plan(m, M, N, K, true, aligned, &v, &sp, &w, nullptr) < 0) return 0;
     if (w > 0) return streamk_bytes(kVariants[v], w);
     return sp > 1 ? splitk_bytes(kVariants[v], sp, M, N) : 0;
+}
+
+size_t sgemm_workspace_size(int M, int N, int K) {
+    // enough for operands of any alignment (the plans differ only where the
+    // small blocks need 128-bit operands)
+    const Machine m = device_machine();
+    const size_t a = plan_bytes(m, M, N, K, true), b = plan_bytes(m, M, N, K, false);
+    return a > b ? a : b;
 }
 
 int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
@@ -740,25 +814,22 @@ int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const fl
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     const Machine m = device_machine();
-    int workers = 0;
-    int v = choose(m, SGEMM_PATH_AUTO, M, N, K, true, &workers);
-    if (v < 0) return v;
+    const bool aligned = operands128(N, K, A, lda, B, ldb, C, ldc);
+    int v = 0, sp = 1, w = 0, rows = 0;
+    const int prc = plan(m, M, N, K, true, aligned, &v, &sp, &w, &rows);
+    if (prc != SGEMM_OK) return prc;
     const bool room = workspace != nullptr && ((uintptr_t)workspace & 255u) == 0;
-    if (workers > 0) {
-        if (room && workspace_bytes >= streamk_bytes(kVariants[v], workers))
-            return launch(m, v, SGEMM_ACCESS_AUTO, 1, workers, workspace, workspace_bytes, M, N, K,
-                          alpha, A, lda, B, ldb, beta, C, ldc, stream);
-        v = select_variant(m, SGEMM_PATH_AUTO, M, N, K);  // not enough workspace: whole tiles only
+    if (w > 0 || sp > 1) {
+        const size_t need = w > 0 ? streamk_bytes(kVariants[v], w) : splitk_bytes(kVariants[v], sp, M, N);
+        if (room && workspace_bytes >= need)
+            return launch(m, v, SGEMM_ACCESS_AUTO, sp, w, workspace, workspace_bytes, M, N, K, alpha, A, lda,
+                          B, ldb, beta, C, ldc, stream);
+        // not enough workspace: exactly sgemm()
+        return sgemm_path(SGEMM_PATH_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
     }
-    int sp = select_splits(m, v, M, N, K);
-    if (sp > 1 && (!room || workspace_bytes < splitk_bytes(kVariants[v], sp, M, N)))
-        sp = 1;  // not enough workspace: the unsplit kernel
-    if (sp == 1) {
-        const int rows = split_rows(m, M, N, K);
-        if (rows > 0) return launch_rows(m, rows, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
-    }
-    return launch(m, v, SGEMM_ACCESS_AUTO, sp, 0, workspace, workspace_bytes, M, N, K, alpha, A, lda, B,
-                  ldb, beta, C, ldc, stream);
+    if (rows > 0) return launch_rows(m, rows, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    return launch(m, v, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                  stream);
 }
 
 int sgemm_ws_noalloc(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
@@ -766,8 +837,9 @@ int sgemm_ws_noalloc(int M, int N, int K, float alpha, const float *A, int lda, 
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     const Machine m = device_machine();
+    const bool aligned = operands128(N, K, A, lda, B, ldb, C, ldc);
     int v = 0, sp = 1, w = 0;
-    const int prc = plan(m, M, N, K, true, &v, &sp, &w, nullptr);
+    const int prc = plan(m, M, N, K, true, aligned, &v, &sp, &w, nullptr);
     if (prc != SGEMM_OK) return prc;
     // the bytes sgemm_ws would use with enough workspace (none when there is
     // no product to split)
@@ -818,7 +890,16 @@ int sgemm_variant_reads_a128(int variant) {
 
 
 int sgemm_select_variant(int path, int M, int N, int K) {
-    return select_variant(device_machine(), path, M, N, K);
+    return select_variant(device_machine(), path, M, N, K, true);
+}
+
+int sgemm_select_variant_for(int path, int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+                             const float *C, int ldc) {
+    return select_variant(device_machine(), path, M, N, K, operands128(N, K, A, lda, B, ldb, C, ldc));
+}
+
+int sgemm_operands_128(int N, int K, const float *A, int lda, const float *B, int ldb, const float *C, int ldc) {
+    return operands128(N, K, A, lda, B, ldb, C, ldc) ? 1 : 0;
 }
 
 const char *sgemm_status_string(int status) {

@@ -63,8 +63,8 @@ def _load():
     lib.sgemm_variant_name.restype = ctypes.c_char_p
     lib.sgemm_variant_tile.argtypes = [i, ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.sgemm_variant_tile.restype = i
-    lib.sgemm_select_variant.argtypes = [i, i, i, i]
-    lib.sgemm_select_variant.restype = i
+    lib.sgemm_select_variant_for.argtypes = [i, i, i, i, vp, i, vp, i, vp, i]
+    lib.sgemm_select_variant_for.restype = i
     lib.sgemm_phase_read.argtypes = [vp, i]
     lib.sgemm_phase_read.restype = i
     return lib
@@ -83,7 +83,9 @@ def run_case(lib, name, variant):
     import torch
 
     p = _problem(name)
-    v = lib.sgemm_select_variant(0, p.M, p.N, p.K) if variant == "auto" else int(variant)
+    a, b, c = p.A.cuda(), p.B.cuda(), p.C.cuda()
+    v = (lib.sgemm_select_variant_for(0, p.M, p.N, p.K, a.data_ptr(), p.lda, b.data_ptr(), p.ldb,
+                                      c.data_ptr(), p.ldc) if variant == "auto" else int(variant))
     raw = lib.sgemm_variant_name(v)
     if raw is None:
         raise ValueError(f"no variant {variant}")
@@ -91,7 +93,6 @@ def run_case(lib, name, variant):
     bm, bn = ctypes.c_int(), ctypes.c_int()
     lib.sgemm_variant_tile(v, ctypes.byref(bm), ctypes.byref(bn))
     wgs = math.ceil(p.M / bm.value) * math.ceil(p.N / bn.value)
-    a, b, c = p.A.cuda(), p.B.cuda(), p.C.cuda()
 
     def launch():
         rc = lib.sgemm_variant(v, p.M, p.N, p.K, p.alpha, a.data_ptr(), p.lda, b.data_ptr(), p.ldb,

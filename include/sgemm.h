@@ -171,8 +171,17 @@ int sgemm_ws_noalloc(int M, int N, int K, float alpha, const float *A, int lda,
                      const float *B, int ldb, float beta, float *C, int ldc,
                      hipStream_t stream);
 
-/* Workspace bytes sgemm_ws() can use for these sizes (0: it never splits). */
+/* Workspace bytes sgemm_ws() can use for these sizes, for operands of any
+ * alignment (0: it never splits). */
 size_t sgemm_workspace_size(int M, int N, int K);
+
+/* The plan queries below (sgemm_select_splits, sgemm_select_streamk,
+ * sgemm_ws_plan, sgemm_select_variant, sgemm_select_rows) answer for
+ * operands that allow 128-bit accesses: A, B and C 16-byte aligned, and N,
+ * K, lda, ldb and ldc multiples of 4.  For other operands the library takes
+ * no block that needs them (the 32 x 32 and 32 x 64 blocks), so small shapes
+ * may get another plan: sgemm_select_variant_for() and sgemm_plan_for()
+ * answer for any operands. */
 
 /* The split count sgemm_ws() uses with enough workspace (1: no split), or a
  * negative argument code.  Host logic only. */
@@ -249,11 +258,25 @@ int sgemm_variant_tile(int variant, int *bm, int *bn);
  * range.  Host logic only. */
 int sgemm_variant_reads_a128(int variant);
 
-/* The variant sgemm_path(path, M, N, K, ...) launches for these sizes, or a
- * negative code (-1..-3, SGEMM_ERR_PATH).  Host logic only, no HIP call.
- * When sgemm_select_rows() is positive, an AUTO or MFMA call runs another
- * plan (below). */
+/* The variant sgemm_path(path, M, N, K, ...) launches for these sizes with
+ * operands that allow 128-bit accesses (above), or a negative code (-1..-3,
+ * SGEMM_ERR_PATH).  Host logic only, no HIP call.  When sgemm_select_rows()
+ * is positive, an AUTO or MFMA call runs another plan (below). */
 int sgemm_select_variant(int path, int M, int N, int K);
+
+/* The same for these operands: the pointers and leading dimensions decide
+ * whether 128-bit accesses are possible (the pointers are only inspected for
+ * alignment, never dereferenced; they may be NULL where sgemm() allows it).
+ * Host logic only. */
+int sgemm_select_variant_for(int path, int M, int N, int K, const float *A, int lda,
+                             const float *B, int ldb, const float *C, int ldc);
+
+/* 1 if these operands allow 128-bit accesses (A, B and C 16-byte aligned;
+ * N, K, lda, ldb and ldc multiples of 4), else 0: the operands_128 argument
+ * of sgemm_plan_for() that describes them.  The pointers are only inspected.
+ * Host logic only. */
+int sgemm_operands_128(int N, int K, const float *A, int lda, const float *B, int ldb,
+                       const float *C, int ldc);
 
 /* Rows of C that sgemm() (path AUTO or MFMA), and sgemm_ws() when it
  * neither splits K nor runs stream-K, compute as a first launch of 256 x 256
@@ -277,13 +300,15 @@ int sgemm_device_shape(int *compute_units, int *xcds);
 
 /* The plan the library makes for these sizes on a device of
  * `compute_units` compute units: with with_workspace != 0 what sgemm_ws()
- * runs with enough workspace, else what sgemm() runs.  Through the pointers
- * (each may be NULL): the variant, the split count (1: none), the stream-K
- * worker count (0: none) and the rows of a first row-split launch (0: one
- * launch).  Returns 0, a negative argument code (-1..-3 for M, N, K), or
- * SGEMM_ERR_MACHINE for compute_units outside 1..2^20.  Host logic only. */
-int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int *variant,
-                   int *splits, int *workers, int *rows);
+ * runs with enough workspace, else what sgemm() runs; operands_128 != 0 for
+ * operands that allow 128-bit accesses (above), 0 for any others.  Through
+ * the pointers (each may be NULL): the variant, the split count (1: none),
+ * the stream-K worker count (0: none) and the rows of a first row-split
+ * launch (0: one launch).  Returns 0, a negative argument code (-1..-3 for
+ * M, N, K), or SGEMM_ERR_MACHINE for compute_units outside 1..2^20.  Host
+ * logic only. */
+int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int operands_128,
+                   int *variant, int *splits, int *workers, int *rows);
 
 /* The workgroup -> tile order of the K-ordered blocks on a device of `xcds`
  * XCDs, for a grid of nbm x nbn tiles: workgroup p computes tile

@@ -185,11 +185,27 @@ def test_large_shapes_pick_the_block_whose_last_round_is_fullest():
     assert "_w8_" in g.sgemm_variant_name(g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 2048, 2048, 2048))
     assert block(3072, 3072, 3072) == (64, 64, 32)      # 128 x 128 would leave 1/4 of a round
     assert block(5120, 5120, 5120) == (64, 64, 32)      # whole rounds of 64 x 64, 6.25 of 128 x 128
-    # too few tiles for any slot count, at most one 64 x 64 tile per CU: the deeper K tile
-    assert block(1024, 1024, 1024) == (64, 64, 64)
-    assert block(1000, 1023, 999) == (64, 64, 64)
-    assert block(512, 512, 8192) == (64, 64, 64)
-    assert block(1088, 1024, 1024) == (64, 64, 32)      # 272 tiles: more than one per CU
+    # too few tiles for any slot count (operands that allow 128-bit
+    # accesses): up to three 32 x 32 tiles per CU, the 32 x 32 block in four
+    # wave groups; up to one 64 x 64 tile per CU, the 32 x 64 block in two
+    assert block(256, 256, 256) == (32, 32, 64)
+    assert block(512, 512, 8192) == (32, 32, 64)
+    assert block(768, 768, 768) == (32, 32, 64)         # 576 tiles of 32 x 32
+    assert block(1024, 1024, 1024) == (32, 64, 64)      # 1024 of 32 x 32, 256 of 64 x 64
+    assert block(1000, 1023, 999) == (32, 64, 64)
+    assert block(1088, 1024, 1024) == (64, 64, 32)      # 272 tiles of 64 x 64: more than one per CU
+    # operands without 128-bit access keep the 64 x 64 blocks, whose 32-bit
+    # builds stage through registers
+    def block_for(M, N, K, lda, ldb, ldc, off=0):
+        v = g.sgemm_select_variant_for(g.SGEMM_PATH_AUTO, M, N, K, 0x10000 + off, lda, 0x20000, ldb,
+                                       0x30000, ldc)
+        return _block(v)
+    assert block_for(1000, 1023, 999, 999, 1023, 1023) == (64, 64, 64)
+    assert block_for(1024, 1024, 1024, 1024, 1024, 1024) == (32, 64, 64)
+    assert block_for(1024, 1024, 1024, 1024, 1024, 1024, off=4) == (64, 64, 64)   # A not 16-byte aligned
+    assert block_for(512, 512, 512, 513, 512, 512) == (64, 64, 64)                # lda not a multiple of 4
+    assert block_for(512, 512, 512, 512, 512, 512) == (32, 32, 64)
+    assert block_for(8192, 8192, 8192, 8192, 8192, 8192) == block(8192, 8192, 8192)
 
 
 def test_streamk_host_logic():
@@ -311,14 +327,21 @@ def test_splitk_host_logic():
     # large shapes fill the chip with tiles: no split, no workspace
     assert g.sgemm_select_splits(8192, 8192, 8192) == 1
     assert g.sgemm_workspace_size(8192, 8192, 8192) == 0
-    # few tiles and a deep K split; shallow K does not
+    # few tiles and a deep K split: 4 parts or more of the 64 x 64 block beat
+    # the small blocks; 2 or 3 do not (with 128-bit operands), but do on the
+    # 64 x 64 block that other operands run; shallow K does not split
     assert g.sgemm_select_splits(512, 512, 8192) == 8
     assert g.sgemm_workspace_size(512, 512, 8192) > 0
-    assert g.sgemm_select_splits(1024, 1024, 4096) == 2
+    assert g.sgemm_select_splits(1024, 1024, 4096) == 1
+    assert g.sgemm_plan_for(256, 1024, 1024, 4096, True, operands_128=False)[2] == 2
+    assert g.sgemm_workspace_size(1024, 1024, 4096) > 0    # enough for either plan
     assert g.sgemm_select_splits(1024, 1024, 1024) == 1
     assert g.sgemm_select_splits(256, 256, 256) == 1
     # fewer tiles than CUs: parts may be as short as 256 of K
-    assert g.sgemm_select_splits(768, 768, 768) == 3
+    assert g.sgemm_select_splits(768, 768, 768) == 1
+    assert g.sgemm_plan_for(256, 768, 768, 768, True, operands_128=False)[2] == 3
+    assert g.sgemm_select_splits(256, 256, 4096) == 16
+    assert _block(g.sgemm_ws_plan(256, 256, 4096)[1]) == (64, 64, 64)
     assert g.sgemm_select_splits(-1, 4, 4) == -1
 
 
@@ -400,7 +423,9 @@ def test_plan_quantises_over_other_cu_counts(cus):
     split-K aims at about two workgroups per CU."""
     per_cu = {"_w16_kcd": 1, "x32_w128x64_kcd": 1, "_wpe4_kcd": 4, "x16_w64x128_kcd": 2,
               "x32_w64x64_w8_kcd": 1, "64x64x32_w32x32_kcd": 4, "x64_w32x64_w8_kcd": 1,
-              "64x64x64_w32x32_kcd": 2, "x32_w64x32_w8_kcd": 2}
+              "_kg2_kcd": 2, "_kg4_kcd": 4, "x32_w64x32_w8_kcd": 2}
+    fallbacks = ("mfma_64x64x64_w64x32_kg2_kcd", "mfma_64x64x32_w32x32_kcd",
+                 "mfma_32x32x64_w32x32_kg4_kcd", "mfma_32x64x64_w32x32_kg2_kcd")
     for M, N, K in [(8192, 8192, 8192), (4096, 4096, 4096), (2048, 2048, 2048), (1024, 1024, 1024),
                     (6144, 6144, 6144), (16384, 16384, 128), (3000, 5000, 2000)]:
         rc, v, sp, w, rows = g.sgemm_plan_for(cus, M, N, K)
@@ -410,8 +435,8 @@ def test_plan_quantises_over_other_cu_counts(cus):
         t = -(-M // bm) * -(-N // bn)
         slots = [n for k, n in per_cu.items() if name.endswith(k)]
         assert slots, name
-        if name != "mfma_64x64x64_w32x32_kcd":
-            assert t >= slots[0] * cus or name == "mfma_64x64x32_w32x32_kcd", (cus, M, N, K, name)
+        if name not in fallbacks:
+            assert t >= slots[0] * cus, (cus, M, N, K, name)
         if t >= 4 * cus and rows == 0:
             assert _last_round_busy(t, cus) >= 0.8, (cus, M, N, K, name, t)
         rc, v2, sp2, w2, _ = g.sgemm_plan_for(cus, M, N, K, with_workspace=True)
@@ -421,13 +446,17 @@ def test_plan_quantises_over_other_cu_counts(cus):
             t2 = -(-M // bm2) * -(-N // bn2)
             assert t2 <= cus and t2 * sp2 <= 2 * cus
     # a 32-CU partition fills its CUs with 128 x 256 blocks at 1024^3, where
-    # 256 CUs need the 64 x 64 latency block
+    # 256 CUs need a small block (32 x 64, or 64 x 64 for other operands)
     assert _block(g.sgemm_plan_for(32, 1024, 1024, 1024)[1])[:2] == (128, 256)
-    assert _block(g.sgemm_plan_for(256, 1024, 1024, 1024)[1])[:2] == (64, 64)
-    # split-K: 64 tiles of 64 x 64 at 512 x 512 x 8192 split in 8 on 256 CUs,
-    # in 2 on 80
+    assert _block(g.sgemm_plan_for(256, 1024, 1024, 1024)[1])[:2] == (32, 64)
+    assert _block(g.sgemm_plan_for(256, 1024, 1024, 1024, operands_128=False)[1])[:2] == (64, 64)
+    # split-K: 64 tiles of 64 x 64 at 512 x 512 x 8192 split in 8 on 256 CUs;
+    # on 80 CUs a split would be in 2, so 128-bit operands take the 32 x 64
+    # block whole instead, and other operands the split
     assert g.sgemm_plan_for(256, 512, 512, 8192, True)[2] == 8
-    assert g.sgemm_plan_for(80, 512, 512, 8192, True)[2] == 2
+    assert g.sgemm_plan_for(80, 512, 512, 8192, True)[2] == 1
+    assert _block(g.sgemm_plan_for(80, 512, 512, 8192, True)[1])[:2] == (32, 64)
+    assert g.sgemm_plan_for(80, 512, 512, 8192, True, operands_128=False)[2] == 2
 
 
 def test_tile_order_is_a_bijection_for_every_xcd_count():
@@ -470,6 +499,17 @@ def test_narrow_n_weighs_the_tiles_area_inside_c():
     # wide N keeps the 256 x 256 block and the row split where they fill C
     assert _block(g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 8192, 8192, 8192))[:2] == (256, 256)
     assert g.sgemm_select_rows(7168, 7168, 7168) == 6912
+
+
+def test_operands_128_condition():
+    """128-bit operands: A, B and C 16-byte aligned and N, K, lda, ldb, ldc
+    multiples of 4 (the pointers are only inspected)."""
+    ok = (1024, 1024, 0x1000, 1024, 0x2000, 1024, 0x3000, 1024)
+    assert g.sgemm_operands_128(*ok)
+    for i, bad in [(0, 1022), (1, 1021), (2, 0x1004), (3, 1025), (4, 0x2008), (5, 1026), (6, 0x300c), (7, 1027)]:
+        args = list(ok)
+        args[i] = bad
+        assert not g.sgemm_operands_128(*args), (i, bad)
 
 
 def test_no_kernel_uses_scratch():
