@@ -319,6 +319,9 @@ double fill(int M, int N, int bm, int bn) {
 // level at 10240^3 and 0.4% below 128 x 128 x 16 at 6144^3.
 constexpr double kStreamKShare = 0.985;
 constexpr int kStreamKMinK = 8;
+// K from which stream-K on 64 x 64 x 32 beats the 64 x 64 x 64 block at one
+// or two tiles per CU (1280^2 x 4096 yes, 1280^3 and 1408^3 no)
+constexpr int kStreamKLongK = 2048;
 
 // Candidate rates, TFLOP/s, of the two 256 x 256 x 32 blocks and of 64 x 64
 // blocks that cannot fill the chip (256 rows of 7168^2 x 7168 ran 114 on
@@ -384,31 +387,41 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool a
         }
     }
     if (best < 0) {
-        // No block fills the chip.  With 128-bit operands and at most three
-        // 32 x 32 tiles per CU, the 32 x 32 block in four wave groups (256^3
-        // 6.2 TFLOP/s against 4.5 on 64 x 64, 512^3 47 against 22, 768^3 69
-        // against 54, 512 x 512 x 8192 62 against 29); else, with at most
-        // one 64 x 64 tile per CU, the 32 x 64 block in two wave groups
-        // (1024^3 104 against 99, 1024 x 1024 x 4096 120 against 113,
-        // 4096 x 256 x 1024 104 against 86).  Otherwise 64 x 64 blocks:
-        // with more tiles than CUs but not a whole number per CU, stream-K
-        // over one worker per CU evens out the K tiles each CU runs (1536^3:
-        // 107.5 TFLOP/s against 95.4); with at most one tile per CU, the
-        // deeper K tile, and select_splits may split K.
+        // No block fills the chip (measured over cubes 256-1920 and
+        // rectangles; TFLOP/s).  With 128-bit operands:
+        //   * at most three 32 x 32 tiles per CU: the 32 x 32 block in four
+        //     wave groups (256^3 6.6 against 4.5 on 64 x 64, 512^3 47 against
+        //     22, 768^3 69 against 54, 512 x 512 x 8192 62 against 29);
+        //   * at most three 32 x 64 tiles per CU (three of its workgroups fit
+        //     a CU's LDS, so that is one round): the 32 x 64 block in two
+        //     wave groups (1024^3 104 against 99, 1024 x 1024 x 4096 120
+        //     against 113, 1152^3 100 against 73, 1536 x 1024 x 2048 122
+        //     against 92, 3072 x 512 x 1024 113 against 86);
+        //   * at most two 64 x 64 tiles per CU (one round of two per CU): the
+        //     64 x 64 x 64 block (1408^3 116 against 110, 2048 x 1024 x 2048
+        //     127 against 120), unless stream-K on 64 x 64 x 32 shares long K
+        //     ranges (1280^2 x 4096: 110 against 102).
+        // Otherwise, and for other operands beyond one 64 x 64 tile per CU,
+        // the 64 x 64 x 32 block at four per CU; with more tiles than CUs but
+        // not a whole number per CU, stream-K over one worker per CU evens
+        // out the K tiles each CU runs (1536^3: 110 against 96).  With at
+        // most one 64 x 64 tile per CU, the deeper K tile, and select_splits
+        // may split K.
         const Variant &v = kVariants[kKcSmall4];
         const long long t = tiles(M, N, v.bm, v.bn), rest = t % cus;
+        const long long kt = (K + v.bk - 1) / v.bk;
+        const bool sk = streamk && rest > 0 && rest * kt >= kStreamKMinK * cus;
         if (aligned && tiles(M, N, 32, 32) <= 3 * cus) {
             if (score_out) *score_out = kSmallRate * fill(M, N, 32, 32);
             return kKcTiny4;
         }
-        if (aligned && t <= cus) {
+        if (aligned && tiles(M, N, 32, 64) <= 3 * cus) {
             if (score_out) *score_out = kSmallRate * fill(M, N, 32, 64);
             return kKcTiny2;
         }
         if (score_out) *score_out = kSmallRate * fill(M, N, v.bm, v.bn);
-        if (t <= cus) return kKcSmall64;
-        const long long kt = (K + v.bk - 1) / v.bk;
-        if (streamk && workers && rest > 0 && rest * kt >= kStreamKMinK * cus) *workers = (int)cus;
+        if (t <= cus || (aligned && t <= 2 * cus && !(sk && K >= kStreamKLongK))) return kKcSmall64;
+        if (sk && workers) *workers = (int)cus;
         return kKcSmall4;
     }
     if (workers) *workers = best_workers;

@@ -193,7 +193,18 @@ def test_large_shapes_pick_the_block_whose_last_round_is_fullest():
     assert block(768, 768, 768) == (32, 32, 64)         # 576 tiles of 32 x 32
     assert block(1024, 1024, 1024) == (32, 64, 64)      # 1024 of 32 x 32, 256 of 64 x 64
     assert block(1000, 1023, 999) == (32, 64, 64)
-    assert block(1088, 1024, 1024) == (64, 64, 32)      # 272 tiles of 64 x 64: more than one per CU
+    assert block(1088, 1024, 1024) == (32, 64, 64)      # 544 of 32 x 64: within one round of 3 per CU
+    assert block(1152, 1152, 1152) == (32, 64, 64)
+    # up to two 64 x 64 tiles per CU, the 64 x 64 x 64 block; beyond, 64 x 64 x 32
+    assert block(1408, 1408, 1408) == (64, 64, 64)
+    assert block(2048, 1024, 1024) == (64, 64, 64)
+    assert block(1664, 1664, 1664) == (64, 64, 32)
+    assert block(1920, 1920, 1920) == (64, 64, 32)
+    # with a workspace and long K, stream-K on 64 x 64 x 32 instead
+    rc, v, sp, w = g.sgemm_ws_plan(1280, 1280, 4096)
+    assert _block(v) == (64, 64, 32) and w == 256
+    rc, v, sp, w = g.sgemm_ws_plan(1408, 1408, 1408)
+    assert _block(v) == (64, 64, 64) and (sp, w) == (1, 0)
     # operands without 128-bit access keep the 64 x 64 blocks, whose 32-bit
     # builds stage through registers
     def block_for(M, N, K, lda, ldb, ldc, off=0):
