@@ -34,6 +34,8 @@ struct Variant {
     KernelFn split1;    // split-K, as vec1
     int a128;           // 1: the vec4 build also reads A 128 bits at a time along K
     int streamk;        // 1: the split builds also run stream-K (phases 2 and 3)
+    int generic_buf;    // 1: `generic` is a buffer-access build too (no plain-pointer
+                        // build exists), so it needs in-tile offsets below 2^31
 };
 
 // VALU: BM x BN x BK block, waves of (8 TM) x (8 TN), TM x TN per lane.
@@ -75,13 +77,14 @@ struct Variant {
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 1, WPE, true, RO>, 1, 1}
 
 // A small K-ordered block of 32 x 32 waves split over KG wave groups; all
-// three builds are sgemm_mfma_kc (128-bit, then 4-byte loads into LDS).
+// three builds are sgemm_mfma_kc (128-bit, then 4-byte loads into LDS), so
+// even its checked build needs in-tile offsets below 2^31.
 #define MFMA_CFG_KG(BM, BN, BK, KG, SUFFIX)                                                   \
     {"mfma_" #BM "x" #BN "x" #BK "_w32x32" SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,                 \
      KG * (BM / 32) * (BN / 32) * 64,                                                         \
      sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2>,                        \
      sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2>,                        \
-     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2>, nullptr, nullptr, 1, 0}
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2>, nullptr, nullptr, 1, 0, 1}
 
 // The table holds the blocks the choice by shape can pick (the VALU pair and
 // the K-ordered blocks) and the alternatives kept for measurement: the
@@ -545,12 +548,15 @@ int check_args(int M, int N, int K, float alpha, const float *A, int lda,
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// The operands allow 128-bit accesses to A (along K), B and C: launch's
-// BUFFER_128 condition for a variant that reads A 128 bits at a time (the
-// 31-bit offset limit aside, which only large leading dimensions break).
+// The operands allow the small blocks' 128-bit builds: launch's BUFFER_128
+// condition for a variant that reads A 128 bits at a time (16-byte aligned
+// A, B and C; N, K and the leading dimensions multiples of 4), with the
+// in-tile byte offsets of a 32 x 64 x 64 block below 2^31.
 bool operands128(int N, int K, const float *A, int lda, const float *B, int ldb, const float *C, int ldc) {
+    const long long lim = 1LL << 31;
     return N % 4 == 0 && K % 4 == 0 && lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0 && aligned16(A) &&
-           aligned16(B) && aligned16(C);
+           aligned16(B) && aligned16(C) && 33LL * lda * 4 < lim && 65LL * ldb * 4 + 64 * 4 < lim &&
+           33LL * ldc * 4 < lim;
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -641,6 +647,7 @@ int launch(const Machine &m, int variant, int access, int splits, int workers, v
             fn = !buf_ok ? v.generic : (vec4 ? v.vec4 : v.vec1);
             break;
     }
+    if (fn == v.generic && v.generic_buf && !buf_ok) return SGEMM_ERR_ACCESS;
     if (splits > 1 || workers > 0) {
         // split-K and stream-K kernels exist for buffer accesses only
         if (fn == v.generic) return SGEMM_ERR_ACCESS;

@@ -121,7 +121,10 @@ int sgemm_variant(int variant, int M, int N, int K, float alpha,
  *   BUFFER_32   the same with 32-bit accesses: any alignment.
  *   CHECKED     plain pointers with every element checked: any arguments.
  * SGEMM_ACCESS_AUTO takes the first of these the arguments allow.  A forced
- * mode the arguments do not allow returns SGEMM_ERR_ACCESS.  For tests and
+ * mode the arguments do not allow returns SGEMM_ERR_ACCESS.  The small
+ * wave-group blocks (32 x 32 and 32 x 64 tiles) have no plain-pointer build:
+ * their CHECKED build uses buffer accesses too, so with in-tile offsets of
+ * 2^31 bytes or more every mode returns SGEMM_ERR_ACCESS for them.  For tests and
  * benchmarks that must cover every compiled kernel. */
 int sgemm_variant_access(int variant, int access, int M, int N, int K,
                          float alpha, const float *A, int lda, const float *B,
@@ -177,8 +180,9 @@ size_t sgemm_workspace_size(int M, int N, int K);
 
 /* The plan queries below (sgemm_select_splits, sgemm_select_streamk,
  * sgemm_ws_plan, sgemm_select_variant, sgemm_select_rows) answer for
- * operands that allow 128-bit accesses: A, B and C 16-byte aligned, and N,
- * K, lda, ldb and ldc multiples of 4.  For other operands the library takes
+ * operands that allow 128-bit accesses: A, B and C 16-byte aligned, N, K,
+ * lda, ldb and ldc multiples of 4 and leading dimensions below about 2^24
+ * (sgemm_operands_128).  For other operands the library takes
  * no block that needs them (the 32 x 32 and 32 x 64 blocks), so small shapes
  * may get another plan: sgemm_select_variant_for() and sgemm_plan_for()
  * answer for any operands. */
@@ -271,10 +275,11 @@ int sgemm_select_variant(int path, int M, int N, int K);
 int sgemm_select_variant_for(int path, int M, int N, int K, const float *A, int lda,
                              const float *B, int ldb, const float *C, int ldc);
 
-/* 1 if these operands allow 128-bit accesses (A, B and C 16-byte aligned;
- * N, K, lda, ldb and ldc multiples of 4), else 0: the operands_128 argument
- * of sgemm_plan_for() that describes them.  The pointers are only inspected.
- * Host logic only. */
+/* 1 if these operands allow the 128-bit builds of the small blocks (A, B and
+ * C 16-byte aligned; N, K, lda, ldb and ldc multiples of 4; leading
+ * dimensions below about 2^24, so that in-tile byte offsets fit 31 bits),
+ * else 0: the operands_128 argument of sgemm_plan_for() that describes them.
+ * The pointers are only inspected.  Host logic only. */
 int sgemm_operands_128(int N, int K, const float *A, int lda, const float *B, int ldb,
                        const float *C, int ldc);
 

@@ -523,6 +523,23 @@ def test_operands_128_condition():
         assert not g.sgemm_operands_128(*args), (i, bad)
 
 
+def test_small_blocks_need_31_bit_offsets():
+    """The 32 x 32 and 32 x 64 wave-group blocks have only buffer-access
+    builds: leading dimensions too large for 31-bit in-tile offsets keep the
+    choice off them, and forcing them is refused before any HIP call."""
+    big = 1 << 26   # floats: 33 rows of A span more than 2^31 bytes
+    assert not g.sgemm_operands_128(512, 512, 0x1000, big, 0x2000, 512, 0x3000, 512)
+    v = g.sgemm_select_variant_for(g.SGEMM_PATH_AUTO, 512, 512, 512, 0x1000, big, 0x2000, 512, 0x3000, 512)
+    assert _block(v) == (64, 64, 64)
+    tiny = [i for i in range(g.sgemm_variant_count()) if (g.sgemm_variant_name(i) or "").startswith("mfma_32x")]
+    assert len(tiny) == 2
+    for t in tiny:
+        for access in (g.SGEMM_ACCESS_AUTO, g.SGEMM_ACCESS_CHECKED):
+            rc = g.sgemm_variant_access(t, access, 512, 512, 512, 1.0, 0x1000, big, 0x2000, 512, 0.0,
+                                        0x3000, 512, stream=0, check=False)
+            assert rc == -23, (t, access, rc)
+
+
 def test_no_kernel_uses_scratch():
     """Every kernel in the library keeps its state in registers and LDS: no
     register spills to scratch memory (read from the AMDGPU metadata of the
