@@ -404,8 +404,9 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool a
         //     64 x 64 x 64 block (1408^3 116 against 110, 2048 x 1024 x 2048
         //     127 against 120), unless stream-K on 64 x 64 x 32 shares long K
         //     ranges (1280^2 x 4096: 110 against 102).
-        // Otherwise, and for other operands beyond one 64 x 64 tile per CU,
-        // the 64 x 64 x 32 block at four per CU; with more tiles than CUs but
+        // Other operands take the 64 x 64 x 64 block up to two tiles per CU
+        // as well (1151^3 69 against 67, 2047 x 1023 x 1023 106 against 100).
+        // Otherwise the 64 x 64 x 32 block at four per CU; with more tiles than CUs but
         // not a whole number per CU, stream-K over one worker per CU evens
         // out the K tiles each CU runs (1536^3: 110 against 96).  With at
         // most one 64 x 64 tile per CU, the deeper K tile, and select_splits
@@ -423,7 +424,7 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool a
             return kKcTiny2;
         }
         if (score_out) *score_out = kSmallRate * fill(M, N, v.bm, v.bn);
-        if (t <= cus || (aligned && t <= 2 * cus && !(sk && K >= kStreamKLongK))) return kKcSmall64;
+        if (t <= cus || (t <= 2 * cus && !(sk && K >= kStreamKLongK))) return kKcSmall64;
         if (sk && workers) *workers = (int)cus;
         return kKcSmall4;
     }
@@ -506,13 +507,18 @@ constexpr int kTinySplitMin = 4;
 // What sgemm_ws (with_workspace) or sgemm (without) runs for these sizes:
 // the variant, split count, stream-K workers and the rows of a first
 // row-split launch (0: none).  Returns 0 or a negative argument code.
+// Split-K and stream-K only for 128-bit operands: their 32-bit builds load
+// 4 bytes per lane straight into LDS, and measured slower than one launch of
+// whole tiles (767^3 in 3 parts 27.6 against 47.5 TFLOP/s, 1535^3 stream-K
+// 60.0 against 88.6, 1023 x 1023 x 4095 in 2 parts 62.7 against 100.2).
 int plan(const Machine &m, int M, int N, int K, bool with_workspace, bool aligned, int *variant,
          int *splits, int *workers, int *rows) {
     int w = 0;
-    int v = choose(m, SGEMM_PATH_AUTO, M, N, K, with_workspace, aligned, &w);
+    const bool parts = with_workspace && aligned;
+    int v = choose(m, SGEMM_PATH_AUTO, M, N, K, parts, aligned, &w);
     if (v < 0) return v;
     int sp = 1, r = 0;
-    if (with_workspace && w == 0) {
+    if (parts && w == 0) {
         if (v == kKcTiny4 || v == kKcTiny2) {
             const int s = select_splits(m, kKcSmall64, M, N, K);
             if (s >= kTinySplitMin) {
@@ -572,6 +578,13 @@ size_t streamk_bytes(const Variant &v, int workers) {
     return round_up((size_t)workers * 2 * v.bm * v.bn * 4, 256);
 }
 
+// Buffer accesses form byte offsets inside one block tile in 31 bits.
+bool buffer_offsets_ok(const Variant &v, int lda, int ldb, int ldc) {
+    const long long lim = 1LL << 31;
+    return (long long)(v.bm + 1) * lda * 4 < lim && (long long)(v.bk + 1) * ldb * 4 + (long long)v.bn * 4 < lim &&
+           (long long)(v.bm + 1) * ldc * 4 < lim;
+}
+
 int launch(const Machine &m, int variant, int access, int splits, int workers, void *workspace,
            size_t workspace_bytes, int M, int N, int K, float alpha, const float *A, int lda,
            const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
@@ -617,11 +630,7 @@ int launch(const Machine &m, int variant, int access, int splits, int workers, v
     a.sk_whole = 0;
     a.sk_workers = 0;
     a.xcd_shift = log2_of(m.xcds);
-    // Buffer accesses form byte offsets inside one block tile in 31 bits.
-    const long long lim = 1LL << 31;
-    const bool buf_ok = (long long)(v.bm + 1) * lda * 4 < lim &&
-                        (long long)(v.bk + 1) * ldb * 4 + (long long)v.bn * 4 < lim &&
-                        (long long)(v.bm + 1) * ldc * 4 < lim;
+    const bool buf_ok = buffer_offsets_ok(v, lda, ldb, ldc);
     // 128-bit accesses to B and C need 16-byte aligned bases and every row
     // start a multiple of 4 floats; N % 4 == 0 keeps each 4-wide piece wholly
     // inside or wholly outside the matrix.  A is read 32 bits at a time, or,
@@ -821,11 +830,8 @@ size_t plan_bytes(const Machine &m, int M, int N, int K, bool aligned) {
 }
 
 size_t sgemm_workspace_size(int M, int N, int K) {
-    // enough for operands of any alignment (the plans differ only where the
-    // small blocks need 128-bit operands)
-    const Machine m = device_machine();
-    const size_t a = plan_bytes(m, M, N, K, true), b = plan_bytes(m, M, N, K, false);
-    return a > b ? a : b;
+    // only 128-bit operands split K or run stream-K
+    return plan_bytes(device_machine(), M, N, K, true);
 }
 
 int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
@@ -841,7 +847,7 @@ int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const fl
     const bool room = workspace != nullptr && ((uintptr_t)workspace & 255u) == 0;
     if (w > 0 || sp > 1) {
         const size_t need = w > 0 ? streamk_bytes(kVariants[v], w) : splitk_bytes(kVariants[v], sp, M, N);
-        if (room && workspace_bytes >= need)
+        if (room && workspace_bytes >= need && buffer_offsets_ok(kVariants[v], lda, ldb, ldc))
             return launch(m, v, SGEMM_ACCESS_AUTO, sp, w, workspace, workspace_bytes, M, N, K, alpha, A, lda,
                           B, ldb, beta, C, ldc, stream);
         // not enough workspace: exactly sgemm()

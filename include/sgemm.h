@@ -146,8 +146,9 @@ int sgemm_variant_access(int variant, int access, int M, int N, int K,
  * library allocates nothing. */
 
 /* C = alpha*A*B + beta*C like sgemm(), using split-K or stream-K (below)
- * when the auto choice calls for it and `workspace_bytes` holds
- * sgemm_workspace_size(M, N, K); otherwise exactly sgemm(). */
+ * when the auto choice calls for it, the operands allow 128-bit accesses
+ * (sgemm_operands_128) and `workspace_bytes` holds sgemm_workspace_size(M,
+ * N, K); otherwise exactly sgemm(). */
 int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda,
              const float *B, int ldb, float beta, float *C, int ldc,
              void *workspace, size_t workspace_bytes, hipStream_t stream);
@@ -174,8 +175,9 @@ int sgemm_ws_noalloc(int M, int N, int K, float alpha, const float *A, int lda,
                      const float *B, int ldb, float beta, float *C, int ldc,
                      hipStream_t stream);
 
-/* Workspace bytes sgemm_ws() can use for these sizes, for operands of any
- * alignment (0: it never splits). */
+/* Workspace bytes sgemm_ws() can use for these sizes (0: it never splits).
+ * Only operands that allow 128-bit accesses (sgemm_operands_128) split K or
+ * run stream-K: for others sgemm_ws() is exactly sgemm(). */
 size_t sgemm_workspace_size(int M, int N, int K);
 
 /* The plan queries below (sgemm_select_splits, sgemm_select_streamk,

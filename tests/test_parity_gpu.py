@@ -372,6 +372,10 @@ def random_configs(n, seed):
         beta = float(rng.choice([0.0, 1.0, -0.75, 0.5]))
         pads = [int(x) for x in rng.integers(0, 6, 3)]
         offs = tuple(int(x) for x in rng.integers(0, 4, 3))
+        if i % 4 == 3:  # operands that allow 128-bit accesses, which split-K needs
+            N, K = -(-N // 4) * 4, -(-K // 4) * 4
+            pads = [4 * (x % 2) for x in pads]
+            offs = (0, 0, 0)
         out.append((i, M, N, K, alpha, beta, pads, offs))
     return out
 
@@ -379,7 +383,9 @@ def random_configs(n, seed):
 @pytest.mark.parametrize("cfg", random_configs(60, 2024), ids=lambda c: f"r{c[0]}")
 def test_random_configs_every_entry_point(cfg):
     """Seeded random sizes, leading-dimension padding, base misalignment and
-    alpha/beta, through sgemm, sgemm_ws (which may split K) and the VALU path."""
+    alpha/beta, through sgemm, sgemm_ws (which may split K: every fourth
+    configuration has few tiles, long K and 128-bit operands) and the VALU
+    path."""
     i, M, N, K, alpha, beta, pads, offs = cfg
     p = inputs.make_problem(M, N, K, dist="upm1", seed=100 + i, alpha=alpha, beta=beta,
                             c_fill="upm1", lda=K + pads[0], ldb=N + pads[1], ldc=N + pads[2])
@@ -395,6 +401,9 @@ def test_random_configs_every_entry_point(cfg):
     oa, _, a = gu.to_gpu(p.A, offs[0])
     ob, _, b = gu.to_gpu(p.B, offs[1])
     oc, first, c = gu.to_gpu(p.C, offs[2])
+    if i % 4 == 3:
+        assert g.sgemm_operands_128(N, K, a, p.lda, b, p.ldb, c, p.ldc)
+        assert g.sgemm_select_splits(M, N, K) > 1, (M, N, K)
     g.sgemm_ws(M, N, K, alpha, a, p.lda, b, p.ldb, beta, c, p.ldc, workspace=ws)
     torch.cuda.synchronize()
     got = oc.cpu().numpy()[first:first + p.C.numel()].reshape(p.C.shape)
