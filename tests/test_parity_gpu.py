@@ -329,6 +329,30 @@ def test_huge_leading_dimension_takes_checked_accesses():
     del oa, ob, oc
 
 
+def test_sgemm_ws_plan_beyond_31_bit_offsets_runs_whole_tiles():
+    """A split plan whose 64 x 64 block cannot address A in 31 bits (lda = 9M
+    floats: 65 rows span more than 2^31 bytes) runs as sgemm() does instead of
+    being refused: here the 32 x 32 block, whose 33 rows still fit."""
+    M, N, K, lda = 8, 64, 4096, 9_000_000
+    p = inputs.make_problem(M, N, K, dist="upm1", seed=67, alpha=1.25, beta=-0.5, c_fill="upm1",
+                            lda=lda)
+    need = g.sgemm_workspace_size(M, N, K)
+    assert need > 0 and g.sgemm_select_splits(M, N, K) > 1
+    ws = torch.full((need // 4 + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    oa, _, a = gu.to_gpu(p.A)
+    ob, _, b = gu.to_gpu(p.B)
+    oc, first, c = gu.to_gpu(p.C)
+    assert g.sgemm_operands_128(N, K, a, lda, b, N, c, N)
+    gu.say("sgemm_ws huge lda", lda)
+    rc = g.sgemm_ws(M, N, K, p.alpha, a, lda, b, N, p.beta, c, N, workspace=ws, check=False)
+    torch.cuda.synchronize()
+    assert rc == 0, rc
+    host = oc.cpu().numpy()
+    assert np.all(np.isnan(np.concatenate([host[:first], host[first + p.C.numel():]])))
+    assert gu.ratio_full(p, host[first:first + p.C.numel()].reshape(p.C.shape)) <= TOL
+    del oa, ob, oc
+
+
 @pytest.mark.parametrize("path", [g.SGEMM_PATH_AUTO, g.SGEMM_PATH_VALU])
 def test_c_beyond_4_gib(path):
     """C of 40000 x 32768 floats (5.2 GB): byte offsets into C pass 2^32 and
