@@ -21,7 +21,7 @@ from . import inputs  # noqa: F401  (seeded synthetic inputs; no GPU needed)
 __all__ = [
     "SGEMM_PATH_AUTO", "SGEMM_PATH_VALU", "SGEMM_PATH_MFMA",
     "SGEMM_ACCESS_AUTO", "SGEMM_ACCESS_BUFFER_128", "SGEMM_ACCESS_BUFFER_32",
-    "SGEMM_ACCESS_CHECKED", "sgemm_variant_access",
+    "SGEMM_ACCESS_CHECKED", "SGEMM_ACCESS_BUFFER_128_AB", "sgemm_variant_access",
     "sgemm_ws", "sgemm_ws_noalloc", "SGEMM_NOALLOC_SCRATCH_BYTES", "sgemm_workspace_size", "sgemm_select_splits", "sgemm_splitk",
     "sgemm_splitk_workspace_size", "sgemm_streamk", "sgemm_streamk_workspace_size",
     "sgemm_select_streamk", "sgemm_ws_plan", "sgemm_select_rows", "sgemm_plan_for",
@@ -29,7 +29,9 @@ __all__ = [
     "SgemmError", "LibraryNotBuilt", "library_path", "load_library",
     "sgemm", "sgemm_path", "sgemm_variant", "sgemm_variant_count",
     "sgemm_variant_name", "sgemm_variant_path", "sgemm_variant_tile", "sgemm_variant_reads_a128",
-    "sgemm_select_variant", "sgemm_select_variant_for", "sgemm_operands_128", "sgemm_status_string", "variants", "sgemm_device_fp32_peak",
+    "sgemm_select_variant", "sgemm_select_variant_for", "sgemm_operands_128", "sgemm_variant_builds",
+    "SGEMM_BUILD_BUFFER_128", "SGEMM_BUILD_BUFFER_32", "SGEMM_BUILD_CHECKED", "SGEMM_BUILD_BUFFER_128_AB",
+    "SGEMM_BUILD_SPLITK", "SGEMM_BUILD_STREAMK", "sgemm_status_string", "variants", "sgemm_device_fp32_peak",
 ]
 
 SGEMM_PATH_AUTO = 0
@@ -40,6 +42,7 @@ SGEMM_ACCESS_AUTO = 0
 SGEMM_ACCESS_BUFFER_128 = 1
 SGEMM_ACCESS_BUFFER_32 = 2
 SGEMM_ACCESS_CHECKED = 3
+SGEMM_ACCESS_BUFFER_128_AB = 4
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIBNAME = "libsgemm_mi355x.so"
@@ -126,6 +129,8 @@ def load_library():
         lib.sgemm_select_variant.restype = i
         lib.sgemm_select_variant_for.argtypes = [i, i, i, i, vp, i, vp, i, vp, i]
         lib.sgemm_select_variant_for.restype = i
+        lib.sgemm_variant_builds.argtypes = [i]
+        lib.sgemm_variant_builds.restype = i
         lib.sgemm_operands_128.argtypes = [i, i, vp, i, vp, i, vp, i]
         lib.sgemm_operands_128.restype = i
         lib.sgemm_status_string.argtypes = [i]
@@ -316,6 +321,15 @@ def variant_has_splitk(variant) -> bool:
 
 def sgemm_variant_count() -> int:
     return int(load_library().sgemm_variant_count())
+
+
+SGEMM_BUILD_BUFFER_128, SGEMM_BUILD_BUFFER_32, SGEMM_BUILD_CHECKED = 1, 2, 4
+SGEMM_BUILD_BUFFER_128_AB, SGEMM_BUILD_SPLITK, SGEMM_BUILD_STREAMK = 8, 16, 32
+
+
+def sgemm_variant_builds(variant) -> int:
+    """Bit mask of the builds a variant has (SGEMM_BUILD_*), or SGEMM_ERR_VARIANT."""
+    return int(load_library().sgemm_variant_builds(int(variant)))
 
 
 def sgemm_variant_name(variant):

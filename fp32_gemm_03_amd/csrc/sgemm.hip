@@ -36,6 +36,8 @@ struct Variant {
     int streamk;        // 1: the split builds also run stream-K (phases 2 and 3)
     int generic_buf;    // 1: `generic` is a buffer-access build too (no plain-pointer
                         // build exists), so it needs in-tile offsets below 2^31
+    KernelFn vec4u;     // 16-byte loads of A and B at any 4-byte alignment, 32-bit C
+                        // (nullptr: no such build)
 };
 
 // VALU: BM x BN x BK block, waves of (8 TM) x (8 TN), TM x TN per lane.
@@ -74,7 +76,8 @@ struct Variant {
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 2, 0, SWZ, true>,       \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, 2, 0, SWZ, true>,      \
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO>,                           \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 1, WPE, true, RO>, 1, 1}
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 1, WPE, true, RO>, 1, 1, 0,                  \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, true>}
 
 // A small K-ordered block of 32 x 32 waves split over KG wave groups; all
 // three builds are sgemm_mfma_kc (128-bit, then 4-byte loads into LDS), so
@@ -84,7 +87,8 @@ struct Variant {
      KG * (BM / 32) * (BN / 32) * 64,                                                         \
      sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2>,                        \
      sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2>,                        \
-     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2>, nullptr, nullptr, 1, 0, 1}
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2>, nullptr, nullptr, 1, 0, 1, \
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2, true>}
 
 // The table holds the blocks the choice by shape can pick (the VALU pair and
 // the K-ordered blocks) and the alternatives kept for measurement: the
@@ -116,7 +120,8 @@ const Variant kVariants[] = {
      sgk::sgemm_mfma<64, 64, 64, 32, 32, 4, 0, 1, 2, true, 1, 2, 0, false, true>,
      sgk::sgemm_mfma<64, 64, 64, 32, 32, 4, 0, 1, 2, false, 1, 2, 0, false, true>,
      sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1>,
-     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 1, 2, true, 1>, 1, 1},
+     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 1, 2, true, 1>, 1, 1, 0,
+     sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2, true>},
     MFMA_CFG_KCD(128, 128, 32, 64, 32, 4, 4, false, 2, "_w8_kcd"),  // 14: 8 waves, 2 workgroups per CU
     // 15: 7 with 16 waves of 64 x 64, four per SIMD, whole tiles only: its
     // split builds would spill (55-96 registers at the 128-register cap), so
@@ -126,7 +131,8 @@ const Variant kVariants[] = {
      sgk::sgemm_mfma_kc<256, 256, 32, 64, 64, 4, 4, false, 2, 1>,
      sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, true, 1, 2, 0, false, true>,
      sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, false, 1, 2, 0, false, true>,
-     nullptr, nullptr, 1, 0},
+     nullptr, nullptr, 1, 0, 0,
+     sgk::sgemm_mfma_kc<256, 256, 32, 64, 64, 4, 4, false, 2, 1, 1, 2, true>},
     // 16: 15 with K tiles of 16 in a ring of four LDS stages, each tile's
     // loads issued three tiles ahead (sgemm_mfma_kc, STG): a measured
     // alternative to the two-stage double buffer, 3% slower at 4096^3 and
@@ -335,9 +341,10 @@ constexpr double kSmallRate = 110.0;
 // The variant for a whole-tile (or, with streamk, stream-K) launch on a
 // machine of m.cus compute units; *score gets its predicted TFLOP/s (rate x
 // the busy share of the last round x the share of the tiles' area inside C).
-// aligned: the operands allow 128-bit accesses (launch's BUFFER_128 mode for
-// a variant that reads A along K), which the small blocks need to be fast.
-int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool aligned, int *workers,
+// small_ok: the operands allow the small blocks' 16-byte loads (rows of A and
+// B 4-byte aligned, in-tile offsets within 31 bits), which they need to be
+// fast (their other builds load 4 bytes per lane into LDS).
+int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool small_ok, int *workers,
            double *score_out = nullptr) {
     if (workers) *workers = 0;
     if (score_out) *score_out = 0.0;
@@ -415,11 +422,11 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool a
         const long long t = tiles(M, N, v.bm, v.bn), rest = t % cus;
         const long long kt = (K + v.bk - 1) / v.bk;
         const bool sk = streamk && rest > 0 && rest * kt >= kStreamKMinK * cus;
-        if (aligned && tiles(M, N, 32, 32) <= 3 * cus) {
+        if (small_ok && tiles(M, N, 32, 32) <= 3 * cus) {
             if (score_out) *score_out = kSmallRate * fill(M, N, 32, 32);
             return kKcTiny4;
         }
-        if (aligned && tiles(M, N, 32, 64) <= 3 * cus) {
+        if (small_ok && tiles(M, N, 32, 64) <= 3 * cus) {
             if (score_out) *score_out = kSmallRate * fill(M, N, 32, 64);
             return kKcTiny2;
         }
@@ -433,8 +440,8 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool a
     return best;
 }
 
-int select_variant(const Machine &m, int path, int M, int N, int K, bool aligned) {
-    return choose(m, path, M, N, K, false, aligned, nullptr);
+int select_variant(const Machine &m, int path, int M, int N, int K, bool small_ok) {
+    return choose(m, path, M, N, K, false, small_ok, nullptr);
 }
 
 // Without a workspace there is no stream-K, and a partial last round of
@@ -446,10 +453,10 @@ int select_variant(const Machine &m, int path, int M, int N, int K, bool aligned
 // 144.5 TFLOP/s against 136.4, 139.1 and 140.2 for one launch (the split the
 // model picks there was within 1% of the best one tried).  Only bottom parts
 // of up to 64 block rows are tried.
-int split_rows(const Machine &m, int M, int N, int K, bool aligned) {
+int split_rows(const Machine &m, int M, int N, int K, bool small_ok) {
     if (K < 512 || M < 512) return 0;
     double single = 0.0;
-    if (choose(m, SGEMM_PATH_AUTO, M, N, K, false, aligned, nullptr, &single) < 0 || single <= 0.0) return 0;
+    if (choose(m, SGEMM_PATH_AUTO, M, N, K, false, small_ok, nullptr, &single) < 0 || single <= 0.0) return 0;
     const long long nbn = (N + 255) / 256;
     const double per_row = 2.0 * N * (double)K;
     const double t_single = per_row * M / single;
@@ -465,7 +472,7 @@ int split_rows(const Machine &m, int M, int N, int K, bool aligned) {
         if (q < 0.96) continue;
         const int m1 = (int)(r * 256), m2 = M - m1;
         double s2 = 0.0;
-        if (choose(m, SGEMM_PATH_AUTO, m2, N, K, false, aligned, nullptr, &s2) < 0 || s2 <= 0.0) continue;
+        if (choose(m, SGEMM_PATH_AUTO, m2, N, K, false, small_ok, nullptr, &s2) < 0 || s2 <= 0.0) continue;
         const double t_split = per_row * m1 / (kHuge16Rate * q * fill_n) + per_row * m2 / s2;
         if (t_split < best_t) {
             best_t = t_split;
@@ -511,11 +518,17 @@ constexpr int kTinySplitMin = 4;
 // 4 bytes per lane straight into LDS, and measured slower than one launch of
 // whole tiles (767^3 in 3 parts 27.6 against 47.5 TFLOP/s, 1535^3 stream-K
 // 60.0 against 88.6, 1023 x 1023 x 4095 in 2 parts 62.7 against 100.2).
-int plan(const Machine &m, int M, int N, int K, bool with_workspace, bool aligned, int *variant,
+struct Operands {
+    bool vec4;   // every 128-bit access: launch's BUFFER_128 mode (for the split builds)
+    bool small;  // the small blocks' 16-byte loads at 4-byte alignment
+};
+constexpr Operands kOperands128 = {true, true};
+
+int plan(const Machine &m, int M, int N, int K, bool with_workspace, Operands ops, int *variant,
          int *splits, int *workers, int *rows) {
     int w = 0;
-    const bool parts = with_workspace && aligned;
-    int v = choose(m, SGEMM_PATH_AUTO, M, N, K, parts, aligned, &w);
+    const bool parts = with_workspace && ops.vec4;
+    int v = choose(m, SGEMM_PATH_AUTO, M, N, K, parts, ops.small, &w);
     if (v < 0) return v;
     int sp = 1, r = 0;
     if (parts && w == 0) {
@@ -529,7 +542,7 @@ int plan(const Machine &m, int M, int N, int K, bool with_workspace, bool aligne
             sp = select_splits(m, v, M, N, K);
         }
     }
-    if (w == 0 && sp == 1) r = split_rows(m, M, N, K, aligned);
+    if (w == 0 && sp == 1) r = split_rows(m, M, N, K, ops.small);
     if (variant) *variant = v;
     if (splits) *splits = sp;
     if (workers) *workers = w;
@@ -553,16 +566,20 @@ int check_args(int M, int N, int K, float alpha, const float *A, int lda,
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
-// The operands allow the small blocks' 128-bit builds: launch's BUFFER_128
-// condition for a variant that reads A 128 bits at a time (16-byte aligned
-// A, B and C; N, K and the leading dimensions multiples of 4), with the
+// What the operands allow: vec4, launch's BUFFER_128 condition for a
+// variant that reads A 128 bits at a time (16-byte aligned A, B and C; N, K
+// and the leading dimensions multiples of 4); small, the 16-byte loads of
+// the small blocks at 4-byte alignment (BUFFER_128_AB); both with the
 // in-tile byte offsets of a 32 x 64 x 64 block below 2^31.
-bool operands128(int N, int K, const float *A, int lda, const float *B, int ldb, const float *C, int ldc) {
+Operands operands(int N, int K, const float *A, int lda, const float *B, int ldb, const float *C, int ldc) {
     const long long lim = 1LL << 31;
-    return N % 4 == 0 && K % 4 == 0 && lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0 && aligned16(A) &&
-           aligned16(B) && aligned16(C) && 33LL * lda * 4 < lim && 65LL * ldb * 4 + 64 * 4 < lim &&
-           33LL * ldc * 4 < lim;
+    const bool offsets = 33LL * lda * 4 < lim && 65LL * ldb * 4 + 64 * 4 < lim && 33LL * ldc * 4 < lim;
+    const bool vec4 = N % 4 == 0 && K % 4 == 0 && lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0 &&
+                      aligned16(A) && aligned16(B) && aligned16(C) && offsets;
+    const bool small = offsets && aligned4(A) && aligned4(B) && aligned4(C);
+    return {vec4, small};
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -591,7 +608,7 @@ int launch(const Machine &m, int variant, int access, int splits, int workers, v
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     if (variant < 0 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
-    if (access < SGEMM_ACCESS_AUTO || access > SGEMM_ACCESS_CHECKED) return SGEMM_ERR_ACCESS;
+    if (access < SGEMM_ACCESS_AUTO || access > SGEMM_ACCESS_BUFFER_128_AB) return SGEMM_ERR_ACCESS;
     if (splits < 1 || splits > kMaxSplits) return SGEMM_ERR_SPLITS;
     if (splits > 1 && kVariants[variant].split4 == nullptr) return SGEMM_ERR_SPLITS;
     if (workers < 0 || workers > kMaxWorkers || (workers > 0 && splits > 1)) return SGEMM_ERR_SPLITS;
@@ -639,6 +656,11 @@ int launch(const Machine &m, int variant, int access, int splits, int workers, v
     const bool vec4 = (N % 4 == 0) && (ldb % 4 == 0) && (ldc % 4 == 0) &&
                       aligned16(B) && aligned16(C) &&
                       (!v.a128 || ((K % 4 == 0) && (lda % 4 == 0) && aligned16(A)));
+    // 16-byte loads of A and B need only 4-byte aligned rows: a buffer load
+    // of 16 bytes at a 4-byte aligned offset reads them, and its range check
+    // is per 4 bytes, so a load that straddles a matrix's end keeps what lies
+    // inside (checked on gfx950 with an in-bounds probe)
+    const bool vec4u = v.vec4u != nullptr && aligned4(A) && aligned4(B) && aligned4(C);
     KernelFn fn;
     switch (access) {
         case SGEMM_ACCESS_BUFFER_128:
@@ -652,8 +674,12 @@ int launch(const Machine &m, int variant, int access, int splits, int workers, v
         case SGEMM_ACCESS_CHECKED:
             fn = v.generic;
             break;
+        case SGEMM_ACCESS_BUFFER_128_AB:
+            if (!buf_ok || !vec4u) return SGEMM_ERR_ACCESS;
+            fn = v.vec4u;
+            break;
         default:
-            fn = !buf_ok ? v.generic : (vec4 ? v.vec4 : v.vec1);
+            fn = !buf_ok ? v.generic : (vec4 ? v.vec4 : (vec4u ? v.vec4u : v.vec1));
             break;
     }
     if (fn == v.generic && v.generic_buf && !buf_ok) return SGEMM_ERR_ACCESS;
@@ -695,8 +721,8 @@ int launch_rows(const Machine &m, int rows, int M, int N, int K, float alpha, co
     int rc = launch(m, kKcHuge16, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, rows, N, K, alpha, A, lda, B,
                     ldb, beta, C, ldc, stream);
     if (rc != SGEMM_OK) return rc;
-    const bool aligned = operands128(N, K, A, lda, B, ldb, C, ldc);
-    const int v2 = select_variant(m, SGEMM_PATH_AUTO, M - rows, N, K, aligned);
+    const bool small = operands(N, K, A, lda, B, ldb, C, ldc).small;
+    const int v2 = select_variant(m, SGEMM_PATH_AUTO, M - rows, N, K, small);
     if (v2 < 0) return v2;
     return launch(m, v2, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M - rows, N, K, alpha,
                   A + (size_t)rows * lda, lda, B, ldb, beta, C + (size_t)rows * ldc, ldc, stream);
@@ -718,11 +744,11 @@ int sgemm_path(int path, int M, int N, int K, float alpha, const float *A,
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     const Machine m = device_machine();
-    const bool aligned = operands128(N, K, A, lda, B, ldb, C, ldc);
-    const int v = select_variant(m, path, M, N, K, aligned);
+    const bool small = operands(N, K, A, lda, B, ldb, C, ldc).small;
+    const int v = select_variant(m, path, M, N, K, small);
     if (v < 0) return v;
     if (path != SGEMM_PATH_VALU) {
-        const int rows = split_rows(m, M, N, K, aligned);
+        const int rows = split_rows(m, M, N, K, small);
         if (rows > 0) return launch_rows(m, rows, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
     }
     return launch(m, v, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C,
@@ -776,19 +802,21 @@ size_t sgemm_streamk_workspace_size(int variant, int workers) {
 
 int sgemm_select_splits(int M, int N, int K) {
     int sp = 1;
-    const int rc = plan(device_machine(), M, N, K, true, true, nullptr, &sp, nullptr, nullptr);
+    const int rc = plan(device_machine(), M, N, K, true, kOperands128, nullptr, &sp, nullptr, nullptr);
     return rc < 0 ? rc : sp;
 }
 
 int sgemm_ws_plan(int M, int N, int K, int *variant, int *splits, int *workers) {
-    return plan(device_machine(), M, N, K, true, true, variant, splits, workers, nullptr);
+    return plan(device_machine(), M, N, K, true, kOperands128, variant, splits, workers, nullptr);
 }
 
 int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int operands_128,
                    int *variant, int *splits, int *workers, int *rows) {
     if (compute_units < 1 || compute_units > (1 << 20)) return SGEMM_ERR_MACHINE;
     const Machine m = {compute_units, kMI355X.xcds};
-    return plan(m, M, N, K, with_workspace != 0, operands_128 != 0, variant, splits, workers, rows);
+    // operands_128 == 0: rows only 4-byte aligned (the small blocks' 16-byte loads still apply)
+    const Operands ops = {operands_128 != 0, true};
+    return plan(m, M, N, K, with_workspace != 0, ops, variant, splits, workers, rows);
 }
 
 int sgemm_device_shape(int *compute_units, int *xcds) {
@@ -817,21 +845,21 @@ int sgemm_select_rows(int M, int N, int K) {
 
 int sgemm_select_streamk(int M, int N, int K) {
     int w = 0;
-    const int rc = plan(device_machine(), M, N, K, true, true, nullptr, nullptr, &w, nullptr);
+    const int rc = plan(device_machine(), M, N, K, true, kOperands128, nullptr, nullptr, &w, nullptr);
     return rc < 0 ? rc : w;
 }
 
 // Workspace bytes of the plan sgemm_ws makes with enough of it.
-size_t plan_bytes(const Machine &m, int M, int N, int K, bool aligned) {
+size_t plan_bytes(const Machine &m, int M, int N, int K, Operands ops) {
     int v = 0, sp = 1, w = 0;
-    if (plan(m, M, N, K, true, aligned, &v, &sp, &w, nullptr) < 0) return 0;
+    if (plan(m, M, N, K, true, ops, &v, &sp, &w, nullptr) < 0) return 0;
     if (w > 0) return streamk_bytes(kVariants[v], w);
     return sp > 1 ? splitk_bytes(kVariants[v], sp, M, N) : 0;
 }
 
 size_t sgemm_workspace_size(int M, int N, int K) {
     // only 128-bit operands split K or run stream-K
-    return plan_bytes(device_machine(), M, N, K, true);
+    return plan_bytes(device_machine(), M, N, K, kOperands128);
 }
 
 int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
@@ -840,9 +868,9 @@ int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const fl
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     const Machine m = device_machine();
-    const bool aligned = operands128(N, K, A, lda, B, ldb, C, ldc);
+    const Operands ops = operands(N, K, A, lda, B, ldb, C, ldc);
     int v = 0, sp = 1, w = 0, rows = 0;
-    const int prc = plan(m, M, N, K, true, aligned, &v, &sp, &w, &rows);
+    const int prc = plan(m, M, N, K, true, ops, &v, &sp, &w, &rows);
     if (prc != SGEMM_OK) return prc;
     const bool room = workspace != nullptr && ((uintptr_t)workspace & 255u) == 0;
     if (w > 0 || sp > 1) {
@@ -863,9 +891,9 @@ int sgemm_ws_noalloc(int M, int N, int K, float alpha, const float *A, int lda, 
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     const Machine m = device_machine();
-    const bool aligned = operands128(N, K, A, lda, B, ldb, C, ldc);
+    const Operands ops = operands(N, K, A, lda, B, ldb, C, ldc);
     int v = 0, sp = 1, w = 0;
-    const int prc = plan(m, M, N, K, true, aligned, &v, &sp, &w, nullptr);
+    const int prc = plan(m, M, N, K, true, ops, &v, &sp, &w, nullptr);
     if (prc != SGEMM_OK) return prc;
     // the bytes sgemm_ws would use with enough workspace (none when there is
     // no product to split)
@@ -881,6 +909,17 @@ int sgemm_ws_noalloc(int M, int N, int K, float alpha, const float *A, int lda, 
 }
 
 int sgemm_variant_count(void) { return kNumVariants; }
+
+int sgemm_variant_builds(int variant) {
+    if (variant < 0 || variant >= kNumVariants) return SGEMM_ERR_VARIANT;
+    const Variant &v = kVariants[variant];
+    int bits = SGEMM_BUILD_BUFFER_128 | SGEMM_BUILD_BUFFER_32;
+    if (!v.generic_buf) bits |= SGEMM_BUILD_CHECKED;
+    if (v.vec4u) bits |= SGEMM_BUILD_BUFFER_128_AB;
+    if (v.split4) bits |= SGEMM_BUILD_SPLITK;
+    if (v.split4 && v.streamk) bits |= SGEMM_BUILD_STREAMK;
+    return bits;
+}
 
 #ifdef SGEMM_PHASES
 // The phase log of the measurement build (fp32_gemm_03_amd/phases.py): n
@@ -921,11 +960,11 @@ int sgemm_select_variant(int path, int M, int N, int K) {
 
 int sgemm_select_variant_for(int path, int M, int N, int K, const float *A, int lda, const float *B, int ldb,
                              const float *C, int ldc) {
-    return select_variant(device_machine(), path, M, N, K, operands128(N, K, A, lda, B, ldb, C, ldc));
+    return select_variant(device_machine(), path, M, N, K, operands(N, K, A, lda, B, ldb, C, ldc).small);
 }
 
 int sgemm_operands_128(int N, int K, const float *A, int lda, const float *B, int ldb, const float *C, int ldc) {
-    return operands128(N, K, A, lda, B, ldb, C, ldc) ? 1 : 0;
+    return operands(N, K, A, lda, B, ldb, C, ldc).vec4 ? 1 : 0;
 }
 
 const char *sgemm_status_string(int status) {

@@ -1199,6 +1199,34 @@ struct DirectStage {
         }
         load_to_lds<W>(rb, Bs + (p * WAVES + wave) * PER_INST, off);
     }
+
+    // With K not a multiple of 4 (16-byte loads at 4-byte alignment), the
+    // chunk of A that holds column K - 1 also brought columns K.. of its row
+    // (the next row's first elements, or 0.0 past A's end).  B's rows >= K
+    // read 0.0, but a non-finite value there would still make 0 * Inf = NaN,
+    // so the stage's copies are cleared once the tile k0.. that holds column
+    // K - 1 has landed, before the barrier that publishes it.
+    __device__ __forceinline__ void fixup_a(const Args &a, float *As, int k0) const {
+        static_assert(W == 4, "chunks of 4 columns");
+#pragma unroll
+        for (int p = 0; p < PA; ++p) {
+            int col;
+            if constexpr (KEEP) {
+                col = acol[p];
+            } else {
+                int l = lane, row;
+                asm volatile("" : "+v"(l));
+                a_pos(p, l, row, col);
+            }
+            const int valid = a.K - (k0 + col);
+            if (valid > 0 && valid < 4) {
+                float *q = As + (p * WAVES + wave) * PER_INST + W * lane;
+#pragma unroll
+                for (int j = 1; j < 4; ++j)
+                    if (j >= valid) q[j] = 0.0f;
+            }
+        }
+    }
 };
 
 // One K tile of MFMAs over a K-ordered A tile.  Inside the tile the k index
@@ -1383,7 +1411,7 @@ __device__ __forceinline__ void ring_barrier() {
 // every wave of the workgroup.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WM, int WN, int VEC, int WPE, bool SPLIT, int RO, int PR = 0,
-          int KG = 1, int STG = 2>
+          int KG = 1, int STG = 2, bool UA = false>
 __global__ void __launch_bounds__(KG * (BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -1402,8 +1430,10 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     // the groups' partial tiles, each in the lanes' own order
     constexpr int RED = KG > 1 ? KG * BM * BN : 0;
     constexpr int SMEM = STG * STAGE > RED ? STG * STAGE : RED;
+    static_assert(!UA || (VEC == 4 && STG == 2 && !SPLIT), "rows at 4-byte alignment: 16-byte whole-tile builds");
     typedef DirectStage<BM, BN, BK, NT, VEC> D;
-    typedef CStoreBuf<NI, VEC> TC;
+    // C in 32-bit accesses when the rows of C need not be 16-byte aligned
+    typedef CStoreBuf<NI, UA ? 1 : VEC> TC;
     __shared__ __attribute__((aligned(16))) float smem[SMEM];
 
     PhaseLog ph;  // whole-tile builds only
@@ -1467,6 +1497,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
         constexpr int AHEAD = (STG - 2) * DP < 63 ? (STG - 2) * DP : 63;
         if constexpr (STG == 2) {
             __builtin_amdgcn_s_waitcnt(0);
+            if constexpr (UA)
+                if ((a.K & 3) != 0 && kb < a.K && kb + BK > a.K) d.fixup_a(a, smem, kb);
             __syncthreads();
         } else if (KT >= STG - 1) {
             ring_barrier<AHEAD>();
@@ -1500,6 +1532,10 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
                 tile_body(smem + (t & 1) * STAGE, smem + ((t + 1) & 1) * STAGE, kb + (t + 1) * BK, true);
                 if (!SPLIT) ph.tile_mid();
                 __builtin_amdgcn_s_waitcnt(0);
+                if constexpr (UA) {
+                    const int kn = kb + (t + 1) * BK;
+                    if ((a.K & 3) != 0 && kn < a.K && kn + BK > a.K) d.fixup_a(a, smem + ((t + 1) & 1) * STAGE, kn);
+                }
                 __syncthreads();
                 if (!SPLIT) ph.tile_end();
             }
@@ -1541,7 +1577,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     auto finish = [&](int bm, int bn) {
         int li_ = li, lh_ = lh;
         if constexpr (SPLIT) asm volatile("" : "+v"(li_), "+v"(lh_));
-        epilogue_mfma_kc<TC, MI, NI, SPLIT ? 8 : 32>(a, bm, bn, wm, wn, li_, lh_, acc);
+        epilogue_mfma_kc<TC, MI, NI, (SPLIT || UA) ? 8 : 32>(a, bm, bn, wm, wn, li_, lh_, acc);
     };
 
     if constexpr (!SPLIT && KG == 1) {
@@ -1582,7 +1618,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
         // 128-byte row segment as in the one-group epilogue.
         constexpr int F4 = BM * BN / 4, PER = F4 / NT;
         static_assert(F4 % NT == 0, "the tile splits into whole 4-float pieces per thread");
-        CStoreBuf<1, VEC> st;
+        CStoreBuf<1, UA ? 1 : VEC> st;
         st.init(a, bm, bn);
         auto pos = [&](int v, int &r, int &c) {
             const int f = tid + NT * (v / 4), e = v % 4;

@@ -1,7 +1,7 @@
 """Time every compiled kernel variant on a set of shapes and compare each
 shape's fastest variant with the one the library's selection picks.
 
-    python -m fp32_gemm_03_amd.tune [--shapes S1,S2,...] [--variants V1,V2,...]
+    python -m fp32_gemm_03_amd.tune [--shapes S1,S2,...] [--variants V1,V2,...] [--access M1,...]
 
 A shape is a named synthetic workload (``square8192_normal`` ...) or MxNxK
 (A, B ~ N(0,1), seed 3, alpha 1, beta 0).  Every launch goes through the C
@@ -77,7 +77,10 @@ def _time(launch, flops, stream, target_s=0.1, warmup_s=0.03):
     return ms, flops / (ms * 1e-3) / 1e12
 
 
-def tune(shapes, variants=None, out=sys.stdout):
+ACCESS_MODES = {"auto": 0, "buf128": 1, "buf32": 2, "checked": 3, "buf128ab": 4}
+
+
+def tune(shapes, variants=None, out=sys.stdout, accesses=("auto",)):
     import torch
     import fp32_gemm_03_amd as g
 
@@ -97,8 +100,14 @@ def tune(shapes, variants=None, out=sys.stdout):
         _, auto, _, _, rows_first = g.sgemm_plan_for(cus, p.M, p.N, p.K, False, o128)
         rows = {}
         for v in variants:
-            ms, tf = _time(lambda: g.sgemm_variant(v, *args, stream=stream), flops, stream)
-            rows[g.sgemm_variant_name(v)] = (ms, tf)
+            for acc in accesses:
+                mode = ACCESS_MODES[acc]
+                if g.sgemm_variant_access(v, mode, *args, stream=stream, check=False) != 0:
+                    continue  # a build these operands do not allow
+                ms, tf = _time(lambda: g.sgemm_variant_access(v, mode, *args, stream=stream),
+                               flops, stream)
+                name = g.sgemm_variant_name(v)
+                rows[name if acc == "auto" else f"{name}:{acc}"] = (ms, tf)
         ms, tf = _time(lambda: g.sgemm(*args, stream=stream), flops, stream)
         rows["auto"] = (ms, tf)
         ws_bytes = g.sgemm_workspace_size(p.M, p.N, p.K)
@@ -139,9 +148,16 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--shapes", default=",".join(DEFAULT_SHAPES))
     ap.add_argument("--variants", default=None, help="comma-separated variant indices (default: all)")
+    ap.add_argument("--access", default="auto",
+                    help="comma-separated access modes to time each variant in: "
+                         + ", ".join(ACCESS_MODES) + " (default: auto, the variant's own choice)")
     args = ap.parse_args()
     variants = None if args.variants is None else [int(x) for x in args.variants.split(",")]
-    tune(args.shapes.split(","), variants)
+    accesses = args.access.split(",")
+    for acc in accesses:
+        if acc not in ACCESS_MODES:
+            ap.error(f"unknown access mode {acc!r}")
+    tune(args.shapes.split(","), variants, accesses=accesses)
 
 
 if __name__ == "__main__":

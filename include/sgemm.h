@@ -27,9 +27,10 @@
  * the device's attributes on first use; the choice of kernel depends on the
  * sizes and that shape only.  No alignment is required: 16-byte aligned bases with leading
  * dimensions and N that are multiples of 4 take 128-bit global accesses
- * (and K a multiple of 4 for the variants that read A 128 bits at a time),
- * anything else takes 32-bit ones (see sgemm_variant_access for the three
- * access modes).  C must not overlap A or B (undefined
+ * (and K a multiple of 4 for the variants that read A 128 bits at a time);
+ * other 4-byte aligned operands take 16-byte loads of A and B at 4-byte
+ * alignment and 32-bit accesses to C on the K-ordered blocks; anything else
+ * takes 32-bit ones (see sgemm_variant_access for the access modes).  C must not overlap A or B (undefined
  * behaviour).  Dimensions and leading dimensions are int; address arithmetic
  * is 64-bit.
  *
@@ -76,6 +77,7 @@ extern "C" {
 #define SGEMM_ACCESS_BUFFER_128 1 /* range-checked buffer accesses, 128-bit on B and C (and A) */
 #define SGEMM_ACCESS_BUFFER_32 2  /* range-checked buffer accesses, 32-bit */
 #define SGEMM_ACCESS_CHECKED 3    /* per-element checked pointer accesses */
+#define SGEMM_ACCESS_BUFFER_128_AB 4 /* 16-byte loads of A and B at 4-byte alignment, 32-bit C */
 
 #define SGEMM_OK 0
 #define SGEMM_ERR_PATH (-20)
@@ -120,7 +122,16 @@ int sgemm_variant(int variant, int M, int N, int K, float alpha,
  *               16-byte aligned A and K and lda multiples of 4 as well.
  *   BUFFER_32   the same with 32-bit accesses: any alignment.
  *   CHECKED     plain pointers with every element checked: any arguments.
- * SGEMM_ACCESS_AUTO takes the first of these the arguments allow.  A forced
+ * and the K-ordered blocks (`_kcd`) once more:
+ *   BUFFER_128_AB  16-byte loads of A and B at any 4-byte alignment (rows of
+ *               any length and leading dimension; a 16-byte buffer load is
+ *               range-checked per 4 bytes, so one that straddles a matrix's
+ *               end keeps what lies inside, and the columns of A past K that
+ *               a load brings along are cleared in LDS), 32-bit accesses to
+ *               C.  Needs 4-byte aligned A, B and C and the in-tile offset
+ *               bound above.
+ * SGEMM_ACCESS_AUTO takes the first of BUFFER_128, BUFFER_128_AB, BUFFER_32
+ * and CHECKED the arguments allow.  A forced
  * mode the arguments do not allow returns SGEMM_ERR_ACCESS.  The small
  * wave-group blocks (32 x 32 and 32 x 64 tiles) have no plain-pointer build:
  * their CHECKED build uses buffer accesses too, so with in-tile offsets of
@@ -177,17 +188,18 @@ int sgemm_ws_noalloc(int M, int N, int K, float alpha, const float *A, int lda,
 
 /* Workspace bytes sgemm_ws() can use for these sizes (0: it never splits).
  * Only operands that allow 128-bit accesses (sgemm_operands_128) split K or
- * run stream-K: for others sgemm_ws() is exactly sgemm(). */
+ * run stream-K: for others sgemm_ws() is exactly sgemm() (their split builds
+ * would load 4 bytes per lane, slower than the whole tiles). */
 size_t sgemm_workspace_size(int M, int N, int K);
 
 /* The plan queries below (sgemm_select_splits, sgemm_select_streamk,
  * sgemm_ws_plan, sgemm_select_variant, sgemm_select_rows) answer for
  * operands that allow 128-bit accesses: A, B and C 16-byte aligned, N, K,
  * lda, ldb and ldc multiples of 4 and leading dimensions below about 2^24
- * (sgemm_operands_128).  For other operands the library takes
- * no block that needs them (the 32 x 32 and 32 x 64 blocks), so small shapes
- * may get another plan: sgemm_select_variant_for() and sgemm_plan_for()
- * answer for any operands. */
+ * (sgemm_operands_128).  Other operands split nothing, and those not 4-byte
+ * aligned or whose tiles span more than 2^31 bytes take neither small block
+ * (32 x 32, 32 x 64), so their plan may differ: sgemm_select_variant_for()
+ * and sgemm_plan_for() answer for any operands. */
 
 /* The split count sgemm_ws() uses with enough workspace (1: no split), or a
  * negative argument code.  Host logic only. */
@@ -247,6 +259,17 @@ size_t sgemm_streamk_workspace_size(int variant, int workers);
 /* Number of compiled kernel variants. */
 int sgemm_variant_count(void);
 
+/* The builds a variant has, as a bit mask (SGEMM_BUILD_*), or
+ * SGEMM_ERR_VARIANT.  CHECKED is set only where that build uses plain
+ * pointers (any leading dimension).  Host logic only. */
+#define SGEMM_BUILD_BUFFER_128 1
+#define SGEMM_BUILD_BUFFER_32 2
+#define SGEMM_BUILD_CHECKED 4
+#define SGEMM_BUILD_BUFFER_128_AB 8
+#define SGEMM_BUILD_SPLITK 16
+#define SGEMM_BUILD_STREAMK 32
+int sgemm_variant_builds(int variant);
+
 /* Static, NUL-terminated name of a variant ("mfma_256x256x32_w128x128" ...),
  * or NULL for an index out of range. */
 const char *sgemm_variant_name(int variant);
@@ -277,8 +300,8 @@ int sgemm_select_variant(int path, int M, int N, int K);
 int sgemm_select_variant_for(int path, int M, int N, int K, const float *A, int lda,
                              const float *B, int ldb, const float *C, int ldc);
 
-/* 1 if these operands allow the 128-bit builds of the small blocks (A, B and
- * C 16-byte aligned; N, K, lda, ldb and ldc multiples of 4; leading
+/* 1 if these operands allow the 128-bit builds, split-K and stream-K (A, B
+ * and C 16-byte aligned; N, K, lda, ldb and ldc multiples of 4; leading
  * dimensions below about 2^24, so that in-tile byte offsets fit 31 bits),
  * else 0: the operands_128 argument of sgemm_plan_for() that describes them.
  * The pointers are only inspected.  Host logic only. */
@@ -308,7 +331,8 @@ int sgemm_device_shape(int *compute_units, int *xcds);
 /* The plan the library makes for these sizes on a device of
  * `compute_units` compute units: with with_workspace != 0 what sgemm_ws()
  * runs with enough workspace, else what sgemm() runs; operands_128 != 0 for
- * operands that allow 128-bit accesses (above), 0 for any others.  Through
+ * operands that allow 128-bit accesses (above), 0 for other 4-byte aligned
+ * ones whose in-tile offsets fit 31 bits.  Through
  * the pointers (each may be NULL): the variant, the split count (1: none),
  * the stream-K worker count (0: none) and the rows of a first row-split
  * launch (0: one launch).  Returns 0, a negative argument code (-1..-3 for

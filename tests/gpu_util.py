@@ -123,7 +123,7 @@ def pad_untouched(p, out):
     return np.array_equal(before.view(np.uint32), after.view(np.uint32))
 
 
-ACCESS_NAMES = {0: "auto", 1: "buf128", 2: "buf32", 3: "checked"}
+ACCESS_NAMES = {0: "auto", 1: "buf128", 2: "buf32", 3: "checked", 4: "buf128ab"}
 
 
 def sum_family(variant, access):
@@ -132,11 +132,25 @@ def sum_family(variant, access):
     ``_kcd`` variants) or the register-staged one ("rs", every other build:
     their 32-bit and checked builds, and every build of the others)."""
     name = g.sgemm_variant_name(variant)
-    return "kc" if name.endswith("_kcd") and access == g.SGEMM_ACCESS_BUFFER_128 else "rs"
+    kc_access = (g.SGEMM_ACCESS_BUFFER_128, g.SGEMM_ACCESS_BUFFER_128_AB)
+    if name.startswith("mfma_32x"):  # the small blocks: every build is the K-ordered kernel
+        return "kc"
+    return "kc" if name.endswith("_kcd") and access in kc_access else "rs"
 
 
 def same_sum_order(variant, a1, a2):
     return sum_family(variant, a1) == sum_family(variant, a2)
+
+
+def auto_access(p, variant, offsets=(0, 0, 0)):
+    """The build SGEMM_ACCESS_AUTO runs for these arguments: the 128-bit
+    one, else the one loading A and B 16 bytes at a time at 4-byte
+    alignment, else the 32-bit one."""
+    modes = allowed_accesses(p, offsets, variant)
+    for m in (g.SGEMM_ACCESS_BUFFER_128, g.SGEMM_ACCESS_BUFFER_128_AB):
+        if m in modes:
+            return m
+    return g.SGEMM_ACCESS_BUFFER_32
 
 
 def allowed_accesses(p, offsets=(0, 0, 0), variant=None):
@@ -150,4 +164,6 @@ def allowed_accesses(p, offsets=(0, 0, 0), variant=None):
         ok128 = ok128 and p.K % 4 == 0 and p.lda % 4 == 0 and offsets[0] % 4 == 0
     if ok128:
         modes.insert(0, g.SGEMM_ACCESS_BUFFER_128)
+    if variant is not None and g.sgemm_variant_builds(variant) & g.SGEMM_BUILD_BUFFER_128_AB:
+        modes.insert(1 if ok128 else 0, g.SGEMM_ACCESS_BUFFER_128_AB)
     return modes

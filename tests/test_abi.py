@@ -99,13 +99,51 @@ def test_access_mode_codes():
                     C=0x3000, ldc=4)
         base.update(kw)
         return g.sgemm_variant_access(0, mode, *base.values(), stream=0, check=False)
-    assert acc(4) == -23
+    assert acc(g.SGEMM_ACCESS_BUFFER_128_AB) == -23             # no such build of this variant
+    assert acc(5) == -23
     assert acc(-1) == -23
     assert acc(g.SGEMM_ACCESS_BUFFER_128, B=0x2004) == -23     # misaligned B
     assert acc(g.SGEMM_ACCESS_BUFFER_128, N=3, ldb=4, ldc=4) == -23
     assert acc(g.SGEMM_ACCESS_BUFFER_32, lda=1 << 30) == -23    # offsets beyond 31 bits
     assert acc(4, M=-1) == -1                                   # argument checks come first
     assert "access mode" in g.sgemm_status_string(-23)
+
+
+def test_builds_loading_a_and_b_16_bytes_at_4_byte_alignment():
+    """The K-ordered blocks' whole-tile build for rows at 4-byte alignment
+    (SGEMM_ACCESS_BUFFER_128_AB): every block the choice takes for large or
+    small shapes has one; forcing it needs A, B, C 4-byte aligned and
+    in-tile offsets below 2^31 (the refusal comes before any HIP call)."""
+    n = g.sgemm_variant_count()
+    builds = [g.sgemm_variant_builds(v) for v in range(n)]
+    assert g.sgemm_variant_builds(n) == -21 and g.sgemm_variant_builds(-1) == -21
+    both = g.SGEMM_BUILD_BUFFER_128 | g.SGEMM_BUILD_BUFFER_32
+    assert all(b & both == both for b in builds)
+    ua = [v for v in range(n) if builds[v] & g.SGEMM_BUILD_BUFFER_128_AB]
+    assert ua and all(g.sgemm_variant_reads_a128(v) == 1 for v in ua)
+    # split builds match the split queries; the checked build uses plain
+    # pointers except on the small blocks
+    for v in range(n):
+        assert bool(builds[v] & g.SGEMM_BUILD_SPLITK) == g.variant_has_splitk(v)
+        assert bool(builds[v] & g.SGEMM_BUILD_STREAMK) == g.variant_has_streamk(v)
+        small = g.sgemm_variant_tile(v)[1] == 32
+        assert bool(builds[v] & g.SGEMM_BUILD_CHECKED) == (not small), g.sgemm_variant_name(v)
+    for shape in [(256, 256, 256), (1000, 1023, 999), (1024, 1024, 1024), (2048, 2048, 2048),
+                  (8192, 8192, 8192), (16384, 16384, 128), (1408, 1408, 1408)]:
+        assert g.sgemm_select_variant(g.SGEMM_PATH_AUTO, *shape) in ua, shape
+    v = g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 8192, 8192, 8192)
+
+    def acc(**kw):
+        base = dict(M=4, N=4, K=4, alpha=1.0, A=0x1000, lda=4, B=0x2000, ldb=4, beta=0.0,
+                    C=0x3000, ldc=4)
+        base.update(kw)
+        return g.sgemm_variant_access(v, g.SGEMM_ACCESS_BUFFER_128_AB, *base.values(), stream=0,
+                                      check=False)
+    assert acc(A=0x1002) == -23          # A not 4-byte aligned
+    assert acc(B=0x2001) == -23
+    assert acc(C=0x3003) == -23
+    assert acc(lda=1 << 24) == -23       # a tile's rows of A beyond 2^31 bytes
+    assert acc(K=0, lda=4, beta=1.0) == 0  # no product: quick return before any launch
 
 
 def test_variants_reading_a_128_bits_need_k_and_a_aligned():
@@ -205,18 +243,21 @@ def test_large_shapes_pick_the_block_whose_last_round_is_fullest():
     assert _block(v) == (64, 64, 32) and w == 256
     rc, v, sp, w = g.sgemm_ws_plan(1408, 1408, 1408)
     assert _block(v) == (64, 64, 64) and (sp, w) == (1, 0)
-    # operands without 128-bit access keep the 64 x 64 blocks, whose 32-bit
-    # builds stage through registers
+    # operands at 4-byte alignment take the same blocks (their 16-byte loads
+    # of A and B need no more); only in-tile offsets beyond 31 bits keep the
+    # 64 x 64 block, whose checked build uses plain pointers
     def block_for(M, N, K, lda, ldb, ldc, off=0):
         v = g.sgemm_select_variant_for(g.SGEMM_PATH_AUTO, M, N, K, 0x10000 + off, lda, 0x20000, ldb,
                                        0x30000, ldc)
         return _block(v)
-    assert block_for(1000, 1023, 999, 999, 1023, 1023) == (64, 64, 64)
+    assert block_for(1000, 1023, 999, 999, 1023, 1023) == (32, 64, 64)
     assert block_for(1024, 1024, 1024, 1024, 1024, 1024) == (32, 64, 64)
-    assert block_for(1024, 1024, 1024, 1024, 1024, 1024, off=4) == (64, 64, 64)   # A not 16-byte aligned
-    assert block_for(512, 512, 512, 513, 512, 512) == (64, 64, 64)                # lda not a multiple of 4
+    assert block_for(1024, 1024, 1024, 1024, 1024, 1024, off=4) == (32, 64, 64)   # A not 16-byte aligned
+    assert block_for(512, 512, 512, 513, 512, 512) == (32, 32, 64)                # lda not a multiple of 4
     assert block_for(512, 512, 512, 512, 512, 512) == (32, 32, 64)
+    assert block_for(512, 512, 512, 1 << 24, 512, 512) == (64, 64, 64)            # 33 rows of A beyond 2^31 bytes
     assert block_for(8192, 8192, 8192, 8192, 8192, 8192) == block(8192, 8192, 8192)
+    assert block_for(8191, 8191, 8191, 8191, 8191, 8191) == block(8192, 8192, 8192)
 
 
 def test_streamk_host_logic():
@@ -459,10 +500,10 @@ def test_plan_quantises_over_other_cu_counts(cus):
             t2 = -(-M // bm2) * -(-N // bn2)
             assert t2 <= cus and t2 * sp2 <= 2 * cus
     # a 32-CU partition fills its CUs with 128 x 256 blocks at 1024^3, where
-    # 256 CUs need a small block (32 x 64, or 64 x 64 for other operands)
+    # 256 CUs need a small block (32 x 64, for either kind of operands)
     assert _block(g.sgemm_plan_for(32, 1024, 1024, 1024)[1])[:2] == (128, 256)
     assert _block(g.sgemm_plan_for(256, 1024, 1024, 1024)[1])[:2] == (32, 64)
-    assert _block(g.sgemm_plan_for(256, 1024, 1024, 1024, operands_128=False)[1])[:2] == (64, 64)
+    assert _block(g.sgemm_plan_for(256, 1024, 1024, 1024, operands_128=False)[1])[:2] == (32, 64)
     # split-K: 64 tiles of 64 x 64 at 512 x 512 x 8192 split in 8 on 256 CUs;
     # on 80 CUs a split would be in 2, so 128-bit operands take the 32 x 64
     # block whole instead, and other operands the split

@@ -229,17 +229,20 @@ def test_zero_padding_invariance(variant):
     big.C[:200, :301] = p.C
     big.alpha, big.beta = p.alpha, p.beta
     gu.say("zero-padding invariance", g.sgemm_variant_name(variant))
-    small = gu.run(p, variant=variant)   # N = 301: 32-bit accesses
-    # N = 384: 128-bit accesses where the variant takes them at this K (the
-    # variants reading A 128 bits at a time need K % 4 == 0, so they stay on
-    # the 32-bit build here): the same arithmetic
+    # N = 301 takes 32-bit accesses, or the build loading A and B 16 bytes at
+    # a time at 4-byte alignment; N = 384 also the 128-bit build where the
+    # variant takes it at this K (the variants reading A 128 bits at a time
+    # need K % 4 == 0, so they do not here): the same arithmetic
+    small = gu.run(p, variant=variant)
     large = gu.run(big, variant=variant)
+    ref_mode = gu.auto_access(big, variant)
+    assert gu.same_sum_order(variant, gu.auto_access(p, variant), ref_mode)
     assert np.array_equal(small.view(np.uint32), large[:200, :301].copy().view(np.uint32))
     # the access modes of one kernel family compute the same sums in the same
     # order (bit for bit); a build of the other family is held to the pass rule
     for acc in gu.allowed_accesses(big, variant=variant):
         other = gu.run(big, variant=variant, access=acc)
-        if gu.same_sum_order(variant, acc, g.SGEMM_ACCESS_BUFFER_32):
+        if gu.same_sum_order(variant, acc, ref_mode):
             assert np.array_equal(other.view(np.uint32), large.view(np.uint32)), acc
         else:
             assert gu.ratio_full(big, other) <= TOL, acc
