@@ -29,7 +29,7 @@ __all__ = [
     "SgemmError", "LibraryNotBuilt", "library_path", "load_library",
     "sgemm", "sgemm_path", "sgemm_variant", "sgemm_variant_count",
     "sgemm_variant_name", "sgemm_variant_path", "sgemm_variant_tile", "sgemm_variant_reads_a128",
-    "sgemm_select_variant", "sgemm_select_variant_for", "sgemm_operands_128", "sgemm_variant_builds",
+    "sgemm_select_variant", "sgemm_select_variant_for", "sgemm_operands_load16", "sgemm_variant_builds",
     "SGEMM_BUILD_BUFFER_128", "SGEMM_BUILD_BUFFER_32", "SGEMM_BUILD_CHECKED", "SGEMM_BUILD_BUFFER_128_AB",
     "SGEMM_BUILD_SPLITK", "SGEMM_BUILD_STREAMK", "sgemm_status_string", "variants", "sgemm_device_fp32_peak",
 ]
@@ -131,8 +131,8 @@ def load_library():
         lib.sgemm_select_variant_for.restype = i
         lib.sgemm_variant_builds.argtypes = [i]
         lib.sgemm_variant_builds.restype = i
-        lib.sgemm_operands_128.argtypes = [i, i, vp, i, vp, i, vp, i]
-        lib.sgemm_operands_128.restype = i
+        lib.sgemm_operands_load16.argtypes = [vp, i, vp, i, vp, i]
+        lib.sgemm_operands_load16.restype = i
         lib.sgemm_status_string.argtypes = [i]
         lib.sgemm_status_string.restype = ctypes.c_char_p
         lib.sgemm_device_fp32_peak.argtypes = [i, vp, vp, vp]
@@ -269,13 +269,13 @@ def sgemm_ws_plan(M, N, K):
     return int(rc), v.value, sp.value, w.value
 
 
-def sgemm_plan_for(compute_units, M, N, K, with_workspace=False, operands_128=True):
+def sgemm_plan_for(compute_units, M, N, K, with_workspace=False, operands_load16=True):
     """``(status, variant, splits, workers, rows)``: the plan for these sizes on a device of
     ``compute_units`` CUs (``sgemm_ws`` with enough workspace, or ``sgemm`` without), for
-    operands that allow 128-bit accesses or (``operands_128=False``) any others."""
+    operands that allow 16-byte loads of A and B or (``operands_load16=False``) others."""
     v, sp, w, r = ctypes.c_int(-1), ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
     rc = load_library().sgemm_plan_for(int(compute_units), int(M), int(N), int(K),
-                                       1 if with_workspace else 0, 1 if operands_128 else 0,
+                                       1 if with_workspace else 0, 1 if operands_load16 else 0,
                                        ctypes.byref(v), ctypes.byref(sp), ctypes.byref(w),
                                        ctypes.byref(r))
     return int(rc), v.value, sp.value, w.value, r.value
@@ -357,10 +357,11 @@ def sgemm_select_variant(path, M, N, K) -> int:
     return int(load_library().sgemm_select_variant(int(path), int(M), int(N), int(K)))
 
 
-def sgemm_operands_128(N, K, A, lda, B, ldb, C, ldc) -> bool:
-    """True when these operands allow 128-bit accesses (the library's small blocks need them)."""
-    return bool(load_library().sgemm_operands_128(int(N), int(K), _ptr(A), int(lda), _ptr(B), int(ldb),
-                                                  _ptr(C), int(ldc)))
+def sgemm_operands_load16(A, lda, B, ldb, C, ldc) -> bool:
+    """True when these operands allow 16-byte loads of A and B (4-byte aligned bases, leading
+    dimensions below about 2^24): the small blocks, split-K and stream-K need them."""
+    return bool(load_library().sgemm_operands_load16(_ptr(A), int(lda), _ptr(B), int(ldb),
+                                                     _ptr(C), int(ldc)))
 
 
 def sgemm_select_variant_for(path, M, N, K, A, lda, B, ldb, C, ldc) -> int:

@@ -30,14 +30,14 @@ struct Variant {
     KernelFn vec4;      // buffer accesses; B, C and their leading dimensions 16-byte friendly
     KernelFn vec1;      // buffer accesses, 32-bit
     KernelFn generic;   // per-element checked pointer accesses (any leading dimension)
-    KernelFn split4;    // split-K, as vec4 (nullptr: no split-K build of this variant)
-    KernelFn split1;    // split-K, as vec1
+    KernelFn split4;    // split-K and stream-K, as vec4 (nullptr: no split-K build of this variant)
     int a128;           // 1: the vec4 build also reads A 128 bits at a time along K
     int streamk;        // 1: the split builds also run stream-K (phases 2 and 3)
     int generic_buf;    // 1: `generic` is a buffer-access build too (no plain-pointer
                         // build exists), so it needs in-tile offsets below 2^31
     KernelFn vec4u;     // 16-byte loads of A and B at any 4-byte alignment, 32-bit C
                         // (nullptr: no such build)
+    KernelFn split4u;   // split-K (and stream-K), as vec4u
 };
 
 // VALU: BM x BN x BK block, waves of (8 TM) x (8 TN), TM x TN per lane.
@@ -46,7 +46,7 @@ struct Variant {
      (BM / (8 * TM)) * (BN / (8 * TN)) * 64,                                             \
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 4, WPE, true>,                       \
      sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, true>,                       \
-     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, false>, nullptr, nullptr, 0, 0}
+     sgk::sgemm_valu<BM, BN, BK, TM, TN, PA, PB, 1, WPE, false>, nullptr, 0, 0}
 
 // A register-staged MFMA block (sgemm_mfma), A transposed in LDS: padded by
 // PA, or unpadded and XOR-swizzled (SWZ); EPI 1 stages the epilogue through
@@ -57,37 +57,39 @@ struct Variant {
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 4, WPE, true, 1, ORD, EPI, SWZ, false>,  \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, ORD, EPI, SWZ, false>,  \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, ORD, EPI, SWZ, false>, \
-     nullptr, nullptr, 0, 0}
+     nullptr, 0, 0}
 
-// A variant with A kept in K order (sgemm_mfma_kc): its 128-bit builds load
-// straight into LDS; also compiled with split-K and stream-K (32-bit split
-// builds load 4 bytes per lane).  Its 32-bit and checked whole-tile builds
-// are the same block on the interleaved schedule (A transposed, padded by PA
-// or XOR-swizzled): loading straight into LDS 4 bytes per lane is 4% slower
-// than that at 8192^3 (140 against 146 TFLOP/s).  Those two sum the k of a
-// K tile in the same order as each other, the 128-bit builds in another.
-// RO is the order of the LDS fragment reads at a K tile's start
-// (mfma_tile_kc), chosen per block by measurement.  All four builds map
-// workgroups to tiles with tile_of<2, 8> (each XCD on its own tile columns).
+// A variant with A kept in K order (sgemm_mfma_kc): its 128-bit builds, and
+// its builds for rows at 4-byte alignment (16-byte loads of A and B, 32-bit
+// C), load straight into LDS, as whole tiles and with split-K and stream-K.
+// Its 32-bit and checked whole-tile builds are the same block on the
+// interleaved schedule (A transposed, padded by PA or XOR-swizzled):
+// loading straight into LDS 4 bytes per lane is 4% slower than that at
+// 8191^3 (140 against 145-146 TFLOP/s).  Those two sum the k of a K tile in
+// the same order as each other, the 16-byte load builds in another.  RO is
+// the order of the LDS fragment reads at a K tile's start (mfma_tile_kc),
+// chosen per block by measurement.  Every build maps workgroups to tiles
+// with tile_of<2, 8> (each XCD on its own tile columns).
 #define MFMA_CFG_KCD(BM, BN, BK, WM, WN, WPE, PA, SWZ, RO, SUFFIX)                      \
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
      (BM / WM) * (BN / WN) * 64,                                                         \
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO>,                          \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 2, 0, SWZ, true>,       \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, 2, 0, SWZ, true>,      \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO>,                           \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 1, WPE, true, RO>, 1, 1, 0,                  \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, true>}
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO>, 1, 1, 0,                  \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, true>,           \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO, 0, 1, 2, true>}
 
 // A small K-ordered block of 32 x 32 waves split over KG wave groups; all
-// three builds are sgemm_mfma_kc (128-bit, then 4-byte loads into LDS), so
-// even its checked build needs in-tile offsets below 2^31.
+// four builds are sgemm_mfma_kc (128-bit, 4-byte loads into LDS twice, and
+// 16-byte loads at 4-byte alignment), so even its checked build needs
+// in-tile offsets below 2^31.
 #define MFMA_CFG_KG(BM, BN, BK, KG, SUFFIX)                                                   \
     {"mfma_" #BM "x" #BN "x" #BK "_w32x32" SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,                 \
      KG * (BM / 32) * (BN / 32) * 64,                                                         \
      sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2>,                        \
      sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2>,                        \
-     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2>, nullptr, nullptr, 1, 0, 1, \
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2>, nullptr, 1, 0, 1,          \
      sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2, true>}
 
 // The table holds the blocks the choice by shape can pick (the VALU pair and
@@ -109,7 +111,8 @@ const Variant kVariants[] = {
     MFMA_CFG_KCD(128, 256, 32, 64, 64, 2, 4, false, 2, "_w8_kcd"),  // 10: 8 waves, 2 per SIMD
     MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, 1, "_kcd"),       // 11: 4 workgroups per CU
     MFMA_CFG_KCD(128, 128, 64, 32, 64, 2, 4, false, 2, "_w8_kcd"),  // 12: 8 waves, 2 per SIMD
-    // 13: the block for at most one tile per CU.  Its 128-bit build is two
+    // 13: the block for at most one tile per CU.  Its 128-bit build (and
+    // the one for rows at 4-byte alignment) is two
     // wave groups (KG 2) of two 64 x 32 waves, each group half of every K
     // tile: two MFMAs per k-step and wave instead of one, and per MFMA half
     // the LDS fragment reads of four 32 x 32 waves.  Its 32-bit and checked
@@ -119,9 +122,9 @@ const Variant kVariants[] = {
      sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2>,
      sgk::sgemm_mfma<64, 64, 64, 32, 32, 4, 0, 1, 2, true, 1, 2, 0, false, true>,
      sgk::sgemm_mfma<64, 64, 64, 32, 32, 4, 0, 1, 2, false, 1, 2, 0, false, true>,
-     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1>,
-     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 1, 2, true, 1>, 1, 1, 0,
-     sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2, true>},
+     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1>, 1, 1, 0,
+     sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2, true>,
+     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1, 0, 1, 2, true>},
     MFMA_CFG_KCD(128, 128, 32, 64, 32, 4, 4, false, 2, "_w8_kcd"),  // 14: 8 waves, 2 workgroups per CU
     // 15: 7 with 16 waves of 64 x 64, four per SIMD, whole tiles only: its
     // split builds would spill (55-96 registers at the 128-register cap), so
@@ -131,7 +134,7 @@ const Variant kVariants[] = {
      sgk::sgemm_mfma_kc<256, 256, 32, 64, 64, 4, 4, false, 2, 1>,
      sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, true, 1, 2, 0, false, true>,
      sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, false, 1, 2, 0, false, true>,
-     nullptr, nullptr, 1, 0, 0,
+     nullptr, 1, 0, 0,
      sgk::sgemm_mfma_kc<256, 256, 32, 64, 64, 4, 4, false, 2, 1, 1, 2, true>},
     // 16: 15 with K tiles of 16 in a ring of four LDS stages, each tile's
     // loads issued three tiles ahead (sgemm_mfma_kc, STG): a measured
@@ -142,7 +145,7 @@ const Variant kVariants[] = {
      sgk::sgemm_mfma_kc<256, 256, 16, 64, 64, 4, 4, false, 2, 1, 1, 4>,
      sgk::sgemm_mfma<256, 256, 16, 64, 64, 4, 0, 1, 4, true, 1, 2, 0, false, true>,
      sgk::sgemm_mfma<256, 256, 16, 64, 64, 4, 0, 1, 4, false, 1, 2, 0, false, true>,
-     nullptr, nullptr, 1, 0},
+     nullptr, 1, 0},
     // 17, 18: small tiles for shapes that cannot give every CU a 64 x 64
     // tile, each tile split over wave groups (KG) so that a workgroup still
     // has four waves: 32 x 32 in four groups of one wave, 32 x 64 in two
@@ -150,8 +153,8 @@ const Variant kVariants[] = {
     // prologue and epilogue (512^3: 47 against 22 TFLOP/s on 64 x 64).
     // Their 32-bit and checked builds are the same block loading 4 bytes
     // per lane straight into LDS, which is slow (the choice takes these
-    // blocks only for operands that allow 128-bit accesses); no split
-    // builds.
+    // blocks only for operands that allow 16-byte loads of A and B); no
+    // split builds.
     MFMA_CFG_KG(32, 32, 64, 4, "_kg4_kcd"),
     MFMA_CFG_KG(32, 64, 64, 2, "_kg2_kcd"),
 };
@@ -514,21 +517,17 @@ constexpr int kTinySplitMin = 4;
 // What sgemm_ws (with_workspace) or sgemm (without) runs for these sizes:
 // the variant, split count, stream-K workers and the rows of a first
 // row-split launch (0: none).  Returns 0 or a negative argument code.
-// Split-K and stream-K only for 128-bit operands: their 32-bit builds load
-// 4 bytes per lane straight into LDS, and measured slower than one launch of
+// load16: the operands allow 16-byte loads of A and B (loads16 below),
+// which the small blocks, split-K and stream-K need: loading 4 bytes per
+// lane straight into LDS, split launches measured slower than one launch of
 // whole tiles (767^3 in 3 parts 27.6 against 47.5 TFLOP/s, 1535^3 stream-K
-// 60.0 against 88.6, 1023 x 1023 x 4095 in 2 parts 62.7 against 100.2).
-struct Operands {
-    bool vec4;   // every 128-bit access: launch's BUFFER_128 mode (for the split builds)
-    bool small;  // the small blocks' 16-byte loads at 4-byte alignment
-};
-constexpr Operands kOperands128 = {true, true};
-
-int plan(const Machine &m, int M, int N, int K, bool with_workspace, Operands ops, int *variant,
+// 60.0 against 88.6, 1023 x 1023 x 4095 in 2 parts 62.7 against 100.2), and
+// the small blocks slower than the 64 x 64 one.
+int plan(const Machine &m, int M, int N, int K, bool with_workspace, bool load16, int *variant,
          int *splits, int *workers, int *rows) {
     int w = 0;
-    const bool parts = with_workspace && ops.vec4;
-    int v = choose(m, SGEMM_PATH_AUTO, M, N, K, parts, ops.small, &w);
+    const bool parts = with_workspace && load16;
+    int v = choose(m, SGEMM_PATH_AUTO, M, N, K, parts, load16, &w);
     if (v < 0) return v;
     int sp = 1, r = 0;
     if (parts && w == 0) {
@@ -542,7 +541,7 @@ int plan(const Machine &m, int M, int N, int K, bool with_workspace, Operands op
             sp = select_splits(m, v, M, N, K);
         }
     }
-    if (w == 0 && sp == 1) r = split_rows(m, M, N, K, ops.small);
+    if (w == 0 && sp == 1) r = split_rows(m, M, N, K, load16);
     if (variant) *variant = v;
     if (splits) *splits = sp;
     if (workers) *workers = w;
@@ -568,18 +567,14 @@ int check_args(int M, int N, int K, float alpha, const float *A, int lda,
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
 
-// What the operands allow: vec4, launch's BUFFER_128 condition for a
-// variant that reads A 128 bits at a time (16-byte aligned A, B and C; N, K
-// and the leading dimensions multiples of 4); small, the 16-byte loads of
-// the small blocks at 4-byte alignment (BUFFER_128_AB); both with the
-// in-tile byte offsets of a 32 x 64 x 64 block below 2^31.
-Operands operands(int N, int K, const float *A, int lda, const float *B, int ldb, const float *C, int ldc) {
+// Whether the operands allow 16-byte loads of A and B (the BUFFER_128 or
+// BUFFER_128_AB builds): A, B and C 4-byte aligned, and the in-tile byte
+// offsets of a 32 x 64 x 64 block below 2^31 (a larger block's launch
+// checks its own with buffer_offsets_ok).
+bool loads16(const float *A, int lda, const float *B, int ldb, const float *C, int ldc) {
     const long long lim = 1LL << 31;
     const bool offsets = 33LL * lda * 4 < lim && 65LL * ldb * 4 + 64 * 4 < lim && 33LL * ldc * 4 < lim;
-    const bool vec4 = N % 4 == 0 && K % 4 == 0 && lda % 4 == 0 && ldb % 4 == 0 && ldc % 4 == 0 &&
-                      aligned16(A) && aligned16(B) && aligned16(C) && offsets;
-    const bool small = offsets && aligned4(A) && aligned4(B) && aligned4(C);
-    return {vec4, small};
+    return offsets && aligned4(A) && aligned4(B) && aligned4(C);
 }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -689,7 +684,11 @@ int launch(const Machine &m, int variant, int access, int splits, int workers, v
         const size_t need = workers > 0 ? streamk_bytes(v, workers) : splitk_bytes(v, splits, M, N);
         if (workspace == nullptr || workspace_bytes < need || ((uintptr_t)workspace & 255u) != 0)
             return SGEMM_ERR_WORKSPACE;
-        fn = fn == v.vec4 ? v.split4 : v.split1;
+        // (only the 16-byte load builds: 4 bytes per lane, a split launch
+        // is slower than whole tiles)
+        if (fn == v.vec4) fn = v.split4;
+        else if (fn == v.vec4u && v.split4u) fn = v.split4u;
+        else return SGEMM_ERR_ACCESS;
         a.splits = splits;
         a.partial = static_cast<float *>(workspace);
         if (workers > 0) {
@@ -721,8 +720,7 @@ int launch_rows(const Machine &m, int rows, int M, int N, int K, float alpha, co
     int rc = launch(m, kKcHuge16, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, rows, N, K, alpha, A, lda, B,
                     ldb, beta, C, ldc, stream);
     if (rc != SGEMM_OK) return rc;
-    const bool small = operands(N, K, A, lda, B, ldb, C, ldc).small;
-    const int v2 = select_variant(m, SGEMM_PATH_AUTO, M - rows, N, K, small);
+    const int v2 = select_variant(m, SGEMM_PATH_AUTO, M - rows, N, K, loads16(A, lda, B, ldb, C, ldc));
     if (v2 < 0) return v2;
     return launch(m, v2, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M - rows, N, K, alpha,
                   A + (size_t)rows * lda, lda, B, ldb, beta, C + (size_t)rows * ldc, ldc, stream);
@@ -744,7 +742,7 @@ int sgemm_path(int path, int M, int N, int K, float alpha, const float *A,
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     const Machine m = device_machine();
-    const bool small = operands(N, K, A, lda, B, ldb, C, ldc).small;
+    const bool small = loads16(A, lda, B, ldb, C, ldc);
     const int v = select_variant(m, path, M, N, K, small);
     if (v < 0) return v;
     if (path != SGEMM_PATH_VALU) {
@@ -802,21 +800,19 @@ size_t sgemm_streamk_workspace_size(int variant, int workers) {
 
 int sgemm_select_splits(int M, int N, int K) {
     int sp = 1;
-    const int rc = plan(device_machine(), M, N, K, true, kOperands128, nullptr, &sp, nullptr, nullptr);
+    const int rc = plan(device_machine(), M, N, K, true, true, nullptr, &sp, nullptr, nullptr);
     return rc < 0 ? rc : sp;
 }
 
 int sgemm_ws_plan(int M, int N, int K, int *variant, int *splits, int *workers) {
-    return plan(device_machine(), M, N, K, true, kOperands128, variant, splits, workers, nullptr);
+    return plan(device_machine(), M, N, K, true, true, variant, splits, workers, nullptr);
 }
 
-int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int operands_128,
+int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int operands_load16,
                    int *variant, int *splits, int *workers, int *rows) {
     if (compute_units < 1 || compute_units > (1 << 20)) return SGEMM_ERR_MACHINE;
     const Machine m = {compute_units, kMI355X.xcds};
-    // operands_128 == 0: rows only 4-byte aligned (the small blocks' 16-byte loads still apply)
-    const Operands ops = {operands_128 != 0, true};
-    return plan(m, M, N, K, with_workspace != 0, ops, variant, splits, workers, rows);
+    return plan(m, M, N, K, with_workspace != 0, operands_load16 != 0, variant, splits, workers, rows);
 }
 
 int sgemm_device_shape(int *compute_units, int *xcds) {
@@ -845,21 +841,21 @@ int sgemm_select_rows(int M, int N, int K) {
 
 int sgemm_select_streamk(int M, int N, int K) {
     int w = 0;
-    const int rc = plan(device_machine(), M, N, K, true, kOperands128, nullptr, nullptr, &w, nullptr);
+    const int rc = plan(device_machine(), M, N, K, true, true, nullptr, nullptr, &w, nullptr);
     return rc < 0 ? rc : w;
 }
 
 // Workspace bytes of the plan sgemm_ws makes with enough of it.
-size_t plan_bytes(const Machine &m, int M, int N, int K, Operands ops) {
+size_t plan_bytes(const Machine &m, int M, int N, int K) {
     int v = 0, sp = 1, w = 0;
-    if (plan(m, M, N, K, true, ops, &v, &sp, &w, nullptr) < 0) return 0;
+    if (plan(m, M, N, K, true, true, &v, &sp, &w, nullptr) < 0) return 0;
     if (w > 0) return streamk_bytes(kVariants[v], w);
     return sp > 1 ? splitk_bytes(kVariants[v], sp, M, N) : 0;
 }
 
 size_t sgemm_workspace_size(int M, int N, int K) {
-    // only 128-bit operands split K or run stream-K
-    return plan_bytes(device_machine(), M, N, K, kOperands128);
+    // the plan of operands that allow 16-byte loads (others never split)
+    return plan_bytes(device_machine(), M, N, K);
 }
 
 int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
@@ -868,9 +864,8 @@ int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const fl
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     const Machine m = device_machine();
-    const Operands ops = operands(N, K, A, lda, B, ldb, C, ldc);
     int v = 0, sp = 1, w = 0, rows = 0;
-    const int prc = plan(m, M, N, K, true, ops, &v, &sp, &w, &rows);
+    const int prc = plan(m, M, N, K, true, loads16(A, lda, B, ldb, C, ldc), &v, &sp, &w, &rows);
     if (prc != SGEMM_OK) return prc;
     const bool room = workspace != nullptr && ((uintptr_t)workspace & 255u) == 0;
     if (w > 0 || sp > 1) {
@@ -891,9 +886,8 @@ int sgemm_ws_noalloc(int M, int N, int K, float alpha, const float *A, int lda, 
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     const Machine m = device_machine();
-    const Operands ops = operands(N, K, A, lda, B, ldb, C, ldc);
     int v = 0, sp = 1, w = 0;
-    const int prc = plan(m, M, N, K, true, ops, &v, &sp, &w, nullptr);
+    const int prc = plan(m, M, N, K, true, loads16(A, lda, B, ldb, C, ldc), &v, &sp, &w, nullptr);
     if (prc != SGEMM_OK) return prc;
     // the bytes sgemm_ws would use with enough workspace (none when there is
     // no product to split)
@@ -960,11 +954,11 @@ int sgemm_select_variant(int path, int M, int N, int K) {
 
 int sgemm_select_variant_for(int path, int M, int N, int K, const float *A, int lda, const float *B, int ldb,
                              const float *C, int ldc) {
-    return select_variant(device_machine(), path, M, N, K, operands(N, K, A, lda, B, ldb, C, ldc).small);
+    return select_variant(device_machine(), path, M, N, K, loads16(A, lda, B, ldb, C, ldc));
 }
 
-int sgemm_operands_128(int N, int K, const float *A, int lda, const float *B, int ldb, const float *C, int ldc) {
-    return operands(N, K, A, lda, B, ldb, C, ldc).vec4 ? 1 : 0;
+int sgemm_operands_load16(const float *A, int lda, const float *B, int ldb, const float *C, int ldc) {
+    return loads16(A, lda, B, ldb, C, ldc) ? 1 : 0;
 }
 
 const char *sgemm_status_string(int status) {

@@ -1430,7 +1430,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     // the groups' partial tiles, each in the lanes' own order
     constexpr int RED = KG > 1 ? KG * BM * BN : 0;
     constexpr int SMEM = STG * STAGE > RED ? STG * STAGE : RED;
-    static_assert(!UA || (VEC == 4 && STG == 2 && !SPLIT), "rows at 4-byte alignment: 16-byte whole-tile builds");
+    static_assert(!UA || (VEC == 4 && STG == 2), "rows at 4-byte alignment: 16-byte loads, two stages");
     typedef DirectStage<BM, BN, BK, NT, VEC> D;
     // C in 32-bit accesses when the rows of C need not be 16-byte aligned
     typedef CStoreBuf<NI, UA ? 1 : VEC> TC;

@@ -96,8 +96,8 @@ def tune(shapes, variants=None, out=sys.stdout, accesses=("auto",)):
         flops = 2.0 * p.M * p.N * p.K
         # the library's plans for these very operands (their alignment matters)
         cus = g.sgemm_device_shape()[0]
-        o128 = g.sgemm_operands_128(p.N, p.K, a, p.lda, b, p.ldb, c, p.ldc)
-        _, auto, _, _, rows_first = g.sgemm_plan_for(cus, p.M, p.N, p.K, False, o128)
+        o16 = g.sgemm_operands_load16(a, p.lda, b, p.ldb, c, p.ldc)
+        _, auto, _, _, rows_first = g.sgemm_plan_for(cus, p.M, p.N, p.K, False, o16)
         rows = {}
         for v in variants:
             for acc in accesses:
@@ -115,14 +115,14 @@ def tune(shapes, variants=None, out=sys.stdout, accesses=("auto",)):
         ms, tf = _time(lambda: g.sgemm_ws(*args, workspace=ws, workspace_bytes=ws_bytes,
                                           stream=stream), flops, stream)
         rows["auto+ws"] = (ms, tf)
-        _, ws_variant, splits, workers, _ = g.sgemm_plan_for(cus, p.M, p.N, p.K, True, o128)
+        _, ws_variant, splits, workers, _ = g.sgemm_plan_for(cus, p.M, p.N, p.K, True, o16)
         for name, (ms, tf) in rows.items():
             print(f"{shape:24s} {name:34s} {tf:8.2f} TFLOP/s {ms:10.4f} ms", file=out, flush=True)
         forced = {k: v for k, v in rows.items() if k not in ("auto", "auto+ws")}
         best = min(forced, key=lambda k: forced[k][0])
         selected = g.sgemm_variant_name(auto)
         if rows_first > 0:  # C split by rows: two launches
-            rest = g.sgemm_plan_for(cus, p.M - rows_first, p.N, p.K, False, o128)[1]
+            rest = g.sgemm_plan_for(cus, p.M - rows_first, p.N, p.K, False, o16)[1]
             selected = (f"rows 0..{rows_first - 1} as 256 x 256 tiles, "
                         f"rest: {g.sgemm_variant_name(rest)}")
         table.append({"shape": shape, "M": p.M, "N": p.N, "K": p.K,

@@ -157,8 +157,8 @@ int sgemm_variant_access(int variant, int access, int M, int N, int K,
  * library allocates nothing. */
 
 /* C = alpha*A*B + beta*C like sgemm(), using split-K or stream-K (below)
- * when the auto choice calls for it, the operands allow 128-bit accesses
- * (sgemm_operands_128) and `workspace_bytes` holds sgemm_workspace_size(M,
+ * when the auto choice calls for it, the operands allow 16-byte loads
+ * (sgemm_operands_load16) and `workspace_bytes` holds sgemm_workspace_size(M,
  * N, K); otherwise exactly sgemm(). */
 int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda,
              const float *B, int ldb, float beta, float *C, int ldc,
@@ -187,19 +187,19 @@ int sgemm_ws_noalloc(int M, int N, int K, float alpha, const float *A, int lda,
                      hipStream_t stream);
 
 /* Workspace bytes sgemm_ws() can use for these sizes (0: it never splits).
- * Only operands that allow 128-bit accesses (sgemm_operands_128) split K or
- * run stream-K: for others sgemm_ws() is exactly sgemm() (their split builds
- * would load 4 bytes per lane, slower than the whole tiles). */
+ * Only operands that allow 16-byte loads of A and B (sgemm_operands_load16)
+ * split K or run stream-K: for others sgemm_ws() is exactly sgemm() (loading
+ * 4 bytes per lane, split launches were slower than whole tiles). */
 size_t sgemm_workspace_size(int M, int N, int K);
 
 /* The plan queries below (sgemm_select_splits, sgemm_select_streamk,
  * sgemm_ws_plan, sgemm_select_variant, sgemm_select_rows) answer for
- * operands that allow 128-bit accesses: A, B and C 16-byte aligned, N, K,
- * lda, ldb and ldc multiples of 4 and leading dimensions below about 2^24
- * (sgemm_operands_128).  Other operands split nothing, and those not 4-byte
- * aligned or whose tiles span more than 2^31 bytes take neither small block
- * (32 x 32, 32 x 64), so their plan may differ: sgemm_select_variant_for()
- * and sgemm_plan_for() answer for any operands. */
+ * operands that allow 16-byte loads of A and B: A, B and C 4-byte aligned
+ * and leading dimensions below about 2^24 (sgemm_operands_load16), however N,
+ * K and the leading dimensions fall against multiples of 4.  Other operands
+ * split nothing and
+ * take neither small block (32 x 32, 32 x 64), so their plan may differ:
+ * sgemm_select_variant_for() and sgemm_plan_for() answer for any operands. */
 
 /* The split count sgemm_ws() uses with enough workspace (1: no split), or a
  * negative argument code.  Host logic only. */
@@ -216,7 +216,9 @@ int sgemm_select_streamk(int M, int N, int K);
 int sgemm_ws_plan(int M, int N, int K, int *variant, int *splits, int *workers);
 
 /* One variant with a forced split count (1 = no split, same as
- * sgemm_variant()).  SGEMM_ERR_SPLITS for a variant without a split-K build. */
+ * sgemm_variant()).  SGEMM_ERR_SPLITS for a variant without a split-K build;
+ * SGEMM_ERR_ACCESS (split-K and stream-K alike) for operands that allow no
+ * 16-byte loads of A and B: the split builds load 16 bytes at a time only. */
 int sgemm_splitk(int variant, int splits, int M, int N, int K, float alpha,
                  const float *A, int lda, const float *B, int ldb, float beta,
                  float *C, int ldc, void *workspace, size_t workspace_bytes,
@@ -288,25 +290,24 @@ int sgemm_variant_tile(int variant, int *bm, int *bn);
 int sgemm_variant_reads_a128(int variant);
 
 /* The variant sgemm_path(path, M, N, K, ...) launches for these sizes with
- * operands that allow 128-bit accesses (above), or a negative code (-1..-3,
+ * operands that allow 16-byte loads (above), or a negative code (-1..-3,
  * SGEMM_ERR_PATH).  Host logic only, no HIP call.  When sgemm_select_rows()
  * is positive, an AUTO or MFMA call runs another plan (below). */
 int sgemm_select_variant(int path, int M, int N, int K);
 
 /* The same for these operands: the pointers and leading dimensions decide
- * whether 128-bit accesses are possible (the pointers are only inspected for
+ * whether 16-byte loads are possible (the pointers are only inspected for
  * alignment, never dereferenced; they may be NULL where sgemm() allows it).
  * Host logic only. */
 int sgemm_select_variant_for(int path, int M, int N, int K, const float *A, int lda,
                              const float *B, int ldb, const float *C, int ldc);
 
-/* 1 if these operands allow the 128-bit builds, split-K and stream-K (A, B
- * and C 16-byte aligned; N, K, lda, ldb and ldc multiples of 4; leading
+/* 1 if these operands allow 16-byte loads of A and B, which the small
+ * blocks, split-K and stream-K need (A, B and C 4-byte aligned; leading
  * dimensions below about 2^24, so that in-tile byte offsets fit 31 bits),
- * else 0: the operands_128 argument of sgemm_plan_for() that describes them.
- * The pointers are only inspected.  Host logic only. */
-int sgemm_operands_128(int N, int K, const float *A, int lda, const float *B, int ldb,
-                       const float *C, int ldc);
+ * else 0: the operands_load16 argument of sgemm_plan_for() that describes
+ * them.  The pointers are only inspected.  Host logic only. */
+int sgemm_operands_load16(const float *A, int lda, const float *B, int ldb, const float *C, int ldc);
 
 /* Rows of C that sgemm() (path AUTO or MFMA), and sgemm_ws() when it
  * neither splits K nor runs stream-K, compute as a first launch of 256 x 256
@@ -330,15 +331,14 @@ int sgemm_device_shape(int *compute_units, int *xcds);
 
 /* The plan the library makes for these sizes on a device of
  * `compute_units` compute units: with with_workspace != 0 what sgemm_ws()
- * runs with enough workspace, else what sgemm() runs; operands_128 != 0 for
- * operands that allow 128-bit accesses (above), 0 for other 4-byte aligned
- * ones whose in-tile offsets fit 31 bits.  Through
+ * runs with enough workspace, else what sgemm() runs; operands_load16 != 0
+ * for operands that allow 16-byte loads (above), 0 for others.  Through
  * the pointers (each may be NULL): the variant, the split count (1: none),
  * the stream-K worker count (0: none) and the rows of a first row-split
  * launch (0: one launch).  Returns 0, a negative argument code (-1..-3 for
  * M, N, K), or SGEMM_ERR_MACHINE for compute_units outside 1..2^20.  Host
  * logic only. */
-int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int operands_128,
+int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int operands_load16,
                    int *variant, int *splits, int *workers, int *rows);
 
 /* The workgroup -> tile order of the K-ordered blocks on a device of `xcds`

@@ -380,16 +380,23 @@ def test_splitk_host_logic():
     assert g.sgemm_select_splits(8192, 8192, 8192) == 1
     assert g.sgemm_workspace_size(8192, 8192, 8192) == 0
     # few tiles and a deep K split: 4 parts or more of the 64 x 64 block beat
-    # the small blocks; 2 or 3 do not (with 128-bit operands), but do on the
-    # 64 x 64 block that other operands run; shallow K does not split
+    # the small blocks; 2 or 3 do not; shallow K does not split
     assert g.sgemm_select_splits(512, 512, 8192) == 8
     assert g.sgemm_workspace_size(512, 512, 8192) > 0
     assert g.sgemm_select_splits(1024, 1024, 4096) == 1
     assert g.sgemm_workspace_size(1024, 1024, 4096) == 0
-    # operands without 128-bit access never split (the split builds' 4-byte
-    # loads into LDS are slower than whole tiles staged through registers)
-    assert g.sgemm_plan_for(256, 512, 512, 8192, True, operands_128=False)[2] == 1
-    assert g.sgemm_plan_for(256, 1536, 1536, 1536, True, operands_128=False)[3] == 0
+    # operands that allow no 16-byte loads never split (loading 4 bytes per
+    # lane into LDS, split launches are slower than whole tiles staged
+    # through registers); rows at 4-byte alignment split as 128-bit ones do
+    assert g.sgemm_plan_for(256, 512, 512, 8192, True, operands_load16=False)[2] == 1
+    assert g.sgemm_plan_for(256, 1536, 1536, 1536, True, operands_load16=False)[3] == 0
+    assert g.sgemm_plan_for(256, 1536, 1536, 1536, True)[3] == 256
+    v = g.sgemm_ws_plan(511, 511, 8191)[1]
+
+    def ws_plan_for(M, N, K, lda, ldb, ldc, A=0x10000, B=0x20000, C=0x30000):
+        return g.sgemm_plan_for(256, M, N, K, True, g.sgemm_operands_load16(A, lda, B, ldb, C, ldc))
+    assert ws_plan_for(511, 511, 8191, 8191, 511, 511)[1:3] == (v, g.sgemm_select_splits(511, 511, 8191))
+    assert ws_plan_for(511, 511, 8191, 8191, 511, 511, A=0x10002)[2] == 1
     assert g.sgemm_select_splits(1024, 1024, 1024) == 1
     assert g.sgemm_select_splits(256, 256, 256) == 1
     # fewer tiles than CUs: parts may be as short as 256 of K
@@ -500,10 +507,12 @@ def test_plan_quantises_over_other_cu_counts(cus):
             t2 = -(-M // bm2) * -(-N // bn2)
             assert t2 <= cus and t2 * sp2 <= 2 * cus
     # a 32-CU partition fills its CUs with 128 x 256 blocks at 1024^3, where
-    # 256 CUs need a small block (32 x 64, for either kind of operands)
+    # 256 CUs need a small block (32 x 64; 64 x 64 for operands that allow
+    # no 16-byte loads)
     assert _block(g.sgemm_plan_for(32, 1024, 1024, 1024)[1])[:2] == (128, 256)
     assert _block(g.sgemm_plan_for(256, 1024, 1024, 1024)[1])[:2] == (32, 64)
-    assert _block(g.sgemm_plan_for(256, 1024, 1024, 1024, operands_128=False)[1])[:2] == (32, 64)
+    assert _block(g.sgemm_plan_for(256, 1024, 1024, 1024, operands_load16=True)[1])[:2] == (32, 64)
+    assert _block(g.sgemm_plan_for(256, 1024, 1024, 1024, operands_load16=False)[1])[:2] == (64, 64)
     # split-K: 64 tiles of 64 x 64 at 512 x 512 x 8192 split in 8 on 256 CUs;
     # on 80 CUs a split would be in 2, so 128-bit operands take the 32 x 64
     # block whole instead, and other operands the split
@@ -554,15 +563,20 @@ def test_narrow_n_weighs_the_tiles_area_inside_c():
     assert g.sgemm_select_rows(7168, 7168, 7168) == 6912
 
 
-def test_operands_128_condition():
-    """128-bit operands: A, B and C 16-byte aligned and N, K, lda, ldb, ldc
-    multiples of 4 (the pointers are only inspected)."""
-    ok = (1024, 1024, 0x1000, 1024, 0x2000, 1024, 0x3000, 1024)
-    assert g.sgemm_operands_128(*ok)
-    for i, bad in [(0, 1022), (1, 1021), (2, 0x1004), (3, 1025), (4, 0x2008), (5, 1026), (6, 0x300c), (7, 1027)]:
+def test_operands_load16_condition():
+    """Operands that allow 16-byte loads of A and B: A, B and C 4-byte
+    aligned and in-tile byte offsets of the small blocks below 2^31, whatever
+    the leading dimensions are modulo 4 (the pointers are only inspected)."""
+    ok = (0x1000, 1024, 0x2000, 1024, 0x3000, 1024)
+    assert g.sgemm_operands_load16(*ok)
+    for i, fine in [(0, 0x1004), (1, 1021), (2, 0x2008), (3, 1026), (4, 0x300c), (5, 1027)]:
+        args = list(ok)
+        args[i] = fine
+        assert g.sgemm_operands_load16(*args), (i, fine)
+    for i, bad in [(0, 0x1002), (1, 1 << 24), (2, 0x2001), (3, 1 << 24), (4, 0x3003), (5, 1 << 24)]:
         args = list(ok)
         args[i] = bad
-        assert not g.sgemm_operands_128(*args), (i, bad)
+        assert not g.sgemm_operands_load16(*args), (i, bad)
 
 
 def test_small_blocks_need_31_bit_offsets():
@@ -570,7 +584,7 @@ def test_small_blocks_need_31_bit_offsets():
     builds: leading dimensions too large for 31-bit in-tile offsets keep the
     choice off them, and forcing them is refused before any HIP call."""
     big = 1 << 26   # floats: 33 rows of A span more than 2^31 bytes
-    assert not g.sgemm_operands_128(512, 512, 0x1000, big, 0x2000, 512, 0x3000, 512)
+    assert not g.sgemm_operands_load16(0x1000, big, 0x2000, 512, 0x3000, 512)
     v = g.sgemm_select_variant_for(g.SGEMM_PATH_AUTO, 512, 512, 512, 0x1000, big, 0x2000, 512, 0x3000, 512)
     assert _block(v) == (64, 64, 64)
     tiny = [i for i in range(g.sgemm_variant_count()) if (g.sgemm_variant_name(i) or "").startswith("mfma_32x")]

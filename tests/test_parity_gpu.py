@@ -345,7 +345,7 @@ def test_sgemm_ws_plan_beyond_31_bit_offsets_runs_whole_tiles():
     oa, _, a = gu.to_gpu(p.A)
     ob, _, b = gu.to_gpu(p.B)
     oc, first, c = gu.to_gpu(p.C)
-    assert g.sgemm_operands_128(N, K, a, lda, b, N, c, N)
+    assert g.sgemm_operands_load16(a, lda, b, N, c, N)
     gu.say("sgemm_ws huge lda", lda)
     rc = g.sgemm_ws(M, N, K, p.alpha, a, lda, b, N, p.beta, c, N, workspace=ws, check=False)
     torch.cuda.synchronize()
@@ -399,7 +399,9 @@ def random_configs(n, seed):
         beta = float(rng.choice([0.0, 1.0, -0.75, 0.5]))
         pads = [int(x) for x in rng.integers(0, 6, 3)]
         offs = tuple(int(x) for x in rng.integers(0, 4, 3))
-        if i % 4 == 3:  # operands that allow 128-bit accesses, which split-K needs
+        if i % 8 == 3:  # operands that allow 128-bit accesses; the rest of the
+            # long-K configurations keep odd sizes and offsets (16-byte loads at
+            # 4-byte alignment)
             N, K = -(-N // 4) * 4, -(-K // 4) * 4
             pads = [4 * (x % 2) for x in pads]
             offs = (0, 0, 0)
@@ -411,8 +413,8 @@ def random_configs(n, seed):
 def test_random_configs_every_entry_point(cfg):
     """Seeded random sizes, leading-dimension padding, base misalignment and
     alpha/beta, through sgemm, sgemm_ws (which may split K: every fourth
-    configuration has few tiles, long K and 128-bit operands) and the VALU
-    path."""
+    configuration has few tiles and long K, half of them with 128-bit
+    operands) and the VALU path."""
     i, M, N, K, alpha, beta, pads, offs = cfg
     p = inputs.make_problem(M, N, K, dist="upm1", seed=100 + i, alpha=alpha, beta=beta,
                             c_fill="upm1", lda=K + pads[0], ldb=N + pads[1], ldc=N + pads[2])
@@ -429,7 +431,7 @@ def test_random_configs_every_entry_point(cfg):
     ob, _, b = gu.to_gpu(p.B, offs[1])
     oc, first, c = gu.to_gpu(p.C, offs[2])
     if i % 4 == 3:
-        assert g.sgemm_operands_128(N, K, a, p.lda, b, p.ldb, c, p.ldc)
+        assert g.sgemm_operands_load16(a, p.lda, b, p.ldb, c, p.ldc)
         assert g.sgemm_select_splits(M, N, K) > 1, (M, N, K)
     g.sgemm_ws(M, N, K, alpha, a, p.lda, b, p.ldb, beta, c, p.ldc, workspace=ws)
     torch.cuda.synchronize()
