@@ -306,6 +306,9 @@ def test_streamk_host_logic():
     assert call(v, 3, ws=0) == -24                      # missing workspace
     assert call(v, 3, nbytes=16) == -24                 # too small
     assert call(v, 3, ws=0x10010) == -24                # not 256-byte aligned
+    # operands without 16-byte loads (A not 4-byte aligned): no split build
+    assert g.sgemm_streamk(v, 3, 300, 260, 1030, 1.0, 0x1002, 1032, 0x2000, 260, 0.0, 0x3000, 260,
+                           workspace=0x10000, workspace_bytes=1 << 30, stream=0, check=False) == -23
 
 
 def test_row_split_host_logic():
@@ -420,6 +423,9 @@ def test_splitk_argument_codes():
     assert call(split_v, 2, ws=0) == -24               # missing workspace
     assert call(split_v, 2, nbytes=16) == -24          # too small
     assert call(split_v, 2, ws=0x10010) == -24         # not 256-byte aligned
+    # operands without 16-byte loads (B not 4-byte aligned): no split build
+    assert g.sgemm_splitk(split_v, 2, 64, 64, 64, 1.0, 0x1000, 64, 0x2002, 64, 0.0, 0x3000, 64,
+                          workspace=0x10000, workspace_bytes=1 << 30, stream=0, check=False) == -23
     assert "workspace" in g.sgemm_status_string(-24)
     assert "split" in g.sgemm_status_string(-25)
 
