@@ -185,8 +185,11 @@ def test_edge_sweep(variant):
 @pytest.mark.parametrize("offsets", [(0, 0, 0), (1, 0, 0), (0, 1, 0), (0, 0, 1), (3, 1, 2)])
 def test_wide_leading_dims_and_misaligned_bases(variant, offsets):
     # pad columns of A, B, C hold NaN; they must never be read or written
+    # (K % 4 != 0 with lda > K: a 16-byte chunk of A that holds column K - 1
+    # brings NaN pad columns along, which must not reach C)
     for (M, N, K, lda, ldb, ldc) in [(130, 196, 72, 75, 200, 204), (97, 64, 40, 41, 67, 66),
-                                     (64, 128, 64, 68, 132, 128)]:
+                                     (64, 128, 64, 68, 132, 128), (70, 50, 41, 43, 53, 52),
+                                     (33, 97, 6, 7, 99, 100)]:
         p = inputs.make_problem(M, N, K, dist="upm1", seed=M + N, alpha=1.25, beta=-0.75,
                                 c_fill="upm1", lda=lda, ldb=ldb, ldc=ldc)
         gu.say("wide-ld", M, N, K, lda, ldb, ldc, offsets, g.sgemm_variant_name(variant))
@@ -466,10 +469,12 @@ def run_split(p, variant, splits, ws=None):
 @pytest.mark.parametrize("variant", split_variants())
 @pytest.mark.parametrize("splits", [2, 3, 4, 7])
 def test_splitk_matches_oracle(variant, splits):
-    for (M, N, K, alpha, beta) in [(200, 301, 777, 1.5, -0.5), (256, 256, 256, 1.0, 0.0),
-                                   (65, 130, 1030, -1.0, 1.0), (64, 64, 40, 2.0, 0.5)]:
+    # the last: K % 4 != 0 and NaN in A's pad columns (lda = K + 2)
+    for (M, N, K, alpha, beta, lda) in [(200, 301, 777, 1.5, -0.5, None), (256, 256, 256, 1.0, 0.0, None),
+                                        (65, 130, 1030, -1.0, 1.0, None), (64, 64, 40, 2.0, 0.5, None),
+                                        (70, 50, 701, 1.0, 1.0, 703)]:
         p = inputs.make_problem(M, N, K, dist="upm1", seed=M + K, alpha=alpha, beta=beta,
-                                c_fill="upm1" if beta != 0 else None)
+                                c_fill="upm1" if beta != 0 else None, lda=lda)
         gu.say("split-K", M, N, K, splits, g.sgemm_variant_name(variant))
         out, ws = run_split(p, variant, splits)
         assert gu.ratio_full(p, out) <= TOL, (M, N, K, splits)
@@ -522,16 +527,17 @@ def run_streamk(p, variant, workers, ws=None):
 # (from 2 tiles of 256 x 256 to 20 of 64 x 64, so the shared tiles range from
 # all of them to a few), with K from 2 K tiles (most workers hold nothing) to
 # 65 (each shared tile spread over several workers).
-STREAMK_SHAPES = [(200, 301, 777, 1.5, -0.5), (300, 260, 1030, -1.0, 1.0), (520, 130, 96, 2.0, 0.5),
-                  (64, 64, 40, 1.0, 0.0)]
+STREAMK_SHAPES = [(200, 301, 777, 1.5, -0.5, None), (300, 260, 1030, -1.0, 1.0, None),
+                  (520, 130, 96, 2.0, 0.5, None), (64, 64, 40, 1.0, 0.0, None),
+                  (150, 70, 301, 1.0, 1.0, 302)]  # the last: NaN in A's pad column, K % 4 != 0
 
 
 @pytest.mark.parametrize("variant", streamk_variants())
 @pytest.mark.parametrize("workers", [3, 5, 16, 256])
 def test_streamk_matches_oracle(variant, workers):
-    for (M, N, K, alpha, beta) in STREAMK_SHAPES:
+    for (M, N, K, alpha, beta, lda) in STREAMK_SHAPES:
         p = inputs.make_problem(M, N, K, dist="upm1", seed=M + K + 1, alpha=alpha, beta=beta,
-                                c_fill="upm1" if beta != 0 else None)
+                                c_fill="upm1" if beta != 0 else None, lda=lda)
         gu.say("stream-K", M, N, K, workers, g.sgemm_variant_name(variant))
         out, _ = run_streamk(p, variant, workers)
         assert gu.ratio_full(p, out) <= TOL, (M, N, K, workers)
