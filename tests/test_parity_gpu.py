@@ -304,6 +304,32 @@ def test_full_size_sampled_auto_path(name):
     assert r <= TOL, (name, r)
 
 
+@pytest.mark.parametrize("shape", [(8191, 8191, 8191, 1.0, 0.0), (4097, 4095, 4093, 1.5, -0.5)])
+def test_full_size_sampled_odd_sizes(shape):
+    """Large shapes whose rows are only 4-byte aligned (the builds loading A
+    and B 16 bytes at a time at 4-byte alignment) through sgemm() and
+    sgemm_ws(), sampled as the full workloads are."""
+    M, N, K, alpha, beta = shape
+    p = inputs.make_problem(M, N, K, dist="normal", seed=29, alpha=alpha, beta=beta,
+                            c_fill="upm1" if beta != 0 else None)
+    gu.say("full size odd", shape, g.sgemm_variant_name(g.sgemm_select_variant(0, M, N, K)))
+    out = gu.run(p)
+    r, rows, cols = gu.ratio_lines(p, out, seed=31)
+    assert rows[-1] == M - 1 and cols[-1] == N - 1
+    assert r <= TOL, (shape, r)
+    need = g.sgemm_workspace_size(M, N, K)
+    ws = torch.full((max(need, 256) // 4 + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    oa, _, a = gu.to_gpu(p.A)
+    ob, _, b = gu.to_gpu(p.B)
+    oc, first, c = gu.to_gpu(p.C)
+    g.sgemm_ws(M, N, K, alpha, a, p.lda, b, p.ldb, beta, c, p.ldc, workspace=ws)
+    torch.cuda.synchronize()
+    out2 = oc.cpu().numpy()[first:first + p.C.numel()].reshape(p.C.shape)
+    r2, _, _ = gu.ratio_lines(p, out2, seed=31)
+    assert r2 <= TOL, (shape, "sgemm_ws", r2)
+    del oa, ob, oc, ws
+
+
 @pytest.mark.parametrize("name", ["square4096_upm1", "square8192_normal"])
 def test_full_size_sampled_valu_path(name):
     p = inputs.workload_problem(name)
@@ -328,7 +354,7 @@ def test_huge_leading_dimension_takes_checked_accesses():
     oa, _, a = gu.to_gpu(p.A)
     ob, _, b = gu.to_gpu(p.B)
     oc, _, c = gu.to_gpu(p.C)
-    for acc in (g.SGEMM_ACCESS_BUFFER_128, g.SGEMM_ACCESS_BUFFER_32):
+    for acc in (g.SGEMM_ACCESS_BUFFER_128, g.SGEMM_ACCESS_BUFFER_32, g.SGEMM_ACCESS_BUFFER_128_AB):
         assert g.sgemm_variant_access(v, acc, M, N, K, 0.75, a, lda, b, N, 0.5, c, N,
                                       check=False) == -23
     torch.cuda.synchronize()

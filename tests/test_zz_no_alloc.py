@@ -45,12 +45,15 @@ def _run(p, noalloc):
 
 # (M, N, K, alpha, beta): stream-K over 256 workers on 64 x 64 tiles (8 MiB of
 # scratch), then split-K in 16 (4 MiB); split-K in 8 (8 MiB), then a shape
-# that needs none
+# that needs none; odd sizes (rows only 4-byte aligned): split-K in 8, then
+# in 15
 PAIRS = [((1536, 1536, 1536, 1.25, -0.5), (256, 256, 4096, 0.75, 0.5)),
-         ((512, 512, 8192, 1.0, 0.0), (200, 130, 333, -1.5, 1.0))]
+         ((512, 512, 8192, 1.0, 0.0), (200, 130, 333, -1.5, 1.0)),
+         ((511, 511, 8191, 1.0, 0.5), (255, 255, 4095, -0.75, 0.0))]
 
 
-@pytest.mark.parametrize("pair", PAIRS, ids=["streamk-then-splitk", "splitk-then-none"])
+@pytest.mark.parametrize("pair", PAIRS, ids=["streamk-then-splitk", "splitk-then-none",
+                                             "odd-splitk-twice"])
 def test_noalloc_matches_sgemm_ws_on_two_calls(pair):
     for idx, (M, N, K, alpha, beta) in enumerate(pair):
         p = inputs.make_problem(M, N, K, dist="upm1", seed=61 + idx, alpha=alpha, beta=beta,
