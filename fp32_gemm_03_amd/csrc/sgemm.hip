@@ -401,7 +401,8 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool s
     }
     if (best < 0) {
         // No block fills the chip (measured over cubes 256-1920 and
-        // rectangles; TFLOP/s).  With 128-bit operands:
+        // rectangles; TFLOP/s).  With operands that allow 16-byte loads
+        // (128-bit ones here; rows at 4-byte alignment run within 1-5%):
         //   * at most three 32 x 32 tiles per CU: the 32 x 32 block in four
         //     wave groups (256^3 6.6 against 4.5 on 64 x 64, 512^3 47 against
         //     22, 768^3 69 against 54, 512 x 512 x 8192 62 against 29);
@@ -415,7 +416,8 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool s
         //     127 against 120), unless stream-K on 64 x 64 x 32 shares long K
         //     ranges (1280^2 x 4096: 110 against 102).
         // Other operands take the 64 x 64 x 64 block up to two tiles per CU
-        // as well (1151^3 69 against 67, 2047 x 1023 x 1023 106 against 100).
+        // as well (32-bit builds: 1151^3 69 against 67, 2047 x 1023 x 1023
+        // 106 against 100).
         // Otherwise the 64 x 64 x 32 block at four per CU; with more tiles than CUs but
         // not a whole number per CU, stream-K over one worker per CU evens
         // out the K tiles each CU runs (1536^3: 110 against 96).  With at
