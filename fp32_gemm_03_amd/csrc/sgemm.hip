@@ -69,16 +69,18 @@ struct Variant {
 // the same order as each other, the 16-byte load builds in another.  RO is
 // the order of the LDS fragment reads at a K tile's start (mfma_tile_kc),
 // chosen per block by measurement.  Every build maps workgroups to tiles
-// with tile_of<2, 8> (each XCD on its own tile columns).
+// with tile_of<2, 8> (each XCD on its own tile columns), and holds each K
+// tile's last k-step of MFMAs over past the barrier (DF: 0.2-7% faster,
+// level nowhere it was measured, 9% on 256 x 256 x 4096 in 16 parts).
 #define MFMA_CFG_KCD(BM, BN, BK, WM, WN, WPE, PA, SWZ, RO, SUFFIX)                      \
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
      (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO>,                          \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, false, true>,    \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 2, 0, SWZ, true>,       \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, 2, 0, SWZ, true>,      \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO>, 1, 1, 0,                  \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, true>,           \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO, 0, 1, 2, true>}
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO, 0, 1, 2, false, true>, 1, 1, 0, \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, true, true>,     \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO, 0, 1, 2, true, true>}
 
 // A small K-ordered block of 32 x 32 waves split over KG wave groups; all
 // four builds are sgemm_mfma_kc (128-bit, 4-byte loads into LDS twice, and
@@ -87,10 +89,10 @@ struct Variant {
 #define MFMA_CFG_KG(BM, BN, BK, KG, SUFFIX)                                                   \
     {"mfma_" #BM "x" #BN "x" #BK "_w32x32" SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,                 \
      KG * (BM / 32) * (BN / 32) * 64,                                                         \
-     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2>,                        \
-     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2>,                        \
-     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2>, nullptr, 1, 0, 1,          \
-     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2, true>}
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2, false, true>,           \
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2, false, true>,           \
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2, false, true>, nullptr, 1, 0, 1, \
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2, true, true>}
 
 // The table holds the blocks the choice by shape can pick (the VALU pair and
 // the K-ordered blocks) and the alternatives kept for measurement: the
@@ -119,17 +121,19 @@ const Variant kVariants[] = {
     // builds are the register-staged 64 x 64 x 64 block, its split-K and
     // stream-K builds the K-ordered one with four 32 x 32 waves.
     {"mfma_64x64x64_w64x32_kg2_kcd", SGEMM_PATH_MFMA, 64, 64, 64, 256,
-     sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2>,
+     sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2, false, true>,
      sgk::sgemm_mfma<64, 64, 64, 32, 32, 4, 0, 1, 2, true, 1, 2, 0, false, true>,
      sgk::sgemm_mfma<64, 64, 64, 32, 32, 4, 0, 1, 2, false, 1, 2, 0, false, true>,
-     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1>, 1, 1, 0,
-     sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2, true>,
-     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1, 0, 1, 2, true>},
+     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1, 0, 1, 2, false, true>, 1, 1, 0,
+     sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2, true, true>,
+     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1, 0, 1, 2, true, true>},
     MFMA_CFG_KCD(128, 128, 32, 64, 32, 4, 4, false, 2, "_w8_kcd"),  // 14: 8 waves, 2 workgroups per CU
     // 15: 7 with 16 waves of 64 x 64, four per SIMD, whole tiles only: its
     // split builds would spill (55-96 registers at the 128-register cap), so
     // split-K and stream-K stay with 7.  Wave priority falls over each K tile
-    // (PR 1).
+    // (PR 1).  Holding the last k-step over the barrier (DF) measured level
+    // here (148.2 against 148.1 TFLOP/s at 8192^3): four waves per SIMD
+    // already keep the matrix unit busy across it, so it is not built in.
     {"mfma_256x256x32_w64x64_w16_kcd", SGEMM_PATH_MFMA, 256, 256, 32, 1024,
      sgk::sgemm_mfma_kc<256, 256, 32, 64, 64, 4, 4, false, 2, 1>,
      sgk::sgemm_mfma<256, 256, 32, 64, 64, 4, 0, 1, 4, true, 1, 2, 0, false, true>,

@@ -1239,9 +1239,37 @@ struct DirectStage {
 // k0 + lh * KX / 2, column wn + NI * li.  hook(j, u) as in mfma_tile.
 // KX is the k extent the wave covers in this call (all of the tile, BK, or
 // its wave group's share of it); A rows stay BK floats long.
-template <int BK, int MI, int NI, int SB, int FD, int CH, int RO, int PR, int KX, class Hook>
+// The operands of one k-step's MFMAs held over to the next K tile (DF).
+template <int MI, int NI> struct KcPending {
+    float x[MI];
+    typename vec_t<NI>::type b;
+};
+
+// The MFMAs of a held-over k-step: into acc_odd when that k-step is odd and
+// the odd k-steps have their own accumulators (CH == 2).
+template <int MI, int NI, int CH, bool ODD>
+__device__ __forceinline__ void mfma_pending_kc(const KcPending<MI, NI> &pd, floatx16 (&acc)[MI][NI],
+                                                floatx16 (&acc_odd)[MI][NI]) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < NI; ++jj) {
+            if (CH == 2 && ODD)
+                acc_odd[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(pd.x[i], vget(pd.b, jj), acc_odd[i][jj], 0, 0, 0);
+            else
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(pd.x[i], vget(pd.b, jj), acc[i][jj], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+}
+
+// DF: the last k-step's MFMAs are not issued here but held in pd, and the
+// caller issues them after the barrier that ends the tile (pd_in: this call
+// issues the previous tile's, right after its own first fragment reads), so
+// the matrix unit has work while those reads are in flight.
+template <int BK, int MI, int NI, int SB, int FD, int CH, int RO, int PR, int KX, bool DF, class Hook>
 __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_off)[KX / 8], const float *bp,
-                                             floatx16 (&acc)[MI][NI], floatx16 (&acc_odd)[MI][NI], Hook hook) {
+                                             floatx16 (&acc)[MI][NI], floatx16 (&acc_odd)[MI][NI], Hook hook,
+                                             KcPending<MI, NI> &pd, bool pd_in) {
     typedef typename vec_t<NI>::type VB;
     static_assert(KX % 8 == 0 && KX <= BK, "k extent: whole chunks of 4 per lane half");
     constexpr int STEPS = KX / 2, QN = KX / 8;
@@ -1290,6 +1318,10 @@ __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_o
     __builtin_amdgcn_sched_barrier(0);
     av[0][0] = *reinterpret_cast<const float4 *>(a_row + a_off[0]);
     }
+    if (DF && pd_in) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_pending_kc<MI, NI, CH, ((STEPS - 1) & 1) != 0>(pd, acc, acc_odd);
+    }
     // RO == 2: the rest of the first group of A and the next B fragment
     // right after the first MFMA
     auto rest_of_first = [&]() {
@@ -1323,6 +1355,17 @@ __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_o
                     av[(q + 1) & 1][i] = *reinterpret_cast<const float4 *>(a_row + i * 32 * BK + a_off[q + 1]);
             }
             __builtin_amdgcn_sched_barrier(0);
+            if (DF && j == STEPS - 1) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i) {
+                    const float4 &ac = av[q & 1][i];
+                    pd.x[i] = e == 0 ? ac.x : e == 1 ? ac.y : e == 2 ? ac.z : ac.w;
+                }
+                pd.b = bv[j % RING];
+#pragma unroll
+                for (int u = 0; u < MI * NI; ++u) hook(j, u);
+                continue;
+            }
 #pragma unroll
             for (int i = 0; i < MI; ++i) {
                 const float4 &ac = av[q & 1][i];
@@ -1411,7 +1454,7 @@ __device__ __forceinline__ void ring_barrier() {
 // every wave of the workgroup.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WM, int WN, int VEC, int WPE, bool SPLIT, int RO, int PR = 0,
-          int KG = 1, int STG = 2, bool UA = false>
+          int KG = 1, int STG = 2, bool UA = false, bool DF = false>
 __global__ void __launch_bounds__(KG * (BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -1509,7 +1552,9 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
         // The stages as restrict pointers: the scoped no-alias information
         // lets the compiler see that the reads of the current stage need not
         // wait for the loads into another one (the waits are explicit).
-        auto tile_body = [&](const float *__restrict__ st, float *__restrict__ nx, int kn, bool issue) {
+        KcPending<MI, NI> pd;
+        auto tile_body = [&](const float *__restrict__ st, float *__restrict__ nx, int kn, bool issue,
+                             bool pd_in) {
             const rsrc_t rb = d.b_rows(a, bn, kn);
             auto hook = [&](int j, int u) {
                 if (j < LSTEPS && issue) {
@@ -1522,14 +1567,15 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
                     }
                 }
             };
-            mfma_tile_kc<BK, MI, NI, SB, 1, CH, RO, PR, KX>(st + a_row, a_off, st + b_off, acc, acc_odd, hook);
+            mfma_tile_kc<BK, MI, NI, SB, 1, CH, RO, PR, KX, DF>(st + a_row, a_off, st + b_off, acc, acc_odd,
+                                                                hook, pd, pd_in);
         };
         if constexpr (STG == 2) {
             // the next tile is always loaded (past the last one it reads
             // zeros or the next range's data into a stage nobody reads)
             for (int t = 0; t < KT; ++t) {
                 if (!SPLIT) ph.tile_begin();
-                tile_body(smem + (t & 1) * STAGE, smem + ((t + 1) & 1) * STAGE, kb + (t + 1) * BK, true);
+                tile_body(smem + (t & 1) * STAGE, smem + ((t + 1) & 1) * STAGE, kb + (t + 1) * BK, true, t > 0);
                 if (!SPLIT) ph.tile_mid();
                 __builtin_amdgcn_s_waitcnt(0);
                 if constexpr (UA) {
@@ -1544,7 +1590,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
             for (int t = 0; t < KT; ++t) {
                 const bool issue = t + STG - 1 < KT;
                 if (!SPLIT) ph.tile_begin();
-                tile_body(smem + cur * STAGE, smem + nxt * STAGE, kb + (t + STG - 1) * BK, issue);
+                tile_body(smem + cur * STAGE, smem + nxt * STAGE, kb + (t + STG - 1) * BK, issue, t > 0);
                 if (!SPLIT) ph.tile_mid();
                 // tile t + 1 has landed; tiles t + 2 .. t + STG - 1 may still be in flight
                 if (issue)
@@ -1556,6 +1602,8 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
                 nxt = nxt + 1 == STG ? 0 : nxt + 1;
             }
         }
+        // the last tile's held-over k-step
+        if (DF && KT > 0) mfma_pending_kc<MI, NI, CH, ((KX / 2 - 1) & 1) != 0>(pd, acc, acc_odd);
         if (CH == 2) {
 #pragma unroll
             for (int i = 0; i < MI; ++i)
