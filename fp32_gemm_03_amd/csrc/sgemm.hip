@@ -70,17 +70,20 @@ struct Variant {
 // the order of the LDS fragment reads at a K tile's start (mfma_tile_kc),
 // chosen per block by measurement.  Every build maps workgroups to tiles
 // with tile_of<2, 8> (each XCD on its own tile columns), and holds each K
-// tile's last k-step of MFMAs over past the barrier (DF: 0.2-7% faster,
-// level nowhere it was measured, 9% on 256 x 256 x 4096 in 16 parts).
-#define MFMA_CFG_KCD(BM, BN, BK, WM, WN, WPE, PA, SWZ, RO, SUFFIX)                      \
+// tile's last k-step of MFMAs over the barrier (DF: 0.2-7% faster on most
+// blocks and shapes, 9% on 256 x 256 x 4096 in 16 parts, at most 1.5%
+// slower on a few).  The split builds of the 64 x 64 blocks hold the last
+// two k-steps (SD 2: another 2-4% on their split-K and stream-K shapes; level
+// on the larger blocks' split builds, mixed on whole tiles).
+#define MFMA_CFG_KCD(BM, BN, BK, WM, WN, WPE, PA, SWZ, RO, SD, SUFFIX)                  \
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
      (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, false, true>,    \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, false, 1>,    \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 2, 0, SWZ, true>,       \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, 2, 0, SWZ, true>,      \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO, 0, 1, 2, false, true>, 1, 1, 0, \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, true, true>,     \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO, 0, 1, 2, true, true>}
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO, 0, 1, 2, false, SD>, 1, 1, 0, \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, true, 1>,     \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO, 0, 1, 2, true, SD>}
 
 // A small K-ordered block of 32 x 32 waves split over KG wave groups; all
 // four builds are sgemm_mfma_kc (128-bit, 4-byte loads into LDS twice, and
@@ -89,10 +92,10 @@ struct Variant {
 #define MFMA_CFG_KG(BM, BN, BK, KG, SUFFIX)                                                   \
     {"mfma_" #BM "x" #BN "x" #BK "_w32x32" SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,                 \
      KG * (BM / 32) * (BN / 32) * 64,                                                         \
-     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2, false, true>,           \
-     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2, false, true>,           \
-     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2, false, true>, nullptr, 1, 0, 1, \
-     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2, true, true>}
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2, false, 1>,           \
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2, false, 1>,           \
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 1, 4, false, 1, 0, KG, 2, false, 1>, nullptr, 1, 0, 1, \
+     sgk::sgemm_mfma_kc<BM, BN, BK, 32, 32, 4, 4, false, 1, 0, KG, 2, true, 1>}
 
 // The table holds the blocks the choice by shape can pick (the VALU pair and
 // the K-ordered blocks) and the alternatives kept for measurement: the
@@ -107,12 +110,12 @@ const Variant kVariants[] = {
     MFMA_CFG(128, 256, 16, 64, 128, 4, 2, 0, 1, false, "_ldsepi"), // 4: LDS-staged epilogue
     MFMA_CFG(256, 128, 16, 128, 64, 4, 2, 0, 1, false, "_ldsepi"), // 5: LDS-staged epilogue
     MFMA_CFG(128, 256, 16, 64, 128, 0, 2, 0, 0, true, "_xorA"),    // 6: A unpadded, XOR-swizzled
-    MFMA_CFG_KCD(256, 256, 32, 128, 64, 2, 4, false, 2, "_kcd"),    // 7: 8 waves, 2 per SIMD
-    MFMA_CFG_KCD(128, 128, 16, 64, 64, 4, 4, false, 0, "_wpe4_kcd"),  // 8: 4 workgroups per CU
-    MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, 0, true, 0, "_kcd"),     // 9: 2 workgroups per CU
-    MFMA_CFG_KCD(128, 256, 32, 64, 64, 2, 4, false, 2, "_w8_kcd"),  // 10: 8 waves, 2 per SIMD
-    MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, 1, "_kcd"),       // 11: 4 workgroups per CU
-    MFMA_CFG_KCD(128, 128, 64, 32, 64, 2, 4, false, 2, "_w8_kcd"),  // 12: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(256, 256, 32, 128, 64, 2, 4, false, 2, 1, "_kcd"),    // 7: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(128, 128, 16, 64, 64, 4, 4, false, 0, 1, "_wpe4_kcd"),  // 8: 4 workgroups per CU
+    MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, 0, true, 0, 1, "_kcd"),     // 9: 2 workgroups per CU
+    MFMA_CFG_KCD(128, 256, 32, 64, 64, 2, 4, false, 2, 1, "_w8_kcd"),  // 10: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, 1, 2, "_kcd"),       // 11: 4 workgroups per CU
+    MFMA_CFG_KCD(128, 128, 64, 32, 64, 2, 4, false, 2, 1, "_w8_kcd"),  // 12: 8 waves, 2 per SIMD
     // 13: the block for at most one tile per CU.  Its 128-bit build (and
     // the one for rows at 4-byte alignment) is two
     // wave groups (KG 2) of two 64 x 32 waves, each group half of every K
@@ -121,13 +124,13 @@ const Variant kVariants[] = {
     // builds are the register-staged 64 x 64 x 64 block, its split-K and
     // stream-K builds the K-ordered one with four 32 x 32 waves.
     {"mfma_64x64x64_w64x32_kg2_kcd", SGEMM_PATH_MFMA, 64, 64, 64, 256,
-     sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2, false, true>,
+     sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2, false, 1>,
      sgk::sgemm_mfma<64, 64, 64, 32, 32, 4, 0, 1, 2, true, 1, 2, 0, false, true>,
      sgk::sgemm_mfma<64, 64, 64, 32, 32, 4, 0, 1, 2, false, 1, 2, 0, false, true>,
-     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1, 0, 1, 2, false, true>, 1, 1, 0,
-     sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2, true, true>,
-     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1, 0, 1, 2, true, true>},
-    MFMA_CFG_KCD(128, 128, 32, 64, 32, 4, 4, false, 2, "_w8_kcd"),  // 14: 8 waves, 2 workgroups per CU
+     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1, 0, 1, 2, false, 2>, 1, 1, 0,
+     sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2, true, 1>,
+     sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1, 0, 1, 2, true, 2>},
+    MFMA_CFG_KCD(128, 128, 32, 64, 32, 4, 4, false, 2, 1, "_w8_kcd"),  // 14: 8 waves, 2 workgroups per CU
     // 15: 7 with 16 waves of 64 x 64, four per SIMD, whole tiles only: its
     // split builds would spill (55-96 registers at the 128-register cap), so
     // split-K and stream-K stay with 7.  Wave priority falls over each K tile
@@ -613,7 +616,8 @@ int launch(const Machine &m, int variant, int access, int splits, int workers, v
     if (splits < 1 || splits > kMaxSplits) return SGEMM_ERR_SPLITS;
     if (splits > 1 && kVariants[variant].split4 == nullptr) return SGEMM_ERR_SPLITS;
     if (workers < 0 || workers > kMaxWorkers || (workers > 0 && splits > 1)) return SGEMM_ERR_SPLITS;
-    if (workers > 0 && !kVariants[variant].streamk) return SGEMM_ERR_SPLITS;
+    if (workers > 0 && (!kVariants[variant].streamk || kVariants[variant].split4 == nullptr))
+        return SGEMM_ERR_SPLITS;
     if (M == 0 || N == 0) return SGEMM_OK;
     const bool no_product = alpha == 0.0f || K == 0;
     if (no_product && beta == 1.0f) return SGEMM_OK;
@@ -800,7 +804,7 @@ int sgemm_streamk(int variant, int workers, int M, int N, int K, float alpha,
 
 size_t sgemm_streamk_workspace_size(int variant, int workers) {
     if (variant < 0 || variant >= kNumVariants || workers < 1 || workers > kMaxWorkers) return 0;
-    if (!kVariants[variant].streamk) return 0;
+    if (!kVariants[variant].streamk || kVariants[variant].split4 == nullptr) return 0;
     return streamk_bytes(kVariants[variant], workers);
 }
 

@@ -1239,37 +1239,43 @@ struct DirectStage {
 // k0 + lh * KX / 2, column wn + NI * li.  hook(j, u) as in mfma_tile.
 // KX is the k extent the wave covers in this call (all of the tile, BK, or
 // its wave group's share of it); A rows stay BK floats long.
-// The operands of one k-step's MFMAs held over to the next K tile (DF).
-template <int MI, int NI> struct KcPending {
-    float x[MI];
-    typename vec_t<NI>::type b;
+// The operands of the last D k-steps' MFMAs of a K tile, held over to the
+// next one (DF).
+template <int MI, int NI, int D> struct KcPending {
+    float x[D > 0 ? D : 1][MI];
+    typename vec_t<NI>::type b[D > 0 ? D : 1];
 };
 
-// The MFMAs of a held-over k-step: into acc_odd when that k-step is odd and
-// the odd k-steps have their own accumulators (CH == 2).
-template <int MI, int NI, int CH, bool ODD>
-__device__ __forceinline__ void mfma_pending_kc(const KcPending<MI, NI> &pd, floatx16 (&acc)[MI][NI],
+// The MFMAs of the held-over k-steps STEPS - D .. STEPS - 1, in that order:
+// an odd k-step into acc_odd when the odd k-steps have their own
+// accumulators (CH == 2).
+template <int MI, int NI, int CH, int D, int STEPS>
+__device__ __forceinline__ void mfma_pending_kc(const KcPending<MI, NI, D> &pd, floatx16 (&acc)[MI][NI],
                                                 floatx16 (&acc_odd)[MI][NI]) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int d = 0; d < D; ++d)
 #pragma unroll
-        for (int jj = 0; jj < NI; ++jj) {
-            if (CH == 2 && ODD)
-                acc_odd[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(pd.x[i], vget(pd.b, jj), acc_odd[i][jj], 0, 0, 0);
-            else
-                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(pd.x[i], vget(pd.b, jj), acc[i][jj], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int jj = 0; jj < NI; ++jj) {
+                if (CH == 2 && ((STEPS - D + d) & 1))
+                    acc_odd[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(pd.x[d][i], vget(pd.b[d], jj),
+                                                                          acc_odd[i][jj], 0, 0, 0);
+                else
+                    acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x2f32(pd.x[d][i], vget(pd.b[d], jj), acc[i][jj],
+                                                                      0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
 }
 
-// DF: the last k-step's MFMAs are not issued here but held in pd, and the
-// caller issues them after the barrier that ends the tile (pd_in: this call
-// issues the previous tile's, right after its own first fragment reads), so
-// the matrix unit has work while those reads are in flight.
-template <int BK, int MI, int NI, int SB, int FD, int CH, int RO, int PR, int KX, bool DF, class Hook>
+// DF > 0: the last DF k-steps' MFMAs are not issued here but held in pd,
+// and the caller issues them after the barrier that ends the tile (pd_in:
+// this call issues the previous tile's, right after its own first fragment
+// reads), so the matrix unit has work while those reads are in flight.
+template <int BK, int MI, int NI, int SB, int FD, int CH, int RO, int PR, int KX, int DF, class Hook>
 __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_off)[KX / 8], const float *bp,
                                              floatx16 (&acc)[MI][NI], floatx16 (&acc_odd)[MI][NI], Hook hook,
-                                             KcPending<MI, NI> &pd, bool pd_in) {
+                                             KcPending<MI, NI, DF> &pd, bool pd_in) {
     typedef typename vec_t<NI>::type VB;
     static_assert(KX % 8 == 0 && KX <= BK, "k extent: whole chunks of 4 per lane half");
     constexpr int STEPS = KX / 2, QN = KX / 8;
@@ -1318,9 +1324,10 @@ __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_o
     __builtin_amdgcn_sched_barrier(0);
     av[0][0] = *reinterpret_cast<const float4 *>(a_row + a_off[0]);
     }
-    if (DF && pd_in) {
+    static_assert(DF >= 0 && DF <= STEPS, "held-over k-steps: at most a tile's");
+    if (DF > 0 && pd_in) {
         __builtin_amdgcn_sched_barrier(0);
-        mfma_pending_kc<MI, NI, CH, ((STEPS - 1) & 1) != 0>(pd, acc, acc_odd);
+        mfma_pending_kc<MI, NI, CH, DF, STEPS>(pd, acc, acc_odd);
     }
     // RO == 2: the rest of the first group of A and the next B fragment
     // right after the first MFMA
@@ -1355,13 +1362,14 @@ __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_o
                     av[(q + 1) & 1][i] = *reinterpret_cast<const float4 *>(a_row + i * 32 * BK + a_off[q + 1]);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (DF && j == STEPS - 1) {
+            if (DF > 0 && j >= STEPS - DF) {
+                const int d = j - (STEPS - DF);
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
                     const float4 &ac = av[q & 1][i];
-                    pd.x[i] = e == 0 ? ac.x : e == 1 ? ac.y : e == 2 ? ac.z : ac.w;
+                    pd.x[d][i] = e == 0 ? ac.x : e == 1 ? ac.y : e == 2 ? ac.z : ac.w;
                 }
-                pd.b = bv[j % RING];
+                pd.b[d] = bv[j % RING];
 #pragma unroll
                 for (int u = 0; u < MI * NI; ++u) hook(j, u);
                 continue;
@@ -1454,7 +1462,7 @@ __device__ __forceinline__ void ring_barrier() {
 // every wave of the workgroup.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WM, int WN, int VEC, int WPE, bool SPLIT, int RO, int PR = 0,
-          int KG = 1, int STG = 2, bool UA = false, bool DF = false>
+          int KG = 1, int STG = 2, bool UA = false, int DF = 0>
 __global__ void __launch_bounds__(KG * (BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -1552,7 +1560,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
         // The stages as restrict pointers: the scoped no-alias information
         // lets the compiler see that the reads of the current stage need not
         // wait for the loads into another one (the waits are explicit).
-        KcPending<MI, NI> pd;
+        KcPending<MI, NI, DF> pd;
         auto tile_body = [&](const float *__restrict__ st, float *__restrict__ nx, int kn, bool issue,
                              bool pd_in) {
             const rsrc_t rb = d.b_rows(a, bn, kn);
@@ -1603,7 +1611,7 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
             }
         }
         // the last tile's held-over k-step
-        if (DF && KT > 0) mfma_pending_kc<MI, NI, CH, ((KX / 2 - 1) & 1) != 0>(pd, acc, acc_odd);
+        if (DF > 0 && KT > 0) mfma_pending_kc<MI, NI, CH, DF, KX / 2>(pd, acc, acc_odd);
         if (CH == 2) {
 #pragma unroll
             for (int i = 0; i < MI; ++i)
