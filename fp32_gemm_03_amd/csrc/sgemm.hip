@@ -74,15 +74,18 @@ struct Variant {
 // blocks and shapes, 9% on 256 x 256 x 4096 in 16 parts, at most 1.5%
 // slower on a few).  The split builds of the 64 x 64 blocks hold the last
 // two k-steps (SD 2: another 2-4% on their split-K and stream-K shapes; level
-// on the larger blocks' split builds, mixed on whole tiles).
-#define MFMA_CFG_KCD(BM, BN, BK, WM, WN, WPE, PA, SWZ, RO, SD, SUFFIX)                  \
+// on the larger blocks' split builds, mixed on whole tiles).  CPG groups of
+// the epilogue's old C values are read during the last K tile (the 128 x 256
+// x 16 block of low K: 118.3 against 116.3 TFLOP/s at 16384^2 x 128 with
+// beta = 1; slower on the 64 x 64 x 32 block, level with beta = 0).
+#define MFMA_CFG_KCD(BM, BN, BK, WM, WN, WPE, PA, SWZ, RO, SD, CPG, SUFFIX)             \
     {"mfma_" #BM "x" #BN "x" #BK "_w" #WM "x" #WN SUFFIX, SGEMM_PATH_MFMA, BM, BN, BK,    \
      (BM / WM) * (BN / WN) * 64,                                                         \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, false, 1>,    \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, false, 1, CPG>, \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, true, 1, 2, 0, SWZ, true>,       \
      sgk::sgemm_mfma<BM, BN, BK, WM, WN, PA, 0, 1, WPE, false, 1, 2, 0, SWZ, true>,      \
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO, 0, 1, 2, false, SD>, 1, 1, 0, \
-     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, true, 1>,     \
+     sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, false, RO, 0, 1, 2, true, 1, CPG>,  \
      sgk::sgemm_mfma_kc<BM, BN, BK, WM, WN, 4, WPE, true, RO, 0, 1, 2, true, SD>}
 
 // A small K-ordered block of 32 x 32 waves split over KG wave groups; all
@@ -110,12 +113,12 @@ const Variant kVariants[] = {
     MFMA_CFG(128, 256, 16, 64, 128, 4, 2, 0, 1, false, "_ldsepi"), // 4: LDS-staged epilogue
     MFMA_CFG(256, 128, 16, 128, 64, 4, 2, 0, 1, false, "_ldsepi"), // 5: LDS-staged epilogue
     MFMA_CFG(128, 256, 16, 64, 128, 0, 2, 0, 0, true, "_xorA"),    // 6: A unpadded, XOR-swizzled
-    MFMA_CFG_KCD(256, 256, 32, 128, 64, 2, 4, false, 2, 1, "_kcd"),    // 7: 8 waves, 2 per SIMD
-    MFMA_CFG_KCD(128, 128, 16, 64, 64, 4, 4, false, 0, 1, "_wpe4_kcd"),  // 8: 4 workgroups per CU
-    MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, 0, true, 0, 1, "_kcd"),     // 9: 2 workgroups per CU
-    MFMA_CFG_KCD(128, 256, 32, 64, 64, 2, 4, false, 2, 1, "_w8_kcd"),  // 10: 8 waves, 2 per SIMD
-    MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, 1, 2, "_kcd"),       // 11: 4 workgroups per CU
-    MFMA_CFG_KCD(128, 128, 64, 32, 64, 2, 4, false, 2, 1, "_w8_kcd"),  // 12: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(256, 256, 32, 128, 64, 2, 4, false, 2, 1, 0, "_kcd"),    // 7: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(128, 128, 16, 64, 64, 4, 4, false, 0, 1, 0, "_wpe4_kcd"),  // 8: 4 workgroups per CU
+    MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, 0, true, 0, 1, 1, "_kcd"),     // 9: 2 workgroups per CU
+    MFMA_CFG_KCD(128, 256, 32, 64, 64, 2, 4, false, 2, 1, 0, "_w8_kcd"),  // 10: 8 waves, 2 per SIMD
+    MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, 1, 2, 0, "_kcd"),       // 11: 4 workgroups per CU
+    MFMA_CFG_KCD(128, 128, 64, 32, 64, 2, 4, false, 2, 1, 0, "_w8_kcd"),  // 12: 8 waves, 2 per SIMD
     // 13: the block for at most one tile per CU.  Its 128-bit build (and
     // the one for rows at 4-byte alignment) is two
     // wave groups (KG 2) of two 64 x 32 waves, each group half of every K
@@ -130,7 +133,7 @@ const Variant kVariants[] = {
      sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1, 0, 1, 2, false, 2>, 1, 1, 0,
      sgk::sgemm_mfma_kc<64, 64, 64, 64, 32, 4, 1, false, 2, 0, 2, 2, true, 1>,
      sgk::sgemm_mfma_kc<64, 64, 64, 32, 32, 4, 2, true, 1, 0, 1, 2, true, 2>},
-    MFMA_CFG_KCD(128, 128, 32, 64, 32, 4, 4, false, 2, 1, "_w8_kcd"),  // 14: 8 waves, 2 workgroups per CU
+    MFMA_CFG_KCD(128, 128, 32, 64, 32, 4, 4, false, 2, 1, 0, "_w8_kcd"),  // 14: 8 waves, 2 workgroups per CU
     // 15: 7 with 16 waves of 64 x 64, four per SIMD, whole tiles only: its
     // split builds would spill (55-96 registers at the 128-register cap), so
     // split-K and stream-K stay with 7.  Wave priority falls over each K tile

@@ -580,6 +580,44 @@ __device__ __forceinline__ void epilogue(const Args &a, const TC &st, Pos pos, V
     }
 }
 
+// The same with the old values of vectors 0 .. NP - 1 already in pre (read
+// before the K loop ended); NP is a whole number of groups.
+template <int NV, int W, class TC, class Pos, class Val, int GV, int NP>
+__device__ __forceinline__ void epilogue_pre(const Args &a, const TC &st, Pos pos, Val val,
+                                             const float (&pre)[NP][W]) {
+    constexpr int G = NV < GV / W ? NV : (GV / W > 0 ? GV / W : 1);
+    static_assert(NV % G == 0 && NP % G == 0 && NP <= NV, "epilogue groups");
+    if (a.beta != 0.0f) {
+#pragma unroll
+        for (int b = 0; b < NV; b += G) {
+            float old[G][W];
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (b + g < NP) {
+#pragma unroll
+                    for (int i = 0; i < W; ++i) old[g][i] = pre[b + g < NP ? b + g : 0][i];
+                } else {
+                    int r, c;
+                    pos(b + g, r, c);
+                    st.load(a, r, c, old[g]);
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                int r, c;
+                pos(b + g, r, c);
+                float v[W], out[W];
+                val(b + g, v);
+#pragma unroll
+                for (int i = 0; i < W; ++i) out[i] = fmaf(a.alpha, v[i], a.beta * old[g][i]);
+                st.store(a, r, c, out);
+            }
+        }
+    } else {
+        epilogue<NV, W, TC, Pos, Val, GV>(a, st, pos, val);
+    }
+}
+
 template <bool BUF, int BM, int BN, int BK, int NT, int PADA, int PADB, int VEC, int W, int STAGES,
           bool SWZ = false>
 struct Staging {
@@ -1419,6 +1457,43 @@ __device__ __forceinline__ void epilogue_mfma_kc(const Args &a, int bm, int bn, 
     epilogue<MI * 16, NI, TC, decltype(pos), decltype(val), GV>(a, st, pos, val);
 }
 
+// Epilogue of the K-ordered kernel with the old C values of its first NP
+// vectors read ahead into pre (c_prefetch_kc, during the last K tile).
+template <int MI, int NI>
+__device__ __forceinline__ void kc_pos(int v, int wm, int wn, int li, int lh, int &r, int &c) {
+    const int i = v / 16, reg = v % 16;
+    r = wm + 32 * i + 8 * (reg >> 2) + 4 * lh + (reg & 3);
+    c = wn + NI * li;
+}
+
+template <class TC, int MI, int NI, int NP>
+__device__ __forceinline__ void c_prefetch_kc(const Args &a, int bm, int bn, int wm, int wn, int li, int lh,
+                                              float (&pre)[NP][NI]) {
+    TC st;
+    st.init(a, bm, bn);
+    const bool en = a.beta != 0.0f;
+#pragma unroll
+    for (int v = 0; v < NP; ++v) {
+        int r, c;
+        kc_pos<MI, NI>(v, wm, wn, li, lh, r, c);
+        st.load_if(en, a, r, c, pre[v]);
+    }
+}
+
+template <class TC, int MI, int NI, int GV, int NP>
+__device__ __forceinline__ void epilogue_mfma_kc_pre(const Args &a, int bm, int bn, int wm, int wn, int li,
+                                                     int lh, const floatx16 (&acc)[MI][NI],
+                                                     const float (&pre)[NP][NI]) {
+    TC st;
+    st.init(a, bm, bn);
+    auto pos = [&](int v, int &r, int &c) { kc_pos<MI, NI>(v, wm, wn, li, lh, r, c); };
+    auto val = [&](int v, float (&x)[NI]) {
+#pragma unroll
+        for (int j = 0; j < NI; ++j) x[j] = acc[v / 16][j][v % 16];
+    };
+    epilogue_pre<MI * 16, NI, TC, decltype(pos), decltype(val), GV, NP>(a, st, pos, val, pre);
+}
+
 // The barrier that ends a K tile of the LDS ring: this wave's loads but the
 // newest N have landed (vmcnt; gfx9 encoding, vmcnt in bits 3:0 and 15:14,
 // expcnt left at its maximum), its LDS reads have returned (lgkmcnt 0:
@@ -1462,7 +1537,7 @@ __device__ __forceinline__ void ring_barrier() {
 // every wave of the workgroup.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WM, int WN, int VEC, int WPE, bool SPLIT, int RO, int PR = 0,
-          int KG = 1, int STG = 2, bool UA = false, int DF = 0>
+          int KG = 1, int STG = 2, bool UA = false, int DF = 0, int CP = 0>
 __global__ void __launch_bounds__(KG * (BM / WM) * (BN / WN) * 64)
 __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -1482,6 +1557,12 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     constexpr int RED = KG > 1 ? KG * BM * BN : 0;
     constexpr int SMEM = STG * STAGE > RED ? STG * STAGE : RED;
     static_assert(!UA || (VEC == 4 && STG == 2), "rows at 4-byte alignment: 16-byte loads, two stages");
+    static_assert(CP == 0 || (!SPLIT && KG == 1 && STG == 2), "C read ahead: one-group whole-tile builds");
+    // CP groups of the epilogue's old C values are read during the last K tile
+    constexpr int CPG = (UA ? 8 : 32) / NI > 0 ? (UA ? 8 : 32) / NI : 1;  // vectors per epilogue group
+    constexpr int CPV = CP * (MI * 16 < CPG ? MI * 16 : CPG) < MI * 16 ? CP * (MI * 16 < CPG ? MI * 16 : CPG)
+                                                                       : MI * 16;
+    float cpre[CPV > 0 ? CPV : 1][NI];
     typedef DirectStage<BM, BN, BK, NT, VEC> D;
     // C in 32-bit accesses when the rows of C need not be 16-byte aligned
     typedef CStoreBuf<NI, UA ? 1 : VEC> TC;
@@ -1583,6 +1664,13 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
             // zeros or the next range's data into a stage nobody reads)
             for (int t = 0; t < KT; ++t) {
                 if (!SPLIT) ph.tile_begin();
+                if constexpr (CP > 0) {
+                    if (t == KT - 1) {
+                        int li_ = li, lh_ = lh;
+                        asm volatile("" : "+v"(li_), "+v"(lh_));
+                        c_prefetch_kc<TC, MI, NI, CPV>(a, bm, bn, wm, wn, li_, lh_, cpre);
+                    }
+                }
                 tile_body(smem + (t & 1) * STAGE, smem + ((t + 1) & 1) * STAGE, kb + (t + 1) * BK, true, t > 0);
                 if (!SPLIT) ph.tile_mid();
                 __builtin_amdgcn_s_waitcnt(0);
@@ -1633,7 +1721,12 @@ __attribute__((amdgpu_waves_per_eu(WPE))) sgemm_mfma_kc(Args a) {
     auto finish = [&](int bm, int bn) {
         int li_ = li, lh_ = lh;
         if constexpr (SPLIT) asm volatile("" : "+v"(li_), "+v"(lh_));
-        epilogue_mfma_kc<TC, MI, NI, (SPLIT || UA) ? 8 : 32>(a, bm, bn, wm, wn, li_, lh_, acc);
+        if constexpr (CP > 0) {
+            if (KT_ALL == 0) c_prefetch_kc<TC, MI, NI, CPV>(a, bm, bn, wm, wn, li_, lh_, cpre);  // no K loop ran
+            epilogue_mfma_kc_pre<TC, MI, NI, UA ? 8 : 32, CPV>(a, bm, bn, wm, wn, li_, lh_, acc, cpre);
+        }
+        else
+            epilogue_mfma_kc<TC, MI, NI, (SPLIT || UA) ? 8 : 32>(a, bm, bn, wm, wn, li_, lh_, acc);
     };
 
     if constexpr (!SPLIT && KG == 1) {
