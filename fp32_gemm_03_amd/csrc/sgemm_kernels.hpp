@@ -1469,14 +1469,14 @@ __device__ __forceinline__ void kc_pos(int v, int wm, int wn, int li, int lh, in
 template <class TC, int MI, int NI, int NP>
 __device__ __forceinline__ void c_prefetch_kc(const Args &a, int bm, int bn, int wm, int wn, int li, int lh,
                                               float (&pre)[NP][NI]) {
+    if (a.beta == 0.0f) return;  // C is not read
     TC st;
     st.init(a, bm, bn);
-    const bool en = a.beta != 0.0f;
 #pragma unroll
     for (int v = 0; v < NP; ++v) {
         int r, c;
         kc_pos<MI, NI>(v, wm, wn, li, lh, r, c);
-        st.load_if(en, a, r, c, pre[v]);
+        st.load(a, r, c, pre[v]);
     }
 }
 

@@ -4,7 +4,8 @@ shape's fastest variant with the one the library's selection picks.
     python -m fp32_gemm_03_amd.tune [--shapes S1,S2,...] [--variants V1,V2,...] [--access M1,...]
 
 A shape is a named synthetic workload (``square8192_normal`` ...) or MxNxK
-(A, B ~ N(0,1), seed 3, alpha 1, beta 0).  Every launch goes through the C
+(A, B ~ N(0,1), seed 3, alpha 1, beta 0; ``MxNxK_beta``: beta 1 with C ~
+U[-1,1), so that the epilogue reads C).  Every launch goes through the C
 ABI on one stream; the time per launch is HIP events around a run of
 launches after about 30 ms of untimed ones (0.5 s after the GPU has idled,
 so that the clock has ramped up).  Besides the forced variants,
@@ -33,7 +34,12 @@ def _problem(shape):
     from . import inputs
     if shape in inputs.WORKLOADS:
         return inputs.workload_problem(shape)
-    M, N, K = (int(x) for x in shape.lower().split("x"))
+    dims, _, opt = shape.lower().partition("_")
+    M, N, K = (int(x) for x in dims.split("x"))
+    if opt == "beta":  # C ~ U[-1, 1), beta = 1: the epilogue reads C
+        return inputs.make_problem(M, N, K, dist="normal", seed=3, beta=1.0, c_fill="upm1", name=shape)
+    if opt:
+        raise ValueError(f"unknown shape option {opt!r} in {shape!r}")
     return inputs.make_problem(M, N, K, dist="normal", seed=3, name=shape)
 
 
