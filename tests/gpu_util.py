@@ -128,9 +128,10 @@ ACCESS_NAMES = {0: "auto", 1: "buf128", 2: "buf32", 3: "checked", 4: "buf128ab"}
 
 def sum_family(variant, access):
     """Which kernel a build of a variant runs, as far as the order of its sums
-    goes: the K-ordered direct-load kernel ("kc", the 128-bit builds of the
-    ``_kcd`` variants) or the register-staged one ("rs", every other build:
-    their 32-bit and checked builds, and every build of the others)."""
+    goes: the K-ordered direct-load kernel ("kc": the 128-bit and
+    BUFFER_128_AB builds of the ``_kcd`` variants, every build of the 32 x 32
+    and 32 x 64 blocks) or the register-staged one ("rs": the other
+    ``_kcd`` builds, and every build of the other variants)."""
     name = g.sgemm_variant_name(variant)
     kc_access = (g.SGEMM_ACCESS_BUFFER_128, g.SGEMM_ACCESS_BUFFER_128_AB)
     if name.startswith("mfma_32x"):  # the small blocks: every build is the K-ordered kernel

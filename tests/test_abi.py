@@ -223,8 +223,8 @@ def test_large_shapes_pick_the_block_whose_last_round_is_fullest():
     assert "_w8_" in g.sgemm_variant_name(g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 2048, 2048, 2048))
     assert block(3072, 3072, 3072) == (64, 64, 32)      # 128 x 128 would leave 1/4 of a round
     assert block(5120, 5120, 5120) == (64, 64, 32)      # whole rounds of 64 x 64, 6.25 of 128 x 128
-    # too few tiles for any slot count (operands that allow 128-bit
-    # accesses): up to three 32 x 32 tiles per CU, the 32 x 32 block in four
+    # too few tiles for any slot count (operands that allow 16-byte loads):
+    # up to three 32 x 32 tiles per CU, the 32 x 32 block in four
     # wave groups; up to one 64 x 64 tile per CU, the 32 x 64 block in two
     assert block(256, 256, 256) == (32, 32, 64)
     assert block(512, 512, 8192) == (32, 32, 64)
@@ -520,11 +520,13 @@ def test_plan_quantises_over_other_cu_counts(cus):
     assert _block(g.sgemm_plan_for(256, 1024, 1024, 1024, operands_load16=True)[1])[:2] == (32, 64)
     assert _block(g.sgemm_plan_for(256, 1024, 1024, 1024, operands_load16=False)[1])[:2] == (64, 64)
     # split-K: 64 tiles of 64 x 64 at 512 x 512 x 8192 split in 8 on 256 CUs;
-    # on 80 CUs a split would be in 2, so 128-bit operands take the 32 x 64
-    # block whole instead, and other operands the split
+    # on 80 CUs a split would be in 2, so the 32 x 64 block runs whole
+    # instead; operands without 16-byte loads neither split nor take it
     assert g.sgemm_plan_for(256, 512, 512, 8192, True)[2] == 8
     assert g.sgemm_plan_for(80, 512, 512, 8192, True)[2] == 1
     assert _block(g.sgemm_plan_for(80, 512, 512, 8192, True)[1])[:2] == (32, 64)
+    assert g.sgemm_plan_for(80, 512, 512, 8192, True, operands_load16=False)[2] == 1
+    assert _block(g.sgemm_plan_for(80, 512, 512, 8192, True, operands_load16=False)[1])[:2] == (64, 64)
 
 
 def test_tile_order_is_a_bijection_for_every_xcd_count():

@@ -653,7 +653,8 @@ def test_sgemm_ws_streamk_full_size_sampled(name):
 def test_row_split_through_sgemm(offsets, beta):
     """A shape that sgemm() splits by rows into two launches (8256 x 2047 x
     512: the first 8192 rows on 256 x 256 tiles, the last 64 rows with their
-    own block): N % 4 != 0 and the misaligned bases take the 32-bit builds;
+    own block): N % 4 != 0 and the misaligned bases take the builds loading
+    A and B 16 bytes at a time at 4-byte alignment;
     ldc is padded (its pad columns must keep their bits), nothing outside C
     is written, beta = 0 runs over a NaN C; every element against the
     oracle."""
