@@ -171,6 +171,21 @@ const Variant kVariants[] = {
     // the 32 x 32 block is level between the orders and keeps 1.
     MFMA_CFG_KG(32, 32, 64, 4, 1, "_kg4_kcd"),
     MFMA_CFG_KG(32, 64, 64, 2, 0, "_kg2_kcd"),
+    // 19: 17 with its K tiles in a ring of three LDS stages, each tile's
+    // loads issued two tiles ahead (128-bit build; its other builds are
+    // 17's): for half a 32 x 32 tile to one per CU and long K, where a lone
+    // workgroup per CU otherwise waits for each tile's loads in turn
+    // (512 x 512 x 2048 69.7 against 53.9 TFLOP/s, 384 x 384 x 2048 39.3
+    // against 30.7, 480 x 480 x 2048 60.9 against 46.4, 512 x 512 x 8192
+    // 80.5 against 60.5).  Slower with more tiles per CU (768 x 768 x 4096
+    // 80.5 against 87.2), with K up to 1024 (512 x 512 x 1024 61.2 against
+    // 64.8), and mixed with fewer tiles (256 x 256 x 2048 17.7 against
+    // 20.0, x 4096 19.2 against 15.0; 128 x 512 x 4096 19.3 against 21.9).
+    {"mfma_32x32x64_w32x32_kg4_s3_kcd", SGEMM_PATH_MFMA, 32, 32, 64, 256,
+     sgk::sgemm_mfma_kc<32, 32, 64, 32, 32, 4, 4, false, 1, 0, 4, 3, false, 1>,
+     sgk::sgemm_mfma_kc<32, 32, 64, 32, 32, 1, 4, false, 1, 0, 4, 2, false, 1>,
+     sgk::sgemm_mfma_kc<32, 32, 64, 32, 32, 1, 4, false, 1, 0, 4, 2, false, 1>, nullptr, 1, 0, 1,
+     sgk::sgemm_mfma_kc<32, 32, 64, 32, 32, 4, 4, false, 1, 0, 4, 2, true, 1>, nullptr},
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
@@ -188,6 +203,8 @@ constexpr int kKcMid8 = 14;      // 128 x 128 x 32, 8 waves, two workgroups per 
 constexpr int kKcHuge16 = 15;    // 256 x 256 x 32, 16 waves, one workgroup per CU, whole tiles only
 constexpr int kKcTiny4 = 17;     // 32 x 32 x 64 in four wave groups
 constexpr int kKcTiny2 = 18;     // 32 x 64 x 64 in two wave groups
+constexpr int kKcTiny4Ring = 19; // 17 with three LDS stages
+constexpr int kRingMinK = 2048;  // the shortest K at which 19 beats 17
 
 // The machine shape the choices depend on: compute units (tile quantisation,
 // stream-K workers, the split-K and row-split thresholds) and XCDs (the
@@ -443,7 +460,10 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool s
         const bool sk = streamk && rest > 0 && rest * kt >= kStreamKMinK * cus;
         if (small_ok && tiles(M, N, 32, 32) <= 3 * cus) {
             if (score_out) *score_out = kSmallRate * fill(M, N, 32, 32);
-            return kKcTiny4;
+            // between half a tile and one tile per CU and long K: the
+            // three-stage ring
+            const long long t32 = tiles(M, N, 32, 32);
+            return t32 <= cus && 2 * t32 >= cus && K >= kRingMinK ? kKcTiny4Ring : kKcTiny4;
         }
         if (small_ok && tiles(M, N, 32, 64) <= 3 * cus) {
             if (score_out) *score_out = kSmallRate * fill(M, N, 32, 64);
@@ -527,8 +547,15 @@ int select_splits(const Machine &m, int variant, int M, int N, int K) {
 // 64 x 64 x 64 block instead when K is long enough for 4 parts or more
 // (512 x 512 x 8192 in 8 parts: 99.6 TFLOP/s against 62 on 32 x 32; with 2
 // or 3 parts the small blocks win: 512^3 47 against 26, 768^3 69 against
-// 57, 1024 x 1024 x 4096 120 against 115).
+// 57, 1024 x 1024 x 4096 120 against 115).  Against the three-stage ring
+// with a 32 x 32 tile for every CU, parts need at least 512 of K (512 x 512
+// x 2048 in 8 parts: 60.9 against 69.7 for the ring; x 4096: 81.5 against
+// 76.4); with fewer tiles than half the CUs the split always wins (256 x 256
+// x 4096: 42.7 against 19.2).  A split into no more workgroups than the
+// small block has loses (512 x 512 x 1024 in 4 parts: 49.3 against 64.8;
+// 256 x 256 x 1024: 13.1 against 16.8), so it needs more.
 constexpr int kTinySplitMin = 4;
+constexpr int kRingSplitMinPart = 512;
 
 // What sgemm_ws (with_workspace) or sgemm (without) runs for these sizes:
 // the variant, split count, stream-K workers and the rows of a first
@@ -547,9 +574,13 @@ int plan(const Machine &m, int M, int N, int K, bool with_workspace, bool load16
     if (v < 0) return v;
     int sp = 1, r = 0;
     if (parts && w == 0) {
-        if (v == kKcTiny4 || v == kKcTiny2) {
+        if (v == kKcTiny4 || v == kKcTiny2 || v == kKcTiny4Ring) {
             const int s = select_splits(m, kKcSmall64, M, N, K);
-            if (s >= kTinySplitMin) {
+            const bool ring_wins = v == kKcTiny4Ring && 2 * tiles(M, N, 32, 32) >= m.cus &&
+                                   K / (s > 0 ? s : 1) < kRingSplitMinPart;
+            // the parts must outnumber the small block's workgroups
+            const long long small_wgs = v == kKcTiny2 ? tiles(M, N, 32, 64) : tiles(M, N, 32, 32);
+            if (s >= kTinySplitMin && tiles(M, N, 64, 64) * s > small_wgs && !ring_wins) {
                 v = kKcSmall64;
                 sp = s;
             }

@@ -228,6 +228,18 @@ def test_large_shapes_pick_the_block_whose_last_round_is_fullest():
     # wave groups; up to one 64 x 64 tile per CU, the 32 x 64 block in two
     assert block(256, 256, 256) == (32, 32, 64)
     assert block(512, 512, 8192) == (32, 32, 64)
+    # with half a 32 x 32 tile to one per CU and K >= 2048, its three-stage
+    # ring; with a workspace that one beats split-K only when a part would
+    # be shorter than 512 of K
+    ring = g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 512, 512, 8192)
+    assert g.sgemm_variant_name(ring).endswith("_s3_kcd")
+    assert g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 384, 384, 2048) == ring   # 144 tiles
+    assert g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 256, 256, 4096) != ring   # 64 tiles
+    assert g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 512, 512, 1024) != ring   # short K
+    assert g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 768, 768, 4096) != ring   # 576 tiles
+    assert g.sgemm_ws_plan(512, 512, 2048)[1:3] == (ring, 1)
+    assert g.sgemm_ws_plan(512, 512, 4096)[2] == 8
+    assert g.sgemm_ws_plan(256, 256, 4096)[2] == 16
     assert block(768, 768, 768) == (32, 32, 64)         # 576 tiles of 32 x 32
     assert block(1024, 1024, 1024) == (32, 64, 64)      # 1024 of 32 x 32, 256 of 64 x 64
     assert block(1000, 1023, 999) == (32, 64, 64)
@@ -596,7 +608,7 @@ def test_small_blocks_need_31_bit_offsets():
     v = g.sgemm_select_variant_for(g.SGEMM_PATH_AUTO, 512, 512, 512, 0x1000, big, 0x2000, 512, 0x3000, 512)
     assert _block(v) == (64, 64, 64)
     tiny = [i for i in range(g.sgemm_variant_count()) if (g.sgemm_variant_name(i) or "").startswith("mfma_32x")]
-    assert len(tiny) == 2
+    assert len(tiny) == 3   # 32 x 32 (two and three LDS stages) and 32 x 64
     for t in tiny:
         for access in (g.SGEMM_ACCESS_AUTO, g.SGEMM_ACCESS_CHECKED):
             rc = g.sgemm_variant_access(t, access, 512, 512, 512, 1.0, 0x1000, big, 0x2000, 512, 0.0,
