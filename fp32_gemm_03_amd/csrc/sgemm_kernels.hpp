@@ -1535,6 +1535,13 @@ __device__ __forceinline__ void ring_barrier() {
 // interleave (in-workgroup split-K).  The groups' partial tiles are summed
 // through LDS in group order (deterministic), and the epilogue is shared by
 // every wave of the workgroup.
+//
+// UA: A and B loaded 16 bytes per lane at any 4-byte alignment (the range
+// checks are per 4 bytes), the columns of A past K that a chunk brings along
+// cleared in LDS once their tile has landed, C in 32-bit accesses.  DF: the
+// last DF k-steps of MFMAs of each K tile are issued after the barrier that
+// ends it (mfma_tile_kc).  CP: CP groups of the epilogue's old C values are
+// read during the last K tile (one-group whole-tile builds).
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WM, int WN, int VEC, int WPE, bool SPLIT, int RO, int PR = 0,
           int KG = 1, int STG = 2, bool UA = false, int DF = 0, int CP = 0>
