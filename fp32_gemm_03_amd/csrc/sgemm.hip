@@ -371,6 +371,18 @@ constexpr int kStreamKLongK = 2048;
 // 64 x 64 x 32; 1024^3 runs 96 on 64 x 64 x 64).
 constexpr double kHuge16Rate = 147.0;
 constexpr double kSmallRate = 110.0;
+// The 64 x 64 x 32 block (four per CU) against the 32 x 64 wave-group block
+// (three per CU) where both have several tiles per CU: the same balance of
+// tiles over the CUs favours the former by 3.5% (3072^3 133.9 against
+// 129.2, 4608^3 130.9 against 126.7), but the finer 32 x 64 grid often
+// balances better (1536^3 110.7 against 96.8 TFLOP/s, 2304^3 118.5 against
+// 112.6, 3072 x 1536 x 2048 125.3 against 117.6).
+// Below K = 1024 the 32 x 64 block's fixed costs per tile lose (3584^2 x 512
+// 112.5 against 121.5, 2560^2 x 256 94.8 against 105.4, K = 128: 16-20%
+// slower), so it is weighed only from there.
+constexpr double kSmall4Rate = 134.0;
+constexpr double kTiny2Rate = 129.3;
+constexpr int kTiny2MinK = 1024;
 
 // The variant for a whole-tile (or, with streamk, stream-K) launch on a
 // machine of m.cus compute units; *score gets its predicted TFLOP/s (rate x
@@ -407,7 +419,7 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool s
                                      {kKcLarge4, 144.0, 4, 256},
                                      {kKcShortK, 144.0, 2, 0},  {kKcWide, 143.0, 1, 512},
                                      {kKcMid8, 142.5, 2, 256},  {kKcDeep8, 139.5, 1, 1024},
-                                     {kKcSmall4, 134.0, 4, 0}};
+                                     {kKcSmall4, kSmall4Rate, 4, 0}};
     int best = -1, best_workers = 0;
     double best_score = -1.0;
     for (const Candidate &c : cand) {
@@ -429,6 +441,15 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool s
             best = c.variant;
             best_workers = w;
         }
+    }
+    // the 32 x 64 block where its tiles balance better over the CUs
+    auto tiny2_score = [&]() {
+        if (K < kTiny2MinK) return 0.0;
+        return kTiny2Rate * quantization(tiles(M, N, 32, 64), cus) * fill(M, N, 32, 64);
+    };
+    if (best == kKcSmall4 && best_workers == 0 && small_ok && tiny2_score() > best_score) {
+        best = kKcTiny2;
+        best_score = tiny2_score();
     }
     if (best < 0) {
         // No block fills the chip (measured over cubes 256-1920 and
@@ -471,7 +492,15 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool s
         }
         if (score_out) *score_out = kSmallRate * fill(M, N, v.bm, v.bn);
         if (t <= cus || (t <= 2 * cus && !(sk && K >= kStreamKLongK))) return kKcSmall64;
-        if (sk && workers) *workers = (int)cus;
+        if (sk && workers) {
+            *workers = (int)cus;
+            return kKcSmall4;
+        }
+        const double s4 = kSmall4Rate * quantization(t, cus) * fill(M, N, v.bm, v.bn);
+        if (small_ok && tiny2_score() > s4) {
+            if (score_out) *score_out = tiny2_score();
+            return kKcTiny2;
+        }
         return kKcSmall4;
     }
     if (workers) *workers = best_workers;
