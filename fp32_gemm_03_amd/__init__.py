@@ -24,7 +24,8 @@ __all__ = [
     "SGEMM_ACCESS_CHECKED", "SGEMM_ACCESS_BUFFER_128_AB", "sgemm_variant_access",
     "sgemm_ws", "sgemm_ws_noalloc", "SGEMM_NOALLOC_SCRATCH_BYTES", "sgemm_workspace_size", "sgemm_select_splits", "sgemm_splitk",
     "sgemm_splitk_workspace_size", "sgemm_streamk", "sgemm_streamk_workspace_size",
-    "sgemm_select_streamk", "sgemm_ws_plan", "sgemm_select_rows", "sgemm_plan_for",
+    "sgemm_select_streamk", "sgemm_ws_plan", "sgemm_select_rows", "sgemm_select_pieces",
+    "sgemm_plan_for", "sgemm_plan_pieces_for",
     "sgemm_device_shape", "sgemm_tile_order",
     "SgemmError", "LibraryNotBuilt", "library_path", "load_library",
     "sgemm", "sgemm_path", "sgemm_variant", "sgemm_variant_count",
@@ -111,6 +112,10 @@ def load_library():
         lib.sgemm_ws_plan.restype = i
         lib.sgemm_plan_for.argtypes = [i, i, i, i, i, i] + [ctypes.POINTER(i)] * 4
         lib.sgemm_plan_for.restype = i
+        lib.sgemm_plan_pieces_for.argtypes = [i, i, i, i, i, i] + [ctypes.POINTER(i)] * 5
+        lib.sgemm_plan_pieces_for.restype = i
+        lib.sgemm_select_pieces.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+        lib.sgemm_select_pieces.restype = i
         lib.sgemm_device_shape.argtypes = [ctypes.POINTER(i), ctypes.POINTER(i)]
         lib.sgemm_device_shape.restype = i
         lib.sgemm_tile_order.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
@@ -257,8 +262,16 @@ def sgemm_select_streamk(M, N, K) -> int:
 
 
 def sgemm_select_rows(M, N, K) -> int:
-    """Rows of C that ``sgemm`` runs as a first launch of 256 x 256 tiles (0: one launch)."""
+    """Rows of the first piece ``sgemm`` cuts C into (0: one launch)."""
     return int(load_library().sgemm_select_rows(int(M), int(N), int(K)))
+
+
+def sgemm_select_pieces(M, N, K):
+    """``(status, rows, cols)``: the first piece ``sgemm`` cuts C into, rows x cols at the
+    top left on 256 x 256 tiles (rows 0: one launch; cols == N: a cut by rows alone)."""
+    r, c = ctypes.c_int(0), ctypes.c_int(0)
+    rc = load_library().sgemm_select_pieces(int(M), int(N), int(K), ctypes.byref(r), ctypes.byref(c))
+    return int(rc), r.value, c.value
 
 
 def sgemm_ws_plan(M, N, K):
@@ -279,6 +292,18 @@ def sgemm_plan_for(compute_units, M, N, K, with_workspace=False, operands_load16
                                        ctypes.byref(v), ctypes.byref(sp), ctypes.byref(w),
                                        ctypes.byref(r))
     return int(rc), v.value, sp.value, w.value, r.value
+
+
+def sgemm_plan_pieces_for(compute_units, M, N, K, with_workspace=False, operands_load16=True):
+    """``sgemm_plan_for`` with the first piece's columns: ``(status, variant, splits,
+    workers, rows, cols)``."""
+    v, sp, w = ctypes.c_int(-1), ctypes.c_int(0), ctypes.c_int(0)
+    r, c = ctypes.c_int(0), ctypes.c_int(0)
+    rc = load_library().sgemm_plan_pieces_for(int(compute_units), int(M), int(N), int(K),
+                                              1 if with_workspace else 0, 1 if operands_load16 else 0,
+                                              ctypes.byref(v), ctypes.byref(sp), ctypes.byref(w),
+                                              ctypes.byref(r), ctypes.byref(c))
+    return int(rc), v.value, sp.value, w.value, r.value, c.value
 
 
 def sgemm_device_shape():

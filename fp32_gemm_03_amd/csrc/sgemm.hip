@@ -501,6 +501,8 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool s
             if (score_out) *score_out = tiny2_score();
             return kKcTiny2;
         }
+        // more than two tiles per CU: the block's own rate holds
+        if (score_out) *score_out = s4;
         return kKcSmall4;
     }
     if (workers) *workers = best_workers;
@@ -512,42 +514,82 @@ int select_variant(const Machine &m, int path, int M, int N, int K, bool small_o
     return choose(m, path, M, N, K, false, small_ok, nullptr);
 }
 
+// The first piece's 256 x 256 tiles run one workgroup per CU: each pays its
+// first loads and its write-back of C with nothing to overlap them, priced
+// as kPiecesTileK more steps of K per tile.  Over 93 shapes measured both
+// ways (cubes 4352-11776, rectangles 2048 to 20000 wide, K 512-8192),
+// pricing the rate alone with K of 2048 or more took 75 cuts, 12 of them up
+// to 3% slower than one launch; with this price the model takes 51, of which
+// 49 ran 0.2-9.3% faster and two 2.4% and 3.1% slower (3.6% faster in
+// geometric mean).  With K of 512, 8 of 10 cuts predicted 2% faster ran
+// slower.
+constexpr double kPiecesTileK = 75.0;
+constexpr int kPiecesMinK = 1024;
+
+struct Pieces {
+    int rows = 0, cols = 0;  // the first piece; rows == 0: one launch
+};
+
 // Without a workspace there is no stream-K, and a partial last round of
-// tiles leaves CUs idle.  C can instead be split by rows into two launches:
-// the first 256 r rows as 256 x 256 tiles that fill their rounds (at least
-// 96% of the last one busy), and the rest with the block chosen for it.
-// Returns those first rows, or 0 when one launch is predicted within 2% of
-// the best split.  Measured at 7168^3, 9216^3 and 11264^3: 143.4, 143.7 and
-// 144.5 TFLOP/s against 136.4, 139.1 and 140.2 for one launch (the split the
-// model picks there was within 1% of the best one tried).  Only bottom parts
-// of up to 64 block rows are tried.
-int split_rows(const Machine &m, int M, int N, int K, bool small_ok) {
-    if (K < 512 || M < 512) return 0;
+// tiles leaves CUs idle.  C can instead be cut into pieces, one launch each:
+// a first piece of rows x cols on 256 x 256 tiles that fill their rounds (at
+// least 96% of the last one busy), the columns right of it over those rows,
+// and the rows below it over every column, each of the two with the block
+// chosen for it.  cols == N cuts by rows alone (the first piece then pads its
+// last tile column), rows == M by columns alone.  Returns {0, 0} when one
+// launch is predicted within 2% of the best cut.  Measured against one
+// launch, in the same process: 4352^3 141.0 against 128.9 TFLOP/s, 5120^3
+// 142.8 against 137.4, 7168^3 144.7 against 138.0, 11264^3 146.1 against
+// 141.6; at 5120^3, 7168^3, 9216^3, 11264^3 and 13824^3 the cut the model
+// picked (without the price of a tile's start) ran within 0.3% of the best
+// of up to 40 cuts tried.  Only the last
+// 64 block rows and 32 block columns are tried as the first piece's edges.
+Pieces split_pieces(const Machine &m, int M, int N, int K, bool small_ok) {
+    Pieces best;
+    if (K < kPiecesMinK || M < 512) return best;
     double single = 0.0;
-    if (choose(m, SGEMM_PATH_AUTO, M, N, K, false, small_ok, nullptr, &single) < 0 || single <= 0.0) return 0;
-    const long long nbn = (N + 255) / 256;
-    const double per_row = 2.0 * N * (double)K;
-    const double t_single = per_row * M / single;
-    // the first part's rows are whole 256-row blocks: only its columns pad
-    const double fill_n = (double)N / (double)(nbn * 256);
+    if (choose(m, SGEMM_PATH_AUTO, M, N, K, false, small_ok, nullptr, &single) < 0 || single <= 0.0) return best;
+    const double per_elem = 2.0 * (double)K;
+    const double t_single = per_elem * M * (double)N / single;
     double best_t = t_single;
-    int best_rows = 0;
-    const long long r_hi = (M - 1) / 256, r_lo = r_hi > 64 ? r_hi - 64 : 1;
-    for (long long r = r_hi; r >= r_lo; --r) {
-        const long long t = r * nbn;
-        if (t < m.cus) break;
-        const double q = quantization(t, m.cus);
-        if (q < 0.96) continue;
-        const int m1 = (int)(r * 256), m2 = M - m1;
-        double s2 = 0.0;
-        if (choose(m, SGEMM_PATH_AUTO, m2, N, K, false, small_ok, nullptr, &s2) < 0 || s2 <= 0.0) continue;
-        const double t_split = per_row * m1 / (kHuge16Rate * q * fill_n) + per_row * m2 / s2;
-        if (t_split < best_t) {
-            best_t = t_split;
-            best_rows = m1;
+    // predicted time of an m1 x n1 piece with the block chosen for it
+    auto piece = [&](int m1, int n1) {
+        if (m1 == 0 || n1 == 0) return 0.0;
+        double s = 0.0;
+        if (choose(m, SGEMM_PATH_AUTO, m1, n1, K, false, small_ok, nullptr, &s) < 0 || s <= 0.0) return -1.0;
+        return per_elem * m1 * (double)n1 / s;
+    };
+    const long long nbn = (N + 255) / 256;
+    const long long rb_hi = M / 256, rb_lo = rb_hi > 64 ? rb_hi - 64 : 1;
+    const long long cb_hi = (N - 1) / 256, cb_lo = cb_hi > 32 ? cb_hi - 32 : 1;
+    for (long long rb = rb_hi; rb >= rb_lo; --rb) {
+        const int m1 = (int)(rb * 256);
+        double t_below = -2.0;  // the piece below, chosen once per rb
+        // cb = nbn: every column, padded (a cut by rows only)
+        for (long long cb = nbn; cb >= cb_lo; --cb) {
+            const bool full = cb == nbn;
+            if (full && m1 == M) continue;  // that is the single launch
+            const long long t = rb * cb;
+            if (t < m.cus) break;
+            const double q = quantization(t, m.cus);
+            if (q < 0.96) continue;
+            const int n1 = full ? N : (int)(cb * 256);
+            if (t_below == -2.0) t_below = piece(M - m1, N);
+            if (t_below < 0.0) break;
+            const double t_right = full ? 0.0 : piece(m1, N - n1);
+            if (t_right < 0.0) continue;
+            const double fill = full ? (double)N / (double)(nbn * 256) : 1.0;
+            const double t_split =
+                per_elem * m1 * (double)n1 / (kHuge16Rate * q * fill) * (K + kPiecesTileK) / K + t_right + t_below;
+            if (t_split < best_t) {
+                best_t = t_split;
+                best.rows = m1;
+                best.cols = n1;
+            }
         }
     }
-    return best_t < 0.98 * t_single ? best_rows : 0;
+    if (best_t < 0.98 * t_single) return best;
+    return Pieces{};
 }
 
 // Split count for a variant when a workspace is available (measured on
@@ -587,8 +629,8 @@ constexpr int kTinySplitMin = 4;
 constexpr int kRingSplitMinPart = 512;
 
 // What sgemm_ws (with_workspace) or sgemm (without) runs for these sizes:
-// the variant, split count, stream-K workers and the rows of a first
-// row-split launch (0: none).  Returns 0 or a negative argument code.
+// the variant, split count, stream-K workers and the first piece of a cut
+// into several launches (rows 0: none).  Returns 0 or a negative argument code.
 // load16: the operands allow 16-byte loads of A and B (loads16 below),
 // which the small blocks, split-K and stream-K need: loading 4 bytes per
 // lane straight into LDS, split launches measured slower than one launch of
@@ -596,12 +638,13 @@ constexpr int kRingSplitMinPart = 512;
 // 60.0 against 88.6, 1023 x 1023 x 4095 in 2 parts 62.7 against 100.2), and
 // the small blocks slower than the 64 x 64 one.
 int plan(const Machine &m, int M, int N, int K, bool with_workspace, bool load16, int *variant,
-         int *splits, int *workers, int *rows) {
+         int *splits, int *workers, Pieces *pieces) {
     int w = 0;
     const bool parts = with_workspace && load16;
     int v = choose(m, SGEMM_PATH_AUTO, M, N, K, parts, load16, &w);
     if (v < 0) return v;
-    int sp = 1, r = 0;
+    int sp = 1;
+    Pieces pc;
     if (parts && w == 0) {
         if (v == kKcTiny4 || v == kKcTiny2 || v == kKcTiny4Ring) {
             const int s = select_splits(m, kKcSmall64, M, N, K);
@@ -617,11 +660,11 @@ int plan(const Machine &m, int M, int N, int K, bool with_workspace, bool load16
             sp = select_splits(m, v, M, N, K);
         }
     }
-    if (w == 0 && sp == 1) r = split_rows(m, M, N, K, load16);
+    if (w == 0 && sp == 1) pc = split_pieces(m, M, N, K, load16);
     if (variant) *variant = v;
     if (splits) *splits = sp;
     if (workers) *workers = w;
-    if (rows) *rows = r;
+    if (pieces) *pieces = pc;
     return SGEMM_OK;
 }
 
@@ -790,17 +833,33 @@ int launch(const Machine &m, int variant, int access, int splits, int workers, v
     return err == hipSuccess ? SGEMM_OK : (int)err;
 }
 
-// C split by rows: rows [0, rows) on the 16-wave 256 x 256 block, the rest
-// with the block chosen for it, one launch each on the same stream.
-int launch_rows(const Machine &m, int rows, int M, int N, int K, float alpha, const float *A, int lda,
-                const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
-    int rc = launch(m, kKcHuge16, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, rows, N, K, alpha, A, lda, B,
-                    ldb, beta, C, ldc, stream);
+// C cut into pieces: rows x cols at the top left on the 16-wave 256 x 256
+// block, then the columns right of it over the same rows and the rows below
+// it over every column, each with the block chosen for it; one launch each,
+// on the same stream.  Moving B and C by cols columns keeps their alignment
+// (cols is a multiple of 256).
+int launch_pieces(const Machine &m, Pieces pc, int M, int N, int K, float alpha, const float *A, int lda,
+                  const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
+    int rc = launch(m, kKcHuge16, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, pc.rows, pc.cols, K, alpha, A, lda,
+                    B, ldb, beta, C, ldc, stream);
     if (rc != SGEMM_OK) return rc;
-    const int v2 = select_variant(m, SGEMM_PATH_AUTO, M - rows, N, K, loads16(A, lda, B, ldb, C, ldc));
-    if (v2 < 0) return v2;
-    return launch(m, v2, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M - rows, N, K, alpha,
-                  A + (size_t)rows * lda, lda, B, ldb, beta, C + (size_t)rows * ldc, ldc, stream);
+    if (pc.cols < N) {
+        const int n2 = N - pc.cols;
+        const float *B2 = B + pc.cols;
+        float *C2 = C + pc.cols;
+        const int v2 = select_variant(m, SGEMM_PATH_AUTO, pc.rows, n2, K, loads16(A, lda, B2, ldb, C2, ldc));
+        if (v2 < 0) return v2;
+        rc = launch(m, v2, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, pc.rows, n2, K, alpha, A, lda, B2, ldb, beta,
+                    C2, ldc, stream);
+        if (rc != SGEMM_OK) return rc;
+    }
+    if (pc.rows == M) return SGEMM_OK;
+    const float *A3 = A + (size_t)pc.rows * lda;
+    float *C3 = C + (size_t)pc.rows * ldc;
+    const int v3 = select_variant(m, SGEMM_PATH_AUTO, M - pc.rows, N, K, loads16(A3, lda, B, ldb, C3, ldc));
+    if (v3 < 0) return v3;
+    return launch(m, v3, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M - pc.rows, N, K, alpha, A3, lda, B, ldb, beta,
+                  C3, ldc, stream);
 }
 
 }  // namespace
@@ -823,8 +882,8 @@ int sgemm_path(int path, int M, int N, int K, float alpha, const float *A,
     const int v = select_variant(m, path, M, N, K, small);
     if (v < 0) return v;
     if (path != SGEMM_PATH_VALU) {
-        const int rows = split_rows(m, M, N, K, small);
-        if (rows > 0) return launch_rows(m, rows, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+        const Pieces pc = split_pieces(m, M, N, K, small);
+        if (pc.rows > 0) return launch_pieces(m, pc, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
     }
     return launch(m, v, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C,
                   ldc, stream);
@@ -887,9 +946,20 @@ int sgemm_ws_plan(int M, int N, int K, int *variant, int *splits, int *workers) 
 
 int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int operands_load16,
                    int *variant, int *splits, int *workers, int *rows) {
+    return sgemm_plan_pieces_for(compute_units, M, N, K, with_workspace, operands_load16, variant, splits,
+                                 workers, rows, nullptr);
+}
+
+int sgemm_plan_pieces_for(int compute_units, int M, int N, int K, int with_workspace, int operands_load16,
+                          int *variant, int *splits, int *workers, int *rows, int *cols) {
     if (compute_units < 1 || compute_units > (1 << 20)) return SGEMM_ERR_MACHINE;
     const Machine m = {compute_units, kMI355X.xcds};
-    return plan(m, M, N, K, with_workspace != 0, operands_load16 != 0, variant, splits, workers, rows);
+    Pieces pc;
+    const int rc = plan(m, M, N, K, with_workspace != 0, operands_load16 != 0, variant, splits, workers, &pc);
+    if (rc != SGEMM_OK) return rc;
+    if (rows) *rows = pc.rows;
+    if (cols) *cols = pc.cols;
+    return SGEMM_OK;
 }
 
 int sgemm_device_shape(int *compute_units, int *xcds) {
@@ -910,10 +980,19 @@ int sgemm_tile_order(int xcds, int nbm, int nbn, int *tile_m, int *tile_n) {
 }
 
 int sgemm_select_rows(int M, int N, int K) {
+    int rows = 0;
+    const int rc = sgemm_select_pieces(M, N, K, &rows, nullptr);
+    return rc < 0 ? rc : rows;
+}
+
+int sgemm_select_pieces(int M, int N, int K, int *rows, int *cols) {
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
-    return split_rows(device_machine(), M, N, K, true);
+    const Pieces pc = split_pieces(device_machine(), M, N, K, true);
+    if (rows) *rows = pc.rows;
+    if (cols) *cols = pc.cols;
+    return SGEMM_OK;
 }
 
 int sgemm_select_streamk(int M, int N, int K) {
@@ -941,8 +1020,9 @@ int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const fl
     const int rc = check_args(M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (rc != SGEMM_OK) return rc;
     const Machine m = device_machine();
-    int v = 0, sp = 1, w = 0, rows = 0;
-    const int prc = plan(m, M, N, K, true, loads16(A, lda, B, ldb, C, ldc), &v, &sp, &w, &rows);
+    int v = 0, sp = 1, w = 0;
+    Pieces pc;
+    const int prc = plan(m, M, N, K, true, loads16(A, lda, B, ldb, C, ldc), &v, &sp, &w, &pc);
     if (prc != SGEMM_OK) return prc;
     const bool room = workspace != nullptr && ((uintptr_t)workspace & 255u) == 0;
     if (w > 0 || sp > 1) {
@@ -953,7 +1033,7 @@ int sgemm_ws(int M, int N, int K, float alpha, const float *A, int lda, const fl
         // not enough workspace: exactly sgemm()
         return sgemm_path(SGEMM_PATH_AUTO, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
     }
-    if (rows > 0) return launch_rows(m, rows, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
+    if (pc.rows > 0) return launch_pieces(m, pc, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream);
     return launch(m, v, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                   stream);
 }

@@ -11,7 +11,8 @@ launches after about 30 ms of untimed ones (0.5 s after the GPU has idled,
 so that the clock has ramped up).  Besides the forced variants,
 two rows time the library's own choice: ``auto`` (``sgemm``) and ``auto+ws``
 (``sgemm_ws`` with the workspace it asks for, which may split K or share the
-K tiles of a last partial round of tiles over stream-K workers).  The last block is a table of the selection
+K tiles of a last partial round of tiles over stream-K workers).  Where
+``sgemm`` cuts C into pieces, a third row times its block as one launch.  The last block is a table of the selection
 against the best variant per shape: the measurement the selection table in
 ``sgemm.hip`` was fitted to, repeatable on any MI355X.
 """
@@ -103,7 +104,7 @@ def tune(shapes, variants=None, out=sys.stdout, accesses=("auto",)):
         # the library's plans for these very operands (their alignment matters)
         cus = g.sgemm_device_shape()[0]
         o16 = g.sgemm_operands_load16(a, p.lda, b, p.ldb, c, p.ldc)
-        _, auto, _, _, rows_first = g.sgemm_plan_for(cus, p.M, p.N, p.K, False, o16)
+        _, auto, _, _, cut_r, cut_c = g.sgemm_plan_pieces_for(cus, p.M, p.N, p.K, False, o16)
         rows = {}
         for v in variants:
             for acc in accesses:
@@ -124,19 +125,30 @@ def tune(shapes, variants=None, out=sys.stdout, accesses=("auto",)):
         _, ws_variant, splits, workers, _ = g.sgemm_plan_for(cus, p.M, p.N, p.K, True, o16)
         for name, (ms, tf) in rows.items():
             print(f"{shape:24s} {name:34s} {tf:8.2f} TFLOP/s {ms:10.4f} ms", file=out, flush=True)
+        one = None
+        if cut_r > 0:  # the same block as one launch over all of C, timed beside the cut
+            one = _time(lambda: g.sgemm_variant(auto, *args, stream=stream), flops, stream)
+            print(f"{shape:24s} {'auto as one launch':34s} {one[1]:8.2f} TFLOP/s {one[0]:10.4f} ms",
+                  file=out, flush=True)
         forced = {k: v for k, v in rows.items() if k not in ("auto", "auto+ws")}
         best = min(forced, key=lambda k: forced[k][0])
         selected = g.sgemm_variant_name(auto)
-        if rows_first > 0:  # C split by rows: two launches
-            rest = g.sgemm_plan_for(cus, p.M - rows_first, p.N, p.K, False, o16)[1]
-            selected = (f"rows 0..{rows_first - 1} as 256 x 256 tiles, "
-                        f"rest: {g.sgemm_variant_name(rest)}")
+        if cut_r > 0:  # C cut into pieces, one launch each
+            parts = [f"{cut_r} x {cut_c} as 256 x 256 tiles"]
+            if cut_c < p.N:
+                right = g.sgemm_plan_for(cus, cut_r, p.N - cut_c, p.K, False, o16)[1]
+                parts.append(f"right {cut_r} x {p.N - cut_c}: {g.sgemm_variant_name(right)}")
+            if cut_r < p.M:
+                below = g.sgemm_plan_for(cus, p.M - cut_r, p.N, p.K, False, o16)[1]
+                parts.append(f"below {p.M - cut_r} x {p.N}: {g.sgemm_variant_name(below)}")
+            selected = ", ".join(parts) + f" (one launch of {g.sgemm_variant_name(auto)}: {one[1]:.2f})"
         table.append({"shape": shape, "M": p.M, "N": p.N, "K": p.K,
                       "selected": selected, "selected_ws": g.sgemm_variant_name(ws_variant),
                       "splits": splits, "workers": workers,
                       "auto_ms": rows["auto"][0], "auto_ws_ms": rows["auto+ws"][0],
                       "best": best, "best_ms": forced[best][0],
-                      "auto_ws_tflops": rows["auto+ws"][1], "auto_tflops": rows["auto"][1]})
+                      "auto_ws_tflops": rows["auto+ws"][1], "auto_tflops": rows["auto"][1],
+                      "one_launch_tflops": one[1] if one else None})
         del a, b, c, ws, p
         torch.cuda.empty_cache()
     print("\n| shape | selected (`sgemm`) | with workspace (`sgemm_ws`: splits, stream-K workers) | "

@@ -90,9 +90,10 @@ extern "C" {
 #define SGEMM_ERR_SCRATCH (-27)
 
 /* C = alpha*A*B + beta*C, automatic choice of inner product and tile.  One
- * kernel launch, or two on the same stream when sgemm_select_rows() is
- * positive (C split by rows, each part a whole product of its own; nothing
- * allocated, no order between the parts' results). */
+ * kernel launch, or two or three on the same stream when sgemm_select_rows()
+ * is positive (C cut into pieces by sgemm_select_pieces(), each a whole
+ * product of its own; nothing allocated, no order between the pieces'
+ * results). */
 int sgemm(int M, int N, int K, float alpha, const float *A, int lda,
           const float *B, int ldb, float beta, float *C, int ldc,
           hipStream_t stream);
@@ -292,7 +293,7 @@ int sgemm_variant_reads_a128(int variant);
 /* The variant sgemm_path(path, M, N, K, ...) launches for these sizes with
  * operands that allow 16-byte loads (above), or a negative code (-1..-3,
  * SGEMM_ERR_PATH).  Host logic only, no HIP call.  When sgemm_select_rows()
- * is positive, an AUTO or MFMA call runs another plan (below). */
+ * is positive, an AUTO or MFMA call cuts C into pieces instead (below). */
 int sgemm_select_variant(int path, int M, int N, int K);
 
 /* The same for these operands: the pointers and leading dimensions decide
@@ -309,14 +310,23 @@ int sgemm_select_variant_for(int path, int M, int N, int K, const float *A, int 
  * them.  The pointers are only inspected.  Host logic only. */
 int sgemm_operands_load16(const float *A, int lda, const float *B, int ldb, const float *C, int ldc);
 
-/* Rows of C that sgemm() (path AUTO or MFMA), and sgemm_ws() when it
- * neither splits K nor runs stream-K, compute as a first launch of 256 x 256
- * tiles that fill their rounds of the device's compute units; the rows below
- * follow in a second launch with the variant
- * sgemm_select_variant(path, M - rows, N, K).  0: one launch.  A multiple
- * of 256 below M, or a negative argument code (-1..-3).  Host logic only.
+/* How sgemm() (path AUTO or MFMA), and sgemm_ws() when it neither splits
+ * K nor runs stream-K, cut C into pieces, one launch each, so that the first
+ * piece's 256 x 256 tiles fill their rounds of the device's compute units:
+ * through *rows and *cols (either may be NULL) the first piece, C's rows
+ * [0, rows) and columns [0, cols), or rows = 0 for one launch.  rows is a
+ * multiple of 256 up to M; cols is N (a cut by rows alone) or a multiple of
+ * 256 below N.  After the first piece come, when cols < N, the columns
+ * [cols, N) of the same rows (with the variant
+ * sgemm_select_variant(AUTO, rows, N - cols, K)), then, when rows < M, the
+ * rows [rows, M) over all N columns (sgemm_select_variant(AUTO, M - rows, N,
+ * K)).  Returns 0 or a negative argument code (-1..-3).  Host logic only.
  * (Quantisation of tiles over the compute units: "如何高效实现矩阵乘？CUDA
  * 初学者的角度入门", section "Wave & L2 cache Hit Rate".) */
+int sgemm_select_pieces(int M, int N, int K, int *rows, int *cols);
+
+/* The rows of sgemm_select_pieces()'s first piece (0: one launch), or a
+ * negative argument code (-1..-3).  Host logic only. */
 int sgemm_select_rows(int M, int N, int K);
 
 /* The machine shape the current device's choices use: its compute units and
@@ -334,12 +344,18 @@ int sgemm_device_shape(int *compute_units, int *xcds);
  * runs with enough workspace, else what sgemm() runs; operands_load16 != 0
  * for operands that allow 16-byte loads (above), 0 for others.  Through
  * the pointers (each may be NULL): the variant, the split count (1: none),
- * the stream-K worker count (0: none) and the rows of a first row-split
- * launch (0: one launch).  Returns 0, a negative argument code (-1..-3 for
- * M, N, K), or SGEMM_ERR_MACHINE for compute_units outside 1..2^20.  Host
- * logic only. */
+ * the stream-K worker count (0: none) and the rows of the first piece when
+ * C is cut into pieces (sgemm_select_pieces(); 0: one launch).  Returns 0, a
+ * negative argument code (-1..-3 for M, N, K), or SGEMM_ERR_MACHINE for
+ * compute_units outside 1..2^20.  Host logic only. */
 int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int operands_load16,
                    int *variant, int *splits, int *workers, int *rows);
+
+/* sgemm_plan_for() that also gives the first piece's columns through *cols
+ * (may be NULL; N for a cut by rows alone, 0 with rows = 0). */
+int sgemm_plan_pieces_for(int compute_units, int M, int N, int K, int with_workspace,
+                          int operands_load16, int *variant, int *splits, int *workers, int *rows,
+                          int *cols);
 
 /* The workgroup -> tile order of the K-ordered blocks on a device of `xcds`
  * XCDs, for a grid of nbm x nbn tiles: workgroup p computes tile

@@ -323,29 +323,42 @@ def test_streamk_host_logic():
                            workspace=0x10000, workspace_bytes=1 << 30, stream=0, check=False) == -23
 
 
-def test_row_split_host_logic():
-    """Without a workspace, a partial last round of 256 x 256 tiles is
-    avoided by a first launch over the rows whose tiles fill their rounds
-    (7168^3: 27 block rows of 28 tiles, 756 = 2.95 rounds); the rows below
-    go to a second launch.  Whole rounds, short K and small shapes keep one
-    launch."""
-    for M, N, K, rows in [(7168, 7168, 7168, 6912), (9216, 9216, 9216, 8960),
-                          (13824, 13824, 13824, 13312)]:
-        got = g.sgemm_select_rows(M, N, K)
-        assert got == rows, (M, N, K, got)
-        t = (got // 256) * ((N + 255) // 256)
-        assert t / (-(-t // 256) * 256) >= 0.96  # busy share of the rounds
+def test_pieces_host_logic():
+    """Without a workspace, a partial last round of tiles is avoided by
+    cutting C into pieces: a first piece at the top left whose 256 x 256
+    tiles fill their rounds (7168^3: 28 x 27 = 756 tiles, 2.95 rounds of
+    256), then the columns right of it, then the rows below it.  Whole
+    rounds, a gain under 2% once each 256 x 256 tile's start is priced
+    (13824^3), K below 1024 and small shapes keep one launch."""
+    for M, N, K, rows, cols in [(7168, 7168, 7168, 7168, 6912), (9216, 9216, 9216, 8192, 8192),
+                                (5120, 5120, 5120, 4096, 4096), (4300, 4301, 2048, 4096, 4096),
+                                (8256, 2047, 2048, 8192, 2047), (65536, 300, 4096, 65536, 256)]:
+        rc, r, c = g.sgemm_select_pieces(M, N, K)
+        assert (rc, r, c) == (0, rows, cols), (M, N, K, r, c)
+        assert g.sgemm_select_rows(M, N, K) == rows
+        t = (r // 256) * -(-c // 256)
+        assert t >= 256 and t / (-(-t // 256) * 256) >= 0.96  # busy share of the rounds
     for M, N, K in [(8192, 8192, 8192), (4096, 4096, 4096), (16384, 16384, 16384), (6144, 6144, 6144),
-                    (5120, 5120, 5120), (16384, 16384, 128), (1024, 8192, 8192), (1000, 1023, 999),
-                    (256, 256, 256), (0, 8192, 8192), (8192, 0, 8192), (8192, 8192, 0)]:
+                    (12288, 12288, 12288), (13824, 13824, 13824), (16384, 16384, 128),
+                    (1024, 8192, 8192), (1000, 1023, 999),
+                    (256, 256, 256), (0, 8192, 8192), (8192, 0, 8192), (8192, 8192, 0),
+                    (8872, 10147, 512), (7926, 6380, 512), (11083, 5078, 1024)]:
+        assert g.sgemm_select_pieces(M, N, K) == (0, 0, 0), (M, N, K)
         assert g.sgemm_select_rows(M, N, K) == 0, (M, N, K)
     for M in range(512, 20000, 509):
         for N in (3000, 7168, 11000):
-            r = g.sgemm_select_rows(M, N, 4096)
-            assert r == 0 or (r % 256 == 0 and 0 < r < M), (M, N, r)
-    assert g.sgemm_select_rows(-1, 4, 4) == -1
-    assert g.sgemm_select_rows(4, -1, 4) == -2
-    assert g.sgemm_select_rows(4, 4, -1) == -3
+            rc, r, c = g.sgemm_select_pieces(M, N, 4096)
+            assert rc == 0
+            if r == 0:
+                assert c == 0
+                continue
+            # the first piece: whole 256 x 256 tiles inside C, or every column
+            assert r % 256 == 0 and 0 < r <= M, (M, N, r, c)
+            assert c == N or (c % 256 == 0 and 0 < c < N), (M, N, r, c)
+            assert (r, c) != (M, N), (M, N)
+    for bad, code in [((-1, 4, 4), -1), ((4, -1, 4), -2), ((4, 4, -1), -3)]:
+        assert g.sgemm_select_rows(*bad) == code
+        assert g.sgemm_select_pieces(*bad)[0] == code
 
 
 def test_only_the_latency_block_splits_k():
@@ -473,6 +486,7 @@ def test_device_shape_and_plan_for_256_cus():
         assert rc == 0 and sp == 1 and w == 0
         assert v == g.sgemm_select_variant(g.SGEMM_PATH_AUTO, M, N, K), (M, N, K)
         assert rows == g.sgemm_select_rows(M, N, K), (M, N, K)
+        assert g.sgemm_plan_pieces_for(cus, M, N, K) == (rc, v, sp, w) + g.sgemm_select_pieces(M, N, K)[1:]
         rc, v2, sp2, w2, rows2 = g.sgemm_plan_for(cus, M, N, K, with_workspace=True)
         assert (rc, v2, sp2, w2) == g.sgemm_ws_plan(M, N, K), (M, N, K)
         assert sp2 == g.sgemm_select_splits(M, N, K) and w2 == g.sgemm_select_streamk(M, N, K)
@@ -570,17 +584,24 @@ def test_tile_order_is_a_bijection_for_every_xcd_count():
 def test_narrow_n_weighs_the_tiles_area_inside_c():
     """Padded tile columns still issue every MFMA: with N = 260 or 300 a
     256-wide block is 51-59% inside C, a 64 x 64 block 81-94%, and the
-    choice follows that share.  The row split's first part is 256 columns
-    wide too, so it is not taken either."""
-    for M, N, K in [(40000, 300, 4096), (65536, 260, 4096), (40000, 260, 4096), (16384, 300, 4096)]:
+    choice follows that share.  A cut into pieces never pads a 256-wide
+    first piece here: it takes the first 256 columns alone where their 256 x
+    256 tiles fill whole rounds (65536 rows: 256 tiles), measured 12.5%
+    faster than one launch at 65536 x 260 x 4096 and 65536 x 300 x 4096, the
+    rest of the columns going to a second launch."""
+    for M, N, K, cut in [(40000, 300, 4096, 0), (65536, 260, 4096, 256), (40000, 260, 4096, 0),
+                         (16384, 300, 4096, 0), (65536, 300, 4096, 256)]:
         v = g.sgemm_select_variant(g.SGEMM_PATH_AUTO, M, N, K)
         bm, bn, _ = _block(v)
         fill = M * N / (-(-M // bm) * bm * -(-N // bn) * bn)
         assert bn == 64 and fill >= 0.8, (M, N, K, g.sgemm_variant_name(v), fill)
-        assert g.sgemm_select_rows(M, N, K) == 0, (M, N, K)
-    # wide N keeps the 256 x 256 block and the row split where they fill C
+        assert g.sgemm_select_pieces(M, N, K) == ((0, M, cut) if cut else (0, 0, 0)), (M, N, K)
+        if cut:
+            v2 = g.sgemm_select_variant(g.SGEMM_PATH_AUTO, M, N - cut, K)
+            assert _block(v2)[1] == 64, g.sgemm_variant_name(v2)
+    # wide N keeps the 256 x 256 block and the cut where they fill C
     assert _block(g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 8192, 8192, 8192))[:2] == (256, 256)
-    assert g.sgemm_select_rows(7168, 7168, 7168) == 6912
+    assert g.sgemm_select_pieces(7168, 7168, 7168) == (0, 7168, 6912)
 
 
 def test_operands_load16_condition():

@@ -619,23 +619,23 @@ def test_sgemm_ws_streamk_full_size_sampled(name):
     """Shapes whose last round of tiles leaves slots idle: sgemm_ws shares
     the K tiles of the rest over one worker per slot (checked on sampled
     points against the oracle).  With no workspace it runs whole tiles, at
-    13824^3 and 7168^3 split by rows into two launches (the two rows at the
-    split are checked in full).  At 13824^3 neither tile grid has a multiple
+    7168^3 cut by columns into two launches and at 5120^3 into three pieces
+    (whole rows and columns on both sides of each cut are checked).  At 13824^3 neither tile grid has a multiple
     of 8 columns (54 of 256 x 256, 108 of 128 x 128), so both runs take the
     per-XCD column order."""
     M, N, K = (int(x) for x in name.split("x"))
     p = inputs.make_problem(M, N, K, dist="normal", seed=37, alpha=0.75, beta=0.5, c_fill="upm1")
     workers = g.sgemm_select_streamk(M, N, K)
     assert workers > 0
-    split = g.sgemm_select_rows(M, N, K)
-    assert (split > 0) == (M in (13824, 7168)), split
+    _, cut_r, cut_c = g.sgemm_select_pieces(M, N, K)
+    assert (cut_r > 0) == (M in (7168, 5120)), (cut_r, cut_c)
     need = g.sgemm_workspace_size(M, N, K)
     ws = torch.full((need // 4 + 64,), float("nan"), dtype=torch.float32, device="cuda")
     rows, cols = inputs.sample_points(M, N, n_random=2048, seed=41)
-    if split > 0:
-        edge = np.repeat(np.array([split - 1, split]), N)
-        rows = np.concatenate([rows, edge])
-        cols = np.concatenate([cols, np.tile(np.arange(N), 2)])
+    if cut_r > 0:
+        r1, c1 = cut_lines(M, N, cut_r, cut_c)
+        rows = np.concatenate([rows, r1])
+        cols = np.concatenate([cols, c1])
     for workspace in (ws, None):
         oa, _, a = gu.to_gpu(p.A)
         ob, _, b = gu.to_gpu(p.B)
@@ -648,25 +648,41 @@ def test_sgemm_ws_streamk_full_size_sampled(name):
         del oa, ob, oc
 
 
+def cut_lines(M, N, rows, cols):
+    """Whole rows and columns on both sides of a cut at (rows, cols), and C's
+    first and last ones, as (rows, cols) point vectors."""
+    er = sorted({x for x in (0, rows - 1, rows, M - 1) if 0 <= x < M})
+    ec = sorted({x for x in (0, cols - 1, cols, N - 1) if 0 <= x < N})
+    r = np.concatenate([np.repeat(er, N), np.tile(np.arange(M), len(ec))]).astype(np.int32)
+    c = np.concatenate([np.tile(np.arange(N), len(er)), np.repeat(ec, M)]).astype(np.int32)
+    return r, c
+
+
 @pytest.mark.parametrize("offsets", [(0, 0, 0), (1, 2, 3)])
 @pytest.mark.parametrize("beta", [0.0, -0.75])
-def test_row_split_through_sgemm(offsets, beta):
-    """A shape that sgemm() splits by rows into two launches (8256 x 2047 x
-    512: the first 8192 rows on 256 x 256 tiles, the last 64 rows with their
-    own block): N % 4 != 0 and the misaligned bases take the builds loading
-    A and B 16 bytes at a time at 4-byte alignment;
-    ldc is padded (its pad columns must keep their bits), nothing outside C
-    is written, beta = 0 runs over a NaN C; every element against the
-    oracle."""
-    M, N, K = 8256, 2047, 512
-    assert g.sgemm_select_rows(M, N, K) == 8192
+@pytest.mark.parametrize("shape", [(8256, 2047, 2048, 8192, 2047), (4300, 4301, 2048, 4096, 4096)])
+def test_pieces_through_sgemm(shape, offsets, beta):
+    """Shapes that sgemm() cuts into pieces: 8256 x 2047 x 2048 by rows (the
+    first 8192 rows on 256 x 256 tiles, the last 64 with their own block),
+    4300 x 4301 x 2048 in three (4096 x 4096 on 256 x 256 tiles, the 205
+    columns right of it over those rows, the 204 rows below over every
+    column).  N % 4 != 0 and the misaligned bases take the builds loading A
+    and B 16 bytes at a time at 4-byte alignment; ldc is padded (its pad
+    columns must keep their bits) and nothing outside C is written.  beta = 0
+    runs over a NaN C, so every element must come out finite: each is written
+    by a piece.  Whole rows and columns on both sides of each cut, C's edges
+    and random points against the oracle."""
+    M, N, K, rows, cols = shape
+    assert g.sgemm_select_pieces(M, N, K) == (0, rows, cols)
     p = inputs.make_problem(M, N, K, dist="upm1", seed=47, alpha=1.25, beta=beta,
                             c_fill="upm1" if beta != 0 else "nan", lda=K + 3, ldb=N + 1, ldc=N + 5)
-    gu.say("row split via sgemm", M, N, K, "beta", beta, "offsets", offsets)
+    gu.say("pieces via sgemm", M, N, K, "cut", rows, cols, "beta", beta, "offsets", offsets)
     out = gu.run(p, offsets=offsets)
     assert gu.pad_untouched(p, out)
     assert np.all(np.isfinite(out[:, :N]))
-    assert gu.ratio_full(p, out) <= TOL
+    r1, c1 = cut_lines(M, N, rows, cols)
+    r2, c2 = inputs.sample_points(M, N, n_random=4096, seed=43)
+    assert gu.ratio_points(p, out, np.concatenate([r1, r2]), np.concatenate([c1, c2])) <= TOL
 
 
 @pytest.mark.parametrize("name", ["square256_u01", "ragged_1000x1023x999", "512x512x8192",
