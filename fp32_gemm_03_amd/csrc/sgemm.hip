@@ -207,7 +207,7 @@ constexpr int kKcTiny4Ring = 19; // 17 with three LDS stages
 constexpr int kRingMinK = 2048;  // the shortest K at which 19 beats 17
 
 // The machine shape the choices depend on: compute units (tile quantisation,
-// stream-K workers, the split-K and row-split thresholds) and XCDs (the
+// stream-K workers, the split-K thresholds and the cut into pieces) and XCDs (the
 // workgroup -> tile order).  The choice of tile is a pure function of the
 // sizes and this shape, so it is the same on every call and testable without
 // a GPU (sgemm_plan_for).
