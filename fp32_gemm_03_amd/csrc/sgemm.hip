@@ -355,13 +355,25 @@ double fill(int M, int N, int bm, int bn) {
 // 128 x 128 x 32, and up to 1% at 5120^3-7168^3 on 128 x 128 x 16.  Scored
 // as the block's full-chip rate times kStreamKShare, the measured cost of the
 // partial tiles and their summing pass, when each worker gets at least
-// kStreamKMinK K tiles.  So with a workspace the large squares whose
-// 256 x 256 tiles leave a partial round (of the cubes measured from 5120^3
-// to 14848^3, all but 8192^3 and 12288^3) run stream-K on 256 x 256 x 32 at
-// 141-146 TFLOP/s: 3-5% above the best whole-tile block, 1% at 12800^3,
-// level at 10240^3 and 0.4% below 128 x 128 x 16 at 6144^3.
+// kStreamKMinK K tiles, and priced by kTileStartK below.  So with a
+// workspace the large squares whose 256 x 256 tiles leave a partial round run
+// stream-K on 256 x 256 x 32 at 141-146 TFLOP/s, 3-5% above the best
+// whole-tile block (5120^3, 7168^3, 13824^3); where stream-K's gain was 1% or
+// less, the price leaves whole tiles (6144^3 0.4% faster on 128 x 128 x 16,
+// 10240^3 and 12800^3 about 1% slower).
 constexpr double kStreamKShare = 0.985;
 constexpr int kStreamKMinK = 8;
+// A fixed cost per tile (its first loads, its write-back of C), as this many
+// more steps of K, where nothing overlaps it: on the stream-K workers'
+// partial tiles, and on the 256 x 256 tiles of a cut's first piece (one
+// workgroup per CU).  For stream-K, over 57 shapes 1024-8192 wide where the
+// price changed the plan of sgemm_ws, the new plans ran 3.5% faster in
+// geometric mean: 5.1% with K = 1024 (33 shapes; 3584 x 8192 x 1024 on
+// whole 128 x 128 x 16 tiles 142.9 against 130.9 stream-K on 256 x 256), 2.3%
+// with K = 2048, level at 4096; five ran 1-4% slower (7680 x 6656 x 1024,
+// 4096 x 5120 x 4096).  Smaller prices took fewer of the gains (25: 1.6%, 50:
+// 2.4%).
+constexpr double kTileStartK = 75.0;
 // K from which stream-K on 64 x 64 x 32 beats the 64 x 64 x 64 block at one
 // or two tiles per CU (1280^2 x 4096 yes, 1280^3 and 1408^3 no)
 constexpr int kStreamKLongK = 2048;
@@ -383,6 +395,15 @@ constexpr double kSmallRate = 110.0;
 constexpr double kSmall4Rate = 134.0;
 constexpr double kTiny2Rate = 129.3;
 constexpr int kTiny2MinK = 1024;
+// A block of one workgroup per CU also qualifies with its tiles just short of
+// one round, at least this share of the CUs busy (scored by that share):
+// over 49 shapes 1024-7680 wide where that changed the choice (to 128 x 256
+// from 128 x 128, or to 256 x 256 from 128 x 256), every one ran as fast or
+// faster, 2.6% in geometric mean (2816^3 135.2 against 131.1, 3584 x 4608 x
+// 4096 145.5 against 141.8).  From 70% of the CUs the smaller blocks' finer
+// grids won back (1536 x 2048 x 2048 on 128 x 128 tiles: 102.4 against 129.2
+// on 64 x 64).
+constexpr double kShortRoundShare = 0.9;
 
 // The variant for a whole-tile (or, with streamk, stream-K) launch on a
 // machine of m.cus compute units; *score gets its predicted TFLOP/s (rate x
@@ -426,14 +447,16 @@ int choose(const Machine &m, int path, int M, int N, int K, bool streamk, bool s
         const Variant &v = kVariants[c.variant];
         const long long t = tiles(M, N, v.bm, v.bn);
         const long long slots = c.per_cu * cus;
-        if (t < slots || K < c.min_k) continue;
+        const bool short_round = c.per_cu == 1 && t < slots;
+        if ((short_round ? (double)t < kShortRoundShare * (double)slots : t < slots) || K < c.min_k) continue;
         const double f = fill(M, N, v.bm, v.bn);
         double score = c.rate * quantization(t, cus) * f;
         int w = 0;
         const long long rest = t % cus, kt = (K + v.bk - 1) / v.bk;
-        if (streamk && v.streamk && rest > 0 && rest * kt >= kStreamKMinK * cus &&
-            c.rate * kStreamKShare * f > score) {
-            score = c.rate * kStreamKShare * f;
+        const double sk_score = c.rate * kStreamKShare * f * K / (K + kTileStartK);
+        if (streamk && v.streamk && !short_round && rest > 0 && rest * kt >= kStreamKMinK * cus &&
+            sk_score > score) {
+            score = sk_score;
             w = (int)cus;
         }
         if (score > best_score) {
@@ -516,14 +539,13 @@ int select_variant(const Machine &m, int path, int M, int N, int K, bool small_o
 
 // The first piece's 256 x 256 tiles run one workgroup per CU: each pays its
 // first loads and its write-back of C with nothing to overlap them, priced
-// as kPiecesTileK more steps of K per tile.  Over 93 shapes measured both
+// as kTileStartK more steps of K per tile.  Over 93 shapes measured both
 // ways (cubes 4352-11776, rectangles 2048 to 20000 wide, K 512-8192),
 // pricing the rate alone with K of 2048 or more took 75 cuts, 12 of them up
 // to 3% slower than one launch; with this price the model takes 51, of which
 // 49 ran 0.2-9.3% faster and two 2.4% and 3.1% slower (3.6% faster in
 // geometric mean).  With K of 512, 8 of 10 cuts predicted 2% faster ran
 // slower.
-constexpr double kPiecesTileK = 75.0;
 constexpr int kPiecesMinK = 1024;
 
 struct Pieces {
@@ -580,7 +602,7 @@ Pieces split_pieces(const Machine &m, int M, int N, int K, bool small_ok) {
             if (t_right < 0.0) continue;
             const double fill = full ? (double)N / (double)(nbn * 256) : 1.0;
             const double t_split =
-                per_elem * m1 * (double)n1 / (kHuge16Rate * q * fill) * (K + kPiecesTileK) / K + t_right + t_below;
+                per_elem * m1 * (double)n1 / (kHuge16Rate * q * fill) * (K + kTileStartK) / K + t_right + t_below;
             if (t_split < best_t) {
                 best_t = t_split;
                 best.rows = m1;
