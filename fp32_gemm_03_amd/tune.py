@@ -2,6 +2,7 @@
 shape's fastest variant with the one the library's selection picks.
 
     python -m fp32_gemm_03_amd.tune [--shapes S1,S2,...] [--variants V1,V2,...] [--access M1,...]
+    python -m fp32_gemm_03_amd.tune --plans MxNxK:V/S/W:V/S/W,...
 
 A shape is a named synthetic workload (``square8192_normal`` ...) or MxNxK
 (A, B ~ N(0,1), seed 3, alpha 1, beta 0; ``MxNxK_beta``: beta 1 with C ~
@@ -87,6 +88,58 @@ def _time(launch, flops, stream, target_s=0.1, warmup_s=0.03):
 ACCESS_MODES = {"auto": 0, "buf128": 1, "buf32": 2, "checked": 3, "buf128ab": 4}
 
 
+def time_plans(items, out=sys.stdout):
+    """Time explicit plans against each other: each item is
+    ``MxNxK:PLAN:PLAN...`` with a PLAN ``variant/splits/workers`` run through
+    sgemm_variant (whole tiles, no cut), sgemm_splitk or sgemm_streamk with a
+    workspace.  Each plan is timed twice, alternating, and its better run kept;
+    the ratio is the last plan's rate over the first's."""
+    import math
+    import torch
+    import fp32_gemm_03_amd as g
+
+    g.load_library()
+    stream = torch.cuda.Stream()
+    ratios = []
+    for item in items:
+        shape, *plans = item.split(":")
+        p = _problem(shape)
+        a, b, c = p.A.cuda(), p.B.cuda(), p.C.cuda()
+        args = (p.M, p.N, p.K, p.alpha, a, p.lda, b, p.ldb, p.beta, c, p.ldc)
+        flops = 2.0 * p.M * p.N * p.K
+        launches = []
+        for plan in plans:
+            v, sp, w = (int(x) for x in plan.split("/"))
+            if w > 0:
+                need = g.sgemm_streamk_workspace_size(v, w)
+            elif sp > 1:
+                need = g.sgemm_splitk_workspace_size(v, sp, p.M, p.N)
+            else:
+                need = 0
+            ws = torch.empty(max(need // 4, 1) + 64, dtype=torch.float32, device="cuda")
+            if w > 0:
+                launches.append(lambda v=v, w=w, ws=ws: g.sgemm_streamk(v, w, *args, workspace=ws, stream=stream))
+            elif sp > 1:
+                launches.append(lambda v=v, sp=sp, ws=ws: g.sgemm_splitk(v, sp, *args, workspace=ws, stream=stream))
+            else:
+                launches.append(lambda v=v: g.sgemm_variant(v, *args, stream=stream))
+        best = [0.0] * len(plans)
+        for _ in range(2):
+            for i, fn in enumerate(launches):
+                best[i] = max(best[i], _time(fn, flops, stream)[1])
+        ratios.append(best[-1] / best[0])
+        cols = "  ".join(f"{pl} {g.sgemm_variant_name(int(pl.split('/')[0]))} {tf:.1f}"
+                         for pl, tf in zip(plans, best))
+        print(f"{shape:20s} {cols}  ratio {best[-1] / best[0]:.3f}", file=out, flush=True)
+        del a, b, c, p, launches
+        torch.cuda.empty_cache()
+    if ratios:
+        geo = math.exp(sum(math.log(r) for r in ratios) / len(ratios))
+        print(f"{len(ratios)} shapes: ratio geometric mean {geo:.3f}, min {min(ratios):.3f}, "
+              f"max {max(ratios):.3f}", file=out, flush=True)
+    return ratios
+
+
 def tune(shapes, variants=None, out=sys.stdout, accesses=("auto",)):
     import torch
     import fp32_gemm_03_amd as g
@@ -166,10 +219,15 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--shapes", default=",".join(DEFAULT_SHAPES))
     ap.add_argument("--variants", default=None, help="comma-separated variant indices (default: all)")
+    ap.add_argument("--plans", default=None,
+                    help="comma-separated MxNxK:v/s/w:v/s/w items: time those plans against each other")
     ap.add_argument("--access", default="auto",
                     help="comma-separated access modes to time each variant in: "
                          + ", ".join(ACCESS_MODES) + " (default: auto, the variant's own choice)")
     args = ap.parse_args()
+    if args.plans:
+        time_plans(args.plans.split(","))
+        return
     variants = None if args.variants is None else [int(x) for x in args.variants.split(",")]
     accesses = args.access.split(",")
     for acc in accesses:
