@@ -112,9 +112,9 @@ def load_library():
         lib.sgemm_ws_plan.restype = i
         lib.sgemm_plan_for.argtypes = [i, i, i, i, i, i] + [ctypes.POINTER(i)] * 4
         lib.sgemm_plan_for.restype = i
-        lib.sgemm_plan_pieces_for.argtypes = [i, i, i, i, i, i] + [ctypes.POINTER(i)] * 5
+        lib.sgemm_plan_pieces_for.argtypes = [i, i, i, i, i, i] + [ctypes.POINTER(i)] * 6
         lib.sgemm_plan_pieces_for.restype = i
-        lib.sgemm_select_pieces.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+        lib.sgemm_select_pieces.argtypes = [i, i, i] + [ctypes.POINTER(i)] * 3
         lib.sgemm_select_pieces.restype = i
         lib.sgemm_device_shape.argtypes = [ctypes.POINTER(i), ctypes.POINTER(i)]
         lib.sgemm_device_shape.restype = i
@@ -267,11 +267,13 @@ def sgemm_select_rows(M, N, K) -> int:
 
 
 def sgemm_select_pieces(M, N, K):
-    """``(status, rows, cols)``: the first piece ``sgemm`` cuts C into, rows x cols at the
-    top left on 256 x 256 tiles (rows 0: one launch; cols == N: a cut by rows alone)."""
-    r, c = ctypes.c_int(0), ctypes.c_int(0)
-    rc = load_library().sgemm_select_pieces(int(M), int(N), int(K), ctypes.byref(r), ctypes.byref(c))
-    return int(rc), r.value, c.value
+    """``(status, rows, cols, first_variant)``: the first piece ``sgemm`` cuts C into, rows x
+    cols at the top left, and the variant it runs on (rows 0: one launch; cols == N: a cut by
+    rows alone)."""
+    r, c, v = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(-1)
+    rc = load_library().sgemm_select_pieces(int(M), int(N), int(K), ctypes.byref(r), ctypes.byref(c),
+                                            ctypes.byref(v))
+    return int(rc), r.value, c.value, v.value
 
 
 def sgemm_ws_plan(M, N, K):
@@ -295,15 +297,15 @@ def sgemm_plan_for(compute_units, M, N, K, with_workspace=False, operands_load16
 
 
 def sgemm_plan_pieces_for(compute_units, M, N, K, with_workspace=False, operands_load16=True):
-    """``sgemm_plan_for`` with the first piece's columns: ``(status, variant, splits,
-    workers, rows, cols)``."""
+    """``sgemm_plan_for`` with the first piece's columns and variant: ``(status, variant,
+    splits, workers, rows, cols, first_variant)``."""
     v, sp, w = ctypes.c_int(-1), ctypes.c_int(0), ctypes.c_int(0)
-    r, c = ctypes.c_int(0), ctypes.c_int(0)
+    r, c, fv = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(-1)
     rc = load_library().sgemm_plan_pieces_for(int(compute_units), int(M), int(N), int(K),
                                               1 if with_workspace else 0, 1 if operands_load16 else 0,
                                               ctypes.byref(v), ctypes.byref(sp), ctypes.byref(w),
-                                              ctypes.byref(r), ctypes.byref(c))
-    return int(rc), v.value, sp.value, w.value, r.value, c.value
+                                              ctypes.byref(r), ctypes.byref(c), ctypes.byref(fv))
+    return int(rc), v.value, sp.value, w.value, r.value, c.value, fv.value
 
 
 def sgemm_device_shape():

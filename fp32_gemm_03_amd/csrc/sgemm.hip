@@ -550,22 +550,37 @@ constexpr int kPiecesMinK = 1024;
 
 struct Pieces {
     int rows = 0, cols = 0;  // the first piece; rows == 0: one launch
+    int variant = -1;        // the first piece's block
 };
+
+// The blocks a cut's first piece may run on, one workgroup per CU each: the
+// 256 x 256 block first; the others only where it gives no cut, and only
+// with K of at least kPiecesOtherMinK.  Measured over 36 shapes 2048-6144
+// wide where only the others gave a cut: 1.8% faster than one launch in
+// geometric mean (5376 x 3328 x 3072 on 128 x 256 tiles 137.9 against 129.9,
+// 4608 x 3072 x 4096 on 128 x 128 140.4 against 132.8), 3 of the 4 slower
+// ones (1.0-1.6%) with K = 1024.
+struct FirstPiece {
+    int variant, bm, bn;
+    double rate;
+};
+constexpr int kPiecesOtherMinK = 1536;
 
 // Without a workspace there is no stream-K, and a partial last round of
 // tiles leaves CUs idle.  C can instead be cut into pieces, one launch each:
-// a first piece of rows x cols on 256 x 256 tiles that fill their rounds (at
-// least 96% of the last one busy), the columns right of it over those rows,
-// and the rows below it over every column, each of the two with the block
-// chosen for it.  cols == N cuts by rows alone (the first piece then pads its
-// last tile column), rows == M by columns alone.  Returns {0, 0} when one
-// launch is predicted within 2% of the best cut.  Measured against one
-// launch, in the same process: 4352^3 141.0 against 128.9 TFLOP/s, 5120^3
-// 142.8 against 137.4, 7168^3 144.7 against 138.0, 11264^3 146.1 against
-// 141.6; at 5120^3, 7168^3, 9216^3, 11264^3 and 13824^3 the cut the model
-// picked (without the price of a tile's start) ran within 0.3% of the best
-// of up to 40 cuts tried.  Only the last
-// 64 block rows and 32 block columns are tried as the first piece's edges.
+// a first piece of rows x cols whose tiles fill their rounds (at least 96% of
+// the last one busy) on a block of one workgroup per CU (FirstPiece), the
+// columns right of it over those rows, and the rows below it over every
+// column, each of the two with the block chosen for it.  cols == N cuts by
+// rows alone (the first piece then pads its last tile column), rows == M by
+// columns alone.  Returns rows = 0 when one launch is predicted within 2% of
+// the best cut.  Measured against one launch, in the same process: 4352^3
+// 141.0 against 128.9 TFLOP/s, 5120^3 142.8 against 137.4, 7168^3 144.7
+// against 138.0, 11264^3 146.1 against 141.6; at 5120^3, 7168^3, 9216^3,
+// 11264^3 and 13824^3 the cut the model picked (without the price of a
+// tile's start) ran within 0.3% of the best of up to 40 cuts tried.  Only the
+// last 64 block rows and 32 block columns are tried as the first piece's
+// edges.
 Pieces split_pieces(const Machine &m, int M, int N, int K, bool small_ok) {
     Pieces best;
     if (K < kPiecesMinK || M < 512) return best;
@@ -581,37 +596,44 @@ Pieces split_pieces(const Machine &m, int M, int N, int K, bool small_ok) {
         if (choose(m, SGEMM_PATH_AUTO, m1, n1, K, false, small_ok, nullptr, &s) < 0 || s <= 0.0) return -1.0;
         return per_elem * m1 * (double)n1 / s;
     };
-    const long long nbn = (N + 255) / 256;
-    const long long rb_hi = M / 256, rb_lo = rb_hi > 64 ? rb_hi - 64 : 1;
-    const long long cb_hi = (N - 1) / 256, cb_lo = cb_hi > 32 ? cb_hi - 32 : 1;
-    for (long long rb = rb_hi; rb >= rb_lo; --rb) {
-        const int m1 = (int)(rb * 256);
-        double t_below = -2.0;  // the piece below, chosen once per rb
-        // cb = nbn: every column, padded (a cut by rows only)
-        for (long long cb = nbn; cb >= cb_lo; --cb) {
-            const bool full = cb == nbn;
-            if (full && m1 == M) continue;  // that is the single launch
-            const long long t = rb * cb;
-            if (t < m.cus) break;
-            const double q = quantization(t, m.cus);
-            if (q < 0.96) continue;
-            const int n1 = full ? N : (int)(cb * 256);
-            if (t_below == -2.0) t_below = piece(M - m1, N);
-            if (t_below < 0.0) break;
-            const double t_right = full ? 0.0 : piece(m1, N - n1);
-            if (t_right < 0.0) continue;
-            const double fill = full ? (double)N / (double)(nbn * 256) : 1.0;
-            const double t_split =
-                per_elem * m1 * (double)n1 / (kHuge16Rate * q * fill) * (K + kTileStartK) / K + t_right + t_below;
-            if (t_split < best_t) {
-                best_t = t_split;
-                best.rows = m1;
-                best.cols = n1;
+    static const FirstPiece firsts[] = {{kKcHuge16, 256, 256, kHuge16Rate},
+                                        {kKcWide, 128, 256, 143.0},
+                                        {kKcDeep8, 128, 128, 139.5}};
+    for (const FirstPiece &fp : firsts) {
+        // the other blocks only where the 256 x 256 one gives no cut
+        if (fp.variant != kKcHuge16 && (best.variant == kKcHuge16 || K < kPiecesOtherMinK)) break;
+        const long long nbn = (N + fp.bn - 1) / fp.bn;
+        const long long rb_hi = M / fp.bm, rb_lo = rb_hi > 64 ? rb_hi - 64 : 1;
+        const long long cb_hi = (N - 1) / fp.bn, cb_lo = cb_hi > 32 ? cb_hi - 32 : 1;
+        for (long long rb = rb_hi; rb >= rb_lo; --rb) {
+            const int m1 = (int)(rb * fp.bm);
+            double t_below = -2.0;  // the piece below, chosen once per rb
+            // cb = nbn: every column, padded (a cut by rows only)
+            for (long long cb = nbn; cb >= cb_lo; --cb) {
+                const bool full = cb == nbn;
+                if (full && m1 == M) continue;  // that is one launch
+                const long long t = rb * cb;
+                if (t < m.cus) break;
+                const double q = quantization(t, m.cus);
+                if (q < 0.96) continue;
+                const int n1 = full ? N : (int)(cb * fp.bn);
+                if (t_below == -2.0) t_below = piece(M - m1, N);
+                if (t_below < 0.0) break;
+                const double t_right = full ? 0.0 : piece(m1, N - n1);
+                if (t_right < 0.0) continue;
+                const double fill = full ? (double)N / (double)(nbn * fp.bn) : 1.0;
+                const double t_split =
+                    per_elem * m1 * (double)n1 / (fp.rate * q * fill) * (K + kTileStartK) / K + t_right + t_below;
+                if (t_split < best_t && t_split < 0.98 * t_single) {
+                    best_t = t_split;
+                    best.rows = m1;
+                    best.cols = n1;
+                    best.variant = fp.variant;
+                }
             }
         }
     }
-    if (best_t < 0.98 * t_single) return best;
-    return Pieces{};
+    return best;
 }
 
 // Split count for a variant when a workspace is available (measured on
@@ -855,14 +877,14 @@ int launch(const Machine &m, int variant, int access, int splits, int workers, v
     return err == hipSuccess ? SGEMM_OK : (int)err;
 }
 
-// C cut into pieces: rows x cols at the top left on the 16-wave 256 x 256
-// block, then the columns right of it over the same rows and the rows below
-// it over every column, each with the block chosen for it; one launch each,
-// on the same stream.  Moving B and C by cols columns keeps their alignment
-// (cols is a multiple of 256).
+// C cut into pieces: rows x cols at the top left on the first piece's block,
+// then the columns right of it over the same rows and the rows below it over
+// every column, each with the block chosen for it; one launch each, on the
+// same stream.  Moving B and C by cols columns keeps their alignment (cols is
+// a multiple of 128).
 int launch_pieces(const Machine &m, Pieces pc, int M, int N, int K, float alpha, const float *A, int lda,
                   const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
-    int rc = launch(m, kKcHuge16, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, pc.rows, pc.cols, K, alpha, A, lda,
+    int rc = launch(m, pc.variant, SGEMM_ACCESS_AUTO, 1, 0, nullptr, 0, pc.rows, pc.cols, K, alpha, A, lda,
                     B, ldb, beta, C, ldc, stream);
     if (rc != SGEMM_OK) return rc;
     if (pc.cols < N) {
@@ -969,11 +991,11 @@ int sgemm_ws_plan(int M, int N, int K, int *variant, int *splits, int *workers) 
 int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, int operands_load16,
                    int *variant, int *splits, int *workers, int *rows) {
     return sgemm_plan_pieces_for(compute_units, M, N, K, with_workspace, operands_load16, variant, splits,
-                                 workers, rows, nullptr);
+                                 workers, rows, nullptr, nullptr);
 }
 
 int sgemm_plan_pieces_for(int compute_units, int M, int N, int K, int with_workspace, int operands_load16,
-                          int *variant, int *splits, int *workers, int *rows, int *cols) {
+                          int *variant, int *splits, int *workers, int *rows, int *cols, int *first_variant) {
     if (compute_units < 1 || compute_units > (1 << 20)) return SGEMM_ERR_MACHINE;
     const Machine m = {compute_units, kMI355X.xcds};
     Pieces pc;
@@ -981,6 +1003,7 @@ int sgemm_plan_pieces_for(int compute_units, int M, int N, int K, int with_works
     if (rc != SGEMM_OK) return rc;
     if (rows) *rows = pc.rows;
     if (cols) *cols = pc.cols;
+    if (first_variant) *first_variant = pc.variant;
     return SGEMM_OK;
 }
 
@@ -1003,17 +1026,18 @@ int sgemm_tile_order(int xcds, int nbm, int nbn, int *tile_m, int *tile_n) {
 
 int sgemm_select_rows(int M, int N, int K) {
     int rows = 0;
-    const int rc = sgemm_select_pieces(M, N, K, &rows, nullptr);
+    const int rc = sgemm_select_pieces(M, N, K, &rows, nullptr, nullptr);
     return rc < 0 ? rc : rows;
 }
 
-int sgemm_select_pieces(int M, int N, int K, int *rows, int *cols) {
+int sgemm_select_pieces(int M, int N, int K, int *rows, int *cols, int *first_variant) {
     if (M < 0) return -1;
     if (N < 0) return -2;
     if (K < 0) return -3;
     const Pieces pc = split_pieces(device_machine(), M, N, K, true);
     if (rows) *rows = pc.rows;
     if (cols) *cols = pc.cols;
+    if (first_variant) *first_variant = pc.variant;
     return SGEMM_OK;
 }
 

@@ -157,7 +157,7 @@ def tune(shapes, variants=None, out=sys.stdout, accesses=("auto",)):
         # the library's plans for these very operands (their alignment matters)
         cus = g.sgemm_device_shape()[0]
         o16 = g.sgemm_operands_load16(a, p.lda, b, p.ldb, c, p.ldc)
-        _, auto, _, _, cut_r, cut_c = g.sgemm_plan_pieces_for(cus, p.M, p.N, p.K, False, o16)
+        _, auto, _, _, cut_r, cut_c, cut_v = g.sgemm_plan_pieces_for(cus, p.M, p.N, p.K, False, o16)
         rows = {}
         for v in variants:
             for acc in accesses:
@@ -187,7 +187,7 @@ def tune(shapes, variants=None, out=sys.stdout, accesses=("auto",)):
         best = min(forced, key=lambda k: forced[k][0])
         selected = g.sgemm_variant_name(auto)
         if cut_r > 0:  # C cut into pieces, one launch each
-            parts = [f"{cut_r} x {cut_c} as 256 x 256 tiles"]
+            parts = [f"{cut_r} x {cut_c}: {g.sgemm_variant_name(cut_v)}"]
             if cut_c < p.N:
                 right = g.sgemm_plan_for(cus, cut_r, p.N - cut_c, p.K, False, o16)[1]
                 parts.append(f"right {cut_r} x {p.N - cut_c}: {g.sgemm_variant_name(right)}")

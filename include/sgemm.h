@@ -312,18 +312,21 @@ int sgemm_operands_load16(const float *A, int lda, const float *B, int ldb, cons
 
 /* How sgemm() (path AUTO or MFMA), and sgemm_ws() when it neither splits
  * K nor runs stream-K, cut C into pieces, one launch each, so that the first
- * piece's 256 x 256 tiles fill their rounds of the device's compute units:
- * through *rows and *cols (either may be NULL) the first piece, C's rows
- * [0, rows) and columns [0, cols), or rows = 0 for one launch.  rows is a
- * multiple of 256 up to M; cols is N (a cut by rows alone) or a multiple of
- * 256 below N.  After the first piece come, when cols < N, the columns
+ * piece's tiles fill their rounds of the device's compute units: through
+ * *rows, *cols and *first_variant (each may be NULL) the first piece, C's
+ * rows [0, rows) and columns [0, cols), and the variant it runs on (a block
+ * of one workgroup per CU: 256 x 256, or 128 x 256 or 128 x 128 where the
+ * 256 x 256 block gives no cut), or rows = 0 (and first_variant -1) for one
+ * launch.  rows is a multiple of the block's rows up to M; cols is N (a cut
+ * by rows alone) or a multiple of the block's columns below N.  After the
+ * first piece come, when cols < N, the columns
  * [cols, N) of the same rows (with the variant
  * sgemm_select_variant(AUTO, rows, N - cols, K)), then, when rows < M, the
  * rows [rows, M) over all N columns (sgemm_select_variant(AUTO, M - rows, N,
  * K)).  Returns 0 or a negative argument code (-1..-3).  Host logic only.
  * (Quantisation of tiles over the compute units: "如何高效实现矩阵乘？CUDA
  * 初学者的角度入门", section "Wave & L2 cache Hit Rate".) */
-int sgemm_select_pieces(int M, int N, int K, int *rows, int *cols);
+int sgemm_select_pieces(int M, int N, int K, int *rows, int *cols, int *first_variant);
 
 /* The rows of sgemm_select_pieces()'s first piece (0: one launch), or a
  * negative argument code (-1..-3).  Host logic only. */
@@ -352,10 +355,11 @@ int sgemm_plan_for(int compute_units, int M, int N, int K, int with_workspace, i
                    int *variant, int *splits, int *workers, int *rows);
 
 /* sgemm_plan_for() that also gives the first piece's columns through *cols
- * (may be NULL; N for a cut by rows alone, 0 with rows = 0). */
+ * (N for a cut by rows alone, 0 with rows = 0) and its variant through
+ * *first_variant (-1 with rows = 0); either may be NULL. */
 int sgemm_plan_pieces_for(int compute_units, int M, int N, int K, int with_workspace,
                           int operands_load16, int *variant, int *splits, int *workers, int *rows,
-                          int *cols);
+                          int *cols, int *first_variant);
 
 /* The workgroup -> tile order of the K-ordered blocks on a device of `xcds`
  * XCDs, for a grid of nbm x nbn tiles: workgroup p computes tile

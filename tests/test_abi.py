@@ -325,37 +325,47 @@ def test_streamk_host_logic():
 
 def test_pieces_host_logic():
     """Without a workspace, a partial last round of tiles is avoided by
-    cutting C into pieces: a first piece at the top left whose 256 x 256
-    tiles fill their rounds (7168^3: 28 x 27 = 756 tiles, 2.95 rounds of
-    256), then the columns right of it, then the rows below it.  Whole
-    rounds, a gain under 2% once each 256 x 256 tile's start is priced
-    (13824^3), K below 1024 and small shapes keep one launch."""
-    for M, N, K, rows, cols in [(7168, 7168, 7168, 7168, 6912), (9216, 9216, 9216, 8192, 8192),
-                                (5120, 5120, 5120, 4096, 4096), (4300, 4301, 2048, 4096, 4096),
-                                (8256, 2047, 2048, 8192, 2047), (65536, 300, 4096, 65536, 256)]:
-        rc, r, c = g.sgemm_select_pieces(M, N, K)
-        assert (rc, r, c) == (0, rows, cols), (M, N, K, r, c)
+    cutting C into pieces: a first piece at the top left whose tiles fill
+    their rounds (7168^3: 28 x 27 = 756 tiles of 256 x 256, 2.95 rounds of
+    256), then the columns right of it, then the rows below it.  The first
+    piece runs on the 256 x 256 block, or on 128 x 256 or 128 x 128 tiles
+    where that gives no cut and K >= 1536.  Whole rounds, a gain under 2%
+    once each tile's start is priced (13824^3), K below 1024 and small shapes
+    keep one launch."""
+    blocks = {15: (256, 256), 10: (128, 256), 12: (128, 128)}
+    for M, N, K, rows, cols, v in [(7168, 7168, 7168, 7168, 6912, 15), (9216, 9216, 9216, 8192, 8192, 15),
+                                   (5120, 5120, 5120, 4096, 4096, 15), (4300, 4301, 2048, 4096, 4096, 15),
+                                   (8256, 2047, 2048, 8192, 2047, 15), (65536, 300, 4096, 65536, 256, 15),
+                                   (5376, 3328, 3072, 4992, 3328, 10), (4608, 3072, 4096, 4096, 1024, 12),
+                                   (2946, 2901, 2048, 2944, 2816, 12)]:
+        got = g.sgemm_select_pieces(M, N, K)
+        assert got == (0, rows, cols, v), (M, N, K, got)
         assert g.sgemm_select_rows(M, N, K) == rows
-        t = (r // 256) * -(-c // 256)
+        bm, bn = blocks[v]
+        assert g.sgemm_variant_tile(v)[1:] == (bm, bn)
+        t = (rows // bm) * -(-cols // bn)
         assert t >= 256 and t / (-(-t // 256) * 256) >= 0.96  # busy share of the rounds
     for M, N, K in [(8192, 8192, 8192), (4096, 4096, 4096), (16384, 16384, 16384), (6144, 6144, 6144),
                     (12288, 12288, 12288), (13824, 13824, 13824), (16384, 16384, 128),
                     (1024, 8192, 8192), (1000, 1023, 999),
                     (256, 256, 256), (0, 8192, 8192), (8192, 0, 8192), (8192, 8192, 0),
-                    (8872, 10147, 512), (7926, 6380, 512), (11083, 5078, 1024)]:
-        assert g.sgemm_select_pieces(M, N, K) == (0, 0, 0), (M, N, K)
+                    (8872, 10147, 512), (7926, 6380, 512), (11083, 5078, 1024), (4608, 3072, 1024)]:
+        assert g.sgemm_select_pieces(M, N, K) == (0, 0, 0, -1), (M, N, K)
         assert g.sgemm_select_rows(M, N, K) == 0, (M, N, K)
     for M in range(512, 20000, 509):
         for N in (3000, 7168, 11000):
-            rc, r, c = g.sgemm_select_pieces(M, N, 4096)
-            assert rc == 0
-            if r == 0:
-                assert c == 0
-                continue
-            # the first piece: whole 256 x 256 tiles inside C, or every column
-            assert r % 256 == 0 and 0 < r <= M, (M, N, r, c)
-            assert c == N or (c % 256 == 0 and 0 < c < N), (M, N, r, c)
-            assert (r, c) != (M, N), (M, N)
+            for K in (1536, 4096):
+                rc, r, c, v = g.sgemm_select_pieces(M, N, K)
+                assert rc == 0
+                if r == 0:
+                    assert (c, v) == (0, -1)
+                    continue
+                # the first piece: whole tiles inside C, or every column
+                bm, bn = blocks[v]
+                assert r % bm == 0 and 0 < r <= M, (M, N, r, c)
+                assert c == N or (c % bn == 0 and 0 < c < N), (M, N, r, c)
+                assert (r, c) != (M, N), (M, N)
+                assert v == 15 or K >= 1536
     for bad, code in [((-1, 4, 4), -1), ((4, -1, 4), -2), ((4, 4, -1), -3)]:
         assert g.sgemm_select_rows(*bad) == code
         assert g.sgemm_select_pieces(*bad)[0] == code
@@ -584,24 +594,27 @@ def test_tile_order_is_a_bijection_for_every_xcd_count():
 def test_narrow_n_weighs_the_tiles_area_inside_c():
     """Padded tile columns still issue every MFMA: with N = 260 or 300 a
     256-wide block is 51-59% inside C, a 64 x 64 block 81-94%, and the
-    choice follows that share.  A cut into pieces never pads a 256-wide
-    first piece here: it takes the first 256 columns alone where their 256 x
-    256 tiles fill whole rounds (65536 rows: 256 tiles), measured 12.5%
-    faster than one launch at 65536 x 260 x 4096 and 65536 x 300 x 4096, the
-    rest of the columns going to a second launch."""
-    for M, N, K, cut in [(40000, 300, 4096, 0), (65536, 260, 4096, 256), (40000, 260, 4096, 0),
-                         (16384, 300, 4096, 0), (65536, 300, 4096, 256)]:
+    choice follows that share.  A cut into pieces never pads a wide first
+    piece here: it takes the first 256 (or 128) columns alone where their
+    tiles fill whole rounds (65536 rows: 256 tiles of 256 x 256; 32768 rows:
+    256 of 128 x 128), the rest of the columns going to a second launch.
+    Measured against one launch: 65536 x 300 x 4096 130.5 against 116.7
+    TFLOP/s, 40000 x 300 x 4096 112.0 against 106.8."""
+    for M, N, K, cut in [(40000, 300, 4096, (32768, 128, 12)), (65536, 260, 4096, (65536, 256, 15)),
+                         (40000, 260, 4096, (32768, 128, 12)), (16384, 300, 4096, None),
+                         (65536, 300, 4096, (65536, 256, 15))]:
         v = g.sgemm_select_variant(g.SGEMM_PATH_AUTO, M, N, K)
         bm, bn, _ = _block(v)
         fill = M * N / (-(-M // bm) * bm * -(-N // bn) * bn)
         assert bn == 64 and fill >= 0.8, (M, N, K, g.sgemm_variant_name(v), fill)
-        assert g.sgemm_select_pieces(M, N, K) == ((0, M, cut) if cut else (0, 0, 0)), (M, N, K)
+        assert g.sgemm_select_pieces(M, N, K) == ((0,) + cut if cut else (0, 0, 0, -1)), (M, N, K)
         if cut:
-            v2 = g.sgemm_select_variant(g.SGEMM_PATH_AUTO, M, N - cut, K)
+            rows, cols, _ = cut
+            v2 = g.sgemm_select_variant(g.SGEMM_PATH_AUTO, rows, N - cols, K)
             assert _block(v2)[1] == 64, g.sgemm_variant_name(v2)
     # wide N keeps the 256 x 256 block and the cut where they fill C
     assert _block(g.sgemm_select_variant(g.SGEMM_PATH_AUTO, 8192, 8192, 8192))[:2] == (256, 256)
-    assert g.sgemm_select_pieces(7168, 7168, 7168) == (0, 7168, 6912)
+    assert g.sgemm_select_pieces(7168, 7168, 7168) == (0, 7168, 6912, 15)
 
 
 def test_operands_load16_condition():

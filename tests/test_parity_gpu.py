@@ -627,7 +627,7 @@ def test_sgemm_ws_streamk_full_size_sampled(name):
     p = inputs.make_problem(M, N, K, dist="normal", seed=37, alpha=0.75, beta=0.5, c_fill="upm1")
     workers = g.sgemm_select_streamk(M, N, K)
     assert workers > 0
-    _, cut_r, cut_c = g.sgemm_select_pieces(M, N, K)
+    _, cut_r, cut_c, _ = g.sgemm_select_pieces(M, N, K)
     assert (cut_r > 0) == (M in (7168, 5120)), (cut_r, cut_c)
     need = g.sgemm_workspace_size(M, N, K)
     ws = torch.full((need // 4 + 64,), float("nan"), dtype=torch.float32, device="cuda")
@@ -660,20 +660,22 @@ def cut_lines(M, N, rows, cols):
 
 @pytest.mark.parametrize("offsets", [(0, 0, 0), (1, 2, 3)])
 @pytest.mark.parametrize("beta", [0.0, -0.75])
-@pytest.mark.parametrize("shape", [(8256, 2047, 2048, 8192, 2047), (4300, 4301, 2048, 4096, 4096)])
+@pytest.mark.parametrize("shape", [(8256, 2047, 2048, 8192, 2047, 15), (4300, 4301, 2048, 4096, 4096, 15),
+                                   (2946, 2901, 2048, 2944, 2816, 12)])
 def test_pieces_through_sgemm(shape, offsets, beta):
     """Shapes that sgemm() cuts into pieces: 8256 x 2047 x 2048 by rows (the
     first 8192 rows on 256 x 256 tiles, the last 64 with their own block),
     4300 x 4301 x 2048 in three (4096 x 4096 on 256 x 256 tiles, the 205
     columns right of it over those rows, the 204 rows below over every
-    column).  N % 4 != 0 and the misaligned bases take the builds loading A
+    column), 2946 x 2901 x 2048 in three with the first piece on 128 x 128
+    tiles (2944 x 2816; then 85 columns, then 2 rows).  N % 4 != 0 and the misaligned bases take the builds loading A
     and B 16 bytes at a time at 4-byte alignment; ldc is padded (its pad
     columns must keep their bits) and nothing outside C is written.  beta = 0
     runs over a NaN C, so every element must come out finite: each is written
     by a piece.  Whole rows and columns on both sides of each cut, C's edges
     and random points against the oracle."""
-    M, N, K, rows, cols = shape
-    assert g.sgemm_select_pieces(M, N, K) == (0, rows, cols)
+    M, N, K, rows, cols, first = shape
+    assert g.sgemm_select_pieces(M, N, K) == (0, rows, cols, first)
     p = inputs.make_problem(M, N, K, dist="upm1", seed=47, alpha=1.25, beta=beta,
                             c_fill="upm1" if beta != 0 else "nan", lda=K + 3, ldb=N + 1, ldc=N + 5)
     gu.say("pieces via sgemm", M, N, K, "cut", rows, cols, "beta", beta, "offsets", offsets)
