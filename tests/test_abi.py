@@ -591,6 +591,35 @@ def test_tile_order_is_a_bijection_for_every_xcd_count():
     assert g.sgemm_tile_order(8, 0, 5) == (0, [], [])
 
 
+@pytest.mark.parametrize("cus", [32, 80, 256, 304])
+def test_pieces_tile_c_on_any_cu_count(cus):
+    """On any CU count, a cut's first piece is whole tiles of its block (or
+    every column, padded) inside C and not all of it, its tiles fill at least
+    96% of their last round of that many CUs, and only K >= 1024 is cut.
+    Random shapes, seeded."""
+    import numpy as np
+    blocks = {15: (256, 256), 10: (128, 256), 12: (128, 128)}
+    rng = np.random.default_rng(cus)
+    taken = 0
+    for _ in range(400):
+        M, N = (int(x) for x in rng.integers(256, 20000, 2))
+        K = int(rng.choice([512, 1024, 1536, 2048, 4096, 8192]))
+        rc, v, sp, w, rows, cols, first = g.sgemm_plan_pieces_for(cus, M, N, K)
+        assert rc == 0 and sp == 1 and w == 0
+        if rows == 0:
+            assert (cols, first) == (0, -1)
+            continue
+        taken += 1
+        assert first in blocks and K >= 1024, (M, N, K, first)
+        bm, bn = blocks[first]
+        assert rows % bm == 0 and 0 < rows <= M
+        assert cols == N or (cols % bn == 0 and 0 < cols < N)
+        assert (rows, cols) != (M, N)
+        t = (rows // bm) * -(-cols // bn)
+        assert t >= cus and t / (-(-t // cus) * cus) >= 0.96, (M, N, K, rows, cols, t)
+    assert taken > 0
+
+
 def test_narrow_n_weighs_the_tiles_area_inside_c():
     """Padded tile columns still issue every MFMA: with N = 260 or 300 a
     256-wide block is 51-59% inside C, a 64 x 64 block 81-94%, and the
