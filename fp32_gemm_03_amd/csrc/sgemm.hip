@@ -588,7 +588,12 @@ Pieces split_pieces(const Machine &m, int M, int N, int K, bool small_ok) {
     if (choose(m, SGEMM_PATH_AUTO, M, N, K, false, small_ok, nullptr, &single) < 0 || single <= 0.0) return best;
     const double per_elem = 2.0 * (double)K;
     const double t_single = per_elem * M * (double)N / single;
-    double best_t = t_single;
+    // No block's predicted rate exceeds the 256 x 256 block's, so no cut can
+    // beat a launch predicted within 2% of it (8192^3, whole rounds), and a
+    // cut whose first piece alone, with the rest at that rate, is slower
+    // than the best so far need not be priced further.
+    if (single >= 0.98 * kHuge16Rate) return best;
+    double best_t = 0.98 * t_single;
     // predicted time of an m1 x n1 piece with the block chosen for it
     auto piece = [&](int m1, int n1) {
         if (m1 == 0 || n1 == 0) return 0.0;
@@ -617,14 +622,16 @@ Pieces split_pieces(const Machine &m, int M, int N, int K, bool small_ok) {
                 const double q = quantization(t, m.cus);
                 if (q < 0.96) continue;
                 const int n1 = full ? N : (int)(cb * fp.bn);
+                const double fill = full ? (double)N / (double)(nbn * fp.bn) : 1.0;
+                const double t_first = per_elem * m1 * (double)n1 / (fp.rate * q * fill) * (K + kTileStartK) / K;
+                const double rest = per_elem * ((double)M * N - (double)m1 * n1) / kHuge16Rate;
+                if (t_first + rest >= best_t) continue;
                 if (t_below == -2.0) t_below = piece(M - m1, N);
                 if (t_below < 0.0) break;
                 const double t_right = full ? 0.0 : piece(m1, N - n1);
                 if (t_right < 0.0) continue;
-                const double fill = full ? (double)N / (double)(nbn * fp.bn) : 1.0;
-                const double t_split =
-                    per_elem * m1 * (double)n1 / (fp.rate * q * fill) * (K + kTileStartK) / K + t_right + t_below;
-                if (t_split < best_t && t_split < 0.98 * t_single) {
+                const double t_split = t_first + t_right + t_below;
+                if (t_split < best_t) {
                     best_t = t_split;
                     best.rows = m1;
                     best.cols = n1;
