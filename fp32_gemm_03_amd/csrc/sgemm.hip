@@ -118,7 +118,18 @@ const Variant kVariants[] = {
     MFMA_CFG_KCD(128, 256, 16, 64, 128, 2, 0, true, 0, 1, 1, "_kcd"),     // 9: 2 workgroups per CU
     MFMA_CFG_KCD(128, 256, 32, 64, 64, 2, 4, false, 2, 1, 0, "_w8_kcd"),  // 10: 8 waves, 2 per SIMD
     MFMA_CFG_KCD(64, 64, 32, 32, 32, 4, 4, false, 1, 2, 0, "_kcd"),       // 11: 4 workgroups per CU
-    MFMA_CFG_KCD(128, 128, 64, 32, 64, 2, 4, false, 2, 1, 0, "_w8_kcd"),  // 12: 8 waves, 2 per SIMD
+    // 12: 8 waves, 2 per SIMD.  Its whole-tile K-ordered builds lower the wave
+    // priority over each K tile (PR 1, as 15 does): 0.15-0.6% faster in ten
+    // paired runs (2048^3 136.4 against 135.6 TFLOP/s, 2048^2 x 4096 138.7
+    // against 138.1); on 14, two workgroups per CU, the same was up to 18%
+    // slower (4096 x 3072 x 4096 116.3 against 142.5).
+    {"mfma_128x128x64_w32x64_w8_kcd", SGEMM_PATH_MFMA, 128, 128, 64, 512,
+     sgk::sgemm_mfma_kc<128, 128, 64, 32, 64, 4, 2, false, 2, 1, 1, 2, false, 1, 0>,
+     sgk::sgemm_mfma<128, 128, 64, 32, 64, 4, 0, 1, 2, true, 1, 2, 0, false, true>,
+     sgk::sgemm_mfma<128, 128, 64, 32, 64, 4, 0, 1, 2, false, 1, 2, 0, false, true>,
+     sgk::sgemm_mfma_kc<128, 128, 64, 32, 64, 4, 2, true, 2, 0, 1, 2, false, 1>, 1, 1, 0,
+     sgk::sgemm_mfma_kc<128, 128, 64, 32, 64, 4, 2, false, 2, 1, 1, 2, true, 1, 0>,
+     sgk::sgemm_mfma_kc<128, 128, 64, 32, 64, 4, 2, true, 2, 0, 1, 2, true, 1>},
     // 13: the block for at most one tile per CU.  Its 128-bit build (and
     // the one for rows at 4-byte alignment) is two
     // wave groups (KG 2) of two 64 x 32 waves, each group half of every K
