@@ -337,7 +337,7 @@ def test_pieces_host_logic():
                                    (5120, 5120, 5120, 4096, 4096, 15), (4300, 4301, 2048, 4096, 4096, 15),
                                    (8256, 2047, 2048, 8192, 2047, 15), (65536, 300, 4096, 65536, 256, 15),
                                    (5376, 3328, 3072, 4992, 3328, 10), (4608, 3072, 4096, 4096, 1024, 12),
-                                   (2946, 2901, 2048, 2944, 2816, 12)]:
+                                   (2946, 2901, 2048, 2944, 2816, 12), (4122, 2098, 1536, 4096, 2048, 10)]:
         got = g.sgemm_select_pieces(M, N, K)
         assert got == (0, rows, cols, v), (M, N, K, got)
         assert g.sgemm_select_rows(M, N, K) == rows

@@ -661,14 +661,15 @@ def cut_lines(M, N, rows, cols):
 @pytest.mark.parametrize("offsets", [(0, 0, 0), (1, 2, 3)])
 @pytest.mark.parametrize("beta", [0.0, -0.75])
 @pytest.mark.parametrize("shape", [(8256, 2047, 2048, 8192, 2047, 15), (4300, 4301, 2048, 4096, 4096, 15),
-                                   (2946, 2901, 2048, 2944, 2816, 12)])
+                                   (2946, 2901, 2048, 2944, 2816, 12), (4122, 2098, 1536, 4096, 2048, 10)])
 def test_pieces_through_sgemm(shape, offsets, beta):
     """Shapes that sgemm() cuts into pieces: 8256 x 2047 x 2048 by rows (the
     first 8192 rows on 256 x 256 tiles, the last 64 with their own block),
     4300 x 4301 x 2048 in three (4096 x 4096 on 256 x 256 tiles, the 205
     columns right of it over those rows, the 204 rows below over every
     column), 2946 x 2901 x 2048 in three with the first piece on 128 x 128
-    tiles (2944 x 2816; then 85 columns, then 2 rows).  N % 4 != 0 and the misaligned bases take the builds loading A
+    tiles (2944 x 2816; then 85 columns, then 2 rows), 4122 x 2098 x 1536 with
+    it on 128 x 256 tiles (4096 x 2048; then 50 columns, then 26 rows).  N % 4 != 0 and the misaligned bases take the builds loading A
     and B 16 bytes at a time at 4-byte alignment; ldc is padded (its pad
     columns must keep their bits) and nothing outside C is written.  beta = 0
     runs over a NaN C, so every element must come out finite: each is written
