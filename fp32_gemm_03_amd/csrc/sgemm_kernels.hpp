@@ -1343,10 +1343,10 @@ __device__ __forceinline__ void mfma_tile_kc(const float *a_row, const int (&a_o
     // SIMD, one workgroup per CU) that is 0.1-0.6% faster in every one of 24
     // paired runs at 4096^3-16384^3, and faster than priority 3 for the first
     // quarter or half of the tile only.  On the 8-wave blocks with one
-    // workgroup per CU it is level to slightly faster (128 x 128 x 64: 0.15-
-    // 0.6% in ten paired runs, so that block uses it too), and up to 23%
-    // slower on blocks with two or four per CU where the last round of tiles
-    // is partial.
+    // workgroup per CU it is slightly faster (128 x 128 x 64 and 128 x 256 x
+    // 32: 0.15-0.7% in ten paired runs each, so those blocks use it too), and
+    // up to 23% slower on blocks with two or four per CU where the last round
+    // of tiles is partial.
     if (RO == 0) {
 #pragma unroll
     for (int i = 0; i < MI; ++i) av[0][i] = *reinterpret_cast<const float4 *>(a_row + i * 32 * BK + a_off[0]);
